@@ -1,0 +1,309 @@
+"""Pins of the CPU oracle: facts fixed by the pages or by mathematics, not by the
+oracle itself.
+
+Each ``pin_*`` takes the oracle module and raises AssertionError when the oracle
+disagrees.  They are collected by tests/test_oracle_pins.py and re-run against
+deliberately broken copies of the oracle in tests/test_oracle_mutations.py to
+show that plausible mistakes (a dropped term, a wrong sign or index, a
+transposed operand) are caught.
+
+Page citations refer to the papernotes.org notes on "Communication-Efficient LLM
+Adaptation over Decentralized GPU Meshes": "Key design 2" (anchor EMA),
+"Key design 3" (SVD, Tikhonov filter, two-sided projection, combination),
+"Training strategy" (AdamW, defaults) and "Ablations" (the meaning of the
+alpha and tau extremes).
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+EPS53 = 2.0 ** -53
+
+
+def _frac(a):
+    return np.array([[float(Fraction(x)) for x in row] for row in a])
+
+
+def _rand(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _haar(seed, n, r):
+    q, rr = np.linalg.qr(_rand(seed, n, r))
+    return q * np.where(np.diag(rr) < 0, -1.0, 1.0)
+
+
+def _relf(a, b):
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+def filt(o, M, G, tau):
+    """Full filter path of the oracle: SVD, Tikhonov response, projection."""
+    U, s, V, _ = o.svd(M, threads=2)
+    return o.project(U, o.tikhonov(s, tau), V, G)
+
+
+# ---- P1: hand-worked 4x3 case (exact rationals) --------------------------------
+
+def pin_worked_4x3(o):
+    g = json.load(open(os.path.join(GOLDEN, "worked_4x3.json")))
+    M = np.array(g["M"])
+    U, s, V, sweeps = o.svd(M, threads=1)
+    assert sweeps > 0
+    assert np.allclose(s, g["singular_values"], rtol=0, atol=1e-14), s
+    d = o.tikhonov(s, g["tau_p"])
+    assert np.allclose(d, [float(Fraction(x)) for x in g["d"]], rtol=0, atol=1e-15), d
+    G = np.array(g["G_mask"])
+    G_filt = o.project(U, d, V, G)
+    assert np.allclose(G_filt, _frac(g["G_filt"]), rtol=0, atol=1e-14), G_filt
+    G_proj = o.combine(G, G_filt, g["alpha"])
+    assert np.allclose(G_proj, _frac(g["G_proj"]), rtol=0, atol=1e-14), G_proj
+
+
+# ---- P2: AdamW with constant gradient, closed form over T steps ------------------
+
+def pin_adamw_constant_grad(o):
+    g = json.load(open(os.path.join(GOLDEN, "worked_4x3.json")))
+    a = g["adamw"]
+    gp = _frac(g["G_proj"])
+    W = np.full(gp.shape, a["W0"])
+    m = np.zeros_like(W)
+    v = np.zeros_like(W)
+    W1 = None
+    for t in range(1, a["T"] + 1):
+        W, m, v = o.adamw(W, m, v, gp, t, a["lr"], a["beta1"], a["beta2"], a["eps"], a["weight_decay"])
+        if t == 1:
+            W1 = W.copy()
+    c = 1.0 - a["lr"] * a["weight_decay"]
+    r = gp / (np.abs(gp) + a["eps"])
+    T = a["T"]
+    WT = c ** T * a["W0"] - a["lr"] * r * (1.0 - c ** T) / (1.0 - c)
+    assert np.allclose(W, WT, rtol=0, atol=1e-14), np.abs(W - WT).max()
+    W1ref = c * a["W0"] - a["lr"] * r
+    assert np.allclose(W1, W1ref, rtol=0, atol=1e-15)
+    # bias-corrected moments equal g and g^2 exactly in exact arithmetic
+    assert np.allclose(m / (1 - a["beta1"] ** T), gp, rtol=1e-13, atol=0)
+    assert np.allclose(v / (1 - a["beta2"] ** T), gp * gp, rtol=1e-12, atol=0)
+
+
+# ---- P3: alpha = 1 is plain AdamW on G_mask (torch.optim.AdamW, fp64, CPU) --------
+
+def pin_alpha1_is_torch_adamw(o):
+    import torch
+    hp = dict(tau_p=1e-3, alpha=1.0, beta_anc=0.9, lr=2e-5, beta1=0.9, beta2=0.999, eps=1e-8,
+              weight_decay=0.01)
+    m_, n_ = 9, 7
+    opt = o.Optimizer([(m_, n_)], hp, w_dtype="f64", state_dtype="f64", threads=1)
+    opt.anchor_update([_rand(1, m_, n_) * 1e-2])
+    W0 = _rand(2, m_, n_) * 0.02
+    p = torch.nn.Parameter(torch.tensor(W0, dtype=torch.float64))
+    topt = torch.optim.AdamW([p], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                             weight_decay=hp["weight_decay"], foreach=False)
+    W = W0.copy()
+    for k in range(6):
+        G = _rand(10 + k, m_, n_) * 1e-3
+        W = opt.step([W], [G])[0]
+        p.grad = torch.tensor(G, dtype=torch.float64)
+        topt.step()
+        assert np.allclose(W, p.detach().numpy(), rtol=0, atol=1e-16), np.abs(W - p.detach().numpy()).max()
+
+
+# ---- P4: tau = 0 and full rank: projectors onto col(M) / row(M) ------------------
+
+def pin_tau0_projectors(o):
+    # square, full rank: G_filt = G
+    M = _rand(3, 12, 12)
+    G = _rand(4, 12, 12)
+    assert _relf(filt(o, M, G, 0.0), G) < 1e-12
+    # tall: G_filt = M (M^T M)^-1 M^T G (row space is all of R^n)
+    M = _rand(5, 15, 6)
+    G = _rand(6, 15, 6)
+    ref = M @ np.linalg.solve(M.T @ M, M.T @ G)
+    assert _relf(filt(o, M, G, 0.0), ref) < 1e-11
+    # wide: G_filt = G M^T (M M^T)^-1 M
+    M = _rand(7, 5, 13)
+    G = _rand(8, 5, 13)
+    ref = (G @ M.T) @ np.linalg.solve(M @ M.T, M)
+    assert _relf(filt(o, M, G, 0.0), ref) < 1e-11
+
+
+# ---- P5: tau > 0, exact low rank with known factors (no SVD in the reference) -----
+
+def pin_known_factors(o):
+    for (m, n, r0, seed) in [(20, 11, 4, 11), (9, 17, 3, 12), (16, 16, 16, 13)]:
+        U0 = _haar(seed, m, r0)
+        V0 = _haar(seed + 100, n, r0)
+        s0 = np.sort(np.random.default_rng(seed).uniform(0.5, 2.0, r0))[::-1] * 1e-2
+        M = (U0 * s0) @ V0.T
+        G = _rand(seed + 200, m, n)
+        tau = 3e-3
+        d0 = s0 / (s0 + tau)
+        ref = U0 @ (d0[:, None] * (U0.T @ G @ V0) * d0[None, :]) @ V0.T
+        assert _relf(filt(o, M, G, tau), ref) < 1e-11, (m, n, _relf(filt(o, M, G, tau), ref))
+
+
+# ---- P6: rank one --------------------------------------------------------------
+
+def pin_rank_one(o):
+    u = _haar(21, 10, 1)[:, 0]
+    v = _haar(22, 7, 1)[:, 0]
+    sig, tau = 2.5, 0.7
+    M = sig * np.outer(u, v)
+    G = _rand(23, 10, 7)
+    d = sig / (sig + tau)
+    ref = d * d * (u @ G @ v) * np.outer(u, v)
+    assert _relf(filt(o, M, G, tau), ref) < 1e-12
+
+
+# ---- P7: a gradient inside a strong subspace passes nearly unchanged -------------
+
+def pin_strong_subspace(o):
+    m, n, k = 40, 30, 5
+    U0 = _haar(31, m, n)
+    V0 = _haar(32, n, n)
+    s = np.concatenate([np.linspace(10.0, 5.0, k), np.linspace(1e-3, 1e-4, n - k)])
+    M = (U0 * s) @ V0.T
+    C = _rand(33, k, k)
+    G = U0[:, :k] @ C @ V0[:, :k].T
+    tau = 1e-3
+    dk = (s[:k] / (s[:k] + tau)).min()
+    err = _relf(filt(o, M, G, tau), G)
+    assert err <= 1 - dk * dk + 1e-12, err
+    assert err < 1e-3
+
+
+# ---- P8: bounds and the two tau extremes -----------------------------------------
+
+def pin_bounds_and_limits(o):
+    import scipy.linalg
+    M = _rand(41, 14, 9)
+    G = _rand(42, 14, 9)
+    U, s, V, _ = o.svd(M, threads=1)
+    for tau in [1e-6, 1e-2, 1.0, 10.0]:
+        d = o.tikhonov(s, tau)
+        assert np.all(d >= 0) and np.all(d < 1)
+        Gf = o.project(U, d, V, G)
+        assert np.linalg.norm(Gf) <= d.max() ** 2 * np.linalg.norm(G) * (1 + 1e-12)
+    # tau -> infinity: tau^2 G_filt -> (M M^T)^1/2 G (M^T M)^1/2, so G_filt -> 0
+    tau = 1e7
+    lim = np.real(scipy.linalg.sqrtm(M @ M.T)) @ G @ np.real(scipy.linalg.sqrtm(M.T @ M))
+    Gf = o.project(U, o.tikhonov(s, tau), V, G)
+    assert _relf(tau * tau * Gf, lim) < 1e-5
+    # tau -> 0 with s >> tau: d -> 1
+    assert np.all(o.tikhonov(s, 1e-14) > 1 - 1e-12)
+    # zero singular value with tau = 0 reads d = 0
+    assert o.tikhonov(np.array([0.0, 1.0]), 0.0).tolist() == [0.0, 1.0]
+
+
+# ---- P9: equivariances -----------------------------------------------------------
+
+def pin_equivariance(o):
+    M = _rand(51, 11, 6)
+    G = _rand(52, 11, 6)
+    tau = 0.3
+    F = filt(o, M, G, tau)
+    # transpose: ties the wide path (A = M^T) to the tall path
+    assert _relf(filt(o, M.T.copy(), G.T.copy(), tau), F.T) < 1e-12
+    # orthogonal change of basis on both sides
+    QL = _haar(53, 11, 11)
+    QR = _haar(54, 6, 6)
+    assert _relf(filt(o, QL @ M @ QR.T, QL @ G @ QR.T, tau), QL @ F @ QR.T) < 1e-12
+    # scaling M and tau together
+    assert _relf(filt(o, 7.0 * M, G, 7.0 * tau), F) < 1e-12
+    # linear in G
+    G2 = _rand(55, 11, 6)
+    assert _relf(filt(o, M, 2.0 * G - 3.0 * G2, tau), 2.0 * F - 3.0 * filt(o, M, G2, tau)) < 1e-12
+
+
+# ---- P10: SVD against LAPACK and its defining properties -------------------------
+
+def pin_svd_lapack(o):
+    for (m, n, seed) in [(37, 23, 61), (23, 37, 62), (30, 30, 63), (64, 48, 64)]:
+        M = _rand(seed, m, n)
+        U, s, V, sweeps = o.svd(M, threads=3)
+        assert sweeps > 0
+        r = min(m, n)
+        s_ref = np.linalg.svd(M, compute_uv=False)
+        assert np.max(np.abs(s - s_ref)) <= 1e-13 * s_ref[0]
+        assert np.all(np.diff(s) <= 0)
+        assert np.linalg.norm((U * s) @ V.T - M) <= 50 * r * EPS53 * np.linalg.norm(M)
+        assert np.linalg.norm(U.T @ U - np.eye(r)) <= 50 * r * EPS53
+        assert np.linalg.norm(V.T @ V - np.eye(r)) <= 50 * r * EPS53
+        # the filtered gradient does not depend on which valid factors are used
+        Ul, sl, Vlt = np.linalg.svd(M, full_matrices=False)
+        G = _rand(seed + 1, m, n)
+        d, dl = o.tikhonov(s, 0.5), o.tikhonov(sl, 0.5)
+        assert _relf(o.project(U, d, V, G), o.project(Ul, dl, Vlt.T, G)) < 1e-12
+
+
+# ---- P11: brute force on tiny cases -----------------------------------------------
+
+def pin_tiny_cases(o):
+    a, b, c, dd = 3.0, -1.0, 2.0, 0.5
+    M = np.array([[a, b], [c, dd]])
+    S = a * a + b * b + c * c + dd * dd
+    D = a * dd - b * c
+    root = np.sqrt(S * S - 4 * D * D)
+    s_ref = np.sqrt([(S + root) / 2, (S - root) / 2])
+    _, s, _, _ = o.svd(M, threads=1)
+    assert np.allclose(s, s_ref, rtol=1e-14, atol=0)
+    # one column: s = ||M||, U = M / s, V = [1]
+    Mc = _rand(71, 6, 1)
+    U, s, V, _ = o.svd(Mc, threads=1)
+    assert abs(s[0] - np.sqrt((Mc ** 2).sum())) < 1e-14 * s[0]
+    assert np.allclose(U[:, 0], Mc[:, 0] / s[0], atol=1e-15) and V[0, 0] == 1.0
+    # one row
+    Mr = _rand(72, 1, 5)
+    U, s, V, _ = o.svd(Mr, threads=1)
+    assert abs(s[0] - np.linalg.norm(Mr)) < 1e-14 * s[0] and U[0, 0] == 1.0
+    # zero matrix: all singular values zero, d = 0, G_filt = 0
+    Z = np.zeros((5, 4))
+    U, s, V, _ = o.svd(Z, threads=1)
+    assert np.all(s == 0)
+    Gf = o.project(U, o.tikhonov(s, 1e-3), V, _rand(73, 5, 4))
+    assert np.all(Gf == 0)
+
+
+# ---- P12: anchor EMA -----------------------------------------------------------
+
+def pin_ema(o):
+    M0 = _rand(81, 6, 5)
+    G = _rand(82, 6, 5)
+    beta = 0.9
+    M = M0.copy()
+    for _ in range(7):
+        M = o.ema(M, G, beta)
+    # k updates with a constant anchor gradient: beta^k M0 + (1 - beta^k) G
+    assert np.allclose(M, beta ** 7 * M0 + (1 - beta ** 7) * G, rtol=0, atol=1e-14)
+    assert np.array_equal(o.ema(M0, G, 0.0), G) and np.array_equal(o.ema(M0, G, 1.0), M0)
+    assert o.ema(np.array([2.0]), np.array([4.0]), 0.5)[0] == 3.0
+
+
+# ---- P13: determinism across thread counts ----------------------------------------
+
+def pin_thread_determinism(o):
+    M = _rand(91, 50, 34)
+    r1 = o.svd(M, threads=1)
+    r5 = o.svd(M, threads=5)
+    for a, b in zip(r1[:3], r5[:3]):
+        assert np.array_equal(a, b)
+    assert r1[3] == r5[3]
+
+
+# ---- storage rounding -----------------------------------------------------------
+
+def pin_storage_rounding(o):
+    x = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8 + 2.0 ** -30), 0.1, 2.0 ** -140])
+    got = o.round_storage(x, "bf16")
+    # ties to even, above-tie rounds up, 0.1 -> 0x3DCD = 0.10009765625, subnormal quantum 2^-133
+    assert got.tolist() == [1.0, 1.0 + 2.0 ** -6, -(1.0 + 2.0 ** -7), 0.10009765625, 0.0]
+    assert o.round_storage(np.array([0.1]), "f32")[0] == float(np.float32(0.1))
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

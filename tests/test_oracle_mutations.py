@@ -1,0 +1,147 @@
+"""Plant plausible mistakes in the CPU oracle and check that the pins catch each.
+
+Every mutation replaces one oracle function by a subtly wrong variant (a
+dropped term, a wrong sign or index, a transposed operand, a swapped
+coefficient) for the duration of one test; at least one pin of
+tests/oracle_pins.py must then fail.
+"""
+import numpy as np
+import pytest
+
+from tests import oracle_pins
+
+
+def _project_one_sided(U, d, V, G):
+    X = (U.T @ G) @ V
+    return (U @ (d[:, None] * X)) @ V.T
+
+
+def _project_transposed_x(U, d, V, G):
+    X = (U.T @ G) @ V
+    Xf = d[:, None] * X * d[None, :]
+    return (U @ Xf.T) @ V.T
+
+
+def _project_no_filter(U, d, V, G):
+    return (U @ ((U.T @ G) @ V)) @ V.T
+
+
+def _project_d_linear(U, d, V, G):
+    X = (U.T @ G) @ V
+    sd = np.sqrt(d)
+    return (U @ (sd[:, None] * X * sd[None, :])) @ V.T
+
+
+def _tikhonov_inverted(s, tau):
+    s = np.asarray(s, np.float64)
+    den = s + tau
+    out = np.zeros_like(s)
+    nz = den != 0
+    out[nz] = tau / den[nz]
+    return out
+
+
+def _tikhonov_double_tau(s, tau):
+    s = np.asarray(s, np.float64)
+    den = s + 2 * tau
+    out = np.zeros_like(s)
+    nz = den != 0
+    out[nz] = s[nz] / den[nz]
+    return out
+
+
+def _combine_swapped(G, Gf, alpha):
+    return (1 - alpha) * np.asarray(G) + alpha * np.asarray(Gf)
+
+
+def _adamw_no_bias_correction(W, m, v, g, t, lr, b1, b2, eps, wd):
+    W = np.asarray(W, np.float64)
+    m = b1 * m + (1 - b1) * g
+    v = b2 * v + (1 - b2) * g * g
+    return W - lr * wd * W - lr * m / (np.sqrt(v) + eps), m, v
+
+
+def _adamw_unscaled_decay(W, m, v, g, t, lr, b1, b2, eps, wd):
+    W = np.asarray(W, np.float64)
+    m = b1 * m + (1 - b1) * g
+    v = b2 * v + (1 - b2) * g * g
+    mh, vh = m / (1 - b1 ** t), v / (1 - b2 ** t)
+    return W - wd * W - lr * mh / (np.sqrt(vh) + eps), m, v
+
+
+def _adamw_eps_inside(W, m, v, g, t, lr, b1, b2, eps, wd):
+    W = np.asarray(W, np.float64)
+    m = b1 * m + (1 - b1) * g
+    v = b2 * v + (1 - b2) * g * g
+    mh, vh = m / (1 - b1 ** t), v / (1 - b2 ** t)
+    return W - lr * wd * W - lr * mh / np.sqrt(vh + eps), m, v
+
+
+def _adamw_swapped_betas(W, m, v, g, t, lr, b1, b2, eps, wd):
+    W = np.asarray(W, np.float64)
+    m = b2 * m + (1 - b2) * g
+    v = b1 * v + (1 - b1) * g * g
+    mh, vh = m / (1 - b2 ** t), v / (1 - b1 ** t)
+    return W - lr * wd * W - lr * mh / (np.sqrt(vh) + eps), m, v
+
+
+def _ema_swapped(M, G, beta):
+    return (1 - beta) * np.asarray(M, np.float64) + beta * np.asarray(G, np.float64)
+
+
+MUTATIONS = {
+    "project_one_sided_d": ("project", _project_one_sided),
+    "project_transposed_x": ("project", _project_transposed_x),
+    "project_no_filter": ("project", _project_no_filter),
+    "project_sqrt_d": ("project", _project_d_linear),
+    "tikhonov_inverted": ("tikhonov", _tikhonov_inverted),
+    "tikhonov_double_tau": ("tikhonov", _tikhonov_double_tau),
+    "combine_swapped": ("combine", _combine_swapped),
+    "adamw_no_bias_correction": ("adamw", _adamw_no_bias_correction),
+    "adamw_unscaled_decay": ("adamw", _adamw_unscaled_decay),
+    "adamw_eps_inside_sqrt": ("adamw", _adamw_eps_inside),
+    "adamw_swapped_betas": ("adamw", _adamw_swapped_betas),
+    "ema_swapped": ("ema", _ema_swapped),
+}
+
+
+def _svd_swapped_factors(orig):
+    def f(M, max_sweeps=100, threads=None):
+        U, s, V, sw = orig(M, max_sweeps, threads)
+        if U.shape[1] == V.shape[0] == V.shape[1] == U.shape[0]:
+            return V, s, U, sw
+        return U[::-1].copy(), s, V, sw  # reversed row index
+    return f
+
+
+def _svd_unsorted_vectors(orig):
+    def f(M, max_sweeps=100, threads=None):
+        U, s, V, sw = orig(M, max_sweeps, threads)
+        return U, s[::-1].copy(), V, sw  # values no longer paired with their vectors
+    return f
+
+
+WRAPPERS = {"svd_swapped_or_reversed": _svd_swapped_factors, "svd_unpaired_values": _svd_unsorted_vectors}
+
+
+def _pins_fail(o):
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(o)
+        except AssertionError:
+            failed.append(pin.__name__)
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, oracle_mod, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(oracle_mod, attr, fn)
+    assert _pins_fail(oracle_mod), f"mutation {name} passed every pin"
+
+
+@pytest.mark.parametrize("name", sorted(WRAPPERS))
+def test_svd_mutation_is_caught(name, oracle_mod, monkeypatch):
+    monkeypatch.setattr(oracle_mod, "svd", WRAPPERS[name](oracle_mod.svd))
+    assert _pins_fail(oracle_mod), f"mutation {name} passed every pin"
