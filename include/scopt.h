@@ -1,0 +1,174 @@
+/*
+ * scopt.h -- C ABI of the spectral-correction AdamW optimizer for AMD MI355X
+ * (gfx950), implemented with hand-written HIP kernels in libscopt.so.
+ *
+ * The method (papernotes.org notes on "Communication-Efficient LLM Adaptation
+ * over Decentralized GPU Meshes", arXiv 2609.14339):
+ *   - "Key design 2" (asynchronous dual circuit): the fast circuit keeps a
+ *     separate anchor momentum per weight matrix, updated with each delayed,
+ *     unmasked anchor gradient by an EMA with coefficient beta_anc;
+ *   - "Key design 3" (spectral-correction optimizer): SVD of the anchor
+ *     momentum M = U S V^T, Tikhonov response d_i = s_i / (s_i + tau_p), the
+ *     two-sided projection X = U^T G V, the filter X_filt = diag(d) X diag(d),
+ *     the reconstruction G_filt = U X_filt V^T and the convex combination
+ *     G_proj = alpha G_mask + (1 - alpha) G_filt;
+ *   - "Overall framework" and "Training strategy": the result feeds AdamW
+ *     (defaults tau_p = 1e-3, alpha = 0.3, beta_anc = 0.9, lr 2e-5).
+ *
+ * Conventions shared by every entry point
+ *   - Matrices are row-major [rows][cols] (PyTorch's [out, in]), contiguous.
+ *   - "device pointer": memory on the handle's device (hipMalloc'ed by the
+ *     caller, e.g. a torch tensor's data_ptr()); "host pointer": CPU memory.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls
+ *     that take a stream only enqueue work on it; the caller keeps inputs
+ *     alive and unmodified until that work is done (usual stream ordering).
+ *     sc_anchor_update / sc_refresh additionally synchronize the stream a few
+ *     times to stop the Jacobi sweeps once every matrix has converged (see
+ *     sc_hparams.sync_check).
+ *   - Return value: SC_OK (0) or a negative SC_ERR_* code; sc_last_error()
+ *     gives a message for the calling thread.  Arguments are validated before
+ *     any GPU work is enqueued; an invalid call changes nothing.
+ *   - A handle is not thread-safe; calls on one handle must be serialized.
+ *   - The library owns all optimizer state (anchor momentum, SVD factors,
+ *     filter, AdamW moments) and frees it in sc_opt_destroy.
+ */
+#ifndef SCOPT_H
+#define SCOPT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SC_OK 0
+#define SC_ERR_INVALID_ARG (-1) /* null pointer, bad index, bad hyper-parameter */
+#define SC_ERR_SHAPE (-2)       /* non-positive or too large matrix shape */
+#define SC_ERR_OOM (-3)         /* device memory allocation failed */
+#define SC_ERR_HIP (-4)         /* a HIP runtime call failed */
+#define SC_ERR_NO_DEVICE (-5)   /* no usable gfx950 device with that index */
+
+typedef struct sc_opt* sc_handle;
+
+typedef enum { SC_F32 = 0, SC_BF16 = 1 } sc_dtype;
+
+typedef struct {
+    float tau_p;        /* Tikhonov threshold tau_p ("Key design 3"), >= 0 */
+    float alpha;        /* convex-combination weight of G_mask, in [0, 1] */
+    float beta_anc;     /* anchor EMA coefficient ("Key design 2"), in [0, 1] */
+    float lr;           /* AdamW learning rate, >= 0 */
+    float beta1, beta2; /* AdamW moment coefficients, in [0, 1) */
+    float eps;          /* AdamW epsilon (added outside the square root), > 0 */
+    float weight_decay; /* decoupled weight decay, scaled by lr, >= 0 */
+    int max_sweeps;     /* Jacobi sweep cap per refresh, >= 1 (e.g. 30) */
+    float jacobi_tol;   /* rotation threshold |a_p.a_q| / (|a_p||a_q|); 0 = default 16 * 2^-24 */
+    int sync_check;     /* 1: poll convergence flags on the host (stops early);
+                           0: fully asynchronous, always max_sweeps sweeps */
+} sc_hparams;
+
+/* Fill `hp` with the defaults of the pages' training strategy:
+ * tau_p 1e-3, alpha 0.3, beta_anc 0.9, lr 2e-5, betas (0.9, 0.999), eps 1e-8,
+ * weight_decay 0.01, max_sweeps 30, jacobi_tol 0 (default), sync_check 1. */
+void sc_default_hparams(sc_hparams* hp);
+
+/* Create an optimizer over n_mats weight matrices of shapes rows[i] x cols[i]
+ * (host arrays).  w_dtype: storage type of the weights W; g_dtype: type of
+ * the masked gradients G_mask and the anchor gradients G_anc.  Anchor
+ * momentum, SVD factors and AdamW moments are float32.  The anchor momentum
+ * starts at zero, so until the first refresh d = 0 and G_filt = 0.
+ * device: HIP device index.  On success *out receives the handle.
+ * Errors: INVALID_ARG (null pointers, n_mats < 1, bad hyper-parameters),
+ * SHAPE (rows/cols < 1 or > 65536), NO_DEVICE, OOM, HIP. */
+int sc_opt_create(sc_handle* out, int n_mats, const int64_t* rows, const int64_t* cols,
+                  sc_dtype w_dtype, sc_dtype g_dtype, const sc_hparams* hp, int device);
+
+/* Free every device allocation of the handle (after synchronizing its device).
+ * NULL is accepted. */
+int sc_opt_destroy(sc_handle h);
+
+/* Anchor arrival ("Key design 2"): for every matrix i,
+ *   M_anc_i <- beta_anc * M_anc_i + (1 - beta_anc) * G_anc[i]
+ * then refresh the thin SVD of M_anc_i (one-sided block Jacobi on the GPU),
+ * the filter d and the projection operands used by sc_step.
+ * G_anc: host array of n_mats device pointers to row-major rows x cols
+ * matrices of g_dtype; read only. */
+int sc_anchor_update(sc_handle h, const void* const* G_anc, void* stream);
+
+/* Recompute SVD, filter and projection operands from the current anchor
+ * momentum without an EMA update (used after sc_set_state of the anchor
+ * momentum; sc_step calls it by itself when the factors are stale). */
+int sc_refresh(sc_handle h, void* stream);
+
+/* One optimizer step ("Key design 3" and AdamW): for every matrix i
+ *   G_filt = U diag(d) (U^T G V) diag(d) V^T,  G_proj = alpha G + (1-alpha) G_filt,
+ *   t <- t + 1; AdamW(W_i, G_proj) in place.
+ * W: host array of n_mats device pointers to row-major w_dtype matrices,
+ * updated in place.  G_mask: host array of n_mats device pointers (g_dtype),
+ * read only. */
+int sc_step(sc_handle h, void* const* W, const void* const* G_mask, void* stream);
+
+/* Change the learning rate used by later steps (e.g. a cosine schedule). */
+int sc_set_lr(sc_handle h, float lr);
+
+/* Change tau_p; d and the projection operands are rebuilt from the cached
+ * singular values before the next step (no new SVD). */
+int sc_set_tau(sc_handle h, float tau_p);
+
+#define SC_STATE_M_ANC 0  /* anchor momentum, rows x cols float32 */
+#define SC_STATE_ADAM_M 1 /* AdamW first moment, rows x cols float32 */
+#define SC_STATE_ADAM_V 2 /* AdamW second moment, rows x cols float32 */
+
+/* Copy one state tensor of matrix idx from/to a caller device buffer of
+ * rows x cols float32 (stream ordered).  Setting the anchor momentum marks
+ * that matrix's factors stale; the next sc_step refreshes them. */
+int sc_set_state(sc_handle h, int idx, int kind, const float* src, void* stream);
+int sc_get_state(sc_handle h, int idx, int kind, float* dst, void* stream);
+
+/* AdamW step count t (number of sc_step calls so far). */
+int sc_set_step(sc_handle h, int64_t t);
+int sc_get_step(sc_handle h, int64_t* t);
+
+/* Install given SVD factors of matrix idx instead of computing them:
+ * U (rows x r), s (r), V (cols x r) device float32 buffers, r = min(rows, cols),
+ * row-major; U and V must have orthonormal columns.  d and the projection
+ * operands are built from them as after a refresh.  For checkpoint restore
+ * and for testing the projection stage on its own. */
+int sc_set_factors(sc_handle h, int idx, const float* U, const float* s, const float* V,
+                   void* stream);
+
+/* Export the current factors of matrix idx (same layout as sc_set_factors).
+ * The singular triplets are in no particular order. */
+int sc_get_factors(sc_handle h, int idx, float* U, float* s, float* V, void* stream);
+
+/* Keep G_proj of each step (costs one more store per element in the AdamW
+ * pass and rows x cols floats per matrix). */
+int sc_keep_proj(sc_handle h, int enable);
+
+/* Copy the last step's G_filt and (if sc_keep_proj was enabled) G_proj of
+ * matrix idx into caller device buffers of rows x cols float32; either may be
+ * NULL. */
+int sc_get_filtered(sc_handle h, int idx, float* G_filt, float* G_proj, void* stream);
+
+typedef struct {
+    int n_mats;
+    int64_t step;          /* AdamW step count t */
+    int refreshes;         /* SVD refreshes done */
+    int sweeps_max;        /* most Jacobi sweeps any matrix needed in the last refresh */
+    int not_converged;     /* matrices that hit max_sweeps in the last refresh */
+    int nonfinite_grad;    /* 1 if a non-finite G_mask value was seen by a step */
+    int nonfinite_anchor;  /* 1 if a non-finite G_anc value was seen by an EMA */
+} sc_stats;
+
+/* Synchronize the handle's work (device-wide) and report counters.
+ * per_mat_sweeps: optional host array of n_mats ints receiving the sweeps of
+ * each matrix in the last refresh. */
+int sc_get_stats(sc_handle h, sc_stats* out, int* per_mat_sweeps);
+
+/* Message of the last error on the calling thread ("" if none). */
+const char* sc_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SCOPT_H */

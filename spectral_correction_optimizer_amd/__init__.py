@@ -1,0 +1,259 @@
+"""Spectral-correction AdamW on AMD MI355X: Python binding of libscopt.
+
+Argument marshalling only: every step of the optimizer runs in the HIP
+kernels of ``libscopt.so`` (C ABI in ``include/scopt.h``).  PyTorch supplies
+device memory and the current HIP stream.  There is no CPU fallback: if the
+library has not been built, importing the binding works but constructing an
+optimizer raises ``ScoptError``.
+
+The method (papernotes.org notes on "Communication-Efficient LLM Adaptation
+over Decentralized GPU Meshes", "Key design 2" and "Key design 3"): per weight
+matrix, an anchor-momentum EMA, a thin SVD of it, the Tikhonov response
+d_i = s_i / (s_i + tau_p), the two-sided projection and reconstruction
+G_filt = U diag(d) (U^T G V) diag(d) V^T, the combination
+G_proj = alpha G + (1 - alpha) G_filt, then AdamW.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first: libscopt then binds to torch's HIP runtime
+
+__all__ = ["SpectralAdamW", "ScoptError", "library_path", "load_library", "EXPORTED_SYMBOLS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libscopt.so")
+_lib = None
+
+EXPORTED_SYMBOLS = (
+    "sc_default_hparams", "sc_opt_create", "sc_opt_destroy", "sc_anchor_update", "sc_refresh",
+    "sc_step", "sc_set_lr", "sc_set_tau", "sc_set_state", "sc_get_state", "sc_set_step",
+    "sc_get_step", "sc_set_factors", "sc_get_factors", "sc_keep_proj", "sc_get_filtered",
+    "sc_get_stats", "sc_last_error",
+)
+
+SC_F32, SC_BF16 = 0, 1
+STATE_KINDS = {"m_anc": 0, "adam_m": 1, "adam_v": 2}
+
+
+class ScoptError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libscopt error {code}: {msg}")
+        self.code = code
+
+
+class HParams(ctypes.Structure):
+    _fields_ = [("tau_p", ctypes.c_float), ("alpha", ctypes.c_float), ("beta_anc", ctypes.c_float),
+                ("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("max_sweeps", ctypes.c_int), ("jacobi_tol", ctypes.c_float),
+                ("sync_check", ctypes.c_int)]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [("n_mats", ctypes.c_int), ("step", ctypes.c_int64), ("refreshes", ctypes.c_int),
+                ("sweeps_max", ctypes.c_int), ("not_converged", ctypes.c_int),
+                ("nonfinite_grad", ctypes.c_int), ("nonfinite_anchor", ctypes.c_int)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libscopt.so (raises ScoptError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ScoptError(-100, f"{_LIB_PATH} is missing; build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)
+    sig = {
+        "sc_default_hparams": (None, [ctypes.POINTER(HParams)]),
+        "sc_opt_create": (ctypes.c_int, [ctypes.POINTER(vp), ctypes.c_int, i64p, i64p, ctypes.c_int,
+                                         ctypes.c_int, ctypes.POINTER(HParams), ctypes.c_int]),
+        "sc_opt_destroy": (ctypes.c_int, [vp]),
+        "sc_anchor_update": (ctypes.c_int, [vp, ctypes.POINTER(vp), vp]),
+        "sc_refresh": (ctypes.c_int, [vp, vp]),
+        "sc_step": (ctypes.c_int, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp]),
+        "sc_set_lr": (ctypes.c_int, [vp, ctypes.c_float]),
+        "sc_set_tau": (ctypes.c_int, [vp, ctypes.c_float]),
+        "sc_set_state": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int, vp, vp]),
+        "sc_get_state": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int, vp, vp]),
+        "sc_set_step": (ctypes.c_int, [vp, ctypes.c_int64]),
+        "sc_get_step": (ctypes.c_int, [vp, i64p]),
+        "sc_set_factors": (ctypes.c_int, [vp, ctypes.c_int, vp, vp, vp, vp]),
+        "sc_get_factors": (ctypes.c_int, [vp, ctypes.c_int, vp, vp, vp, vp]),
+        "sc_keep_proj": (ctypes.c_int, [vp, ctypes.c_int]),
+        "sc_get_filtered": (ctypes.c_int, [vp, ctypes.c_int, vp, vp, vp]),
+        "sc_get_stats": (ctypes.c_int, [vp, ctypes.POINTER(Stats), ctypes.POINTER(ctypes.c_int)]),
+        "sc_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise ScoptError(rc, load_library().sc_last_error().decode())
+
+
+def default_hparams() -> dict:
+    hp = HParams()
+    load_library().sc_default_hparams(ctypes.byref(hp))
+    return {name: getattr(hp, name) for name, _ in HParams._fields_}
+
+
+_DT = {torch.float32: SC_F32, torch.bfloat16: SC_BF16}
+
+
+class SpectralAdamW:
+    """Spectral-correction AdamW over a fixed list of weight-matrix shapes.
+
+    shapes: [(rows, cols), ...] of the row-major weights ([out, in]).
+    w_dtype: torch.float32 or torch.bfloat16 (storage of W); g_dtype: type of
+    G_mask and G_anc.  Keyword hyper-parameters: tau_p, alpha, beta_anc, lr,
+    beta1, beta2, eps, weight_decay, max_sweeps, jacobi_tol, sync_check.
+    """
+
+    def __init__(self, shapes, w_dtype=torch.float32, g_dtype=torch.float32, device=None, **hp):
+        lib = load_library()
+        self.shapes = [(int(r), int(c)) for r, c in shapes]
+        self.n = len(self.shapes)
+        if w_dtype not in _DT or g_dtype not in _DT:
+            raise ValueError("dtypes must be torch.float32 or torch.bfloat16")
+        self.w_dtype, self.g_dtype = w_dtype, g_dtype
+        self.device = torch.device(device if device is not None else "cuda")
+        if self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        h = HParams()
+        lib.sc_default_hparams(ctypes.byref(h))
+        for k, v in hp.items():
+            if not hasattr(h, k):
+                raise TypeError(f"unknown hyper-parameter {k}")
+            setattr(h, k, v)
+        self.hp = {name: getattr(h, name) for name, _ in HParams._fields_}
+        rows = (ctypes.c_int64 * self.n)(*[r for r, _ in self.shapes])
+        cols = (ctypes.c_int64 * self.n)(*[c for _, c in self.shapes])
+        handle = ctypes.c_void_p()
+        _check(lib.sc_opt_create(ctypes.byref(handle), self.n, rows, cols, _DT[w_dtype],
+                                 _DT[g_dtype], ctypes.byref(h), self.device.index))
+        self._h = handle
+        self._lib = lib
+
+    # -- helpers -------------------------------------------------------------------------
+    def _stream(self):
+        return ctypes.c_void_p(torch.cuda.current_stream(self.device).cuda_stream)
+
+    def _ptrs(self, tensors, dtype, what):
+        if len(tensors) != self.n:
+            raise ValueError(f"{what}: expected {self.n} tensors, got {len(tensors)}")
+        arr = (ctypes.c_void_p * self.n)()
+        for i, (t, shp) in enumerate(zip(tensors, self.shapes)):
+            if t.device != self.device or t.dtype != dtype or tuple(t.shape) != shp or \
+                    not t.is_contiguous():
+                raise ValueError(f"{what}[{i}] must be a contiguous {dtype} tensor of shape {shp} "
+                                 f"on {self.device}, got {t.dtype} {tuple(t.shape)} on {t.device}")
+            arr[i] = t.data_ptr()
+        return arr
+
+    def _f32(self, idx, t, shape, what):
+        if t.device != self.device or t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) \
+                or not t.is_contiguous():
+            raise ValueError(f"{what} must be a contiguous float32 tensor of shape {tuple(shape)}")
+        return ctypes.c_void_p(t.data_ptr())
+
+    # -- the method ----------------------------------------------------------------------
+    def anchor_update(self, G_anc):
+        """EMA of the anchor momentum with G_anc, then SVD refresh."""
+        _check(self._lib.sc_anchor_update(self._h, self._ptrs(G_anc, self.g_dtype, "G_anc"),
+                                          self._stream()))
+
+    def refresh(self):
+        _check(self._lib.sc_refresh(self._h, self._stream()))
+
+    def step(self, W, G_mask):
+        """One spectral-corrected AdamW step; W is updated in place."""
+        _check(self._lib.sc_step(self._h, self._ptrs(W, self.w_dtype, "W"),
+                                 self._ptrs(G_mask, self.g_dtype, "G_mask"), self._stream()))
+
+    def set_lr(self, lr: float):
+        _check(self._lib.sc_set_lr(self._h, float(lr)))
+
+    def set_tau(self, tau_p: float):
+        _check(self._lib.sc_set_tau(self._h, float(tau_p)))
+
+    def set_state(self, idx: int, kind: str, src: torch.Tensor):
+        _check(self._lib.sc_set_state(self._h, idx, STATE_KINDS[kind],
+                                      self._f32(idx, src, self.shapes[idx], kind), self._stream()))
+
+    def get_state(self, idx: int, kind: str) -> torch.Tensor:
+        out = torch.empty(self.shapes[idx], dtype=torch.float32, device=self.device)
+        _check(self._lib.sc_get_state(self._h, idx, STATE_KINDS[kind],
+                                      ctypes.c_void_p(out.data_ptr()), self._stream()))
+        return out
+
+    @property
+    def step_count(self) -> int:
+        t = ctypes.c_int64()
+        _check(self._lib.sc_get_step(self._h, ctypes.byref(t)))
+        return t.value
+
+    @step_count.setter
+    def step_count(self, t: int):
+        _check(self._lib.sc_set_step(self._h, int(t)))
+
+    def set_factors(self, idx: int, U: torch.Tensor, s: torch.Tensor, V: torch.Tensor):
+        m, n = self.shapes[idx]
+        r = min(m, n)
+        _check(self._lib.sc_set_factors(self._h, idx, self._f32(idx, U, (m, r), "U"),
+                                        self._f32(idx, s, (r,), "s"), self._f32(idx, V, (n, r), "V"),
+                                        self._stream()))
+
+    def get_factors(self, idx: int):
+        m, n = self.shapes[idx]
+        r = min(m, n)
+        U = torch.empty((m, r), dtype=torch.float32, device=self.device)
+        s = torch.empty((r,), dtype=torch.float32, device=self.device)
+        V = torch.empty((n, r), dtype=torch.float32, device=self.device)
+        _check(self._lib.sc_get_factors(self._h, idx, ctypes.c_void_p(U.data_ptr()),
+                                        ctypes.c_void_p(s.data_ptr()), ctypes.c_void_p(V.data_ptr()),
+                                        self._stream()))
+        return U, s, V
+
+    def keep_proj(self, enable: bool = True):
+        _check(self._lib.sc_keep_proj(self._h, 1 if enable else 0))
+
+    def get_filtered(self, idx: int, proj: bool = False):
+        shp = self.shapes[idx]
+        gf = torch.empty(shp, dtype=torch.float32, device=self.device)
+        gp = torch.empty(shp, dtype=torch.float32, device=self.device) if proj else None
+        _check(self._lib.sc_get_filtered(self._h, idx, ctypes.c_void_p(gf.data_ptr()),
+                                         ctypes.c_void_p(gp.data_ptr() if gp is not None else None),
+                                         self._stream()))
+        return (gf, gp) if proj else gf
+
+    def stats(self):
+        st = Stats()
+        per = (ctypes.c_int * self.n)()
+        _check(self._lib.sc_get_stats(self._h, ctypes.byref(st), per))
+        d = {name: getattr(st, name) for name, _ in Stats._fields_}
+        d["sweeps"] = list(per)
+        return d
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.sc_opt_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,798 @@
+// Host side of libscopt: the C ABI declared in include/scopt.h.
+//
+// Argument validation, device-state allocation (one arena per handle), work
+// lists and grouped-GEMM problem tables (built once at create), and the
+// stream-ordered launch sequences of the anchor update (EMA + SVD refresh)
+// and of the optimizer step.  Method: papernotes.org notes on
+// "Communication-Efficient LLM Adaptation over Decentralized GPU Meshes",
+// "Key design 2" (anchor EMA) and "Key design 3" (SVD, Tikhonov filter,
+// two-sided projection, combination), followed by AdamW.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "internal.hpp"
+#include "scopt.h"
+
+using namespace scopt;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+#define HIP_TRY(expr)                                                                      \
+    do {                                                                                   \
+        hipError_t e_ = (expr);                                                            \
+        if (e_ != hipSuccess)                                                              \
+            return fail(SC_ERR_HIP, "%s failed: %s (%s:%d)", #expr, hipGetErrorString(e_), \
+                        __FILE__, __LINE__);                                               \
+    } while (0)
+
+constexpr int64_t kMaxDim = 65536;
+constexpr int kChunk = 16384;  // elements per elementwise workgroup
+constexpr float kDefaultTol = 16.0f * 5.9604644775390625e-08f;
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) == hipSuccess && hipSetDevice(dev) == hipSuccess) ok = true;
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+struct GemmGroup {
+    std::vector<GemmProb> h;
+    GemmProb* d = nullptr;
+    int total = 0;
+    bool ta = false, tb = false, abf = false, bbf = false;
+};
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int round_up(int x, int a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+struct sc_opt {
+    int device = 0;
+    int n = 0;
+    sc_dtype wdt = SC_F32, gdt = SC_F32;
+    sc_hparams hp{};
+    float tol = kDefaultTol;
+    std::vector<MatDev> mh;
+    MatDev* md = nullptr;
+    MatFlags* flags_d = nullptr;
+    MatFlags* flags_h = nullptr;  // pinned
+    int* status_d = nullptr;      // [0] non-finite G_mask, [1] non-finite G_anc
+    char* arena = nullptr;
+    char* proj_arena = nullptr;
+    Chunk* chunks_d = nullptr;
+    int nchunks = 0;
+    GramItem* gi_d = nullptr;
+    int ngi = 0;
+    SolveItem* si_d = nullptr;
+    int nsi = 0;
+    ApplyItem* ai_d = nullptr;
+    int nai = 0;
+    int max_nb = 2, max_kpad = 64, max_K = 1, max_k = 1;
+    // refresh GEMMs
+    GemmGroup lowdin_eF, lowdin_F, lowdin_eW, lowdin_W, proj;
+    // step GEMMs
+    GemmGroup s1_nn_a, s1_nn_b, s1_nt, s2_nn, s3_tn, s3_nn;
+    int64_t t = 0;
+    int refreshes = 0;
+    std::vector<char> stale;
+    bool any_stale = false;
+    bool proj_stale = false;
+    bool keep_proj = false;
+    std::vector<int> last_sweeps;
+    int last_not_conv = 0;
+    std::vector<void*> dev_allocs;
+};
+
+namespace {
+
+int upload_group(sc_opt* h, GemmGroup& g) {
+    int start = 0;
+    for (auto& p : g.h) {
+        int tm = (p.M + kGemmBM - 1) / kGemmBM;
+        p.tiles_n = (p.N + kGemmBN - 1) / kGemmBN;
+        p.tile_start = start;
+        start += tm * p.tiles_n;
+    }
+    g.total = start;
+    if (g.h.empty()) return SC_OK;
+    void* d = nullptr;
+    HIP_TRY(hipMalloc(&d, sizeof(GemmProb) * g.h.size()));
+    h->dev_allocs.push_back(d);
+    g.d = (GemmProb*)d;
+    HIP_TRY(hipMemcpy(g.d, g.h.data(), sizeof(GemmProb) * g.h.size(), hipMemcpyHostToDevice));
+    return SC_OK;
+}
+
+GemmProb make_prob(const void* A, int lda, const void* B, int ldb, float* C, int ldc, int M, int N,
+                   int K) {
+    GemmProb p;
+    memset(&p, 0, sizeof(p));
+    p.A = A;
+    p.B = B;
+    p.C = C;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.alpha = 1.0f;
+    p.beta = 0.0f;
+    p.a_ptr = -1;
+    p.b_ptr = -1;
+    return p;
+}
+
+int run_group(const GemmGroup& g, const PtrTable& pt, hipStream_t st) {
+    if (g.h.empty()) return SC_OK;
+    HIP_TRY(launch_gemm(g.d, (int)g.h.size(), g.total, g.ta, g.tb, g.abf, g.bbf, pt, st));
+    return SC_OK;
+}
+
+int check_hp(const sc_hparams* hp) {
+    if (!hp) return fail(SC_ERR_INVALID_ARG, "hparams is NULL");
+    if (!(hp->tau_p >= 0.0f) || !std::isfinite(hp->tau_p))
+        return fail(SC_ERR_INVALID_ARG, "tau_p must be finite and >= 0");
+    if (!(hp->alpha >= 0.0f && hp->alpha <= 1.0f))
+        return fail(SC_ERR_INVALID_ARG, "alpha must be in [0, 1]");
+    if (!(hp->beta_anc >= 0.0f && hp->beta_anc <= 1.0f))
+        return fail(SC_ERR_INVALID_ARG, "beta_anc must be in [0, 1]");
+    if (!(hp->lr >= 0.0f) || !std::isfinite(hp->lr))
+        return fail(SC_ERR_INVALID_ARG, "lr must be finite and >= 0");
+    if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) || !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+        return fail(SC_ERR_INVALID_ARG, "beta1 and beta2 must be in [0, 1)");
+    if (!(hp->eps > 0.0f) || !std::isfinite(hp->eps))
+        return fail(SC_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (!(hp->weight_decay >= 0.0f) || !std::isfinite(hp->weight_decay))
+        return fail(SC_ERR_INVALID_ARG, "weight_decay must be finite and >= 0");
+    if (hp->max_sweeps < 1 || hp->max_sweeps > 1000)
+        return fail(SC_ERR_INVALID_ARG, "max_sweeps must be in [1, 1000]");
+    if (!(hp->jacobi_tol >= 0.0f && hp->jacobi_tol < 1.0f))
+        return fail(SC_ERR_INVALID_ARG, "jacobi_tol must be in [0, 1)");
+    return SC_OK;
+}
+
+int check_ptrs(const sc_opt* h, const void* const* p, sc_dtype dt, const char* what) {
+    if (!p) return fail(SC_ERR_INVALID_ARG, "%s pointer array is NULL", what);
+    const uintptr_t mask = dt == SC_F32 ? 15 : 7;
+    for (int i = 0; i < h->n; ++i) {
+        if (!p[i]) return fail(SC_ERR_INVALID_ARG, "%s[%d] is NULL", what, i);
+        if ((uintptr_t)p[i] & mask)
+            return fail(SC_ERR_INVALID_ARG, "%s[%d] is not %d-byte aligned", what, i,
+                        (int)(mask + 1));
+    }
+    return SC_OK;
+}
+
+PtrTable make_table(const sc_opt* h, const void* const* p) {
+    PtrTable t;
+    memset(&t, 0, sizeof(t));
+    if (p)
+        for (int i = 0; i < h->n; ++i) t.p[i] = p[i];
+    return t;
+}
+
+// ---- refresh ------------------------------------------------------------------------
+
+int build_projectors(sc_opt* h, hipStream_t st) {
+    HIP_TRY(launch_filter(h->md, h->n, h->hp.tau_p, h->max_kpad, st));
+    PtrTable none = make_table(h, nullptr);
+    int rc = run_group(h->proj, none, st);
+    if (rc) return rc;
+    h->proj_stale = false;
+    return SC_OK;
+}
+
+int finalize_factors(sc_opt* h, hipStream_t st) {
+    PtrTable none = make_table(h, nullptr);
+    HIP_TRY(launch_rownorm(h->md, h->n, 0, h->max_kpad, st));
+    HIP_TRY(launch_normalize(h->md, h->flags_d, h->n, 0, h->max_kpad, h->max_K, st));
+    HIP_TRY(launch_rownorm(h->md, h->n, 1, h->max_kpad, st));
+    HIP_TRY(launch_normalize(h->md, h->flags_d, h->n, 1, h->max_kpad, h->max_K, st));
+    int rc;
+    if ((rc = run_group(h->lowdin_eF, none, st))) return rc;
+    if ((rc = run_group(h->lowdin_F, none, st))) return rc;
+    if ((rc = run_group(h->lowdin_eW, none, st))) return rc;
+    if ((rc = run_group(h->lowdin_W, none, st))) return rc;
+    return build_projectors(h, st);
+}
+
+int do_refresh(sc_opt* h, hipStream_t st) {
+    HIP_TRY(launch_jacobi_load(h->md, h->n, h->max_kpad, h->max_K + 128, st));
+    HIP_TRY(launch_rownorm(h->md, h->n, 0, h->max_kpad, st));
+    HIP_TRY(launch_jacobi_init_flags(h->md, h->flags_d, h->n, st));
+    const int rps = h->max_nb - 1;  // rounds per sweep of the largest matrix
+    const int max_rounds = h->hp.max_sweeps * rps;
+    const int first_check = std::min(max_rounds, 4 * rps);
+    for (int r = 0; r < max_rounds; ++r) {
+        HIP_TRY(launch_jacobi_round(h->md, h->flags_d, h->gi_d, h->ngi, h->si_d, h->nsi, h->ai_d,
+                                    h->nai, r, h->hp.max_sweeps, h->tol, h->n, st));
+        if (h->hp.sync_check && r + 1 >= first_check && (r + 1) % rps == 0 && r + 1 < max_rounds) {
+            HIP_TRY(hipMemcpyAsync(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n,
+                                   hipMemcpyDeviceToHost, st));
+            HIP_TRY(hipStreamSynchronize(st));
+            bool all = true;
+            for (int i = 0; i < h->n; ++i) all = all && h->flags_h[i].done;
+            if (all) break;
+        }
+    }
+    int rc = finalize_factors(h, st);
+    if (rc) return rc;
+    h->refreshes += 1;
+    for (auto& s : h->stale) s = 0;
+    h->any_stale = false;
+    return SC_OK;
+}
+
+// ---- construction -------------------------------------------------------------------------
+
+int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
+    const int n = h->n;
+    h->mh.resize(n);
+    // layout pass: sizes of every buffer, carved from one arena
+    std::vector<size_t> off;
+    size_t total = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = total;
+        total += align_up(bytes ? bytes : 1, 256);
+        return o;
+    };
+    struct Offs {
+        size_t Manc, madam, vadam, A, V, F, W, PL, PR, s, d, norm2, Gfilt, Y, T, E, gram, rot, rflag;
+    };
+    std::vector<Offs> o(n);
+    for (int i = 0; i < n; ++i) {
+        MatDev& m = h->mh[i];
+        memset(&m, 0, sizeof(m));
+        m.m = (int)rows[i];
+        m.n = (int)cols[i];
+        m.tall = m.m >= m.n;
+        m.K = std::max(m.m, m.n);
+        m.k = std::min(m.m, m.n);
+        m.kpad = round_up(m.k, kPw);
+        m.K_ld = round_up(m.K, 128);
+        m.nb = m.kpad / kJb;
+        m.numel = (int64_t)m.m * m.n;
+        int L = round_up((m.K_ld + 7) / 8, 256);
+        if (L < 256) L = 256;
+        m.ksplit_len = L;
+        m.nsplit = (m.K_ld + L - 1) / L;
+        const size_t f = sizeof(float);
+        const size_t mn = (size_t)m.numel * f;
+        const size_t kk = (size_t)m.k * m.k * f;
+        o[i].Manc = take(mn);
+        o[i].madam = take(mn);
+        o[i].vadam = take(mn);
+        o[i].A = take((size_t)m.kpad * m.K_ld * f);
+        o[i].V = take((size_t)m.kpad * m.kpad * f);
+        o[i].F = take((size_t)m.k * m.K_ld * f);
+        o[i].W = take(kk);
+        o[i].PL = take(m.m <= m.n ? (size_t)m.m * m.m * f : 0);
+        o[i].PR = take(m.m >= m.n ? (size_t)m.n * m.n * f : 0);
+        o[i].s = take((size_t)m.kpad * f);
+        o[i].d = take((size_t)m.kpad * f);
+        o[i].norm2 = take((size_t)m.kpad * sizeof(double));
+        o[i].Gfilt = take(mn);
+        o[i].Y = take(kk);
+        o[i].T = take(kk);
+        o[i].E = take(kk);
+        o[i].gram = take((size_t)(m.nb / 2) * m.nsplit * kPw * kPw * sizeof(double));
+        o[i].rot = take((size_t)(m.nb / 2) * kPw * kPw * f);
+        o[i].rflag = take((size_t)(m.nb / 2) * sizeof(int));
+        h->max_nb = std::max(h->max_nb, m.nb);
+        h->max_kpad = std::max(h->max_kpad, m.kpad);
+        h->max_K = std::max(h->max_K, m.K_ld);
+        h->max_k = std::max(h->max_k, m.k);
+    }
+    void* arena = nullptr;
+    if (hipMalloc(&arena, total) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SC_ERR_OOM, "device allocation of %zu bytes failed", total);
+    }
+    h->arena = (char*)arena;
+    // Zero everything: anchor momentum, moments and factors start at zero, so
+    // until the first refresh d = 0 and G_filt = 0.
+    HIP_TRY(hipMemset(h->arena, 0, total));
+    for (int i = 0; i < n; ++i) {
+        MatDev& m = h->mh[i];
+        char* b = h->arena;
+        m.Manc = (float*)(b + o[i].Manc);
+        m.madam = (float*)(b + o[i].madam);
+        m.vadam = (float*)(b + o[i].vadam);
+        m.A = (float*)(b + o[i].A);
+        m.V = (float*)(b + o[i].V);
+        m.F = (float*)(b + o[i].F);
+        m.W = (float*)(b + o[i].W);
+        m.PL = m.m <= m.n ? (float*)(b + o[i].PL) : nullptr;
+        m.PR = m.m >= m.n ? (float*)(b + o[i].PR) : nullptr;
+        m.s = (float*)(b + o[i].s);
+        m.d = (float*)(b + o[i].d);
+        m.norm2 = (double*)(b + o[i].norm2);
+        m.Gfilt = (float*)(b + o[i].Gfilt);
+        m.Gproj = nullptr;
+        m.Y = (float*)(b + o[i].Y);
+        m.T = (float*)(b + o[i].T);
+        m.E = (float*)(b + o[i].E);
+        m.gram = (double*)(b + o[i].gram);
+        m.rot = (float*)(b + o[i].rot);
+        m.rot_flag = (int*)(b + o[i].rflag);
+    }
+    void* p = nullptr;
+    HIP_TRY(hipMalloc(&p, sizeof(MatDev) * n));
+    h->dev_allocs.push_back(p);
+    h->md = (MatDev*)p;
+    HIP_TRY(hipMemcpy(h->md, h->mh.data(), sizeof(MatDev) * n, hipMemcpyHostToDevice));
+    HIP_TRY(hipMalloc(&p, sizeof(MatFlags) * n));
+    h->dev_allocs.push_back(p);
+    h->flags_d = (MatFlags*)p;
+    HIP_TRY(hipMemset(h->flags_d, 0, sizeof(MatFlags) * n));
+    HIP_TRY(hipHostMalloc(&p, sizeof(MatFlags) * n, hipHostMallocDefault));
+    h->flags_h = (MatFlags*)p;
+    memset(h->flags_h, 0, sizeof(MatFlags) * n);
+    HIP_TRY(hipMalloc(&p, 4 * sizeof(int)));
+    h->dev_allocs.push_back(p);
+    h->status_d = (int*)p;
+    HIP_TRY(hipMemset(h->status_d, 0, 4 * sizeof(int)));
+
+    // work lists
+    std::vector<Chunk> ch;
+    std::vector<GramItem> gi;
+    std::vector<SolveItem> si;
+    std::vector<ApplyItem> ai;
+    for (int i = 0; i < n; ++i) {
+        const MatDev& m = h->mh[i];
+        for (int64_t off0 = 0; off0 < m.numel; off0 += kChunk)
+            ch.push_back(Chunk{i, off0, (int)std::min<int64_t>(kChunk, m.numel - off0)});
+        for (int s = 0; s < m.nb / 2; ++s) {
+            for (int sp = 0; sp < m.nsplit; ++sp) gi.push_back(GramItem{i, s, sp});
+            si.push_back(SolveItem{i, s});
+            for (int c = 0; c < m.K_ld / 128; ++c) ai.push_back(ApplyItem{i, s, 0, c});
+            for (int c = 0; c < (m.kpad + 127) / 128; ++c) ai.push_back(ApplyItem{i, s, 1, c});
+        }
+    }
+    auto upload = [&](auto& vec, auto** dst, int* cnt) -> int {
+        *cnt = (int)vec.size();
+        void* q = nullptr;
+        HIP_TRY(hipMalloc(&q, sizeof(vec[0]) * std::max<size_t>(vec.size(), 1)));
+        h->dev_allocs.push_back(q);
+        *dst = (typename std::remove_reference<decltype(**dst)>::type*)q;
+        if (!vec.empty())
+            HIP_TRY(hipMemcpy(q, vec.data(), sizeof(vec[0]) * vec.size(), hipMemcpyHostToDevice));
+        return SC_OK;
+    };
+    int rc;
+    if ((rc = upload(ch, &h->chunks_d, &h->nchunks))) return rc;
+    if ((rc = upload(gi, &h->gi_d, &h->ngi))) return rc;
+    if ((rc = upload(si, &h->si_d, &h->nsi))) return rc;
+    if ((rc = upload(ai, &h->ai_d, &h->nai))) return rc;
+
+    // GEMM problem tables
+    const bool gbf = h->gdt == SC_BF16;
+    h->lowdin_eF.tb = true;
+    h->lowdin_eW.tb = true;
+    h->proj.ta = true;
+    h->s1_nn_a.abf = gbf;  // square: A = G
+    h->s1_nn_b.bbf = gbf;  // tall: B = G
+    h->s1_nt.tb = true;    // wide: A = G, B = F^T
+    h->s1_nt.abf = gbf;
+    h->s3_tn.ta = true;
+    for (int i = 0; i < n; ++i) {
+        MatDev& m = h->mh[i];
+        // Loewdin re-orthogonalization of the unit rows of A (-> F) and V (-> W):
+        //   E = X X^T with zero diagonal;  X_out = X - 0.5 E X
+        GemmProb p = make_prob(m.A, m.K_ld, m.A, m.K_ld, m.E, m.k, m.k, m.k, m.K_ld);
+        p.flags = GF_ZERO_DIAG;
+        h->lowdin_eF.h.push_back(p);
+        p = make_prob(m.E, m.k, m.A, m.K_ld, m.F, m.K_ld, m.k, m.K_ld, m.k);
+        p.Cin = m.A;
+        p.ldcin = m.K_ld;
+        p.alpha = -0.5f;
+        p.beta = 1.0f;
+        h->lowdin_F.h.push_back(p);
+        p = make_prob(m.V, m.kpad, m.V, m.kpad, m.E, m.k, m.k, m.k, m.k);
+        p.flags = GF_ZERO_DIAG;
+        h->lowdin_eW.h.push_back(p);
+        p = make_prob(m.E, m.k, m.V, m.kpad, m.W, m.k, m.k, m.k, m.k);
+        p.Cin = m.V;
+        p.ldcin = m.kpad;
+        p.alpha = -0.5f;
+        p.beta = 1.0f;
+        h->lowdin_W.h.push_back(p);
+        // projectors X^T diag(d) X
+        const bool square = m.m == m.n;
+        if (square) {
+            p = make_prob(m.F, m.K_ld, m.F, m.K_ld, m.PL, m.m, m.m, m.m, m.k);
+            p.k_scale = m.d;
+            h->proj.h.push_back(p);
+        }
+        p = make_prob(m.W, m.k, m.W, m.k, m.tall ? m.PR : m.PL, m.k, m.k, m.k, m.k);
+        p.k_scale = m.d;
+        h->proj.h.push_back(p);
+        // step chain
+        if (square) {
+            p = make_prob(nullptr, m.n, m.PR, m.n, m.T, m.n, m.m, m.n, m.n);  // T = G P_R
+            p.a_ptr = i;
+            h->s1_nn_a.h.push_back(p);
+            p = make_prob(m.PL, m.m, m.T, m.n, m.Gfilt, m.n, m.m, m.n, m.m);  // G_filt = P_L T
+            h->s2_nn.h.push_back(p);
+        } else if (m.tall) {
+            p = make_prob(m.F, m.K_ld, nullptr, m.n, m.Y, m.k, m.k, m.n, m.m);  // Y = D F G
+            p.b_ptr = i;
+            p.row_scale = m.d;
+            h->s1_nn_b.h.push_back(p);
+            p = make_prob(m.Y, m.k, m.PR, m.n, m.T, m.k, m.k, m.n, m.n);  // T = Y P_R
+            h->s2_nn.h.push_back(p);
+            p = make_prob(m.F, m.K_ld, m.T, m.k, m.Gfilt, m.n, m.m, m.n, m.k);  // G_filt = F^T T
+            h->s3_tn.h.push_back(p);
+        } else {
+            p = make_prob(nullptr, m.n, m.F, m.K_ld, m.Y, m.k, m.m, m.k, m.n);  // Y = G F^T D
+            p.a_ptr = i;
+            p.col_scale = m.d;
+            h->s1_nt.h.push_back(p);
+            p = make_prob(m.PL, m.m, m.Y, m.k, m.T, m.k, m.m, m.k, m.m);  // T = P_L Y
+            h->s2_nn.h.push_back(p);
+            p = make_prob(m.T, m.k, m.F, m.K_ld, m.Gfilt, m.n, m.m, m.n, m.k);  // G_filt = T F
+            h->s3_nn.h.push_back(p);
+        }
+    }
+    for (GemmGroup* g : {&h->lowdin_eF, &h->lowdin_F, &h->lowdin_eW, &h->lowdin_W, &h->proj,
+                         &h->s1_nn_a, &h->s1_nn_b, &h->s1_nt, &h->s2_nn, &h->s3_tn, &h->s3_nn})
+        if ((rc = upload_group(h, *g))) return rc;
+    h->stale.assign(n, 0);
+    h->last_sweeps.assign(n, 0);
+    HIP_TRY(hipDeviceSynchronize());
+    return SC_OK;
+}
+
+void release(sc_opt* h) {
+    if (!h) return;
+    DeviceGuard g(h->device);
+    (void)hipDeviceSynchronize();
+    for (void* p : h->dev_allocs) (void)hipFree(p);
+    if (h->arena) (void)hipFree(h->arena);
+    if (h->proj_arena) (void)hipFree(h->proj_arena);
+    if (h->flags_h) (void)hipHostFree(h->flags_h);
+    delete h;
+}
+
+int check_handle(sc_opt* h) {
+    if (!h) return fail(SC_ERR_INVALID_ARG, "handle is NULL");
+    return SC_OK;
+}
+
+int check_idx(sc_opt* h, int idx) {
+    if (idx < 0 || idx >= h->n) return fail(SC_ERR_INVALID_ARG, "matrix index %d out of range", idx);
+    return SC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void sc_default_hparams(sc_hparams* hp) {
+    if (!hp) return;
+    hp->tau_p = 1e-3f;
+    hp->alpha = 0.3f;
+    hp->beta_anc = 0.9f;
+    hp->lr = 2e-5f;
+    hp->beta1 = 0.9f;
+    hp->beta2 = 0.999f;
+    hp->eps = 1e-8f;
+    hp->weight_decay = 0.01f;
+    hp->max_sweeps = 30;
+    hp->jacobi_tol = 0.0f;
+    hp->sync_check = 1;
+}
+
+const char* sc_last_error(void) { return g_err.c_str(); }
+
+int sc_opt_create(sc_handle* out, int n_mats, const int64_t* rows, const int64_t* cols,
+                  sc_dtype w_dtype, sc_dtype g_dtype, const sc_hparams* hp, int device) {
+    g_err.clear();
+    if (!out) return fail(SC_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (n_mats < 1 || n_mats > kMaxPtrs)
+        return fail(SC_ERR_INVALID_ARG, "n_mats must be in [1, %d]", kMaxPtrs);
+    if (!rows || !cols) return fail(SC_ERR_INVALID_ARG, "rows/cols is NULL");
+    for (int i = 0; i < n_mats; ++i)
+        if (rows[i] < 1 || cols[i] < 1 || rows[i] > kMaxDim || cols[i] > kMaxDim)
+            return fail(SC_ERR_SHAPE, "matrix %d has shape %lld x %lld (allowed 1..%lld)", i,
+                        (long long)rows[i], (long long)cols[i], (long long)kMaxDim);
+    if ((w_dtype != SC_F32 && w_dtype != SC_BF16) || (g_dtype != SC_F32 && g_dtype != SC_BF16))
+        return fail(SC_ERR_INVALID_ARG, "unknown dtype");
+    int rc = check_hp(hp);
+    if (rc) return rc;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+        (void)hipGetLastError();
+        return fail(SC_ERR_NO_DEVICE, "no HIP device");
+    }
+    if (device < 0 || device >= ndev)
+        return fail(SC_ERR_NO_DEVICE, "device %d out of range (%d devices)", device, ndev);
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess)
+        return fail(SC_ERR_NO_DEVICE, "cannot query device %d", device);
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(SC_ERR_NO_DEVICE, "device %d is %s; libscopt is built for gfx950", device,
+                    prop.gcnArchName);
+    DeviceGuard guard(device);
+    if (!guard.ok) return fail(SC_ERR_NO_DEVICE, "cannot select device %d", device);
+    sc_opt* h = new (std::nothrow) sc_opt();
+    if (!h) return fail(SC_ERR_OOM, "host allocation failed");
+    h->device = device;
+    h->n = n_mats;
+    h->wdt = w_dtype;
+    h->gdt = g_dtype;
+    h->hp = *hp;
+    h->tol = hp->jacobi_tol > 0.0f ? hp->jacobi_tol : kDefaultTol;
+    rc = build(h, rows, cols);
+    if (rc) {
+        std::string msg = g_err;
+        release(h);
+        g_err = msg;
+        return rc;
+    }
+    *out = h;
+    return SC_OK;
+}
+
+int sc_opt_destroy(sc_handle h) {
+    release(h);
+    return SC_OK;
+}
+
+int sc_anchor_update(sc_handle h, const void* const* G_anc, void* stream) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    if ((rc = check_ptrs(h, G_anc, h->gdt, "G_anc"))) return rc;
+    DeviceGuard g(h->device);
+    hipStream_t st = (hipStream_t)stream;
+    PtrTable pt = make_table(h, G_anc);
+    HIP_TRY(launch_ema(h->md, h->chunks_d, h->nchunks, pt, h->gdt == SC_BF16, h->hp.beta_anc,
+                       h->status_d + 1, st));
+    return do_refresh(h, st);
+}
+
+int sc_refresh(sc_handle h, void* stream) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    DeviceGuard g(h->device);
+    return do_refresh(h, (hipStream_t)stream);
+}
+
+int sc_step(sc_handle h, void* const* W, const void* const* G_mask, void* stream) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    if ((rc = check_ptrs(h, (const void* const*)W, h->wdt, "W"))) return rc;
+    if ((rc = check_ptrs(h, G_mask, h->gdt, "G_mask"))) return rc;
+    DeviceGuard g(h->device);
+    hipStream_t st = (hipStream_t)stream;
+    if (h->any_stale) {
+        if ((rc = do_refresh(h, st))) return rc;
+    }
+    if (h->proj_stale) {
+        if ((rc = build_projectors(h, st))) return rc;
+    }
+    PtrTable gt = make_table(h, G_mask);
+    PtrTable wt = make_table(h, (const void* const*)W);
+    if ((rc = run_group(h->s1_nn_a, gt, st))) return rc;
+    if ((rc = run_group(h->s1_nn_b, gt, st))) return rc;
+    if ((rc = run_group(h->s1_nt, gt, st))) return rc;
+    if ((rc = run_group(h->s2_nn, gt, st))) return rc;
+    if ((rc = run_group(h->s3_tn, gt, st))) return rc;
+    if ((rc = run_group(h->s3_nn, gt, st))) return rc;
+    const int64_t t = h->t + 1;
+    const double lr = h->hp.lr, b1 = h->hp.beta1, b2 = h->hp.beta2;
+    const double bc1 = 1.0 - std::pow(b1, (double)t);
+    const double bc2 = 1.0 - std::pow(b2, (double)t);
+    const float step_size = (float)(lr / bc1);
+    const float inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+    const float lr_wd = (float)(lr * (double)h->hp.weight_decay);
+    HIP_TRY(launch_combine_adamw(h->md, h->chunks_d, h->nchunks, wt, gt, h->wdt == SC_BF16,
+                                 h->gdt == SC_BF16, h->hp.alpha, h->hp.beta1, h->hp.beta2,
+                                 h->hp.eps, step_size, inv_sqrt_bc2, lr_wd, h->keep_proj ? 1 : 0,
+                                 h->status_d, st));
+    h->t = t;
+    return SC_OK;
+}
+
+int sc_set_lr(sc_handle h, float lr) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    if (!(lr >= 0.0f) || !std::isfinite(lr)) return fail(SC_ERR_INVALID_ARG, "lr must be >= 0");
+    h->hp.lr = lr;
+    return SC_OK;
+}
+
+int sc_set_tau(sc_handle h, float tau_p) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    if (!(tau_p >= 0.0f) || !std::isfinite(tau_p))
+        return fail(SC_ERR_INVALID_ARG, "tau_p must be finite and >= 0");
+    h->hp.tau_p = tau_p;
+    h->proj_stale = true;
+    return SC_OK;
+}
+
+int sc_set_state(sc_handle h, int idx, int kind, const float* src, void* stream) {
+    int rc;
+    if ((rc = check_handle(h)) || (rc = check_idx(h, idx))) return rc;
+    if (!src) return fail(SC_ERR_INVALID_ARG, "src is NULL");
+    const MatDev& m = h->mh[idx];
+    float* dst = kind == SC_STATE_M_ANC ? m.Manc
+                 : kind == SC_STATE_ADAM_M ? m.madam
+                 : kind == SC_STATE_ADAM_V ? m.vadam
+                                           : nullptr;
+    if (!dst) return fail(SC_ERR_INVALID_ARG, "unknown state kind %d", kind);
+    DeviceGuard g(h->device);
+    HIP_TRY(hipMemcpyAsync(dst, src, sizeof(float) * m.numel, hipMemcpyDeviceToDevice,
+                           (hipStream_t)stream));
+    if (kind == SC_STATE_M_ANC) {
+        h->stale[idx] = 1;
+        h->any_stale = true;
+    }
+    return SC_OK;
+}
+
+int sc_get_state(sc_handle h, int idx, int kind, float* dst, void* stream) {
+    int rc;
+    if ((rc = check_handle(h)) || (rc = check_idx(h, idx))) return rc;
+    if (!dst) return fail(SC_ERR_INVALID_ARG, "dst is NULL");
+    const MatDev& m = h->mh[idx];
+    const float* src = kind == SC_STATE_M_ANC ? m.Manc
+                       : kind == SC_STATE_ADAM_M ? m.madam
+                       : kind == SC_STATE_ADAM_V ? m.vadam
+                                                 : nullptr;
+    if (!src) return fail(SC_ERR_INVALID_ARG, "unknown state kind %d", kind);
+    DeviceGuard g(h->device);
+    HIP_TRY(hipMemcpyAsync(dst, src, sizeof(float) * m.numel, hipMemcpyDeviceToDevice,
+                           (hipStream_t)stream));
+    return SC_OK;
+}
+
+int sc_set_step(sc_handle h, int64_t t) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    if (t < 0) return fail(SC_ERR_INVALID_ARG, "step count must be >= 0");
+    h->t = t;
+    return SC_OK;
+}
+
+int sc_get_step(sc_handle h, int64_t* t) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    if (!t) return fail(SC_ERR_INVALID_ARG, "t is NULL");
+    *t = h->t;
+    return SC_OK;
+}
+
+int sc_set_factors(sc_handle h, int idx, const float* U, const float* s, const float* V,
+                   void* stream) {
+    int rc;
+    if ((rc = check_handle(h)) || (rc = check_idx(h, idx))) return rc;
+    if (!U || !s || !V) return fail(SC_ERR_INVALID_ARG, "U, s and V must be non-NULL");
+    const MatDev& m = h->mh[idx];
+    DeviceGuard g(h->device);
+    hipStream_t st = (hipStream_t)stream;
+    // A-side (rows of F, length K): U for m >= n, V for m < n; the other side -> W.
+    const float* fa = m.tall ? U : V;
+    const float* wa = m.tall ? V : U;
+    const int frows = m.tall ? m.m : m.n;  // K
+    const int wrows = m.tall ? m.n : m.m;  // k
+    HIP_TRY(hipMemsetAsync(m.F, 0, sizeof(float) * (size_t)m.k * m.K_ld, st));
+    HIP_TRY(launch_transpose(fa, frows, m.k, m.k, m.F, m.K_ld, st));
+    HIP_TRY(launch_transpose(wa, wrows, m.k, m.k, m.W, m.k, st));
+    HIP_TRY(hipMemsetAsync(m.s, 0, sizeof(float) * m.kpad, st));
+    HIP_TRY(hipMemcpyAsync(m.s, s, sizeof(float) * m.k, hipMemcpyDeviceToDevice, st));
+    h->stale[idx] = 0;
+    h->any_stale = false;
+    for (char c : h->stale) h->any_stale = h->any_stale || c;
+    return build_projectors(h, st);
+}
+
+int sc_get_factors(sc_handle h, int idx, float* U, float* s, float* V, void* stream) {
+    int rc;
+    if ((rc = check_handle(h)) || (rc = check_idx(h, idx))) return rc;
+    const MatDev& m = h->mh[idx];
+    DeviceGuard g(h->device);
+    hipStream_t st = (hipStream_t)stream;
+    float* fa = m.tall ? U : V;
+    float* wa = m.tall ? V : U;
+    if (fa) HIP_TRY(launch_transpose(m.F, m.k, m.tall ? m.m : m.n, m.K_ld, fa, m.k, st));
+    if (wa) HIP_TRY(launch_transpose(m.W, m.k, m.k, m.k, wa, m.k, st));
+    if (s) HIP_TRY(hipMemcpyAsync(s, m.s, sizeof(float) * m.k, hipMemcpyDeviceToDevice, st));
+    return SC_OK;
+}
+
+int sc_keep_proj(sc_handle h, int enable) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    DeviceGuard g(h->device);
+    if (enable && !h->proj_arena) {
+        size_t total = 0;
+        std::vector<size_t> offs(h->n);
+        for (int i = 0; i < h->n; ++i) {
+            offs[i] = total;
+            total += align_up((size_t)h->mh[i].numel * sizeof(float), 256);
+        }
+        void* p = nullptr;
+        if (hipMalloc(&p, total) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(SC_ERR_OOM, "device allocation of %zu bytes failed", total);
+        }
+        h->proj_arena = (char*)p;
+        HIP_TRY(hipMemset(p, 0, total));
+        for (int i = 0; i < h->n; ++i) h->mh[i].Gproj = (float*)(h->proj_arena + offs[i]);
+        HIP_TRY(hipMemcpy(h->md, h->mh.data(), sizeof(MatDev) * h->n, hipMemcpyHostToDevice));
+    }
+    h->keep_proj = enable && h->proj_arena;
+    return SC_OK;
+}
+
+int sc_get_filtered(sc_handle h, int idx, float* G_filt, float* G_proj, void* stream) {
+    int rc;
+    if ((rc = check_handle(h)) || (rc = check_idx(h, idx))) return rc;
+    const MatDev& m = h->mh[idx];
+    if (G_proj && !m.Gproj) return fail(SC_ERR_INVALID_ARG, "G_proj is not kept (sc_keep_proj)");
+    DeviceGuard g(h->device);
+    hipStream_t st = (hipStream_t)stream;
+    if (G_filt)
+        HIP_TRY(hipMemcpyAsync(G_filt, m.Gfilt, sizeof(float) * m.numel, hipMemcpyDeviceToDevice,
+                               st));
+    if (G_proj)
+        HIP_TRY(hipMemcpyAsync(G_proj, m.Gproj, sizeof(float) * m.numel, hipMemcpyDeviceToDevice,
+                               st));
+    return SC_OK;
+}
+
+int sc_get_stats(sc_handle h, sc_stats* out, int* per_mat_sweeps) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    if (!out) return fail(SC_ERR_INVALID_ARG, "out is NULL");
+    DeviceGuard g(h->device);
+    HIP_TRY(hipDeviceSynchronize());
+    HIP_TRY(hipMemcpy(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n, hipMemcpyDeviceToHost));
+    int status[4];
+    HIP_TRY(hipMemcpy(status, h->status_d, sizeof(status), hipMemcpyDeviceToHost));
+    memset(out, 0, sizeof(*out));
+    out->n_mats = h->n;
+    out->step = h->t;
+    out->refreshes = h->refreshes;
+    for (int i = 0; i < h->n; ++i) {
+        const MatFlags& f = h->flags_h[i];
+        out->sweeps_max = std::max(out->sweeps_max, f.sweeps);
+        if (h->refreshes > 0 && !f.converged) out->not_converged += 1;
+        if (per_mat_sweeps) per_mat_sweeps[i] = f.sweeps;
+    }
+    out->nonfinite_grad = status[0] != 0;
+    out->nonfinite_anchor = status[1] != 0;
+    return SC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Device helpers shared by the HIP kernels of libscopt (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace scopt {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// bfloat16 <-> float32.  bf16 is the upper half of an IEEE float32;
+// narrowing rounds to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+};
+template <> struct Elem<uint16_t> {
+    __device__ __forceinline__ static float load(const uint16_t* p, int64_t i) {
+        return bf16_to_f32(p[i]);
+    }
+};
+
+// Load 4 consecutive elements (the address must be 4-element aligned).
+__device__ __forceinline__ float4 load4(const float* p) { return *(const float4*)p; }
+__device__ __forceinline__ float4 load4(const uint16_t* p) {
+    uint2 u = *(const uint2*)p;
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
+// The compute units of an MI355X are spread over 8 dies (XCDs), each with
+// its own L2; consecutive workgroup ids are dealt round robin to the XCDs.
+// Remap so that every XCD receives a contiguous range of logical ids: tiles
+// that share operand panels then share an L2.
+__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
+    const int nx = 8;
+    int per = nwg / nx, rem = nwg % nx;
+    int x = wg % nx, slot = wg / nx;
+    // XCDs with index < rem get per + 1 ids.
+    int base = x * per + (x < rem ? x : rem);
+    int cnt = per + (x < rem ? 1 : 0);
+    if (slot >= cnt) return wg;  // cannot happen when nwg ids are launched
+    return base + slot;
+}
+
+// Round-robin ("circle") pairing of nb items: round r in [0, nb-1),
+// slot i in [0, nb/2); returns p < q.
+__device__ __host__ __forceinline__ void rr_pair(int nb, int r, int i, int* p, int* q) {
+    int n = nb - 1, a, b;
+    if (i == 0) {
+        a = nb - 1;
+        b = r;
+    } else {
+        a = (r + i) % n;
+        b = (r - i + n) % n;
+    }
+    *p = a < b ? a : b;
+    *q = a < b ? b : a;
+}
+
+}  // namespace scopt

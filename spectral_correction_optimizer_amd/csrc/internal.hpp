@@ -1,0 +1,128 @@
+// Internal structures of libscopt shared by the host orchestration (api.cpp)
+// and the kernel launchers (elementwise.hip, gemm.hip, jacobi.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace scopt {
+
+constexpr int kMaxPtrs = 128;  // matrices per launch when pointers travel as kernel arguments
+constexpr int kJb = 32;        // Jacobi column-block width b; a pair block holds 2b = 64 columns
+constexpr int kPw = 2 * kJb;   // pair width
+
+// Caller pointers of one call (weights / gradients), passed by value.
+struct PtrTable {
+    const void* p[kMaxPtrs];
+};
+
+// Per-matrix geometry and device buffers (device-visible copy in MatDev[]).
+struct MatDev {
+    int m, n;        // weight shape, row-major [m][n]
+    int K, k;        // Jacobi operand A is K x k with K = max(m,n), k = min(m,n)
+    int kpad;        // k rounded up to a multiple of 2b
+    int K_ld;        // row stride of A and F: K rounded up to a multiple of 128
+    int nb;          // kpad / b column blocks
+    int tall;        // 1 when m >= n (A = M), 0 when m < n (A = M^T)
+    int64_t numel;   // m * n
+    float* Manc;     // [m][n] anchor momentum
+    float* madam;    // [m][n] AdamW first moment
+    float* vadam;    // [m][n] AdamW second moment
+    float* A;        // [kpad][K_ld] Jacobi operand, rows = columns of A (zero padded)
+    float* V;        // [kpad][kpad] accumulated rotations, rows = columns of V_A
+    float* F;        // [k][K_ld] final A-side singular vectors (rows), unit norm
+    float* W;        // [k][k] final accumulated-side singular vectors (rows)
+    float* PL;       // [m][m] left projector U D U^T (square or wide)
+    float* PR;       // [n][n] right projector V D V^T (square or tall)
+    float* s;        // [kpad] singular values
+    float* d;        // [kpad] Tikhonov response
+    double* norm2;   // [kpad] squared row norms (scratch)
+    float* Gfilt;    // [m][n] filtered gradient of the last step
+    float* Gproj;    // [m][n] combined gradient (only when kept), else null
+    float* Y;        // [k][k] step intermediate
+    float* T;        // [k][k] step intermediate
+    float* E;        // [k][k] refresh scratch (Gram of factors, scaled copies)
+    double* gram;    // [nb/2][nsplit][2b][2b] split partial Gram blocks
+    float* rot;      // [nb/2][2b][2b] R = Q - I of each pair
+    int* rot_flag;   // [nb/2] 1 when the pair's rotation must be applied
+    int nsplit;      // K-splits of a pair Gram
+    int ksplit_len;  // K range of one split (multiple of 256)
+    int pad0;
+};
+
+// Per-matrix device flags / counters.
+struct MatFlags {
+    unsigned int sweep_max;  // max relative off-diagonal seen this sweep (float bits)
+    int converged;           // 1 once a sweep saw nothing above tolerance
+    int sweeps;              // sweeps done in the current refresh
+    int done;                // converged or sweep cap reached
+    float floor2;            // squared column-norm floor: columns below are zero
+    int pad[3];
+};
+
+// ---- work items ------------------------------------------------------------------
+
+struct GramItem { int mat, slot, split; };
+struct SolveItem { int mat, slot; };
+struct ApplyItem { int mat, slot, which, chunk; };  // which: 0 = A rows, 1 = V rows
+struct Chunk { int mat; int64_t off; int len; };    // elementwise chunk of one matrix
+
+// ---- grouped GEMM ----------------------------------------------------------------
+
+enum { GF_ZERO_DIAG = 1 };
+
+struct GemmProb {
+    const void* A;   // M x K (or K x M when transposed), element type of the launch
+    const void* B;   // K x N (or N x K when transposed)
+    float* C;        // M x N float32 output
+    const float* Cin;  // optional, out = alpha*acc + beta*Cin
+    const float* row_scale;  // optional scale of output row i
+    const float* col_scale;  // optional scale of output column j
+    const float* k_scale;    // optional scale of B's reduction index (row of B)
+    int M, N, K;
+    int lda, ldb, ldc, ldcin;
+    float alpha, beta;
+    int flags;
+    int a_ptr, b_ptr;  // >= 0: take A (B) from the call's PtrTable entry
+    int tiles_n, tile_start;
+};
+
+// Launch one grouped GEMM over `probs` (device array, nprob entries, tile
+// prefix filled); ta/tb: operand stored transposed; a_bf16/b_bf16: operand
+// element type.  ptrs: caller pointers referenced by a_ptr/b_ptr.
+hipError_t launch_gemm(const GemmProb* probs_dev, int nprob, int total_tiles, bool ta, bool tb,
+                       bool a_bf16, bool b_bf16, const PtrTable& ptrs, hipStream_t st);
+constexpr int kGemmBM = 128, kGemmBN = 128;
+
+// ---- elementwise -------------------------------------------------------------------
+
+hipError_t launch_ema(const MatDev* mats, const Chunk* chunks, int nchunks, const PtrTable& g,
+                      bool g_bf16, float beta, int* nonfinite, hipStream_t st);
+hipError_t launch_combine_adamw(const MatDev* mats, const Chunk* chunks, int nchunks,
+                                const PtrTable& w, const PtrTable& g, bool w_bf16, bool g_bf16,
+                                float alpha, float beta1, float beta2, float eps,
+                                float step_size, float inv_sqrt_bc2, float lr_wd, int keep_proj,
+                                int* nonfinite, hipStream_t st);
+// A <- M (copy or transpose), V <- I, for matrices in mat_list.
+hipError_t launch_jacobi_load(const MatDev* mats, int nmat, int max_kpad, int max_K,
+                              hipStream_t st);
+// norm2[j] = sum_x X[j][x]^2 (fp64) for the rows of A (which=0) or V (which=1)
+hipError_t launch_rownorm(const MatDev* mats, int nmat, int which, int max_kpad, hipStream_t st);
+// floor2 = (2^-24)^2 * sum_j norm2[j]; clears sweep flags
+hipError_t launch_jacobi_init_flags(const MatDev* mats, MatFlags* flags, int nmat, hipStream_t st);
+// Normalize rows of A (which=0, into F) or V (which=1, into W scratch in place).
+hipError_t launch_normalize(const MatDev* mats, const MatFlags* flags, int nmat, int which,
+                            int max_kpad, int max_K, hipStream_t st);
+hipError_t launch_filter(const MatDev* mats, int nmat, float tau, int max_kpad, hipStream_t st);
+
+// ---- Jacobi sweeps -------------------------------------------------------------------
+
+hipError_t launch_jacobi_round(const MatDev* mats, MatFlags* flags, const GramItem* gi, int ngi,
+                               const SolveItem* si, int nsi, const ApplyItem* ai, int nai,
+                               int round, int max_sweeps, float tol, int nmat, hipStream_t st);
+
+// dst[c * ld_dst + r] = src[r * ld_src + c] for r < rows, c < cols
+hipError_t launch_transpose(const float* src, int rows, int cols, int ld_src, float* dst,
+                            int ld_dst, hipStream_t st);
+
+}  // namespace scopt

@@ -1,0 +1,349 @@
+// Blocked one-sided Jacobi (Hestenes) SVD sweeps on gfx950.
+//
+// The spectral-correction optimizer takes a thin SVD of each matrix's anchor
+// momentum ("Key design 3" of the papernotes.org notes on "Communication-
+// Efficient LLM Adaptation over Decentralized GPU Meshes").  The operand A
+// (K x k, K >= k; A = M or M^T) is kept as rows = columns of A.  Its k columns
+// are cut into blocks of b = 32; a sweep visits every block pair once in
+// round-robin order (nb - 1 rounds of nb/2 disjoint pairs).  One round is three
+// launches over all pairs of all matrices:
+//
+//   gram   per (pair, K split): G_part = X X^T, X = the pair's 64 rows of A,
+//          fp32 MFMA accumulation restarted every 256 columns and summed in
+//          fp64 registers (bounds the rounding of long dot products).
+//   solve  per pair: sum the split partials in fixed order (fp64), measure the
+//          largest relative off-diagonal |g_pq| / sqrt(g_pp g_qq); if above the
+//          tolerance run one cyclic sweep of 2x2 Jacobi rotations on the 64x64
+//          Gram in LDS (round-robin order, 32 disjoint rotations per step),
+//          accumulating Q; store R = Q - I.
+//   apply  per (pair, 128-column chunk, A or V): X <- X + R^T X on fp32 MFMA.
+//          The correction form keeps the rounding of near-identity rotations
+//          at the level of one addition.
+//
+// Every row of A and V belongs to exactly one pair per round, so the kernels
+// of a round never write the same memory from two workgroups.  Reductions run
+// in a fixed order: results are bitwise reproducible.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace scopt {
+
+namespace {
+
+constexpr int PW = kPw;          // 64 rows per pair block
+constexpr int KC = 32;           // K columns per LDS stage
+constexpr int XS = PW + 32;      // LDS row stride of the k-major X tile (96)
+constexpr int CHUNK = 256;       // fp32 accumulation length before folding into fp64
+constexpr int APPLY_NC = 128;    // columns per apply workgroup
+
+__device__ __forceinline__ int pair_row(int blkI, int blkJ, int rho) {
+    return rho < kJb ? blkI * kJb + rho : blkJ * kJb + (rho - kJb);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict__ mats,
+                                                       const MatFlags* __restrict__ flags,
+                                                       const GramItem* __restrict__ items,
+                                                       int round) {
+    __shared__ float Xs[2][KC][XS];
+    const GramItem it = items[blockIdx.x];
+    if (flags[it.mat].done) return;
+    const MatDev& md = mats[it.mat];
+    const int nb = md.nb;
+    int bI, bJ;
+    rr_pair(nb, round % (nb - 1), it.slot, &bI, &bJ);
+    const int x_begin = it.split * md.ksplit_len;
+    int x_end = x_begin + md.ksplit_len;
+    if (x_end > md.K_ld) x_end = md.K_ld;
+
+    // loader: 64 rows x 32 columns = 512 float4 slots, 2 per thread
+    // slot s: row = s >> 3, q = s & 7
+    const float* rowp[2];
+    int lrow[2], lq[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        int s = threadIdx.x + 256 * e;
+        lrow[e] = s >> 3;
+        lq[e] = s & 7;
+        rowp[e] = md.A + (int64_t)pair_row(bI, bJ, lrow[e]) * md.K_ld;
+    }
+    float4 reg[2];
+    auto gload = [&](int x0) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) reg[e] = *(const float4*)(rowp[e] + x0 + 4 * lq[e]);
+    };
+    auto lstore = [&](int b) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            Xs[b][4 * lq[e] + 0][lrow[e]] = reg[e].x;
+            Xs[b][4 * lq[e] + 1][lrow[e]] = reg[e].y;
+            Xs[b][4 * lq[e] + 2][lrow[e]] = reg[e].z;
+            Xs[b][4 * lq[e] + 3][lrow[e]] = reg[e].w;
+        }
+    };
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tr = (wave >> 1) * 32, tc = (wave & 1) * 32;
+    const int hl = lane >> 5, ll = lane & 31;
+    v16f acc;
+    double acc64[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        acc[r] = 0.0f;
+        acc64[r] = 0.0;
+    }
+    const int nst = (x_end - x_begin) / KC;  // K_ld and split lengths are multiples of KC
+    if (nst > 0) {
+        gload(x_begin);
+        lstore(0);
+    }
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+        const int b = st & 1;
+        if (st + 1 < nst) gload(x_begin + (st + 1) * KC);
+#pragma unroll
+        for (int kk = 0; kk < KC; kk += 2) {
+            float a = Xs[b][kk + hl][tr + ll];
+            float c = Xs[b][kk + hl][tc + ll];
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, c, acc, 0, 0, 0);
+        }
+        if (((st + 1) * KC) % CHUNK == 0 || st + 1 == nst) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                acc64[r] += (double)acc[r];
+                acc[r] = 0.0f;
+            }
+        }
+        if (st + 1 < nst) lstore(b ^ 1);
+        __syncthreads();
+    }
+    // write this wave's 32x32 block of the 64x64 partial
+    double* out = md.gram + ((int64_t)it.slot * md.nsplit + it.split) * (PW * PW);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = tr + 8 * (r >> 2) + 4 * hl + (r & 3);
+        out[row * PW + tc + ll] = acc64[r];
+    }
+}
+
+// ---------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict__ mats,
+                                                        MatFlags* __restrict__ flags,
+                                                        const SolveItem* __restrict__ items,
+                                                        float tol) {
+    // G: float32 working copy of the pair Gram (guides the rotation angles).
+    // Q: float64 accumulated rotation.  The rotation parameters are computed in
+    // float64 so that every applied 2x2 rotation is orthogonal to ~1e-16: with
+    // float32 (c, s) a tiny rotation has c == 1 and c^2 + s^2 > 1, a biased
+    // growth of the column norms that accumulates over thousands of rotations.
+    __shared__ float G[PW][PW + 1];
+    __shared__ double Q[PW][PW + 1];
+    __shared__ double dg[PW];
+    __shared__ float red[4];
+    __shared__ double cs_c[PW / 2], cs_s[PW / 2];
+    __shared__ int pp[PW / 2], qq[PW / 2];
+
+    const SolveItem it = items[blockIdx.x];
+    MatFlags& fl = flags[it.mat];
+    if (fl.done) return;
+    const MatDev& md = mats[it.mat];
+    const float floor2 = fl.floor2;
+    const int tid = threadIdx.x;
+
+    // 1. sum split partials (fixed order) into fp64, keep fp32 copy in LDS
+    const double* gp = md.gram + (int64_t)it.slot * md.nsplit * (PW * PW);
+    double gv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int idx = tid + 256 * e;
+        double s = 0.0;
+        for (int sp = 0; sp < md.nsplit; ++sp) s += gp[(int64_t)sp * PW * PW + idx];
+        gv[e] = s;
+        G[idx >> 6][idx & 63] = (float)s;
+        if ((idx >> 6) == (idx & 63)) dg[idx & 63] = s;
+    }
+    __syncthreads();
+
+    // 2. largest relative off-diagonal over columns above the zero floor
+    float mo = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int idx = tid + 256 * e;
+        const int a = idx >> 6, b = idx & 63;
+        if (a < b) {
+            const double da = dg[a], db = dg[b];
+            if (da > (double)floor2 && db > (double)floor2) {
+                float o = (float)(fabs(gv[e]) / sqrt(da * db));
+                mo = fmaxf(mo, o);
+            }
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) mo = fmaxf(mo, __shfl_xor(mo, o));
+    if ((tid & 63) == 0) red[tid >> 6] = mo;
+    __syncthreads();
+    mo = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (tid == 0) atomicMax(&fl.sweep_max, __float_as_uint(mo));
+    int* rflag = md.rot_flag + it.slot;
+    if (!(mo > tol)) {
+        if (tid == 0) *rflag = 0;
+        return;
+    }
+
+    // 3. one cyclic sweep of 2x2 rotations on G, accumulating Q (starts at I)
+    for (int idx = tid; idx < PW * PW; idx += 256)
+        Q[idx >> 6][idx & 63] = (idx >> 6) == (idx & 63) ? 1.0 : 0.0;
+    __syncthreads();
+    for (int ir = 0; ir < PW - 1; ++ir) {
+        if (tid < PW / 2) {
+            int p, q;
+            rr_pair(PW, ir, tid, &p, &q);
+            const double gpp = G[p][p], gqq = G[q][q], gpq = G[p][q];
+            double c = 1.0, s = 0.0;
+            if (gpp > floor2 && gqq > floor2 && fabs(gpq) > tol * sqrt(gpp * gqq)) {
+                const double zeta = (gqq - gpp) / (2.0 * gpq);
+                const double t = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + hypot(1.0, zeta));
+                c = 1.0 / sqrt(1.0 + t * t);
+                s = c * t;
+            }
+            cs_c[tid] = c;
+            cs_s[tid] = s;
+            pp[tid] = p;
+            qq[tid] = q;
+        }
+        __syncthreads();
+        // columns of G and Q: [col_p, col_q] <- [c col_p - s col_q, s col_p + c col_q]
+        for (int w = tid; w < (PW / 2) * PW; w += 256) {
+            const int i = w >> 6, a = w & 63;
+            const double s = cs_s[i];
+            if (s != 0.0) {
+                const double c = cs_c[i];
+                const int p = pp[i], q = qq[i];
+                const float cf = (float)c, sf = (float)s;
+                const float x = G[a][p], y = G[a][q];
+                G[a][p] = cf * x - sf * y;
+                G[a][q] = sf * x + cf * y;
+                const double xd = Q[a][p], yd = Q[a][q];
+                Q[a][p] = c * xd - s * yd;
+                Q[a][q] = s * xd + c * yd;
+            }
+        }
+        __syncthreads();
+        // rows of G
+        for (int w = tid; w < (PW / 2) * PW; w += 256) {
+            const int i = w >> 6, bcol = w & 63;
+            const double s = cs_s[i];
+            if (s != 0.0) {
+                const float cf = (float)cs_c[i], sf = (float)s;
+                const int p = pp[i], q = qq[i];
+                const float x = G[p][bcol], y = G[q][bcol];
+                G[p][bcol] = cf * x - sf * y;
+                G[q][bcol] = sf * x + cf * y;
+            }
+        }
+        __syncthreads();
+    }
+    // 4. R = Q - I (formed in float64, stored float32), row-major [b][a]
+    //    (X_new[a] = X[a] + sum_b R[b][a] X[b])
+    float* R = md.rot + (int64_t)it.slot * PW * PW;
+    for (int idx = tid; idx < PW * PW; idx += 256) {
+        const int b = idx >> 6, a = idx & 63;
+        R[idx] = (float)(Q[b][a] - (b == a ? 1.0 : 0.0));
+    }
+    if (tid == 0) *rflag = 1;
+}
+
+// ---------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void jac_apply_kernel(const MatDev* __restrict__ mats,
+                                                        const MatFlags* __restrict__ flags,
+                                                        const ApplyItem* __restrict__ items,
+                                                        int round) {
+    __shared__ float Rs[PW][PW + 32];
+    __shared__ float Xs[PW][APPLY_NC + 32];
+    const ApplyItem it = items[blockIdx.x];
+    if (flags[it.mat].done) return;
+    const MatDev& md = mats[it.mat];
+    if (md.rot_flag[it.slot] == 0) return;
+    int bI, bJ;
+    rr_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
+    float* base = it.which == 0 ? md.A : md.V;
+    const int ld = it.which == 0 ? md.K_ld : md.kpad;
+    const int x0 = it.chunk * APPLY_NC;
+    const int ncols = min(APPLY_NC, ld - x0);  // multiple of 4 (ld is a multiple of 64)
+
+    const float* R = md.rot + (int64_t)it.slot * PW * PW;
+    for (int idx = threadIdx.x; idx < PW * PW / 4; idx += 256) {
+        const int b = idx >> 4, a4 = (idx & 15) * 4;
+        *(float4*)&Rs[b][a4] = *(const float4*)(R + b * PW + a4);
+    }
+    for (int idx = threadIdx.x; idx < PW * APPLY_NC / 4; idx += 256) {
+        const int rho = idx >> 5, c4 = (idx & 31) * 4;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (c4 < ncols)
+            v = *(const float4*)(base + (int64_t)pair_row(bI, bJ, rho) * ld + x0 + c4);
+        *(float4*)&Xs[rho][c4] = v;
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ta = (wave >> 1) * 32, tn = (wave & 1) * 64;
+    const int hl = lane >> 5, ll = lane & 31;
+    v16f acc0, acc1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        acc0[r] = 0.0f;
+        acc1[r] = 0.0f;
+    }
+#pragma unroll
+    for (int kb = 0; kb < PW; kb += 2) {
+        const float a = Rs[kb + hl][ta + ll];
+        const float x0v = Xs[kb + hl][tn + ll];
+        const float x1v = Xs[kb + hl][tn + 32 + ll];
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, x0v, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, x1v, acc1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int arow = ta + 8 * (r >> 2) + 4 * hl + (r & 3);
+        float* dst = base + (int64_t)pair_row(bI, bJ, arow) * ld + x0;
+        const int c0 = tn + ll, c1 = tn + 32 + ll;
+        if (c0 < ncols) dst[c0] = Xs[arow][c0] + acc0[r];
+        if (c1 < ncols) dst[c1] = Xs[arow][c1] + acc1[r];
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// End-of-round bookkeeping: a matrix whose sweep ended this round is
+// converged when nothing above tolerance was seen during the sweep.
+__global__ void jac_sweep_end_kernel(const MatDev* __restrict__ mats, MatFlags* __restrict__ flags,
+                                     int nmat, int round, int max_sweeps, float tol) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nmat) return;
+    MatFlags& f = flags[i];
+    if (f.done) return;
+    const int nbm1 = mats[i].nb - 1;
+    if (round % nbm1 != nbm1 - 1) return;
+    f.sweeps += 1;
+    const float mo = __uint_as_float(f.sweep_max);
+    f.sweep_max = 0u;
+    if (!(mo > tol)) {
+        f.converged = 1;
+        f.done = 1;
+    } else if (f.sweeps >= max_sweeps) {
+        f.done = 1;
+    }
+}
+
+hipError_t launch_jacobi_round(const MatDev* mats, MatFlags* flags, const GramItem* gi, int ngi,
+                               const SolveItem* si, int nsi, const ApplyItem* ai, int nai,
+                               int round, int max_sweeps, float tol, int nmat, hipStream_t st) {
+    hipLaunchKernelGGL(jac_gram_kernel, dim3(ngi), dim3(256), 0, st, mats, flags, gi, round);
+    hipLaunchKernelGGL(jac_solve_kernel, dim3(nsi), dim3(256), 0, st, mats, flags, si, tol);
+    hipLaunchKernelGGL(jac_apply_kernel, dim3(nai), dim3(256), 0, st, mats, flags, ai, round);
+    hipLaunchKernelGGL(jac_sweep_end_kernel, dim3((nmat + 63) / 64), dim3(64), 0, st, mats, flags,
+                       nmat, round, max_sweeps, tol);
+    return hipGetLastError();
+}
+
+}  // namespace scopt

@@ -1,0 +1,160 @@
+"""Shared driver of the GPU parity tests: run the HIP path (through the C ABI
+binding) and the CPU oracle on identical seeded inputs and compare.
+
+Gates (the tolerances of the benchmark spec; see the design notes for the
+step-1 reading):
+  * G_filt and G_proj: relative Frobenius error <= 1e-4 against the oracle;
+  * float32 W: max-abs error <= 1e-7 on every element whose step-1 oracle
+    |G_proj| >= 1e-6 (near g = 0 the first AdamW update lr g / (|g| + eps)
+    has slope lr / eps = 2000, so a tolerated 1e-4 G_proj error can move
+    such elements by more than 1e-7); the excluded set is reported;
+  * bfloat16 W: at most one bfloat16 ulp from the oracle's rounded value.
+"""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+import torch
+
+import gen
+import oracle
+
+REL_TOL = 1e-4
+W_TOL = 1e-7
+SMALL_G = 1e-6
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def relf(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a))
+
+
+def to_dev(payload, dtype, device):
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(payload)).to(device)
+    # bf16 bit patterns (uint16) -> torch.bfloat16
+    t = torch.from_numpy(np.ascontiguousarray(payload).view(np.int16)).to(device)
+    return t.view(torch.bfloat16)
+
+
+def from_dev(t):
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def bf16_ulp(x):
+    x = np.abs(np.asarray(x, np.float64))
+    _, e = np.frexp(np.where(x > 0, x, 1.0))
+    return np.ldexp(1.0, np.maximum(e - 8, -133))
+
+
+class Scenario:
+    """M_anc seeded from the generator, anchor refreshes every `anchor_every`
+    steps (first one before step 1), `steps` fast steps."""
+
+    def __init__(self, shapes, ids, hp=None, steps=5, anchor_every=None, w_dtype="f32",
+                 g_dtype="f32", r0=None, noise=True, threads=None, max_sweeps=30):
+        self.shapes = [tuple(s) for s in shapes]
+        self.ids = ids
+        self.hp = dict(gen.DEFAULT_HP)
+        if hp:
+            self.hp.update(hp)
+        self.steps = steps
+        self.anchor_every = anchor_every or steps + 1
+        self.w_dtype, self.g_dtype = w_dtype, g_dtype
+        self.inputs = [gen.MatrixInputs(c, b, m, r, col, r0=r0, noise=noise)
+                       for (c, b, m), (r, col) in zip(ids, self.shapes)]
+        self.threads = threads
+        self.max_sweeps = max_sweeps
+
+    def run(self, device="cuda", check_every_step=True, gpu_hp=None):
+        dev = torch.device(device)
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+        import spectral_correction_optimizer_amd as sco
+        opt = sco.SpectralAdamW(self.shapes, w_dtype=tdt[self.w_dtype], g_dtype=tdt[self.g_dtype],
+                                device=dev, max_sweeps=self.max_sweeps, **self.hp, **(gpu_hp or {}))
+        opt.keep_proj(True)
+        ora = oracle.Optimizer(self.shapes, self.hp, w_dtype=self.w_dtype, state_dtype="f32",
+                               threads=self.threads)
+        W_dev, W_ora = [], []
+        for i, mi in enumerate(self.inputs):
+            m0_payload, m0_val = gen.stored(mi.m0(), "f32")
+            opt.set_state(i, "m_anc", to_dev(m0_payload, "f32", dev))
+            ora.set_anchor_momentum(i, m0_val)
+            wp, wv = gen.stored(mi.w0(), self.w_dtype)
+            W_dev.append(to_dev(wp, self.w_dtype, dev))
+            W_ora.append(wv)
+        report = dict(gfilt=[], gproj=[], w=[], excluded=[], sweeps=[], t_gpu=0.0, t_ora=0.0)
+        step1_small = [None] * len(self.shapes)
+        anchor_k = 0
+        for step in range(self.steps):
+            if step % self.anchor_every == 0:
+                ga_pay, ga_val = zip(*[gen.stored(mi.g_anc(anchor_k), self.g_dtype)
+                                       for mi in self.inputs])
+                t0 = time.time()
+                opt.anchor_update([to_dev(p, self.g_dtype, dev) for p in ga_pay])
+                torch.cuda.synchronize(dev)
+                report["t_gpu"] += time.time() - t0
+                t0 = time.time()
+                ora.anchor_update(list(ga_val))
+                report["t_ora"] += time.time() - t0
+                report["sweeps"].append((opt.stats()["sweeps"], list(ora.sweeps)))
+                anchor_k += 1
+            gm_pay, gm_val = zip(*[gen.stored(mi.g_mask(step), self.g_dtype) for mi in self.inputs])
+            t0 = time.time()
+            opt.step(W_dev, [to_dev(p, self.g_dtype, dev) for p in gm_pay])
+            torch.cuda.synchronize(dev)
+            report["t_gpu"] += time.time() - t0
+            t0 = time.time()
+            W_ora = ora.step(W_ora, list(gm_val))
+            report["t_ora"] += time.time() - t0
+            if step == 0:
+                step1_small = [np.abs(p) < SMALL_G for p in ora.last_proj]
+            if not (check_every_step or step == self.steps - 1):
+                continue
+            for i in range(len(self.shapes)):
+                gf, gp = opt.get_filtered(i, proj=True)
+                gf, gp = from_dev(gf), from_dev(gp)
+                report["gfilt"].append((step, i, relf(gf, ora.last_filt[i])))
+                report["gproj"].append((step, i, relf(gp, ora.last_proj[i])))
+                w = from_dev(W_dev[i])
+                err = np.abs(w - W_ora[i])
+                if self.w_dtype == "f32":
+                    mask = ~step1_small[i]
+                    report["w"].append((step, i, float(err[mask].max()) if mask.any() else 0.0))
+                    report["excluded"].append((step, i, int((~mask).sum()),
+                                               float(err[~mask].max()) if (~mask).any() else 0.0))
+                else:
+                    ulps = err / bf16_ulp(W_ora[i])
+                    report["w"].append((step, i, float(ulps.max())))
+                    report["excluded"].append((step, i, int((ulps > 0).sum()), 0.0))
+        report["stats"] = opt.stats()
+        opt.close()
+        return report
+
+    @staticmethod
+    def check(report, w_tol=W_TOL, rel_tol=REL_TOL, w_dtype="f32"):
+        worst_f = max(e for _, _, e in report["gfilt"])
+        worst_p = max(e for _, _, e in report["gproj"])
+        worst_w = max(e for _, _, e in report["w"])
+        say(f"  worst relF G_filt {worst_f:.3e}  G_proj {worst_p:.3e}  W {worst_w:.3e}"
+            f"  sweeps {report['sweeps']}  t_gpu {report['t_gpu']:.2f}s t_oracle {report['t_ora']:.2f}s")
+        exc = [(s, i, c, e) for s, i, c, e in report["excluded"] if c]
+        if exc:
+            say(f"  excluded small-|G_proj| elements (step, mat, count, max err): {exc[-3:]}")
+        assert worst_f <= rel_tol, report["gfilt"]
+        assert worst_p <= rel_tol, report["gproj"]
+        if w_dtype == "f32":
+            assert worst_w <= w_tol, report["w"]
+        else:
+            assert worst_w <= 1.0 + 1e-9, report["w"]

@@ -1,0 +1,228 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Seeded synthetic inputs of the workloads' shapes and distributions (gen).
+Sizes are chosen so the oracle finishes in seconds while spanning several
+GEMM tiles, several Jacobi block pairs and ragged tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+from tests.gpu_harness import Scenario, relf, say, to_dev, from_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import spectral_correction_optimizer_amd as sco
+    sco.load_library()
+
+
+def test_single_64x48_five_steps():
+    """The small single-matrix workload: 64x48 fp32, 1 anchor update, 5 steps.
+    W is gated on every element."""
+    say("case: 64x48, 1 refresh + 5 steps")
+    sc = Scenario([(64, 48)], [(1, 0, 0)], steps=5)
+    rep = sc.run()
+    Scenario.check(rep)
+    assert max(e for _, _, c, e in rep["excluded"]) <= 1e-7
+
+
+@pytest.mark.parametrize("shape", [(200, 136), (136, 200), (130, 130), (520, 96), (96, 520),
+                                   (300, 64), (33, 70), (257, 1), (1, 45)])
+def test_ragged_shapes(shape):
+    say(f"case: ragged {shape}, 1 refresh + 3 steps")
+    sc = Scenario([shape], [(90, 0, 0)], steps=3)
+    Scenario.check(sc.run())
+
+
+def test_group_of_mixed_shapes_two_refreshes():
+    """Several matrices of all three shape classes in one handle; the anchor
+    arrives every 2 steps."""
+    shapes = [(256, 256), (96, 256), (512, 128), (128, 512), (72, 40)]
+    say(f"case: group {shapes}, refresh every 2 steps, 5 steps")
+    sc = Scenario(shapes, [(91, 0, i) for i in range(len(shapes))], steps=5, anchor_every=2)
+    Scenario.check(sc.run())
+
+
+@pytest.mark.parametrize("tau", [1e-4, 1e-2, 0.0])
+def test_tau_values(tau):
+    say(f"case: tau {tau}, 192x160")
+    sc = Scenario([(192, 160)], [(92, 0, 0)], hp=dict(tau_p=tau), steps=2)
+    Scenario.check(sc.run())
+
+
+def test_alpha_one_is_plain_adamw():
+    """alpha = 1: G_proj = G_mask ("pure mask" ablation), the step is AdamW on G_mask."""
+    say("case: alpha 1")
+    sc = Scenario([(160, 96)], [(93, 0, 0)], hp=dict(alpha=1.0), steps=3)
+    Scenario.check(sc.run())
+
+
+def test_alpha_zero_pure_filtered():
+    say("case: alpha 0")
+    sc = Scenario([(160, 96)], [(94, 0, 0)], hp=dict(alpha=0.0), steps=2)
+    Scenario.check(sc.run())
+
+
+def test_bf16_weights_and_gradients():
+    """bfloat16 W, G_mask and G_anc (float32 states): W within one bf16 ulp."""
+    say("case: bf16 W/G, 256x192 and 128x320")
+    sc = Scenario([(256, 192), (128, 320)], [(95, 0, 0), (95, 0, 1)], steps=3, w_dtype="bf16",
+                  g_dtype="bf16")
+    rep = sc.run()
+    Scenario.check(rep, w_dtype="bf16")
+
+
+def test_no_anchor_yet_gives_alpha_g():
+    """Before any anchor arrives M_anc = 0, so d = 0, G_filt = 0 and G_proj = alpha G."""
+    import spectral_correction_optimizer_amd as sco
+    say("case: no anchor")
+    dev = torch.device("cuda")
+    opt = sco.SpectralAdamW([(96, 64)], device=dev)
+    opt.keep_proj(True)
+    g = torch.randn(96, 64, device=dev) * 1e-3
+    w = torch.randn(96, 64, device=dev) * 0.02
+    opt.step([w], [g])
+    gf, gp = opt.get_filtered(0, proj=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(gf).item() == 0
+    assert torch.allclose(gp, 0.3 * g, rtol=1e-6, atol=0)
+    opt.close()
+
+
+def test_injected_oracle_factors_isolate_projection():
+    """Install the oracle's (fp32-rounded) factors, then compare G_filt: this
+    isolates the projection / reconstruction GEMM chain from the SVD."""
+    import spectral_correction_optimizer_amd as sco
+    dev = torch.device("cuda")
+    for (m, n) in [(384, 256), (256, 384), (320, 320)]:
+        say(f"case: injected factors {m}x{n}")
+        mi = gen.MatrixInputs(96, 0, 0, m, n)
+        M = gen.stored(mi.m0(), "f32")[1]
+        U, s, V, _ = oracle.svd(M)
+        U32, s32, V32 = (x.astype(np.float32) for x in (U, s, V))
+        G = gen.stored(mi.g_mask(0), "f32")[0]
+        opt = sco.SpectralAdamW([(m, n)], device=dev)
+        opt.set_factors(0, *(torch.from_numpy(x).to(dev) for x in (U32, s32, V32)))
+        w = torch.zeros(m, n, device=dev)
+        opt.step([w], [torch.from_numpy(G).to(dev)])
+        gf = from_dev(opt.get_filtered(0))
+        ref = oracle.project(U32.astype(np.float64), oracle.tikhonov(s32.astype(np.float64), 1e-3),
+                             V32.astype(np.float64), G.astype(np.float64))
+        err = relf(gf, ref)
+        say(f"  relF {err:.3e}")
+        assert err < 1e-5
+        # exported factors round-trip
+        U2, s2, V2 = (x.cpu().numpy() for x in opt.get_factors(0))
+        assert np.array_equal(s2, s32) and np.array_equal(U2, U32) and np.array_equal(V2, V32)
+        opt.close()
+
+
+def test_svd_self_consistency():
+    """GPU factors reconstruct M and are orthonormal to float32 accuracy."""
+    import spectral_correction_optimizer_amd as sco
+    dev = torch.device("cuda")
+    for (m, n) in [(320, 192), (192, 320), (256, 256)]:
+        say(f"case: svd self-check {m}x{n}")
+        mi = gen.MatrixInputs(97, 0, 0, m, n)
+        pay, M = gen.stored(mi.m0(), "f32")
+        opt = sco.SpectralAdamW([(m, n)], device=dev)
+        opt.set_state(0, "m_anc", torch.from_numpy(pay).to(dev))
+        opt.refresh()
+        U, s, V = (x.double().cpu().numpy() for x in opt.get_factors(0))
+        r = min(m, n)
+        rec = np.linalg.norm((U * s) @ V.T - M) / np.linalg.norm(M)
+        ou = np.linalg.norm(U.T @ U - np.eye(r)) / np.sqrt(r)
+        ov = np.linalg.norm(V.T @ V - np.eye(r)) / np.sqrt(r)
+        s_ref = np.linalg.svd(M, compute_uv=False)
+        se = np.abs(np.sort(s)[::-1] - s_ref).max() / s_ref[0]
+        say(f"  recon {rec:.2e} orthU {ou:.2e} orthV {ov:.2e} s err {se:.2e} stats {opt.stats()}")
+        assert rec < 1e-5 and ou < 1e-5 and ov < 1e-5 and se < 1e-5
+        opt.close()
+
+
+def test_determinism_bitwise():
+    """Two runs on identical inputs give bitwise identical weights."""
+    say("case: determinism 192x256 + 256x128")
+    outs = []
+    for _ in range(2):
+        import spectral_correction_optimizer_amd as sco
+        dev = torch.device("cuda")
+        shapes = [(192, 256), (256, 128)]
+        opt = sco.SpectralAdamW(shapes, device=dev)
+        ins = [gen.MatrixInputs(98, 0, i, *s) for i, s in enumerate(shapes)]
+        for i, mi in enumerate(ins):
+            opt.set_state(i, "m_anc", to_dev(gen.stored(mi.m0(), "f32")[0], "f32", dev))
+        W = [to_dev(gen.stored(mi.w0(), "f32")[0], "f32", dev) for mi in ins]
+        opt.anchor_update([to_dev(gen.stored(mi.g_anc(0), "f32")[0], "f32", dev) for mi in ins])
+        for k in range(3):
+            opt.step(W, [to_dev(gen.stored(mi.g_mask(k), "f32")[0], "f32", dev) for mi in ins])
+        torch.cuda.synchronize()
+        outs.append([w.cpu().numpy().copy() for w in W])
+        opt.close()
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
+def test_checkpoint_resume_bitwise():
+    """Save M_anc, m, v, t and the factors after 2 steps; a fresh handle restored
+    from them continues bitwise identically to the uninterrupted run."""
+    import spectral_correction_optimizer_amd as sco
+    say("case: checkpoint / resume 160x224")
+    dev = torch.device("cuda")
+    shape = (160, 224)
+    mi = gen.MatrixInputs(99, 0, 0, *shape)
+    g = [to_dev(gen.stored(mi.g_mask(k), "f32")[0], "f32", dev) for k in range(4)]
+    a = sco.SpectralAdamW([shape], device=dev)
+    a.set_state(0, "m_anc", to_dev(gen.stored(mi.m0(), "f32")[0], "f32", dev))
+    Wa = to_dev(gen.stored(mi.w0(), "f32")[0], "f32", dev)
+    a.anchor_update([to_dev(gen.stored(mi.g_anc(0), "f32")[0], "f32", dev)])
+    a.step([Wa], [g[0]])
+    a.step([Wa], [g[1]])
+    ck = {k: a.get_state(0, k) for k in ("m_anc", "adam_m", "adam_v")}
+    fac = a.get_factors(0)
+    t = a.step_count
+    Wb = Wa.clone()
+    b = sco.SpectralAdamW([shape], device=dev)
+    for k, v in ck.items():
+        b.set_state(0, k, v)
+    b.set_factors(0, *fac)
+    b.step_count = t
+    for k in (2, 3):
+        a.step([Wa], [g[k]])
+        b.step([Wb], [g[k]])
+    torch.cuda.synchronize()
+    assert torch.equal(Wa, Wb)
+    a.close()
+    b.close()
+
+
+def test_nonfinite_gradient_flag():
+    import spectral_correction_optimizer_amd as sco
+    say("case: non-finite flag")
+    dev = torch.device("cuda")
+    opt = sco.SpectralAdamW([(64, 64)], device=dev)
+    g = torch.zeros(64, 64, device=dev)
+    g[3, 5] = float("nan")
+    w = torch.zeros(64, 64, device=dev)
+    st = opt.stats()
+    assert st["nonfinite_grad"] == 0
+    opt.step([w], [g])
+    st = opt.stats()
+    assert st["nonfinite_grad"] == 1 and st["step"] == 1
+    opt.close()
+
+
+def test_q_proj_2048_full_config():
+    """The single q_proj workload: 2048x2048 fp32, 1 anchor update, 25 steps
+    with fresh noise per step, against the oracle in full."""
+    say("case: 2048x2048, 1 refresh + 25 steps (oracle ~1 min)")
+    sc = Scenario([(2048, 2048)], [(2, 0, 0)], steps=25)
+    rep = sc.run(check_every_step=False)
+    Scenario.check(rep)
