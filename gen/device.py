@@ -1,0 +1,66 @@
+"""Seeded synthetic inputs generated on the GPU with torch (timing workloads).
+
+Same recipe as ``gen.MatrixInputs`` (see the package docstring) but drawn with
+torch's device generator, so the 112-matrix workload is produced in seconds.
+Values differ from the host generator's (different random streams); parity
+tests use the host generator.  Holds no arithmetic of the method.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (ENTROPY, GANC_NOISE, GMASK_NOISE, GMASK_SIGNAL, M0_NOISE, S_GANC, S_GMASK, S_M0,
+               S_U0, S_V0, S_W, SIGNAL_POWER, SIGNAL_SCALE, W_STD)
+
+
+def _seed(cfg, block, mat, stream, k=0) -> int:
+    x = (ENTROPY * 1000003 + cfg) * 1000003 + block
+    x = (x * 1000003 + mat) * 1000003 + stream
+    x = x * 1000003 + k
+    return x % (2 ** 62)
+
+
+def _gen(device, *key):
+    g = torch.Generator(device=device)
+    g.manual_seed(_seed(*key))
+    return g
+
+
+def _haar(device, key, n, r):
+    z = torch.randn((n, r), generator=_gen(device, *key), device=device, dtype=torch.float32)
+    q, rr = torch.linalg.qr(z)
+    sgn = torch.sign(torch.diagonal(rr))
+    sgn[sgn == 0] = 1.0
+    return (q * sgn).contiguous()
+
+
+class DeviceMatrixInputs:
+    def __init__(self, cfg, block, mat, m, n, device, dtype=torch.float32):
+        self.key = (cfg, block, mat)
+        self.m, self.n = m, n
+        self.device = device
+        self.dtype = dtype
+        r = min(m, n)
+        u0 = _haar(device, self.key + (S_U0,), m, r)
+        v0 = _haar(device, self.key + (S_V0,), n, r)
+        i = torch.arange(1, r + 1, device=device, dtype=torch.float32)
+        s0 = SIGNAL_SCALE * i.pow(-SIGNAL_POWER)
+        self.signal = ((u0 * s0) @ v0.t().contiguous()).contiguous()
+        del u0, v0
+
+    def _noise(self, stream, k, std):
+        return std * torch.randn((self.m, self.n), generator=_gen(self.device, *self.key, stream, k),
+                                 device=self.device, dtype=torch.float32)
+
+    def m0(self):
+        return (self.signal + self._noise(S_M0, 0, M0_NOISE)).contiguous()
+
+    def g_anc(self, k):
+        return (self.signal + self._noise(S_GANC, k, GANC_NOISE)).to(self.dtype).contiguous()
+
+    def g_mask(self, k):
+        return (GMASK_SIGNAL * self.signal + self._noise(S_GMASK, k, GMASK_NOISE)).to(
+            self.dtype).contiguous()
+
+    def w0(self):
+        return self._noise(S_W, 0, W_STD).to(self.dtype).contiguous()

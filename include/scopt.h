@@ -164,6 +164,26 @@ typedef struct {
  * each matrix in the last refresh. */
 int sc_get_stats(sc_handle h, sc_stats* out, int* per_mat_sweeps);
 
+/* Kernel timing for measurement: when enabled, every kernel launch of the
+ * handle is bracketed by a pair of HIP events on the launch stream (small
+ * host overhead per launch; device timing is unaffected).  Enabling or
+ * disabling resets the accumulated totals.  A refresh run with timing on also
+ * synchronizes the stream once after its sweeps to read the work counters. */
+int sc_profile(sc_handle h, int enable);
+
+typedef struct {
+    char name[32];     /* kernel family, e.g. "jacobi_gram", "step_gemm1", "combine_adamw" */
+    int64_t launches;  /* launches timed */
+    double total_ms;   /* summed event time of those launches */
+    double flops;      /* algorithmic floating-point operations of those launches */
+    double bytes;      /* algorithmic HBM bytes of those launches (streaming kernels) */
+} sc_kernel_time;
+
+/* Synchronize the device, fold finished timings in, and copy up to
+ * max_entries per-family records to `out` (host array); *count receives the
+ * number of families with at least one launch. */
+int sc_get_kernel_times(sc_handle h, sc_kernel_time* out, int max_entries, int* count);
+
 /* Message of the last error on the calling thread ("" if none). */
 const char* sc_last_error(void);
 

@@ -30,7 +30,7 @@ EXPORTED_SYMBOLS = (
     "sc_default_hparams", "sc_opt_create", "sc_opt_destroy", "sc_anchor_update", "sc_refresh",
     "sc_step", "sc_set_lr", "sc_set_tau", "sc_set_state", "sc_get_state", "sc_set_step",
     "sc_get_step", "sc_set_factors", "sc_get_factors", "sc_keep_proj", "sc_get_filtered",
-    "sc_get_stats", "sc_last_error",
+    "sc_get_stats", "sc_profile", "sc_get_kernel_times", "sc_last_error",
 )
 
 SC_F32, SC_BF16 = 0, 1
@@ -49,6 +49,12 @@ class HParams(ctypes.Structure):
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
                 ("max_sweeps", ctypes.c_int), ("jacobi_tol", ctypes.c_float),
                 ("sync_check", ctypes.c_int)]
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double), ("flops", ctypes.c_double),
+                ("bytes", ctypes.c_double)]
 
 
 class Stats(ctypes.Structure):
@@ -89,6 +95,9 @@ def load_library():
         "sc_keep_proj": (ctypes.c_int, [vp, ctypes.c_int]),
         "sc_get_filtered": (ctypes.c_int, [vp, ctypes.c_int, vp, vp, vp]),
         "sc_get_stats": (ctypes.c_int, [vp, ctypes.POINTER(Stats), ctypes.POINTER(ctypes.c_int)]),
+        "sc_profile": (ctypes.c_int, [vp, ctypes.c_int]),
+        "sc_get_kernel_times": (ctypes.c_int, [vp, ctypes.POINTER(KernelTime), ctypes.c_int,
+                                               ctypes.POINTER(ctypes.c_int)]),
         "sc_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -246,6 +255,22 @@ class SpectralAdamW:
         d = {name: getattr(st, name) for name, _ in Stats._fields_}
         d["sweeps"] = list(per)
         return d
+
+    def profile(self, enable: bool = True):
+        """Enable / disable per-kernel event timing (resets the totals)."""
+        _check(self._lib.sc_profile(self._h, 1 if enable else 0))
+
+    def kernel_times(self):
+        """{family: dict(launches, total_ms, flops, bytes)} accumulated since profile(True)."""
+        arr = (KernelTime * 64)()
+        cnt = ctypes.c_int()
+        _check(self._lib.sc_get_kernel_times(self._h, arr, 64, ctypes.byref(cnt)))
+        out = {}
+        for i in range(min(cnt.value, 64)):
+            k = arr[i]
+            out[k.name.decode()] = dict(launches=k.launches, total_ms=k.total_ms, flops=k.flops,
+                                        bytes=k.bytes)
+        return out
 
     def close(self):
         if getattr(self, "_h", None):

@@ -68,6 +68,32 @@ struct GemmGroup {
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+enum ProfKind {
+    PK_EMA, PK_LOAD, PK_ROWNORM, PK_INIT_FLAGS, PK_GRAM, PK_SOLVE, PK_APPLY, PK_SWEEP_END,
+    PK_NORMALIZE, PK_LOWDIN, PK_FILTER, PK_PROJECTORS, PK_STEP_GEMM1, PK_STEP_GEMM2,
+    PK_STEP_GEMM3, PK_ADAMW, PK_COUNT
+};
+const char* const kProfNames[PK_COUNT] = {
+    "ema", "jacobi_load", "rownorm", "jacobi_init", "jacobi_gram", "jacobi_solve",
+    "jacobi_apply", "jacobi_sweep_end", "normalize", "lowdin_gemm", "filter", "projector_gemm",
+    "step_gemm1", "step_gemm2", "step_gemm3", "combine_adamw"};
+
+// Optional kernel timing: HIP events recorded around every launch on the
+// caller's stream; totals are folded in by sc_get_kernel_times.
+struct Prof {
+    bool on = false;
+    struct Rec {
+        int kind;
+        hipEvent_t a, b;
+    };
+    std::vector<hipEvent_t> pool;
+    std::vector<Rec> recs;
+    int64_t launches[PK_COUNT] = {};
+    double ms[PK_COUNT] = {};
+    double flops[PK_COUNT] = {};
+    double bytes[PK_COUNT] = {};
+};
 int round_up(int x, int a) { return (x + a - 1) / a * a; }
 
 }  // namespace
@@ -107,6 +133,10 @@ struct sc_opt {
     std::vector<int> last_sweeps;
     int last_not_conv = 0;
     std::vector<void*> dev_allocs;
+    Prof prof;
+    double total_numel = 0.0;
+    double ema_bytes = 0.0;    // read M, read G_anc, write M
+    double adamw_bytes = 0.0;  // read G, G_filt, W, m, v; write W, m, v
 };
 
 namespace {
@@ -149,9 +179,43 @@ GemmProb make_prob(const void* A, int lda, const void* B, int ldb, float* C, int
     return p;
 }
 
-int run_group(const GemmGroup& g, const PtrTable& pt, hipStream_t st) {
+hipEvent_t prof_event(Prof& p) {
+    hipEvent_t e = nullptr;
+    if (!p.pool.empty()) {
+        e = p.pool.back();
+        p.pool.pop_back();
+    } else if (hipEventCreate(&e) != hipSuccess) {
+        (void)hipGetLastError();
+        e = nullptr;
+    }
+    return e;
+}
+
+// Run `launch` (returns hipError_t); when profiling, bracket it with events.
+template <typename F>
+hipError_t timed(sc_opt* h, int kind, hipStream_t st, F launch) {
+    if (!h->prof.on) return launch();
+    hipEvent_t a = prof_event(h->prof), b = prof_event(h->prof);
+    if (a) (void)hipEventRecord(a, st);
+    hipError_t e = launch();
+    if (b) (void)hipEventRecord(b, st);
+    if (a && b) h->prof.recs.push_back(Prof::Rec{kind, a, b});
+    h->prof.launches[kind] += 1;
+    return e;
+}
+
+double group_flops(const GemmGroup& g) {
+    double f = 0.0;
+    for (const auto& p : g.h) f += 2.0 * p.M * (double)p.N * p.K;
+    return f;
+}
+
+int run_group(sc_opt* h, const GemmGroup& g, int kind, const PtrTable& pt, hipStream_t st) {
     if (g.h.empty()) return SC_OK;
-    HIP_TRY(launch_gemm(g.d, (int)g.h.size(), g.total, g.ta, g.tb, g.abf, g.bbf, pt, st));
+    HIP_TRY(timed(h, kind, st, [&] {
+        return launch_gemm(g.d, (int)g.h.size(), g.total, g.ta, g.tb, g.abf, g.bbf, pt, st);
+    }));
+    if (h->prof.on) h->prof.flops[kind] += group_flops(g);
     return SC_OK;
 }
 
@@ -201,9 +265,10 @@ PtrTable make_table(const sc_opt* h, const void* const* p) {
 // ---- refresh ------------------------------------------------------------------------
 
 int build_projectors(sc_opt* h, hipStream_t st) {
-    HIP_TRY(launch_filter(h->md, h->n, h->hp.tau_p, h->max_kpad, st));
+    HIP_TRY(timed(h, PK_FILTER, st,
+                  [&] { return launch_filter(h->md, h->n, h->hp.tau_p, h->max_kpad, st); }));
     PtrTable none = make_table(h, nullptr);
-    int rc = run_group(h->proj, none, st);
+    int rc = run_group(h, h->proj, PK_PROJECTORS, none, st);
     if (rc) return rc;
     h->proj_stale = false;
     return SC_OK;
@@ -211,28 +276,61 @@ int build_projectors(sc_opt* h, hipStream_t st) {
 
 int finalize_factors(sc_opt* h, hipStream_t st) {
     PtrTable none = make_table(h, nullptr);
-    HIP_TRY(launch_rownorm(h->md, h->n, 0, h->max_kpad, st));
-    HIP_TRY(launch_normalize(h->md, h->flags_d, h->n, 0, h->max_kpad, h->max_K, st));
-    HIP_TRY(launch_rownorm(h->md, h->n, 1, h->max_kpad, st));
-    HIP_TRY(launch_normalize(h->md, h->flags_d, h->n, 1, h->max_kpad, h->max_K, st));
+    for (int which = 0; which < 2; ++which) {
+        HIP_TRY(timed(h, PK_ROWNORM, st,
+                      [&] { return launch_rownorm(h->md, h->n, which, h->max_kpad, st); }));
+        HIP_TRY(timed(h, PK_NORMALIZE, st, [&] {
+            return launch_normalize(h->md, h->flags_d, h->n, which, h->max_kpad, h->max_K, st);
+        }));
+    }
     int rc;
-    if ((rc = run_group(h->lowdin_eF, none, st))) return rc;
-    if ((rc = run_group(h->lowdin_F, none, st))) return rc;
-    if ((rc = run_group(h->lowdin_eW, none, st))) return rc;
-    if ((rc = run_group(h->lowdin_W, none, st))) return rc;
+    if ((rc = run_group(h, h->lowdin_eF, PK_LOWDIN, none, st))) return rc;
+    if ((rc = run_group(h, h->lowdin_F, PK_LOWDIN, none, st))) return rc;
+    if ((rc = run_group(h, h->lowdin_eW, PK_LOWDIN, none, st))) return rc;
+    if ((rc = run_group(h, h->lowdin_W, PK_LOWDIN, none, st))) return rc;
     return build_projectors(h, st);
 }
 
+// Algorithmic work of the Jacobi sweeps from the device counters (profiling only):
+// per active round and pair the 64x64 Gram over K (2 * 64 * 64 * K flops); per
+// applied pair the update of 64 rows of A (length K) and V (length k),
+// 2 * 64 * 64 * (K + k) flops and 8 * 64 * (K + k) + 4 * 64 * 64 bytes.
+void account_sweeps(sc_opt* h) {
+    for (int i = 0; i < h->n; ++i) {
+        const MatDev& m = h->mh[i];
+        const MatFlags& f = h->flags_h[i];
+        const double pw = kPw;
+        h->prof.flops[PK_GRAM] += (double)f.rounds_active * (m.nb / 2) * 2.0 * pw * pw * m.K;
+        h->prof.flops[PK_APPLY] += (double)f.pairs_applied * 2.0 * pw * pw * (m.K + m.k);
+        h->prof.bytes[PK_APPLY] +=
+            (double)f.pairs_applied * (8.0 * pw * (m.K + m.k) + 4.0 * pw * pw);
+        h->prof.bytes[PK_GRAM] += (double)f.rounds_active * (m.nb / 2) * 4.0 * pw * m.K;
+    }
+}
+
 int do_refresh(sc_opt* h, hipStream_t st) {
-    HIP_TRY(launch_jacobi_load(h->md, h->n, h->max_kpad, h->max_K + 128, st));
-    HIP_TRY(launch_rownorm(h->md, h->n, 0, h->max_kpad, st));
-    HIP_TRY(launch_jacobi_init_flags(h->md, h->flags_d, h->n, st));
+    HIP_TRY(timed(h, PK_LOAD, st,
+                  [&] { return launch_jacobi_load(h->md, h->n, h->max_kpad, h->max_K + 128, st); }));
+    HIP_TRY(timed(h, PK_ROWNORM, st, [&] { return launch_rownorm(h->md, h->n, 0, h->max_kpad, st); }));
+    HIP_TRY(timed(h, PK_INIT_FLAGS, st,
+                  [&] { return launch_jacobi_init_flags(h->md, h->flags_d, h->n, st); }));
     const int rps = h->max_nb - 1;  // rounds per sweep of the largest matrix
     const int max_rounds = h->hp.max_sweeps * rps;
     const int first_check = std::min(max_rounds, 4 * rps);
     for (int r = 0; r < max_rounds; ++r) {
-        HIP_TRY(launch_jacobi_round(h->md, h->flags_d, h->gi_d, h->ngi, h->si_d, h->nsi, h->ai_d,
-                                    h->nai, r, h->hp.max_sweeps, h->tol, h->n, st));
+        HIP_TRY(timed(h, PK_GRAM, st, [&] {
+            return launch_jacobi_gram(h->md, h->flags_d, h->gi_d, h->ngi, r, st);
+        }));
+        HIP_TRY(timed(h, PK_SOLVE, st, [&] {
+            return launch_jacobi_solve(h->md, h->flags_d, h->si_d, h->nsi, h->tol, st);
+        }));
+        HIP_TRY(timed(h, PK_APPLY, st, [&] {
+            return launch_jacobi_apply(h->md, h->flags_d, h->ai_d, h->nai, r, st);
+        }));
+        HIP_TRY(timed(h, PK_SWEEP_END, st, [&] {
+            return launch_jacobi_sweep_end(h->md, h->flags_d, h->n, r, h->hp.max_sweeps, h->tol,
+                                           st);
+        }));
         if (h->hp.sync_check && r + 1 >= first_check && (r + 1) % rps == 0 && r + 1 < max_rounds) {
             HIP_TRY(hipMemcpyAsync(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n,
                                    hipMemcpyDeviceToHost, st));
@@ -241,6 +339,12 @@ int do_refresh(sc_opt* h, hipStream_t st) {
             for (int i = 0; i < h->n; ++i) all = all && h->flags_h[i].done;
             if (all) break;
         }
+    }
+    if (h->prof.on) {
+        HIP_TRY(hipMemcpyAsync(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n,
+                               hipMemcpyDeviceToHost, st));
+        HIP_TRY(hipStreamSynchronize(st));
+        account_sweeps(h);
     }
     int rc = finalize_factors(h, st);
     if (rc) return rc;
@@ -466,6 +570,10 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         if ((rc = upload_group(h, *g))) return rc;
     h->stale.assign(n, 0);
     h->last_sweeps.assign(n, 0);
+    const double gsz = h->gdt == SC_BF16 ? 2.0 : 4.0, wsz = h->wdt == SC_BF16 ? 2.0 : 4.0;
+    for (int i = 0; i < n; ++i) h->total_numel += (double)h->mh[i].numel;
+    h->ema_bytes = h->total_numel * (8.0 + gsz);
+    h->adamw_bytes = h->total_numel * (gsz + 4.0 + 2.0 * wsz + 16.0);
     HIP_TRY(hipDeviceSynchronize());
     return SC_OK;
 }
@@ -474,6 +582,11 @@ void release(sc_opt* h) {
     if (!h) return;
     DeviceGuard g(h->device);
     (void)hipDeviceSynchronize();
+    for (auto& r : h->prof.recs) {
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    for (hipEvent_t e : h->prof.pool) (void)hipEventDestroy(e);
     for (void* p : h->dev_allocs) (void)hipFree(p);
     if (h->arena) (void)hipFree(h->arena);
     if (h->proj_arena) (void)hipFree(h->proj_arena);
@@ -574,8 +687,11 @@ int sc_anchor_update(sc_handle h, const void* const* G_anc, void* stream) {
     DeviceGuard g(h->device);
     hipStream_t st = (hipStream_t)stream;
     PtrTable pt = make_table(h, G_anc);
-    HIP_TRY(launch_ema(h->md, h->chunks_d, h->nchunks, pt, h->gdt == SC_BF16, h->hp.beta_anc,
-                       h->status_d + 1, st));
+    HIP_TRY(timed(h, PK_EMA, st, [&] {
+        return launch_ema(h->md, h->chunks_d, h->nchunks, pt, h->gdt == SC_BF16, h->hp.beta_anc,
+                          h->status_d + 1, st);
+    }));
+    if (h->prof.on) h->prof.bytes[PK_EMA] += h->ema_bytes;
     return do_refresh(h, st);
 }
 
@@ -601,12 +717,12 @@ int sc_step(sc_handle h, void* const* W, const void* const* G_mask, void* stream
     }
     PtrTable gt = make_table(h, G_mask);
     PtrTable wt = make_table(h, (const void* const*)W);
-    if ((rc = run_group(h->s1_nn_a, gt, st))) return rc;
-    if ((rc = run_group(h->s1_nn_b, gt, st))) return rc;
-    if ((rc = run_group(h->s1_nt, gt, st))) return rc;
-    if ((rc = run_group(h->s2_nn, gt, st))) return rc;
-    if ((rc = run_group(h->s3_tn, gt, st))) return rc;
-    if ((rc = run_group(h->s3_nn, gt, st))) return rc;
+    if ((rc = run_group(h, h->s1_nn_a, PK_STEP_GEMM1, gt, st))) return rc;
+    if ((rc = run_group(h, h->s1_nn_b, PK_STEP_GEMM1, gt, st))) return rc;
+    if ((rc = run_group(h, h->s1_nt, PK_STEP_GEMM1, gt, st))) return rc;
+    if ((rc = run_group(h, h->s2_nn, PK_STEP_GEMM2, gt, st))) return rc;
+    if ((rc = run_group(h, h->s3_tn, PK_STEP_GEMM3, gt, st))) return rc;
+    if ((rc = run_group(h, h->s3_nn, PK_STEP_GEMM3, gt, st))) return rc;
     const int64_t t = h->t + 1;
     const double lr = h->hp.lr, b1 = h->hp.beta1, b2 = h->hp.beta2;
     const double bc1 = 1.0 - std::pow(b1, (double)t);
@@ -614,10 +730,14 @@ int sc_step(sc_handle h, void* const* W, const void* const* G_mask, void* stream
     const float step_size = (float)(lr / bc1);
     const float inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
     const float lr_wd = (float)(lr * (double)h->hp.weight_decay);
-    HIP_TRY(launch_combine_adamw(h->md, h->chunks_d, h->nchunks, wt, gt, h->wdt == SC_BF16,
-                                 h->gdt == SC_BF16, h->hp.alpha, h->hp.beta1, h->hp.beta2,
-                                 h->hp.eps, step_size, inv_sqrt_bc2, lr_wd, h->keep_proj ? 1 : 0,
-                                 h->status_d, st));
+    HIP_TRY(timed(h, PK_ADAMW, st, [&] {
+        return launch_combine_adamw(h->md, h->chunks_d, h->nchunks, wt, gt, h->wdt == SC_BF16,
+                                    h->gdt == SC_BF16, h->hp.alpha, h->hp.beta1, h->hp.beta2,
+                                    h->hp.eps, step_size, inv_sqrt_bc2, lr_wd,
+                                    h->keep_proj ? 1 : 0, h->status_d, st);
+    }));
+    if (h->prof.on)
+        h->prof.bytes[PK_ADAMW] += h->adamw_bytes + (h->keep_proj ? 4.0 * h->total_numel : 0.0);
     h->t = t;
     return SC_OK;
 }
@@ -792,6 +912,59 @@ int sc_get_stats(sc_handle h, sc_stats* out, int* per_mat_sweeps) {
     }
     out->nonfinite_grad = status[0] != 0;
     out->nonfinite_anchor = status[1] != 0;
+    return SC_OK;
+}
+
+int sc_profile(sc_handle h, int enable) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    DeviceGuard g(h->device);
+    if (!h->prof.recs.empty()) {
+        HIP_TRY(hipDeviceSynchronize());
+        for (auto& r : h->prof.recs) {
+            h->prof.pool.push_back(r.a);
+            h->prof.pool.push_back(r.b);
+        }
+        h->prof.recs.clear();
+    }
+    for (int k = 0; k < PK_COUNT; ++k) {
+        h->prof.launches[k] = 0;
+        h->prof.ms[k] = h->prof.flops[k] = h->prof.bytes[k] = 0.0;
+    }
+    h->prof.on = enable != 0;
+    return SC_OK;
+}
+
+int sc_get_kernel_times(sc_handle h, sc_kernel_time* out, int max_entries, int* count) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    if (!count || (max_entries > 0 && !out))
+        return fail(SC_ERR_INVALID_ARG, "out/count is NULL");
+    DeviceGuard g(h->device);
+    HIP_TRY(hipDeviceSynchronize());
+    for (auto& r : h->prof.recs) {
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) h->prof.ms[r.kind] += ms;
+        else (void)hipGetLastError();
+        h->prof.pool.push_back(r.a);
+        h->prof.pool.push_back(r.b);
+    }
+    h->prof.recs.clear();
+    int n = 0;
+    for (int k = 0; k < PK_COUNT; ++k) {
+        if (h->prof.launches[k] == 0) continue;
+        if (n < max_entries) {
+            sc_kernel_time& t = out[n];
+            memset(&t, 0, sizeof(t));
+            snprintf(t.name, sizeof(t.name), "%s", kProfNames[k]);
+            t.launches = h->prof.launches[k];
+            t.total_ms = h->prof.ms[k];
+            t.flops = h->prof.flops[k];
+            t.bytes = h->prof.bytes[k];
+        }
+        ++n;
+    }
+    *count = n;
     return SC_OK;
 }
 

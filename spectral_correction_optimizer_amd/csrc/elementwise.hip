@@ -313,6 +313,8 @@ __global__ __launch_bounds__(256) void init_flags_kernel(const MatDev* __restric
         f.converged = 0;
         f.sweeps = 0;
         f.done = 0;
+        f.rounds_active = 0;
+        f.pairs_applied = 0;
     }
 }
 

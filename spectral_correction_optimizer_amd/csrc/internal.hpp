@@ -57,7 +57,9 @@ struct MatFlags {
     int sweeps;              // sweeps done in the current refresh
     int done;                // converged or sweep cap reached
     float floor2;            // squared column-norm floor: columns below are zero
-    int pad[3];
+    int rounds_active;       // rounds this matrix took part in (work accounting)
+    int pairs_applied;       // pair rotations applied (work accounting)
+    int pad;
 };
 
 // ---- work items ------------------------------------------------------------------
@@ -117,9 +119,14 @@ hipError_t launch_filter(const MatDev* mats, int nmat, float tau, int max_kpad, 
 
 // ---- Jacobi sweeps -------------------------------------------------------------------
 
-hipError_t launch_jacobi_round(const MatDev* mats, MatFlags* flags, const GramItem* gi, int ngi,
-                               const SolveItem* si, int nsi, const ApplyItem* ai, int nai,
-                               int round, int max_sweeps, float tol, int nmat, hipStream_t st);
+hipError_t launch_jacobi_gram(const MatDev* mats, const MatFlags* flags, const GramItem* gi,
+                              int ngi, int round, hipStream_t st);
+hipError_t launch_jacobi_solve(const MatDev* mats, MatFlags* flags, const SolveItem* si, int nsi,
+                               float tol, hipStream_t st);
+hipError_t launch_jacobi_apply(const MatDev* mats, const MatFlags* flags, const ApplyItem* ai,
+                               int nai, int round, hipStream_t st);
+hipError_t launch_jacobi_sweep_end(const MatDev* mats, MatFlags* flags, int nmat, int round,
+                                   int max_sweeps, float tol, hipStream_t st);
 
 // dst[c * ld_dst + r] = src[r * ld_src + c] for r < rows, c < cols
 hipError_t launch_transpose(const float* src, int rows, int cols, int ld_src, float* dst,

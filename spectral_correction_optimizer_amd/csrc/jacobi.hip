@@ -251,7 +251,10 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
         const int b = idx >> 6, a = idx & 63;
         R[idx] = (float)(Q[b][a] - (b == a ? 1.0 : 0.0));
     }
-    if (tid == 0) *rflag = 1;
+    if (tid == 0) {
+        *rflag = 1;
+        atomicAdd(&fl.pairs_applied, 1);
+    }
 }
 
 // ---------------------------------------------------------------------------------
@@ -322,6 +325,7 @@ __global__ void jac_sweep_end_kernel(const MatDev* __restrict__ mats, MatFlags* 
     if (i >= nmat) return;
     MatFlags& f = flags[i];
     if (f.done) return;
+    f.rounds_active += 1;
     const int nbm1 = mats[i].nb - 1;
     if (round % nbm1 != nbm1 - 1) return;
     f.sweeps += 1;
@@ -335,12 +339,26 @@ __global__ void jac_sweep_end_kernel(const MatDev* __restrict__ mats, MatFlags* 
     }
 }
 
-hipError_t launch_jacobi_round(const MatDev* mats, MatFlags* flags, const GramItem* gi, int ngi,
-                               const SolveItem* si, int nsi, const ApplyItem* ai, int nai,
-                               int round, int max_sweeps, float tol, int nmat, hipStream_t st) {
+hipError_t launch_jacobi_gram(const MatDev* mats, const MatFlags* flags, const GramItem* gi,
+                              int ngi, int round, hipStream_t st) {
     hipLaunchKernelGGL(jac_gram_kernel, dim3(ngi), dim3(256), 0, st, mats, flags, gi, round);
+    return hipGetLastError();
+}
+
+hipError_t launch_jacobi_solve(const MatDev* mats, MatFlags* flags, const SolveItem* si, int nsi,
+                               float tol, hipStream_t st) {
     hipLaunchKernelGGL(jac_solve_kernel, dim3(nsi), dim3(256), 0, st, mats, flags, si, tol);
+    return hipGetLastError();
+}
+
+hipError_t launch_jacobi_apply(const MatDev* mats, const MatFlags* flags, const ApplyItem* ai,
+                               int nai, int round, hipStream_t st) {
     hipLaunchKernelGGL(jac_apply_kernel, dim3(nai), dim3(256), 0, st, mats, flags, ai, round);
+    return hipGetLastError();
+}
+
+hipError_t launch_jacobi_sweep_end(const MatDev* mats, MatFlags* flags, int nmat, int round,
+                                   int max_sweeps, float tol, hipStream_t st) {
     hipLaunchKernelGGL(jac_sweep_end_kernel, dim3((nmat + 63) / 64), dim3(64), 0, st, mats, flags,
                        nmat, round, max_sweeps, tol);
     return hipGetLastError();
