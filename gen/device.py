@@ -26,12 +26,21 @@ def _gen(device, *key):
     return g
 
 
-def _haar(device, key, n, r):
+def _haar(device, key, n, r, max_iter=60):
+    """Orthonormal n x r factor: the polar factor Z (Z^T Z)^(-1/2) of a Gaussian
+    Z (Haar distributed), by the Newton-Schulz iteration X <- X (3I - X^T X) / 2
+    started from Z / (sqrt(n) + sqrt(r)) (spectral norm below sqrt(3)).  Uses
+    matrix products only, accurate to float32 rounding."""
     z = torch.randn((n, r), generator=_gen(device, *key), device=device, dtype=torch.float32)
-    q, rr = torch.linalg.qr(z)
-    sgn = torch.sign(torch.diagonal(rr))
-    sgn[sgn == 0] = 1.0
-    return (q * sgn).contiguous()
+    x = z / (n ** 0.5 + r ** 0.5)
+    eye = torch.eye(r, device=device, dtype=torch.float32)
+    for _ in range(max_iter):
+        g = x.t().contiguous() @ x
+        err = torch.linalg.matrix_norm(g - eye).item() / r ** 0.5
+        x = 1.5 * x - 0.5 * (x @ g)
+        if err < 1e-6:
+            break
+    return x.contiguous()
 
 
 class DeviceMatrixInputs:

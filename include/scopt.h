@@ -64,11 +64,14 @@ typedef struct {
     float jacobi_tol;   /* rotation threshold |a_p.a_q| / (|a_p||a_q|); 0 = default 16 * 2^-24 */
     int sync_check;     /* 1: poll convergence flags on the host (stops early);
                            0: fully asynchronous, always max_sweeps sweeps */
+    int warm_start;     /* 1: a refresh starts its sweeps from the previous factors
+                           (A = M V_prev); 0: always from A = M, V = I */
 } sc_hparams;
 
 /* Fill `hp` with the defaults of the pages' training strategy:
  * tau_p 1e-3, alpha 0.3, beta_anc 0.9, lr 2e-5, betas (0.9, 0.999), eps 1e-8,
- * weight_decay 0.01, max_sweeps 30, jacobi_tol 0 (default), sync_check 1. */
+ * weight_decay 0.01, max_sweeps 30, jacobi_tol 0 (default), sync_check 1,
+ * warm_start 1. */
 void sc_default_hparams(sc_hparams* hp);
 
 /* Create an optimizer over n_mats weight matrices of shapes rows[i] x cols[i]

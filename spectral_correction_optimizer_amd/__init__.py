@@ -48,7 +48,7 @@ class HParams(ctypes.Structure):
                 ("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
                 ("max_sweeps", ctypes.c_int), ("jacobi_tol", ctypes.c_float),
-                ("sync_check", ctypes.c_int)]
+                ("sync_check", ctypes.c_int), ("warm_start", ctypes.c_int)]
 
 
 class KernelTime(ctypes.Structure):

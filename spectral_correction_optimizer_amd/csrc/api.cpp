@@ -72,12 +72,12 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 enum ProfKind {
     PK_EMA, PK_LOAD, PK_ROWNORM, PK_INIT_FLAGS, PK_GRAM, PK_SOLVE, PK_APPLY, PK_SWEEP_END,
     PK_NORMALIZE, PK_LOWDIN, PK_FILTER, PK_PROJECTORS, PK_STEP_GEMM1, PK_STEP_GEMM2,
-    PK_STEP_GEMM3, PK_ADAMW, PK_COUNT
+    PK_STEP_GEMM3, PK_ADAMW, PK_WARM, PK_COUNT
 };
 const char* const kProfNames[PK_COUNT] = {
     "ema", "jacobi_load", "rownorm", "jacobi_init", "jacobi_gram", "jacobi_solve",
     "jacobi_apply", "jacobi_sweep_end", "normalize", "lowdin_gemm", "filter", "projector_gemm",
-    "step_gemm1", "step_gemm2", "step_gemm3", "combine_adamw"};
+    "step_gemm1", "step_gemm2", "step_gemm3", "combine_adamw", "warm_start"};
 
 // Optional kernel timing: HIP events recorded around every launch on the
 // caller's stream; totals are folded in by sc_get_kernel_times.
@@ -122,6 +122,8 @@ struct sc_opt {
     int max_nb = 2, max_kpad = 64, max_K = 1, max_k = 1;
     // refresh GEMMs
     GemmGroup lowdin_eF, lowdin_F, lowdin_eW, lowdin_W, proj;
+    GemmGroup warm_nt, warm_nn;  // warm start: A_rows = W M^T (m >= n) or W M (m < n)
+    bool have_factors = false;   // W holds orthonormal rows from a refresh / sc_set_factors
     // step GEMMs
     GemmGroup s1_nn_a, s1_nn_b, s1_nt, s2_nn, s3_tn, s3_nn;
     int64_t t = 0;
@@ -309,8 +311,18 @@ void account_sweeps(sc_opt* h) {
 }
 
 int do_refresh(sc_opt* h, hipStream_t st) {
-    HIP_TRY(timed(h, PK_LOAD, st,
-                  [&] { return launch_jacobi_load(h->md, h->n, h->max_kpad, h->max_K + 128, st); }));
+    if (h->hp.warm_start && h->have_factors) {
+        // Start the sweeps from the previous factors: V = W_prev, A = M V_prev.
+        HIP_TRY(timed(h, PK_WARM, st, [&] { return launch_jacobi_warm(h->md, h->n, st); }));
+        PtrTable none = make_table(h, nullptr);
+        int rc;
+        if ((rc = run_group(h, h->warm_nt, PK_WARM, none, st))) return rc;
+        if ((rc = run_group(h, h->warm_nn, PK_WARM, none, st))) return rc;
+    } else {
+        HIP_TRY(timed(h, PK_LOAD, st, [&] {
+            return launch_jacobi_load(h->md, h->n, h->max_kpad, h->max_K + 128, st);
+        }));
+    }
     HIP_TRY(timed(h, PK_ROWNORM, st, [&] { return launch_rownorm(h->md, h->n, 0, h->max_kpad, st); }));
     HIP_TRY(timed(h, PK_INIT_FLAGS, st,
                   [&] { return launch_jacobi_init_flags(h->md, h->flags_d, h->n, st); }));
@@ -348,6 +360,7 @@ int do_refresh(sc_opt* h, hipStream_t st) {
     }
     int rc = finalize_factors(h, st);
     if (rc) return rc;
+    h->have_factors = true;
     h->refreshes += 1;
     for (auto& s : h->stale) s = 0;
     h->any_stale = false;
@@ -506,6 +519,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
     h->s1_nt.tb = true;    // wide: A = G, B = F^T
     h->s1_nt.abf = gbf;
     h->s3_tn.ta = true;
+    h->warm_nt.tb = true;
     for (int i = 0; i < n; ++i) {
         MatDev& m = h->mh[i];
         // Loewdin re-orthogonalization of the unit rows of A (-> F) and V (-> W):
@@ -528,6 +542,14 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         p.alpha = -0.5f;
         p.beta = 1.0f;
         h->lowdin_W.h.push_back(p);
+        // warm start: rows of A = W op(M): m >= n: a_j = M w_j; m < n: a_j = M^T w_j
+        if (m.tall) {
+            p = make_prob(m.W, m.k, m.Manc, m.n, m.A, m.K_ld, m.k, m.m, m.n);
+            h->warm_nt.h.push_back(p);
+        } else {
+            p = make_prob(m.W, m.k, m.Manc, m.n, m.A, m.K_ld, m.k, m.n, m.m);
+            h->warm_nn.h.push_back(p);
+        }
         // projectors X^T diag(d) X
         const bool square = m.m == m.n;
         if (square) {
@@ -565,7 +587,8 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             h->s3_nn.h.push_back(p);
         }
     }
-    for (GemmGroup* g : {&h->lowdin_eF, &h->lowdin_F, &h->lowdin_eW, &h->lowdin_W, &h->proj,
+    for (GemmGroup* g : {&h->warm_nt, &h->warm_nn, &h->lowdin_eF, &h->lowdin_F, &h->lowdin_eW,
+                         &h->lowdin_W, &h->proj,
                          &h->s1_nn_a, &h->s1_nn_b, &h->s1_nt, &h->s2_nn, &h->s3_tn, &h->s3_nn})
         if ((rc = upload_group(h, *g))) return rc;
     h->stale.assign(n, 0);
@@ -621,6 +644,7 @@ void sc_default_hparams(sc_hparams* hp) {
     hp->max_sweeps = 30;
     hp->jacobi_tol = 0.0f;
     hp->sync_check = 1;
+    hp->warm_start = 1;
 }
 
 const char* sc_last_error(void) { return g_err.c_str(); }
@@ -833,6 +857,9 @@ int sc_set_factors(sc_handle h, int idx, const float* U, const float* s, const f
     h->stale[idx] = 0;
     h->any_stale = false;
     for (char c : h->stale) h->any_stale = h->any_stale || c;
+    // other matrices may still hold zero factors: warm start only once every
+    // matrix has had factors installed or computed
+    h->have_factors = h->have_factors || h->n == 1;
     return build_projectors(h, st);
 }
 

@@ -259,6 +259,29 @@ hipError_t launch_jacobi_load(const MatDev* mats, int nmat, int max_kpad, int ma
     return hipGetLastError();
 }
 
+// Warm start of a refresh from the previous factors: V <- [W 0; 0 I] (rows of
+// the previous accumulated-side singular vectors) and zero padding rows of A
+// (the rows j < k of A are then written by the GEMM A_rows = W op(M)).
+__global__ __launch_bounds__(256) void jacobi_warm_kernel(const MatDev* __restrict__ mats) {
+    const MatDev& md = mats[blockIdx.y];
+    const int64_t nv = (int64_t)md.kpad * md.kpad;
+    const int64_t na = (int64_t)(md.kpad - md.k) * md.K_ld;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nv + na;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        if (i < nv) {
+            const int j = (int)(i / md.kpad), x = (int)(i % md.kpad);
+            md.V[i] = (j < md.k && x < md.k) ? md.W[(int64_t)j * md.k + x] : (j == x ? 1.0f : 0.0f);
+        } else {
+            md.A[(int64_t)md.k * md.K_ld + (i - nv)] = 0.0f;
+        }
+    }
+}
+
+hipError_t launch_jacobi_warm(const MatDev* mats, int nmat, hipStream_t st) {
+    hipLaunchKernelGGL(jacobi_warm_kernel, dim3(512, nmat), dim3(256), 0, st, mats);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------------
 // Row norms in float64 with a fixed reduction order (deterministic).
 // which = 0: rows j < kpad of A (length K_ld); 1: rows j < k of V (length k).

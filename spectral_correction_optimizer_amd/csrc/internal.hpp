@@ -108,6 +108,8 @@ hipError_t launch_combine_adamw(const MatDev* mats, const Chunk* chunks, int nch
 // A <- M (copy or transpose), V <- I, for matrices in mat_list.
 hipError_t launch_jacobi_load(const MatDev* mats, int nmat, int max_kpad, int max_K,
                               hipStream_t st);
+// Warm start: V <- previous W (padded with identity), zero padding rows of A.
+hipError_t launch_jacobi_warm(const MatDev* mats, int nmat, hipStream_t st);
 // norm2[j] = sum_x X[j][x]^2 (fp64) for the rows of A (which=0) or V (which=1)
 hipError_t launch_rownorm(const MatDev* mats, int nmat, int which, int max_kpad, hipStream_t st);
 // floor2 = (2^-24)^2 * sum_j norm2[j]; clears sweep flags
