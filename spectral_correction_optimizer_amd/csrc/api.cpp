@@ -113,12 +113,23 @@ struct sc_opt {
     char* proj_arena = nullptr;
     Chunk* chunks_d = nullptr;
     int nchunks = 0;
-    GramItem* gi_d = nullptr;
-    int ngi = 0;
-    SolveItem* si_d = nullptr;
-    int nsi = 0;
-    ApplyItem* ai_d = nullptr;
-    int nai = 0;
+    // Jacobi work lists of the two matrix groups whose rounds run on two
+    // internal streams (one group's pair solves overlap the other's Gram /
+    // rotation kernels); matrices are assigned to groups by decreasing work.
+    struct JGroup {
+        GramItem* gi = nullptr;
+        int ngi = 0;
+        SolveItem* si = nullptr;
+        int nsi = 0;
+        ApplyItem* ai = nullptr;
+        int nai = 0;
+        int* mats = nullptr;
+        int nmat = 0;
+        int max_nb = 2;
+        hipStream_t st = nullptr;
+        hipEvent_t join = nullptr;
+    } jg[2];
+    hipEvent_t fork = nullptr;
     int max_nb = 2, max_kpad = 64, max_K = 1, max_k = 1;
     // refresh GEMMs
     GemmGroup lowdin_eF, lowdin_F, lowdin_eW, lowdin_W, proj;
@@ -329,28 +340,41 @@ int do_refresh(sc_opt* h, hipStream_t st) {
     const int rps = h->max_nb - 1;  // rounds per sweep of the largest matrix
     const int max_rounds = h->hp.max_sweeps * rps;
     const int first_check = std::min(max_rounds, 4 * rps);
+    HIP_TRY(hipEventRecord(h->fork, st));
+    for (auto& G : h->jg)
+        if (G.nmat) HIP_TRY(hipStreamWaitEvent(G.st, h->fork, 0));
     for (int r = 0; r < max_rounds; ++r) {
-        HIP_TRY(timed(h, PK_GRAM, st, [&] {
-            return launch_jacobi_gram(h->md, h->flags_d, h->gi_d, h->ngi, r, st);
-        }));
-        HIP_TRY(timed(h, PK_SOLVE, st, [&] {
-            return launch_jacobi_solve(h->md, h->flags_d, h->si_d, h->nsi, h->tol, st);
-        }));
-        HIP_TRY(timed(h, PK_APPLY, st, [&] {
-            return launch_jacobi_apply(h->md, h->flags_d, h->ai_d, h->nai, r, st);
-        }));
-        HIP_TRY(timed(h, PK_SWEEP_END, st, [&] {
-            return launch_jacobi_sweep_end(h->md, h->flags_d, h->n, r, h->hp.max_sweeps, h->tol,
-                                           st);
-        }));
+        for (auto& G : h->jg) {
+            if (!G.nmat || r >= h->hp.max_sweeps * (G.max_nb - 1)) continue;
+            hipStream_t gs = G.st;
+            HIP_TRY(timed(h, PK_GRAM, gs, [&] {
+                return launch_jacobi_gram(h->md, h->flags_d, G.gi, G.ngi, r, gs);
+            }));
+            HIP_TRY(timed(h, PK_SOLVE, gs, [&] {
+                return launch_jacobi_solve(h->md, h->flags_d, G.si, G.nsi, h->tol, gs);
+            }));
+            HIP_TRY(timed(h, PK_APPLY, gs, [&] {
+                return launch_jacobi_apply(h->md, h->flags_d, G.ai, G.nai, r, gs);
+            }));
+            HIP_TRY(timed(h, PK_SWEEP_END, gs, [&] {
+                return launch_jacobi_sweep_end(h->md, h->flags_d, G.mats, G.nmat, r,
+                                               h->hp.max_sweeps, h->tol, gs);
+            }));
+        }
         if (h->hp.sync_check && r + 1 >= first_check && (r + 1) % rps == 0 && r + 1 < max_rounds) {
-            HIP_TRY(hipMemcpyAsync(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n,
-                                   hipMemcpyDeviceToHost, st));
-            HIP_TRY(hipStreamSynchronize(st));
+            for (auto& G : h->jg)
+                if (G.nmat) HIP_TRY(hipStreamSynchronize(G.st));
+            HIP_TRY(hipMemcpy(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n,
+                              hipMemcpyDeviceToHost));
             bool all = true;
             for (int i = 0; i < h->n; ++i) all = all && h->flags_h[i].done;
             if (all) break;
         }
+    }
+    for (auto& G : h->jg) {
+        if (!G.nmat) continue;
+        HIP_TRY(hipEventRecord(G.join, G.st));
+        HIP_TRY(hipStreamWaitEvent(st, G.join, 0));
     }
     if (h->prof.on) {
         HIP_TRY(hipMemcpyAsync(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n,
@@ -479,19 +503,21 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
 
     // work lists
     std::vector<Chunk> ch;
-    std::vector<GramItem> gi;
-    std::vector<SolveItem> si;
-    std::vector<ApplyItem> ai;
     for (int i = 0; i < n; ++i) {
         const MatDev& m = h->mh[i];
         for (int64_t off0 = 0; off0 < m.numel; off0 += kChunk)
             ch.push_back(Chunk{i, off0, (int)std::min<int64_t>(kChunk, m.numel - off0)});
-        for (int s = 0; s < m.nb / 2; ++s) {
-            for (int sp = 0; sp < m.nsplit; ++sp) gi.push_back(GramItem{i, s, sp});
-            si.push_back(SolveItem{i, s});
-            for (int c = 0; c < m.K_ld / 128; ++c) ai.push_back(ApplyItem{i, s, 0, c});
-            for (int c = 0; c < (m.kpad + 127) / 128; ++c) ai.push_back(ApplyItem{i, s, 1, c});
-        }
+    }
+    std::vector<int> order(n);
+    for (int i = 0; i < n; ++i) order[i] = i;
+    auto work = [&](int i) { return (double)h->mh[i].kpad * (h->mh[i].K_ld + h->mh[i].kpad); };
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return work(a) > work(b); });
+    std::vector<int> gm[2];
+    double load[2] = {0.0, 0.0};
+    for (int i : order) {
+        const int g = load[0] <= load[1] ? 0 : 1;
+        gm[g].push_back(i);
+        load[g] += work(i);
     }
     auto upload = [&](auto& vec, auto** dst, int* cnt) -> int {
         *cnt = (int)vec.size();
@@ -505,9 +531,32 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
     };
     int rc;
     if ((rc = upload(ch, &h->chunks_d, &h->nchunks))) return rc;
-    if ((rc = upload(gi, &h->gi_d, &h->ngi))) return rc;
-    if ((rc = upload(si, &h->si_d, &h->nsi))) return rc;
-    if ((rc = upload(ai, &h->ai_d, &h->nai))) return rc;
+    for (int g = 0; g < 2; ++g) {
+        std::vector<GramItem> gi;
+        std::vector<SolveItem> si;
+        std::vector<ApplyItem> ai;
+        auto& G = h->jg[g];
+        std::sort(gm[g].begin(), gm[g].end());
+        for (int i : gm[g]) {
+            const MatDev& m = h->mh[i];
+            G.max_nb = std::max(G.max_nb, m.nb);
+            for (int s = 0; s < m.nb / 2; ++s) {
+                for (int sp = 0; sp < m.nsplit; ++sp) gi.push_back(GramItem{i, s, sp});
+                si.push_back(SolveItem{i, s});
+                for (int c = 0; c < m.K_ld / 128; ++c) ai.push_back(ApplyItem{i, s, 0, c});
+                for (int c = 0; c < (m.kpad + 127) / 128; ++c) ai.push_back(ApplyItem{i, s, 1, c});
+            }
+        }
+        if ((rc = upload(gi, &G.gi, &G.ngi))) return rc;
+        if ((rc = upload(si, &G.si, &G.nsi))) return rc;
+        if ((rc = upload(ai, &G.ai, &G.nai))) return rc;
+        if ((rc = upload(gm[g], &G.mats, &G.nmat))) return rc;
+        if (G.nmat > 0) {
+            HIP_TRY(hipStreamCreateWithFlags(&G.st, hipStreamNonBlocking));
+            HIP_TRY(hipEventCreateWithFlags(&G.join, hipEventDisableTiming));
+        }
+    }
+    HIP_TRY(hipEventCreateWithFlags(&h->fork, hipEventDisableTiming));
 
     // GEMM problem tables
     const bool gbf = h->gdt == SC_BF16;
@@ -610,6 +659,11 @@ void release(sc_opt* h) {
         (void)hipEventDestroy(r.b);
     }
     for (hipEvent_t e : h->prof.pool) (void)hipEventDestroy(e);
+    for (auto& G : h->jg) {
+        if (G.st) (void)hipStreamDestroy(G.st);
+        if (G.join) (void)hipEventDestroy(G.join);
+    }
+    if (h->fork) (void)hipEventDestroy(h->fork);
     for (void* p : h->dev_allocs) (void)hipFree(p);
     if (h->arena) (void)hipFree(h->arena);
     if (h->proj_arena) (void)hipFree(h->proj_arena);

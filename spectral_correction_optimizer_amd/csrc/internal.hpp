@@ -127,8 +127,9 @@ hipError_t launch_jacobi_solve(const MatDev* mats, MatFlags* flags, const SolveI
                                float tol, hipStream_t st);
 hipError_t launch_jacobi_apply(const MatDev* mats, const MatFlags* flags, const ApplyItem* ai,
                                int nai, int round, hipStream_t st);
-hipError_t launch_jacobi_sweep_end(const MatDev* mats, MatFlags* flags, int nmat, int round,
-                                   int max_sweeps, float tol, hipStream_t st);
+hipError_t launch_jacobi_sweep_end(const MatDev* mats, MatFlags* flags, const int* mat_idx,
+                                   int nmat, int round, int max_sweeps, float tol,
+                                   hipStream_t st);
 
 // dst[c * ld_dst + r] = src[r * ld_src + c] for r < rows, c < cols
 hipError_t launch_transpose(const float* src, int rows, int cols, int ld_src, float* dst,

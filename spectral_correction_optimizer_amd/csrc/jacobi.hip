@@ -320,9 +320,11 @@ __global__ __launch_bounds__(256) void jac_apply_kernel(const MatDev* __restrict
 // End-of-round bookkeeping: a matrix whose sweep ended this round is
 // converged when nothing above tolerance was seen during the sweep.
 __global__ void jac_sweep_end_kernel(const MatDev* __restrict__ mats, MatFlags* __restrict__ flags,
-                                     int nmat, int round, int max_sweeps, float tol) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= nmat) return;
+                                     const int* __restrict__ mat_idx, int nmat, int round,
+                                     int max_sweeps, float tol) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= nmat) return;
+    const int i = mat_idx[t];
     MatFlags& f = flags[i];
     if (f.done) return;
     f.rounds_active += 1;
@@ -357,10 +359,11 @@ hipError_t launch_jacobi_apply(const MatDev* mats, const MatFlags* flags, const 
     return hipGetLastError();
 }
 
-hipError_t launch_jacobi_sweep_end(const MatDev* mats, MatFlags* flags, int nmat, int round,
-                                   int max_sweeps, float tol, hipStream_t st) {
+hipError_t launch_jacobi_sweep_end(const MatDev* mats, MatFlags* flags, const int* mat_idx,
+                                   int nmat, int round, int max_sweeps, float tol,
+                                   hipStream_t st) {
     hipLaunchKernelGGL(jac_sweep_end_kernel, dim3((nmat + 63) / 64), dim3(64), 0, st, mats, flags,
-                       nmat, round, max_sweeps, tol);
+                       mat_idx, nmat, round, max_sweeps, tol);
     return hipGetLastError();
 }
 
