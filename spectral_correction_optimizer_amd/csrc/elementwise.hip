@@ -94,8 +94,12 @@ __device__ __forceinline__ float adam_elem(float G, float Gf, float& m, float& v
     m = fmaf(a.b1, m, a.omb1 * g);
     v = fmaf(a.b2, v, a.omb2 * (g * g));
     float denom = fmaf(sqrtf(v), a.inv_sqrt_bc2, a.eps);
-    float w1 = fmaf(-a.lr_wd, w, w);
-    return w1 - a.step_size * (m / denom);
+    // Form the whole update first (|u| << ulp(w), so its own rounding is
+    // negligible) and round at w's scale once: W - (lr wd W + step m / denom).
+    // Rounding w - lr wd w separately would add a second w-scale rounding per
+    // step and let the stored weights drift from the exactly rounded values.
+    float u = fmaf(a.lr_wd, w, a.step_size * (m / denom));
+    return w - u;
 }
 
 template <typename WT>
