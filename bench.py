@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--tau", type=float, default=None, help="override tau_p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true")
+    ap.add_argument("--profile-timed", action="store_true",
+                    help="time kernels inside the timed region itself (serializes the two "
+                         "Jacobi streams) instead of in one extra pass after it")
     ap.add_argument("--max-sweeps", type=int, default=30)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 3 times (to scale HBM "
@@ -63,6 +66,32 @@ def copy_calibration(nbytes):
     torch.cuda.synchronize(dev)
     print(json.dumps({"copy_calibration_bytes_per_copy": n * 4, "copies": 3,
                       "read_bytes": n * 4, "write_bytes": n * 4}), flush=True)
+
+
+# HBM bytes per launch of a kernel family from rocprofv3 counter passes
+# (FETCH_SIZE x read calibration + WRITE_SIZE x write calibration, calibrated
+# on a plain device copy of known size), valid only for the kernel source they
+# were taken on (sha256 of the file); otherwise reported as null.
+TRAFFIC = {
+    "jacobi_gram": {"source": "jacobi.hip", "sha256": "9edf0977cf3d52c449805380ada93d9c8de3d47dac605cf664d86065be6efff2",
+        "bytes_per_launch": 1.64748e+09},
+    "jacobi_apply": {"source": "jacobi.hip", "sha256": "9edf0977cf3d52c449805380ada93d9c8de3d47dac605cf664d86065be6efff2",
+        "bytes_per_launch": 2.27683e+09},
+    "combine_adamw": {"source": "elementwise.hip", "sha256": "e4a48da8a49650e6813f3104ffd6be0fdea1368406e796c113e935ffc8229e55",
+        "bytes_per_launch": 3.11482e+10},
+    "ema": {"source": "elementwise.hip", "sha256": "e4a48da8a49650e6813f3104ffd6be0fdea1368406e796c113e935ffc8229e55",
+        "bytes_per_launch": 1.16866e+10},
+}
+
+
+def traffic_for(name):
+    import hashlib
+    t = TRAFFIC.get(name)
+    if not t:
+        return None
+    src = os.path.join(ROOT, "spectral_correction_optimizer_amd", "csrc", t["source"])
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    return t["bytes_per_launch"] if h == t["sha256"] else None
 
 
 def flops_step_chain(m, n):
@@ -141,7 +170,8 @@ def main():
     if args.tau is not None:
         hp["tau_p"] = args.tau
     shapes, ids = wl["shapes"], wl["ids"]
-    total_iters = args.warmup + args.steps
+    extra_pass = not args.no_kernel_times and not args.profile_timed
+    total_iters = args.warmup + args.steps + (1 if extra_pass else 0)
 
     t_gen = time.perf_counter()
     M0, W, G_anc, G_mask = [], [], [[] for _ in range(total_iters)], [[] for _ in range(total_iters)]
@@ -169,7 +199,7 @@ def main():
         print(f"# warmup {k} done", file=sys.stderr, flush=True)
     torch.cuda.synchronize(dev)
 
-    if not args.no_kernel_times:
+    if args.profile_timed:
         opt.profile(True)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -189,8 +219,23 @@ def main():
     refresh_ms = [a.elapsed_time(b) for a, b, _ in ev]
     step_ms = [b.elapsed_time(c) for _, b, c in ev]
     st = opt.stats()
-    kt = opt.kernel_times() if not args.no_kernel_times else {}
-    opt.profile(False)
+    kt = {}
+    if args.profile_timed:
+        kt = opt.kernel_times()
+        opt.profile(False)
+    elif extra_pass:
+        # one more pass with per-kernel event timing (Jacobi rounds serialized
+        # on the caller's stream), outside the timed region
+        k = args.warmup + args.steps
+        opt.profile(True)
+        opt.anchor_update(G_anc[k])
+        opt.step(W, G_mask[k])
+        kt = opt.kernel_times()
+        opt.profile(False)
+    sweeps_by_shape = {}
+    for (m, n), sw in zip(shapes, st["sweeps"]):
+        key = f"{m}x{n}"
+        sweeps_by_shape[key] = max(sweeps_by_shape.get(key, 0), sw)
 
     ms_per_pass = wall * 1e3 / args.steps
     r_med, s_med = statistics.median(refresh_ms), statistics.median(step_ms)
@@ -214,12 +259,12 @@ def main():
             ach = d["bytes"] / d["launches"] / per_launch_s / 1e9
             roofline = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1),
                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                        "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None}
+                        "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic_for(name)}
         else:
             ach = d["flops"] / d["launches"] / per_launch_s / 1e12
             roofline = {"kernel": name, "bound": "mfma", "achieved": round(ach, 2),
                         "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(ach / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": None}
+                        "frac": round(ach / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": traffic_for(name)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -249,6 +294,9 @@ def main():
         "amortized_step_ms_anchor_every_25": round(s_med + r_med / 25.0, 3),
         "step_chain_tflops": round(chain_flops / (s_med * 1e9), 2),
         "jacobi_sweeps_max": st["sweeps_max"],
+        "jacobi_sweeps_by_shape": sweeps_by_shape,
+        "kernel_times_source": ("timed region" if args.profile_timed else
+                                "one extra pass after the timed region, Jacobi rounds serialized"),
         "jacobi_not_converged": st["not_converged"],
         "roofline": roofline,
         "cpu_baseline": cpu,

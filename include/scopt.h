@@ -171,7 +171,9 @@ int sc_get_stats(sc_handle h, sc_stats* out, int* per_mat_sweeps);
  * handle is bracketed by a pair of HIP events on the launch stream (small
  * host overhead per launch; device timing is unaffected).  Enabling or
  * disabling resets the accumulated totals.  A refresh run with timing on also
- * synchronizes the stream once after its sweeps to read the work counters. */
+ * synchronizes the stream once after its sweeps to read the work counters, and
+ * runs all Jacobi rounds on the caller's stream (without timing they are split
+ * over two internal streams so that independent matrices overlap). */
 int sc_profile(sc_handle h, int enable);
 
 typedef struct {

@@ -340,13 +340,18 @@ int do_refresh(sc_opt* h, hipStream_t st) {
     const int rps = h->max_nb - 1;  // rounds per sweep of the largest matrix
     const int max_rounds = h->hp.max_sweeps * rps;
     const int first_check = std::min(max_rounds, 4 * rps);
-    HIP_TRY(hipEventRecord(h->fork, st));
-    for (auto& G : h->jg)
-        if (G.nmat) HIP_TRY(hipStreamWaitEvent(G.st, h->fork, 0));
+    // With kernel timing on, both groups run on the caller's stream so that
+    // every kernel's events bracket it alone (no overlap between groups).
+    const bool split = !h->prof.on;
+    if (split) {
+        HIP_TRY(hipEventRecord(h->fork, st));
+        for (auto& G : h->jg)
+            if (G.nmat) HIP_TRY(hipStreamWaitEvent(G.st, h->fork, 0));
+    }
     for (int r = 0; r < max_rounds; ++r) {
         for (auto& G : h->jg) {
             if (!G.nmat || r >= h->hp.max_sweeps * (G.max_nb - 1)) continue;
-            hipStream_t gs = G.st;
+            hipStream_t gs = split ? G.st : st;
             HIP_TRY(timed(h, PK_GRAM, gs, [&] {
                 return launch_jacobi_gram(h->md, h->flags_d, G.gi, G.ngi, r, gs);
             }));
@@ -363,7 +368,7 @@ int do_refresh(sc_opt* h, hipStream_t st) {
         }
         if (h->hp.sync_check && r + 1 >= first_check && (r + 1) % rps == 0 && r + 1 < max_rounds) {
             for (auto& G : h->jg)
-                if (G.nmat) HIP_TRY(hipStreamSynchronize(G.st));
+                if (G.nmat) HIP_TRY(hipStreamSynchronize(split ? G.st : st));
             HIP_TRY(hipMemcpy(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n,
                               hipMemcpyDeviceToHost));
             bool all = true;
@@ -372,7 +377,7 @@ int do_refresh(sc_opt* h, hipStream_t st) {
         }
     }
     for (auto& G : h->jg) {
-        if (!G.nmat) continue;
+        if (!G.nmat || !split) continue;
         HIP_TRY(hipEventRecord(G.join, G.st));
         HIP_TRY(hipStreamWaitEvent(st, G.join, 0));
     }
