@@ -262,8 +262,12 @@ __global__ __launch_bounds__(256) void jac_apply_kernel(const MatDev* __restrict
                                                         const MatFlags* __restrict__ flags,
                                                         const ApplyItem* __restrict__ items,
                                                         int round) {
+    // A workgroup updates 64 rows x 128 columns; wave w owns columns
+    // [x0 + 32 w, x0 + 32 w + 32).  Only R goes through LDS: each lane loads its
+    // column's 32 rows of one parity straight into registers, which are exactly
+    // the MFMA B operands it needs (B[k][j] = X[b][n], lane half hl supplies
+    // b = kb + hl), so many loads are in flight and LDS stays small.
     __shared__ float Rs[PW][PW + 32];
-    __shared__ float Xs[PW][APPLY_NC + 32];
     const ApplyItem it = items[blockIdx.x];
     if (flags[it.mat].done) return;
     const MatDev& md = mats[it.mat];
@@ -271,27 +275,27 @@ __global__ __launch_bounds__(256) void jac_apply_kernel(const MatDev* __restrict
     int bI, bJ;
     rr_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
     float* base = it.which == 0 ? md.A : md.V;
-    const int ld = it.which == 0 ? md.K_ld : md.kpad;
+    const int ld = it.which == 0 ? md.K_ld : md.kpad;  // multiple of 64
     const int x0 = it.chunk * APPLY_NC;
-    const int ncols = min(APPLY_NC, ld - x0);  // multiple of 4 (ld is a multiple of 64)
 
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int hl = lane >> 5, ll = lane & 31;
+    const int n = x0 + wave * 32 + ll;
+    const bool active = x0 + wave * 32 < ld;  // a wave's 32 columns are all in or all out
+    float xb[PW / 2];
+    if (active) {
+#pragma unroll
+        for (int s = 0; s < PW / 2; ++s)
+            xb[s] = base[(int64_t)pair_row(bI, bJ, hl + 2 * s) * ld + n];
+    }
     const float* R = md.rot + (int64_t)it.slot * PW * PW;
     for (int idx = threadIdx.x; idx < PW * PW / 4; idx += 256) {
         const int b = idx >> 4, a4 = (idx & 15) * 4;
         *(float4*)&Rs[b][a4] = *(const float4*)(R + b * PW + a4);
     }
-    for (int idx = threadIdx.x; idx < PW * APPLY_NC / 4; idx += 256) {
-        const int rho = idx >> 5, c4 = (idx & 31) * 4;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (c4 < ncols)
-            v = *(const float4*)(base + (int64_t)pair_row(bI, bJ, rho) * ld + x0 + c4);
-        *(float4*)&Xs[rho][c4] = v;
-    }
     __syncthreads();
+    if (!active) return;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int ta = (wave >> 1) * 32, tn = (wave & 1) * 64;
-    const int hl = lane >> 5, ll = lane & 31;
     v16f acc0, acc1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -300,19 +304,20 @@ __global__ __launch_bounds__(256) void jac_apply_kernel(const MatDev* __restrict
     }
 #pragma unroll
     for (int kb = 0; kb < PW; kb += 2) {
-        const float a = Rs[kb + hl][ta + ll];
-        const float x0v = Xs[kb + hl][tn + ll];
-        const float x1v = Xs[kb + hl][tn + 32 + ll];
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, x0v, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a, x1v, acc1, 0, 0, 0);
+        const float a0 = Rs[kb + hl][ll];
+        const float a1 = Rs[kb + hl][32 + ll];
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, xb[kb >> 1], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, xb[kb >> 1], acc1, 0, 0, 0);
     }
+    // X_new[a][n] = X[a][n] + acc: each lane re-reads (from cache) exactly the
+    // elements it then overwrites.
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int arow = ta + 8 * (r >> 2) + 4 * hl + (r & 3);
-        float* dst = base + (int64_t)pair_row(bI, bJ, arow) * ld + x0;
-        const int c0 = tn + ll, c1 = tn + 32 + ll;
-        if (c0 < ncols) dst[c0] = Xs[arow][c0] + acc0[r];
-        if (c1 < ncols) dst[c1] = Xs[arow][c1] + acc1[r];
+        const int a = 8 * (r >> 2) + 4 * hl + (r & 3);
+        float* p0 = base + (int64_t)pair_row(bI, bJ, a) * ld + n;
+        float* p1 = base + (int64_t)pair_row(bI, bJ, a + 32) * ld + n;
+        *p0 = *p0 + acc0[r];
+        *p1 = *p1 + acc1[r];
     }
 }
 
