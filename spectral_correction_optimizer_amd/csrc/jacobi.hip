@@ -32,7 +32,6 @@ namespace {
 
 constexpr int PW = kPw;          // 64 rows per pair block
 constexpr int KC = 32;           // K columns per LDS stage
-constexpr int XS = PW + 32;      // LDS row stride of the k-major X tile (96)
 constexpr int CHUNK = 256;       // fp32 accumulation length before folding into fp64
 constexpr int APPLY_NC = 128;    // columns per apply workgroup
 
@@ -43,11 +42,32 @@ __device__ __forceinline__ int pair_row(int blkI, int blkJ, int rho) {
 }  // namespace
 
 // ---------------------------------------------------------------------------------
+// Pair Gram G = X X^T (64 x 64, X = the pair's 64 rows of A over one K split).
+// Only the 10 upper-triangle 16x16 tiles are computed (v_mfma_f32_16x16x4_f32),
+// 3/3/2/2 per wave, and mirrored on output.  For X X^T the A and B operands of
+// a tile are strips of the same rows, so a wave reads each of its strips once
+// per k-step.  LDS holds X k-major with the row index XOR-swizzled by
+// 8 * ((k >> 2) & 7): the transposing stores and the fragment reads are then
+// both free of bank conflicts (row stride 80 floats).
+namespace {
+constexpr int GXS = 80;
+
+template <int NT>
+struct GramTiles {
+    v4f acc[NT];
+    double acc64[NT][4];
+};
+
+__device__ __forceinline__ float gram_frag(const float (*Xs)[GXS], int k, int t, int lane, int sw) {
+    return Xs[k][(16 * t + (lane & 15)) ^ sw];
+}
+}  // namespace
+
 __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict__ mats,
                                                        const MatFlags* __restrict__ flags,
                                                        const GramItem* __restrict__ items,
                                                        int round) {
-    __shared__ float Xs[2][KC][XS];
+    __shared__ float Xs[2][KC][GXS];
     const GramItem it = items[blockIdx.x];
     if (flags[it.mat].done) return;
     const MatDev& md = mats[it.mat];
@@ -59,7 +79,7 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
     if (x_end > md.K_ld) x_end = md.K_ld;
 
     // loader: 64 rows x 32 columns = 512 float4 slots, 2 per thread
-    // slot s: row = s >> 3, q = s & 7
+    // slot s: row = s >> 3, q = s & 7 (columns 4q..4q+3 of the stage)
     const float* rowp[2];
     int lrow[2], lq[2];
 #pragma unroll
@@ -77,23 +97,30 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
     auto lstore = [&](int b) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            Xs[b][4 * lq[e] + 0][lrow[e]] = reg[e].x;
-            Xs[b][4 * lq[e] + 1][lrow[e]] = reg[e].y;
-            Xs[b][4 * lq[e] + 2][lrow[e]] = reg[e].z;
-            Xs[b][4 * lq[e] + 3][lrow[e]] = reg[e].w;
+            const int col = lrow[e] ^ (8 * lq[e]);
+            Xs[b][4 * lq[e] + 0][col] = reg[e].x;
+            Xs[b][4 * lq[e] + 1][col] = reg[e].y;
+            Xs[b][4 * lq[e] + 2][col] = reg[e].z;
+            Xs[b][4 * lq[e] + 3][col] = reg[e].w;
         }
     };
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int tr = (wave >> 1) * 32, tc = (wave & 1) * 32;
-    const int hl = lane >> 5, ll = lane & 31;
-    v16f acc;
-    double acc64[16];
+    // tiles (row strip, column strip) per wave
+    int ti[3], tj[3], nt;
+    if (wave == 0) { ti[0] = 0; tj[0] = 0; ti[1] = 0; tj[1] = 1; ti[2] = 0; tj[2] = 2; nt = 3; }
+    else if (wave == 1) { ti[0] = 0; tj[0] = 3; ti[1] = 1; tj[1] = 1; ti[2] = 1; tj[2] = 2; nt = 3; }
+    else if (wave == 2) { ti[0] = 1; tj[0] = 3; ti[1] = 2; tj[1] = 2; ti[2] = 0; tj[2] = 0; nt = 2; }
+    else { ti[0] = 2; tj[0] = 3; ti[1] = 3; tj[1] = 3; ti[2] = 0; tj[2] = 0; nt = 2; }
+    v4f acc[3];
+    double acc64[3][4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        acc[r] = 0.0f;
-        acc64[r] = 0.0;
-    }
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            acc[t][r] = 0.0f;
+            acc64[t][r] = 0.0;
+        }
     const int nst = (x_end - x_begin) / KC;  // K_ld and split lengths are multiples of KC
     if (nst > 0) {
         gload(x_begin);
@@ -104,27 +131,60 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
         const int b = st & 1;
         if (st + 1 < nst) gload(x_begin + (st + 1) * KC);
 #pragma unroll
-        for (int kk = 0; kk < KC; kk += 2) {
-            float a = Xs[b][kk + hl][tr + ll];
-            float c = Xs[b][kk + hl][tc + ll];
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, c, acc, 0, 0, 0);
+        for (int kk = 0; kk < KC; kk += 4) {
+            const int k = kk + (lane >> 4);
+            const int sw = 8 * ((kk >> 2) & 7);
+#define SC_MF(t, a, b) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[t], 0, 0, 0)
+            switch (wave) {  // wave-uniform: a scalar branch, fragments chosen at compile time
+                case 0: {
+                    const float f0 = gram_frag(Xs[b], k, 0, lane, sw), f1 = gram_frag(Xs[b], k, 1, lane, sw),
+                                f2 = gram_frag(Xs[b], k, 2, lane, sw);
+                    SC_MF(0, f0, f0); SC_MF(1, f0, f1); SC_MF(2, f0, f2);
+                    break;
+                }
+                case 1: {
+                    const float f0 = gram_frag(Xs[b], k, 0, lane, sw), f1 = gram_frag(Xs[b], k, 1, lane, sw),
+                                f2 = gram_frag(Xs[b], k, 2, lane, sw), f3 = gram_frag(Xs[b], k, 3, lane, sw);
+                    SC_MF(0, f0, f3); SC_MF(1, f1, f1); SC_MF(2, f1, f2);
+                    break;
+                }
+                case 2: {
+                    const float f1 = gram_frag(Xs[b], k, 1, lane, sw), f2 = gram_frag(Xs[b], k, 2, lane, sw),
+                                f3 = gram_frag(Xs[b], k, 3, lane, sw);
+                    SC_MF(0, f1, f3); SC_MF(1, f2, f2);
+                    break;
+                }
+                default: {
+                    const float f2 = gram_frag(Xs[b], k, 2, lane, sw), f3 = gram_frag(Xs[b], k, 3, lane, sw);
+                    SC_MF(0, f2, f3); SC_MF(1, f3, f3);
+                    break;
+                }
+            }
+#undef SC_MF
         }
         if (((st + 1) * KC) % CHUNK == 0 || st + 1 == nst) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                acc64[r] += (double)acc[r];
-                acc[r] = 0.0f;
-            }
+            for (int t = 0; t < 3; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    acc64[t][r] += (double)acc[t][r];
+                    acc[t][r] = 0.0f;
+                }
         }
         if (st + 1 < nst) lstore(b ^ 1);
         __syncthreads();
     }
-    // write this wave's 32x32 block of the 64x64 partial
+    // 16x16 output layout: lane l, register r -> row 4 (l / 16) + r, column l % 16
     double* out = md.gram + ((int64_t)it.slot * md.nsplit + it.split) * (PW * PW);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = tr + 8 * (r >> 2) + 4 * hl + (r & 3);
-        out[row * PW + tc + ll] = acc64[r];
+    for (int t = 0; t < 3; ++t) {
+        if (t >= nt) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * ti[t] + 4 * (lane >> 4) + r, col = 16 * tj[t] + (lane & 15);
+            out[row * PW + col] = acc64[t][r];
+            if (ti[t] != tj[t]) out[col * PW + row] = acc64[t][r];
+        }
     }
 }
 
@@ -134,15 +194,16 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
                                                         const SolveItem* __restrict__ items,
                                                         float tol) {
     // G: float32 working copy of the pair Gram (guides the rotation angles).
-    // Q: float64 accumulated rotation.  The rotation parameters are computed in
-    // float64 so that every applied 2x2 rotation is orthogonal to ~1e-16: with
-    // float32 (c, s) a tiny rotation has c == 1 and c^2 + s^2 > 1, a biased
-    // growth of the column norms that accumulates over thousands of rotations.
+    // R: the accumulated rotation minus the identity, Q = I + R, kept directly
+    // in float32.  Each 2x2 rotation is computed in float64 and enters R through
+    // (c - 1) = -t s / (1 + sqrt(1 + t^2)) and s, so a tiny rotation is carried
+    // exactly (storing Q itself in float32 would round c to 1 while s != 0, a
+    // biased growth of the column norms over thousands of rotations).
     __shared__ float G[PW][PW + 1];
-    __shared__ double Q[PW][PW + 1];
+    __shared__ float R[PW][PW + 1];
     __shared__ double dg[PW];
     __shared__ float red[4];
-    __shared__ double cs_c[PW / 2], cs_s[PW / 2];
+    __shared__ float cs_s[PW / 2], cs_cm1[PW / 2], cs_cf[PW / 2];
     __shared__ int pp[PW / 2], qq[PW / 2];
 
     const SolveItem it = items[blockIdx.x];
@@ -162,6 +223,7 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
         for (int sp = 0; sp < md.nsplit; ++sp) s += gp[(int64_t)sp * PW * PW + idx];
         gv[e] = s;
         G[idx >> 6][idx & 63] = (float)s;
+        R[idx >> 6][idx & 63] = 0.0f;
         if ((idx >> 6) == (idx & 63)) dg[idx & 63] = s;
     }
     __syncthreads();
@@ -191,66 +253,71 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
         return;
     }
 
-    // 3. one cyclic sweep of 2x2 rotations on G, accumulating Q (starts at I)
-    for (int idx = tid; idx < PW * PW; idx += 256)
-        Q[idx >> 6][idx & 63] = (idx >> 6) == (idx & 63) ? 1.0 : 0.0;
-    __syncthreads();
+    // 3. one cyclic sweep of 2x2 rotations on G, accumulating R
     for (int ir = 0; ir < PW - 1; ++ir) {
         if (tid < PW / 2) {
             int p, q;
             rr_pair(PW, ir, tid, &p, &q);
             const double gpp = G[p][p], gqq = G[q][q], gpq = G[p][q];
-            double c = 1.0, s = 0.0;
+            double c = 1.0, s = 0.0, cm1 = 0.0;
             if (gpp > floor2 && gqq > floor2 && fabs(gpq) > tol * sqrt(gpp * gqq)) {
                 const double zeta = (gqq - gpp) / (2.0 * gpq);
                 const double t = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + hypot(1.0, zeta));
-                c = 1.0 / sqrt(1.0 + t * t);
-                s = c * t;
+                const double h = sqrt(1.0 + t * t);
+                c = 1.0 / h;
+                s = t / h;
+                cm1 = -t * s / (1.0 + h);
             }
-            cs_c[tid] = c;
-            cs_s[tid] = s;
+            cs_s[tid] = (float)s;
+            cs_cm1[tid] = (float)cm1;
+            cs_cf[tid] = (float)c;
             pp[tid] = p;
             qq[tid] = q;
         }
         __syncthreads();
-        // columns of G and Q: [col_p, col_q] <- [c col_p - s col_q, s col_p + c col_q]
+        // columns of G and R: [col_p, col_q] <- [c col_p - s col_q, s col_p + c col_q]
+        // (for R: plus (J - I), i.e. (c - 1) on the diagonal and +-s off it)
         for (int w = tid; w < (PW / 2) * PW; w += 256) {
             const int i = w >> 6, a = w & 63;
-            const double s = cs_s[i];
-            if (s != 0.0) {
-                const double c = cs_c[i];
+            const float s = cs_s[i];
+            if (s != 0.0f) {
+                const float cf = cs_cf[i], cm1 = cs_cm1[i];
                 const int p = pp[i], q = qq[i];
-                const float cf = (float)c, sf = (float)s;
                 const float x = G[a][p], y = G[a][q];
-                G[a][p] = cf * x - sf * y;
-                G[a][q] = sf * x + cf * y;
-                const double xd = Q[a][p], yd = Q[a][q];
-                Q[a][p] = c * xd - s * yd;
-                Q[a][q] = s * xd + c * yd;
+                G[a][p] = cf * x - s * y;
+                G[a][q] = s * x + cf * y;
+                const float xr = R[a][p], yr = R[a][q];
+                float np = fmaf(cm1, xr, xr) - s * yr;
+                float nq = fmaf(cm1, yr, yr) + s * xr;
+                if (a == p) {
+                    np += cm1;
+                    nq += s;
+                } else if (a == q) {
+                    np -= s;
+                    nq += cm1;
+                }
+                R[a][p] = np;
+                R[a][q] = nq;
             }
         }
         __syncthreads();
         // rows of G
         for (int w = tid; w < (PW / 2) * PW; w += 256) {
             const int i = w >> 6, bcol = w & 63;
-            const double s = cs_s[i];
-            if (s != 0.0) {
-                const float cf = (float)cs_c[i], sf = (float)s;
+            const float s = cs_s[i];
+            if (s != 0.0f) {
+                const float cf = cs_cf[i];
                 const int p = pp[i], q = qq[i];
                 const float x = G[p][bcol], y = G[q][bcol];
-                G[p][bcol] = cf * x - sf * y;
-                G[q][bcol] = sf * x + cf * y;
+                G[p][bcol] = cf * x - s * y;
+                G[q][bcol] = s * x + cf * y;
             }
         }
         __syncthreads();
     }
-    // 4. R = Q - I (formed in float64, stored float32), row-major [b][a]
-    //    (X_new[a] = X[a] + sum_b R[b][a] X[b])
-    float* R = md.rot + (int64_t)it.slot * PW * PW;
-    for (int idx = tid; idx < PW * PW; idx += 256) {
-        const int b = idx >> 6, a = idx & 63;
-        R[idx] = (float)(Q[b][a] - (b == a ? 1.0 : 0.0));
-    }
+    // 4. R row-major [b][a] (X_new[a] = X[a] + sum_b R[b][a] X[b])
+    float* Rg = md.rot + (int64_t)it.slot * PW * PW;
+    for (int idx = tid; idx < PW * PW; idx += 256) Rg[idx] = R[idx >> 6][idx & 63];
     if (tid == 0) {
         *rflag = 1;
         atomicAdd(&fl.pairs_applied, 1);
