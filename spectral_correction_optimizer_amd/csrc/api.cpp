@@ -72,12 +72,12 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 enum ProfKind {
     PK_EMA, PK_LOAD, PK_ROWNORM, PK_INIT_FLAGS, PK_GRAM, PK_SOLVE, PK_APPLY, PK_SWEEP_END,
     PK_NORMALIZE, PK_LOWDIN, PK_FILTER, PK_PROJECTORS, PK_STEP_GEMM1, PK_STEP_GEMM2,
-    PK_STEP_GEMM3, PK_ADAMW, PK_WARM, PK_COUNT
+    PK_STEP_GEMM3, PK_ADAMW, PK_WARM, PK_SORT, PK_COUNT
 };
 const char* const kProfNames[PK_COUNT] = {
     "ema", "jacobi_load", "rownorm", "jacobi_init", "jacobi_gram", "jacobi_solve",
     "jacobi_apply", "jacobi_sweep_end", "normalize", "lowdin_gemm", "filter", "projector_gemm",
-    "step_gemm1", "step_gemm2", "step_gemm3", "combine_adamw", "warm_start"};
+    "step_gemm1", "step_gemm2", "step_gemm3", "combine_adamw", "warm_start", "jacobi_sort"};
 
 // Optional kernel timing: HIP events recorded around every launch on the
 // caller's stream; totals are folded in by sc_get_kernel_times.
@@ -352,11 +352,14 @@ int do_refresh(sc_opt* h, hipStream_t st) {
         for (auto& G : h->jg) {
             if (!G.nmat || r >= h->hp.max_sweeps * (G.max_nb - 1)) continue;
             hipStream_t gs = split ? G.st : st;
+            HIP_TRY(timed(h, PK_SORT, gs, [&] {
+                return launch_jacobi_sort(h->md, h->flags_d, G.mats, G.nmat, r, gs);
+            }));
             HIP_TRY(timed(h, PK_GRAM, gs, [&] {
                 return launch_jacobi_gram(h->md, h->flags_d, G.gi, G.ngi, r, gs);
             }));
             HIP_TRY(timed(h, PK_SOLVE, gs, [&] {
-                return launch_jacobi_solve(h->md, h->flags_d, G.si, G.nsi, h->tol, gs);
+                return launch_jacobi_solve(h->md, h->flags_d, G.si, G.nsi, r, h->tol, gs);
             }));
             HIP_TRY(timed(h, PK_APPLY, gs, [&] {
                 return launch_jacobi_apply(h->md, h->flags_d, G.ai, G.nai, r, gs);
@@ -410,7 +413,8 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         return o;
     };
     struct Offs {
-        size_t Manc, madam, vadam, A, V, F, W, PL, PR, s, d, norm2, Gfilt, Y, T, E, gram, rot, rflag;
+        size_t Manc, madam, vadam, A, V, F, W, PL, PR, s, d, norm2, Gfilt, Y, T, E, gram, rot, rflag,
+            perm, cnorm;
     };
     std::vector<Offs> o(n);
     for (int i = 0; i < n; ++i) {
@@ -451,6 +455,8 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         o[i].gram = take((size_t)(m.nb / 2) * m.nsplit * kPw * kPw * sizeof(double));
         o[i].rot = take((size_t)(m.nb / 2) * kPw * kPw * f);
         o[i].rflag = take((size_t)(m.nb / 2) * sizeof(int));
+        o[i].perm = take((size_t)m.kpad * sizeof(int));
+        o[i].cnorm = take((size_t)m.kpad * sizeof(float));
         h->max_nb = std::max(h->max_nb, m.nb);
         h->max_kpad = std::max(h->max_kpad, m.kpad);
         h->max_K = std::max(h->max_K, m.K_ld);
@@ -488,6 +494,8 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         m.gram = (double*)(b + o[i].gram);
         m.rot = (float*)(b + o[i].rot);
         m.rot_flag = (int*)(b + o[i].rflag);
+        m.perm = (int*)(b + o[i].perm);
+        m.cnorm = (float*)(b + o[i].cnorm);
     }
     void* p = nullptr;
     HIP_TRY(hipMalloc(&p, sizeof(MatDev) * n));

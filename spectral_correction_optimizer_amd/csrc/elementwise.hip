@@ -343,6 +343,11 @@ __global__ __launch_bounds__(256) void init_flags_kernel(const MatDev* __restric
         f.rounds_active = 0;
         f.pairs_applied = 0;
     }
+    // identity column order; column norms for the first sweep's ordering
+    for (int j = threadIdx.x; j < md.kpad; j += blockDim.x) {
+        md.perm[j] = j;
+        md.cnorm[j] = (float)md.norm2[j];
+    }
 }
 
 hipError_t launch_jacobi_init_flags(const MatDev* mats, MatFlags* flags, int nmat,

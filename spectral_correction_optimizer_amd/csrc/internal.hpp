@@ -37,6 +37,8 @@ struct MatDev {
     float* s;        // [kpad] singular values
     float* d;        // [kpad] Tikhonov response
     double* norm2;   // [kpad] squared row norms (scratch)
+    int* perm;       // [kpad] Jacobi column order: logical position -> physical row of A / V
+    float* cnorm;    // [kpad] squared column norms by physical row (sweep-start ordering)
     float* Gfilt;    // [m][n] filtered gradient of the last step
     float* Gproj;    // [m][n] combined gradient (only when kept), else null
     float* Y;        // [k][k] step intermediate
@@ -124,9 +126,12 @@ hipError_t launch_filter(const MatDev* mats, int nmat, float tau, int max_kpad, 
 hipError_t launch_jacobi_gram(const MatDev* mats, const MatFlags* flags, const GramItem* gi,
                               int ngi, int round, hipStream_t st);
 hipError_t launch_jacobi_solve(const MatDev* mats, MatFlags* flags, const SolveItem* si, int nsi,
-                               float tol, hipStream_t st);
+                               int round, float tol, hipStream_t st);
 hipError_t launch_jacobi_apply(const MatDev* mats, const MatFlags* flags, const ApplyItem* ai,
                                int nai, int round, hipStream_t st);
+// At a matrix's sweep start: order its columns by decreasing norm (perm).
+hipError_t launch_jacobi_sort(const MatDev* mats, const MatFlags* flags, const int* mat_idx,
+                              int nmat, int round, hipStream_t st);
 hipError_t launch_jacobi_sweep_end(const MatDev* mats, MatFlags* flags, const int* mat_idx,
                                    int nmat, int round, int max_sweeps, float tol,
                                    hipStream_t st);
