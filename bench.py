@@ -48,6 +48,8 @@ def parse():
                     help="time kernels inside the timed region itself (serializes the two "
                          "Jacobi streams) instead of in one extra pass after it")
     ap.add_argument("--max-sweeps", type=int, default=30)
+    ap.add_argument("--no-precondition", action="store_true",
+                    help="plain Jacobi sweeps for every matrix (no Cholesky factor phase)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 3 times (to scale HBM "
                          "byte counters) and exit")
@@ -188,7 +190,8 @@ def main():
     print(f"# inputs generated in {t_gen:.1f} s", file=sys.stderr, flush=True)
 
     opt = sco.SpectralAdamW(shapes, w_dtype=tdt, g_dtype=tdt, device=dev,
-                            max_sweeps=args.max_sweeps, **hp)
+                            max_sweeps=args.max_sweeps,
+                            precondition=0 if args.no_precondition else 1, **hp)
     for i, x in enumerate(M0):
         opt.set_state(i, "m_anc", x)
     del M0
@@ -232,10 +235,12 @@ def main():
         opt.step(W, G_mask[k])
         kt = opt.kernel_times()
         opt.profile(False)
-    sweeps_by_shape = {}
-    for (m, n), sw in zip(shapes, st["sweeps"]):
+    sweeps_by_shape, factor_by_shape = {}, {}
+    for (m, n), sw, fs in zip(shapes, st["sweeps"], st["factor_sweeps"]):
         key = f"{m}x{n}"
         sweeps_by_shape[key] = max(sweeps_by_shape.get(key, 0), sw)
+        if fs:
+            factor_by_shape[key] = max(factor_by_shape.get(key, 0), fs)
 
     ms_per_pass = wall * 1e3 / args.steps
     r_med, s_med = statistics.median(refresh_ms), statistics.median(step_ms)
@@ -295,6 +300,8 @@ def main():
         "step_chain_tflops": round(chain_flops / (s_med * 1e9), 2),
         "jacobi_sweeps_max": st["sweeps_max"],
         "jacobi_sweeps_by_shape": sweeps_by_shape,
+        "jacobi_factor_sweeps_by_shape": factor_by_shape,
+        "cholesky_rejected": st["factor_rejected"],
         "kernel_times_source": ("timed region" if args.profile_timed else
                                 "one extra pass after the timed region, Jacobi rounds serialized"),
         "jacobi_not_converged": st["not_converged"],

@@ -61,17 +61,26 @@ typedef struct {
     float eps;          /* AdamW epsilon (added outside the square root), > 0 */
     float weight_decay; /* decoupled weight decay, scaled by lr, >= 0 */
     int max_sweeps;     /* Jacobi sweep cap per refresh, >= 1 (e.g. 30) */
-    float jacobi_tol;   /* rotation threshold |a_p.a_q| / (|a_p||a_q|); 0 = default 16 * 2^-24 */
+    float jacobi_tol;   /* rotation and convergence threshold on |a_p.a_q| / (|a_p||a_q|);
+                           0 = default: rotate above 16 * 2^-24, stop after a sweep whose
+                           largest ratio is <= 2^-24 * max(16, sqrt(max(rows, cols))) */
     int sync_check;     /* 1: poll convergence flags on the host (stops early);
                            0: fully asynchronous, always max_sweeps sweeps */
     int warm_start;     /* 1: a refresh starts its sweeps from the previous factors
                            (A = M V_prev); 0: always from A = M, V = I */
+    int precondition;   /* 1: for matrices with max(rows, cols) >= 2 min(rows, cols) the
+                           sweeps first run on the k x k Cholesky factor of the Gram
+                           A^T A (same rotations, rows k instead of K long), then
+                           polish on A = M V until converged; a matrix whose
+                           factorization is rejected runs the plain sweeps.  Used
+                           by refreshes that start from previous factors
+                           (warm_start = 1) and with sync_check = 1. */
 } sc_hparams;
 
 /* Fill `hp` with the defaults of the pages' training strategy:
  * tau_p 1e-3, alpha 0.3, beta_anc 0.9, lr 2e-5, betas (0.9, 0.999), eps 1e-8,
  * weight_decay 0.01, max_sweeps 30, jacobi_tol 0 (default), sync_check 1,
- * warm_start 1. */
+ * warm_start 1, precondition 1. */
 void sc_default_hparams(sc_hparams* hp);
 
 /* Create an optimizer over n_mats weight matrices of shapes rows[i] x cols[i]
@@ -160,12 +169,20 @@ typedef struct {
     int not_converged;     /* matrices that hit max_sweeps in the last refresh */
     int nonfinite_grad;    /* 1 if a non-finite G_mask value was seen by a step */
     int nonfinite_anchor;  /* 1 if a non-finite G_anc value was seen by an EMA */
+    int factor_sweeps_max; /* most sweeps any matrix ran on its Cholesky factor (last refresh) */
+    int factor_rejected;   /* matrices whose Cholesky factorization was rejected (last refresh) */
 } sc_stats;
 
 /* Synchronize the handle's work (device-wide) and report counters.
  * per_mat_sweeps: optional host array of n_mats ints receiving the sweeps of
- * each matrix in the last refresh. */
+ * each matrix in the last refresh (factor and polishing sweeps together). */
 int sc_get_stats(sc_handle h, sc_stats* out, int* per_mat_sweeps);
+
+/* Synchronize the handle's work (device-wide) and copy per-matrix sweep counts
+ * of the last refresh into host arrays of n_mats ints (either may be NULL):
+ * total[i] all sweeps, factor[i] the sweeps run on the Cholesky factor (0 when
+ * the matrix was not preconditioned or its factorization was rejected). */
+int sc_get_sweep_counts(sc_handle h, int* total, int* factor);
 
 /* Kernel timing for measurement: when enabled, every kernel launch of the
  * handle is bracketed by a pair of HIP events on the launch stream (small

@@ -30,7 +30,7 @@ EXPORTED_SYMBOLS = (
     "sc_default_hparams", "sc_opt_create", "sc_opt_destroy", "sc_anchor_update", "sc_refresh",
     "sc_step", "sc_set_lr", "sc_set_tau", "sc_set_state", "sc_get_state", "sc_set_step",
     "sc_get_step", "sc_set_factors", "sc_get_factors", "sc_keep_proj", "sc_get_filtered",
-    "sc_get_stats", "sc_profile", "sc_get_kernel_times", "sc_last_error",
+    "sc_get_stats", "sc_get_sweep_counts", "sc_profile", "sc_get_kernel_times", "sc_last_error",
 )
 
 SC_F32, SC_BF16 = 0, 1
@@ -48,7 +48,8 @@ class HParams(ctypes.Structure):
                 ("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
                 ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
                 ("max_sweeps", ctypes.c_int), ("jacobi_tol", ctypes.c_float),
-                ("sync_check", ctypes.c_int), ("warm_start", ctypes.c_int)]
+                ("sync_check", ctypes.c_int), ("warm_start", ctypes.c_int),
+                ("precondition", ctypes.c_int)]
 
 
 class KernelTime(ctypes.Structure):
@@ -60,7 +61,8 @@ class KernelTime(ctypes.Structure):
 class Stats(ctypes.Structure):
     _fields_ = [("n_mats", ctypes.c_int), ("step", ctypes.c_int64), ("refreshes", ctypes.c_int),
                 ("sweeps_max", ctypes.c_int), ("not_converged", ctypes.c_int),
-                ("nonfinite_grad", ctypes.c_int), ("nonfinite_anchor", ctypes.c_int)]
+                ("nonfinite_grad", ctypes.c_int), ("nonfinite_anchor", ctypes.c_int),
+                ("factor_sweeps_max", ctypes.c_int), ("factor_rejected", ctypes.c_int)]
 
 
 def library_path() -> str:
@@ -95,6 +97,8 @@ def load_library():
         "sc_keep_proj": (ctypes.c_int, [vp, ctypes.c_int]),
         "sc_get_filtered": (ctypes.c_int, [vp, ctypes.c_int, vp, vp, vp]),
         "sc_get_stats": (ctypes.c_int, [vp, ctypes.POINTER(Stats), ctypes.POINTER(ctypes.c_int)]),
+        "sc_get_sweep_counts": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_int),
+                                               ctypes.POINTER(ctypes.c_int)]),
         "sc_profile": (ctypes.c_int, [vp, ctypes.c_int]),
         "sc_get_kernel_times": (ctypes.c_int, [vp, ctypes.POINTER(KernelTime), ctypes.c_int,
                                                ctypes.POINTER(ctypes.c_int)]),
@@ -128,7 +132,8 @@ class SpectralAdamW:
     shapes: [(rows, cols), ...] of the row-major weights ([out, in]).
     w_dtype: torch.float32 or torch.bfloat16 (storage of W); g_dtype: type of
     G_mask and G_anc.  Keyword hyper-parameters: tau_p, alpha, beta_anc, lr,
-    beta1, beta2, eps, weight_decay, max_sweeps, jacobi_tol, sync_check.
+    beta1, beta2, eps, weight_decay, max_sweeps, jacobi_tol, sync_check,
+    warm_start, precondition.
     """
 
     def __init__(self, shapes, w_dtype=torch.float32, g_dtype=torch.float32, device=None, **hp):
@@ -254,6 +259,9 @@ class SpectralAdamW:
         _check(self._lib.sc_get_stats(self._h, ctypes.byref(st), per))
         d = {name: getattr(st, name) for name, _ in Stats._fields_}
         d["sweeps"] = list(per)
+        fac = (ctypes.c_int * self.n)()
+        _check(self._lib.sc_get_sweep_counts(self._h, None, fac))
+        d["factor_sweeps"] = list(fac)
         return d
 
     def profile(self, enable: bool = True):

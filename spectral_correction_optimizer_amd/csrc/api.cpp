@@ -47,7 +47,6 @@ int fail(int code, const char* fmt, ...) {
 
 constexpr int64_t kMaxDim = 65536;
 constexpr int kChunk = 16384;  // elements per elementwise workgroup
-constexpr float kDefaultTol = 16.0f * 5.9604644775390625e-08f;
 
 struct DeviceGuard {
     int prev = -1;
@@ -72,12 +71,13 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 enum ProfKind {
     PK_EMA, PK_LOAD, PK_ROWNORM, PK_INIT_FLAGS, PK_GRAM, PK_SOLVE, PK_APPLY, PK_SWEEP_END,
     PK_NORMALIZE, PK_LOWDIN, PK_FILTER, PK_PROJECTORS, PK_STEP_GEMM1, PK_STEP_GEMM2,
-    PK_STEP_GEMM3, PK_ADAMW, PK_WARM, PK_SORT, PK_COUNT
+    PK_STEP_GEMM3, PK_ADAMW, PK_WARM, PK_SORT, PK_CHOL_GEMM, PK_CHOL, PK_POLISH_GEMM, PK_COUNT
 };
 const char* const kProfNames[PK_COUNT] = {
     "ema", "jacobi_load", "rownorm", "jacobi_init", "jacobi_gram", "jacobi_solve",
     "jacobi_apply", "jacobi_sweep_end", "normalize", "lowdin_gemm", "filter", "projector_gemm",
-    "step_gemm1", "step_gemm2", "step_gemm3", "combine_adamw", "warm_start", "jacobi_sort"};
+    "step_gemm1", "step_gemm2", "step_gemm3", "combine_adamw", "warm_start", "jacobi_sort",
+    "chol_syrk", "cholesky", "polish_gemm"};
 
 // Optional kernel timing: HIP events recorded around every launch on the
 // caller's stream; totals are folded in by sc_get_kernel_times.
@@ -96,6 +96,12 @@ struct Prof {
 };
 int round_up(int x, int a) { return (x + a - 1) / a * a; }
 
+// K-splits of a pair Gram over rows of length len (a multiple of 128): about 8
+// splits of a multiple of 256 columns each, so that the fp64 folds of the Gram
+// kernel see whole 256-column chunks.
+int split_len(int len) { return std::max(256, round_up((len + 7) / 8, 256)); }
+int split_count(int len) { return (len + split_len(len) - 1) / split_len(len); }
+
 }  // namespace
 
 struct sc_opt {
@@ -103,7 +109,6 @@ struct sc_opt {
     int n = 0;
     sc_dtype wdt = SC_F32, gdt = SC_F32;
     sc_hparams hp{};
-    float tol = kDefaultTol;
     std::vector<MatDev> mh;
     MatDev* md = nullptr;
     MatFlags* flags_d = nullptr;
@@ -116,7 +121,10 @@ struct sc_opt {
     // Jacobi work lists of the two matrix groups whose rounds run on two
     // internal streams (one group's pair solves overlap the other's Gram /
     // rotation kernels); matrices are assigned to groups by decreasing work.
-    struct JGroup {
+    // Three list sets: plain (every matrix, full rows), factor (every matrix;
+    // preconditioned ones over their klen-long factor rows) and polish (only
+    // the preconditioned matrices, full rows).
+    struct Lists {
         GramItem* gi = nullptr;
         int ngi = 0;
         SolveItem* si = nullptr;
@@ -126,9 +134,19 @@ struct sc_opt {
         int* mats = nullptr;
         int nmat = 0;
         int max_nb = 2;
+    };
+    struct JGroup {
+        Lists L[3];
         hipStream_t st = nullptr;
         hipEvent_t join = nullptr;
     } jg[2];
+    // preconditioned matrices (max(m, n) >= 2 min(m, n) when hp.precondition)
+    int* cap_d = nullptr;
+    int ncap = 0;
+    int max_nbk = 0;  // largest ceil(k / 64) among them
+    SyrkItem* syrk_d = nullptr;     // lower tiles of A^T A of those matrices
+    int nsyrk = 0;
+    GemmGroup polish_nt, polish_nn; // A_rows = V op(M) after the factor phase
     hipEvent_t fork = nullptr;
     int max_nb = 2, max_kpad = 64, max_K = 1, max_k = 1;
     // refresh GEMMs
@@ -252,6 +270,9 @@ int check_hp(const sc_hparams* hp) {
         return fail(SC_ERR_INVALID_ARG, "max_sweeps must be in [1, 1000]");
     if (!(hp->jacobi_tol >= 0.0f && hp->jacobi_tol < 1.0f))
         return fail(SC_ERR_INVALID_ARG, "jacobi_tol must be in [0, 1)");
+    if ((hp->sync_check != 0 && hp->sync_check != 1) || (hp->warm_start != 0 && hp->warm_start != 1) ||
+        (hp->precondition != 0 && hp->precondition != 1))
+        return fail(SC_ERR_INVALID_ARG, "sync_check, warm_start and precondition must be 0 or 1");
     return SC_OK;
 }
 
@@ -305,28 +326,95 @@ int finalize_factors(sc_opt* h, hipStream_t st) {
 }
 
 // Algorithmic work of the Jacobi sweeps from the device counters (profiling only):
-// per active round and pair the 64x64 Gram over K (2 * 64 * 64 * K flops); per
-// applied pair the update of 64 rows of A (length K) and V (length k),
-// 2 * 64 * 64 * (K + k) flops and 8 * 64 * (K + k) + 4 * 64 * 64 bytes.
+// per active round and pair the 64x64 Gram over the row length L (2 * 64 * 64 * L
+// flops, 4 * 64 * L bytes); per applied pair the update of 64 rows of A (length L)
+// and V (length k), 2 * 64 * 64 * (L + k) flops and 8 * 64 * (L + k) + 4 * 64 * 64
+// bytes.  L = klen for the rounds on the Cholesky factor, K otherwise.
 void account_sweeps(sc_opt* h) {
     for (int i = 0; i < h->n; ++i) {
         const MatDev& m = h->mh[i];
         const MatFlags& f = h->flags_h[i];
         const double pw = kPw;
-        h->prof.flops[PK_GRAM] += (double)f.rounds_active * (m.nb / 2) * 2.0 * pw * pw * m.K;
-        h->prof.flops[PK_APPLY] += (double)f.pairs_applied * 2.0 * pw * pw * (m.K + m.k);
-        h->prof.bytes[PK_APPLY] +=
-            (double)f.pairs_applied * (8.0 * pw * (m.K + m.k) + 4.0 * pw * pw);
-        h->prof.bytes[PK_GRAM] += (double)f.rounds_active * (m.nb / 2) * 4.0 * pw * m.K;
+        const double rounds[2] = {(double)f.rounds_pre, (double)(f.rounds_active - f.rounds_pre)};
+        const double pairs[2] = {(double)f.pairs_pre, (double)(f.pairs_applied - f.pairs_pre)};
+        const double len[2] = {(double)m.klen, (double)m.K};
+        for (int ph = 0; ph < 2; ++ph) {
+            h->prof.flops[PK_GRAM] += rounds[ph] * (m.nb / 2) * 2.0 * pw * pw * len[ph];
+            h->prof.bytes[PK_GRAM] += rounds[ph] * (m.nb / 2) * 4.0 * pw * len[ph];
+            h->prof.flops[PK_APPLY] += pairs[ph] * 2.0 * pw * pw * (len[ph] + m.k);
+            h->prof.bytes[PK_APPLY] += pairs[ph] * (8.0 * pw * (len[ph] + m.k) + 4.0 * pw * pw);
+        }
     }
 }
 
+// Jacobi rounds over list set `which` of both groups until every matrix is done
+// (polled on the host once per sweep from sweep `first_check` on) or the sweep
+// cap is reached.  Without kernel timing the groups run on their own streams,
+// forked from and joined back into `st`.
+int run_rounds(sc_opt* h, hipStream_t st, int which, int first_check_sweeps) {
+    int max_nb = 2;
+    for (auto& G : h->jg)
+        if (G.L[which].nmat) max_nb = std::max(max_nb, G.L[which].max_nb);
+    const int rps = max_nb - 1;  // rounds per sweep of the largest matrix
+    const int max_rounds = h->hp.max_sweeps * rps;
+    const int first_check = std::min(max_rounds, first_check_sweeps * rps);
+    // With kernel timing on, both groups run on the caller's stream so that
+    // every kernel's events bracket it alone (no overlap between groups).
+    const bool split = !h->prof.on;
+    if (split) {
+        HIP_TRY(hipEventRecord(h->fork, st));
+        for (auto& G : h->jg)
+            if (G.L[which].nmat) HIP_TRY(hipStreamWaitEvent(G.st, h->fork, 0));
+    }
+    for (int r = 0; r < max_rounds; ++r) {
+        for (auto& G : h->jg) {
+            const sc_opt::Lists& L = G.L[which];
+            if (!L.nmat || r >= h->hp.max_sweeps * (L.max_nb - 1)) continue;
+            hipStream_t gs = split ? G.st : st;
+            HIP_TRY(timed(h, PK_SORT, gs, [&] {
+                return launch_jacobi_sort(h->md, h->flags_d, L.mats, L.nmat, r, gs);
+            }));
+            HIP_TRY(timed(h, PK_GRAM, gs, [&] {
+                return launch_jacobi_gram(h->md, h->flags_d, L.gi, L.ngi, r, gs);
+            }));
+            HIP_TRY(timed(h, PK_SOLVE, gs, [&] {
+                return launch_jacobi_solve(h->md, h->flags_d, L.si, L.nsi, r, gs);
+            }));
+            HIP_TRY(timed(h, PK_APPLY, gs, [&] {
+                return launch_jacobi_apply(h->md, h->flags_d, L.ai, L.nai, r, gs);
+            }));
+            HIP_TRY(timed(h, PK_SWEEP_END, gs, [&] {
+                return launch_jacobi_sweep_end(h->md, h->flags_d, L.mats, L.nmat, r,
+                                               h->hp.max_sweeps, gs);
+            }));
+        }
+        if (h->hp.sync_check && r + 1 >= first_check && (r + 1) % rps == 0 && r + 1 < max_rounds) {
+            for (auto& G : h->jg)
+                if (G.L[which].nmat) HIP_TRY(hipStreamSynchronize(split ? G.st : st));
+            HIP_TRY(hipMemcpy(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n,
+                              hipMemcpyDeviceToHost));
+            bool all = true;
+            for (int i = 0; i < h->n; ++i) all = all && h->flags_h[i].done;
+            if (all) break;
+        }
+    }
+    for (auto& G : h->jg) {
+        if (!G.L[which].nmat || !split) continue;
+        HIP_TRY(hipEventRecord(G.join, G.st));
+        HIP_TRY(hipStreamWaitEvent(st, G.join, 0));
+    }
+    return SC_OK;
+}
+
+enum { LIST_PLAIN = 0, LIST_FACTOR = 1, LIST_POLISH = 2 };
+
 int do_refresh(sc_opt* h, hipStream_t st) {
-    if (h->hp.warm_start && h->have_factors) {
+    PtrTable none = make_table(h, nullptr);
+    int rc;
+    const bool warm = h->hp.warm_start && h->have_factors;
+    if (warm) {
         // Start the sweeps from the previous factors: V = W_prev, A = M V_prev.
         HIP_TRY(timed(h, PK_WARM, st, [&] { return launch_jacobi_warm(h->md, h->n, st); }));
-        PtrTable none = make_table(h, nullptr);
-        int rc;
         if ((rc = run_group(h, h->warm_nt, PK_WARM, none, st))) return rc;
         if ((rc = run_group(h, h->warm_nn, PK_WARM, none, st))) return rc;
     } else {
@@ -337,52 +425,37 @@ int do_refresh(sc_opt* h, hipStream_t st) {
     HIP_TRY(timed(h, PK_ROWNORM, st, [&] { return launch_rownorm(h->md, h->n, 0, h->max_kpad, st); }));
     HIP_TRY(timed(h, PK_INIT_FLAGS, st,
                   [&] { return launch_jacobi_init_flags(h->md, h->flags_d, h->n, st); }));
-    const int rps = h->max_nb - 1;  // rounds per sweep of the largest matrix
-    const int max_rounds = h->hp.max_sweeps * rps;
-    const int first_check = std::min(max_rounds, 4 * rps);
-    // With kernel timing on, both groups run on the caller's stream so that
-    // every kernel's events bracket it alone (no overlap between groups).
-    const bool split = !h->prof.on;
-    if (split) {
-        HIP_TRY(hipEventRecord(h->fork, st));
-        for (auto& G : h->jg)
-            if (G.nmat) HIP_TRY(hipStreamWaitEvent(G.st, h->fork, 0));
+    // The factor phase needs a well-conditioned Gram: from the previous factors the
+    // columns of A = M V_prev are close to orthogonal.  From a cold start (A = M)
+    // a graded spectrum would make most factorizations fail, so it is skipped.
+    const bool pre = h->ncap > 0 && h->hp.sync_check && warm;
+    if (pre) {
+        // Factor phase: Jacobi on R = L^T, A^T A = L L^T (same Gram, k-long rows).
+        HIP_TRY(timed(h, PK_CHOL_GEMM, st,
+                      [&] { return launch_chol_syrk(h->md, h->syrk_d, h->nsyrk, st); }));
+        if (h->prof.on)
+            for (int i = 0; i < h->n; ++i)
+                if (h->mh[i].klen) {
+                    const double kt = (h->mh[i].k + 127) / 128;
+                    h->prof.flops[PK_CHOL_GEMM] += kt * (kt + 1) / 2 * 2.0 * 128 * 128 * h->mh[i].K_ld;
+                }
+        HIP_TRY(timed(h, PK_CHOL, st, [&] {
+            return launch_cholesky(h->md, h->flags_d, h->cap_d, h->ncap, h->max_nbk, st);
+        }));
+        if (h->prof.on)
+            for (int i = 0; i < h->n; ++i)
+                if (h->mh[i].klen) h->prof.flops[PK_CHOL] += std::pow((double)h->mh[i].k, 3) / 3.0;
     }
-    for (int r = 0; r < max_rounds; ++r) {
-        for (auto& G : h->jg) {
-            if (!G.nmat || r >= h->hp.max_sweeps * (G.max_nb - 1)) continue;
-            hipStream_t gs = split ? G.st : st;
-            HIP_TRY(timed(h, PK_SORT, gs, [&] {
-                return launch_jacobi_sort(h->md, h->flags_d, G.mats, G.nmat, r, gs);
-            }));
-            HIP_TRY(timed(h, PK_GRAM, gs, [&] {
-                return launch_jacobi_gram(h->md, h->flags_d, G.gi, G.ngi, r, gs);
-            }));
-            HIP_TRY(timed(h, PK_SOLVE, gs, [&] {
-                return launch_jacobi_solve(h->md, h->flags_d, G.si, G.nsi, r, h->tol, gs);
-            }));
-            HIP_TRY(timed(h, PK_APPLY, gs, [&] {
-                return launch_jacobi_apply(h->md, h->flags_d, G.ai, G.nai, r, gs);
-            }));
-            HIP_TRY(timed(h, PK_SWEEP_END, gs, [&] {
-                return launch_jacobi_sweep_end(h->md, h->flags_d, G.mats, G.nmat, r,
-                                               h->hp.max_sweeps, h->tol, gs);
-            }));
-        }
-        if (h->hp.sync_check && r + 1 >= first_check && (r + 1) % rps == 0 && r + 1 < max_rounds) {
-            for (auto& G : h->jg)
-                if (G.nmat) HIP_TRY(hipStreamSynchronize(split ? G.st : st));
-            HIP_TRY(hipMemcpy(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n,
-                              hipMemcpyDeviceToHost));
-            bool all = true;
-            for (int i = 0; i < h->n; ++i) all = all && h->flags_h[i].done;
-            if (all) break;
-        }
-    }
-    for (auto& G : h->jg) {
-        if (!G.nmat || !split) continue;
-        HIP_TRY(hipEventRecord(G.join, G.st));
-        HIP_TRY(hipStreamWaitEvent(st, G.join, 0));
+    if ((rc = run_rounds(h, st, pre ? LIST_FACTOR : LIST_PLAIN, 4))) return rc;
+    if (pre) {
+        // Polishing phase on the true operand A = M V (V holds the factor phase's
+        // rotations); a rejected matrix gets back its unchanged operand and runs
+        // all its sweeps here.
+        if ((rc = run_group(h, h->polish_nt, PK_POLISH_GEMM, none, st))) return rc;
+        if ((rc = run_group(h, h->polish_nn, PK_POLISH_GEMM, none, st))) return rc;
+        HIP_TRY(timed(h, PK_INIT_FLAGS, st,
+                      [&] { return launch_phase2_reset(h->md, h->flags_d, h->cap_d, h->ncap, st); }));
+        if ((rc = run_rounds(h, st, LIST_POLISH, 1))) return rc;
     }
     if (h->prof.on) {
         HIP_TRY(hipMemcpyAsync(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n,
@@ -390,7 +463,7 @@ int do_refresh(sc_opt* h, hipStream_t st) {
         HIP_TRY(hipStreamSynchronize(st));
         account_sweeps(h);
     }
-    int rc = finalize_factors(h, st);
+    rc = finalize_factors(h, st);
     if (rc) return rc;
     h->have_factors = true;
     h->refreshes += 1;
@@ -414,7 +487,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
     };
     struct Offs {
         size_t Manc, madam, vadam, A, V, F, W, PL, PR, s, d, norm2, Gfilt, Y, T, E, gram, rot, rflag,
-            perm, cnorm;
+            perm, cnorm, chol;
     };
     std::vector<Offs> o(n);
     for (int i = 0; i < n; ++i) {
@@ -428,11 +501,22 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         m.kpad = round_up(m.k, kPw);
         m.K_ld = round_up(m.K, 128);
         m.nb = m.kpad / kJb;
+        // Pairs are rotated above 16 * 2^-24.  Float32 sweeps leave relative
+        // off-diagonals of about that size behind (rounding of the Gram and of the
+        // rotations), so the last few pairs above it reappear in every sweep; the
+        // sweeps therefore stop once a sweep's largest ratio is within the usual
+        // one-sided Jacobi bound 2^-24 sqrt(K) (K float32 terms per inner
+        // product), floored at the rotation threshold.  A given jacobi_tol sets both.
+        const double eps = 5.9604644775390625e-08;
+        m.tol = h->hp.jacobi_tol > 0.0f ? h->hp.jacobi_tol : (float)(16.0 * eps);
+        m.tol_conv = h->hp.jacobi_tol > 0.0f
+                         ? h->hp.jacobi_tol
+                         : (float)(eps * std::max(16.0, std::sqrt((double)m.K)));
         m.numel = (int64_t)m.m * m.n;
-        int L = round_up((m.K_ld + 7) / 8, 256);
-        if (L < 256) L = 256;
-        m.ksplit_len = L;
-        m.nsplit = (m.K_ld + L - 1) / L;
+        // Cholesky-preconditioned when the operand is at least twice as long as wide
+        m.klen = (h->hp.precondition && m.K >= 2 * m.k) ? round_up(m.k, 128) : 0;
+        m.nsplit = split_count(m.K_ld);
+        if (m.klen) m.nsplit = std::max(m.nsplit, split_count(m.klen));
         const size_t f = sizeof(float);
         const size_t mn = (size_t)m.numel * f;
         const size_t kk = (size_t)m.k * m.k * f;
@@ -457,6 +541,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         o[i].rflag = take((size_t)(m.nb / 2) * sizeof(int));
         o[i].perm = take((size_t)m.kpad * sizeof(int));
         o[i].cnorm = take((size_t)m.kpad * sizeof(float));
+        o[i].chol = take(m.klen ? (size_t)m.k * m.k * sizeof(double) : 0);
         h->max_nb = std::max(h->max_nb, m.nb);
         h->max_kpad = std::max(h->max_kpad, m.kpad);
         h->max_K = std::max(h->max_K, m.K_ld);
@@ -496,6 +581,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         m.rot_flag = (int*)(b + o[i].rflag);
         m.perm = (int*)(b + o[i].perm);
         m.cnorm = (float*)(b + o[i].cnorm);
+        m.chol = m.klen ? (double*)(b + o[i].chol) : nullptr;
     }
     void* p = nullptr;
     HIP_TRY(hipMalloc(&p, sizeof(MatDev) * n));
@@ -523,7 +609,10 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
     }
     std::vector<int> order(n);
     for (int i = 0; i < n; ++i) order[i] = i;
-    auto work = [&](int i) { return (double)h->mh[i].kpad * (h->mh[i].K_ld + h->mh[i].kpad); };
+    auto work = [&](int i) {
+        const MatDev& m = h->mh[i];
+        return (double)m.kpad * ((m.klen ? m.klen : m.K_ld) + m.kpad);
+    };
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return work(a) > work(b); });
     std::vector<int> gm[2];
     double load[2] = {0.0, 0.0};
@@ -545,29 +634,52 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
     int rc;
     if ((rc = upload(ch, &h->chunks_d, &h->nchunks))) return rc;
     for (int g = 0; g < 2; ++g) {
-        std::vector<GramItem> gi;
-        std::vector<SolveItem> si;
-        std::vector<ApplyItem> ai;
         auto& G = h->jg[g];
         std::sort(gm[g].begin(), gm[g].end());
-        for (int i : gm[g]) {
-            const MatDev& m = h->mh[i];
-            G.max_nb = std::max(G.max_nb, m.nb);
-            for (int s = 0; s < m.nb / 2; ++s) {
-                for (int sp = 0; sp < m.nsplit; ++sp) gi.push_back(GramItem{i, s, sp});
-                si.push_back(SolveItem{i, s});
-                for (int c = 0; c < m.K_ld / 128; ++c) ai.push_back(ApplyItem{i, s, 0, c});
-                for (int c = 0; c < (m.kpad + 127) / 128; ++c) ai.push_back(ApplyItem{i, s, 1, c});
+        for (int which = 0; which < 3; ++which) {
+            std::vector<GramItem> gi;
+            std::vector<SolveItem> si;
+            std::vector<ApplyItem> ai;
+            std::vector<int> mats;
+            auto& L = G.L[which];
+            for (int i : gm[g]) {
+                const MatDev& m = h->mh[i];
+                if (which == 2 && !m.klen) continue;  // polish: preconditioned matrices only
+                const int len = (which == 1 && m.klen) ? m.klen : m.K_ld;
+                const int sl = split_len(len), ns = split_count(len);
+                mats.push_back(i);
+                L.max_nb = std::max(L.max_nb, m.nb);
+                for (int s = 0; s < m.nb / 2; ++s) {
+                    for (int sp = 0; sp < ns; ++sp)
+                        gi.push_back(GramItem{i, s, sp, sp * sl, std::min(len, (sp + 1) * sl)});
+                    si.push_back(SolveItem{i, s, ns});
+                    for (int c = 0; c < len / 128; ++c) ai.push_back(ApplyItem{i, s, 0, c});
+                    for (int c = 0; c < (m.kpad + 127) / 128; ++c) ai.push_back(ApplyItem{i, s, 1, c});
+                }
             }
+            if ((rc = upload(gi, &L.gi, &L.ngi))) return rc;
+            if ((rc = upload(si, &L.si, &L.nsi))) return rc;
+            if ((rc = upload(ai, &L.ai, &L.nai))) return rc;
+            if ((rc = upload(mats, &L.mats, &L.nmat))) return rc;
         }
-        if ((rc = upload(gi, &G.gi, &G.ngi))) return rc;
-        if ((rc = upload(si, &G.si, &G.nsi))) return rc;
-        if ((rc = upload(ai, &G.ai, &G.nai))) return rc;
-        if ((rc = upload(gm[g], &G.mats, &G.nmat))) return rc;
-        if (G.nmat > 0) {
+        if (G.L[0].nmat > 0) {
             HIP_TRY(hipStreamCreateWithFlags(&G.st, hipStreamNonBlocking));
             HIP_TRY(hipEventCreateWithFlags(&G.join, hipEventDisableTiming));
         }
+    }
+    {
+        std::vector<int> cap;
+        std::vector<SyrkItem> sy;
+        for (int i = 0; i < n; ++i)
+            if (h->mh[i].klen) {
+                cap.push_back(i);
+                h->max_nbk = std::max(h->max_nbk, (h->mh[i].k + 63) / 64);
+                const int kt = (h->mh[i].k + 127) / 128;
+                for (int ti = 0; ti < kt; ++ti)
+                    for (int tj = 0; tj <= ti; ++tj) sy.push_back(SyrkItem{i, ti, tj});
+            }
+        if ((rc = upload(cap, &h->cap_d, &h->ncap))) return rc;
+        if ((rc = upload(sy, &h->syrk_d, &h->nsyrk))) return rc;
     }
     HIP_TRY(hipEventCreateWithFlags(&h->fork, hipEventDisableTiming));
 
@@ -582,6 +694,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
     h->s1_nt.abf = gbf;
     h->s3_tn.ta = true;
     h->warm_nt.tb = true;
+    h->polish_nt.tb = true;
     for (int i = 0; i < n; ++i) {
         MatDev& m = h->mh[i];
         // Loewdin re-orthogonalization of the unit rows of A (-> F) and V (-> W):
@@ -611,6 +724,16 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         } else {
             p = make_prob(m.W, m.k, m.Manc, m.n, m.A, m.K_ld, m.k, m.n, m.m);
             h->warm_nn.h.push_back(p);
+        }
+        if (m.klen) {
+            // after the factor phase: A_rows = V op(M) with V's rows (length kpad)
+            if (m.tall) {
+                p = make_prob(m.V, m.kpad, m.Manc, m.n, m.A, m.K_ld, m.k, m.m, m.n);
+                h->polish_nt.h.push_back(p);
+            } else {
+                p = make_prob(m.V, m.kpad, m.Manc, m.n, m.A, m.K_ld, m.k, m.n, m.m);
+                h->polish_nn.h.push_back(p);
+            }
         }
         // projectors X^T diag(d) X
         const bool square = m.m == m.n;
@@ -649,7 +772,8 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             h->s3_nn.h.push_back(p);
         }
     }
-    for (GemmGroup* g : {&h->warm_nt, &h->warm_nn, &h->lowdin_eF, &h->lowdin_F, &h->lowdin_eW,
+    for (GemmGroup* g : {&h->warm_nt, &h->warm_nn, &h->polish_nt, &h->polish_nn,
+                         &h->lowdin_eF, &h->lowdin_F, &h->lowdin_eW,
                          &h->lowdin_W, &h->proj,
                          &h->s1_nn_a, &h->s1_nn_b, &h->s1_nt, &h->s2_nn, &h->s3_tn, &h->s3_nn})
         if ((rc = upload_group(h, *g))) return rc;
@@ -712,6 +836,7 @@ void sc_default_hparams(sc_hparams* hp) {
     hp->jacobi_tol = 0.0f;
     hp->sync_check = 1;
     hp->warm_start = 1;
+    hp->precondition = 1;
 }
 
 const char* sc_last_error(void) { return g_err.c_str(); }
@@ -754,7 +879,6 @@ int sc_opt_create(sc_handle* out, int n_mats, const int64_t* rows, const int64_t
     h->wdt = w_dtype;
     h->gdt = g_dtype;
     h->hp = *hp;
-    h->tol = hp->jacobi_tol > 0.0f ? hp->jacobi_tol : kDefaultTol;
     rc = build(h, rows, cols);
     if (rc) {
         std::string msg = g_err;
@@ -1002,10 +1126,25 @@ int sc_get_stats(sc_handle h, sc_stats* out, int* per_mat_sweeps) {
         const MatFlags& f = h->flags_h[i];
         out->sweeps_max = std::max(out->sweeps_max, f.sweeps);
         if (h->refreshes > 0 && !f.converged) out->not_converged += 1;
+        out->factor_sweeps_max = std::max(out->factor_sweeps_max, f.sweep_base);
+        out->factor_rejected += f.chol_fail;
         if (per_mat_sweeps) per_mat_sweeps[i] = f.sweeps;
     }
     out->nonfinite_grad = status[0] != 0;
     out->nonfinite_anchor = status[1] != 0;
+    return SC_OK;
+}
+
+int sc_get_sweep_counts(sc_handle h, int* total, int* factor) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    DeviceGuard g(h->device);
+    HIP_TRY(hipDeviceSynchronize());
+    HIP_TRY(hipMemcpy(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n, hipMemcpyDeviceToHost));
+    for (int i = 0; i < h->n; ++i) {
+        if (total) total[i] = h->flags_h[i].sweeps;
+        if (factor) factor[i] = h->flags_h[i].sweep_base;
+    }
     return SC_OK;
 }
 

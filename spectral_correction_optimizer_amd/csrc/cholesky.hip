@@ -1,0 +1,380 @@
+// Cholesky preconditioning of the Jacobi SVD for operands at least twice as
+// long as wide (K >= 2k).
+//
+// One-sided Jacobi only ever looks at the Gram of the operand's columns.  With
+// C = A^T A = L L^T, the k x k operand R = L^T has exactly that Gram, so the
+// same rotations can be found on rows k long instead of K (the factor phase);
+// afterwards A = M V is formed once and polished by ordinary sweeps.  The
+// factor phase is only worth it if R's Gram matches A's to about the sweep
+// tolerance, otherwise the polish needs many full-length sweeps; hence:
+//
+//   chol_syrk    C = A^T A (lower 128 x 128 tiles), float32 MFMA products whose
+//                running sums are folded into float64 every 256 columns, the
+//                same scheme as the pair Gram of the sweeps;
+//   chol_diag    factor a 64 x 64 diagonal tile in float64 (LDS);
+//   chol_panel   L_ib,jb = C_ib,jb L_jb,jb^-T below it (float64);
+//   chol_update  C_ib,kb -= L_ib,jb L_kb,jb^T for the trailing lower tiles
+//                (float64 FMA, register-blocked);
+//   chol_commit  rows of A <- float32(rows of L), zero beyond the diagonal.
+//
+// Rounding L to float32 perturbs each Gram entry by about 2^-24 of the two
+// columns' norms, well inside the sweep tolerance.
+//
+// A pivot that keeps less than a tenth of its column's squared norm (the
+// column nearly lies in the span of the previous ones) rejects the matrix: it
+// sits the factor phase out and runs plain sweeps in the polishing phase.
+// Columns at or below the zero floor get a zero pivot.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace scopt {
+
+namespace {
+constexpr int CT = 64;   // Cholesky tile
+constexpr double kKeep = 0.1;
+
+__device__ __forceinline__ bool chol_active(const MatDev& md, const MatFlags& f, int jb) {
+    return !f.chol_fail && jb * CT < md.k;
+}
+}  // namespace
+
+// ---------------------------------------------------------------------------------
+// C = A^T A over the rows of the Jacobi operand (row j = column j of A, length
+// K_ld, zero padded).  One workgroup per lower 128 x 128 tile (ti >= tj); four
+// waves of 64 x 64, each 2 x 2 v_mfma_f32_32x32x2f32 blocks.  LDS holds 32
+// columns of both row strips k-major (row stride 160 floats) with the row index
+// XOR-swizzled by 8 * ((k >> 2) & 7): the transposing stores and the fragment
+// reads are both free of bank conflicts.  The diagonal tiles read one strip.
+namespace {
+constexpr int SB = 128, SK = 32, SLD = 160, SFOLD = 256;
+}
+
+__global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict__ mats,
+                                                        const SyrkItem* __restrict__ items) {
+    __shared__ float Xs[2][SK][SLD];
+    const SyrkItem it = items[blockIdx.x];
+    const MatDev& md = mats[it.mat];
+    const bool diag = it.ti == it.tj;
+    const int k = md.k, ld = md.K_ld;
+    const int r0[2] = {it.ti * SB, it.tj * SB};
+
+    // loader: 128 rows x 32 columns = 1024 float4 per strip, 4 per thread;
+    // slot s: row = s >> 3, q = s & 7 (columns 4q .. 4q + 3 of the stage)
+    const int nstrip = diag ? 1 : 2;
+    float4 reg[2][4];
+    auto gload = [&](int x0) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if (t >= nstrip) break;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = threadIdx.x + 256 * e;
+                const int row = r0[t] + (s >> 3), q = s & 7;
+                reg[t][e] = row < k ? *(const float4*)(md.A + (int64_t)row * ld + x0 + 4 * q)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            if (t >= nstrip) break;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = threadIdx.x + 256 * e;
+                const int q = s & 7, col = (s >> 3) ^ (8 * q);
+                Xs[t][4 * q + 0][col] = reg[t][e].x;
+                Xs[t][4 * q + 1][col] = reg[t][e].y;
+                Xs[t][4 * q + 2][col] = reg[t][e].z;
+                Xs[t][4 * q + 3][col] = reg[t][e].w;
+            }
+        }
+    };
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int hl = lane >> 5, ll = lane & 31;
+    const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;
+    const int sj = diag ? 0 : 1;
+    v16f acc[2][2];
+    double acc64[2][2][16];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                acc[a][b][r] = 0.0f;
+                acc64[a][b][r] = 0.0;
+            }
+    const int nst = ld / SK;  // K_ld is a multiple of 128
+    gload(0);
+    for (int st = 0; st < nst; ++st) {
+        lstore();
+        __syncthreads();
+        if (st + 1 < nst) gload((st + 1) * SK);
+#pragma unroll
+        for (int kk = 0; kk < SK; kk += 2) {
+            const int kr = kk + hl;
+            const int sw = 8 * ((kk >> 2) & 7);
+            const float a0 = Xs[0][kr][(wr + ll) ^ sw], a1 = Xs[0][kr][(wr + 32 + ll) ^ sw];
+            const float b0 = Xs[sj][kr][(wc + ll) ^ sw], b1 = Xs[sj][kr][(wc + 32 + ll) ^ sw];
+            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+        }
+        if (((st + 1) * SK) % SFOLD == 0 || st + 1 == nst) {
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        acc64[a][b][r] += (double)acc[a][b][r];
+                        acc[a][b][r] = 0.0f;
+                    }
+        }
+        __syncthreads();
+    }
+    // 32x32 output layout: lane l, register r -> row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = r0[0] + wr + 32 * a + 8 * (r >> 2) + 4 * hl + (r & 3);
+                const int col = r0[1] + wc + 32 * b + ll;
+                if (row < k && col < k) md.chol[(int64_t)row * k + col] = acc64[a][b][r];
+            }
+}
+
+// ---------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void chol_diag_kernel(const MatDev* __restrict__ mats,
+                                                        MatFlags* __restrict__ flags,
+                                                        const int* __restrict__ mat_idx, int jb) {
+    __shared__ double T[CT][CT + 1];
+    __shared__ double piv[CT];
+    __shared__ int fail;
+    const int i = mat_idx[blockIdx.x];
+    MatFlags& f = flags[i];
+    const MatDev& md = mats[i];
+    if (!chol_active(md, f, jb)) return;
+    const int k = md.k, r0 = jb * CT;
+    double* C = md.chol;  // [k][k], lower triangle
+    for (int idx = threadIdx.x; idx < CT * CT; idx += blockDim.x) {
+        const int r = idx >> 6, c = idx & 63;
+        const int gr = r0 + r, gc = r0 + c;
+        T[r][c] = (gr < k && gc < k) ? (c <= r ? C[(int64_t)gr * k + gc] : 0.0) : (r == c ? 1.0 : 0.0);
+    }
+    if (threadIdx.x == 0) fail = 0;
+    __syncthreads();
+    for (int c = 0; c < CT; ++c) {
+        if (threadIdx.x == 0) {
+            const int gc = r0 + c;
+            double l = 1.0;  // padding: identity
+            if (gc < k) {
+                const double orig = md.norm2[gc];
+                const double p = T[c][c];
+                if (orig <= (double)f.floor2) l = 0.0;  // zero column
+                else if (!(p > kKeep * orig)) fail = 1;
+                else l = sqrt(p);
+            }
+            piv[c] = l;
+        }
+        __syncthreads();
+        if (fail) break;
+        const double l = piv[c];
+        for (int r = c + 1 + threadIdx.x; r < CT; r += blockDim.x)
+            T[r][c] = l > 0.0 ? T[r][c] / l : 0.0;
+        __syncthreads();
+        const int rem = CT - c - 1;
+        for (int idx = threadIdx.x; idx < rem * rem; idx += blockDim.x) {
+            const int r = c + 1 + idx / rem, s = c + 1 + idx % rem;
+            if (s <= r) T[r][s] -= T[r][c] * T[s][c];
+        }
+        __syncthreads();
+    }
+    if (fail) {
+        if (threadIdx.x == 0) f.chol_fail = 1;
+        return;
+    }
+    for (int idx = threadIdx.x; idx < CT * CT; idx += blockDim.x) {
+        const int r = idx >> 6, c = idx & 63;
+        const int gr = r0 + r, gc = r0 + c;
+        if (gr < k && gc <= gr) C[(int64_t)gr * k + gc] = c < r ? T[r][c] : piv[r];
+    }
+}
+
+// X L^T = B for the tile rows below the diagonal tile:
+//   x_c = (b_c - sum_{s<c} x_s L[c][s]) / L[c][c], one thread per row.
+__global__ __launch_bounds__(256) void chol_panel_kernel(const MatDev* __restrict__ mats,
+                                                         const MatFlags* __restrict__ flags,
+                                                         const int* __restrict__ mat_idx, int jb) {
+    __shared__ double Lp[CT * (CT + 1) / 2];  // diagonal tile, packed lower triangle
+    __shared__ double B[CT][CT + 1];
+    const int i = mat_idx[blockIdx.y];
+    const MatFlags& f = flags[i];
+    const MatDev& md = mats[i];
+    if (!chol_active(md, f, jb)) return;
+    const int k = md.k, nbk = (k + CT - 1) / CT;
+    const int ib = jb + 1 + blockIdx.x;
+    if (ib >= nbk) return;
+    double* C = md.chol;
+    const int r0 = ib * CT, c0 = jb * CT;
+    for (int idx = threadIdx.x; idx < CT * CT; idx += blockDim.x) {
+        const int r = idx >> 6, c = idx & 63;
+        if (c <= r)
+            Lp[r * (r + 1) / 2 + c] =
+                (c0 + r < k) ? C[(int64_t)(c0 + r) * k + c0 + c] : (r == c ? 1.0 : 0.0);
+        B[r][c] = (r0 + r < k && c0 + c < k) ? C[(int64_t)(r0 + r) * k + c0 + c] : 0.0;
+    }
+    __syncthreads();
+    if (threadIdx.x < CT) {
+        const int r = threadIdx.x;
+        for (int c = 0; c < CT; ++c) {
+            const double* Lc = Lp + c * (c + 1) / 2;
+            double acc = B[r][c];
+            for (int s = 0; s < c; ++s) acc -= B[r][s] * Lc[s];
+            const double d = Lc[c];
+            B[r][c] = d > 0.0 ? acc / d : 0.0;
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < CT * CT; idx += blockDim.x) {
+        const int r = idx >> 6, c = idx & 63;
+        if (r0 + r < k && c0 + c < k) C[(int64_t)(r0 + r) * k + c0 + c] = B[r][c];
+    }
+}
+
+// C_ib,kb -= L_ib,jb L_kb,jb^T for jb < kb <= ib (the lower trailing tiles).
+// 16 x 16 threads, each a 4 x 4 block of outputs (rows ty + 16 a, columns
+// tx + 16 b); the two panels pass through LDS 32 columns at a time.
+__global__ __launch_bounds__(256) void chol_update_kernel(const MatDev* __restrict__ mats,
+                                                          const MatFlags* __restrict__ flags,
+                                                          const int* __restrict__ mat_idx, int jb) {
+    __shared__ double P[32][CT];  // L_ib,jb, k-major: P[s][r]
+    __shared__ double Q[32][CT];  // L_kb,jb, k-major: Q[s][c]
+    const int i = mat_idx[blockIdx.y];
+    const MatFlags& f = flags[i];
+    const MatDev& md = mats[i];
+    if (!chol_active(md, f, jb)) return;
+    const int k = md.k, nbk = (k + CT - 1) / CT;
+    const int nt = nbk - jb - 1;  // trailing tile rows of this matrix
+    const int t = blockIdx.x;
+    if (t >= nt * (nt + 1) / 2) return;
+    // t -> (a, b), 0 <= b <= a < nt, row by row over the lower triangle
+    int a = (int)((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
+    while ((a + 1) * (a + 2) / 2 <= t) ++a;
+    while (a * (a + 1) / 2 > t) --a;
+    const int b = t - a * (a + 1) / 2;
+    const int ri = (jb + 1 + a) * CT, rk = (jb + 1 + b) * CT, c0 = jb * CT;
+    double* C = md.chol;
+    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    double acc[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
+    for (int s0 = 0; s0 < CT; s0 += 32) {
+        for (int idx = threadIdx.x; idx < 32 * CT; idx += blockDim.x) {
+            const int r = idx >> 5, s = idx & 31;
+            const int gs = c0 + s0 + s;
+            P[s][r] = (ri + r < k && gs < k) ? C[(int64_t)(ri + r) * k + gs] : 0.0;
+            Q[s][r] = (rk + r < k && gs < k) ? C[(int64_t)(rk + r) * k + gs] : 0.0;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int s = 0; s < 32; ++s) {
+            double pv[4], qv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                pv[u] = P[s][ty + 16 * u];
+                qv[u] = Q[s][tx + 16 * u];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[u][v] = fma(pv[u], qv[v], acc[u][v]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int row = ri + ty + 16 * u, col = rk + tx + 16 * v;
+            if (row < k && col < k && col <= row) C[(int64_t)row * k + col] -= acc[u][v];
+        }
+}
+
+// Accepted factorizations: the rows of the Jacobi operand become float32 rows
+// of L (column j of R = L^T), klen long, zero beyond the diagonal.  A rejected
+// matrix keeps its operand and sits the factor phase out (done = 1).
+__global__ __launch_bounds__(256) void chol_commit_kernel(const MatDev* __restrict__ mats,
+                                                          MatFlags* __restrict__ flags,
+                                                          const int* __restrict__ mat_idx) {
+    const int i = mat_idx[blockIdx.y];
+    MatFlags& f = flags[i];
+    const MatDev& md = mats[i];
+    if (f.chol_fail) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) f.done = 1;
+        return;
+    }
+    const int k = md.k, klen = md.klen;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < (int64_t)k * klen;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int j = (int)(idx / klen), c = (int)(idx % klen);
+        md.A[(int64_t)j * md.K_ld + c] = (c <= j && c < k) ? (float)md.chol[(int64_t)j * k + c] : 0.0f;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) f.precond = 1;
+}
+
+hipError_t launch_chol_syrk(const MatDev* mats, const SyrkItem* items, int nitems, hipStream_t st) {
+    hipLaunchKernelGGL(chol_syrk_kernel, dim3(nitems), dim3(256), 0, st, mats, items);
+    return hipGetLastError();
+}
+
+hipError_t launch_cholesky(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
+                           int max_nbk, hipStream_t st) {
+    for (int jb = 0; jb < max_nbk; ++jb) {
+        hipLaunchKernelGGL(chol_diag_kernel, dim3(nmat), dim3(256), 0, st, mats, flags, mat_idx, jb);
+        const int nt = max_nbk - jb - 1;
+        if (nt > 0) {
+            hipLaunchKernelGGL(chol_panel_kernel, dim3(nt, nmat), dim3(256), 0, st, mats, flags,
+                               mat_idx, jb);
+            hipLaunchKernelGGL(chol_update_kernel, dim3(nt * (nt + 1) / 2, nmat), dim3(256), 0, st,
+                               mats, flags, mat_idx, jb);
+        }
+    }
+    hipLaunchKernelGGL(chol_commit_kernel, dim3(512, nmat), dim3(256), 0, st, mats, flags, mat_idx);
+    return hipGetLastError();
+}
+
+// Start of the polishing phase (A = M V already recomputed by a GEMM): clear
+// the convergence state, count the sweep cap from here, keep the work counters
+// of the factor phase apart.  The column order (perm) and the norms it was
+// sorted by (cnorm) carry over: the factor's Gram equals A's up to rounding.
+__global__ void phase2_reset_kernel(MatFlags* __restrict__ flags, const int* __restrict__ mat_idx,
+                                    int nmat) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= nmat) return;
+    MatFlags& f = flags[mat_idx[t]];
+    f.precond = 0;
+    f.done = 0;
+    f.converged = 0;
+    f.sweep_max = 0u;
+    f.sweep_base = f.sweeps;
+    f.rounds_pre = f.rounds_active;
+    f.pairs_pre = f.pairs_applied;
+}
+
+hipError_t launch_phase2_reset(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
+                               hipStream_t st) {
+    (void)mats;
+    hipLaunchKernelGGL(phase2_reset_kernel, dim3((nmat + 63) / 64), dim3(64), 0, st, flags, mat_idx,
+                       nmat);
+    return hipGetLastError();
+}
+
+}  // namespace scopt

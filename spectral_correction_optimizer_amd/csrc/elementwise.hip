@@ -342,6 +342,11 @@ __global__ __launch_bounds__(256) void init_flags_kernel(const MatDev* __restric
         f.done = 0;
         f.rounds_active = 0;
         f.pairs_applied = 0;
+        f.sweep_base = 0;
+        f.precond = 0;
+        f.chol_fail = 0;
+        f.rounds_pre = 0;
+        f.pairs_pre = 0;
     }
     // identity column order; column norms for the first sweep's ordering
     for (int j = threadIdx.x; j < md.kpad; j += blockDim.x) {

@@ -47,9 +47,12 @@ struct MatDev {
     double* gram;    // [nb/2][nsplit][2b][2b] split partial Gram blocks
     float* rot;      // [nb/2][2b][2b] R = Q - I of each pair
     int* rot_flag;   // [nb/2] 1 when the pair's rotation must be applied
-    int nsplit;      // K-splits of a pair Gram
-    int ksplit_len;  // K range of one split (multiple of 256)
-    int pad0;
+    int nsplit;      // K-splits of a pair Gram (room in `gram`; a phase may use fewer)
+    int klen;        // row length of the Cholesky-factor operand: k rounded up to 128 (0: none)
+    float tol;       // a pair is rotated when |a_p.a_q| / (|a_p| |a_q|) > tol
+    float tol_conv;  // a sweep whose largest such ratio is <= tol_conv ends the sweeps
+    int pad1;
+    double* chol;    // [k][k] Gram of A, then its Cholesky factor (lower triangle); klen > 0 only
 };
 
 // Per-matrix device flags / counters.
@@ -61,15 +64,21 @@ struct MatFlags {
     float floor2;            // squared column-norm floor: columns below are zero
     int rounds_active;       // rounds this matrix took part in (work accounting)
     int pairs_applied;       // pair rotations applied (work accounting)
-    int pad;
+    int sweep_base;          // sweeps done before the current phase (the cap counts from here)
+    int precond;             // 1 while the sweeps run on the Cholesky factor (short rows)
+    int chol_fail;           // 1 when the Gram's Cholesky factorization was rejected
+    int rounds_pre;          // rounds_active / pairs_applied at the end of the factor phase
+    int pairs_pre;
+    int pad[3];
 };
 
 // ---- work items ------------------------------------------------------------------
 
-struct GramItem { int mat, slot, split; };
-struct SolveItem { int mat, slot; };
+struct GramItem { int mat, slot, split, x0, x1; };  // operand columns [x0, x1) of one split
+struct SolveItem { int mat, slot, nsplit; };
 struct ApplyItem { int mat, slot, which, chunk; };  // which: 0 = A rows, 1 = V rows
 struct Chunk { int mat; int64_t off; int len; };    // elementwise chunk of one matrix
+struct SyrkItem { int mat, ti, tj; };               // lower 128 x 128 tile (ti >= tj) of A^T A
 
 // ---- grouped GEMM ----------------------------------------------------------------
 
@@ -126,15 +135,28 @@ hipError_t launch_filter(const MatDev* mats, int nmat, float tau, int max_kpad, 
 hipError_t launch_jacobi_gram(const MatDev* mats, const MatFlags* flags, const GramItem* gi,
                               int ngi, int round, hipStream_t st);
 hipError_t launch_jacobi_solve(const MatDev* mats, MatFlags* flags, const SolveItem* si, int nsi,
-                               int round, float tol, hipStream_t st);
+                               int round, hipStream_t st);
 hipError_t launch_jacobi_apply(const MatDev* mats, const MatFlags* flags, const ApplyItem* ai,
                                int nai, int round, hipStream_t st);
 // At a matrix's sweep start: order its columns by decreasing norm (perm).
 hipError_t launch_jacobi_sort(const MatDev* mats, const MatFlags* flags, const int* mat_idx,
                               int nmat, int round, hipStream_t st);
 hipError_t launch_jacobi_sweep_end(const MatDev* mats, MatFlags* flags, const int* mat_idx,
-                                   int nmat, int round, int max_sweeps, float tol,
+                                   int nmat, int round, int max_sweeps,
                                    hipStream_t st);
+
+// ---- Cholesky preconditioning of tall operands ------------------------------------------
+
+// chol = A^T A (lower 128 x 128 tiles listed in items), float64 sums.
+hipError_t launch_chol_syrk(const MatDev* mats, const SyrkItem* items, int nitems, hipStream_t st);
+// chol = L L^T (in place, lower triangle) for the matrices in mat_idx; on success the
+// rows of A become the rows of L (length klen) and precond = 1, else chol_fail = 1
+// and done = 1 (the matrix sits the factor phase out).  max_nbk: largest ceil(k / 64).
+hipError_t launch_cholesky(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
+                           int max_nbk, hipStream_t st);
+// Start of the polishing phase for the matrices in mat_idx (A already recomputed).
+hipError_t launch_phase2_reset(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
+                               hipStream_t st);
 
 // dst[c * ld_dst + r] = src[r * ld_src + c] for r < rows, c < cols
 hipError_t launch_transpose(const float* src, int rows, int cols, int ld_src, float* dst,

@@ -75,9 +75,7 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
     const int nb = md.nb;
     int bI, bJ;
     rr_pair(nb, round % (nb - 1), it.slot, &bI, &bJ);
-    const int x_begin = it.split * md.ksplit_len;
-    int x_end = x_begin + md.ksplit_len;
-    if (x_end > md.K_ld) x_end = md.K_ld;
+    const int x_begin = it.x0, x_end = it.x1;
 
     // loader: 64 rows x 32 columns = 512 float4 slots, 2 per thread
     // slot s: row = s >> 3, q = s & 7 (columns 4q..4q+3 of the stage)
@@ -122,7 +120,7 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
             acc[t][r] = 0.0f;
             acc64[t][r] = 0.0;
         }
-    const int nst = (x_end - x_begin) / KC;  // K_ld and split lengths are multiples of KC
+    const int nst = (x_end - x_begin) / KC;  // split bounds are multiples of KC
     if (nst > 0) {
         gload(x_begin);
         lstore(0);
@@ -193,7 +191,7 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
 __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict__ mats,
                                                         MatFlags* __restrict__ flags,
                                                         const SolveItem* __restrict__ items,
-                                                        int round, float tol) {
+                                                        int round) {
     // G: float32 working copy of the pair Gram (guides the rotation angles).
     // R: the accumulated rotation minus the identity, Q = I + R, kept directly
     // in float32.  Each 2x2 rotation is computed in float64 and enters R through
@@ -212,6 +210,7 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
     if (fl.done) return;
     const MatDev& md = mats[it.mat];
     const float floor2 = fl.floor2;
+    const float tol = md.tol;
     const int tid = threadIdx.x;
     int bI, bJ;
     rr_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
@@ -223,7 +222,7 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
     for (int e = 0; e < 16; ++e) {
         const int idx = tid + 256 * e;
         double s = 0.0;
-        for (int sp = 0; sp < md.nsplit; ++sp) s += gp[(int64_t)sp * PW * PW + idx];
+        for (int sp = 0; sp < it.nsplit; ++sp) s += gp[(int64_t)sp * PW * PW + idx];
         gv[e] = s;
         G[idx >> 6][idx & 63] = (float)s;
         R[idx >> 6][idx & 63] = 0.0f;
@@ -453,7 +452,7 @@ hipError_t launch_jacobi_sort(const MatDev* mats, const MatFlags* flags, const i
 // converged when nothing above tolerance was seen during the sweep.
 __global__ void jac_sweep_end_kernel(const MatDev* __restrict__ mats, MatFlags* __restrict__ flags,
                                      const int* __restrict__ mat_idx, int nmat, int round,
-                                     int max_sweeps, float tol) {
+                                     int max_sweeps) {
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= nmat) return;
     const int i = mat_idx[t];
@@ -465,10 +464,10 @@ __global__ void jac_sweep_end_kernel(const MatDev* __restrict__ mats, MatFlags* 
     f.sweeps += 1;
     const float mo = __uint_as_float(f.sweep_max);
     f.sweep_max = 0u;
-    if (!(mo > tol)) {
+    if (!(mo > mats[i].tol_conv)) {
         f.converged = 1;
         f.done = 1;
-    } else if (f.sweeps >= max_sweeps) {
+    } else if (f.sweeps - f.sweep_base >= max_sweeps) {
         f.done = 1;
     }
 }
@@ -480,8 +479,8 @@ hipError_t launch_jacobi_gram(const MatDev* mats, const MatFlags* flags, const G
 }
 
 hipError_t launch_jacobi_solve(const MatDev* mats, MatFlags* flags, const SolveItem* si, int nsi,
-                               int round, float tol, hipStream_t st) {
-    hipLaunchKernelGGL(jac_solve_kernel, dim3(nsi), dim3(256), 0, st, mats, flags, si, round, tol);
+                               int round, hipStream_t st) {
+    hipLaunchKernelGGL(jac_solve_kernel, dim3(nsi), dim3(256), 0, st, mats, flags, si, round);
     return hipGetLastError();
 }
 
@@ -492,10 +491,10 @@ hipError_t launch_jacobi_apply(const MatDev* mats, const MatFlags* flags, const 
 }
 
 hipError_t launch_jacobi_sweep_end(const MatDev* mats, MatFlags* flags, const int* mat_idx,
-                                   int nmat, int round, int max_sweeps, float tol,
+                                   int nmat, int round, int max_sweeps,
                                    hipStream_t st) {
     hipLaunchKernelGGL(jac_sweep_end_kernel, dim3((nmat + 63) / 64), dim3(64), 0, st, mats, flags,
-                       mat_idx, nmat, round, max_sweeps, tol);
+                       mat_idx, nmat, round, max_sweeps);
     return hipGetLastError();
 }
 

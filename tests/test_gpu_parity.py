@@ -128,7 +128,7 @@ def test_svd_self_consistency():
     """GPU factors reconstruct M and are orthonormal to float32 accuracy."""
     import spectral_correction_optimizer_amd as sco
     dev = torch.device("cuda")
-    for (m, n) in [(320, 192), (192, 320), (256, 256)]:
+    for (m, n) in [(320, 192), (192, 320), (256, 256), (640, 160), (160, 640)]:
         say(f"case: svd self-check {m}x{n}")
         mi = gen.MatrixInputs(97, 0, 0, m, n)
         pay, M = gen.stored(mi.m0(), "f32")
@@ -145,6 +145,58 @@ def test_svd_self_consistency():
         say(f"  recon {rec:.2e} orthU {ou:.2e} orthV {ov:.2e} s err {se:.2e} stats {opt.stats()}")
         assert rec < 1e-5 and ou < 1e-5 and ov < 1e-5 and se < 1e-5
         opt.close()
+
+
+@pytest.mark.parametrize("precondition", [1, 0])
+def test_cholesky_preconditioned_shapes(precondition):
+    """Operands at least twice as long as wide run their first sweeps on the
+    Cholesky factor of the Gram, then polish on A = M V; both settings meet the
+    gates, and the factor phase really ran (or did not)."""
+    shapes = [(520, 96), (96, 520), (1024, 256), (256, 640), (200, 136)]
+    say(f"case: precondition={precondition} {shapes}, refresh every 2 steps, 4 steps")
+    sc = Scenario(shapes, [(93, 0, i) for i in range(len(shapes))], steps=4, anchor_every=2)
+    rep = sc.run(gpu_hp=dict(precondition=precondition))
+    Scenario.check(rep)
+    st = rep["stats"]
+    say(f"  stats {st}")
+    assert st["factor_rejected"] == 0
+    assert (st["factor_sweeps_max"] > 0) == bool(precondition)
+
+
+def test_cholesky_rejected_for_rank_deficient_operand():
+    """Warm start from a full-rank anchor's factors, then a rank-8 anchor: the
+    operand A = M V_prev has linearly dependent columns, the Gram factorization
+    is rejected and the matrix runs the plain sweeps; factors and G_filt still
+    agree with the oracle."""
+    import spectral_correction_optimizer_amd as sco
+    dev = torch.device("cuda")
+    shapes = [(384, 96), (96, 384)]
+    say(f"case: rank-8 anchors {shapes} after a full-rank refresh, rejected factorization")
+    opt = sco.SpectralAdamW(shapes, device=dev)
+    full = [gen.MatrixInputs(94, 0, i, m, n) for i, (m, n) in enumerate(shapes)]
+    low = [gen.MatrixInputs(94, 1, i, m, n, r0=8, noise=False) for i, (m, n) in enumerate(shapes)]
+    for i, mi in enumerate(full):
+        opt.set_state(i, "m_anc", to_dev(gen.stored(mi.m0(), "f32")[0], "f32", dev))
+    opt.refresh()
+    Ms = []
+    for i, mi in enumerate(low):
+        pay, M = gen.stored(mi.m0(), "f32")
+        Ms.append(M)
+        opt.set_state(i, "m_anc", to_dev(pay, "f32", dev))
+    opt.refresh()
+    st = opt.stats()
+    say(f"  stats {st}")
+    assert st["factor_rejected"] == 2 and st["not_converged"] == 0
+    W = [torch.zeros(m, n, device=dev) for m, n in shapes]
+    G = [gen.stored(mi.g_mask(0), "f32") for mi in full]
+    opt.step(W, [to_dev(p, "f32", dev) for p, _ in G])
+    for i, M in enumerate(Ms):
+        U, s, V, _ = oracle.svd(M)
+        ref = oracle.project(U, oracle.tikhonov(s, opt.hp["tau_p"]), V, G[i][1])
+        err = relf(from_dev(opt.get_filtered(i)), ref)
+        say(f"  mat {i}: relF G_filt {err:.3e}")
+        assert err <= 1e-4
+    opt.close()
 
 
 def test_determinism_bitwise():
