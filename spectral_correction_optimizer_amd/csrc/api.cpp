@@ -96,11 +96,18 @@ struct Prof {
 };
 int round_up(int x, int a) { return (x + a - 1) / a * a; }
 
-// K-splits of a pair Gram over rows of length len (a multiple of 128): about 8
-// splits of a multiple of 256 columns each, so that the fp64 folds of the Gram
-// kernel see whole 256-column chunks.
-int split_len(int len) { return std::max(256, round_up((len + 7) / 8, 256)); }
-int split_count(int len) { return (len + split_len(len) - 1) / split_len(len); }
+// K-splits of a pair Gram over rows of length len (a multiple of 128): about nt
+// splits (nt <= 8) of a multiple of 256 columns each, so that the fp64 folds of
+// the Gram kernel see whole 256-column chunks.
+constexpr int kMaxSplits = 8;
+int split_len(int len, int nt) { return std::max(256, round_up((len + nt - 1) / nt, 256)); }
+int split_count(int len, int nt) { return (len + split_len(len, nt) - 1) / split_len(len, nt); }
+// Splits per pair for a launch over `pairs` pairs: enough workgroups to fill the
+// chip (about 2048), no more, since every split writes and the solve re-reads a
+// 64 x 64 float64 partial.
+int splits_for(int pairs) {
+    return std::min(kMaxSplits, std::max(1, (2048 + pairs - 1) / std::max(pairs, 1)));
+}
 
 }  // namespace
 
@@ -515,8 +522,8 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         m.numel = (int64_t)m.m * m.n;
         // Cholesky-preconditioned when the operand is at least twice as long as wide
         m.klen = (h->hp.precondition && m.K >= 2 * m.k) ? round_up(m.k, 128) : 0;
-        m.nsplit = split_count(m.K_ld);
-        if (m.klen) m.nsplit = std::max(m.nsplit, split_count(m.klen));
+        m.nsplit = split_count(m.K_ld, kMaxSplits);  // capacity of the partial buffer
+        if (m.klen) m.nsplit = std::max(m.nsplit, split_count(m.klen, kMaxSplits));
         const size_t f = sizeof(float);
         const size_t mn = (size_t)m.numel * f;
         const size_t kk = (size_t)m.k * m.k * f;
@@ -642,11 +649,15 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             std::vector<ApplyItem> ai;
             std::vector<int> mats;
             auto& L = G.L[which];
+            int pairs = 0;
+            for (int i : gm[g])
+                if (which != 2 || h->mh[i].klen) pairs += h->mh[i].nb / 2;
+            const int nt = splits_for(pairs);
             for (int i : gm[g]) {
                 const MatDev& m = h->mh[i];
                 if (which == 2 && !m.klen) continue;  // polish: preconditioned matrices only
                 const int len = (which == 1 && m.klen) ? m.klen : m.K_ld;
-                const int sl = split_len(len), ns = split_count(len);
+                const int sl = split_len(len, nt), ns = split_count(len, nt);
                 mats.push_back(i);
                 L.max_nb = std::max(L.max_nb, m.nb);
                 for (int s = 0; s < m.nb / 2; ++s) {

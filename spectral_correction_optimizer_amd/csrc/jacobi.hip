@@ -173,7 +173,8 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
         if (st + 1 < nst) lstore(b ^ 1);
         __syncthreads();
     }
-    // 16x16 output layout: lane l, register r -> row 4 (l / 16) + r, column l % 16
+    // 16x16 output layout: lane l, register r -> row 4 (l / 16) + r, column l % 16.
+    // Only the upper tiles are stored; the solve mirrors them.
     double* out = md.gram + ((int64_t)it.slot * md.nsplit + it.split) * (PW * PW);
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
@@ -182,7 +183,6 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * ti[t] + 4 * (lane >> 4) + r, col = 16 * tj[t] + (lane & 15);
             out[row * PW + col] = acc64[t][r];
-            if (ti[t] != tj[t]) out[col * PW + row] = acc64[t][r];
         }
     }
 }
@@ -192,16 +192,19 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
                                                         MatFlags* __restrict__ flags,
                                                         const SolveItem* __restrict__ items,
                                                         int round) {
-    // G: float32 working copy of the pair Gram (guides the rotation angles).
+    // G: float32 working copy of the pair Gram, scaled by 1 / max diagonal so
+    // that the solve does not depend on the matrix's magnitude.
     // R: the accumulated rotation minus the identity, Q = I + R, kept directly
-    // in float32.  Each 2x2 rotation is computed in float64 and enters R through
-    // (c - 1) = -t s / (1 + sqrt(1 + t^2)) and s, so a tiny rotation is carried
-    // exactly (storing Q itself in float32 would round c to 1 while s != 0, a
-    // biased growth of the column norms over thousands of rotations).
+    // in float32.  Each 2x2 rotation enters R through (c - 1) = -t s / (1 + h),
+    // h = sqrt(1 + t^2), and s, so a tiny rotation is carried exactly (storing
+    // Q itself in float32 would round c to 1 while s != 0, a biased growth of
+    // the column norms over thousands of rotations).  c = 1 / h and s = t c
+    // satisfy c^2 + s^2 = 1 to float32 rounding, so float32 parameters suffice.
     __shared__ float G[PW][PW + 1];
     __shared__ float R[PW][PW + 1];
     __shared__ double dg[PW];
     __shared__ float red[4];
+    __shared__ double redd[4];
     __shared__ float cs_s[PW / 2], cs_cm1[PW / 2], cs_cf[PW / 2];
     __shared__ int pp[PW / 2], qq[PW / 2];
 
@@ -209,26 +212,37 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
     MatFlags& fl = flags[it.mat];
     if (fl.done) return;
     const MatDev& md = mats[it.mat];
-    const float floor2 = fl.floor2;
     const float tol = md.tol;
     const int tid = threadIdx.x;
     int bI, bJ;
     rr_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
 
-    // 1. sum split partials (fixed order) into fp64, keep fp32 copy in LDS
+    // 1. sum split partials (fixed order) into fp64; the partials hold the upper
+    //    16x16 tiles only, an entry of a lower tile is read at its mirror position
     const double* gp = md.gram + (int64_t)it.slot * md.nsplit * (PW * PW);
     double gv[16];
+    double dmax = 0.0;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         const int idx = tid + 256 * e;
+        const int row = idx >> 6, col = idx & 63;
+        const int src = (row >> 4) <= (col >> 4) ? idx : col * PW + row;
         double s = 0.0;
-        for (int sp = 0; sp < it.nsplit; ++sp) s += gp[(int64_t)sp * PW * PW + idx];
+        for (int sp = 0; sp < it.nsplit; ++sp) s += gp[(int64_t)sp * PW * PW + src];
         gv[e] = s;
-        G[idx >> 6][idx & 63] = (float)s;
         R[idx >> 6][idx & 63] = 0.0f;
-        if ((idx >> 6) == (idx & 63)) dg[idx & 63] = s;
+        if ((idx >> 6) == (idx & 63)) {
+            dg[idx & 63] = s;
+            dmax = fmax(dmax, s);
+        }
     }
+    for (int o = 32; o > 0; o >>= 1) dmax = fmax(dmax, __shfl_xor(dmax, o));
+    if ((tid & 63) == 0) redd[tid >> 6] = dmax;
     __syncthreads();
+    dmax = fmax(fmax(redd[0], redd[1]), fmax(redd[2], redd[3]));
+    const double scale = dmax > 0.0 ? 1.0 / dmax : 1.0;
+    const double floor2d = (double)fl.floor2;
+    const float floor2 = (float)(floor2d * scale);
 
     // 2. largest relative off-diagonal over columns above the zero floor
     float mo = 0.0f;
@@ -236,9 +250,10 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
     for (int e = 0; e < 16; ++e) {
         const int idx = tid + 256 * e;
         const int a = idx >> 6, b = idx & 63;
+        G[a][b] = (float)(gv[e] * scale);
         if (a < b) {
             const double da = dg[a], db = dg[b];
-            if (da > (double)floor2 && db > (double)floor2) {
+            if (da > floor2d && db > floor2d) {
                 float o = (float)(fabs(gv[e]) / sqrt(da * db));
                 mo = fmaxf(mo, o);
             }
@@ -257,39 +272,66 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
         return;
     }
 
-    // 3. one cyclic sweep of 2x2 rotations on G, accumulating R
+    // 3. one cyclic sweep of 2x2 rotations on G (G <- J^T G J), accumulating R
     for (int ir = 0; ir < PW - 1; ++ir) {
         if (tid < PW / 2) {
             int p, q;
             rr_pair(PW, ir, tid, &p, &q);
-            const double gpp = G[p][p], gqq = G[q][q], gpq = G[p][q];
-            double c = 1.0, s = 0.0, cm1 = 0.0;
-            if (gpp > floor2 && gqq > floor2 && fabs(gpq) > tol * sqrt(gpp * gqq)) {
-                const double zeta = (gqq - gpp) / (2.0 * gpq);
-                const double t = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + hypot(1.0, zeta));
-                const double h = sqrt(1.0 + t * t);
-                c = 1.0 / h;
-                s = t / h;
-                cm1 = -t * s / (1.0 + h);
+            const float gpp = G[p][p], gqq = G[q][q], gpq = G[p][q];
+            float c = 1.0f, s = 0.0f, cm1 = 0.0f;
+            if (gpp > floor2 && gqq > floor2 && fabsf(gpq) > tol * (sqrtf(gpp) * sqrtf(gqq))) {
+                const float zeta = (gqq - gpp) / (2.0f * gpq);
+                const float az = fabsf(zeta);
+                // t = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)), without overflow
+                const float den = az < 1e18f ? az + sqrtf(1.0f + az * az) : 2.0f * az;
+                const float t = copysignf(1.0f / den, zeta);
+                const float h = sqrtf(1.0f + t * t);
+                c = 1.0f / h;
+                s = t * c;
+                cm1 = -t * s / (1.0f + h);
             }
-            cs_s[tid] = (float)s;
-            cs_cm1[tid] = (float)cm1;
-            cs_cf[tid] = (float)c;
+            cs_s[tid] = s;
+            cs_cm1[tid] = cm1;
+            cs_cf[tid] = c;
             pp[tid] = p;
             qq[tid] = q;
         }
         __syncthreads();
-        // columns of G and R: [col_p, col_q] <- [c col_p - s col_q, s col_p + c col_q]
-        // (for R: plus (J - I), i.e. (c - 1) on the diagonal and +-s off it)
+        // G: each 2x2 block (rows p_i, q_i; columns p_j, q_j), i <= j, is
+        // rotated on both sides in one pass and mirrored (the pairs of a step are
+        // disjoint, so the blocks are independent)
+        for (int w = tid; w < (PW / 2) * (PW / 2); w += 256) {
+            const int i = w >> 5, j = w & 31;
+            if (i > j) continue;
+            const float si = cs_s[i], sj = cs_s[j];
+            if (si == 0.0f && sj == 0.0f) continue;
+            const float ci = cs_cf[i], cj = cs_cf[j];
+            const int pi = pp[i], qi = qq[i], pj = pp[j], qj = qq[j];
+            const float x00 = G[pi][pj], x01 = G[pi][qj], x10 = G[qi][pj], x11 = G[qi][qj];
+            // columns: [x_p, x_q] <- [c x_p - s x_q, s x_p + c x_q]
+            const float y00 = cj * x00 - sj * x01, y01 = sj * x00 + cj * x01;
+            const float y10 = cj * x10 - sj * x11, y11 = sj * x10 + cj * x11;
+            // rows
+            const float z00 = ci * y00 - si * y10, z10 = si * y00 + ci * y10;
+            const float z01 = ci * y01 - si * y11, z11 = si * y01 + ci * y11;
+            G[pi][pj] = z00;
+            G[pi][qj] = z01;
+            G[qi][pj] = z10;
+            G[qi][qj] = z11;
+            if (i != j) {
+                G[pj][pi] = z00;
+                G[qj][pi] = z01;
+                G[pj][qi] = z10;
+                G[qj][qi] = z11;
+            }
+        }
+        // R: columns p, q (plus (J - I): (c - 1) on the diagonal and +-s off it)
         for (int w = tid; w < (PW / 2) * PW; w += 256) {
             const int i = w >> 6, a = w & 63;
             const float s = cs_s[i];
             if (s != 0.0f) {
-                const float cf = cs_cf[i], cm1 = cs_cm1[i];
+                const float cm1 = cs_cm1[i];
                 const int p = pp[i], q = qq[i];
-                const float x = G[a][p], y = G[a][q];
-                G[a][p] = cf * x - s * y;
-                G[a][q] = s * x + cf * y;
                 const float xr = R[a][p], yr = R[a][q];
                 float np = fmaf(cm1, xr, xr) - s * yr;
                 float nq = fmaf(cm1, yr, yr) + s * xr;
@@ -305,25 +347,12 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
             }
         }
         __syncthreads();
-        // rows of G
-        for (int w = tid; w < (PW / 2) * PW; w += 256) {
-            const int i = w >> 6, bcol = w & 63;
-            const float s = cs_s[i];
-            if (s != 0.0f) {
-                const float cf = cs_cf[i];
-                const int p = pp[i], q = qq[i];
-                const float x = G[p][bcol], y = G[q][bcol];
-                G[p][bcol] = cf * x - s * y;
-                G[q][bcol] = s * x + cf * y;
-            }
-        }
-        __syncthreads();
     }
     // 4. R row-major [b][a] (X_new[a] = X[a] + sum_b R[b][a] X[b])
     float* Rg = md.rot + (int64_t)it.slot * PW * PW;
     for (int idx = tid; idx < PW * PW; idx += 256) Rg[idx] = R[idx >> 6][idx & 63];
     // rotated squared column norms (diagonal of Q^T G Q) for the next sweep's ordering
-    if (tid < PW) md.cnorm[pair_row(md, bI, bJ, tid)] = G[tid][tid];
+    if (tid < PW) md.cnorm[pair_row(md, bI, bJ, tid)] = (float)(G[tid][tid] * dmax);
     if (tid == 0) {
         *rflag = 1;
         atomicAdd(&fl.pairs_applied, 1);
@@ -331,16 +360,26 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
 }
 
 // ---------------------------------------------------------------------------------
+namespace {
+// Row of the pair block fed by lane half hl at contraction step s of the apply.
+// The order is chosen so that a lane's 32 B operands are exactly the 32 rows of
+// its 32x32 MFMA outputs (row 8 (r / 4) + 4 hl + r % 4 of acc0, 32 more of acc1).
+__device__ __forceinline__ int apply_row(int s, int hl) {
+    return 32 * (s >> 4) + 8 * ((s & 15) >> 2) + 4 * hl + (s & 3);
+}
+constexpr int RLD = 72;  // LDS row stride of R: rows 4 apart fall 32 banks apart
+}  // namespace
+
 __global__ __launch_bounds__(256) void jac_apply_kernel(const MatDev* __restrict__ mats,
                                                         const MatFlags* __restrict__ flags,
                                                         const ApplyItem* __restrict__ items,
                                                         int round) {
     // A workgroup updates 64 rows x 128 columns; wave w owns columns
-    // [x0 + 32 w, x0 + 32 w + 32).  Only R goes through LDS: each lane loads its
-    // column's 32 rows of one parity straight into registers, which are exactly
-    // the MFMA B operands it needs (B[k][j] = X[b][n], lane half hl supplies
-    // b = kb + hl), so many loads are in flight and LDS stays small.
-    __shared__ float Rs[PW][PW + 32];
+    // [x0 + 32 w, x0 + 32 w + 32).  Only R goes through LDS: each lane loads
+    // 32 rows of its column straight into registers; they are both its MFMA B
+    // operands (B[k][j] = X[b][n] over the contraction order apply_row) and the
+    // old values of its output elements, so X_new = X + R^T X needs no re-read.
+    __shared__ float Rs[PW][RLD];
     const ApplyItem it = items[blockIdx.x];
     if (flags[it.mat].done) return;
     const MatDev& md = mats[it.mat];
@@ -356,10 +395,13 @@ __global__ __launch_bounds__(256) void jac_apply_kernel(const MatDev* __restrict
     const int n = x0 + wave * 32 + ll;
     const bool active = x0 + wave * 32 < ld;  // a wave's 32 columns are all in or all out
     float xb[PW / 2];
+    int prow[PW / 2];  // physical rows (kept as indices: fewer registers than pointers)
+#pragma unroll
+    for (int s = 0; s < PW / 2; ++s) prow[s] = pair_row(md, bI, bJ, apply_row(s, hl));
+    float* const col = base + n;
     if (active) {
 #pragma unroll
-        for (int s = 0; s < PW / 2; ++s)
-            xb[s] = base[(int64_t)pair_row(md, bI, bJ, hl + 2 * s) * ld + n];
+        for (int s = 0; s < PW / 2; ++s) xb[s] = col[(int64_t)prow[s] * ld];
     }
     const float* R = md.rot + (int64_t)it.slot * PW * PW;
     for (int idx = threadIdx.x; idx < PW * PW / 4; idx += 256) {
@@ -376,21 +418,16 @@ __global__ __launch_bounds__(256) void jac_apply_kernel(const MatDev* __restrict
         acc1[r] = 0.0f;
     }
 #pragma unroll
-    for (int kb = 0; kb < PW; kb += 2) {
-        const float a0 = Rs[kb + hl][ll];
-        const float a1 = Rs[kb + hl][32 + ll];
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, xb[kb >> 1], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, xb[kb >> 1], acc1, 0, 0, 0);
+    for (int s = 0; s < PW / 2; ++s) {
+        const int b = apply_row(s, hl);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(Rs[b][ll], xb[s], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(Rs[b][32 + ll], xb[s], acc1, 0, 0, 0);
     }
-    // X_new[a][n] = X[a][n] + acc: each lane re-reads (from cache) exactly the
-    // elements it then overwrites.
+    // acc0 register r is row apply_row(r, hl), acc1 register r is row apply_row(16 + r, hl)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int a = 8 * (r >> 2) + 4 * hl + (r & 3);
-        float* p0 = base + (int64_t)pair_row(md, bI, bJ, a) * ld + n;
-        float* p1 = base + (int64_t)pair_row(md, bI, bJ, a + 32) * ld + n;
-        *p0 = *p0 + acc0[r];
-        *p1 = *p1 + acc1[r];
+        col[(int64_t)prow[r] * ld] = xb[r] + acc0[r];
+        col[(int64_t)prow[16 + r] * ld] = xb[16 + r] + acc1[r];
     }
 }
 
