@@ -664,8 +664,10 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
                     for (int sp = 0; sp < ns; ++sp)
                         gi.push_back(GramItem{i, s, sp, sp * sl, std::min(len, (sp + 1) * sl)});
                     si.push_back(SolveItem{i, s, ns});
-                    for (int c = 0; c < len / 128; ++c) ai.push_back(ApplyItem{i, s, 0, c});
-                    for (int c = 0; c < (m.kpad + 127) / 128; ++c) ai.push_back(ApplyItem{i, s, 1, c});
+                    for (int c = 0; c < (len + kApplyCols - 1) / kApplyCols; ++c)
+                        ai.push_back(ApplyItem{i, s, 0, c});
+                    for (int c = 0; c < (m.kpad + kApplyCols - 1) / kApplyCols; ++c)
+                        ai.push_back(ApplyItem{i, s, 1, c});
                 }
             }
             if ((rc = upload(gi, &L.gi, &L.ngi))) return rc;

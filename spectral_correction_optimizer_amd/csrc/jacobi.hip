@@ -33,7 +33,6 @@ namespace {
 constexpr int PW = kPw;          // 64 rows per pair block
 constexpr int KC = 32;           // K columns per LDS stage
 constexpr int CHUNK = 256;       // fp32 accumulation length before folding into fp64
-constexpr int APPLY_NC = 128;    // columns per apply workgroup
 
 // Physical row of A / V holding local column rho (0..63) of block pair (I, J).
 __device__ __forceinline__ int pair_row(const MatDev& md, int blkI, int blkJ, int rho) {
@@ -200,13 +199,11 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
     // Q itself in float32 would round c to 1 while s != 0, a biased growth of
     // the column norms over thousands of rotations).  c = 1 / h and s = t c
     // satisfy c^2 + s^2 = 1 to float32 rounding, so float32 parameters suffice.
-    __shared__ float G[PW][PW + 1];
+    __shared__ float G[2][PW][PW + 1];
     __shared__ float R[PW][PW + 1];
     __shared__ double dg[PW];
     __shared__ float red[4];
     __shared__ double redd[4];
-    __shared__ float cs_s[PW / 2], cs_cm1[PW / 2], cs_cf[PW / 2];
-    __shared__ int pp[PW / 2], qq[PW / 2];
 
     const SolveItem it = items[blockIdx.x];
     MatFlags& fl = flags[it.mat];
@@ -250,7 +247,7 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
     for (int e = 0; e < 16; ++e) {
         const int idx = tid + 256 * e;
         const int a = idx >> 6, b = idx & 63;
-        G[a][b] = (float)(gv[e] * scale);
+        G[0][a][b] = (float)(gv[e] * scale);
         if (a < b) {
             const double da = dg[a], db = dg[b];
             if (da > floor2d && db > floor2d) {
@@ -272,87 +269,78 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
         return;
     }
 
-    // 3. one cyclic sweep of 2x2 rotations on G (G <- J^T G J), accumulating R
+    // 3. one cyclic sweep of 2x2 rotations on G (G <- J^T G J), accumulating R.
+    //    Lane l works on pair j = l % 32 of the step: every lane computes that
+    //    pair's rotation itself (8 identical copies per workgroup), and takes the
+    //    rotation of pair i from lane i by a shuffle, so a step needs a single
+    //    barrier.  G is double-buffered (a step reads one copy and writes the
+    //    other); R's columns p_j, q_j belong to lane group j alone within a step.
+    const int j = tid & 31, r8 = tid >> 5;  // pair, and 8 row groups
     for (int ir = 0; ir < PW - 1; ++ir) {
-        if (tid < PW / 2) {
-            int p, q;
-            rr_pair(PW, ir, tid, &p, &q);
-            const float gpp = G[p][p], gqq = G[q][q], gpq = G[p][q];
-            float c = 1.0f, s = 0.0f, cm1 = 0.0f;
-            if (gpp > floor2 && gqq > floor2 && fabsf(gpq) > tol * (sqrtf(gpp) * sqrtf(gqq))) {
-                const float zeta = (gqq - gpp) / (2.0f * gpq);
+        const float (*Gc)[PW + 1] = G[ir & 1];
+        float (*Gn)[PW + 1] = G[(ir & 1) ^ 1];
+        int pj, qj;
+        rr_pair(PW, ir, j, &pj, &qj);
+        float c = 1.0f, sn = 0.0f, cm1 = 0.0f;
+        {
+            const float gpp = Gc[pj][pj], gqq = Gc[qj][qj], gpq = Gc[pj][qj];
+            if (gpp > floor2 && gqq > floor2 &&
+                fabsf(gpq) > tol * (__builtin_sqrtf(gpp) * __builtin_sqrtf(gqq))) {
+                const float zeta = (gqq - gpp) * 0.5f * __builtin_amdgcn_rcpf(gpq);
                 const float az = fabsf(zeta);
                 // t = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)), without overflow
-                const float den = az < 1e18f ? az + sqrtf(1.0f + az * az) : 2.0f * az;
-                const float t = copysignf(1.0f / den, zeta);
-                const float h = sqrtf(1.0f + t * t);
-                c = 1.0f / h;
-                s = t * c;
-                cm1 = -t * s / (1.0f + h);
-            }
-            cs_s[tid] = s;
-            cs_cm1[tid] = cm1;
-            cs_cf[tid] = c;
-            pp[tid] = p;
-            qq[tid] = q;
-        }
-        __syncthreads();
-        // G: each 2x2 block (rows p_i, q_i; columns p_j, q_j), i <= j, is
-        // rotated on both sides in one pass and mirrored (the pairs of a step are
-        // disjoint, so the blocks are independent)
-        for (int w = tid; w < (PW / 2) * (PW / 2); w += 256) {
-            const int i = w >> 5, j = w & 31;
-            if (i > j) continue;
-            const float si = cs_s[i], sj = cs_s[j];
-            if (si == 0.0f && sj == 0.0f) continue;
-            const float ci = cs_cf[i], cj = cs_cf[j];
-            const int pi = pp[i], qi = qq[i], pj = pp[j], qj = qq[j];
-            const float x00 = G[pi][pj], x01 = G[pi][qj], x10 = G[qi][pj], x11 = G[qi][qj];
-            // columns: [x_p, x_q] <- [c x_p - s x_q, s x_p + c x_q]
-            const float y00 = cj * x00 - sj * x01, y01 = sj * x00 + cj * x01;
-            const float y10 = cj * x10 - sj * x11, y11 = sj * x10 + cj * x11;
-            // rows
-            const float z00 = ci * y00 - si * y10, z10 = si * y00 + ci * y10;
-            const float z01 = ci * y01 - si * y11, z11 = si * y01 + ci * y11;
-            G[pi][pj] = z00;
-            G[pi][qj] = z01;
-            G[qi][pj] = z10;
-            G[qi][qj] = z11;
-            if (i != j) {
-                G[pj][pi] = z00;
-                G[qj][pi] = z01;
-                G[pj][qi] = z10;
-                G[qj][qi] = z11;
+                const float den = az < 1e18f ? az + __builtin_sqrtf(fmaf(az, az, 1.0f)) : 2.0f * az;
+                const float t = copysignf(__builtin_amdgcn_rcpf(den), zeta);
+                const float h = __builtin_sqrtf(fmaf(t, t, 1.0f));
+                c = __builtin_amdgcn_rcpf(h);
+                sn = t * c;
+                cm1 = -t * sn * __builtin_amdgcn_rcpf(1.0f + h);
             }
         }
-        // R: columns p, q (plus (J - I): (c - 1) on the diagonal and +-s off it)
-        for (int w = tid; w < (PW / 2) * PW; w += 256) {
-            const int i = w >> 6, a = w & 63;
-            const float s = cs_s[i];
-            if (s != 0.0f) {
-                const float cm1 = cs_cm1[i];
-                const int p = pp[i], q = qq[i];
-                const float xr = R[a][p], yr = R[a][q];
-                float np = fmaf(cm1, xr, xr) - s * yr;
-                float nq = fmaf(cm1, yr, yr) + s * xr;
-                if (a == p) {
+        // G: blocks (i, j) for i = r8 + 8 m -- rows p_i, q_i; columns p_j, q_j
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int i = r8 + 8 * m;
+            const float ci = __shfl(c, i), si = __shfl(sn, i);
+            int pi, qi;
+            rr_pair(PW, ir, i, &pi, &qi);
+            const float x00 = Gc[pi][pj], x01 = Gc[pi][qj], x10 = Gc[qi][pj], x11 = Gc[qi][qj];
+            // columns: [x_p, x_q] <- [c x_p - s x_q, s x_p + c x_q]; then rows
+            const float y00 = c * x00 - sn * x01, y01 = sn * x00 + c * x01;
+            const float y10 = c * x10 - sn * x11, y11 = sn * x10 + c * x11;
+            Gn[pi][pj] = ci * y00 - si * y10;
+            Gn[qi][pj] = si * y00 + ci * y10;
+            Gn[pi][qj] = ci * y01 - si * y11;
+            Gn[qi][qj] = si * y01 + ci * y11;
+        }
+        // R: columns p_j, q_j of rows a = r8 + 8 m (plus (J - I): (c - 1) on the
+        // diagonal and +-s off it)
+        if (sn != 0.0f) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int a = r8 + 8 * m;
+                const float xr = R[a][pj], yr = R[a][qj];
+                float np = fmaf(cm1, xr, xr) - sn * yr;
+                float nq = fmaf(cm1, yr, yr) + sn * xr;
+                if (a == pj) {
                     np += cm1;
-                    nq += s;
-                } else if (a == q) {
-                    np -= s;
+                    nq += sn;
+                } else if (a == qj) {
+                    np -= sn;
                     nq += cm1;
                 }
-                R[a][p] = np;
-                R[a][q] = nq;
+                R[a][pj] = np;
+                R[a][qj] = nq;
             }
         }
         __syncthreads();
     }
+    const float (*Gf)[PW + 1] = G[(PW - 1) & 1];
     // 4. R row-major [b][a] (X_new[a] = X[a] + sum_b R[b][a] X[b])
     float* Rg = md.rot + (int64_t)it.slot * PW * PW;
     for (int idx = tid; idx < PW * PW; idx += 256) Rg[idx] = R[idx >> 6][idx & 63];
     // rotated squared column norms (diagonal of Q^T G Q) for the next sweep's ordering
-    if (tid < PW) md.cnorm[pair_row(md, bI, bJ, tid)] = (float)(G[tid][tid] * dmax);
+    if (tid < PW) md.cnorm[pair_row(md, bI, bJ, tid)] = (float)(Gf[tid][tid] * dmax);
     if (tid == 0) {
         *rflag = 1;
         atomicAdd(&fl.pairs_applied, 1);
@@ -370,11 +358,11 @@ __device__ __forceinline__ int apply_row(int s, int hl) {
 constexpr int RLD = 72;  // LDS row stride of R: rows 4 apart fall 32 banks apart
 }  // namespace
 
-__global__ __launch_bounds__(256) void jac_apply_kernel(const MatDev* __restrict__ mats,
+__global__ __launch_bounds__(kApplyThreads) void jac_apply_kernel(const MatDev* __restrict__ mats,
                                                         const MatFlags* __restrict__ flags,
                                                         const ApplyItem* __restrict__ items,
                                                         int round) {
-    // A workgroup updates 64 rows x 128 columns; wave w owns columns
+    // A workgroup updates 64 rows x kApplyCols columns; wave w owns columns
     // [x0 + 32 w, x0 + 32 w + 32).  Only R goes through LDS: each lane loads
     // 32 rows of its column straight into registers; they are both its MFMA B
     // operands (B[k][j] = X[b][n] over the contraction order apply_row) and the
@@ -388,7 +376,7 @@ __global__ __launch_bounds__(256) void jac_apply_kernel(const MatDev* __restrict
     rr_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
     float* base = it.which == 0 ? md.A : md.V;
     const int ld = it.which == 0 ? md.K_ld : md.kpad;  // multiple of 64
-    const int x0 = it.chunk * APPLY_NC;
+    const int x0 = it.chunk * kApplyCols;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int hl = lane >> 5, ll = lane & 31;
@@ -404,7 +392,7 @@ __global__ __launch_bounds__(256) void jac_apply_kernel(const MatDev* __restrict
         for (int s = 0; s < PW / 2; ++s) xb[s] = col[(int64_t)prow[s] * ld];
     }
     const float* R = md.rot + (int64_t)it.slot * PW * PW;
-    for (int idx = threadIdx.x; idx < PW * PW / 4; idx += 256) {
+    for (int idx = threadIdx.x; idx < PW * PW / 4; idx += kApplyThreads) {
         const int b = idx >> 4, a4 = (idx & 15) * 4;
         *(float4*)&Rs[b][a4] = *(const float4*)(R + b * PW + a4);
     }
@@ -523,7 +511,7 @@ hipError_t launch_jacobi_solve(const MatDev* mats, MatFlags* flags, const SolveI
 
 hipError_t launch_jacobi_apply(const MatDev* mats, const MatFlags* flags, const ApplyItem* ai,
                                int nai, int round, hipStream_t st) {
-    hipLaunchKernelGGL(jac_apply_kernel, dim3(nai), dim3(256), 0, st, mats, flags, ai, round);
+    hipLaunchKernelGGL(jac_apply_kernel, dim3(nai), dim3(kApplyThreads), 0, st, mats, flags, ai, round);
     return hipGetLastError();
 }
 
