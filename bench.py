@@ -75,14 +75,14 @@ def copy_calibration(nbytes):
 # on a plain device copy of known size), valid only for the kernel source they
 # were taken on (sha256 of the file); otherwise reported as null.
 TRAFFIC = {
-    "jacobi_gram": {"source": "jacobi.hip", "sha256": "9edf0977cf3d52c449805380ada93d9c8de3d47dac605cf664d86065be6efff2",
-        "bytes_per_launch": 1.64748e+09},
-    "jacobi_apply": {"source": "jacobi.hip", "sha256": "9edf0977cf3d52c449805380ada93d9c8de3d47dac605cf664d86065be6efff2",
-        "bytes_per_launch": 2.27683e+09},
-    "combine_adamw": {"source": "elementwise.hip", "sha256": "e4a48da8a49650e6813f3104ffd6be0fdea1368406e796c113e935ffc8229e55",
+    "jacobi_gram": {"source": "jacobi.hip", "sha256": "88b66451de2f9d80df5a71b0e9013752e7d434a7ddb5e12d72e2e7509c3f29c2",
+        "bytes_per_launch": 7.1432e+08},
+    "jacobi_apply": {"source": "jacobi.hip", "sha256": "88b66451de2f9d80df5a71b0e9013752e7d434a7ddb5e12d72e2e7509c3f29c2",
+        "bytes_per_launch": 2.06757e+09},
+    "combine_adamw": {"source": "elementwise.hip", "sha256": "492eb4650cbcded5935d5e85055ac555da87f64f5d515c046d66b7d1e420f8f3",
         "bytes_per_launch": 3.11482e+10},
-    "ema": {"source": "elementwise.hip", "sha256": "e4a48da8a49650e6813f3104ffd6be0fdea1368406e796c113e935ffc8229e55",
-        "bytes_per_launch": 1.16866e+10},
+    "ema": {"source": "elementwise.hip", "sha256": "492eb4650cbcded5935d5e85055ac555da87f64f5d515c046d66b7d1e420f8f3",
+        "bytes_per_launch": 1.16867e+10},
 }
 
 
