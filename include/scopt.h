@@ -69,12 +69,13 @@ typedef struct {
     int warm_start;     /* 1: a refresh starts its sweeps from the previous factors
                            (A = M V_prev); 0: always from A = M, V = I */
     int precondition;   /* 1: for matrices with max(rows, cols) >= 2 min(rows, cols) the
-                           sweeps first run on the k x k Cholesky factor of the Gram
-                           A^T A (same rotations, rows k instead of K long), then
-                           polish on A = M V until converged; a matrix whose
-                           factorization is rejected runs the plain sweeps.  Used
-                           by refreshes that start from previous factors
-                           (warm_start = 1) and with sync_check = 1. */
+                           sweeps first run on the k x k Cholesky factor L of the Gram
+                           A^T A = L L^T (the right singular vectors of A are the left
+                           ones of L; rows k instead of K long, no accumulated
+                           rotations), then polish on A = M V until converged; a
+                           matrix whose factorization is rejected runs the plain
+                           sweeps.  Used by refreshes that start from previous
+                           factors (warm_start = 1) and with sync_check = 1. */
 } sc_hparams;
 
 /* Fill `hp` with the defaults of the pages' training strategy:

@@ -154,6 +154,8 @@ struct sc_opt {
     SyrkItem* syrk_d = nullptr;     // lower tiles of A^T A of those matrices
     int nsyrk = 0;
     GemmGroup polish_nt, polish_nn; // A_rows = V op(M) after the factor phase
+    GemmGroup factor_v;             // V rows <- diag(1/|x_j|) X^T V_prev (gated per matrix)
+    int max_klen = 0;
     hipEvent_t fork = nullptr;
     int max_nb = 2, max_kpad = 64, max_K = 1, max_k = 1;
     // refresh GEMMs
@@ -334,9 +336,10 @@ int finalize_factors(sc_opt* h, hipStream_t st) {
 
 // Algorithmic work of the Jacobi sweeps from the device counters (profiling only):
 // per active round and pair the 64x64 Gram over the row length L (2 * 64 * 64 * L
-// flops, 4 * 64 * L bytes); per applied pair the update of 64 rows of A (length L)
-// and V (length k), 2 * 64 * 64 * (L + k) flops and 8 * 64 * (L + k) + 4 * 64 * 64
-// bytes.  L = klen for the rounds on the Cholesky factor, K otherwise.
+// flops, 4 * 64 * L bytes); per applied pair the update of 64 rows of the operand
+// (length L) and of V (length k), 2 * 64 * 64 * (L + k) flops and
+// 8 * 64 * (L + k) + 4 * 64 * 64 bytes.  In the factor phase L = klen and V is not
+// touched (its k term drops out); otherwise L = K.
 void account_sweeps(sc_opt* h) {
     for (int i = 0; i < h->n; ++i) {
         const MatDev& m = h->mh[i];
@@ -345,11 +348,13 @@ void account_sweeps(sc_opt* h) {
         const double rounds[2] = {(double)f.rounds_pre, (double)(f.rounds_active - f.rounds_pre)};
         const double pairs[2] = {(double)f.pairs_pre, (double)(f.pairs_applied - f.pairs_pre)};
         const double len[2] = {(double)m.klen, (double)m.K};
+        const double vlen[2] = {0.0, (double)m.k};
         for (int ph = 0; ph < 2; ++ph) {
             h->prof.flops[PK_GRAM] += rounds[ph] * (m.nb / 2) * 2.0 * pw * pw * len[ph];
             h->prof.bytes[PK_GRAM] += rounds[ph] * (m.nb / 2) * 4.0 * pw * len[ph];
-            h->prof.flops[PK_APPLY] += pairs[ph] * 2.0 * pw * pw * (len[ph] + m.k);
-            h->prof.bytes[PK_APPLY] += pairs[ph] * (8.0 * pw * (len[ph] + m.k) + 4.0 * pw * pw);
+            h->prof.flops[PK_APPLY] += pairs[ph] * 2.0 * pw * pw * (len[ph] + vlen[ph]);
+            h->prof.bytes[PK_APPLY] +=
+                pairs[ph] * (8.0 * pw * (len[ph] + vlen[ph]) + 4.0 * pw * pw);
         }
     }
 }
@@ -437,7 +442,7 @@ int do_refresh(sc_opt* h, hipStream_t st) {
     // a graded spectrum would make most factorizations fail, so it is skipped.
     const bool pre = h->ncap > 0 && h->hp.sync_check && warm;
     if (pre) {
-        // Factor phase: Jacobi on R = L^T, A^T A = L L^T (same Gram, k-long rows).
+        // Factor phase: Jacobi on X = L, A^T A = L L^T (k-long rows, no V).
         HIP_TRY(timed(h, PK_CHOL_GEMM, st,
                       [&] { return launch_chol_syrk(h->md, h->syrk_d, h->nsyrk, st); }));
         if (h->prof.on)
@@ -447,7 +452,8 @@ int do_refresh(sc_opt* h, hipStream_t st) {
                     h->prof.flops[PK_CHOL_GEMM] += kt * (kt + 1) / 2 * 2.0 * 128 * 128 * h->mh[i].K_ld;
                 }
         HIP_TRY(timed(h, PK_CHOL, st, [&] {
-            return launch_cholesky(h->md, h->flags_d, h->cap_d, h->ncap, h->max_nbk, st);
+            return launch_cholesky(h->md, h->flags_d, h->cap_d, h->ncap, h->max_nbk, h->max_klen,
+                                   st);
         }));
         if (h->prof.on)
             for (int i = 0; i < h->n; ++i)
@@ -455,9 +461,14 @@ int do_refresh(sc_opt* h, hipStream_t st) {
     }
     if ((rc = run_rounds(h, st, pre ? LIST_FACTOR : LIST_PLAIN, 4))) return rc;
     if (pre) {
-        // Polishing phase on the true operand A = M V (V holds the factor phase's
-        // rotations); a rejected matrix gets back its unchanged operand and runs
-        // all its sweeps here.
+        // Right singular vectors of A from the factor phase: V <- diag(1/|x_j|) X^T V_prev
+        // (rows), then the polishing phase on the true operand A = M V.  A rejected
+        // matrix keeps V = V_prev, gets back its unchanged operand and runs all its
+        // sweeps here.
+        HIP_TRY(timed(h, PK_POLISH_GEMM, st, [&] {
+            return launch_factor_invnorm(h->md, h->flags_d, h->cap_d, h->ncap, h->max_k, st);
+        }));
+        if ((rc = run_group(h, h->factor_v, PK_POLISH_GEMM, none, st))) return rc;
         if ((rc = run_group(h, h->polish_nt, PK_POLISH_GEMM, none, st))) return rc;
         if ((rc = run_group(h, h->polish_nn, PK_POLISH_GEMM, none, st))) return rc;
         HIP_TRY(timed(h, PK_INIT_FLAGS, st,
@@ -521,6 +532,10 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
                          : (float)(eps * std::max(16.0, std::sqrt((double)m.K)));
         m.numel = (int64_t)m.m * m.n;
         // Cholesky-preconditioned when the operand is at least twice as long as wide
+        // Cholesky factor phase for operands at least twice as long as wide: their
+        // singular values stay away from zero, so the Gram A^T A loses nothing
+        // (square operands keep the plain sweeps: A^T A squares their condition
+        // number and the factor phase then needs more sweeps, not fewer)
         m.klen = (h->hp.precondition && m.K >= 2 * m.k) ? round_up(m.k, 128) : 0;
         m.nsplit = split_count(m.K_ld, kMaxSplits);  // capacity of the partial buffer
         if (m.klen) m.nsplit = std::max(m.nsplit, split_count(m.klen, kMaxSplits));
@@ -666,6 +681,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
                     si.push_back(SolveItem{i, s, ns});
                     for (int c = 0; c < (len + kApplyCols - 1) / kApplyCols; ++c)
                         ai.push_back(ApplyItem{i, s, 0, c});
+                    if (which == 1 && m.klen) continue;  // the factor phase accumulates no V
                     for (int c = 0; c < (m.kpad + kApplyCols - 1) / kApplyCols; ++c)
                         ai.push_back(ApplyItem{i, s, 1, c});
                 }
@@ -687,6 +703,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             if (h->mh[i].klen) {
                 cap.push_back(i);
                 h->max_nbk = std::max(h->max_nbk, (h->mh[i].k + 63) / 64);
+                h->max_klen = std::max(h->max_klen, h->mh[i].klen);
                 const int kt = (h->mh[i].k + 127) / 128;
                 for (int ti = 0; ti < kt; ++ti)
                     for (int tj = 0; tj <= ti; ++tj) sy.push_back(SyrkItem{i, ti, tj});
@@ -739,7 +756,12 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             h->warm_nn.h.push_back(p);
         }
         if (m.klen) {
-            // after the factor phase: A_rows = V op(M) with V's rows (length kpad)
+            // after the factor phase: V rows = scaled rows of X^T times W (= V_prev),
+            // only where the factorization was accepted; then A_rows = V op(M)
+            p = make_prob(m.A, m.K_ld, m.W, m.k, m.V, m.kpad, m.k, m.k, m.k);
+            p.row_scale = m.Y;
+            p.gate = &h->flags_d[i].precond;
+            h->factor_v.h.push_back(p);
             if (m.tall) {
                 p = make_prob(m.V, m.kpad, m.Manc, m.n, m.A, m.K_ld, m.k, m.m, m.n);
                 h->polish_nt.h.push_back(p);
@@ -785,7 +807,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             h->s3_nn.h.push_back(p);
         }
     }
-    for (GemmGroup* g : {&h->warm_nt, &h->warm_nn, &h->polish_nt, &h->polish_nn,
+    for (GemmGroup* g : {&h->warm_nt, &h->warm_nn, &h->factor_v, &h->polish_nt, &h->polish_nn,
                          &h->lowdin_eF, &h->lowdin_F, &h->lowdin_eW,
                          &h->lowdin_W, &h->proj,
                          &h->s1_nn_a, &h->s1_nn_b, &h->s1_nt, &h->s2_nn, &h->s3_tn, &h->s3_nn})

@@ -1,12 +1,17 @@
-// Cholesky preconditioning of the Jacobi SVD for operands at least twice as
-// long as wide (K >= 2k).
+// Cholesky preconditioning of the Jacobi SVD for operands at least twice as long
+// as wide, in refreshes that start from the previous factors (A = M V_prev with
+// nearly orthogonal columns).
 //
-// One-sided Jacobi only ever looks at the Gram of the operand's columns.  With
-// C = A^T A = L L^T, the k x k operand R = L^T has exactly that Gram, so the
-// same rotations can be found on rows k long instead of K (the factor phase);
-// afterwards A = M V is formed once and polished by ordinary sweeps.  The
-// factor phase is only worth it if R's Gram matches A's to about the sweep
-// tolerance, otherwise the polish needs many full-length sweeps; hence:
+// With C = A^T A = L L^T, i.e. A = Q R with R = L^T, the SVD of A follows from
+// the SVD of the k x k lower-triangular X = R^T = L:  X = U_x S V_x^T gives
+// R = V_x S U_x^T and A = (Q V_x) S U_x^T, so the right singular vectors of A
+// are U_x, the normalized columns of X after its one-sided Jacobi sweeps (the
+// factor phase).  The rotations of X need not be accumulated at all; the
+// sweeps move rows k long instead of K and touch no V, and the columns of X
+// (rows of R, graded like the singular values) converge in fewer sweeps than
+// those of A.  Afterwards V <- U_x^T-combination of V_prev (one k x k GEMM),
+// A = M V is formed once and ordinary sweeps polish it until converged.  This
+// only pays if X^T X matches A^T A to about the sweep tolerance; hence:
 //
 //   chol_syrk    C = A^T A (lower 128 x 128 tiles), float32 MFMA products whose
 //                running sums are folded into float64 every 256 columns, the
@@ -15,15 +20,15 @@
 //   chol_panel   L_ib,jb = C_ib,jb L_jb,jb^-T below it (float64);
 //   chol_update  C_ib,kb -= L_ib,jb L_kb,jb^T for the trailing lower tiles
 //                (float64 FMA, register-blocked);
-//   chol_commit  rows of A <- float32(rows of L), zero beyond the diagonal.
+//   chol_commit  rows of the operand <- float32(columns of L) (tiled transpose).
 //
-// Rounding L to float32 perturbs each Gram entry by about 2^-24 of the two
-// columns' norms, well inside the sweep tolerance.
+// Rounding L to float32 perturbs each entry by 2^-24 of itself, well inside the
+// sweep tolerance.
 //
 // A pivot that keeps less than a tenth of its column's squared norm (the
-// column nearly lies in the span of the previous ones) rejects the matrix: it
+// column nearly lies in the span of the previous ones), or a column at or
+// below the zero floor (U_x would be undefined there), rejects the matrix: it
 // sits the factor phase out and runs plain sweeps in the polishing phase.
-// Columns at or below the zero floor get a zero pivot.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -176,8 +181,7 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(const MatDev* __restrict
             if (gc < k) {
                 const double orig = md.norm2[gc];
                 const double p = T[c][c];
-                if (orig <= (double)f.floor2) l = 0.0;  // zero column
-                else if (!(p > kKeep * orig)) fail = 1;
+                if (!(orig > (double)f.floor2) || !(p > kKeep * orig)) fail = 1;
                 else l = sqrt(p);
             }
             piv[c] = l;
@@ -308,26 +312,60 @@ __global__ __launch_bounds__(256) void chol_update_kernel(const MatDev* __restri
         }
 }
 
-// Accepted factorizations: the rows of the Jacobi operand become float32 rows
-// of L (column j of R = L^T), klen long, zero beyond the diagonal.  A rejected
-// matrix keeps its operand and sits the factor phase out (done = 1).
+// Accepted factorizations: the rows of the Jacobi operand become the float32
+// columns of L (row j = X[:, j], X = L), klen long, zero above the diagonal of
+// L and beyond k.  64 x 64 tiles transposed through LDS.  A rejected matrix
+// keeps its operand and sits the factor phase out (done = 1).
 __global__ __launch_bounds__(256) void chol_commit_kernel(const MatDev* __restrict__ mats,
                                                           MatFlags* __restrict__ flags,
                                                           const int* __restrict__ mat_idx) {
-    const int i = mat_idx[blockIdx.y];
+    __shared__ float T[CT][CT + 1];
+    const int i = mat_idx[blockIdx.z];
     MatFlags& f = flags[i];
     const MatDev& md = mats[i];
     if (f.chol_fail) {
-        if (blockIdx.x == 0 && threadIdx.x == 0) f.done = 1;
+        if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) f.done = 1;
         return;
     }
     const int k = md.k, klen = md.klen;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < (int64_t)k * klen;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        const int j = (int)(idx / klen), c = (int)(idx % klen);
-        md.A[(int64_t)j * md.K_ld + c] = (c <= j && c < k) ? (float)md.chol[(int64_t)j * k + c] : 0.0f;
+    const int j0 = blockIdx.y * CT;  // operand rows (columns of L)
+    const int c0 = blockIdx.x * CT;  // operand columns (rows of L)
+    if (j0 >= k || c0 >= klen) return;
+    for (int idx = threadIdx.x; idx < CT * CT; idx += blockDim.x) {
+        const int r = idx >> 6, c = idx & 63;  // T[r][c] = L[c0 + r][j0 + c]
+        const int lr = c0 + r, lc = j0 + c;
+        T[r][c] = (lr < k && lc < k && lc <= lr) ? (float)md.chol[(int64_t)lr * k + lc] : 0.0f;
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) f.precond = 1;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < CT * CT; idx += blockDim.x) {
+        const int r = idx >> 6, c = idx & 63;  // operand[j0 + r][c0 + c] = L[c0 + c][j0 + r]
+        if (j0 + r < k) md.A[(int64_t)(j0 + r) * md.K_ld + c0 + c] = T[c][r];
+    }
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) f.precond = 1;
+}
+
+// inv[j] = 1 / ||operand row j|| over its klen entries (float64 sum), j < k, into
+// md.Y, for the matrices whose factor phase ran: the row scales of V = U_x^T V_prev.
+__global__ __launch_bounds__(256) void factor_invnorm_kernel(const MatDev* __restrict__ mats,
+                                                             const MatFlags* __restrict__ flags,
+                                                             const int* __restrict__ mat_idx) {
+    __shared__ double red[4];
+    const int i = mat_idx[blockIdx.y];
+    const MatDev& md = mats[i];
+    const int j = blockIdx.x;
+    if (!flags[i].precond || j >= md.k) return;
+    const float* x = md.A + (int64_t)j * md.K_ld;
+    double acc = 0.0;
+    for (int c = threadIdx.x; c < md.klen; c += blockDim.x) acc += (double)x[c] * (double)x[c];
+    acc = block_sum_f64(acc, red);
+    if (threadIdx.x == 0) md.Y[j] = acc > 0.0 ? (float)(1.0 / sqrt(acc)) : 0.0f;
+}
+
+hipError_t launch_factor_invnorm(const MatDev* mats, const MatFlags* flags, const int* mat_idx,
+                                 int nmat, int max_k, hipStream_t st) {
+    hipLaunchKernelGGL(factor_invnorm_kernel, dim3(max_k, nmat), dim3(256), 0, st, mats, flags,
+                       mat_idx);
+    return hipGetLastError();
 }
 
 hipError_t launch_chol_syrk(const MatDev* mats, const SyrkItem* items, int nitems, hipStream_t st) {
@@ -336,7 +374,7 @@ hipError_t launch_chol_syrk(const MatDev* mats, const SyrkItem* items, int nitem
 }
 
 hipError_t launch_cholesky(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
-                           int max_nbk, hipStream_t st) {
+                           int max_nbk, int max_klen, hipStream_t st) {
     for (int jb = 0; jb < max_nbk; ++jb) {
         hipLaunchKernelGGL(chol_diag_kernel, dim3(nmat), dim3(256), 0, st, mats, flags, mat_idx, jb);
         const int nt = max_nbk - jb - 1;
@@ -347,7 +385,8 @@ hipError_t launch_cholesky(const MatDev* mats, MatFlags* flags, const int* mat_i
                                mats, flags, mat_idx, jb);
         }
     }
-    hipLaunchKernelGGL(chol_commit_kernel, dim3(512, nmat), dim3(256), 0, st, mats, flags, mat_idx);
+    hipLaunchKernelGGL(chol_commit_kernel, dim3((max_klen + CT - 1) / CT, max_nbk, nmat), dim3(256),
+                       0, st, mats, flags, mat_idx);
     return hipGetLastError();
 }
 

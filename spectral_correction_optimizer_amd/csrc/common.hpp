@@ -54,6 +54,20 @@ __device__ __forceinline__ int xcd_remap(int wg, int nwg) {
     return base + slot;
 }
 
+// Sum of v over the workgroup (wave shuffles, then the per-wave partials in a
+// fixed order); red holds blockDim.x / 64 doubles.  Every thread gets the sum.
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    double s = 0.0;
+    const int nw = blockDim.x >> 6;
+    for (int i = 0; i < nw; ++i) s += red[i];
+    __syncthreads();
+    return s;
+}
+
 // Round-robin ("circle") pairing of nb items: round r in [0, nb-1),
 // slot i in [0, nb/2); returns p < q.
 __device__ __host__ __forceinline__ void rr_pair(int nb, int r, int i, int* p, int* q) {

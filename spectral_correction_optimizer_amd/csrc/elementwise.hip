@@ -289,18 +289,6 @@ hipError_t launch_jacobi_warm(const MatDev* mats, int nmat, hipStream_t st) {
 // ---------------------------------------------------------------------------------
 // Row norms in float64 with a fixed reduction order (deterministic).
 // which = 0: rows j < kpad of A (length K_ld); 1: rows j < k of V (length k).
-__device__ double block_sum_f64(double v, double* red) {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[w] = v;
-    __syncthreads();
-    double s = 0.0;
-    const int nw = blockDim.x >> 6;
-    for (int i = 0; i < nw; ++i) s += red[i];
-    __syncthreads();
-    return s;
-}
-
 __global__ __launch_bounds__(256) void rownorm_kernel(const MatDev* __restrict__ mats, int which) {
     __shared__ double red[4];
     const MatDev& md = mats[blockIdx.y];

@@ -154,6 +154,7 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
         else hi = mid - 1;
     }
     const GemmProb& P = probs[lo];
+    if (P.gate && *P.gate == 0) return;
     const int local = wg - P.tile_start;
     const int m0 = (local / P.tiles_n) * BM, n0 = (local % P.tiles_n) * BN;
     const int M = P.M, N = P.N, K = P.K;

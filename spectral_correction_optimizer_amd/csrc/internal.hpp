@@ -100,6 +100,7 @@ struct GemmProb {
     int flags;
     int a_ptr, b_ptr;  // >= 0: take A (B) from the call's PtrTable entry
     int tiles_n, tile_start;
+    const int* gate;   // optional: the problem is skipped when *gate == 0
 };
 
 // Launch one grouped GEMM over `probs` (device array, nprob entries, tile
@@ -152,10 +153,15 @@ hipError_t launch_jacobi_sweep_end(const MatDev* mats, MatFlags* flags, const in
 // chol = A^T A (lower 128 x 128 tiles listed in items), float64 sums.
 hipError_t launch_chol_syrk(const MatDev* mats, const SyrkItem* items, int nitems, hipStream_t st);
 // chol = L L^T (in place, lower triangle) for the matrices in mat_idx; on success the
-// rows of A become the rows of L (length klen) and precond = 1, else chol_fail = 1
-// and done = 1 (the matrix sits the factor phase out).  max_nbk: largest ceil(k / 64).
+// rows of A become the columns of L (length klen) and precond = 1, else chol_fail = 1
+// and done = 1 (the matrix sits the factor phase out).  max_nbk: largest ceil(k / 64),
+// max_klen: largest klen.
 hipError_t launch_cholesky(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
-                           int max_nbk, hipStream_t st);
+                           int max_nbk, int max_klen, hipStream_t st);
+// inv[j] = 1 / sqrt(cnorm[j]) for j < k of the accepted matrices (into md.Y):
+// row scales that make V = L^T-phase vectors x W_prev orthonormal.
+hipError_t launch_factor_invnorm(const MatDev* mats, const MatFlags* flags, const int* mat_idx,
+                                 int nmat, int max_k, hipStream_t st);
 // Start of the polishing phase for the matrices in mat_idx (A already recomputed).
 hipError_t launch_phase2_reset(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
                                hipStream_t st);
