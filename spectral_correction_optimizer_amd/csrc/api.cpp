@@ -71,13 +71,14 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 enum ProfKind {
     PK_EMA, PK_LOAD, PK_ROWNORM, PK_INIT_FLAGS, PK_GRAM, PK_SOLVE, PK_APPLY, PK_SWEEP_END,
     PK_NORMALIZE, PK_LOWDIN, PK_FILTER, PK_PROJECTORS, PK_STEP_GEMM1, PK_STEP_GEMM2,
-    PK_STEP_GEMM3, PK_ADAMW, PK_WARM, PK_SORT, PK_CHOL_GEMM, PK_CHOL, PK_POLISH_GEMM, PK_COUNT
+    PK_STEP_GEMM3, PK_ADAMW, PK_WARM, PK_SORT, PK_CHOL_GEMM, PK_CHOL, PK_POLISH_GEMM,
+    PK_GRAM_E, PK_COUNT
 };
 const char* const kProfNames[PK_COUNT] = {
     "ema", "jacobi_load", "rownorm", "jacobi_init", "jacobi_gram", "jacobi_solve",
     "jacobi_apply", "jacobi_sweep_end", "normalize", "lowdin_gemm", "filter", "projector_gemm",
     "step_gemm1", "step_gemm2", "step_gemm3", "combine_adamw", "warm_start", "jacobi_sort",
-    "chol_syrk", "cholesky", "polish_gemm"};
+    "chol_syrk", "cholesky", "polish_gemm", "final_gram"};
 
 // Optional kernel timing: HIP events recorded around every launch on the
 // caller's stream; totals are folded in by sc_get_kernel_times.
@@ -153,13 +154,17 @@ struct sc_opt {
     int max_nbk = 0;  // largest ceil(k / 64) among them
     SyrkItem* syrk_d = nullptr;     // lower tiles of A^T A of those matrices
     int nsyrk = 0;
+    SyrkItem* syrk_all_d = nullptr; // lower tiles of A^T A of every matrix (final Gram)
+    int nsyrk_all = 0;
+    int* all_d = nullptr;           // 0 .. n-1
+    int max_t64 = 1;                // largest ceil(k / 64)
     GemmGroup polish_nt, polish_nn; // A_rows = V op(M) after the factor phase
     GemmGroup factor_v;             // V rows <- diag(1/|x_j|) X^T V_prev (gated per matrix)
     int max_klen = 0;
     hipEvent_t fork = nullptr;
     int max_nb = 2, max_kpad = 64, max_K = 1, max_k = 1;
     // refresh GEMMs
-    GemmGroup lowdin_eF, lowdin_F, lowdin_eW, lowdin_W, proj;
+    GemmGroup lowdin_F, lowdin_eW, lowdin_W, proj;
     GemmGroup warm_nt, warm_nn;  // warm start: A_rows = W M^T (m >= n) or W M (m < n)
     bool have_factors = false;   // W holds orthonormal rows from a refresh / sc_set_factors
     // step GEMMs
@@ -317,6 +322,21 @@ int build_projectors(sc_opt* h, hipStream_t st) {
     return SC_OK;
 }
 
+// chol = A^T A (float64 sums) and E = its normalized off-diagonal part, all matrices.
+int final_gram(sc_opt* h, hipStream_t st) {
+    HIP_TRY(timed(h, PK_GRAM_E, st,
+                  [&] { return launch_chol_syrk(h->md, h->syrk_all_d, h->nsyrk_all, st); }));
+    HIP_TRY(timed(h, PK_GRAM_E, st, [&] {
+        return launch_gram_to_e(h->md, h->flags_d, h->all_d, h->n, h->max_t64, st);
+    }));
+    if (h->prof.on)
+        for (int i = 0; i < h->n; ++i) {
+            const double kt = (h->mh[i].k + 127) / 128;
+            h->prof.flops[PK_GRAM_E] += kt * (kt + 1) / 2 * 2.0 * 128 * 128 * h->mh[i].K_ld;
+        }
+    return SC_OK;
+}
+
 int finalize_factors(sc_opt* h, hipStream_t st) {
     PtrTable none = make_table(h, nullptr);
     for (int which = 0; which < 2; ++which) {
@@ -327,7 +347,7 @@ int finalize_factors(sc_opt* h, hipStream_t st) {
         }));
     }
     int rc;
-    if ((rc = run_group(h, h->lowdin_eF, PK_LOWDIN, none, st))) return rc;
+    // E (normalized Gram of the A-side rows, zero diagonal) comes from final_gram
     if ((rc = run_group(h, h->lowdin_F, PK_LOWDIN, none, st))) return rc;
     if ((rc = run_group(h, h->lowdin_eW, PK_LOWDIN, none, st))) return rc;
     if ((rc = run_group(h, h->lowdin_W, PK_LOWDIN, none, st))) return rc;
@@ -473,7 +493,23 @@ int do_refresh(sc_opt* h, hipStream_t st) {
         if ((rc = run_group(h, h->polish_nn, PK_POLISH_GEMM, none, st))) return rc;
         HIP_TRY(timed(h, PK_INIT_FLAGS, st,
                       [&] { return launch_phase2_reset(h->md, h->flags_d, h->cap_d, h->ncap, st); }));
-        if ((rc = run_rounds(h, st, LIST_POLISH, 1))) return rc;
+    }
+    // Gram of every final operand in float64 sums: the Loewdin step's E, and for the
+    // preconditioned matrices the certificate that A = M V is already converged.
+    // Only matrices that fail it run polishing sweeps (and get a new Gram after them).
+    if ((rc = final_gram(h, st))) return rc;
+    if (pre) {
+        HIP_TRY(timed(h, PK_INIT_FLAGS, st,
+                      [&] { return launch_certify(h->md, h->flags_d, h->cap_d, h->ncap, st); }));
+        HIP_TRY(hipMemcpyAsync(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n,
+                               hipMemcpyDeviceToHost, st));
+        HIP_TRY(hipStreamSynchronize(st));
+        bool all = true;
+        for (int i = 0; i < h->n; ++i) all = all && h->flags_h[i].done;
+        if (!all) {
+            if ((rc = run_rounds(h, st, LIST_POLISH, 1))) return rc;
+            if ((rc = final_gram(h, st))) return rc;
+        }
     }
     if (h->prof.on) {
         HIP_TRY(hipMemcpyAsync(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n,
@@ -563,7 +599,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         o[i].rflag = take((size_t)(m.nb / 2) * sizeof(int));
         o[i].perm = take((size_t)m.kpad * sizeof(int));
         o[i].cnorm = take((size_t)m.kpad * sizeof(float));
-        o[i].chol = take(m.klen ? (size_t)m.k * m.k * sizeof(double) : 0);
+        o[i].chol = take((size_t)m.k * m.k * sizeof(double));
         h->max_nb = std::max(h->max_nb, m.nb);
         h->max_kpad = std::max(h->max_kpad, m.kpad);
         h->max_K = std::max(h->max_K, m.K_ld);
@@ -603,7 +639,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         m.rot_flag = (int*)(b + o[i].rflag);
         m.perm = (int*)(b + o[i].perm);
         m.cnorm = (float*)(b + o[i].cnorm);
-        m.chol = m.klen ? (double*)(b + o[i].chol) : nullptr;
+        m.chol = (double*)(b + o[i].chol);
     }
     void* p = nullptr;
     HIP_TRY(hipMalloc(&p, sizeof(MatDev) * n));
@@ -710,12 +746,23 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             }
         if ((rc = upload(cap, &h->cap_d, &h->ncap))) return rc;
         if ((rc = upload(sy, &h->syrk_d, &h->nsyrk))) return rc;
+        std::vector<int> all;
+        std::vector<SyrkItem> sa;
+        for (int i = 0; i < n; ++i) {
+            all.push_back(i);
+            h->max_t64 = std::max(h->max_t64, (h->mh[i].k + 63) / 64);
+            const int kt = (h->mh[i].k + 127) / 128;
+            for (int ti = 0; ti < kt; ++ti)
+                for (int tj = 0; tj <= ti; ++tj) sa.push_back(SyrkItem{i, ti, tj});
+        }
+        int nall = 0;
+        if ((rc = upload(all, &h->all_d, &nall))) return rc;
+        if ((rc = upload(sa, &h->syrk_all_d, &h->nsyrk_all))) return rc;
     }
     HIP_TRY(hipEventCreateWithFlags(&h->fork, hipEventDisableTiming));
 
     // GEMM problem tables
     const bool gbf = h->gdt == SC_BF16;
-    h->lowdin_eF.tb = true;
     h->lowdin_eW.tb = true;
     h->proj.ta = true;
     h->s1_nn_a.abf = gbf;  // square: A = G
@@ -729,10 +776,8 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         MatDev& m = h->mh[i];
         // Loewdin re-orthogonalization of the unit rows of A (-> F) and V (-> W):
         //   E = X X^T with zero diagonal;  X_out = X - 0.5 E X
-        GemmProb p = make_prob(m.A, m.K_ld, m.A, m.K_ld, m.E, m.k, m.k, m.k, m.K_ld);
-        p.flags = GF_ZERO_DIAG;
-        h->lowdin_eF.h.push_back(p);
-        p = make_prob(m.E, m.k, m.A, m.K_ld, m.F, m.K_ld, m.k, m.K_ld, m.k);
+        // (E of the A side is formed by final_gram before the rows are normalized)
+        GemmProb p = make_prob(m.E, m.k, m.A, m.K_ld, m.F, m.K_ld, m.k, m.K_ld, m.k);
         p.Cin = m.A;
         p.ldcin = m.K_ld;
         p.alpha = -0.5f;
@@ -808,7 +853,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         }
     }
     for (GemmGroup* g : {&h->warm_nt, &h->warm_nn, &h->factor_v, &h->polish_nt, &h->polish_nn,
-                         &h->lowdin_eF, &h->lowdin_F, &h->lowdin_eW,
+                         &h->lowdin_F, &h->lowdin_eW,
                          &h->lowdin_W, &h->proj,
                          &h->s1_nn_a, &h->s1_nn_b, &h->s1_nt, &h->s2_nn, &h->s3_tn, &h->s3_nn})
         if ((rc = upload_group(h, *g))) return rc;

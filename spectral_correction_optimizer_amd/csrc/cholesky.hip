@@ -390,6 +390,91 @@ hipError_t launch_cholesky(const MatDev* mats, MatFlags* flags, const int* mat_i
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------
+// Normalized Gram of the final operand for the Loewdin step and the convergence
+// certificate: one workgroup per lower 64 x 64 tile (a >= b) of md.chol.  The
+// upper tile of E is written through an LDS transpose.
+__global__ __launch_bounds__(256) void gram_to_e_kernel(const MatDev* __restrict__ mats,
+                                                        MatFlags* __restrict__ flags,
+                                                        const int* __restrict__ mat_idx) {
+    __shared__ float T[CT][CT + 1];
+    __shared__ double rdi[CT], cdi[CT];
+    __shared__ float red[4];
+    const int i = mat_idx[blockIdx.y];
+    MatFlags& f = flags[i];
+    const MatDev& md = mats[i];
+    const int k = md.k, nt = (k + CT - 1) / CT;
+    const int t = blockIdx.x;
+    if (t >= nt * (nt + 1) / 2) return;
+    int a = (int)((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
+    while ((a + 1) * (a + 2) / 2 <= t) ++a;
+    while (a * (a + 1) / 2 > t) --a;
+    const int b = t - a * (a + 1) / 2;
+    const int r0 = a * CT, c0 = b * CT;
+    const double* C = md.chol;
+    const double fl2 = (double)f.floor2;
+    if (threadIdx.x < CT) {
+        const int r = r0 + threadIdx.x, c = c0 + threadIdx.x;
+        const double dr = r < k ? C[(int64_t)r * k + r] : 0.0, dc = c < k ? C[(int64_t)c * k + c] : 0.0;
+        rdi[threadIdx.x] = dr > fl2 ? 1.0 / sqrt(dr) : 0.0;
+        cdi[threadIdx.x] = dc > fl2 ? 1.0 / sqrt(dc) : 0.0;
+    }
+    __syncthreads();
+    float mo = 0.0f;
+    for (int idx = threadIdx.x; idx < CT * CT; idx += blockDim.x) {
+        const int r = idx >> 6, c = idx & 63;
+        const int gr = r0 + r, gc = c0 + c;
+        float e = 0.0f;
+        if (gr < k && gc < k && gc < gr) {
+            e = (float)(C[(int64_t)gr * k + gc] * rdi[r] * cdi[c]);
+            mo = fmaxf(mo, fabsf(e));
+        }
+        T[r][c] = e;
+        if (gr < k && gc < k && (a != b || gc <= gr)) md.E[(int64_t)gr * k + gc] = e;
+    }
+    for (int o = 32; o > 0; o >>= 1) mo = fmaxf(mo, __shfl_xor(mo, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mo;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        atomicMax(&f.check_off, __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
+    // mirror: E[c0 + c][r0 + r] = T[r][c]
+    for (int idx = threadIdx.x; idx < CT * CT; idx += blockDim.x) {
+        const int c = idx >> 6, r = idx & 63;
+        const int gr = r0 + r, gc = c0 + c;
+        if (gr < k && gc < k && gc < gr) md.E[(int64_t)gc * k + gr] = T[r][c];
+    }
+}
+
+hipError_t launch_gram_to_e(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
+                            int max_t64, hipStream_t st) {
+    hipLaunchKernelGGL(gram_to_e_kernel, dim3(max_t64 * (max_t64 + 1) / 2, nmat), dim3(256), 0, st,
+                       mats, flags, mat_idx);
+    return hipGetLastError();
+}
+
+__global__ void certify_kernel(const MatDev* __restrict__ mats, MatFlags* __restrict__ flags,
+                               const int* __restrict__ mat_idx, int nmat) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= nmat) return;
+    const int i = mat_idx[t];
+    MatFlags& f = flags[i];
+    if (!(__uint_as_float(f.check_off) > mats[i].tol_conv)) {
+        f.converged = 1;
+        f.done = 1;
+    } else {
+        f.converged = 0;
+        f.done = 0;
+        f.check_off = 0u;
+    }
+}
+
+hipError_t launch_certify(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
+                          hipStream_t st) {
+    hipLaunchKernelGGL(certify_kernel, dim3((nmat + 63) / 64), dim3(64), 0, st, mats, flags, mat_idx,
+                       nmat);
+    return hipGetLastError();
+}
+
 // Start of the polishing phase (A = M V already recomputed by a GEMM): clear
 // the convergence state, count the sweep cap from here, keep the work counters
 // of the factor phase apart.  The column order (perm) and the norms it was
@@ -406,6 +491,7 @@ __global__ void phase2_reset_kernel(MatFlags* __restrict__ flags, const int* __r
     f.sweep_base = f.sweeps;
     f.rounds_pre = f.rounds_active;
     f.pairs_pre = f.pairs_applied;
+    f.check_off = 0u;
 }
 
 hipError_t launch_phase2_reset(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,

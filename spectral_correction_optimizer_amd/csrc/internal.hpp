@@ -71,7 +71,8 @@ struct MatFlags {
     int chol_fail;           // 1 when the Gram's Cholesky factorization was rejected
     int rounds_pre;          // rounds_active / pairs_applied at the end of the factor phase
     int pairs_pre;
-    int pad[3];
+    unsigned int check_off;  // largest |a_p.a_q| / (|a_p| |a_q|) of the final operand (float bits)
+    int pad[2];
 };
 
 // ---- work items ------------------------------------------------------------------
@@ -158,6 +159,16 @@ hipError_t launch_chol_syrk(const MatDev* mats, const SyrkItem* items, int nitem
 // max_klen: largest klen.
 hipError_t launch_cholesky(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
                            int max_nbk, int max_klen, hipStream_t st);
+// E[i][j] = c_ij / sqrt(c_ii c_jj) (i != j; 0 on the diagonal and for columns at
+// the zero floor) from the float64 Gram in md.chol (lower triangle, from
+// launch_chol_syrk), for the matrices in mat_idx; the largest |E_ij| goes to
+// check_off.  max_t64: largest ceil(k / 64).
+hipError_t launch_gram_to_e(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
+                            int max_t64, hipStream_t st);
+// For the matrices in mat_idx: converged and done when check_off <= tol_conv,
+// otherwise not done (polishing sweeps follow) and check_off cleared.
+hipError_t launch_certify(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
+                          hipStream_t st);
 // inv[j] = 1 / sqrt(cnorm[j]) for j < k of the accepted matrices (into md.Y):
 // row scales that make V = L^T-phase vectors x W_prev orthonormal.
 hipError_t launch_factor_invnorm(const MatDev* mats, const MatFlags* flags, const int* mat_idx,
