@@ -76,13 +76,13 @@ def copy_calibration(nbytes):
 # were taken on (sha256 of the file); otherwise reported as null.
 TRAFFIC = {
     "jacobi_gram": {"source": "jacobi.hip", "sha256": "88b66451de2f9d80df5a71b0e9013752e7d434a7ddb5e12d72e2e7509c3f29c2",
-        "bytes_per_launch": 7.1432e+08},
+        "bytes_per_launch": 5.5386e+08},
     "jacobi_apply": {"source": "jacobi.hip", "sha256": "88b66451de2f9d80df5a71b0e9013752e7d434a7ddb5e12d72e2e7509c3f29c2",
-        "bytes_per_launch": 2.06757e+09},
-    "combine_adamw": {"source": "elementwise.hip", "sha256": "492eb4650cbcded5935d5e85055ac555da87f64f5d515c046d66b7d1e420f8f3",
+        "bytes_per_launch": 1.27495e+09},
+    "combine_adamw": {"source": "elementwise.hip", "sha256": "bed522873952defbc9da72cf6111d0732fc05759f37af33de11f58df8803dd0c",
         "bytes_per_launch": 3.11482e+10},
-    "ema": {"source": "elementwise.hip", "sha256": "492eb4650cbcded5935d5e85055ac555da87f64f5d515c046d66b7d1e420f8f3",
-        "bytes_per_launch": 1.16867e+10},
+    "ema": {"source": "elementwise.hip", "sha256": "bed522873952defbc9da72cf6111d0732fc05759f37af33de11f58df8803dd0c",
+        "bytes_per_launch": 1.16866e+10},
 }
 
 
