@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict
             for (int e = 0; e < 4; ++e) {
                 const int s = threadIdx.x + 256 * e;
                 const int row = r0[t] + (s >> 3), q = s & 7;
-                reg[t][e] = row < k ? *(const float4*)(md.A + (int64_t)row * ld + x0 + 4 * q)
+                reg[t][e] = row < k ? load4(md.A + (int64_t)row * ld + x0 + 4 * q)
                                     : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict
             for (int r = 0; r < 16; ++r) {
                 const int row = r0[0] + wr + 32 * a + 8 * (r >> 2) + 4 * hl + (r & 3);
                 const int col = r0[1] + wc + 32 * b + ll;
-                if (row < k && col < k) md.chol[(int64_t)row * k + col] = acc64[a][b][r];
+                if (row < k && col < k) gst(md.chol + (int64_t)row * k + col, acc64[a][b][r]);
             }
 }
 
@@ -426,11 +426,11 @@ __global__ __launch_bounds__(256) void gram_to_e_kernel(const MatDev* __restrict
         const int gr = r0 + r, gc = c0 + c;
         float e = 0.0f;
         if (gr < k && gc < k && gc < gr) {
-            e = (float)(C[(int64_t)gr * k + gc] * rdi[r] * cdi[c]);
+            e = (float)(gld(C + (int64_t)gr * k + gc) * rdi[r] * cdi[c]);
             mo = fmaxf(mo, fabsf(e));
         }
         T[r][c] = e;
-        if (gr < k && gc < k && (a != b || gc <= gr)) md.E[(int64_t)gr * k + gc] = e;
+        if (gr < k && gc < k && (a != b || gc <= gr)) gst(md.E + (int64_t)gr * k + gc, e);
     }
     for (int o = 32; o > 0; o >>= 1) mo = fmaxf(mo, __shfl_xor(mo, o));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mo;
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(256) void gram_to_e_kernel(const MatDev* __restrict
     for (int idx = threadIdx.x; idx < CT * CT; idx += blockDim.x) {
         const int c = idx >> 6, r = idx & 63;
         const int gr = r0 + r, gc = c0 + c;
-        if (gr < k && gc < k && gc < gr) md.E[(int64_t)gc * k + gr] = T[r][c];
+        if (gr < k && gc < k && gc < gr) gst(md.E + (int64_t)gc * k + gr, T[r][c]);
     }
 }
 

@@ -21,20 +21,49 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Device-memory accessors that compile to global_load / global_store.  A
+// pointer read from a struct in memory is generic, and generic (flat) accesses
+// are counted by the LDS wait counter as well: an s_waitcnt for an LDS read
+// would then also wait for every outstanding global prefetch.  All buffers of
+// the library and the caller's tensors are device (global) memory.
+#define SC_GLOBAL __attribute__((address_space(1)))
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+template <typename T>
+__device__ __forceinline__ SC_GLOBAL T* gptr(T* p) {
+    return (SC_GLOBAL T*)p;
+}
+template <typename T>
+__device__ __forceinline__ const SC_GLOBAL T* gptr(const T* p) {
+    return (const SC_GLOBAL T*)p;
+}
+template <typename T>
+__device__ __forceinline__ T gld(const T* p) {
+    return *gptr(p);
+}
+template <typename T>
+__device__ __forceinline__ void gst(T* p, T v) {
+    *gptr(p) = v;
+}
+__device__ __forceinline__ v4f gld4(const float* p) { return *(const SC_GLOBAL v4f*)p; }
+__device__ __forceinline__ void gst4(float* p, v4f v) { *(SC_GLOBAL v4f*)p = v; }
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
-    __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+    __device__ __forceinline__ static float load(const float* p, int64_t i) { return gld(p + i); }
 };
 template <> struct Elem<uint16_t> {
     __device__ __forceinline__ static float load(const uint16_t* p, int64_t i) {
-        return bf16_to_f32(p[i]);
+        return bf16_to_f32(gld(p + i));
     }
 };
 
 // Load 4 consecutive elements (the address must be 4-element aligned).
-__device__ __forceinline__ float4 load4(const float* p) { return *(const float4*)p; }
+__device__ __forceinline__ float4 load4(const float* p) {
+    const v4f v = gld4(p);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ float4 load4(const uint16_t* p) {
-    uint2 u = *(const uint2*)p;
+    const v2u u = *(const SC_GLOBAL v2u*)p;
     return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }

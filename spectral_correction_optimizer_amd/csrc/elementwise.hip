@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kEwThreads) void ema_kernel(const MatDev* __restric
         for (int u = 0; u < 4; ++u) {
             int v = v0 + u * kEwThreads;
             if (v < nvec) {
-                mv[u] = *(const float4*)(M + 4 * v);
+                mv[u] = load4(M + 4 * v);
                 gv[u] = load4(G + 4 * v);
             }
         }
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kEwThreads) void ema_kernel(const MatDev* __restric
                 r.w = fmaf(beta, mv[u].w, omb * gv[u].w);
                 bad |= !(isfinite(gv[u].x) && isfinite(gv[u].y) && isfinite(gv[u].z) &&
                          isfinite(gv[u].w));
-                *(float4*)(M + 4 * v) = r;
+                gst4(M + 4 * v, v4f{r.x, r.y, r.z, r.w});
             }
         }
     }
@@ -106,7 +106,7 @@ template <typename WT>
 __device__ __forceinline__ void store_w4(WT* p, float4 w);
 template <>
 __device__ __forceinline__ void store_w4<float>(float* p, float4 w) {
-    *(float4*)p = w;
+    gst4(p, v4f{w.x, w.y, w.z, w.w});
 }
 template <>
 __device__ __forceinline__ void store_w4<uint16_t>(uint16_t* p, float4 w) {
@@ -148,10 +148,10 @@ __global__ __launch_bounds__(kEwThreads) void combine_adamw_kernel(
             int v = v0 + u * kEwThreads;
             if (v < nvec) {
                 gv[u] = load4(G + 4 * v);
-                fv[u] = *(const float4*)(Gf + 4 * v);
+                fv[u] = load4(Gf + 4 * v);
                 wv[u] = load4(W + 4 * v);
-                mv[u] = *(const float4*)(Mm + 4 * v);
-                vv[u] = *(const float4*)(Vv + 4 * v);
+                mv[u] = load4(Mm + 4 * v);
+                vv[u] = load4(Vv + 4 * v);
             }
         }
 #pragma unroll
@@ -166,9 +166,9 @@ __global__ __launch_bounds__(kEwThreads) void combine_adamw_kernel(
                 bad |= !(isfinite(gv[u].x) && isfinite(gv[u].y) && isfinite(gv[u].z) &&
                          isfinite(gv[u].w));
                 store_w4<WT>(W + 4 * v, w);
-                *(float4*)(Mm + 4 * v) = mv[u];
-                *(float4*)(Vv + 4 * v) = vv[u];
-                if (Gp) *(float4*)(Gp + 4 * v) = p;
+                gst4(Mm + 4 * v, v4f{mv[u].x, mv[u].y, mv[u].z, mv[u].w});
+                gst4(Vv + 4 * v, v4f{vv[u].x, vv[u].y, vv[u].z, vv[u].w});
+                if (Gp) gst4(Gp + 4 * v, v4f{p.x, p.y, p.z, p.w});
             }
         }
     }

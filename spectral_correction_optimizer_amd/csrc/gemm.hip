@@ -93,7 +93,7 @@ struct TileLoader<true, T> {
                     if (c + 3 < cols) v.w = Elem<T>::load(q, 3);
                 }
                 if (kscale) {
-                    float f = kscale[kk];
+                    float f = gld(kscale + kk);
                     v.x *= f;
                     v.y *= f;
                     v.z *= f;
@@ -125,10 +125,10 @@ struct TileLoaderRowsK : TileLoader<false, T> {
                 int s = threadIdx.x + e * 256;
                 int kk = k0 + 4 * (s & 3);
                 float4& v = this->r[e];
-                if (kk + 0 < kdim) v.x *= kscale[kk + 0];
-                if (kk + 1 < kdim) v.y *= kscale[kk + 1];
-                if (kk + 2 < kdim) v.z *= kscale[kk + 2];
-                if (kk + 3 < kdim) v.w *= kscale[kk + 3];
+                if (kk + 0 < kdim) v.x *= gld(kscale + kk + 0);
+                if (kk + 1 < kdim) v.y *= gld(kscale + kk + 1);
+                if (kk + 2 < kdim) v.z *= gld(kscale + kk + 2);
+                if (kk + 3 < kdim) v.w *= gld(kscale + kk + 3);
             }
         }
     }
@@ -220,16 +220,16 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
         for (int j = 0; j < 2; ++j) {
             const int col = n0 + wn + 32 * j + ll;
             if (col >= N) continue;
-            const float cs = P.col_scale ? P.col_scale[col] : 1.0f;
+            const float cs = P.col_scale ? gld(P.col_scale + col) : 1.0f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * hl + (r & 3);
                 if (row >= M) continue;
                 float v = alpha * acc[i][j][r] * cs;
-                if (P.row_scale) v *= P.row_scale[row];
+                if (P.row_scale) v *= gld(P.row_scale + row);
                 if (zdiag && row == col) v = 0.0f;
-                if (P.Cin) v += beta * P.Cin[(int64_t)row * P.ldcin + col];
-                P.C[(int64_t)row * P.ldc + col] = v;
+                if (P.Cin) v += beta * gld(P.Cin + (int64_t)row * P.ldcin + col);
+                gst(P.C + (int64_t)row * P.ldc + col, v);
             }
         }
     }

@@ -36,7 +36,7 @@ constexpr int CHUNK = 256;       // fp32 accumulation length before folding into
 
 // Physical row of A / V holding local column rho (0..63) of block pair (I, J).
 __device__ __forceinline__ int pair_row(const MatDev& md, int blkI, int blkJ, int rho) {
-    return md.perm[rho < kJb ? blkI * kJb + rho : blkJ * kJb + (rho - kJb)];
+    return gld(md.perm + (rho < kJb ? blkI * kJb + rho : blkJ * kJb + (rho - kJb)));
 }
 
 }  // namespace
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
     float4 reg[2];
     auto gload = [&](int x0) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) reg[e] = *(const float4*)(rowp[e] + x0 + 4 * lq[e]);
+        for (int e = 0; e < 2; ++e) reg[e] = load4(rowp[e] + x0 + 4 * lq[e]);
     };
     auto lstore = [&](int b) {
 #pragma unroll
@@ -103,7 +103,9 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
         }
     };
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    // wave index made visibly uniform so that the tile switch is a scalar branch
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     // tiles (row strip, column strip) per wave
     int ti[3], tj[3], nt;
     if (wave == 0) { ti[0] = 0; tj[0] = 0; ti[1] = 0; tj[1] = 1; ti[2] = 0; tj[2] = 2; nt = 3; }
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * ti[t] + 4 * (lane >> 4) + r, col = 16 * tj[t] + (lane & 15);
-            out[row * PW + col] = acc64[t][r];
+            gst(out + row * PW + col, acc64[t][r]);
         }
     }
 }
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
         const int row = idx >> 6, col = idx & 63;
         const int src = (row >> 4) <= (col >> 4) ? idx : col * PW + row;
         double s = 0.0;
-        for (int sp = 0; sp < it.nsplit; ++sp) s += gp[(int64_t)sp * PW * PW + src];
+        for (int sp = 0; sp < it.nsplit; ++sp) s += gld(gp + (int64_t)sp * PW * PW + src);
         gv[e] = s;
         R[idx >> 6][idx & 63] = 0.0f;
         if ((idx >> 6) == (idx & 63)) {
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
     int* rflag = md.rot_flag + it.slot;
     if (!(mo > tol)) {
         // columns unchanged: their norms for the next sweep's ordering
-        if (tid < PW) md.cnorm[pair_row(md, bI, bJ, tid)] = (float)dg[tid];
+        if (tid < PW) gst(md.cnorm + pair_row(md, bI, bJ, tid), (float)dg[tid]);
         if (tid == 0) *rflag = 0;
         return;
     }
@@ -338,9 +340,9 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
     const float (*Gf)[PW + 1] = G[(PW - 1) & 1];
     // 4. R row-major [b][a] (X_new[a] = X[a] + sum_b R[b][a] X[b])
     float* Rg = md.rot + (int64_t)it.slot * PW * PW;
-    for (int idx = tid; idx < PW * PW; idx += 256) Rg[idx] = R[idx >> 6][idx & 63];
+    for (int idx = tid; idx < PW * PW; idx += 256) gst(Rg + idx, R[idx >> 6][idx & 63]);
     // rotated squared column norms (diagonal of Q^T G Q) for the next sweep's ordering
-    if (tid < PW) md.cnorm[pair_row(md, bI, bJ, tid)] = (float)(Gf[tid][tid] * dmax);
+    if (tid < PW) gst(md.cnorm + pair_row(md, bI, bJ, tid), (float)(Gf[tid][tid] * dmax));
     if (tid == 0) {
         *rflag = 1;
         atomicAdd(&fl.pairs_applied, 1);
@@ -389,12 +391,12 @@ __global__ __launch_bounds__(kApplyThreads) void jac_apply_kernel(const MatDev* 
     float* const col = base + n;
     if (active) {
 #pragma unroll
-        for (int s = 0; s < PW / 2; ++s) xb[s] = col[(int64_t)prow[s] * ld];
+        for (int s = 0; s < PW / 2; ++s) xb[s] = gld(col + (int64_t)prow[s] * ld);
     }
     const float* R = md.rot + (int64_t)it.slot * PW * PW;
     for (int idx = threadIdx.x; idx < PW * PW / 4; idx += kApplyThreads) {
         const int b = idx >> 4, a4 = (idx & 15) * 4;
-        *(float4*)&Rs[b][a4] = *(const float4*)(R + b * PW + a4);
+        *(v4f*)&Rs[b][a4] = gld4(R + b * PW + a4);
     }
     __syncthreads();
     if (!active) return;
@@ -414,8 +416,8 @@ __global__ __launch_bounds__(kApplyThreads) void jac_apply_kernel(const MatDev* 
     // acc0 register r is row apply_row(r, hl), acc1 register r is row apply_row(16 + r, hl)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        col[(int64_t)prow[r] * ld] = xb[r] + acc0[r];
-        col[(int64_t)prow[16 + r] * ld] = xb[16 + r] + acc1[r];
+        gst(col + (int64_t)prow[r] * ld, xb[r] + acc0[r]);
+        gst(col + (int64_t)prow[16 + r] * ld, xb[16 + r] + acc1[r]);
     }
 }
 
