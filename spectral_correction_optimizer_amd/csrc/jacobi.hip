@@ -87,12 +87,14 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
         lq[e] = s & 7;
         rowp[e] = md.A + (int64_t)pair_row(md, bI, bJ, lrow[e]) * md.K_ld;
     }
-    float4 reg[2];
-    auto gload = [&](int x0) {
+    // two register sets: the loads of a stage are issued two stages before its
+    // LDS store, so about two stages of compute cover the memory latency
+    float4 regA[2], regB[2];
+    auto gload = [&](float4 (&reg)[2], int x0) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) reg[e] = load4(rowp[e] + x0 + 4 * lq[e]);
     };
-    auto lstore = [&](int b) {
+    auto lstore = [&](const float4 (&reg)[2], int b) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int col = lrow[e] ^ (8 * lq[e]);
@@ -122,14 +124,7 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
             acc64[t][r] = 0.0;
         }
     const int nst = (x_end - x_begin) / KC;  // split bounds are multiples of KC
-    if (nst > 0) {
-        gload(x_begin);
-        lstore(0);
-    }
-    __syncthreads();
-    for (int st = 0; st < nst; ++st) {
-        const int b = st & 1;
-        if (st + 1 < nst) gload(x_begin + (st + 1) * KC);
+    auto compute = [&](int b) {
 #pragma unroll
         for (int kk = 0; kk < KC; kk += 4) {
             const int k = kk + (lane >> 4);
@@ -162,6 +157,8 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
             }
 #undef SC_MF
         }
+    };
+    auto fold = [&](int st) {
         if (((st + 1) * KC) % CHUNK == 0 || st + 1 == nst) {
 #pragma unroll
             for (int t = 0; t < 3; ++t)
@@ -171,7 +168,27 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
                     acc[t][r] = 0.0f;
                 }
         }
-        if (st + 1 < nst) lstore(b ^ 1);
+    };
+    if (nst > 0) {
+        gload(regA, x_begin);
+        lstore(regA, 0);
+    }
+    if (nst > 1) gload(regA, x_begin + KC);
+    if (nst > 2) gload(regB, x_begin + 2 * KC);
+    __syncthreads();
+    // stage st lives in Xs[st & 1]; at the top of an even stage regA holds stage
+    // st + 1 and regB stage st + 2 (both possibly still in flight)
+    for (int st = 0; st < nst; st += 2) {
+        compute(0);
+        fold(st);
+        if (st + 1 < nst) lstore(regA, 1);
+        if (st + 3 < nst) gload(regA, x_begin + (st + 3) * KC);
+        __syncthreads();
+        if (st + 1 >= nst) break;
+        compute(1);
+        fold(st + 1);
+        if (st + 2 < nst) lstore(regB, 0);
+        if (st + 4 < nst) gload(regB, x_begin + (st + 4) * KC);
         __syncthreads();
     }
     // 16x16 output layout: lane l, register r -> row 4 (l / 16) + r, column l % 16.
