@@ -92,7 +92,10 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
     float4 regA[2], regB[2];
     auto gload = [&](float4 (&reg)[2], int x0) {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) reg[e] = load4(rowp[e] + x0 + 4 * lq[e]);
+        for (int e = 0; e < 2; ++e) {
+            const v4f v = __builtin_nontemporal_load((const SC_GLOBAL v4f*)(rowp[e] + x0 + 4 * lq[e]));
+            reg[e] = make_float4(v.x, v.y, v.z, v.w);
+        }
     };
     auto lstore = [&](const float4 (&reg)[2], int b) {
 #pragma unroll
@@ -408,7 +411,8 @@ __global__ __launch_bounds__(kApplyThreads) void jac_apply_kernel(const MatDev* 
     float* const col = base + n;
     if (active) {
 #pragma unroll
-        for (int s = 0; s < PW / 2; ++s) xb[s] = gld(col + (int64_t)prow[s] * ld);
+        for (int s = 0; s < PW / 2; ++s)
+            xb[s] = __builtin_nontemporal_load(gptr(col + (int64_t)prow[s] * ld));
     }
     const float* R = md.rot + (int64_t)it.slot * PW * PW;
     for (int idx = threadIdx.x; idx < PW * PW / 4; idx += kApplyThreads) {
@@ -433,8 +437,8 @@ __global__ __launch_bounds__(kApplyThreads) void jac_apply_kernel(const MatDev* 
     // acc0 register r is row apply_row(r, hl), acc1 register r is row apply_row(16 + r, hl)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        gst(col + (int64_t)prow[r] * ld, xb[r] + acc0[r]);
-        gst(col + (int64_t)prow[16 + r] * ld, xb[16 + r] + acc1[r]);
+        __builtin_nontemporal_store(xb[r] + acc0[r], gptr(col + (int64_t)prow[r] * ld));
+        __builtin_nontemporal_store(xb[16 + r] + acc1[r], gptr(col + (int64_t)prow[16 + r] * ld));
     }
 }
 
