@@ -57,6 +57,26 @@ template <> struct Elem<uint16_t> {
     }
 };
 
+// Streaming (nontemporal) variants for data touched once per pass: they keep
+// the stream from displacing other lines in the caches.  4-element aligned.
+__device__ __forceinline__ float4 load4_nt(const float* p) {
+    const v4f v = __builtin_nontemporal_load((const SC_GLOBAL v4f*)p);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 load4_nt(const uint16_t* p) {
+    const v2u u = __builtin_nontemporal_load((const SC_GLOBAL v2u*)p);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+__device__ __forceinline__ void store4_nt(float* p, float4 w) {
+    __builtin_nontemporal_store(v4f{w.x, w.y, w.z, w.w}, (SC_GLOBAL v4f*)p);
+}
+__device__ __forceinline__ void store4_nt(uint16_t* p, float4 w) {
+    const v2u u = {(uint32_t)f32_to_bf16(w.x) | ((uint32_t)f32_to_bf16(w.y) << 16),
+                   (uint32_t)f32_to_bf16(w.z) | ((uint32_t)f32_to_bf16(w.w) << 16)};
+    __builtin_nontemporal_store(u, (SC_GLOBAL v2u*)p);
+}
+
 // Load 4 consecutive elements (the address must be 4-element aligned).
 __device__ __forceinline__ float4 load4(const float* p) {
     const v4f v = gld4(p);

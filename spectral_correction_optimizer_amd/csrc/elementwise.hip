@@ -36,8 +36,8 @@ __global__ __launch_bounds__(kEwThreads) void ema_kernel(const MatDev* __restric
         for (int u = 0; u < 4; ++u) {
             int v = v0 + u * kEwThreads;
             if (v < nvec) {
-                mv[u] = load4(M + 4 * v);
-                gv[u] = load4(G + 4 * v);
+                mv[u] = load4_nt(M + 4 * v);
+                gv[u] = load4_nt(G + 4 * v);
             }
         }
 #pragma unroll
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(kEwThreads) void ema_kernel(const MatDev* __restric
                 r.w = fmaf(beta, mv[u].w, omb * gv[u].w);
                 bad |= !(isfinite(gv[u].x) && isfinite(gv[u].y) && isfinite(gv[u].z) &&
                          isfinite(gv[u].w));
-                gst4(M + 4 * v, v4f{r.x, r.y, r.z, r.w});
+                store4_nt(M + 4 * v, r);
             }
         }
     }
@@ -147,11 +147,11 @@ __global__ __launch_bounds__(kEwThreads) void combine_adamw_kernel(
         for (int u = 0; u < 2; ++u) {
             int v = v0 + u * kEwThreads;
             if (v < nvec) {
-                gv[u] = load4(G + 4 * v);
-                fv[u] = load4(Gf + 4 * v);
-                wv[u] = load4(W + 4 * v);
-                mv[u] = load4(Mm + 4 * v);
-                vv[u] = load4(Vv + 4 * v);
+                gv[u] = load4_nt(G + 4 * v);
+                fv[u] = load4_nt(Gf + 4 * v);
+                wv[u] = load4_nt(W + 4 * v);
+                mv[u] = load4_nt(Mm + 4 * v);
+                vv[u] = load4_nt(Vv + 4 * v);
             }
         }
 #pragma unroll
@@ -165,10 +165,10 @@ __global__ __launch_bounds__(kEwThreads) void combine_adamw_kernel(
                 w.w = adam_elem(gv[u].w, fv[u].w, mv[u].w, vv[u].w, wv[u].w, a, p.w);
                 bad |= !(isfinite(gv[u].x) && isfinite(gv[u].y) && isfinite(gv[u].z) &&
                          isfinite(gv[u].w));
-                store_w4<WT>(W + 4 * v, w);
-                gst4(Mm + 4 * v, v4f{mv[u].x, mv[u].y, mv[u].z, mv[u].w});
-                gst4(Vv + 4 * v, v4f{vv[u].x, vv[u].y, vv[u].z, vv[u].w});
-                if (Gp) gst4(Gp + 4 * v, v4f{p.x, p.y, p.z, p.w});
+                store4_nt(W + 4 * v, w);
+                store4_nt(Mm + 4 * v, mv[u]);
+                store4_nt(Vv + 4 * v, vv[u]);
+                if (Gp) store4_nt(Gp + 4 * v, p);
             }
         }
     }
