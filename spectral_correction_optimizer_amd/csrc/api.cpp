@@ -126,12 +126,15 @@ struct sc_opt {
     char* proj_arena = nullptr;
     Chunk* chunks_d = nullptr;
     int nchunks = 0;
-    // Jacobi work lists of the two matrix groups whose rounds run on two
-    // internal streams (one group's pair solves overlap the other's Gram /
-    // rotation kernels); matrices are assigned to groups by decreasing work.
-    // Three list sets: plain (every matrix, full rows), factor (every matrix;
-    // preconditioned ones over their klen-long factor rows) and polish (only
-    // the preconditioned matrices, full rows).
+    // The refresh runs as up to two pipelines ("pipes"), each over about half of
+    // the work on its own internal stream (default priority) with its own work
+    // lists, GEMM tables and progress: one pipe's MFMA-bound GEMMs and
+    // latency-bound pair solves overlap the other's memory-bound sweeps, and
+    // neither waits for the other's convergence checks.  Jacobi work lists come
+    // in three sets: plain
+    // (every matrix of the pipe, full rows), factor (every matrix; preconditioned
+    // ones over their klen-long factor rows, without V) and polish (only the
+    // preconditioned matrices, full rows).
     struct Lists {
         GramItem* gi = nullptr;
         int ngi = 0;
@@ -143,29 +146,31 @@ struct sc_opt {
         int nmat = 0;
         int max_nb = 2;
     };
-    struct JGroup {
+    struct Pipe {
         Lists L[3];
+        std::vector<int> host_mats;
+        int* mats = nullptr;  // every matrix of the pipe
+        int nmat = 0;
+        int* cap = nullptr;   // those with a factor phase (max(m, n) >= 2 min(m, n))
+        int ncap = 0;
+        SyrkItem* syrk_cap = nullptr;  // lower 128 x 128 tiles of A^T A, factor-phase matrices
+        int nsyrk_cap = 0;
+        SyrkItem* syrk_all = nullptr;  // the same for every matrix (final Gram)
+        int nsyrk_all = 0;
+        int max_kpad = 64, max_K = 128, max_k = 1, max_nbk = 0, max_klen = 0, max_t64 = 1;
+        GemmGroup warm_nt, warm_nn;      // warm start: A_rows = W M^T (m >= n) or W M (m < n)
+        GemmGroup factor_v;              // V rows <- diag(1/|x_j|) X^T V_prev (gated per matrix)
+        GemmGroup polish_nt, polish_nn;  // A_rows = V op(M) after the factor phase
+        GemmGroup lowdin_F, lowdin_eW, lowdin_W, proj;
         hipStream_t st = nullptr;
-        hipEvent_t join = nullptr;
-    } jg[2];
-    // preconditioned matrices (max(m, n) >= 2 min(m, n) when hp.precondition)
-    int* cap_d = nullptr;
-    int ncap = 0;
-    int max_nbk = 0;  // largest ceil(k / 64) among them
-    SyrkItem* syrk_d = nullptr;     // lower tiles of A^T A of those matrices
-    int nsyrk = 0;
-    SyrkItem* syrk_all_d = nullptr; // lower tiles of A^T A of every matrix (final Gram)
-    int nsyrk_all = 0;
-    int* all_d = nullptr;           // 0 .. n-1
-    int max_t64 = 1;                // largest ceil(k / 64)
-    GemmGroup polish_nt, polish_nn; // A_rows = V op(M) after the factor phase
-    GemmGroup factor_v;             // V rows <- diag(1/|x_j|) X^T V_prev (gated per matrix)
-    int max_klen = 0;
+        hipEvent_t join = nullptr, poll = nullptr;
+        MatFlags* flags_h = nullptr;  // pinned target of this pipe's flag polls
+        // progress of the refresh in flight
+        int stage = 0, which = 0, r = 0, rps = 1, max_rounds = 0, first_check = 0, poll_round = 0;
+        bool pre = false, poll_pending = false;
+    } pipes[2];
+    int npipes = 0;
     hipEvent_t fork = nullptr;
-    int max_nb = 2, max_kpad = 64, max_K = 1, max_k = 1;
-    // refresh GEMMs
-    GemmGroup lowdin_F, lowdin_eW, lowdin_W, proj;
-    GemmGroup warm_nt, warm_nn;  // warm start: A_rows = W M^T (m >= n) or W M (m < n)
     bool have_factors = false;   // W holds orthonormal rows from a refresh / sc_set_factors
     // step GEMMs
     GemmGroup s1_nn_a, s1_nn_b, s1_nt, s2_nn, s3_tn, s3_nn;
@@ -175,8 +180,6 @@ struct sc_opt {
     bool any_stale = false;
     bool proj_stale = false;
     bool keep_proj = false;
-    std::vector<int> last_sweeps;
-    int last_not_conv = 0;
     std::vector<void*> dev_allocs;
     Prof prof;
     double total_numel = 0.0;
@@ -312,46 +315,58 @@ PtrTable make_table(const sc_opt* h, const void* const* p) {
 
 // ---- refresh ------------------------------------------------------------------------
 
-int build_projectors(sc_opt* h, hipStream_t st) {
+enum { LIST_PLAIN = 0, LIST_FACTOR = 1, LIST_POLISH = 2 };
+enum { STAGE_ROUNDS = 0, STAGE_CERT = 1, STAGE_DONE = 2 };
+typedef sc_opt::Pipe Pipe;
+
+// d = s / (s + tau) and the projectors X^T diag(d) X of the pipe's matrices.
+int pipe_projectors(sc_opt* h, Pipe& p, hipStream_t st) {
     HIP_TRY(timed(h, PK_FILTER, st,
-                  [&] { return launch_filter(h->md, h->n, h->hp.tau_p, h->max_kpad, st); }));
-    PtrTable none = make_table(h, nullptr);
-    int rc = run_group(h, h->proj, PK_PROJECTORS, none, st);
-    if (rc) return rc;
+                  [&] { return launch_filter(h->md, p.mats, p.nmat, h->hp.tau_p, st); }));
+    return run_group(h, p.proj, PK_PROJECTORS, make_table(h, nullptr), st);
+}
+
+int build_projectors(sc_opt* h, hipStream_t st) {
+    for (int q = 0; q < h->npipes; ++q) {
+        int rc = pipe_projectors(h, h->pipes[q], st);
+        if (rc) return rc;
+    }
     h->proj_stale = false;
     return SC_OK;
 }
 
-// chol = A^T A (float64 sums) and E = its normalized off-diagonal part, all matrices.
-int final_gram(sc_opt* h, hipStream_t st) {
+// chol = A^T A (float64 sums) and E = its normalized off-diagonal part.
+int pipe_final_gram(sc_opt* h, Pipe& p, hipStream_t st) {
     HIP_TRY(timed(h, PK_GRAM_E, st,
-                  [&] { return launch_chol_syrk(h->md, h->syrk_all_d, h->nsyrk_all, st); }));
+                  [&] { return launch_chol_syrk(h->md, p.syrk_all, p.nsyrk_all, st); }));
     HIP_TRY(timed(h, PK_GRAM_E, st, [&] {
-        return launch_gram_to_e(h->md, h->flags_d, h->all_d, h->n, h->max_t64, st);
+        return launch_gram_to_e(h->md, h->flags_d, p.mats, p.nmat, p.max_t64, st);
     }));
     if (h->prof.on)
-        for (int i = 0; i < h->n; ++i) {
+        for (int i : p.host_mats) {
             const double kt = (h->mh[i].k + 127) / 128;
             h->prof.flops[PK_GRAM_E] += kt * (kt + 1) / 2 * 2.0 * 128 * 128 * h->mh[i].K_ld;
         }
     return SC_OK;
 }
 
-int finalize_factors(sc_opt* h, hipStream_t st) {
+// Unit rows, s_j = |a_j| / |v_j|, one Loewdin step on both factors, projectors.
+int pipe_finalize(sc_opt* h, Pipe& p, hipStream_t st) {
     PtrTable none = make_table(h, nullptr);
     for (int which = 0; which < 2; ++which) {
-        HIP_TRY(timed(h, PK_ROWNORM, st,
-                      [&] { return launch_rownorm(h->md, h->n, which, h->max_kpad, st); }));
+        HIP_TRY(timed(h, PK_ROWNORM, st, [&] {
+            return launch_rownorm(h->md, p.mats, p.nmat, which, p.max_kpad, st);
+        }));
         HIP_TRY(timed(h, PK_NORMALIZE, st, [&] {
-            return launch_normalize(h->md, h->flags_d, h->n, which, h->max_kpad, h->max_K, st);
+            return launch_normalize(h->md, p.mats, h->flags_d, p.nmat, which, p.max_kpad, st);
         }));
     }
     int rc;
-    // E (normalized Gram of the A-side rows, zero diagonal) comes from final_gram
-    if ((rc = run_group(h, h->lowdin_F, PK_LOWDIN, none, st))) return rc;
-    if ((rc = run_group(h, h->lowdin_eW, PK_LOWDIN, none, st))) return rc;
-    if ((rc = run_group(h, h->lowdin_W, PK_LOWDIN, none, st))) return rc;
-    return build_projectors(h, st);
+    // E (normalized Gram of the A-side rows, zero diagonal) comes from the final Gram
+    if ((rc = run_group(h, p.lowdin_F, PK_LOWDIN, none, st))) return rc;
+    if ((rc = run_group(h, p.lowdin_eW, PK_LOWDIN, none, st))) return rc;
+    if ((rc = run_group(h, p.lowdin_W, PK_LOWDIN, none, st))) return rc;
+    return pipe_projectors(h, p, st);
 }
 
 // Algorithmic work of the Jacobi sweeps from the device counters (profiling only):
@@ -379,146 +394,215 @@ void account_sweeps(sc_opt* h) {
     }
 }
 
-// Jacobi rounds over list set `which` of both groups until every matrix is done
-// (polled on the host once per sweep from sweep `first_check` on) or the sweep
-// cap is reached.  Without kernel timing the groups run on their own streams,
-// forked from and joined back into `st`.
-int run_rounds(sc_opt* h, hipStream_t st, int which, int first_check_sweeps) {
-    int max_nb = 2;
-    for (auto& G : h->jg)
-        if (G.L[which].nmat) max_nb = std::max(max_nb, G.L[which].max_nb);
-    const int rps = max_nb - 1;  // rounds per sweep of the largest matrix
-    const int max_rounds = h->hp.max_sweeps * rps;
-    const int first_check = std::min(max_rounds, first_check_sweeps * rps);
-    // With kernel timing on, both groups run on the caller's stream so that
-    // every kernel's events bracket it alone (no overlap between groups).
-    const bool split = !h->prof.on;
-    if (split) {
-        HIP_TRY(hipEventRecord(h->fork, st));
-        for (auto& G : h->jg)
-            if (G.L[which].nmat) HIP_TRY(hipStreamWaitEvent(G.st, h->fork, 0));
+// Start of a refresh for one pipe: operand A (warm: A = M V_prev; cold: A = M),
+// row norms, flags, and for the factor phase A^T A and its Cholesky factor.
+int pipe_pre(sc_opt* h, Pipe& p, hipStream_t st, bool warm) {
+    PtrTable none = make_table(h, nullptr);
+    int rc;
+    if (warm) {
+        HIP_TRY(timed(h, PK_WARM, st,
+                      [&] { return launch_jacobi_warm(h->md, p.mats, p.nmat, st); }));
+        if ((rc = run_group(h, p.warm_nt, PK_WARM, none, st))) return rc;
+        if ((rc = run_group(h, p.warm_nn, PK_WARM, none, st))) return rc;
+    } else {
+        HIP_TRY(timed(h, PK_LOAD, st, [&] {
+            return launch_jacobi_load(h->md, p.mats, p.nmat, p.max_kpad, p.max_K + 128, st);
+        }));
     }
-    for (int r = 0; r < max_rounds; ++r) {
-        for (auto& G : h->jg) {
-            const sc_opt::Lists& L = G.L[which];
-            if (!L.nmat || r >= h->hp.max_sweeps * (L.max_nb - 1)) continue;
-            hipStream_t gs = split ? G.st : st;
-            HIP_TRY(timed(h, PK_SORT, gs, [&] {
-                return launch_jacobi_sort(h->md, h->flags_d, L.mats, L.nmat, r, gs);
-            }));
-            HIP_TRY(timed(h, PK_GRAM, gs, [&] {
-                return launch_jacobi_gram(h->md, h->flags_d, L.gi, L.ngi, r, gs);
-            }));
-            HIP_TRY(timed(h, PK_SOLVE, gs, [&] {
-                return launch_jacobi_solve(h->md, h->flags_d, L.si, L.nsi, r, gs);
-            }));
-            HIP_TRY(timed(h, PK_APPLY, gs, [&] {
-                return launch_jacobi_apply(h->md, h->flags_d, L.ai, L.nai, r, gs);
-            }));
-            HIP_TRY(timed(h, PK_SWEEP_END, gs, [&] {
-                return launch_jacobi_sweep_end(h->md, h->flags_d, L.mats, L.nmat, r,
-                                               h->hp.max_sweeps, gs);
-            }));
-        }
-        if (h->hp.sync_check && r + 1 >= first_check && (r + 1) % rps == 0 && r + 1 < max_rounds) {
-            for (auto& G : h->jg)
-                if (G.L[which].nmat) HIP_TRY(hipStreamSynchronize(split ? G.st : st));
-            HIP_TRY(hipMemcpy(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n,
-                              hipMemcpyDeviceToHost));
-            bool all = true;
-            for (int i = 0; i < h->n; ++i) all = all && h->flags_h[i].done;
-            if (all) break;
-        }
-    }
-    for (auto& G : h->jg) {
-        if (!G.L[which].nmat || !split) continue;
-        HIP_TRY(hipEventRecord(G.join, G.st));
-        HIP_TRY(hipStreamWaitEvent(st, G.join, 0));
+    HIP_TRY(timed(h, PK_ROWNORM, st,
+                  [&] { return launch_rownorm(h->md, p.mats, p.nmat, 0, p.max_kpad, st); }));
+    HIP_TRY(timed(h, PK_INIT_FLAGS, st, [&] {
+        return launch_jacobi_init_flags(h->md, p.mats, h->flags_d, p.nmat, st);
+    }));
+    if (p.pre) {
+        // Factor phase: Jacobi on X = L, A^T A = L L^T (k-long rows, no V).
+        HIP_TRY(timed(h, PK_CHOL_GEMM, st,
+                      [&] { return launch_chol_syrk(h->md, p.syrk_cap, p.nsyrk_cap, st); }));
+        HIP_TRY(timed(h, PK_CHOL, st, [&] {
+            return launch_cholesky(h->md, h->flags_d, p.cap, p.ncap, p.max_nbk, p.max_klen, st);
+        }));
+        if (h->prof.on)
+            for (int i : p.host_mats)
+                if (h->mh[i].klen) {
+                    const double kt = (h->mh[i].k + 127) / 128;
+                    h->prof.flops[PK_CHOL_GEMM] +=
+                        kt * (kt + 1) / 2 * 2.0 * 128 * 128 * h->mh[i].K_ld;
+                    h->prof.flops[PK_CHOL] += std::pow((double)h->mh[i].k, 3) / 3.0;
+                }
     }
     return SC_OK;
 }
 
-enum { LIST_PLAIN = 0, LIST_FACTOR = 1, LIST_POLISH = 2 };
+void pipe_start_rounds(sc_opt* h, Pipe& p, int which, int first_check_sweeps) {
+    p.stage = STAGE_ROUNDS;
+    p.which = which;
+    p.r = 0;
+    p.rps = std::max(1, p.L[which].max_nb - 1);  // rounds per sweep of the largest matrix
+    p.max_rounds = p.L[which].nmat ? h->hp.max_sweeps * p.rps : 0;
+    p.first_check = std::min(p.max_rounds, first_check_sweeps * p.rps);
+    p.poll_pending = false;
+}
+
+// One Jacobi round of the pipe's current list set.
+int pipe_round(sc_opt* h, Pipe& p, hipStream_t st) {
+    const sc_opt::Lists& L = p.L[p.which];
+    const int r = p.r;
+    HIP_TRY(timed(h, PK_SORT, st,
+                  [&] { return launch_jacobi_sort(h->md, h->flags_d, L.mats, L.nmat, r, st); }));
+    HIP_TRY(timed(h, PK_GRAM, st,
+                  [&] { return launch_jacobi_gram(h->md, h->flags_d, L.gi, L.ngi, r, st); }));
+    HIP_TRY(timed(h, PK_SOLVE, st,
+                  [&] { return launch_jacobi_solve(h->md, h->flags_d, L.si, L.nsi, r, st); }));
+    HIP_TRY(timed(h, PK_APPLY, st,
+                  [&] { return launch_jacobi_apply(h->md, h->flags_d, L.ai, L.nai, r, st); }));
+    HIP_TRY(timed(h, PK_SWEEP_END, st, [&] {
+        return launch_jacobi_sweep_end(h->md, h->flags_d, L.mats, L.nmat, r, h->hp.max_sweeps, st);
+    }));
+    return SC_OK;
+}
+
+// Copy the flags to the pipe's pinned buffer behind the work queued so far and
+// mark the point with an event; the host polls it without blocking the queues.
+int pipe_poll(sc_opt* h, Pipe& p, hipStream_t st) {
+    HIP_TRY(hipMemcpyAsync(p.flags_h, h->flags_d, sizeof(MatFlags) * h->n, hipMemcpyDeviceToHost,
+                           st));
+    HIP_TRY(hipEventRecord(p.poll, st));
+    p.poll_pending = true;
+    return SC_OK;
+}
+
+bool pipe_all_done(const sc_opt* h, const Pipe& p) {
+    for (int i : p.host_mats)
+        if (!p.flags_h[i].done) return false;
+    return true;
+}
+
+// End of a pipe's sweeps.  After the factor phase: V from the factor, A = M V,
+// the final Gram and its certificate (polled); otherwise the final Gram and the
+// finalization.
+int pipe_after_rounds(sc_opt* h, Pipe& p, hipStream_t st) {
+    int rc;
+    if (p.which == LIST_FACTOR) {
+        // Right singular vectors of A from the factor phase: V <- diag(1/|x_j|) X^T V_prev
+        // (rows), then the true operand A = M V.  A rejected matrix keeps V = V_prev and
+        // gets back its unchanged operand (it runs all its sweeps in the polishing phase).
+        PtrTable none = make_table(h, nullptr);
+        HIP_TRY(timed(h, PK_POLISH_GEMM, st, [&] {
+            return launch_factor_invnorm(h->md, h->flags_d, p.cap, p.ncap, p.max_k, st);
+        }));
+        if ((rc = run_group(h, p.factor_v, PK_POLISH_GEMM, none, st))) return rc;
+        if ((rc = run_group(h, p.polish_nt, PK_POLISH_GEMM, none, st))) return rc;
+        if ((rc = run_group(h, p.polish_nn, PK_POLISH_GEMM, none, st))) return rc;
+        HIP_TRY(timed(h, PK_INIT_FLAGS, st,
+                      [&] { return launch_phase2_reset(h->md, h->flags_d, p.cap, p.ncap, st); }));
+        // the Gram of every final operand in float64 sums: the Loewdin step's E and the
+        // certificate that A = M V is converged; only matrices failing it are polished
+        if ((rc = pipe_final_gram(h, p, st))) return rc;
+        HIP_TRY(timed(h, PK_INIT_FLAGS, st,
+                      [&] { return launch_certify(h->md, h->flags_d, p.cap, p.ncap, st); }));
+        p.stage = STAGE_CERT;
+        return pipe_poll(h, p, st);
+    }
+    if ((rc = pipe_final_gram(h, p, st))) return rc;
+    if ((rc = pipe_finalize(h, p, st))) return rc;
+    p.stage = STAGE_DONE;
+    return SC_OK;
+}
 
 int do_refresh(sc_opt* h, hipStream_t st) {
-    PtrTable none = make_table(h, nullptr);
     int rc;
     const bool warm = h->hp.warm_start && h->have_factors;
-    if (warm) {
-        // Start the sweeps from the previous factors: V = W_prev, A = M V_prev.
-        HIP_TRY(timed(h, PK_WARM, st, [&] { return launch_jacobi_warm(h->md, h->n, st); }));
-        if ((rc = run_group(h, h->warm_nt, PK_WARM, none, st))) return rc;
-        if ((rc = run_group(h, h->warm_nn, PK_WARM, none, st))) return rc;
-    } else {
-        HIP_TRY(timed(h, PK_LOAD, st, [&] {
-            return launch_jacobi_load(h->md, h->n, h->max_kpad, h->max_K + 128, st);
-        }));
+    // With kernel timing on, every pipe runs on the caller's stream so that each
+    // kernel's events bracket it alone (no overlap between pipes).
+    const bool split = !h->prof.on;
+    auto pst = [&](Pipe& p) { return split ? p.st : st; };
+    if (split) {
+        HIP_TRY(hipEventRecord(h->fork, st));
+        for (int q = 0; q < h->npipes; ++q) HIP_TRY(hipStreamWaitEvent(h->pipes[q].st, h->fork, 0));
     }
-    HIP_TRY(timed(h, PK_ROWNORM, st, [&] { return launch_rownorm(h->md, h->n, 0, h->max_kpad, st); }));
-    HIP_TRY(timed(h, PK_INIT_FLAGS, st,
-                  [&] { return launch_jacobi_init_flags(h->md, h->flags_d, h->n, st); }));
-    // The factor phase needs a well-conditioned Gram: from the previous factors the
-    // columns of A = M V_prev are close to orthogonal.  From a cold start (A = M)
-    // a graded spectrum would make most factorizations fail, so it is skipped.
-    const bool pre = h->ncap > 0 && h->hp.sync_check && warm;
-    if (pre) {
-        // Factor phase: Jacobi on X = L, A^T A = L L^T (k-long rows, no V).
-        HIP_TRY(timed(h, PK_CHOL_GEMM, st,
-                      [&] { return launch_chol_syrk(h->md, h->syrk_d, h->nsyrk, st); }));
-        if (h->prof.on)
-            for (int i = 0; i < h->n; ++i)
-                if (h->mh[i].klen) {
-                    const double kt = (h->mh[i].k + 127) / 128;
-                    h->prof.flops[PK_CHOL_GEMM] += kt * (kt + 1) / 2 * 2.0 * 128 * 128 * h->mh[i].K_ld;
+    for (int q = 0; q < h->npipes; ++q) {
+        Pipe& p = h->pipes[q];
+        // The factor phase needs a well-conditioned Gram: from the previous factors the
+        // columns of A = M V_prev are close to orthogonal.  From a cold start (A = M) a
+        // graded spectrum would make most factorizations fail, so it is skipped.
+        p.pre = p.ncap > 0 && h->hp.sync_check && warm;
+        if ((rc = pipe_pre(h, p, pst(p), warm))) return rc;
+        pipe_start_rounds(h, p, p.pre ? LIST_FACTOR : LIST_PLAIN, 4);
+    }
+    // Round-robin over the pipes: enqueue one round per pipe per turn, poll the
+    // convergence flags once per sweep of a pipe's largest matrix (after its
+    // first_check rounds) without blocking, and keep at most one sweep queued
+    // beyond a pending poll.  Rounds of converged matrices exit at once.
+    for (;;) {
+        bool queued = false, waiting = false, active = false;
+        for (int q = 0; q < h->npipes; ++q) {
+            Pipe& p = h->pipes[q];
+            if (p.stage == STAGE_DONE) continue;
+            active = true;
+            hipStream_t ps = pst(p);
+            if (p.poll_pending) {
+                const hipError_t e = hipEventQuery(p.poll);
+                if (e == hipErrorNotReady) {
+                    waiting = true;
+                } else if (e != hipSuccess) {
+                    return fail(SC_ERR_HIP, "hipEventQuery: %s", hipGetErrorString(e));
+                } else {
+                    p.poll_pending = false;
+                    const bool all = pipe_all_done(h, p);
+                    if (p.stage == STAGE_CERT) {
+                        if (all) {
+                            if ((rc = pipe_finalize(h, p, ps))) return rc;
+                            p.stage = STAGE_DONE;
+                        } else {
+                            pipe_start_rounds(h, p, LIST_POLISH, 1);
+                        }
+                        queued = true;
+                        continue;
+                    }
+                    if (all || p.r >= p.max_rounds) {
+                        if ((rc = pipe_after_rounds(h, p, ps))) return rc;
+                        queued = true;
+                        continue;
+                    }
                 }
-        HIP_TRY(timed(h, PK_CHOL, st, [&] {
-            return launch_cholesky(h->md, h->flags_d, h->cap_d, h->ncap, h->max_nbk, h->max_klen,
-                                   st);
-        }));
-        if (h->prof.on)
-            for (int i = 0; i < h->n; ++i)
-                if (h->mh[i].klen) h->prof.flops[PK_CHOL] += std::pow((double)h->mh[i].k, 3) / 3.0;
-    }
-    if ((rc = run_rounds(h, st, pre ? LIST_FACTOR : LIST_PLAIN, 4))) return rc;
-    if (pre) {
-        // Right singular vectors of A from the factor phase: V <- diag(1/|x_j|) X^T V_prev
-        // (rows), then the polishing phase on the true operand A = M V.  A rejected
-        // matrix keeps V = V_prev, gets back its unchanged operand and runs all its
-        // sweeps here.
-        HIP_TRY(timed(h, PK_POLISH_GEMM, st, [&] {
-            return launch_factor_invnorm(h->md, h->flags_d, h->cap_d, h->ncap, h->max_k, st);
-        }));
-        if ((rc = run_group(h, h->factor_v, PK_POLISH_GEMM, none, st))) return rc;
-        if ((rc = run_group(h, h->polish_nt, PK_POLISH_GEMM, none, st))) return rc;
-        if ((rc = run_group(h, h->polish_nn, PK_POLISH_GEMM, none, st))) return rc;
-        HIP_TRY(timed(h, PK_INIT_FLAGS, st,
-                      [&] { return launch_phase2_reset(h->md, h->flags_d, h->cap_d, h->ncap, st); }));
-    }
-    // Gram of every final operand in float64 sums: the Loewdin step's E, and for the
-    // preconditioned matrices the certificate that A = M V is already converged.
-    // Only matrices that fail it run polishing sweeps (and get a new Gram after them).
-    if ((rc = final_gram(h, st))) return rc;
-    if (pre) {
-        HIP_TRY(timed(h, PK_INIT_FLAGS, st,
-                      [&] { return launch_certify(h->md, h->flags_d, h->cap_d, h->ncap, st); }));
-        HIP_TRY(hipMemcpyAsync(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n,
-                               hipMemcpyDeviceToHost, st));
-        HIP_TRY(hipStreamSynchronize(st));
-        bool all = true;
-        for (int i = 0; i < h->n; ++i) all = all && h->flags_h[i].done;
-        if (!all) {
-            if ((rc = run_rounds(h, st, LIST_POLISH, 1))) return rc;
-            if ((rc = final_gram(h, st))) return rc;
+            }
+            if (p.stage != STAGE_ROUNDS) continue;
+            if (p.r < p.max_rounds && (!p.poll_pending || p.r < p.poll_round + p.rps)) {
+                if ((rc = pipe_round(h, p, ps))) return rc;
+                p.r += 1;
+                queued = true;
+                if (h->hp.sync_check && !p.poll_pending && p.r >= p.first_check &&
+                    p.r % p.rps == 0 && p.r < p.max_rounds) {
+                    if ((rc = pipe_poll(h, p, ps))) return rc;
+                    p.poll_round = p.r;
+                }
+            } else if (p.r >= p.max_rounds && !p.poll_pending) {
+                if ((rc = pipe_after_rounds(h, p, ps))) return rc;
+                queued = true;
+            }
+        }
+        if (!active) break;
+        if (!queued && waiting) {
+            // nothing to queue: block until the oldest pending poll completes
+            for (int q = 0; q < h->npipes; ++q)
+                if (h->pipes[q].poll_pending) {
+                    HIP_TRY(hipEventSynchronize(h->pipes[q].poll));
+                    break;
+                }
         }
     }
+    if (split)
+        for (int q = 0; q < h->npipes; ++q) {
+            HIP_TRY(hipEventRecord(h->pipes[q].join, h->pipes[q].st));
+            HIP_TRY(hipStreamWaitEvent(st, h->pipes[q].join, 0));
+        }
     if (h->prof.on) {
         HIP_TRY(hipMemcpyAsync(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n,
                                hipMemcpyDeviceToHost, st));
         HIP_TRY(hipStreamSynchronize(st));
         account_sweeps(h);
     }
-    rc = finalize_factors(h, st);
-    if (rc) return rc;
+    h->proj_stale = false;
     h->have_factors = true;
     h->refreshes += 1;
     for (auto& s : h->stale) s = 0;
@@ -600,10 +684,6 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         o[i].perm = take((size_t)m.kpad * sizeof(int));
         o[i].cnorm = take((size_t)m.kpad * sizeof(float));
         o[i].chol = take((size_t)m.k * m.k * sizeof(double));
-        h->max_nb = std::max(h->max_nb, m.nb);
-        h->max_kpad = std::max(h->max_kpad, m.kpad);
-        h->max_K = std::max(h->max_K, m.K_ld);
-        h->max_k = std::max(h->max_k, m.k);
     }
     void* arena = nullptr;
     if (hipMalloc(&arena, total) != hipSuccess) {
@@ -665,19 +745,28 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         for (int64_t off0 = 0; off0 < m.numel; off0 += kChunk)
             ch.push_back(Chunk{i, off0, (int)std::min<int64_t>(kChunk, m.numel - off0)});
     }
-    std::vector<int> order(n);
-    for (int i = 0; i < n; ++i) order[i] = i;
+    // Pipes: matrices are dealt by decreasing per-round work (pairs times the row
+    // length swept, operand plus V) to the less loaded pipe.  Dealing by kind
+    // instead (factor-phase matrices in one pipe, the others in the second) was
+    // measured slower: the two pipes then end far apart.
     auto work = [&](int i) {
         const MatDev& m = h->mh[i];
         return (double)m.kpad * ((m.klen ? m.klen : m.K_ld) + m.kpad);
     };
-    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return work(a) > work(b); });
     std::vector<int> gm[2];
-    double load[2] = {0.0, 0.0};
-    for (int i : order) {
-        const int g = load[0] <= load[1] ? 0 : 1;
-        gm[g].push_back(i);
-        load[g] += work(i);
+    {
+        std::vector<int> order(n);
+        for (int i = 0; i < n; ++i) order[i] = i;
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int x, int y) { return work(x) > work(y); });
+        double load[2] = {0.0, 0.0};
+        for (int i : order) {
+            const int g = load[0] <= load[1] ? 0 : 1;
+            gm[g].push_back(i);
+            load[g] += work(i);
+        }
+        std::sort(gm[0].begin(), gm[0].end());
+        std::sort(gm[1].begin(), gm[1].end());
     }
     auto upload = [&](auto& vec, auto** dst, int* cnt) -> int {
         *cnt = (int)vec.size();
@@ -691,23 +780,24 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
     };
     int rc;
     if ((rc = upload(ch, &h->chunks_d, &h->nchunks))) return rc;
-    for (int g = 0; g < 2; ++g) {
-        auto& G = h->jg[g];
-        std::sort(gm[g].begin(), gm[g].end());
+    h->npipes = gm[1].empty() ? 1 : 2;
+    for (int g = 0; g < h->npipes; ++g) {
+        Pipe& P = h->pipes[g];
+        P.host_mats = gm[g];
         for (int which = 0; which < 3; ++which) {
             std::vector<GramItem> gi;
             std::vector<SolveItem> si;
             std::vector<ApplyItem> ai;
             std::vector<int> mats;
-            auto& L = G.L[which];
+            auto& L = P.L[which];
             int pairs = 0;
             for (int i : gm[g])
-                if (which != 2 || h->mh[i].klen) pairs += h->mh[i].nb / 2;
+                if (which != LIST_POLISH || h->mh[i].klen) pairs += h->mh[i].nb / 2;
             const int nt = splits_for(pairs);
             for (int i : gm[g]) {
                 const MatDev& m = h->mh[i];
-                if (which == 2 && !m.klen) continue;  // polish: preconditioned matrices only
-                const int len = (which == 1 && m.klen) ? m.klen : m.K_ld;
+                if (which == LIST_POLISH && !m.klen) continue;  // preconditioned matrices only
+                const int len = (which == LIST_FACTOR && m.klen) ? m.klen : m.K_ld;
                 const int sl = split_len(len, nt), ns = split_count(len, nt);
                 mats.push_back(i);
                 L.max_nb = std::max(L.max_nb, m.nb);
@@ -717,7 +807,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
                     si.push_back(SolveItem{i, s, ns});
                     for (int c = 0; c < (len + kApplyCols - 1) / kApplyCols; ++c)
                         ai.push_back(ApplyItem{i, s, 0, c});
-                    if (which == 1 && m.klen) continue;  // the factor phase accumulates no V
+                    if (which == LIST_FACTOR && m.klen) continue;  // no V in the factor phase
                     for (int c = 0; c < (m.kpad + kApplyCols - 1) / kApplyCols; ++c)
                         ai.push_back(ApplyItem{i, s, 1, c});
                 }
@@ -727,53 +817,58 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             if ((rc = upload(ai, &L.ai, &L.nai))) return rc;
             if ((rc = upload(mats, &L.mats, &L.nmat))) return rc;
         }
-        if (G.L[0].nmat > 0) {
-            HIP_TRY(hipStreamCreateWithFlags(&G.st, hipStreamNonBlocking));
-            HIP_TRY(hipEventCreateWithFlags(&G.join, hipEventDisableTiming));
-        }
-    }
-    {
         std::vector<int> cap;
-        std::vector<SyrkItem> sy;
-        for (int i = 0; i < n; ++i)
-            if (h->mh[i].klen) {
+        std::vector<SyrkItem> sy, sa;
+        for (int i : gm[g]) {
+            const MatDev& m = h->mh[i];
+            P.max_kpad = std::max(P.max_kpad, m.kpad);
+            P.max_K = std::max(P.max_K, m.K_ld);
+            P.max_k = std::max(P.max_k, m.k);
+            P.max_t64 = std::max(P.max_t64, (m.k + 63) / 64);
+            const int kt = (m.k + 127) / 128;
+            for (int ti = 0; ti < kt; ++ti)
+                for (int tj = 0; tj <= ti; ++tj) sa.push_back(SyrkItem{i, ti, tj});
+            if (m.klen) {
                 cap.push_back(i);
-                h->max_nbk = std::max(h->max_nbk, (h->mh[i].k + 63) / 64);
-                h->max_klen = std::max(h->max_klen, h->mh[i].klen);
-                const int kt = (h->mh[i].k + 127) / 128;
+                P.max_nbk = std::max(P.max_nbk, (m.k + 63) / 64);
+                P.max_klen = std::max(P.max_klen, m.klen);
                 for (int ti = 0; ti < kt; ++ti)
                     for (int tj = 0; tj <= ti; ++tj) sy.push_back(SyrkItem{i, ti, tj});
             }
-        if ((rc = upload(cap, &h->cap_d, &h->ncap))) return rc;
-        if ((rc = upload(sy, &h->syrk_d, &h->nsyrk))) return rc;
-        std::vector<int> all;
-        std::vector<SyrkItem> sa;
-        for (int i = 0; i < n; ++i) {
-            all.push_back(i);
-            h->max_t64 = std::max(h->max_t64, (h->mh[i].k + 63) / 64);
-            const int kt = (h->mh[i].k + 127) / 128;
-            for (int ti = 0; ti < kt; ++ti)
-                for (int tj = 0; tj <= ti; ++tj) sa.push_back(SyrkItem{i, ti, tj});
         }
-        int nall = 0;
-        if ((rc = upload(all, &h->all_d, &nall))) return rc;
-        if ((rc = upload(sa, &h->syrk_all_d, &h->nsyrk_all))) return rc;
+        if ((rc = upload(gm[g], &P.mats, &P.nmat))) return rc;
+        if ((rc = upload(cap, &P.cap, &P.ncap))) return rc;
+        if ((rc = upload(sy, &P.syrk_cap, &P.nsyrk_cap))) return rc;
+        if ((rc = upload(sa, &P.syrk_all, &P.nsyrk_all))) return rc;
+        HIP_TRY(hipStreamCreateWithFlags(&P.st, hipStreamNonBlocking));
+        HIP_TRY(hipEventCreateWithFlags(&P.join, hipEventDisableTiming));
+        HIP_TRY(hipEventCreateWithFlags(&P.poll, hipEventDisableTiming));
+        void* q = nullptr;
+        HIP_TRY(hipHostMalloc(&q, sizeof(MatFlags) * n, hipHostMallocDefault));
+        P.flags_h = (MatFlags*)q;
+        memset(P.flags_h, 0, sizeof(MatFlags) * n);
     }
     HIP_TRY(hipEventCreateWithFlags(&h->fork, hipEventDisableTiming));
+    std::vector<int> pipe_of(n, 0);
+    for (int g = 0; g < h->npipes; ++g)
+        for (int i : gm[g]) pipe_of[i] = g;
 
     // GEMM problem tables
     const bool gbf = h->gdt == SC_BF16;
-    h->lowdin_eW.tb = true;
-    h->proj.ta = true;
+    for (int g = 0; g < h->npipes; ++g) {
+        h->pipes[g].lowdin_eW.tb = true;
+        h->pipes[g].proj.ta = true;
+        h->pipes[g].warm_nt.tb = true;
+        h->pipes[g].polish_nt.tb = true;
+    }
     h->s1_nn_a.abf = gbf;  // square: A = G
     h->s1_nn_b.bbf = gbf;  // tall: B = G
     h->s1_nt.tb = true;    // wide: A = G, B = F^T
     h->s1_nt.abf = gbf;
     h->s3_tn.ta = true;
-    h->warm_nt.tb = true;
-    h->polish_nt.tb = true;
     for (int i = 0; i < n; ++i) {
         MatDev& m = h->mh[i];
+        Pipe& P = h->pipes[pipe_of[i]];
         // Loewdin re-orthogonalization of the unit rows of A (-> F) and V (-> W):
         //   E = X X^T with zero diagonal;  X_out = X - 0.5 E X
         // (E of the A side is formed by final_gram before the rows are normalized)
@@ -782,23 +877,23 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         p.ldcin = m.K_ld;
         p.alpha = -0.5f;
         p.beta = 1.0f;
-        h->lowdin_F.h.push_back(p);
+        P.lowdin_F.h.push_back(p);
         p = make_prob(m.V, m.kpad, m.V, m.kpad, m.E, m.k, m.k, m.k, m.k);
         p.flags = GF_ZERO_DIAG;
-        h->lowdin_eW.h.push_back(p);
+        P.lowdin_eW.h.push_back(p);
         p = make_prob(m.E, m.k, m.V, m.kpad, m.W, m.k, m.k, m.k, m.k);
         p.Cin = m.V;
         p.ldcin = m.kpad;
         p.alpha = -0.5f;
         p.beta = 1.0f;
-        h->lowdin_W.h.push_back(p);
+        P.lowdin_W.h.push_back(p);
         // warm start: rows of A = W op(M): m >= n: a_j = M w_j; m < n: a_j = M^T w_j
         if (m.tall) {
             p = make_prob(m.W, m.k, m.Manc, m.n, m.A, m.K_ld, m.k, m.m, m.n);
-            h->warm_nt.h.push_back(p);
+            P.warm_nt.h.push_back(p);
         } else {
             p = make_prob(m.W, m.k, m.Manc, m.n, m.A, m.K_ld, m.k, m.n, m.m);
-            h->warm_nn.h.push_back(p);
+            P.warm_nn.h.push_back(p);
         }
         if (m.klen) {
             // after the factor phase: V rows = scaled rows of X^T times W (= V_prev),
@@ -806,13 +901,13 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             p = make_prob(m.A, m.K_ld, m.W, m.k, m.V, m.kpad, m.k, m.k, m.k);
             p.row_scale = m.Y;
             p.gate = &h->flags_d[i].precond;
-            h->factor_v.h.push_back(p);
+            P.factor_v.h.push_back(p);
             if (m.tall) {
                 p = make_prob(m.V, m.kpad, m.Manc, m.n, m.A, m.K_ld, m.k, m.m, m.n);
-                h->polish_nt.h.push_back(p);
+                P.polish_nt.h.push_back(p);
             } else {
                 p = make_prob(m.V, m.kpad, m.Manc, m.n, m.A, m.K_ld, m.k, m.n, m.m);
-                h->polish_nn.h.push_back(p);
+                P.polish_nn.h.push_back(p);
             }
         }
         // projectors X^T diag(d) X
@@ -820,11 +915,11 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         if (square) {
             p = make_prob(m.F, m.K_ld, m.F, m.K_ld, m.PL, m.m, m.m, m.m, m.k);
             p.k_scale = m.d;
-            h->proj.h.push_back(p);
+            P.proj.h.push_back(p);
         }
         p = make_prob(m.W, m.k, m.W, m.k, m.tall ? m.PR : m.PL, m.k, m.k, m.k, m.k);
         p.k_scale = m.d;
-        h->proj.h.push_back(p);
+        P.proj.h.push_back(p);
         // step chain
         if (square) {
             p = make_prob(nullptr, m.n, m.PR, m.n, m.T, m.n, m.m, m.n, m.n);  // T = G P_R
@@ -852,13 +947,15 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             h->s3_nn.h.push_back(p);
         }
     }
-    for (GemmGroup* g : {&h->warm_nt, &h->warm_nn, &h->factor_v, &h->polish_nt, &h->polish_nn,
-                         &h->lowdin_F, &h->lowdin_eW,
-                         &h->lowdin_W, &h->proj,
-                         &h->s1_nn_a, &h->s1_nn_b, &h->s1_nt, &h->s2_nn, &h->s3_tn, &h->s3_nn})
+    for (int g = 0; g < h->npipes; ++g) {
+        Pipe& P = h->pipes[g];
+        for (GemmGroup* gg : {&P.warm_nt, &P.warm_nn, &P.factor_v, &P.polish_nt, &P.polish_nn,
+                              &P.lowdin_F, &P.lowdin_eW, &P.lowdin_W, &P.proj})
+            if ((rc = upload_group(h, *gg))) return rc;
+    }
+    for (GemmGroup* g : {&h->s1_nn_a, &h->s1_nn_b, &h->s1_nt, &h->s2_nn, &h->s3_tn, &h->s3_nn})
         if ((rc = upload_group(h, *g))) return rc;
     h->stale.assign(n, 0);
-    h->last_sweeps.assign(n, 0);
     const double gsz = h->gdt == SC_BF16 ? 2.0 : 4.0, wsz = h->wdt == SC_BF16 ? 2.0 : 4.0;
     for (int i = 0; i < n; ++i) h->total_numel += (double)h->mh[i].numel;
     h->ema_bytes = h->total_numel * (8.0 + gsz);
@@ -876,9 +973,11 @@ void release(sc_opt* h) {
         (void)hipEventDestroy(r.b);
     }
     for (hipEvent_t e : h->prof.pool) (void)hipEventDestroy(e);
-    for (auto& G : h->jg) {
-        if (G.st) (void)hipStreamDestroy(G.st);
-        if (G.join) (void)hipEventDestroy(G.join);
+    for (auto& P : h->pipes) {
+        if (P.st) (void)hipStreamDestroy(P.st);
+        if (P.join) (void)hipEventDestroy(P.join);
+        if (P.poll) (void)hipEventDestroy(P.poll);
+        if (P.flags_h) (void)hipHostFree(P.flags_h);
     }
     if (h->fork) (void)hipEventDestroy(h->fork);
     for (void* p : h->dev_allocs) (void)hipFree(p);

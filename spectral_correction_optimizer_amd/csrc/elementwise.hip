@@ -14,6 +14,9 @@ namespace scopt {
 
 constexpr int kEwThreads = 256;
 
+// Matrix of a per-matrix workgroup: entry b of the index list, or b itself.
+__device__ __forceinline__ int mat_of(const int* mat_idx, int b) { return mat_idx ? mat_idx[b] : b; }
+
 // ---------------------------------------------------------------------------------
 // Anchor EMA:  M <- beta * M + (1 - beta) * G_anc
 // One workgroup per chunk; 4 consecutive elements per thread and iteration,
@@ -214,9 +217,10 @@ hipError_t launch_combine_adamw(const MatDev* mats, const Chunk* chunks, int nch
 //   m >= n:  A = M,   A_rows[j][x] = M[x][j]   (transpose, 32x32 LDS tiles)
 //   m <  n:  A = M^T, A_rows[j][x] = M[j][x]   (copy)
 // zero beyond k rows / K columns; V <- identity (kpad x kpad).
-__global__ __launch_bounds__(256) void jacobi_load_kernel(const MatDev* __restrict__ mats) {
+__global__ __launch_bounds__(256) void jacobi_load_kernel(const MatDev* __restrict__ mats,
+                                                          const int* __restrict__ mat_idx) {
     __shared__ float tile[32][33];
-    const MatDev& md = mats[blockIdx.y];
+    const MatDev& md = mats[mat_of(mat_idx, blockIdx.y)];
     const int tj = md.kpad / 32, tx = md.K_ld / 32;
     const int ntA = tj * tx;
     const int ntV = (md.kpad / 32) * (md.kpad / 32);
@@ -254,20 +258,21 @@ __global__ __launch_bounds__(256) void jacobi_load_kernel(const MatDev* __restri
     }
 }
 
-hipError_t launch_jacobi_load(const MatDev* mats, int nmat, int max_kpad, int max_K,
-                              hipStream_t st) {
+hipError_t launch_jacobi_load(const MatDev* mats, const int* mat_idx, int nmat, int max_kpad,
+                              int max_K, hipStream_t st) {
     int tiles = (max_kpad / 32) * ((max_K + 31) / 32) + (max_kpad / 32) * (max_kpad / 32);
     int gx = tiles < 2048 ? tiles : 2048;
     if (gx < 1) gx = 1;
-    hipLaunchKernelGGL(jacobi_load_kernel, dim3(gx, nmat), dim3(256), 0, st, mats);
+    hipLaunchKernelGGL(jacobi_load_kernel, dim3(gx, nmat), dim3(256), 0, st, mats, mat_idx);
     return hipGetLastError();
 }
 
 // Warm start of a refresh from the previous factors: V <- [W 0; 0 I] (rows of
 // the previous accumulated-side singular vectors) and zero padding rows of A
 // (the rows j < k of A are then written by the GEMM A_rows = W op(M)).
-__global__ __launch_bounds__(256) void jacobi_warm_kernel(const MatDev* __restrict__ mats) {
-    const MatDev& md = mats[blockIdx.y];
+__global__ __launch_bounds__(256) void jacobi_warm_kernel(const MatDev* __restrict__ mats,
+                                                          const int* __restrict__ mat_idx) {
+    const MatDev& md = mats[mat_of(mat_idx, blockIdx.y)];
     const int64_t nv = (int64_t)md.kpad * md.kpad;
     const int64_t na = (int64_t)(md.kpad - md.k) * md.K_ld;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nv + na;
@@ -281,17 +286,18 @@ __global__ __launch_bounds__(256) void jacobi_warm_kernel(const MatDev* __restri
     }
 }
 
-hipError_t launch_jacobi_warm(const MatDev* mats, int nmat, hipStream_t st) {
-    hipLaunchKernelGGL(jacobi_warm_kernel, dim3(512, nmat), dim3(256), 0, st, mats);
+hipError_t launch_jacobi_warm(const MatDev* mats, const int* mat_idx, int nmat, hipStream_t st) {
+    hipLaunchKernelGGL(jacobi_warm_kernel, dim3(512, nmat), dim3(256), 0, st, mats, mat_idx);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------
 // Row norms in float64 with a fixed reduction order (deterministic).
 // which = 0: rows j < kpad of A (length K_ld); 1: rows j < k of V (length k).
-__global__ __launch_bounds__(256) void rownorm_kernel(const MatDev* __restrict__ mats, int which) {
+__global__ __launch_bounds__(256) void rownorm_kernel(const MatDev* __restrict__ mats,
+                                                      const int* __restrict__ mat_idx, int which) {
     __shared__ double red[4];
-    const MatDev& md = mats[blockIdx.y];
+    const MatDev& md = mats[mat_of(mat_idx, blockIdx.y)];
     const int j = blockIdx.x;
     const int rows = which == 0 ? md.kpad : md.k;
     if (j >= rows) return;
@@ -306,22 +312,25 @@ __global__ __launch_bounds__(256) void rownorm_kernel(const MatDev* __restrict__
     if (threadIdx.x == 0) md.norm2[j] = acc;
 }
 
-hipError_t launch_rownorm(const MatDev* mats, int nmat, int which, int max_kpad, hipStream_t st) {
-    hipLaunchKernelGGL(rownorm_kernel, dim3(max_kpad, nmat), dim3(256), 0, st, mats, which);
+hipError_t launch_rownorm(const MatDev* mats, const int* mat_idx, int nmat, int which, int max_kpad,
+                          hipStream_t st) {
+    hipLaunchKernelGGL(rownorm_kernel, dim3(max_kpad, nmat), dim3(256), 0, st, mats, mat_idx, which);
     return hipGetLastError();
 }
 
 // floor2 = (2^-24 ||M||_F)^2: a column of A whose squared norm stays below it
 // is indistinguishable from float32 rounding noise of M and is treated as zero.
 __global__ __launch_bounds__(256) void init_flags_kernel(const MatDev* __restrict__ mats,
+                                                         const int* __restrict__ mat_idx,
                                                          MatFlags* __restrict__ flags) {
     __shared__ double red[4];
-    const MatDev& md = mats[blockIdx.x];
+    const int mi = mat_of(mat_idx, blockIdx.x);
+    const MatDev& md = mats[mi];
     double acc = 0.0;
     for (int j = threadIdx.x; j < md.kpad; j += blockDim.x) acc += md.norm2[j];
     acc = block_sum_f64(acc, red);
     if (threadIdx.x == 0) {
-        MatFlags& f = flags[blockIdx.x];
+        MatFlags& f = flags[mi];
         const double e = 5.9604644775390625e-08;  // 2^-24
         f.floor2 = (float)(acc * e * e);
         f.sweep_max = 0u;
@@ -344,9 +353,9 @@ __global__ __launch_bounds__(256) void init_flags_kernel(const MatDev* __restric
     }
 }
 
-hipError_t launch_jacobi_init_flags(const MatDev* mats, MatFlags* flags, int nmat,
-                                    hipStream_t st) {
-    hipLaunchKernelGGL(init_flags_kernel, dim3(nmat), dim3(256), 0, st, mats, flags);
+hipError_t launch_jacobi_init_flags(const MatDev* mats, const int* mat_idx, MatFlags* flags,
+                                    int nmat, hipStream_t st) {
+    hipLaunchKernelGGL(init_flags_kernel, dim3(nmat), dim3(256), 0, st, mats, mat_idx, flags);
     return hipGetLastError();
 }
 
@@ -354,14 +363,16 @@ hipError_t launch_jacobi_init_flags(const MatDev* mats, MatFlags* flags, int nma
 // the floor (and padding rows) become zero with s_j = 0.
 // which = 1: rows j < k of V -> unit rows in place (first k entries).
 __global__ __launch_bounds__(256) void normalize_kernel(const MatDev* __restrict__ mats,
+                                                        const int* __restrict__ mat_idx,
                                                         const MatFlags* __restrict__ flags,
                                                         int which) {
-    const MatDev& md = mats[blockIdx.y];
+    const int mi = mat_of(mat_idx, blockIdx.y);
+    const MatDev& md = mats[mi];
     const int j = blockIdx.x;
     if (which == 0) {
         if (j >= md.kpad) return;
         const double n2 = md.norm2[j];
-        const bool keep = j < md.k && n2 > (double)flags[blockIdx.y].floor2;
+        const bool keep = j < md.k && n2 > (double)flags[mi].floor2;
         const float sv = keep ? (float)sqrt(n2) : 0.0f;
         float* x = md.A + (int64_t)j * md.K_ld;
         for (int i = threadIdx.x; i < md.K_ld; i += blockDim.x) x[i] = keep ? x[i] / sv : 0.0f;
@@ -378,17 +389,17 @@ __global__ __launch_bounds__(256) void normalize_kernel(const MatDev* __restrict
     }
 }
 
-hipError_t launch_normalize(const MatDev* mats, const MatFlags* flags, int nmat, int which,
-                            int max_kpad, int max_K, hipStream_t st) {
-    (void)max_K;
-    hipLaunchKernelGGL(normalize_kernel, dim3(max_kpad, nmat), dim3(256), 0, st, mats, flags,
-                       which);
+hipError_t launch_normalize(const MatDev* mats, const int* mat_idx, const MatFlags* flags,
+                            int nmat, int which, int max_kpad, hipStream_t st) {
+    hipLaunchKernelGGL(normalize_kernel, dim3(max_kpad, nmat), dim3(256), 0, st, mats, mat_idx,
+                       flags, which);
     return hipGetLastError();
 }
 
 // d_j = s_j / (s_j + tau), and 0 where s_j + tau = 0.
-__global__ __launch_bounds__(256) void filter_kernel(const MatDev* __restrict__ mats, float tau) {
-    const MatDev& md = mats[blockIdx.x];
+__global__ __launch_bounds__(256) void filter_kernel(const MatDev* __restrict__ mats,
+                                                     const int* __restrict__ mat_idx, float tau) {
+    const MatDev& md = mats[mat_of(mat_idx, blockIdx.x)];
     for (int j = threadIdx.x; j < md.kpad; j += blockDim.x) {
         float s = md.s[j];
         float den = s + tau;
@@ -396,9 +407,9 @@ __global__ __launch_bounds__(256) void filter_kernel(const MatDev* __restrict__ 
     }
 }
 
-hipError_t launch_filter(const MatDev* mats, int nmat, float tau, int max_kpad, hipStream_t st) {
-    (void)max_kpad;
-    hipLaunchKernelGGL(filter_kernel, dim3(nmat), dim3(256), 0, st, mats, tau);
+hipError_t launch_filter(const MatDev* mats, const int* mat_idx, int nmat, float tau,
+                         hipStream_t st) {
+    hipLaunchKernelGGL(filter_kernel, dim3(nmat), dim3(256), 0, st, mats, mat_idx, tau);
     return hipGetLastError();
 }
 

@@ -120,19 +120,24 @@ hipError_t launch_combine_adamw(const MatDev* mats, const Chunk* chunks, int nch
                                 float alpha, float beta1, float beta2, float eps,
                                 float step_size, float inv_sqrt_bc2, float lr_wd, int keep_proj,
                                 int* nonfinite, hipStream_t st);
-// A <- M (copy or transpose), V <- I, for matrices in mat_list.
-hipError_t launch_jacobi_load(const MatDev* mats, int nmat, int max_kpad, int max_K,
-                              hipStream_t st);
+// The per-matrix passes below run over nmat matrices: mat_idx[0 .. nmat) (device
+// list) or, with mat_idx == nullptr, matrices 0 .. nmat - 1.
+// A <- M (copy or transpose), V <- I.
+hipError_t launch_jacobi_load(const MatDev* mats, const int* mat_idx, int nmat, int max_kpad,
+                              int max_K, hipStream_t st);
 // Warm start: V <- previous W (padded with identity), zero padding rows of A.
-hipError_t launch_jacobi_warm(const MatDev* mats, int nmat, hipStream_t st);
+hipError_t launch_jacobi_warm(const MatDev* mats, const int* mat_idx, int nmat, hipStream_t st);
 // norm2[j] = sum_x X[j][x]^2 (fp64) for the rows of A (which=0) or V (which=1)
-hipError_t launch_rownorm(const MatDev* mats, int nmat, int which, int max_kpad, hipStream_t st);
+hipError_t launch_rownorm(const MatDev* mats, const int* mat_idx, int nmat, int which, int max_kpad,
+                          hipStream_t st);
 // floor2 = (2^-24)^2 * sum_j norm2[j]; clears sweep flags
-hipError_t launch_jacobi_init_flags(const MatDev* mats, MatFlags* flags, int nmat, hipStream_t st);
-// Normalize rows of A (which=0, into F) or V (which=1, into W scratch in place).
-hipError_t launch_normalize(const MatDev* mats, const MatFlags* flags, int nmat, int which,
-                            int max_kpad, int max_K, hipStream_t st);
-hipError_t launch_filter(const MatDev* mats, int nmat, float tau, int max_kpad, hipStream_t st);
+hipError_t launch_jacobi_init_flags(const MatDev* mats, const int* mat_idx, MatFlags* flags,
+                                    int nmat, hipStream_t st);
+// Normalize rows of A (which=0, in place, s) or V (which=1, in place).
+hipError_t launch_normalize(const MatDev* mats, const int* mat_idx, const MatFlags* flags,
+                            int nmat, int which, int max_kpad, hipStream_t st);
+hipError_t launch_filter(const MatDev* mats, const int* mat_idx, int nmat, float tau,
+                         hipStream_t st);
 
 // ---- Jacobi sweeps -------------------------------------------------------------------
 
