@@ -100,6 +100,8 @@ int round_up(int x, int a) { return (x + a - 1) / a * a; }
 // K-splits of a pair Gram over rows of length len (a multiple of 128): about nt
 // splits (nt <= 8) of a multiple of 256 columns each, so that the fp64 folds of
 // the Gram kernel see whole 256-column chunks.
+// Pipelines of the refresh (one internal stream each).
+constexpr int kPipes = 2;
 constexpr int kMaxSplits = 8;
 int split_len(int len, int nt) { return std::max(256, round_up((len + nt - 1) / nt, 256)); }
 int split_count(int len, int nt) { return (len + split_len(len, nt) - 1) / split_len(len, nt); }
@@ -168,7 +170,7 @@ struct sc_opt {
         // progress of the refresh in flight
         int stage = 0, which = 0, r = 0, rps = 1, max_rounds = 0, first_check = 0, poll_round = 0;
         bool pre = false, poll_pending = false;
-    } pipes[2];
+    } pipes[kPipes];
     int npipes = 0;
     hipEvent_t fork = nullptr;
     bool have_factors = false;   // W holds orthonormal rows from a refresh / sc_set_factors
@@ -753,20 +755,21 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         const MatDev& m = h->mh[i];
         return (double)m.kpad * ((m.klen ? m.klen : m.K_ld) + m.kpad);
     };
-    std::vector<int> gm[2];
+    std::vector<int> gm[kPipes];
     {
         std::vector<int> order(n);
         for (int i = 0; i < n; ++i) order[i] = i;
         std::stable_sort(order.begin(), order.end(),
                          [&](int x, int y) { return work(x) > work(y); });
-        double load[2] = {0.0, 0.0};
+        double load[kPipes] = {};
         for (int i : order) {
-            const int g = load[0] <= load[1] ? 0 : 1;
+            int g = 0;
+            for (int q = 1; q < kPipes; ++q)
+                if (load[q] < load[g]) g = q;
             gm[g].push_back(i);
             load[g] += work(i);
         }
-        std::sort(gm[0].begin(), gm[0].end());
-        std::sort(gm[1].begin(), gm[1].end());
+        for (auto& v : gm) std::sort(v.begin(), v.end());
     }
     auto upload = [&](auto& vec, auto** dst, int* cnt) -> int {
         *cnt = (int)vec.size();
@@ -780,7 +783,8 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
     };
     int rc;
     if ((rc = upload(ch, &h->chunks_d, &h->nchunks))) return rc;
-    h->npipes = gm[1].empty() ? 1 : 2;
+    h->npipes = 0;
+    while (h->npipes < kPipes && !gm[h->npipes].empty()) ++h->npipes;
     for (int g = 0; g < h->npipes; ++g) {
         Pipe& P = h->pipes[g];
         P.host_mats = gm[g];

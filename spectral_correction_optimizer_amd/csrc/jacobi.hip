@@ -209,10 +209,13 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
 }
 
 // ---------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict__ mats,
-                                                        MatFlags* __restrict__ flags,
-                                                        const SolveItem* __restrict__ items,
-                                                        int round) {
+__global__ __launch_bounds__(64) void jac_solve_kernel(const MatDev* __restrict__ mats,
+                                                       MatFlags* __restrict__ flags,
+                                                       const SolveItem* __restrict__ items,
+                                                       int round) {
+    // One wavefront per pair: LDS accesses of a wavefront are carried out in
+    // issue order, so the steps of the inner sweep need no barriers, only
+    // compiler fences that keep the accesses in program order.
     // G: float32 working copy of the pair Gram, scaled by 1 / max diagonal so
     // that the solve does not depend on the matrix's magnitude.
     // R: the accumulated rotation minus the identity, Q = I + R, kept directly
@@ -221,149 +224,156 @@ __global__ __launch_bounds__(256) void jac_solve_kernel(const MatDev* __restrict
     // Q itself in float32 would round c to 1 while s != 0, a biased growth of
     // the column norms over thousands of rotations).  c = 1 / h and s = t c
     // satisfy c^2 + s^2 = 1 to float32 rounding, so float32 parameters suffice.
-    __shared__ float G[2][PW][PW + 1];
+    __shared__ float G[PW][PW + 1];
     __shared__ float R[PW][PW + 1];
-    __shared__ double dg[PW];
-    __shared__ float red[4];
-    __shared__ double redd[4];
+    __shared__ float4 cs[PW / 2];  // per pair of the step: c, s, c - 1, p | q << 8
+    __shared__ double rs[PW];      // 1 / sqrt(g_aa) above the zero floor, else 0
 
     const SolveItem it = items[blockIdx.x];
     MatFlags& fl = flags[it.mat];
     if (fl.done) return;
     const MatDev& md = mats[it.mat];
     const float tol = md.tol;
-    const int tid = threadIdx.x;
+    const int l = threadIdx.x;
     int bI, bJ;
     rr_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
 
-    // 1. sum split partials (fixed order) into fp64; the partials hold the upper
-    //    16x16 tiles only, an entry of a lower tile is read at its mirror position
+    // 1. diagonal of the pair Gram: split partials summed in fixed order (fp64)
     const double* gp = md.gram + (int64_t)it.slot * md.nsplit * (PW * PW);
-    double gv[16];
-    double dmax = 0.0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int idx = tid + 256 * e;
-        const int row = idx >> 6, col = idx & 63;
-        const int src = (row >> 4) <= (col >> 4) ? idx : col * PW + row;
-        double s = 0.0;
-        for (int sp = 0; sp < it.nsplit; ++sp) s += gld(gp + (int64_t)sp * PW * PW + src);
-        gv[e] = s;
-        R[idx >> 6][idx & 63] = 0.0f;
-        if ((idx >> 6) == (idx & 63)) {
-            dg[idx & 63] = s;
-            dmax = fmax(dmax, s);
-        }
-    }
+    double dl = 0.0;
+    for (int sp = 0; sp < it.nsplit; ++sp) dl += gld(gp + (int64_t)sp * PW * PW + l * (PW + 1));
+    double dmax = dl;
     for (int o = 32; o > 0; o >>= 1) dmax = fmax(dmax, __shfl_xor(dmax, o));
-    if ((tid & 63) == 0) redd[tid >> 6] = dmax;
-    __syncthreads();
-    dmax = fmax(fmax(redd[0], redd[1]), fmax(redd[2], redd[3]));
     const double scale = dmax > 0.0 ? 1.0 / dmax : 1.0;
     const double floor2d = (double)fl.floor2;
     const float floor2 = (float)(floor2d * scale);
+    const double rsl = dl > floor2d ? 1.0 / sqrt(dl) : 0.0;
+    rs[l] = rsl;
+    __syncthreads();
 
-    // 2. largest relative off-diagonal over columns above the zero floor
+    // 2. the stored upper 16x16 tiles (10 of 16), each read once and mirrored in
+    //    LDS; the largest relative off-diagonal |g_ab| / sqrt(g_aa g_bb) over
+    //    columns above the zero floor (rs = 0 below it)
     float mo = 0.0f;
+#pragma unroll 1
+    for (int t = 0; t < 10; ++t) {
+        const int ti = t < 4 ? 0 : t < 7 ? 1 : t < 9 ? 2 : 3;
+        const int tj = ti + t - (ti == 0 ? 0 : ti == 1 ? 4 : ti == 2 ? 7 : 9);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const int idx = tid + 256 * e;
-        const int a = idx >> 6, b = idx & 63;
-        G[0][a][b] = (float)(gv[e] * scale);
-        if (a < b) {
-            const double da = dg[a], db = dg[b];
-            if (da > floor2d && db > floor2d) {
-                float o = (float)(fabs(gv[e]) / sqrt(da * db));
-                mo = fmaxf(mo, o);
-            }
+        for (int k = 0; k < 4; ++k) {
+            const int a = 16 * ti + (l >> 4) + 4 * k, b = 16 * tj + (l & 15);
+            double s = 0.0;
+            for (int sp = 0; sp < it.nsplit; ++sp) s += gld(gp + (int64_t)sp * PW * PW + a * PW + b);
+            const float g = (float)(s * scale);
+            G[a][b] = g;
+            if (ti != tj) G[b][a] = g;  // a diagonal tile is stored whole
+            if (a < b) mo = fmaxf(mo, (float)(fabs(s) * rs[a] * rs[b]));
         }
     }
+#pragma unroll 8
+    for (int e = 0; e < PW; ++e) R[e][l] = 0.0f;
     for (int o = 32; o > 0; o >>= 1) mo = fmaxf(mo, __shfl_xor(mo, o));
-    if ((tid & 63) == 0) red[tid >> 6] = mo;
-    __syncthreads();
-    mo = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    if (tid == 0) atomicMax(&fl.sweep_max, __float_as_uint(mo));
+    if (l == 0) atomicMax(&fl.sweep_max, __float_as_uint(mo));
     int* rflag = md.rot_flag + it.slot;
     if (!(mo > tol)) {
         // columns unchanged: their norms for the next sweep's ordering
-        if (tid < PW) gst(md.cnorm + pair_row(md, bI, bJ, tid), (float)dg[tid]);
-        if (tid == 0) *rflag = 0;
+        gst(md.cnorm + pair_row(md, bI, bJ, l), (float)dl);
+        if (l == 0) *rflag = 0;
         return;
     }
+    __syncthreads();
 
     // 3. one cyclic sweep of 2x2 rotations on G (G <- J^T G J), accumulating R.
-    //    Lane l works on pair j = l % 32 of the step: every lane computes that
-    //    pair's rotation itself (8 identical copies per workgroup), and takes the
-    //    rotation of pair i from lane i by a shuffle, so a step needs a single
-    //    barrier.  G is double-buffered (a step reads one copy and writes the
-    //    other); R's columns p_j, q_j belong to lane group j alone within a step.
-    const int j = tid & 31, r8 = tid >> 5;  // pair, and 8 row groups
+    //    Lane l: pair j = l % 32 of the step, half h = l / 32.  Both halves
+    //    compute pair j's rotation from G; the lower half publishes it in cs.
+    //    G: lane l updates the 2x2 blocks (i, j), i = 16 h + m, rows p_i, q_i x
+    //    columns p_j, q_j -- every entry of G belongs to one lane per step.
+    //    R: columns p_j, q_j of rows a = h + 2 m.  A lane issues all its reads
+    //    of a step before its first write, so the LDS latency is paid once.
+    const int j = l & 31, h = l >> 5;
+#pragma unroll 1
     for (int ir = 0; ir < PW - 1; ++ir) {
-        const float (*Gc)[PW + 1] = G[ir & 1];
-        float (*Gn)[PW + 1] = G[(ir & 1) ^ 1];
         int pj, qj;
         rr_pair(PW, ir, j, &pj, &qj);
         float c = 1.0f, sn = 0.0f, cm1 = 0.0f;
         {
-            const float gpp = Gc[pj][pj], gqq = Gc[qj][qj], gpq = Gc[pj][qj];
+            const float gpp = G[pj][pj], gqq = G[qj][qj], gpq = G[pj][qj];
             if (gpp > floor2 && gqq > floor2 &&
-                fabsf(gpq) > tol * (__builtin_sqrtf(gpp) * __builtin_sqrtf(gqq))) {
+                fabsf(gpq) > tol * __builtin_amdgcn_sqrtf(gpp * gqq)) {
                 const float zeta = (gqq - gpp) * 0.5f * __builtin_amdgcn_rcpf(gpq);
                 const float az = fabsf(zeta);
                 // t = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)), without overflow
-                const float den = az < 1e18f ? az + __builtin_sqrtf(fmaf(az, az, 1.0f)) : 2.0f * az;
+                const float den =
+                    az < 1e18f ? az + __builtin_amdgcn_sqrtf(fmaf(az, az, 1.0f)) : 2.0f * az;
                 const float t = copysignf(__builtin_amdgcn_rcpf(den), zeta);
-                const float h = __builtin_sqrtf(fmaf(t, t, 1.0f));
-                c = __builtin_amdgcn_rcpf(h);
+                const float hh = __builtin_amdgcn_sqrtf(fmaf(t, t, 1.0f));
+                c = __builtin_amdgcn_rcpf(hh);
                 sn = t * c;
-                cm1 = -t * sn * __builtin_amdgcn_rcpf(1.0f + h);
+                cm1 = -t * sn * __builtin_amdgcn_rcpf(1.0f + hh);
             }
         }
-        // G: blocks (i, j) for i = r8 + 8 m -- rows p_i, q_i; columns p_j, q_j
+        if (h == 0) cs[j] = make_float4(c, sn, cm1, __int_as_float(pj | (qj << 8)));
+        __asm__ volatile("" ::: "memory");
+        float4 ri[16];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int i = r8 + 8 * m;
-            const float ci = __shfl(c, i), si = __shfl(sn, i);
-            int pi, qi;
-            rr_pair(PW, ir, i, &pi, &qi);
-            const float x00 = Gc[pi][pj], x01 = Gc[pi][qj], x10 = Gc[qi][pj], x11 = Gc[qi][qj];
-            // columns: [x_p, x_q] <- [c x_p - s x_q, s x_p + c x_q]; then rows
-            const float y00 = c * x00 - sn * x01, y01 = sn * x00 + c * x01;
-            const float y10 = c * x10 - sn * x11, y11 = sn * x10 + c * x11;
-            Gn[pi][pj] = ci * y00 - si * y10;
-            Gn[qi][pj] = si * y00 + ci * y10;
-            Gn[pi][qj] = ci * y01 - si * y11;
-            Gn[qi][qj] = si * y01 + ci * y11;
+        for (int m = 0; m < 16; ++m) ri[m] = cs[16 * h + m];
+        float x[16][4];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const int pq = __float_as_int(ri[m].w), pi = pq & 255, qi = pq >> 8;
+            x[m][0] = G[pi][pj];
+            x[m][1] = G[pi][qj];
+            x[m][2] = G[qi][pj];
+            x[m][3] = G[qi][qj];
         }
-        // R: columns p_j, q_j of rows a = r8 + 8 m (plus (J - I): (c - 1) on the
-        // diagonal and +-s off it)
-        if (sn != 0.0f) {
+        const bool rot = sn != 0.0f;
+        float xr[32], yr[32];
+        if (rot) {
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int a = r8 + 8 * m;
-                const float xr = R[a][pj], yr = R[a][qj];
-                float np = fmaf(cm1, xr, xr) - sn * yr;
-                float nq = fmaf(cm1, yr, yr) + sn * xr;
-                if (a == pj) {
-                    np += cm1;
-                    nq += sn;
-                } else if (a == qj) {
-                    np -= sn;
-                    nq += cm1;
-                }
-                R[a][pj] = np;
-                R[a][qj] = nq;
+            for (int m = 0; m < 32; ++m) {
+                xr[m] = R[h + 2 * m][pj];
+                yr[m] = R[h + 2 * m][qj];
             }
         }
-        __syncthreads();
+        // G: columns first ([x_p, x_q] <- [c x_p - s x_q, s x_p + c x_q]), then
+        // rows with pair i's rotation
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const int pq = __float_as_int(ri[m].w), pi = pq & 255, qi = pq >> 8;
+            const float ci = ri[m].x, si = ri[m].y;
+            const float y00 = c * x[m][0] - sn * x[m][1], y01 = sn * x[m][0] + c * x[m][1];
+            const float y10 = c * x[m][2] - sn * x[m][3], y11 = sn * x[m][2] + c * x[m][3];
+            G[pi][pj] = ci * y00 - si * y10;
+            G[qi][pj] = si * y00 + ci * y10;
+            G[pi][qj] = ci * y01 - si * y11;
+            G[qi][qj] = si * y01 + ci * y11;
+        }
+        // R <- R J (plus J - I on rows p_j, q_j)
+        if (rot) {
+#pragma unroll
+            for (int m = 0; m < 32; ++m) {
+                R[h + 2 * m][pj] = fmaf(cm1, xr[m], xr[m]) - sn * yr[m];
+                R[h + 2 * m][qj] = fmaf(cm1, yr[m], yr[m]) + sn * xr[m];
+            }
+            if ((pj & 1) == h) {
+                R[pj][pj] += cm1;
+                R[pj][qj] += sn;
+            }
+            if ((qj & 1) == h) {
+                R[qj][pj] -= sn;
+                R[qj][qj] += cm1;
+            }
+        }
+        __asm__ volatile("" ::: "memory");
     }
-    const float (*Gf)[PW + 1] = G[(PW - 1) & 1];
+    __syncthreads();
     // 4. R row-major [b][a] (X_new[a] = X[a] + sum_b R[b][a] X[b])
     float* Rg = md.rot + (int64_t)it.slot * PW * PW;
-    for (int idx = tid; idx < PW * PW; idx += 256) gst(Rg + idx, R[idx >> 6][idx & 63]);
+#pragma unroll 8
+    for (int e = 0; e < PW; ++e) gst(Rg + e * PW + l, R[e][l]);
     // rotated squared column norms (diagonal of Q^T G Q) for the next sweep's ordering
-    if (tid < PW) gst(md.cnorm + pair_row(md, bI, bJ, tid), (float)(Gf[tid][tid] * dmax));
-    if (tid == 0) {
+    gst(md.cnorm + pair_row(md, bI, bJ, l), (float)(G[l][l] * dmax));
+    if (l == 0) {
         *rflag = 1;
         atomicAdd(&fl.pairs_applied, 1);
     }
@@ -528,7 +538,7 @@ hipError_t launch_jacobi_gram(const MatDev* mats, const MatFlags* flags, const G
 
 hipError_t launch_jacobi_solve(const MatDev* mats, MatFlags* flags, const SolveItem* si, int nsi,
                                int round, hipStream_t st) {
-    hipLaunchKernelGGL(jac_solve_kernel, dim3(nsi), dim3(256), 0, st, mats, flags, si, round);
+    hipLaunchKernelGGL(jac_solve_kernel, dim3(nsi), dim3(64), 0, st, mats, flags, si, round);
     return hipGetLastError();
 }
 
