@@ -435,11 +435,14 @@ int pipe_pre(sc_opt* h, Pipe& p, hipStream_t st, bool warm) {
     return SC_OK;
 }
 
-void pipe_start_rounds(sc_opt* h, Pipe& p, int which, int first_check_sweeps) {
+// Rounds of list set `which` until every matrix of the pipe is done.  The host
+// polls once per `rps` rounds: a sweep of the largest matrix still in work
+// (max_nb; 0 = the largest of the list).  Each matrix counts its own sweeps.
+void pipe_start_rounds(sc_opt* h, Pipe& p, int which, int first_check_sweeps, int max_nb = 0) {
     p.stage = STAGE_ROUNDS;
     p.which = which;
     p.r = 0;
-    p.rps = std::max(1, p.L[which].max_nb - 1);  // rounds per sweep of the largest matrix
+    p.rps = std::max(1, (max_nb ? max_nb : p.L[which].max_nb) - 1);
     p.max_rounds = p.L[which].nmat ? h->hp.max_sweeps * p.rps : 0;
     p.first_check = std::min(p.max_rounds, first_check_sweeps * p.rps);
     p.poll_pending = false;
@@ -556,7 +559,12 @@ int do_refresh(sc_opt* h, hipStream_t st) {
                             if ((rc = pipe_finalize(h, p, ps))) return rc;
                             p.stage = STAGE_DONE;
                         } else {
-                            pipe_start_rounds(h, p, LIST_POLISH, 1);
+                            // polish the matrices that failed the certificate
+                            int nb = 2;
+                            for (int i : p.host_mats)
+                                if (h->mh[i].klen && !p.flags_h[i].done)
+                                    nb = std::max(nb, h->mh[i].nb);
+                            pipe_start_rounds(h, p, LIST_POLISH, 1, nb);
                         }
                         queued = true;
                         continue;
