@@ -8,6 +8,7 @@ namespace scopt {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 
 // bfloat16 <-> float32.  bf16 is the upper half of an IEEE float32;
 // narrowing rounds to nearest, ties to even (NaN stays NaN).

@@ -209,25 +209,68 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
 }
 
 // ---------------------------------------------------------------------------------
+// Pair solve: one cyclic sweep of 2x2 Jacobi rotations on the 64x64 pair Gram.
+//
+// The sweep runs in a moving frame ("slots"): at every step pair j rotates slots
+// (2j, 2j+1), and afterwards every column moves to slot sigma(s) -- slot 0 stays,
+// the others advance one place along the cycle 1, 3, 5, ..., 63, 62, 60, ..., 2.
+// This is the circle (round-robin tournament) ordering: in 63 steps every two
+// columns share a pair exactly once, and the cycle closes, so the final frame is
+// the original one.  Reads of a step are then at fixed, conflict-free LDS
+// addresses, and the move is folded into the step's writes.
+namespace {
+constexpr int SG = 66;  // LDS row stride of G (upper triangle + diagonal, slot frame)
+constexpr int SR = 68;  // LDS row stride of R^T (row = slot, column = original row of R)
+// A lower-triangle entry of G, never read: it takes the writes of lanes without a block.
+constexpr int kSink = (PW - 1) * SG;
+
+__device__ __forceinline__ int slot_next(int s) {
+    return s == 0 ? 0 : s == 2 ? 1 : (s & 1) ? (s == 63 ? 62 : s + 2) : s - 2;
+}
+// Position of slot s (> 0) on the cycle, and the slot at position k.
+__device__ __forceinline__ int cycle_pos(int s) { return (s & 1) ? (s - 1) >> 1 : 32 + ((62 - s) >> 1); }
+__device__ __forceinline__ int cycle_slot(int k) { return k < 32 ? 2 * k + 1 : 126 - 2 * k; }
+
+// Pair-blocks (i < j) of each bank class t = (2 i + j) mod 16, in order of i then
+// j (30 or 32 per class): bit 15 marks an entry, bits 0-7 hold i, bits 8-15 j.
+struct BlockTable {
+    unsigned short v[16][32];
+};
+constexpr BlockTable make_block_table() {
+    BlockTable t{};
+    for (int c = 0; c < 16; ++c) {
+        int n = 0;
+        for (int i = 0; i < 32; ++i)
+            for (int e = 0; e < 2; ++e) {
+                const int j = ((c - 2 * i) & 15) + 16 * e;
+                if (j > i) t.v[c][n++] = (unsigned short)(0x8000 | i | (j << 8));
+            }
+    }
+    return t;
+}
+__constant__ BlockTable kBlocks = make_block_table();
+}  // namespace
+
 __global__ __launch_bounds__(64) void jac_solve_kernel(const MatDev* __restrict__ mats,
                                                        MatFlags* __restrict__ flags,
                                                        const SolveItem* __restrict__ items,
                                                        int round) {
     // One wavefront per pair: LDS accesses of a wavefront are carried out in
-    // issue order, so the steps of the inner sweep need no barriers, only
-    // compiler fences that keep the accesses in program order.
-    // G: float32 working copy of the pair Gram, scaled by 1 / max diagonal so
-    // that the solve does not depend on the matrix's magnitude.
+    // issue order, so the steps need no barriers, only compiler fences that keep
+    // the accesses in program order; all reads of a step precede its writes.
+    // G: float32 working copy of the pair Gram (upper triangle), scaled by
+    // 1 / max diagonal so that the solve does not depend on the magnitude.
     // R: the accumulated rotation minus the identity, Q = I + R, kept directly
-    // in float32.  Each 2x2 rotation enters R through (c - 1) = -t s / (1 + h),
-    // h = sqrt(1 + t^2), and s, so a tiny rotation is carried exactly (storing
-    // Q itself in float32 would round c to 1 while s != 0, a biased growth of
-    // the column norms over thousands of rotations).  c = 1 / h and s = t c
-    // satisfy c^2 + s^2 = 1 to float32 rounding, so float32 parameters suffice.
-    __shared__ float G[PW][PW + 1];
-    __shared__ float R[PW][PW + 1];
-    __shared__ float4 cs[PW / 2];  // per pair of the step: c, s, c - 1, p | q << 8
-    __shared__ double rs[PW];      // 1 / sqrt(g_aa) above the zero floor, else 0
+    // in float32 (stored transposed, one slot per row).  Each 2x2 rotation enters
+    // R through (c - 1) = -t s / (1 + h), h = sqrt(1 + t^2), and s, so a tiny
+    // rotation is carried exactly (storing Q itself in float32 would round c to 1
+    // while s != 0, a biased growth of the column norms over thousands of
+    // rotations).  c = 1 / h and s = t c satisfy c^2 + s^2 = 1 to float32
+    // rounding, so float32 parameters suffice.
+    __shared__ __align__(16) float G[PW * SG];
+    __shared__ __align__(16) float RT[PW * SR];
+    __shared__ float cc[PW / 2], ss[PW / 2];  // rotation of each pair of the step
+    __shared__ double rs[PW];                 // 1 / sqrt(g_aa) above the zero floor, else 0
 
     const SolveItem it = items[blockIdx.x];
     MatFlags& fl = flags[it.mat];
@@ -238,40 +281,46 @@ __global__ __launch_bounds__(64) void jac_solve_kernel(const MatDev* __restrict_
     int bI, bJ;
     rr_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
 
-    // 1. diagonal of the pair Gram: split partials summed in fixed order (fp64)
+    // 1. the pair Gram: split partials summed in fixed order (fp64).  Lane l
+    //    takes the diagonal entry of column l and 4 entries of each stored upper
+    //    16x16 tile (10 of 16); all loads of a split are in flight together.
     const double* gp = md.gram + (int64_t)it.slot * md.nsplit * (PW * PW);
-    double dl = 0.0;
-    for (int sp = 0; sp < it.nsplit; ++sp) dl += gld(gp + (int64_t)sp * PW * PW + l * (PW + 1));
+    double dl = 0.0, acc[40];
+#pragma unroll
+    for (int e = 0; e < 40; ++e) acc[e] = 0.0;
+    auto tile_row = [&](int e) {
+        const int t = e >> 2, ti = t < 4 ? 0 : t < 7 ? 1 : t < 9 ? 2 : 3;
+        return 16 * ti + (l >> 4) + 4 * (e & 3);
+    };
+    auto tile_col = [&](int e) {
+        const int t = e >> 2, ti = t < 4 ? 0 : t < 7 ? 1 : t < 9 ? 2 : 3;
+        const int tj = ti + t - (ti == 0 ? 0 : ti == 1 ? 4 : ti == 2 ? 7 : 9);
+        return 16 * tj + (l & 15);
+    };
+#pragma unroll 2
+    for (int sp = 0; sp < it.nsplit; ++sp) {
+        const double* g = gp + (int64_t)sp * PW * PW;
+        dl += gld(g + l * (PW + 1));
+#pragma unroll
+        for (int e = 0; e < 40; ++e) acc[e] += gld(g + tile_row(e) * PW + tile_col(e));
+    }
     double dmax = dl;
     for (int o = 32; o > 0; o >>= 1) dmax = fmax(dmax, __shfl_xor(dmax, o));
     const double scale = dmax > 0.0 ? 1.0 / dmax : 1.0;
     const double floor2d = (double)fl.floor2;
     const float floor2 = (float)(floor2d * scale);
-    const double rsl = dl > floor2d ? 1.0 / sqrt(dl) : 0.0;
-    rs[l] = rsl;
+    rs[l] = dl > floor2d ? 1.0 / sqrt(dl) : 0.0;
     __syncthreads();
 
-    // 2. the stored upper 16x16 tiles (10 of 16), each read once and mirrored in
-    //    LDS; the largest relative off-diagonal |g_ab| / sqrt(g_aa g_bb) over
-    //    columns above the zero floor (rs = 0 below it)
+    // 2. G keeps the upper triangle.  The largest relative off-diagonal
+    //    |g_ab| / sqrt(g_aa g_bb) over columns above the zero floor (rs = 0 below it).
     float mo = 0.0f;
-#pragma unroll 1
-    for (int t = 0; t < 10; ++t) {
-        const int ti = t < 4 ? 0 : t < 7 ? 1 : t < 9 ? 2 : 3;
-        const int tj = ti + t - (ti == 0 ? 0 : ti == 1 ? 4 : ti == 2 ? 7 : 9);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int a = 16 * ti + (l >> 4) + 4 * k, b = 16 * tj + (l & 15);
-            double s = 0.0;
-            for (int sp = 0; sp < it.nsplit; ++sp) s += gld(gp + (int64_t)sp * PW * PW + a * PW + b);
-            const float g = (float)(s * scale);
-            G[a][b] = g;
-            if (ti != tj) G[b][a] = g;  // a diagonal tile is stored whole
-            if (a < b) mo = fmaxf(mo, (float)(fabs(s) * rs[a] * rs[b]));
-        }
+    for (int e = 0; e < 40; ++e) {
+        const int a = tile_row(e), b = tile_col(e);
+        if (a <= b) G[a * SG + b] = (float)(acc[e] * scale);
+        if (a < b) mo = fmaxf(mo, (float)(fabs(acc[e]) * rs[a] * rs[b]));
     }
-#pragma unroll 8
-    for (int e = 0; e < PW; ++e) R[e][l] = 0.0f;
     for (int o = 32; o > 0; o >>= 1) mo = fmaxf(mo, __shfl_xor(mo, o));
     if (l == 0) atomicMax(&fl.sweep_max, __float_as_uint(mo));
     int* rflag = md.rot_flag + it.slot;
@@ -281,98 +330,148 @@ __global__ __launch_bounds__(64) void jac_solve_kernel(const MatDev* __restrict_
         if (l == 0) *rflag = 0;
         return;
     }
-    __syncthreads();
+    for (int e = l; e < PW * SR / 4; e += 64) *(v4f*)&RT[4 * e] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // 3. one cyclic sweep of 2x2 rotations on G (G <- J^T G J), accumulating R.
-    //    Lane l: pair j = l % 32 of the step, half h = l / 32.  Both halves
-    //    compute pair j's rotation from G; the lower half publishes it in cs.
-    //    G: lane l updates the 2x2 blocks (i, j), i = 16 h + m, rows p_i, q_i x
-    //    columns p_j, q_j -- every entry of G belongs to one lane per step.
-    //    R: columns p_j, q_j of rows a = h + 2 m.  A lane issues all its reads
-    //    of a step before its first write, so the LDS latency is paid once.
-    const int j = l & 31, h = l >> 5;
+    // 3. per-lane addresses, fixed for the whole sweep.
+    //    Rotation: lanes 2j, 2j+1 both compute pair j's.
+    //    G: lane l takes the pair-blocks (i < j) of bank class t = l % 16, numbers
+    //    8 (l / 16) .. + 7 within the class: the 16 lanes of a quarter read 16
+    //    distinct bank pairs.  Its 4 entries go to their moved slots (upper
+    //    triangle); odd lane quarters write them in the order (0,1), (0,0), (1,1),
+    //    (1,0), which puts the two quarters of a half-wave on opposite banks.
+    //    Pair j's own 2x2 block: lanes 2j and 2j+1 (the same values).
+    //    R^T: lane l updates rows (slots) 2j, 2j+1 of pair j = l / 2, columns
+    //    8 k + 4 (l % 2) .. + 3, k = 0..7.
+    const int jr = l >> 1, hh = l & 1, cls = l & 15, odd = (l >> 4) & 1;
+    int blk_ij[8], blk_rd[8], blk_wr[8][4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        // past the end of a class: computes on block (0, 1), writes nothing
+        const int v = kBlocks.v[cls][8 * (l >> 4) + u];
+        const bool ok = v & 0x8000;
+        const int i = ok ? v & 255 : 0, j = ok ? (v >> 8) & 127 : 1;
+        blk_ij[u] = i | (j << 8);
+        blk_rd[u] = 2 * i * SG + 2 * j;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ee = odd ? (e ^ 1) : e;  // entry (ee >> 1, ee & 1) of the block
+            const int r = slot_next(2 * i + (ee >> 1)), c = slot_next(2 * j + (ee & 1));
+            blk_wr[u][e] = ok ? min(r, c) * SG + max(r, c) : kSink;
+        }
+    }
+    const int sp_ = slot_next(2 * jr), sq_ = slot_next(2 * jr + 1);
+    const int dg_pp = sp_ * SG + sp_, dg_qq = sq_ * SG + sq_, dg_pq = min(sp_, sq_) * SG + max(sp_, sq_);
+    const int rt_rd = 2 * jr * SR + 4 * hh, rt_wp = sp_ * SR + 4 * hh, rt_wq = sq_ * SR + 4 * hh;
+    // original columns held by slots 2 jr, 2 jr + 1: positions on the cycle
+    int kp = jr == 0 ? -1 : cycle_pos(2 * jr), kq = cycle_pos(2 * jr + 1);
+    __syncthreads();
+    // rotation inputs of the step: g_pp, g_pq, g_qq of the lane's pair
+    v2f dpq = *(const v2f*)&G[2 * jr * SG + 2 * jr];
+    float gqq = G[(2 * jr + 1) * SG + 2 * jr + 1];
+
 #pragma unroll 1
     for (int ir = 0; ir < PW - 1; ++ir) {
-        int pj, qj;
-        rr_pair(PW, ir, j, &pj, &qj);
+        // ---- reads (the rotation inputs were read at the end of the last step)
+        __asm__ volatile("" ::"v"(dpq), "v"(gqq));
+        v2f x0[8], x1[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            x0[u] = *(const v2f*)&G[blk_rd[u]];
+            x1[u] = *(const v2f*)&G[blk_rd[u] + SG];
+        }
+        v4f xr[8], yr[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            xr[k] = *(const v4f*)&RT[rt_rd + 8 * k];
+            yr[k] = *(const v4f*)&RT[rt_rd + SR + 8 * k];
+        }
+        // the elements of rows 2 jr, 2 jr + 1 at the original columns op, oq held by
+        // the pair's slots: R's identity entries sit there (both lanes read them)
+        const int op = kp < 0 ? 0 : cycle_slot(kp), oq = cycle_slot(kq);
+        const float xop = RT[2 * jr * SR + op], yop = RT[(2 * jr + 1) * SR + op];
+        const float xoq = RT[2 * jr * SR + oq], yoq = RT[(2 * jr + 1) * SR + oq];
+        // ---- rotation of pair jr (both lanes of the pair compute and publish it)
+        const float gpp = dpq[0], gpq = dpq[1];
         float c = 1.0f, sn = 0.0f, cm1 = 0.0f;
+        if (gpp > floor2 && gqq > floor2 && fabsf(gpq) > tol * __builtin_amdgcn_sqrtf(gpp * gqq)) {
+            const float zeta = (gqq - gpp) * 0.5f * __builtin_amdgcn_rcpf(gpq);
+            const float az = fabsf(zeta);
+            // t = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)), without overflow
+            const float den = az < 1e18f ? az + __builtin_amdgcn_sqrtf(fmaf(az, az, 1.0f)) : 2.0f * az;
+            const float t = copysignf(__builtin_amdgcn_rcpf(den), zeta);
+            const float hq = __builtin_amdgcn_sqrtf(fmaf(t, t, 1.0f));
+            c = __builtin_amdgcn_rcpf(hq);
+            sn = t * c;
+            cm1 = -t * sn * __builtin_amdgcn_rcpf(1.0f + hq);
+        }
+        cc[jr] = c;
+        ss[jr] = sn;
+        __asm__ volatile("" ::: "memory");
+        // ---- G: off-diagonal pair-blocks; columns first ([x_p, x_q] <-
+        //      [c x_p - s x_q, s x_p + c x_q]), then rows with pair i's rotation
+        float wv[8][4];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = blk_ij[u] & 255, j = (blk_ij[u] >> 8) & 255;
+            const float ci = cc[i], si = ss[i], cj = cc[j], sj = ss[j];
+            const float y00 = cj * x0[u][0] - sj * x0[u][1], y01 = sj * x0[u][0] + cj * x0[u][1];
+            const float y10 = cj * x1[u][0] - sj * x1[u][1], y11 = sj * x1[u][0] + cj * x1[u][1];
+            const float z00 = ci * y00 - si * y10, z01 = ci * y01 - si * y11;
+            const float z10 = si * y00 + ci * y10, z11 = si * y01 + ci * y11;
+            wv[u][0] = odd ? z01 : z00;
+            wv[u][1] = odd ? z00 : z01;
+            wv[u][2] = odd ? z11 : z10;
+            wv[u][3] = odd ? z10 : z11;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) G[blk_wr[u][e]] = wv[u][e];
+        // ---- G: the pair's own block (both lanes write the same values)
         {
-            const float gpp = G[pj][pj], gqq = G[qj][qj], gpq = G[pj][qj];
-            if (gpp > floor2 && gqq > floor2 &&
-                fabsf(gpq) > tol * __builtin_amdgcn_sqrtf(gpp * gqq)) {
-                const float zeta = (gqq - gpp) * 0.5f * __builtin_amdgcn_rcpf(gpq);
-                const float az = fabsf(zeta);
-                // t = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)), without overflow
-                const float den =
-                    az < 1e18f ? az + __builtin_amdgcn_sqrtf(fmaf(az, az, 1.0f)) : 2.0f * az;
-                const float t = copysignf(__builtin_amdgcn_rcpf(den), zeta);
-                const float hh = __builtin_amdgcn_sqrtf(fmaf(t, t, 1.0f));
-                c = __builtin_amdgcn_rcpf(hh);
-                sn = t * c;
-                cm1 = -t * sn * __builtin_amdgcn_rcpf(1.0f + hh);
-            }
+            const float y00 = c * gpp - sn * gpq, y01 = sn * gpp + c * gpq;
+            const float y10 = c * gpq - sn * gqq, y11 = sn * gpq + c * gqq;
+            G[dg_pp] = c * y00 - sn * y10;
+            G[dg_pq] = c * y01 - sn * y11;
+            G[dg_qq] = sn * y01 + c * y11;
         }
-        if (h == 0) cs[j] = make_float4(c, sn, cm1, __int_as_float(pj | (qj << 8)));
+        // ---- R <- R J: rows 2 jr, 2 jr + 1 of R^T, written to their moved slots
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            v4f np, nq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                np[e] = fmaf(cm1, xr[k][e], xr[k][e]) - sn * yr[k][e];
+                nq[e] = fmaf(cm1, yr[k][e], yr[k][e]) + sn * xr[k][e];
+            }
+            *(v4f*)&RT[rt_wp + 8 * k] = np;
+            *(v4f*)&RT[rt_wq + 8 * k] = nq;
+        }
+        // plus J - I on those four elements: both lanes of the pair overwrite them
+        // with the same corrected values
+        RT[sp_ * SR + op] = fmaf(cm1, xop, xop) - sn * yop + cm1;
+        RT[sq_ * SR + op] = fmaf(cm1, yop, yop) + sn * xop + sn;
+        RT[sp_ * SR + oq] = fmaf(cm1, xoq, xoq) - sn * yoq - sn;
+        RT[sq_ * SR + oq] = fmaf(cm1, yoq, yoq) + sn * xoq + cm1;
+        kp = kp < 0 ? -1 : (kp == 0 ? 62 : kp - 1);
+        kq = kq == 0 ? 62 : kq - 1;
         __asm__ volatile("" ::: "memory");
-        float4 ri[16];
-#pragma unroll
-        for (int m = 0; m < 16; ++m) ri[m] = cs[16 * h + m];
-        float x[16][4];
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const int pq = __float_as_int(ri[m].w), pi = pq & 255, qi = pq >> 8;
-            x[m][0] = G[pi][pj];
-            x[m][1] = G[pi][qj];
-            x[m][2] = G[qi][pj];
-            x[m][3] = G[qi][qj];
-        }
-        const bool rot = sn != 0.0f;
-        float xr[32], yr[32];
-        if (rot) {
-#pragma unroll
-            for (int m = 0; m < 32; ++m) {
-                xr[m] = R[h + 2 * m][pj];
-                yr[m] = R[h + 2 * m][qj];
-            }
-        }
-        // G: columns first ([x_p, x_q] <- [c x_p - s x_q, s x_p + c x_q]), then
-        // rows with pair i's rotation
-#pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const int pq = __float_as_int(ri[m].w), pi = pq & 255, qi = pq >> 8;
-            const float ci = ri[m].x, si = ri[m].y;
-            const float y00 = c * x[m][0] - sn * x[m][1], y01 = sn * x[m][0] + c * x[m][1];
-            const float y10 = c * x[m][2] - sn * x[m][3], y11 = sn * x[m][2] + c * x[m][3];
-            G[pi][pj] = ci * y00 - si * y10;
-            G[qi][pj] = si * y00 + ci * y10;
-            G[pi][qj] = ci * y01 - si * y11;
-            G[qi][qj] = si * y01 + ci * y11;
-        }
-        // R <- R J (plus J - I on rows p_j, q_j)
-        if (rot) {
-#pragma unroll
-            for (int m = 0; m < 32; ++m) {
-                R[h + 2 * m][pj] = fmaf(cm1, xr[m], xr[m]) - sn * yr[m];
-                R[h + 2 * m][qj] = fmaf(cm1, yr[m], yr[m]) + sn * xr[m];
-            }
-            if ((pj & 1) == h) {
-                R[pj][pj] += cm1;
-                R[pj][qj] += sn;
-            }
-            if ((qj & 1) == h) {
-                R[qj][pj] -= sn;
-                R[qj][qj] += cm1;
-            }
-        }
-        __asm__ volatile("" ::: "memory");
+        // rotation inputs of the next step
+        dpq = *(const v2f*)&G[2 * jr * SG + 2 * jr];
+        gqq = G[(2 * jr + 1) * SG + 2 * jr + 1];
     }
     __syncthreads();
-    // 4. R row-major [b][a] (X_new[a] = X[a] + sum_b R[b][a] X[b])
+    // 4. R row-major [b][a] (X_new[a] = X[a] + sum_b R[b][a] X[b]); the frame is the
+    //    original one again, so R[b][a] = R^T[a][b]
     float* Rg = md.rot + (int64_t)it.slot * PW * PW;
-#pragma unroll 8
-    for (int e = 0; e < PW; ++e) gst(Rg + e * PW + l, R[e][l]);
+#pragma unroll 4
+    for (int b0 = 0; b0 < PW; b0 += 4) {
+        const v4f v = *(const v4f*)&RT[l * SR + b0];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gst(Rg + (b0 + e) * PW + l, v[e]);
+    }
     // rotated squared column norms (diagonal of Q^T G Q) for the next sweep's ordering
-    gst(md.cnorm + pair_row(md, bI, bJ, l), (float)(G[l][l] * dmax));
+    gst(md.cnorm + pair_row(md, bI, bJ, l), (float)(G[l * SG + l] * dmax));
     if (l == 0) {
         *rflag = 1;
         atomicAdd(&fl.pairs_applied, 1);
