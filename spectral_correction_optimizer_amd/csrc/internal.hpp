@@ -10,7 +10,7 @@ namespace scopt {
 constexpr int kMaxPtrs = 128;  // matrices per launch when pointers travel as kernel arguments
 constexpr int kJb = 32;        // Jacobi column-block width b; a pair block holds 2b = 64 columns
 constexpr int kPw = 2 * kJb;   // pair width
-constexpr int kApplyCols = 256;            // columns per rotation-apply workgroup
+constexpr int kApplyCols = 128;            // columns per rotation-apply workgroup
 constexpr int kApplyThreads = 2 * kApplyCols;  // a 64-lane wave updates 32 columns
 
 // Caller pointers of one call (weights / gradients), passed by value.
