@@ -337,15 +337,18 @@ int build_projectors(sc_opt* h, hipStream_t st) {
     return SC_OK;
 }
 
-// chol = A^T A (float64 sums) and E = its normalized off-diagonal part.
-int pipe_final_gram(sc_opt* h, Pipe& p, hipStream_t st) {
-    HIP_TRY(timed(h, PK_GRAM_E, st,
-                  [&] { return launch_chol_syrk(h->md, p.syrk_all, p.nsyrk_all, st); }));
+// chol = A^T A (float64 sums) and E = its normalized off-diagonal part; with
+// only_regram, for the matrices polished after failing the certificate alone.
+int pipe_final_gram(sc_opt* h, Pipe& p, hipStream_t st, bool only_regram = false) {
     HIP_TRY(timed(h, PK_GRAM_E, st, [&] {
-        return launch_gram_to_e(h->md, h->flags_d, p.mats, p.nmat, p.max_t64, st);
+        return launch_chol_syrk(h->md, h->flags_d, p.syrk_all, p.nsyrk_all, only_regram, st);
+    }));
+    HIP_TRY(timed(h, PK_GRAM_E, st, [&] {
+        return launch_gram_to_e(h->md, h->flags_d, p.mats, p.nmat, p.max_t64, only_regram, st);
     }));
     if (h->prof.on)
         for (int i : p.host_mats) {
+            if (only_regram && !(h->mh[i].klen && !p.flags_h[i].done)) continue;
             const double kt = (h->mh[i].k + 127) / 128;
             h->prof.flops[PK_GRAM_E] += kt * (kt + 1) / 2 * 2.0 * 128 * 128 * h->mh[i].K_ld;
         }
@@ -418,8 +421,9 @@ int pipe_pre(sc_opt* h, Pipe& p, hipStream_t st, bool warm) {
     }));
     if (p.pre) {
         // Factor phase: Jacobi on X = L, A^T A = L L^T (k-long rows, no V).
-        HIP_TRY(timed(h, PK_CHOL_GEMM, st,
-                      [&] { return launch_chol_syrk(h->md, p.syrk_cap, p.nsyrk_cap, st); }));
+        HIP_TRY(timed(h, PK_CHOL_GEMM, st, [&] {
+            return launch_chol_syrk(h->md, h->flags_d, p.syrk_cap, p.nsyrk_cap, 0, st);
+        }));
         HIP_TRY(timed(h, PK_CHOL, st, [&] {
             return launch_cholesky(h->md, h->flags_d, p.cap, p.ncap, p.max_nbk, p.max_klen, st);
         }));
@@ -508,7 +512,7 @@ int pipe_after_rounds(sc_opt* h, Pipe& p, hipStream_t st) {
         p.stage = STAGE_CERT;
         return pipe_poll(h, p, st);
     }
-    if ((rc = pipe_final_gram(h, p, st))) return rc;
+    if ((rc = pipe_final_gram(h, p, st, p.which == LIST_POLISH))) return rc;
     if ((rc = pipe_finalize(h, p, st))) return rc;
     p.stage = STAGE_DONE;
     return SC_OK;

@@ -55,9 +55,12 @@ constexpr int SB = 128, SK = 32, SLD = 160, SFOLD = 256;
 }
 
 __global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict__ mats,
-                                                        const SyrkItem* __restrict__ items) {
+                                                        const MatFlags* __restrict__ flags,
+                                                        const SyrkItem* __restrict__ items,
+                                                        int only_regram) {
     __shared__ float Xs[2][SK][SLD];
     const SyrkItem it = items[blockIdx.x];
+    if (only_regram && !flags[it.mat].regram) return;
     const MatDev& md = mats[it.mat];
     const bool diag = it.ti == it.tj;
     const int k = md.k, ld = md.K_ld;
@@ -368,8 +371,10 @@ hipError_t launch_factor_invnorm(const MatDev* mats, const MatFlags* flags, cons
     return hipGetLastError();
 }
 
-hipError_t launch_chol_syrk(const MatDev* mats, const SyrkItem* items, int nitems, hipStream_t st) {
-    hipLaunchKernelGGL(chol_syrk_kernel, dim3(nitems), dim3(256), 0, st, mats, items);
+hipError_t launch_chol_syrk(const MatDev* mats, const MatFlags* flags, const SyrkItem* items,
+                            int nitems, int only_regram, hipStream_t st) {
+    hipLaunchKernelGGL(chol_syrk_kernel, dim3(nitems), dim3(256), 0, st, mats, flags, items,
+                       only_regram);
     return hipGetLastError();
 }
 
@@ -396,12 +401,14 @@ hipError_t launch_cholesky(const MatDev* mats, MatFlags* flags, const int* mat_i
 // upper tile of E is written through an LDS transpose.
 __global__ __launch_bounds__(256) void gram_to_e_kernel(const MatDev* __restrict__ mats,
                                                         MatFlags* __restrict__ flags,
-                                                        const int* __restrict__ mat_idx) {
+                                                        const int* __restrict__ mat_idx,
+                                                        int only_regram) {
     __shared__ float T[CT][CT + 1];
     __shared__ double rdi[CT], cdi[CT];
     __shared__ float red[4];
     const int i = mat_idx[blockIdx.y];
     MatFlags& f = flags[i];
+    if (only_regram && !f.regram) return;
     const MatDev& md = mats[i];
     const int k = md.k, nt = (k + CT - 1) / CT;
     const int t = blockIdx.x;
@@ -446,9 +453,9 @@ __global__ __launch_bounds__(256) void gram_to_e_kernel(const MatDev* __restrict
 }
 
 hipError_t launch_gram_to_e(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
-                            int max_t64, hipStream_t st) {
+                            int max_t64, int only_regram, hipStream_t st) {
     hipLaunchKernelGGL(gram_to_e_kernel, dim3(max_t64 * (max_t64 + 1) / 2, nmat), dim3(256), 0, st,
-                       mats, flags, mat_idx);
+                       mats, flags, mat_idx, only_regram);
     return hipGetLastError();
 }
 
@@ -461,10 +468,12 @@ __global__ void certify_kernel(const MatDev* __restrict__ mats, MatFlags* __rest
     if (!(__uint_as_float(f.check_off) > mats[i].tol_conv)) {
         f.converged = 1;
         f.done = 1;
+        f.regram = 0;
     } else {
         f.converged = 0;
         f.done = 0;
         f.check_off = 0u;
+        f.regram = 1;
     }
 }
 

@@ -72,7 +72,8 @@ struct MatFlags {
     int rounds_pre;          // rounds_active / pairs_applied at the end of the factor phase
     int pairs_pre;
     unsigned int check_off;  // largest |a_p.a_q| / (|a_p| |a_q|) of the final operand (float bits)
-    int pad[2];
+    int regram;              // 1 when the certificate failed: polished, its final Gram is redone
+    int pad[1];
 };
 
 // ---- work items ------------------------------------------------------------------
@@ -157,7 +158,8 @@ hipError_t launch_jacobi_sweep_end(const MatDev* mats, MatFlags* flags, const in
 // ---- Cholesky preconditioning of tall operands ------------------------------------------
 
 // chol = A^T A (lower 128 x 128 tiles listed in items), float64 sums.
-hipError_t launch_chol_syrk(const MatDev* mats, const SyrkItem* items, int nitems, hipStream_t st);
+hipError_t launch_chol_syrk(const MatDev* mats, const MatFlags* flags, const SyrkItem* items,
+                            int nitems, int only_regram, hipStream_t st);
 // chol = L L^T (in place, lower triangle) for the matrices in mat_idx; on success the
 // rows of A become the columns of L (length klen) and precond = 1, else chol_fail = 1
 // and done = 1 (the matrix sits the factor phase out).  max_nbk: largest ceil(k / 64),
@@ -169,7 +171,7 @@ hipError_t launch_cholesky(const MatDev* mats, MatFlags* flags, const int* mat_i
 // launch_chol_syrk), for the matrices in mat_idx; the largest |E_ij| goes to
 // check_off.  max_t64: largest ceil(k / 64).
 hipError_t launch_gram_to_e(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
-                            int max_t64, hipStream_t st);
+                            int max_t64, int only_regram, hipStream_t st);
 // For the matrices in mat_idx: converged and done when check_off <= tol_conv,
 // otherwise not done (polishing sweeps follow) and check_off cleared.
 hipError_t launch_certify(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,

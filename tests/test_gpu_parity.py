@@ -278,3 +278,44 @@ def test_q_proj_2048_full_config():
     sc = Scenario([(2048, 2048)], [(2, 0, 0)], steps=25)
     rep = sc.run(check_every_step=False)
     Scenario.check(rep)
+
+
+def test_certificate_failure_polishes_that_matrix_alone():
+    """Second (warm) refresh with the factor phase: a noiseless power-law anchor
+    (condition number about 1.4e3) fails the Gram certificate of A = M V and is
+    polished; a long, narrow pure-noise one (condition number about 1.4, short
+    dot products in A = M V) passes it and is not.  Only the polished matrix's final Gram is redone, so
+    every matrix must still carry its own E: G_filt of all three matrices
+    agrees with the oracle."""
+    import spectral_correction_optimizer_amd as sco
+    dev = torch.device("cuda")
+    shapes = [(512, 128), (2048, 64), (256, 256)]
+    say(f"case: certificate failure on one of {shapes}")
+    ins = [gen.MatrixInputs(95, 0, 0, *shapes[0], noise=False),
+           gen.MatrixInputs(95, 0, 1, *shapes[1], r0=0),
+           gen.MatrixInputs(95, 0, 2, *shapes[2])]
+    opt = sco.SpectralAdamW(shapes, device=dev)
+    for i, mi in enumerate(ins):
+        opt.set_state(i, "m_anc", to_dev(gen.stored(mi.m0(), "f32")[0], "f32", dev))
+    opt.refresh()
+    Ms = []
+    for i, mi in enumerate(ins):
+        pay, M = gen.stored(mi.g_anc(1), "f32")
+        Ms.append(M)
+        opt.set_state(i, "m_anc", to_dev(pay, "f32", dev))
+    opt.refresh()
+    st = opt.stats()
+    say(f"  stats {st}")
+    assert st["not_converged"] == 0 and st["factor_rejected"] == 0
+    assert st["sweeps"][0] > st["factor_sweeps"][0] > 0      # factor phase, then polished
+    assert st["sweeps"][1] == st["factor_sweeps"][1] > 0     # certified after the factor phase
+    W = [torch.zeros(m, n, device=dev) for m, n in shapes]
+    G = [gen.stored(mi.g_mask(0), "f32") for mi in ins]
+    opt.step(W, [to_dev(p, "f32", dev) for p, _ in G])
+    for i, M in enumerate(Ms):
+        U, s, V, _ = oracle.svd(M)
+        ref = oracle.project(U, oracle.tikhonov(s, opt.hp["tau_p"]), V, G[i][1])
+        err = relf(from_dev(opt.get_filtered(i)), ref)
+        say(f"  mat {i}: relF G_filt {err:.3e}")
+        assert err <= 1e-4
+    opt.close()
