@@ -147,6 +147,7 @@ struct sc_opt {
         int* mats = nullptr;
         int nmat = 0;
         int max_nb = 2;
+        std::vector<int> nbs;  // distinct block counts of the list's matrices
     };
     struct Pipe {
         Lists L[3];
@@ -385,7 +386,9 @@ void account_sweeps(sc_opt* h) {
         const MatDev& m = h->mh[i];
         const MatFlags& f = h->flags_h[i];
         const double pw = kPw;
-        const double rounds[2] = {(double)f.rounds_pre, (double)(f.rounds_active - f.rounds_pre)};
+        // a matrix stops only at the end of one of its sweeps (nb - 1 rounds each)
+        const double rounds[2] = {(double)f.sweep_base * (m.nb - 1),
+                                  (double)(f.sweeps - f.sweep_base) * (m.nb - 1)};
         const double pairs[2] = {(double)f.pairs_pre, (double)(f.pairs_applied - f.pairs_pre)};
         const double len[2] = {(double)m.klen, (double)m.K};
         const double vlen[2] = {0.0, (double)m.k};
@@ -456,17 +459,28 @@ void pipe_start_rounds(sc_opt* h, Pipe& p, int which, int first_check_sweeps, in
 int pipe_round(sc_opt* h, Pipe& p, hipStream_t st) {
     const sc_opt::Lists& L = p.L[p.which];
     const int r = p.r;
-    HIP_TRY(timed(h, PK_SORT, st,
-                  [&] { return launch_jacobi_sort(h->md, h->flags_d, L.mats, L.nmat, r, st); }));
+    // the sort acts on the first round of a matrix's sweep, the sweep end on its
+    // last: launched only in rounds where some matrix of the list has one
+    bool first = false, last = false;
+    for (int nb : L.nbs) {
+        first = first || r % (nb - 1) == 0;
+        last = last || r % (nb - 1) == nb - 2;
+    }
+    if (first)
+        HIP_TRY(timed(h, PK_SORT, st, [&] {
+            return launch_jacobi_sort(h->md, h->flags_d, L.mats, L.nmat, r, st);
+        }));
     HIP_TRY(timed(h, PK_GRAM, st,
                   [&] { return launch_jacobi_gram(h->md, h->flags_d, L.gi, L.ngi, r, st); }));
     HIP_TRY(timed(h, PK_SOLVE, st,
                   [&] { return launch_jacobi_solve(h->md, h->flags_d, L.si, L.nsi, r, st); }));
     HIP_TRY(timed(h, PK_APPLY, st,
                   [&] { return launch_jacobi_apply(h->md, h->flags_d, L.ai, L.nai, r, st); }));
-    HIP_TRY(timed(h, PK_SWEEP_END, st, [&] {
-        return launch_jacobi_sweep_end(h->md, h->flags_d, L.mats, L.nmat, r, h->hp.max_sweeps, st);
-    }));
+    if (last)
+        HIP_TRY(timed(h, PK_SWEEP_END, st, [&] {
+            return launch_jacobi_sweep_end(h->md, h->flags_d, L.mats, L.nmat, r, h->hp.max_sweeps,
+                                           st);
+        }));
     return SC_OK;
 }
 
@@ -817,6 +831,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
                 const int sl = split_len(len, nt), ns = split_count(len, nt);
                 mats.push_back(i);
                 L.max_nb = std::max(L.max_nb, m.nb);
+                if (std::find(L.nbs.begin(), L.nbs.end(), m.nb) == L.nbs.end()) L.nbs.push_back(m.nb);
                 for (int s = 0; s < m.nb / 2; ++s) {
                     for (int sp = 0; sp < ns; ++sp)
                         gi.push_back(GramItem{i, s, sp, sp * sl, std::min(len, (sp + 1) * sl)});

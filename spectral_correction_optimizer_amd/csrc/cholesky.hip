@@ -498,7 +498,6 @@ __global__ void phase2_reset_kernel(MatFlags* __restrict__ flags, const int* __r
     f.converged = 0;
     f.sweep_max = 0u;
     f.sweep_base = f.sweeps;
-    f.rounds_pre = f.rounds_active;
     f.pairs_pre = f.pairs_applied;
     f.check_off = 0u;
 }

@@ -337,12 +337,10 @@ __global__ __launch_bounds__(256) void init_flags_kernel(const MatDev* __restric
         f.converged = 0;
         f.sweeps = 0;
         f.done = 0;
-        f.rounds_active = 0;
         f.pairs_applied = 0;
         f.sweep_base = 0;
         f.precond = 0;
         f.chol_fail = 0;
-        f.rounds_pre = 0;
         f.pairs_pre = 0;
         f.check_off = 0u;
         f.regram = 0;

@@ -64,13 +64,11 @@ struct MatFlags {
     int sweeps;              // sweeps done in the current refresh
     int done;                // converged or sweep cap reached
     float floor2;            // squared column-norm floor: columns below are zero
-    int rounds_active;       // rounds this matrix took part in (work accounting)
     int pairs_applied;       // pair rotations applied (work accounting)
     int sweep_base;          // sweeps done before the current phase (the cap counts from here)
     int precond;             // 1 while the sweeps run on the Cholesky factor (short rows)
     int chol_fail;           // 1 when the Gram's Cholesky factorization was rejected
-    int rounds_pre;          // rounds_active / pairs_applied at the end of the factor phase
-    int pairs_pre;
+    int pairs_pre;           // pairs_applied at the end of the factor phase
     unsigned int check_off;  // largest |a_p.a_q| / (|a_p| |a_q|) of the final operand (float bits)
     int regram;              // 1 when the certificate failed: polished, its final Gram is redone
     int pad[1];

@@ -615,7 +615,6 @@ __global__ void jac_sweep_end_kernel(const MatDev* __restrict__ mats, MatFlags* 
     const int i = mat_idx[t];
     MatFlags& f = flags[i];
     if (f.done) return;
-    f.rounds_active += 1;
     const int nbm1 = mats[i].nb - 1;
     if (round % nbm1 != nbm1 - 1) return;
     f.sweeps += 1;
