@@ -75,13 +75,13 @@ def copy_calibration(nbytes):
 # on a plain device copy of known size), valid only for the kernel source they
 # were taken on (sha256 of the file); otherwise reported as null.
 TRAFFIC = {
-    "jacobi_gram": {"source": "jacobi.hip", "sha256": "88b66451de2f9d80df5a71b0e9013752e7d434a7ddb5e12d72e2e7509c3f29c2",
-        "bytes_per_launch": 5.5386e+08},
-    "jacobi_apply": {"source": "jacobi.hip", "sha256": "88b66451de2f9d80df5a71b0e9013752e7d434a7ddb5e12d72e2e7509c3f29c2",
-        "bytes_per_launch": 1.27495e+09},
-    "combine_adamw": {"source": "elementwise.hip", "sha256": "bed522873952defbc9da72cf6111d0732fc05759f37af33de11f58df8803dd0c",
-        "bytes_per_launch": 3.11482e+10},
-    "ema": {"source": "elementwise.hip", "sha256": "bed522873952defbc9da72cf6111d0732fc05759f37af33de11f58df8803dd0c",
+    "jacobi_gram": {"source": "jacobi.hip", "sha256": "1cb558c9ab493fbbefc340a5174db7ab53baa92c810f9d478f9de2aa84dafcfc",
+        "bytes_per_launch": 5.80048e+08},
+    "jacobi_apply": {"source": "jacobi.hip", "sha256": "1cb558c9ab493fbbefc340a5174db7ab53baa92c810f9d478f9de2aa84dafcfc",
+        "bytes_per_launch": 1.3231e+09},
+    "combine_adamw": {"source": "elementwise.hip", "sha256": "0c09b9374f97495b495395fa41dedf152598946e324adfa6ca6fe895def28277",
+        "bytes_per_launch": 3.1148e+10},
+    "ema": {"source": "elementwise.hip", "sha256": "0c09b9374f97495b495395fa41dedf152598946e324adfa6ca6fe895def28277",
         "bytes_per_launch": 1.16866e+10},
 }
 

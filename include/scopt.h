@@ -189,9 +189,10 @@ int sc_get_sweep_counts(sc_handle h, int* total, int* factor);
  * handle is bracketed by a pair of HIP events on the launch stream (small
  * host overhead per launch; device timing is unaffected).  Enabling or
  * disabling resets the accumulated totals.  A refresh run with timing on also
- * synchronizes the stream once after its sweeps to read the work counters, and
- * runs all Jacobi rounds on the caller's stream (without timing they are split
- * over two internal streams so that independent matrices overlap). */
+ * synchronizes the stream once after its sweeps to read the work counters,
+ * waits for each convergence poll before queueing more rounds, and runs all
+ * kernels on the caller's stream (without timing the refresh is split over two
+ * internal streams so that independent matrices overlap). */
 int sc_profile(sc_handle h, int enable);
 
 typedef struct {

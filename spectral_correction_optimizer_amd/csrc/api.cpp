@@ -486,10 +486,13 @@ int pipe_round(sc_opt* h, Pipe& p, hipStream_t st) {
 
 // Copy the flags to the pipe's pinned buffer behind the work queued so far and
 // mark the point with an event; the host polls it without blocking the queues.
+// With kernel timing on, the host waits for it at once: no rounds are queued
+// past a pending check, so the launch sequence does not depend on host timing.
 int pipe_poll(sc_opt* h, Pipe& p, hipStream_t st) {
     HIP_TRY(hipMemcpyAsync(p.flags_h, h->flags_d, sizeof(MatFlags) * h->n, hipMemcpyDeviceToHost,
                            st));
     HIP_TRY(hipEventRecord(p.poll, st));
+    if (h->prof.on) HIP_TRY(hipEventSynchronize(p.poll));
     p.poll_pending = true;
     return SC_OK;
 }
