@@ -850,11 +850,13 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
                     for (int sp = 0; sp < ns; ++sp)
                         gi.push_back(GramItem{i, s, sp, sp * sl, std::min(len, (sp + 1) * sl)});
                     si.push_back(SolveItem{i, s, ns});
-                    for (int c = 0; c < (len + kApplyCols - 1) / kApplyCols; ++c)
-                        ai.push_back(ApplyItem{i, s, 0, c});
+                    const int nca = (len + kApplyCols - 1) / kApplyCols;
+                    for (int c = 0; c < nca; c += kApplyRun)
+                        ai.push_back(ApplyItem{i, s, 0, c, std::min(kApplyRun, nca - c)});
                     if (which == LIST_FACTOR && m.klen) continue;  // no V in the factor phase
-                    for (int c = 0; c < (m.kpad + kApplyCols - 1) / kApplyCols; ++c)
-                        ai.push_back(ApplyItem{i, s, 1, c});
+                    const int ncv = (m.kpad + kApplyCols - 1) / kApplyCols;
+                    for (int c = 0; c < ncv; c += kApplyRun)
+                        ai.push_back(ApplyItem{i, s, 1, c, std::min(kApplyRun, ncv - c)});
                 }
             }
             if ((rc = upload(gi, &L.gi, &L.ngi))) return rc;

@@ -10,6 +10,24 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 
+// Raw buffer access (gfx9 buffer resource: 48-bit base, no stride, num_records
+// bytes, the gfx9 default format word): 32-bit byte offsets in VGPRs plus a
+// wave-uniform offset in an SGPR; accesses beyond num_records read zero and
+// write nothing.  kBufNT selects the nontemporal (streaming) cache policy.
+constexpr int kBufNT = 2;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+template <int AUX>
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ void buf_store_f32(float v, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), r, voff, soff, AUX);
+}
+
 // bfloat16 <-> float32.  bf16 is the upper half of an IEEE float32;
 // narrowing rounds to nearest, ties to even (NaN stays NaN).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

@@ -12,6 +12,7 @@ constexpr int kJb = 32;        // Jacobi column-block width b; a pair block hold
 constexpr int kPw = 2 * kJb;   // pair width
 constexpr int kApplyCols = 128;            // columns per rotation-apply workgroup
 constexpr int kApplyThreads = 2 * kApplyCols;  // a 64-lane wave updates 32 columns
+constexpr int kApplyRun = 4;  // column chunks per rotation-apply workgroup (pipelined)
 
 // Caller pointers of one call (weights / gradients), passed by value.
 struct PtrTable {
@@ -78,7 +79,8 @@ struct MatFlags {
 
 struct GramItem { int mat, slot, split, x0, x1; };  // operand columns [x0, x1) of one split
 struct SolveItem { int mat, slot, nsplit; };
-struct ApplyItem { int mat, slot, which, chunk; };  // which: 0 = A rows, 1 = V rows
+// which: 0 = A rows, 1 = V rows; chunks [chunk, chunk + nchunk) of kApplyCols columns
+struct ApplyItem { int mat, slot, which, chunk, nchunk; };
 struct Chunk { int mat; int64_t off; int len; };    // elementwise chunk of one matrix
 struct SyrkItem { int mat, ti, tj; };               // lower 128 x 128 tile (ti >= tj) of A^T A
 

@@ -493,11 +493,13 @@ __global__ __launch_bounds__(kApplyThreads) void jac_apply_kernel(const MatDev* 
                                                         const MatFlags* __restrict__ flags,
                                                         const ApplyItem* __restrict__ items,
                                                         int round) {
-    // A workgroup updates 64 rows x kApplyCols columns; wave w owns columns
-    // [x0 + 32 w, x0 + 32 w + 32).  Only R goes through LDS: each lane loads
-    // 32 rows of its column straight into registers; they are both its MFMA B
-    // operands (B[k][j] = X[b][n] over the contraction order apply_row) and the
-    // old values of its output elements, so X_new = X + R^T X needs no re-read.
+    // A workgroup updates 64 rows over a run of consecutive chunks of
+    // kApplyCols columns; in a chunk, wave w owns columns [x0 + 32 w, x0 + 32 w + 32).
+    // Only R goes through LDS (staged once for the run): each lane loads 32 rows
+    // of its column straight into registers; they are both its MFMA B operands
+    // (B[k][j] = X[b][n] over the contraction order apply_row) and the old values
+    // of its output elements, so X_new = X + R^T X needs no re-read.  The loads
+    // of chunk c + 1 are issued before the MFMAs of chunk c (two register sets).
     __shared__ float Rs[PW][RLD];
     const ApplyItem it = items[blockIdx.x];
     if (flags[it.mat].done) return;
@@ -507,47 +509,61 @@ __global__ __launch_bounds__(kApplyThreads) void jac_apply_kernel(const MatDev* 
     rr_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
     float* base = it.which == 0 ? md.A : md.V;
     const int ld = it.which == 0 ? md.K_ld : md.kpad;  // multiple of 64
-    const int x0 = it.chunk * kApplyCols;
+    // the operand (kpad rows of ld floats) as a buffer; byte offsets: the lane's
+    // row and column in VGPRs, the chunk's first column (wave-uniform) in an SGPR
+    const __amdgpu_buffer_rsrc_t buf = buf_rsrc(base, (uint32_t)md.kpad * ld * 4u);
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hl = lane >> 5, ll = lane & 31;
-    const int n = x0 + wave * 32 + ll;
-    const bool active = x0 + wave * 32 < ld;  // a wave's 32 columns are all in or all out
-    float xb[PW / 2];
-    int prow[PW / 2];  // physical rows (kept as indices: fewer registers than pointers)
+    int voff[PW / 2];
 #pragma unroll
-    for (int s = 0; s < PW / 2; ++s) prow[s] = pair_row(md, bI, bJ, apply_row(s, hl));
-    float* const col = base + n;
-    if (active) {
+    for (int s = 0; s < PW / 2; ++s) voff[s] = (pair_row(md, bI, bJ, apply_row(s, hl)) * ld + ll) * 4;
+    // first column of the wave in chunk c, and whether the wave's 32 columns are
+    // in (they are all in or all out: ld is a multiple of 64)
+    auto col0 = [&](int c) { return (it.chunk + c) * kApplyCols + wave * 32; };
+    auto load = [&](float (&x)[PW / 2], int c) {
+        if (col0(c) >= ld) return;
+        const int so = col0(c) * 4;
 #pragma unroll
-        for (int s = 0; s < PW / 2; ++s)
-            xb[s] = __builtin_nontemporal_load(gptr(col + (int64_t)prow[s] * ld));
-    }
+        for (int s = 0; s < PW / 2; ++s) x[s] = buf_load_f32<kBufNT>(buf, voff[s], so);
+    };
+    auto update = [&](const float (&x)[PW / 2], int c) {
+        if (col0(c) >= ld) return;
+        v16f acc0, acc1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            acc0[r] = 0.0f;
+            acc1[r] = 0.0f;
+        }
+#pragma unroll
+        for (int s = 0; s < PW / 2; ++s) {
+            const int b = apply_row(s, hl);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(Rs[b][ll], x[s], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(Rs[b][32 + ll], x[s], acc1, 0, 0, 0);
+        }
+        // acc0 register r is row apply_row(r, hl), acc1 register r is row apply_row(16 + r, hl)
+        const int so = col0(c) * 4;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            buf_store_f32<kBufNT>(x[r] + acc0[r], buf, voff[r], so);
+            buf_store_f32<kBufNT>(x[16 + r] + acc1[r], buf, voff[16 + r], so);
+        }
+    };
+    float xa[PW / 2], xb[PW / 2];
+    load(xa, 0);
     const float* R = md.rot + (int64_t)it.slot * PW * PW;
     for (int idx = threadIdx.x; idx < PW * PW / 4; idx += kApplyThreads) {
         const int b = idx >> 4, a4 = (idx & 15) * 4;
         *(v4f*)&Rs[b][a4] = gld4(R + b * PW + a4);
     }
     __syncthreads();
-    if (!active) return;
-
-    v16f acc0, acc1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        acc0[r] = 0.0f;
-        acc1[r] = 0.0f;
-    }
-#pragma unroll
-    for (int s = 0; s < PW / 2; ++s) {
-        const int b = apply_row(s, hl);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(Rs[b][ll], xb[s], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(Rs[b][32 + ll], xb[s], acc1, 0, 0, 0);
-    }
-    // acc0 register r is row apply_row(r, hl), acc1 register r is row apply_row(16 + r, hl)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        __builtin_nontemporal_store(xb[r] + acc0[r], gptr(col + (int64_t)prow[r] * ld));
-        __builtin_nontemporal_store(xb[16 + r] + acc1[r], gptr(col + (int64_t)prow[16 + r] * ld));
+    const int n = it.nchunk;
+    for (int c = 0; c < n; c += 2) {
+        if (c + 1 < n) load(xb, c + 1);
+        update(xa, c);
+        if (c + 1 >= n) break;
+        if (c + 2 < n) load(xa, c + 2);
+        update(xb, c + 1);
     }
 }
 
