@@ -4,9 +4,10 @@
 // momentum ("Key design 3" of the papernotes.org notes on "Communication-
 // Efficient LLM Adaptation over Decentralized GPU Meshes").  The operand A
 // (K x k, K >= k; A = M or M^T) is kept as rows = columns of A.  Its k columns
-// are cut into blocks of b = 32; a sweep visits every block pair once in
-// round-robin order (nb - 1 rounds of nb/2 disjoint pairs).  One round is three
-// launches over all pairs of all matrices:
+// are cut into blocks of b = 32; a sweep visits every block pair once in nb - 1
+// rounds of nb/2 disjoint pairs (XOR order for power-of-two nb, round-robin
+// otherwise: block_pair).  One round is three launches over all pairs of all
+// matrices:
 //
 //   gram   per (pair, K split): G_part = X X^T, X = the pair's 64 rows of A,
 //          fp32 MFMA accumulation restarted every 256 columns and summed in
@@ -14,11 +15,11 @@
 //   solve  per pair: sum the split partials in fixed order (fp64), measure the
 //          largest relative off-diagonal |g_pq| / sqrt(g_pp g_qq); if above the
 //          tolerance run one cyclic sweep of 2x2 Jacobi rotations on the 64x64
-//          Gram in LDS (round-robin order, 32 disjoint rotations per step),
-//          accumulating Q; store R = Q - I.
-//   apply  per (pair, 128-column chunk, A or V): X <- X + R^T X on fp32 MFMA.
-//          The correction form keeps the rounding of near-identity rotations
-//          at the level of one addition.
+//          Gram in LDS (circle order in a moving frame, 32 disjoint rotations
+//          per step), accumulating Q; store R = Q - I.
+//   apply  per (pair, run of 128-column chunks, A or V): X <- X + R^T X on fp32
+//          MFMA.  The correction form keeps the rounding of near-identity
+//          rotations at the level of one addition.
 //
 // Every row of A and V belongs to exactly one pair per round, so the kernels
 // of a round never write the same memory from two workgroups.  Reductions run
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
     const MatDev& md = mats[it.mat];
     const int nb = md.nb;
     int bI, bJ;
-    rr_pair(nb, round % (nb - 1), it.slot, &bI, &bJ);
+    block_pair(nb, round % (nb - 1), it.slot, &bI, &bJ);
     const int x_begin = it.x0, x_end = it.x1;
 
     // loader: 64 rows x 32 columns = 512 float4 slots, 2 per thread
@@ -279,7 +280,7 @@ __global__ __launch_bounds__(64) void jac_solve_kernel(const MatDev* __restrict_
     const float tol = md.tol;
     const int l = threadIdx.x;
     int bI, bJ;
-    rr_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
+    block_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
 
     // 1. the pair Gram: split partials summed in fixed order (fp64).  Lane l
     //    takes the diagonal entry of column l and 4 entries of each stored upper
@@ -506,7 +507,7 @@ __global__ __launch_bounds__(kApplyThreads) void jac_apply_kernel(const MatDev* 
     const MatDev& md = mats[it.mat];
     if (md.rot_flag[it.slot] == 0) return;
     int bI, bJ;
-    rr_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
+    block_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
     float* base = it.which == 0 ? md.A : md.V;
     const int ld = it.which == 0 ? md.K_ld : md.kpad;  // multiple of 64
     // the operand (kpad rows of ld floats) as a buffer; byte offsets: the lane's
