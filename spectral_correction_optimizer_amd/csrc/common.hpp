@@ -152,13 +152,14 @@ __device__ __host__ __forceinline__ void rr_pair(int nb, int r, int i, int* p, i
 }
 
 // Block pair of slot i in round r of a sweep over nb blocks.  For nb a power of
-// two: the XOR ordering, round r pairs block p with p ^ (r + 1) (slot i is p with
-// a zero bit inserted at the top bit of r + 1); measured on the workload's
-// operands it needs one or two sweeps fewer than the round-robin ordering, which
-// serves the other block counts.
+// two: the XOR ordering, round r pairs block p with p ^ m, m = nb - 1 - r (slot i
+// is p with a zero bit inserted at the top bit of m): the first round pairs the
+// most distant blocks of the norm order, the last one neighbours.  It needs one
+// or two sweeps fewer than the round-robin ordering, which serves the other
+// block counts, and than the ascending XOR order.
 __device__ __host__ __forceinline__ void block_pair(int nb, int r, int i, int* p, int* q) {
     if ((nb & (nb - 1)) == 0) {
-        const int m = r + 1, h = 31 - __builtin_clz(m);
+        const int m = nb - 1 - r, h = 31 - __builtin_clz(m);
         const int lo = i & ((1 << h) - 1);
         *p = ((i >> h) << (h + 1)) | lo;
         *q = *p ^ m;
