@@ -105,3 +105,100 @@ def test_full_workload_handle_runs_and_is_consistent():
         assert torch.linalg.matrix_norm(gf).item() <= bound * (1 + 1e-5)
         assert e < 1e-5
     opt.close()
+
+
+# Sampled parity at full size on noisy inputs, in the benchmark's launch
+# configuration: all 112 matrices of the 16-block workload in one handle, the
+# sampled ones drawn by the host generator (the oracle gets the identical
+# stored values), the others generated on the device.  One refresh and one
+# step; the oracle runs each sampled matrix on its own.  The float32 samples
+# cover the code paths: square operands (plain sweeps), m < n and m > n
+# (Cholesky factor phase, certificate, polishing for the 512x2048 ones).  The
+# bfloat16 configuration (W, G_mask and G_anc in bfloat16, float32 states) is
+# sampled at the two outer filter strengths.
+NB = len(gen.BLOCK_SHAPES)
+CASES = [("f32", 1e-3, (3, 0)), ("f32", 1e-3, (7, 1)), ("f32", 1e-3, (11, 4)), ("f32", 1e-3, (15, 6)),
+         ("bf16", 1e-4, (5, 3)), ("bf16", 1e-4, (9, 2)), ("bf16", 1e-2, (5, 3)), ("bf16", 1e-2, (9, 2))]
+CASE_IDS = ["f32_q_blk3", "f32_k_blk7", "f32_gate_blk11", "f32_down_blk15",
+            "bf16_tau1e-4_o_blk5", "bf16_tau1e-4_v_blk9", "bf16_tau1e-2_o_blk5", "bf16_tau1e-2_v_blk9"]
+_runs = {}
+
+
+def _sampled_run(dtype, tau):
+    """GPU outputs of the sampled matrices for one (dtype, tau) configuration."""
+    key = (dtype, tau)
+    if key in _runs:
+        return _runs[key]
+    _runs.clear()
+    import spectral_correction_optimizer_amd as sco
+    from gen.device import DeviceMatrixInputs
+    dev = torch.device("cuda")
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    wl = gen.workload("blocks16_1b")
+    hp = dict(gen.DEFAULT_HP, tau_p=tau)
+    picked = sorted({b * NB + m for d, t, (b, m) in CASES if (d, t) == key})
+    say(f"case: 112-matrix workload, {dtype}, tau {tau}, host-generated samples {picked}")
+    opt = sco.SpectralAdamW(wl["shapes"], w_dtype=tdt, g_dtype=tdt, device=dev, **hp)
+    opt.keep_proj(True)
+    W, G, GA, host = [], [], [], {}
+    for idx, ((c, b, m_), (m, n)) in enumerate(zip(wl["ids"], wl["shapes"])):
+        if idx in picked:
+            mi = gen.MatrixInputs(c, b, m_, m, n)
+            m0 = gen.stored(mi.m0(), "f32")
+            ga, gm, w0 = (gen.stored(x, dtype) for x in (mi.g_anc(0), mi.g_mask(0), mi.w0()))
+            host[idx] = (m0[1], ga[1], gm[1], w0[1])
+            opt.set_state(idx, "m_anc", to_dev(m0[0], "f32", dev))
+            GA.append(to_dev(ga[0], dtype, dev))
+            G.append(to_dev(gm[0], dtype, dev))
+            W.append(to_dev(w0[0], dtype, dev))
+        else:
+            mi = DeviceMatrixInputs(c, b, m_, m, n, dev, dtype=tdt)
+            opt.set_state(idx, "m_anc", mi.m0())
+            GA.append(mi.g_anc(0))
+            G.append(mi.g_mask(0))
+            W.append(mi.w0())
+        del mi
+    opt.anchor_update(GA)
+    opt.step(W, G)
+    st = opt.stats()
+    say(f"  GPU pass done: sweeps max {st['sweeps_max']} not_converged {st['not_converged']}")
+    out = {}
+    for idx in picked:
+        gf, gp = opt.get_filtered(idx, proj=True)
+        out[idx] = (from_dev(gf), from_dev(gp), from_dev(W[idx]))
+    opt.close()
+    del W, G, GA
+    torch.cuda.empty_cache()
+    _runs[key] = (wl, hp, host, out, st)
+    return _runs[key]
+
+
+@pytest.mark.parametrize("dtype,tau,sample", CASES, ids=CASE_IDS)
+def test_sampled_noisy_parity_16_blocks(dtype, tau, sample):
+    from tests.gpu_harness import REL_TOL, SMALL_G, W_TOL, bf16_ulp
+    wl, hp, host, out, st = _sampled_run(dtype, tau)
+    idx = sample[0] * NB + sample[1]
+    m, n = wl["shapes"][idx]
+    assert st["not_converged"] == 0
+    M0, GA, GM, W0 = host[idx]
+    ora = oracle.Optimizer([(m, n)], hp, w_dtype=dtype, state_dtype="f32")
+    ora.set_anchor_momentum(0, M0)
+    ora.anchor_update([GA])
+    W1 = ora.step([W0], [GM])[0]
+    gf, gp, w = out[idx]
+    ef, ep = relf(gf, ora.last_filt[0]), relf(gp, ora.last_proj[0])
+    err = np.abs(w - W1)
+    if dtype == "f32":
+        keep = np.abs(ora.last_proj[0]) >= SMALL_G
+        ew, ok_w = float(err[keep].max()), float(err[keep].max()) <= W_TOL
+        wnote = f"W {ew:.3e} (excluded {int((~keep).sum())}, max {float(err[~keep].max()) if (~keep).any() else 0.0:.3e})"
+    else:
+        keep = np.abs(ora.last_proj[0]) >= SMALL_G
+        ulps = err / bf16_ulp(W1)
+        ok_w = float(ulps[keep].max()) <= 1.0
+        bad = ulps > 1.0
+        wnote = (f"W max {float(ulps[keep].max()):.2f} bf16 ulp ({int((ulps > 0).sum())} elements "
+                 f"differ; excluded {int((~keep).sum())}, max {float(ulps[~keep].max()) if (~keep).any() else 0.0:.1f} ulp; "
+                 f"{int(bad.sum())} above 1 ulp, their |G_proj| <= {float(np.abs(ora.last_proj[0])[bad].max()) if bad.any() else 0.0:.2e})")
+    say(f"  mat {idx} {m}x{n}: relF G_filt {ef:.3e} G_proj {ep:.3e} {wnote} oracle sweeps {ora.sweeps[0]}")
+    assert ef <= REL_TOL and ep <= REL_TOL and ok_w
