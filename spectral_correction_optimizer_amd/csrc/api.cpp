@@ -261,10 +261,30 @@ double group_flops(const GemmGroup& g) {
     return f;
 }
 
+// Whether every problem of a group can load its row-major operands (A unless
+// transposed, B if transposed) 8 elements at a time: rows aligned to 16 bytes
+// (8 for bfloat16) and K a multiple of 8.  Caller pointers (a_ptr / b_ptr) are
+// aligned by check_ptrs.
+bool group_vec(const GemmGroup& g, const PtrTable& pt) {
+    for (const GemmProb& p : g.h) {
+        if (p.K % 8) return false;
+        if (!g.ta) {
+            const uintptr_t a = (uintptr_t)(p.a_ptr >= 0 ? pt.p[p.a_ptr] : p.A);
+            if (p.lda % 4 || a % (g.abf ? 8 : 16)) return false;
+        }
+        if (g.tb) {
+            const uintptr_t b = (uintptr_t)(p.b_ptr >= 0 ? pt.p[p.b_ptr] : p.B);
+            if (p.ldb % 4 || b % (g.bbf ? 8 : 16)) return false;
+        }
+    }
+    return true;
+}
+
 int run_group(sc_opt* h, const GemmGroup& g, int kind, const PtrTable& pt, hipStream_t st) {
     if (g.h.empty()) return SC_OK;
+    const bool vec = group_vec(g, pt);
     HIP_TRY(timed(h, kind, st, [&] {
-        return launch_gemm(g.d, (int)g.h.size(), g.total, g.ta, g.tb, g.abf, g.bbf, pt, st);
+        return launch_gemm(g.d, (int)g.h.size(), g.total, g.ta, g.tb, g.abf, g.bbf, vec, pt, st);
     }));
     if (h->prof.on) h->prof.flops[kind] += group_flops(g);
     return SC_OK;

@@ -1,4 +1,5 @@
-// Grouped GEMM on the gfx950 float32 matrix cores (v_mfma_f32_32x32x2_f32).
+// Grouped GEMM on the gfx950 bfloat16 matrix cores with float32-level accuracy
+// (three-way bfloat16 split of each operand, v_mfma_f32_32x32x16_bf16).
 //
 // Used for the two-sided projection X = U^T G V and the reconstruction
 // G_filt = U X_filt V^T ("Key design 3" of the papernotes.org notes on
@@ -9,11 +10,11 @@
 //
 // Tiling: a 256-thread workgroup computes a 128 x 128 tile; its four waves
 // each own 64 x 64 (2 x 2 MFMA blocks of 32 x 32, 64 accumulator registers).
-// K advances in steps of 16 through double-buffered LDS; operand tiles are
-// stored k-major in LDS so each MFMA operand is one conflict-free 32-float
-// row segment per half-wave.  Workgroup ids are remapped so that each XCD
-// (own L2) works on a contiguous range of tiles; tiles are row-major within a
-// problem so consecutive tiles share the A panel.
+// K advances in steps of 16 through double-buffered LDS holding the split
+// operand tiles row-major (k contiguous), so each MFMA operand is one 16-byte
+// read per lane.  Workgroup ids are remapped so that each XCD (own L2) works
+// on a contiguous range of tiles; tiles are row-major within a problem so
+// consecutive tiles share the A panel.
 #include <type_traits>
 
 #include "common.hpp"
@@ -24,127 +25,113 @@ namespace scopt {
 namespace {
 
 constexpr int BM = 128, BN = 128, BK = 16;
-constexpr int LDS_STRIDE = 128 + 32;  // rows k and k+1 land on disjoint bank halves
 
-template <bool TRANS, typename T>
-struct TileLoader;
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-// A operand, not transposed: A[M][K] row-major, tile 128(m) x 16(k).
-// Slot s in [0, 512): row = s >> 2, k4 = s & 3.
-// B operand, transposed: B[N][K]; identical pattern with n in place of m.
-template <typename T>
-struct TileLoader<false, T> {
-    float4 r[2];
-    __device__ void load(const T* __restrict__ p, int ld, int rows, int kdim, int r0, int k0,
-                         bool vec_ok, const float* kscale) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            int s = threadIdx.x + e * 256;
-            int row = r0 + (s >> 2), kk = k0 + 4 * (s & 3);
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (row < rows) {
-                const T* q = p + (int64_t)row * ld + kk;
-                if (vec_ok && kk + 3 < kdim) {
-                    v = load4(q);
-                } else {
-                    if (kk + 0 < kdim) v.x = Elem<T>::load(q, 0);
-                    if (kk + 1 < kdim) v.y = Elem<T>::load(q, 1);
-                    if (kk + 2 < kdim) v.z = Elem<T>::load(q, 2);
-                    if (kk + 3 < kdim) v.w = Elem<T>::load(q, 3);
-                }
-            }
-            (void)kscale;
-            r[e] = v;
-        }
-    }
-    __device__ void store(float (*S)[LDS_STRIDE]) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            int s = threadIdx.x + e * 256;
-            int row = s >> 2, kq = 4 * (s & 3);
-            S[kq + 0][row] = r[e].x;
-            S[kq + 1][row] = r[e].y;
-            S[kq + 2][row] = r[e].z;
-            S[kq + 3][row] = r[e].w;
-        }
-    }
+// Exact three-way split of float32 values into bfloat16 parts, x = hi + mid + lo:
+// hi = RNE(x), mid = RNE(x - hi), lo = x - hi - mid (|x - hi| <= 2^-8 |x| and
+// |mid|, |lo| carry the next 8 and the last <= 8 significant bits; both
+// differences are exact in float32).
+struct Split8 {
+    v8bf h, m, l;
 };
-
-// A operand transposed (stored [K][M]) or B not transposed (B[K][N]):
-// tile 16(k) x 128(m or n). Slot s: k = s >> 5, c4 = s & 31.
-template <typename T>
-struct TileLoader<true, T> {
-    float4 r[2];
-    __device__ void load(const T* __restrict__ p, int ld, int cols, int kdim, int c0, int k0,
-                         bool vec_ok, const float* kscale) {
+__device__ __forceinline__ Split8 split8(const float (&f)[8]) {
+    Split8 s;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            int s = threadIdx.x + e * 256;
-            int kk = k0 + (s >> 5), c = c0 + 4 * (s & 31);
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (kk < kdim) {
-                const T* q = p + (int64_t)kk * ld + c;
-                if (vec_ok && c + 3 < cols) {
-                    v = load4(q);
-                } else {
-                    if (c + 0 < cols) v.x = Elem<T>::load(q, 0);
-                    if (c + 1 < cols) v.y = Elem<T>::load(q, 1);
-                    if (c + 2 < cols) v.z = Elem<T>::load(q, 2);
-                    if (c + 3 < cols) v.w = Elem<T>::load(q, 3);
-                }
-                if (kscale) {
-                    float f = gld(kscale + kk);
-                    v.x *= f;
-                    v.y *= f;
-                    v.z *= f;
-                    v.w *= f;
-                }
-            }
-            r[e] = v;
-        }
+    for (int i = 0; i < 8; ++i) {
+        const __bf16 h = (__bf16)f[i];
+        const float r1 = f[i] - (float)h;
+        const __bf16 m = (__bf16)r1;
+        s.h[i] = h;
+        s.m[i] = m;
+        s.l[i] = (__bf16)(r1 - (float)m);
     }
-    __device__ void store(float (*S)[LDS_STRIDE]) {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            int s = threadIdx.x + e * 256;
-            *(float4*)&S[s >> 5][4 * (s & 31)] = r[e];
-        }
-    }
-};
-
-// Transposed-B loader with a k-scale: the non-transposed-A pattern (rows = n)
-// but each of the 4 k values gets its own factor.
-template <typename T>
-struct TileLoaderRowsK : TileLoader<false, T> {
-    __device__ void load(const T* __restrict__ p, int ld, int rows, int kdim, int r0, int k0,
-                         bool vec_ok, const float* kscale) {
-        TileLoader<false, T>::load(p, ld, rows, kdim, r0, k0, vec_ok, nullptr);
-        if (kscale) {
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                int s = threadIdx.x + e * 256;
-                int kk = k0 + 4 * (s & 3);
-                float4& v = this->r[e];
-                if (kk + 0 < kdim) v.x *= gld(kscale + kk + 0);
-                if (kk + 1 < kdim) v.y *= gld(kscale + kk + 1);
-                if (kk + 2 < kdim) v.z *= gld(kscale + kk + 2);
-                if (kk + 3 < kdim) v.w *= gld(kscale + kk + 3);
-            }
-        }
-    }
-};
-
-__device__ __forceinline__ bool aligned16(const void* p, int elem_bytes) {
-    return ((uintptr_t)p & (uintptr_t)(4 * elem_bytes - 1)) == 0;
+    return s;
 }
+
+// LDS tile of one operand: 3 planes (hi, mid, lo) of 128 rows x 16 k, k
+// contiguous, as two 8-element chunks per row whose order flips with bit 2 of
+// the row: the 16-byte fragment reads of 8 consecutive lanes (8 rows) and the
+// loaders' 16-byte writes then cover all banks once.
+__device__ __forceinline__ int lds_chunk(int row, int half) {
+    return row * BK + ((half ^ ((row >> 2) & 1)) << 3);
+}
+
+// Loader of an operand tile into registers: thread t holds 8 consecutive k
+// values of one tile row (row = m of A or n of B).
+//   KMAJOR = false: the operand is stored [rows][K] (A not transposed, B
+//     transposed): row = t >> 1, k half = t & 1; two 16-byte loads when VEC
+//     (rows 16-byte aligned and K a multiple of 8), else eight element loads.
+//   KMAJOR = true: stored [K][rows] (A transposed, B not transposed): row =
+//     t & 127, k half = t >> 7, eight element loads, each coalesced over 64
+//     consecutive rows.
+// Every load is issued (addresses clamped into the operand; rows, kdim >= 1)
+// and elements outside it are zeroed when the tile is stored, so loading is
+// free of per-lane branches.  KS: the loader also fetches the k scales of its
+// 8 values when the problem has them.
+template <bool KMAJOR, bool VEC, bool KS, typename T>
+struct TileLoader {
+    float v[8], ks[KS ? 8 : 1];
+    int row, half, rr, kk;
+    __device__ void load(const T* __restrict__ p, int ld, int rows, int kdim, int r0, int k0,
+                         const float* kscale, const float* dummy) {
+        row = KMAJOR ? (threadIdx.x & 127) : (threadIdx.x >> 1);
+        half = KMAJOR ? (threadIdx.x >> 7) : (threadIdx.x & 1);
+        rr = r0 + row;
+        kk = k0 + 8 * half;
+        const int rc = min(rr, rows - 1);
+        if (!KMAJOR && VEC) {
+            const T* q = p + (int64_t)rc * ld + min(kk, kdim - 8);
+            const float4 a = load4(q), b = load4(q + 4);
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        } else if (!KMAJOR) {
+            const T* q = p + (int64_t)rc * ld;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = Elem<T>::load(q, min(kk + j, kdim - 1));
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = Elem<T>::load(p, (int64_t)min(kk + j, kdim - 1) * ld + rc);
+        }
+        if (KS && kscale) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ks[j] = gld(kscale + min(kk + j, kdim - 1));
+        }
+        (void)dummy;
+    }
+    __device__ void store(__bf16 (*S)[BM * BK], int rows, int kdim, bool scaled) const {
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float x = (rr < rows && kk + j < kdim) ? v[j] : 0.0f;
+            if (KS && scaled) x *= ks[KS ? j : 0];
+            f[j] = x;
+        }
+        const Split8 s = split8(f);
+        const int o = lds_chunk(row, half);
+        *(v8bf*)&S[0][o] = s.h;
+        *(v8bf*)&S[1][o] = s.m;
+        *(v8bf*)&S[2][o] = s.l;
+    }
+};
+
 
 }  // namespace
 
-template <bool TA, bool TB, typename TEA, typename TEB>
+// C = alpha op(A) op(B) [scales] + beta Cin with float32 operands and outputs.
+// Each operand element is split exactly into three bfloat16 parts and the
+// product is formed from the six largest of the nine part products on the
+// bfloat16 matrix cores (v_mfma_f32_32x32x16_bf16, float32 accumulation); the
+// three dropped ones (mid*lo, lo*mid, lo*lo) are below 2^-23 of |a b|, the
+// order of float32 rounding.  This is the bfloat16 splitting of Henry, Tang and
+// Heinecke ("Leveraging the bfloat16 artificial intelligence datatype for
+// higher-precision computations", 2019); the bfloat16 cores run it 2.7x faster
+// than float32 MFMA for the same float32-level result.
+template <bool TA, bool TB, bool VEC, typename TEA, typename TEB>
 __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __restrict__ probs,
                                                               int nprob, PtrTable ptrs) {
-    __shared__ float As[2][BK][LDS_STRIDE];
-    __shared__ float Bs[2][BK][LDS_STRIDE];
+    __shared__ __align__(16) __bf16 As[2][3][BM * BK];
+    __shared__ __align__(16) __bf16 Bs[2][3][BN * BK];
 
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     int lo = 0, hi = nprob - 1;
@@ -161,20 +148,22 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
     const TEA* __restrict__ Ap = (const TEA*)(P.a_ptr >= 0 ? ptrs.p[P.a_ptr] : P.A);
     const TEB* __restrict__ Bp = (const TEB*)(P.b_ptr >= 0 ? ptrs.p[P.b_ptr] : P.B);
     const float* kscale = P.k_scale;
-    const bool va = (P.lda % 4 == 0) && aligned16(Ap, sizeof(TEA));
-    const bool vb = (P.ldb % 4 == 0) && aligned16(Bp, sizeof(TEB));
 
-    TileLoader<TA, TEA> la;
-    // B: not transposed -> [K][N] k-rows (the "true" pattern); transposed -> [N][K].
-    typename std::conditional<TB, TileLoaderRowsK<TEB>, TileLoader<true, TEB> >::type lb;
-
+    // A: [M][K] unless transposed; B: [K][N] unless transposed ([N][K]).
+    TileLoader<TA, VEC, false, TEA> la;
+    TileLoader<!TB, VEC, true, TEB> lb;
     auto load_tiles = [&](int k0) {
-        la.load(Ap, P.lda, M, K, m0, k0, va, nullptr);
-        lb.load(Bp, P.ldb, N, K, n0, k0, vb, kscale);
+        la.load(Ap, P.lda, M, K, m0, k0, nullptr, nullptr);
+        lb.load(Bp, P.ldb, N, K, n0, k0, kscale, P.C);
+    };
+    auto store_tiles = [&](int buf) {
+        la.store(As[buf], M, K, false);
+        lb.store(Bs[buf], N, K, kscale != nullptr);
     };
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    const int hl = lane >> 5, ll = lane & 31;
     v16f acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -182,31 +171,35 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    // fragment of lane (ll, hl): row ll of a 32-row block, k = 8 hl .. 8 hl + 7
+    const int fa0 = lds_chunk(wm + ll, hl), fa1 = lds_chunk(wm + 32 + ll, hl);
+    const int fb0 = lds_chunk(wn + ll, hl), fb1 = lds_chunk(wn + 32 + ll, hl);
 
     const int nk = (K + BK - 1) / BK;
-    load_tiles(0);
-    la.store(As[0]);
-    lb.store(Bs[0]);
-    __syncthreads();
-    const int hl = lane >> 5, ll = lane & 31;
+    if (nk > 0) {
+        load_tiles(0);
+        store_tiles(0);
+        __syncthreads();
+    }
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
         if (kt + 1 < nk) load_tiles((kt + 1) * BK);
+        v8bf a[2][3], b[2][3];
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 2) {
-            float a0 = As[buf][kk + hl][wm + ll];
-            float a1 = As[buf][kk + hl][wm + 32 + ll];
-            float b0 = Bs[buf][kk + hl][wn + ll];
-            float b1 = Bs[buf][kk + hl][wn + 32 + ll];
-            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+        for (int p = 0; p < 3; ++p) {
+            a[0][p] = *(const v8bf*)&As[buf][p][fa0];
+            a[1][p] = *(const v8bf*)&As[buf][p][fa1];
+            b[0][p] = *(const v8bf*)&Bs[buf][p][fb0];
+            b[1][p] = *(const v8bf*)&Bs[buf][p][fb1];
         }
-        if (kt + 1 < nk) {
-            la.store(As[buf ^ 1]);
-            lb.store(Bs[buf ^ 1]);
-        }
+        // smallest terms first; consecutive products go to different accumulators
+#define SC_TERM(PA, PB)                                                                        \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                               \
+        _Pragma("unroll") for (int j = 0; j < 2; ++j)                                           \
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][PA], b[j][PB], acc[i][j], 0, 0, 0);
+        SC_TERM(2, 0) SC_TERM(1, 1) SC_TERM(0, 2) SC_TERM(1, 0) SC_TERM(0, 1) SC_TERM(0, 0)
+#undef SC_TERM
+        if (kt + 1 < nk) store_tiles(buf ^ 1);
         __syncthreads();
     }
 
@@ -236,21 +229,28 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
 }
 
 hipError_t launch_gemm(const GemmProb* probs_dev, int nprob, int total_tiles, bool ta, bool tb,
-                       bool a_bf16, bool b_bf16, const PtrTable& ptrs, hipStream_t st) {
+                       bool a_bf16, bool b_bf16, bool vec, const PtrTable& ptrs, hipStream_t st) {
     if (nprob <= 0 || total_tiles <= 0) return hipSuccess;
     dim3 grid(total_tiles), blk(256);
-#define SC_GEMM_CASE(TA_, TB_, EA, EB)                                                         \
-    if (ta == TA_ && tb == TB_ && a_bf16 == (sizeof(EA) == 2) && b_bf16 == (sizeof(EB) == 2)) { \
-        hipLaunchKernelGGL((gemm_grouped_kernel<TA_, TB_, EA, EB>), grid, blk, 0, st, probs_dev, \
-                           nprob, ptrs);                                                       \
-        return hipGetLastError();                                                              \
+    if (ta) vec = false;  // a k-major A has no row loads to vectorize
+#define SC_GEMM_CASE(TA_, TB_, V_, EA, EB)                                                      \
+    if (ta == TA_ && tb == TB_ && vec == V_ && a_bf16 == (sizeof(EA) == 2) &&                  \
+        b_bf16 == (sizeof(EB) == 2)) {                                                          \
+        hipLaunchKernelGGL((gemm_grouped_kernel<TA_, TB_, V_, EA, EB>), grid, blk, 0, st,       \
+                           probs_dev, nprob, ptrs);                                             \
+        return hipGetLastError();                                                               \
     }
-    SC_GEMM_CASE(false, false, float, float)
-    SC_GEMM_CASE(false, false, uint16_t, float)
-    SC_GEMM_CASE(false, false, float, uint16_t)
-    SC_GEMM_CASE(false, true, float, float)
-    SC_GEMM_CASE(false, true, uint16_t, float)
-    SC_GEMM_CASE(true, false, float, float)
+    SC_GEMM_CASE(false, false, true, float, float)
+    SC_GEMM_CASE(false, false, false, float, float)
+    SC_GEMM_CASE(false, false, true, uint16_t, float)
+    SC_GEMM_CASE(false, false, false, uint16_t, float)
+    SC_GEMM_CASE(false, false, true, float, uint16_t)
+    SC_GEMM_CASE(false, false, false, float, uint16_t)
+    SC_GEMM_CASE(false, true, true, float, float)
+    SC_GEMM_CASE(false, true, false, float, float)
+    SC_GEMM_CASE(false, true, true, uint16_t, float)
+    SC_GEMM_CASE(false, true, false, uint16_t, float)
+    SC_GEMM_CASE(true, false, false, float, float)
 #undef SC_GEMM_CASE
     return hipErrorInvalidValue;
 }
