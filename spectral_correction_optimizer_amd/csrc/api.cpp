@@ -400,7 +400,10 @@ int pipe_finalize(sc_opt* h, Pipe& p, hipStream_t st) {
 // flops, 4 * 64 * L bytes); per applied pair the update of 64 rows of the operand
 // (length L) and of V (length k), 2 * 64 * 64 * (L + k) flops and
 // 8 * 64 * (L + k) + 4 * 64 * 64 bytes.  In the factor phase L = klen and V is not
-// touched (its k term drops out); otherwise L = K.
+// touched (its k term drops out); otherwise L = K.  Per rotated pair the solve
+// applies one cyclic sweep of 64 * 63 / 2 rotations, each to two rows and two
+// columns of the 64 x 64 Gram and to two rows of R: 18 * 64 flops per rotation
+// (vector ALU work, no HBM traffic).
 void account_sweeps(sc_opt* h) {
     for (int i = 0; i < h->n; ++i) {
         const MatDev& m = h->mh[i];
@@ -416,6 +419,7 @@ void account_sweeps(sc_opt* h) {
             h->prof.flops[PK_GRAM] += rounds[ph] * (m.nb / 2) * 2.0 * pw * pw * len[ph];
             h->prof.bytes[PK_GRAM] += rounds[ph] * (m.nb / 2) * 4.0 * pw * len[ph];
             h->prof.flops[PK_APPLY] += pairs[ph] * 2.0 * pw * pw * (len[ph] + vlen[ph]);
+            h->prof.flops[PK_SOLVE] += pairs[ph] * (pw * (pw - 1) / 2) * 18.0 * pw;
             h->prof.bytes[PK_APPLY] +=
                 pairs[ph] * (8.0 * pw * (len[ph] + vlen[ph]) + 4.0 * pw * pw);
         }
