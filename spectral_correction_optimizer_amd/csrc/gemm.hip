@@ -8,8 +8,8 @@
 // the reduction index, and for the refresh's projector and re-orthogonalization
 // products.  C = alpha * op(A) op(B) [* scales] + beta * Cin, float32 accumulate.
 //
-// Tiling: a 256-thread workgroup computes a 128 x 128 tile; its four waves
-// each own 64 x 64 (2 x 2 MFMA blocks of 32 x 32, 64 accumulator registers).
+// Tiling: a 256-thread workgroup computes a 256 x 128 tile; its four waves
+// each own 128 x 64 (4 x 2 MFMA blocks of 32 x 32, 128 accumulator registers).
 // K advances in steps of 16 through double-buffered LDS holding the split
 // operand tiles row-major (k contiguous), so each MFMA operand is one 16-byte
 // read per lane.  Workgroup ids are remapped so that each XCD (own L2) works
@@ -24,7 +24,7 @@ namespace scopt {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 16;
+constexpr int BM = kGemmBM, BN = kGemmBN, BK = 16;
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
@@ -74,8 +74,8 @@ struct TileLoader {
     float v[8], ks[KS ? 8 : 1];
     int row, half, rr, kk;
     __device__ void load(const T* __restrict__ p, int ld, int rows, int kdim, int r0, int k0,
-                         const float* kscale, const float* dummy) {
-        row = KMAJOR ? (threadIdx.x & 127) : (threadIdx.x >> 1);
+                         const float* kscale, const float* dummy, int roff = 0) {
+        row = roff + (KMAJOR ? (threadIdx.x & 127) : (threadIdx.x >> 1));
         half = KMAJOR ? (threadIdx.x >> 7) : (threadIdx.x & 1);
         rr = r0 + row;
         kk = k0 + 8 * half;
@@ -99,7 +99,8 @@ struct TileLoader {
         }
         (void)dummy;
     }
-    __device__ void store(__bf16 (*S)[BM * BK], int rows, int kdim, bool scaled) const {
+    template <int NR>
+    __device__ void store(__bf16 (*S)[NR * BK], int rows, int kdim, bool scaled) const {
         float f[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -132,6 +133,7 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
                                                               int nprob, PtrTable ptrs) {
     __shared__ __align__(16) __bf16 As[2][3][BM * BK];
     __shared__ __align__(16) __bf16 Bs[2][3][BN * BK];
+    static_assert(BM == 256 && BN == 128, "tile shape of the wave layout below");
 
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     int lo = 0, hi = nprob - 1;
@@ -150,30 +152,37 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
     const float* kscale = P.k_scale;
 
     // A: [M][K] unless transposed; B: [K][N] unless transposed ([N][K]).
-    TileLoader<TA, VEC, false, TEA> la;
+    // A's 256 tile rows take two loaders (rows 0-127 and 128-255).
+    TileLoader<TA, VEC, false, TEA> la0, la1;
     TileLoader<!TB, VEC, true, TEB> lb;
     auto load_tiles = [&](int k0) {
-        la.load(Ap, P.lda, M, K, m0, k0, nullptr, nullptr);
+        la0.load(Ap, P.lda, M, K, m0, k0, nullptr, nullptr, 0);
+        la1.load(Ap, P.lda, M, K, m0, k0, nullptr, nullptr, 128);
         lb.load(Bp, P.ldb, N, K, n0, k0, kscale, P.C);
     };
     auto store_tiles = [&](int buf) {
-        la.store(As[buf], M, K, false);
-        lb.store(Bs[buf], N, K, kscale != nullptr);
+        la0.template store<BM>(As[buf], M, K, false);
+        la1.template store<BM>(As[buf], M, K, false);
+        lb.template store<BN>(Bs[buf], N, K, kscale != nullptr);
     };
 
+    // waves 2 x 2, each 128 (m) x 64 (n): 4 x 2 MFMA blocks of 32 x 32
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    const int wm = (wave >> 1) * 128, wn = (wave & 1) * 64;
     const int hl = lane >> 5, ll = lane & 31;
-    v16f acc[2][2];
+    v16f acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     // fragment of lane (ll, hl): row ll of a 32-row block, k = 8 hl .. 8 hl + 7
-    const int fa0 = lds_chunk(wm + ll, hl), fa1 = lds_chunk(wm + 32 + ll, hl);
-    const int fb0 = lds_chunk(wn + ll, hl), fb1 = lds_chunk(wn + 32 + ll, hl);
+    int fa[4], fb[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = lds_chunk(wm + 32 * i + ll, hl);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[j] = lds_chunk(wn + 32 * j + ll, hl);
 
     const int nk = (K + BK - 1) / BK;
     if (nk > 0) {
@@ -184,17 +193,17 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
         if (kt + 1 < nk) load_tiles((kt + 1) * BK);
-        v8bf a[2][3], b[2][3];
+        v8bf a[4][3], b[2][3];
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
-            a[0][p] = *(const v8bf*)&As[buf][p][fa0];
-            a[1][p] = *(const v8bf*)&As[buf][p][fa1];
-            b[0][p] = *(const v8bf*)&Bs[buf][p][fb0];
-            b[1][p] = *(const v8bf*)&Bs[buf][p][fb1];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i][p] = *(const v8bf*)&As[buf][p][fa[i]];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) b[j][p] = *(const v8bf*)&Bs[buf][p][fb[j]];
         }
         // smallest terms first; consecutive products go to different accumulators
 #define SC_TERM(PA, PB)                                                                        \
-    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                               \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                               \
         _Pragma("unroll") for (int j = 0; j < 2; ++j)                                           \
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][PA], b[j][PB], acc[i][j], 0, 0, 0);
         SC_TERM(2, 0) SC_TERM(1, 1) SC_TERM(0, 2) SC_TERM(1, 0) SC_TERM(0, 1) SC_TERM(0, 0)
@@ -208,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
     const float alpha = P.alpha, beta = P.beta;
     const bool zdiag = (P.flags & GF_ZERO_DIAG) != 0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int col = n0 + wn + 32 * j + ll;

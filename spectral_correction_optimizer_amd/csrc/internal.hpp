@@ -112,7 +112,7 @@ struct GemmProb {
 // ptrs: caller pointers referenced by a_ptr/b_ptr.
 hipError_t launch_gemm(const GemmProb* probs_dev, int nprob, int total_tiles, bool ta, bool tb,
                        bool a_bf16, bool b_bf16, bool vec, const PtrTable& ptrs, hipStream_t st);
-constexpr int kGemmBM = 128, kGemmBN = 128;
+constexpr int kGemmBM = 256, kGemmBN = 128;
 
 // ---- elementwise -------------------------------------------------------------------
 
