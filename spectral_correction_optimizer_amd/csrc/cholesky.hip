@@ -46,19 +46,21 @@ __device__ __forceinline__ bool chol_active(const MatDev& md, const MatFlags& f,
 // ---------------------------------------------------------------------------------
 // C = A^T A over the rows of the Jacobi operand (row j = column j of A, length
 // K_ld, zero padded).  One workgroup per lower 128 x 128 tile (ti >= tj); four
-// waves of 64 x 64, each 2 x 2 v_mfma_f32_32x32x2f32 blocks.  LDS holds 32
-// columns of both row strips k-major (row stride 160 floats) with the row index
-// XOR-swizzled by 8 * ((k >> 2) & 7): the transposing stores and the fragment
-// reads are both free of bank conflicts.  The diagonal tiles read one strip.
+// waves of 64 x 64, each 2 x 2 blocks of v_mfma_f32_32x32x16_bf16 over the
+// exact three-way bfloat16 split of the operand (six part products, float32
+// accumulation, the dropped ones below 2^-23 of each product).  K advances by 16
+// columns through double-buffered LDS holding the split rows of both strips
+// (the diagonal tiles read one strip); the float32 accumulators are folded into
+// float64 every 256 columns.
 namespace {
-constexpr int SB = 128, SK = 32, SLD = 160, SFOLD = 256;
+constexpr int SB = 128, SKB = 16, SFOLD = 256;
 }
 
 __global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict__ mats,
                                                         const MatFlags* __restrict__ flags,
                                                         const SyrkItem* __restrict__ items,
                                                         int only_regram) {
-    __shared__ float Xs[2][SK][SLD];
+    __shared__ __align__(16) __bf16 Xs[2][2][3][SB * SKB];  // [buffer][strip][plane]
     const SyrkItem it = items[blockIdx.x];
     if (only_regram && !flags[it.mat].regram) return;
     const MatDev& md = mats[it.mat];
@@ -66,36 +68,34 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict
     const int k = md.k, ld = md.K_ld;
     const int r0[2] = {it.ti * SB, it.tj * SB};
 
-    // loader: 128 rows x 32 columns = 1024 float4 per strip, 4 per thread;
-    // slot s: row = s >> 3, q = s & 7 (columns 4q .. 4q + 3 of the stage)
+    // loader: thread t holds 8 consecutive columns (half t & 1 of the step's 16)
+    // of strip row t >> 1; rows at or beyond k read as zero
     const int nstrip = diag ? 1 : 2;
-    float4 reg[2][4];
+    const int lrow = threadIdx.x >> 1, lhalf = threadIdx.x & 1;
+    float4 reg[2][2];
     auto gload = [&](int x0) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             if (t >= nstrip) break;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int s = threadIdx.x + 256 * e;
-                const int row = r0[t] + (s >> 3), q = s & 7;
-                reg[t][e] = row < k ? load4(md.A + (int64_t)row * ld + x0 + 4 * q)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+            const int row = r0[t] + lrow;
+            const float* q = md.A + (int64_t)min(row, k - 1) * ld + x0 + 8 * lhalf;
+            reg[t][0] = load4(q);
+            reg[t][1] = load4(q + 4);
         }
     };
-    auto lstore = [&]() {
+    auto lstore = [&](int buf) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             if (t >= nstrip) break;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int s = threadIdx.x + 256 * e;
-                const int q = s & 7, col = (s >> 3) ^ (8 * q);
-                Xs[t][4 * q + 0][col] = reg[t][e].x;
-                Xs[t][4 * q + 1][col] = reg[t][e].y;
-                Xs[t][4 * q + 2][col] = reg[t][e].z;
-                Xs[t][4 * q + 3][col] = reg[t][e].w;
-            }
+            const bool in = r0[t] + lrow < k;
+            const float f[8] = {in ? reg[t][0].x : 0.f, in ? reg[t][0].y : 0.f, in ? reg[t][0].z : 0.f,
+                                in ? reg[t][0].w : 0.f, in ? reg[t][1].x : 0.f, in ? reg[t][1].y : 0.f,
+                                in ? reg[t][1].z : 0.f, in ? reg[t][1].w : 0.f};
+            const Split8 sp = split8(f);
+            const int o = split_chunk16(lrow, lhalf);
+            *(v8bf*)&Xs[buf][t][0][o] = sp.h;
+            *(v8bf*)&Xs[buf][t][1][o] = sp.m;
+            *(v8bf*)&Xs[buf][t][2][o] = sp.l;
         }
     };
 
@@ -103,6 +103,8 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict
     const int hl = lane >> 5, ll = lane & 31;
     const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;
     const int sj = diag ? 0 : 1;
+    const int fa0 = split_chunk16(wr + ll, hl), fa1 = split_chunk16(wr + 32 + ll, hl);
+    const int fb0 = split_chunk16(wc + ll, hl), fb1 = split_chunk16(wc + 32 + ll, hl);
     v16f acc[2][2];
     double acc64[2][2][16];
 #pragma unroll
@@ -114,46 +116,51 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict
                 acc[a][b][r] = 0.0f;
                 acc64[a][b][r] = 0.0;
             }
-    const int nst = ld / SK;  // K_ld is a multiple of 128
+    const int nst = ld / SKB;  // K_ld is a multiple of 128
     gload(0);
+    lstore(0);
+    __syncthreads();
     for (int st = 0; st < nst; ++st) {
-        lstore();
-        __syncthreads();
-        if (st + 1 < nst) gload((st + 1) * SK);
+        const int buf = st & 1;
+        if (st + 1 < nst) gload((st + 1) * SKB);
+        v8bf a[2][3], b[2][3];
 #pragma unroll
-        for (int kk = 0; kk < SK; kk += 2) {
-            const int kr = kk + hl;
-            const int sw = 8 * ((kk >> 2) & 7);
-            const float a0 = Xs[0][kr][(wr + ll) ^ sw], a1 = Xs[0][kr][(wr + 32 + ll) ^ sw];
-            const float b0 = Xs[sj][kr][(wc + ll) ^ sw], b1 = Xs[sj][kr][(wc + 32 + ll) ^ sw];
-            acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-            acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-            acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-            acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+        for (int p = 0; p < 3; ++p) {
+            a[0][p] = *(const v8bf*)&Xs[buf][0][p][fa0];
+            a[1][p] = *(const v8bf*)&Xs[buf][0][p][fa1];
+            b[0][p] = *(const v8bf*)&Xs[buf][sj][p][fb0];
+            b[1][p] = *(const v8bf*)&Xs[buf][sj][p][fb1];
         }
-        if (((st + 1) * SK) % SFOLD == 0 || st + 1 == nst) {
+#define SC_TERM(PA, PB)                                                                        \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                               \
+        _Pragma("unroll") for (int j = 0; j < 2; ++j)                                           \
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][PA], b[j][PB], acc[i][j], 0, 0, 0);
+        SC_TERM(2, 0) SC_TERM(1, 1) SC_TERM(0, 2) SC_TERM(1, 0) SC_TERM(0, 1) SC_TERM(0, 0)
+#undef SC_TERM
+        if (((st + 1) * SKB) % SFOLD == 0 || st + 1 == nst) {
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
+                for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        acc64[a][b][r] += (double)acc[a][b][r];
-                        acc[a][b][r] = 0.0f;
+                        acc64[a2][b2][r] += (double)acc[a2][b2][r];
+                        acc[a2][b2][r] = 0.0f;
                     }
         }
+        if (st + 1 < nst) lstore(buf ^ 1);
         __syncthreads();
     }
     // 32x32 output layout: lane l, register r -> row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = r0[0] + wr + 32 * a + 8 * (r >> 2) + 4 * hl + (r & 3);
-                const int col = r0[1] + wc + 32 * b + ll;
-                if (row < k && col < k) gst(md.chol + (int64_t)row * k + col, acc64[a][b][r]);
+                const int row = r0[0] + wr + 32 * a2 + 8 * (r >> 2) + 4 * hl + (r & 3);
+                const int col = r0[1] + wc + 32 * b2 + ll;
+                if (row < k && col < k) gst(md.chol + (int64_t)row * k + col, acc64[a2][b2][r]);
             }
 }
 

@@ -168,4 +168,37 @@ __device__ __host__ __forceinline__ void block_pair(int nb, int r, int i, int* p
     }
 }
 
+// ---- float32 products on the bfloat16 matrix cores -------------------------------
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// Exact three-way split of float32 values into bfloat16 parts, x = hi + mid + lo:
+// hi = RNE(x), mid = RNE(x - hi), lo = x - hi - mid (|x - hi| <= 2^-8 |x|; mid
+// and lo carry the next 8 and the last <= 8 significant bits; both differences
+// are exact in float32).  Of the nine part products of a * b the six largest
+// (hh, hm, mh, hl, lh, mm) leave out less than 2^-23 |a b|.
+struct Split8 {
+    v8bf h, m, l;
+};
+__device__ __forceinline__ Split8 split8(const float (&f)[8]) {
+    Split8 s;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const __bf16 h = (__bf16)f[i];
+        const float r1 = f[i] - (float)h;
+        const __bf16 m = (__bf16)r1;
+        s.h[i] = h;
+        s.m[i] = m;
+        s.l[i] = (__bf16)(r1 - (float)m);
+    }
+    return s;
+}
+
+// LDS layout of a split operand tile: per plane, rows of 16 k (k contiguous) as
+// two 8-element chunks whose order flips with bit 2 of the row, so the 16-byte
+// MFMA fragment reads of 8 consecutive lanes (8 rows) and the loaders' 16-byte
+// writes cover all banks once.  Element offset of chunk `half` of `row`.
+__device__ __forceinline__ int split_chunk16(int row, int half) {
+    return row * 16 + ((half ^ ((row >> 2) & 1)) << 3);
+}
+
 }  // namespace scopt

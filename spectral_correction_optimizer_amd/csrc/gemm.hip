@@ -25,37 +25,7 @@ namespace scopt {
 namespace {
 
 constexpr int BM = kGemmBM, BN = kGemmBN, BK = 16;
-
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-
-// Exact three-way split of float32 values into bfloat16 parts, x = hi + mid + lo:
-// hi = RNE(x), mid = RNE(x - hi), lo = x - hi - mid (|x - hi| <= 2^-8 |x| and
-// |mid|, |lo| carry the next 8 and the last <= 8 significant bits; both
-// differences are exact in float32).
-struct Split8 {
-    v8bf h, m, l;
-};
-__device__ __forceinline__ Split8 split8(const float (&f)[8]) {
-    Split8 s;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const __bf16 h = (__bf16)f[i];
-        const float r1 = f[i] - (float)h;
-        const __bf16 m = (__bf16)r1;
-        s.h[i] = h;
-        s.m[i] = m;
-        s.l[i] = (__bf16)(r1 - (float)m);
-    }
-    return s;
-}
-
-// LDS tile of one operand: 3 planes (hi, mid, lo) of 128 rows x 16 k, k
-// contiguous, as two 8-element chunks per row whose order flips with bit 2 of
-// the row: the 16-byte fragment reads of 8 consecutive lanes (8 rows) and the
-// loaders' 16-byte writes then cover all banks once.
-__device__ __forceinline__ int lds_chunk(int row, int half) {
-    return row * BK + ((half ^ ((row >> 2) & 1)) << 3);
-}
+static_assert(BK == 16, "split_chunk16 lays out 16 k per row");
 
 // Loader of an operand tile into registers: thread t holds 8 consecutive k
 // values of one tile row (row = m of A or n of B).
@@ -109,7 +79,7 @@ struct TileLoader {
             f[j] = x;
         }
         const Split8 s = split8(f);
-        const int o = lds_chunk(row, half);
+        const int o = split_chunk16(row, half);
         *(v8bf*)&S[0][o] = s.h;
         *(v8bf*)&S[1][o] = s.m;
         *(v8bf*)&S[2][o] = s.l;
@@ -180,9 +150,9 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
     // fragment of lane (ll, hl): row ll of a 32-row block, k = 8 hl .. 8 hl + 7
     int fa[4], fb[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[i] = lds_chunk(wm + 32 * i + ll, hl);
+    for (int i = 0; i < 4; ++i) fa[i] = split_chunk16(wm + 32 * i + ll, hl);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) fb[j] = lds_chunk(wn + 32 * j + ll, hl);
+    for (int j = 0; j < 2; ++j) fb[j] = split_chunk16(wn + 32 * j + ll, hl);
 
     const int nk = (K + BK - 1) / BK;
     if (nk > 0) {
