@@ -49,6 +49,9 @@ def parse():
                     help="time kernels inside the timed region itself (serializes the two "
                          "Jacobi streams) instead of in one extra pass after it")
     ap.add_argument("--max-sweeps", type=int, default=30)
+    ap.add_argument("--async-refresh", type=int, default=0, metavar="N",
+                    help="also time N steps alone and N steps issued beside an asynchronous "
+                         "refresh (sc_anchor_update_async ... sc_refresh_wait)")
     ap.add_argument("--no-precondition", action="store_true",
                     help="plain Jacobi sweeps for every matrix (no Cholesky factor phase)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -146,6 +149,41 @@ def cpu_baseline(hp):
                        f"(chain flops) to the 112-matrix pass; extrapolated")}
 
 
+def async_measure(opt, W, g_anc, G_mask, n):
+    """n steps alone, then n steps issued beside an asynchronous refresh: the
+    steps' HIP-event times and the wall time from the asynchronous call to the
+    completed refresh (all on the caller's stream)."""
+    import torch
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    alone = []
+    for j in range(n):
+        a, b = mk(), mk()
+        a.record()
+        opt.step(W, G_mask[j % len(G_mask)])
+        b.record()
+        alone.append((a, b))
+    torch.cuda.synchronize()
+    t_alone = [a.elapsed_time(b) for a, b in alone]
+    start, end = mk(), mk()
+    during = []
+    start.record()
+    opt.anchor_update_async(g_anc)
+    for j in range(n):
+        a, b = mk(), mk()
+        a.record()
+        opt.step(W, G_mask[j % len(G_mask)])
+        b.record()
+        during.append((a, b))
+    opt.refresh_wait()
+    end.record()
+    torch.cuda.synchronize()
+    t_during = [a.elapsed_time(b) for a, b in during]
+    return {"steps": n, "step_ms_alone": round(statistics.median(t_alone), 3),
+            "step_ms_beside_refresh": round(statistics.median(t_during), 3),
+            "step_ms_beside_refresh_max": round(max(t_during), 3),
+            "wall_ms": round(start.elapsed_time(end), 2)}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -236,6 +274,9 @@ def main():
         opt.step(W, G_mask[k])
         kt = opt.kernel_times()
         opt.profile(False)
+    async_info = None
+    if args.async_refresh > 0:
+        async_info = async_measure(opt, W, G_anc[-1], G_mask, args.async_refresh)
     sweeps_by_shape, factor_by_shape = {}, {}
     for (m, n), sw, fs in zip(shapes, st["sweeps"], st["factor_sweeps"]):
         key = f"{m}x{n}"
@@ -313,6 +354,9 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
     }
+    if async_info is not None:
+        async_info["sequential_ms"] = round(r_med + args.async_refresh * async_info["step_ms_alone"], 2)
+        out["async_refresh"] = async_info
     print(json.dumps(out), flush=True)
     opt.close()
 

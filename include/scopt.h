@@ -112,6 +112,38 @@ int sc_anchor_update(sc_handle h, const void* const* G_anc, void* stream);
  * momentum; sc_step calls it by itself when the factors are stale). */
 int sc_refresh(sc_handle h, void* stream);
 
+/* Asynchronous anchor arrival: the same EMA and refresh as sc_anchor_update,
+ * run beside the steps that follow, so that the refresh stays off their
+ * critical path ("Key design 2": the anchor circuit runs beside the fast
+ * replicas).  The EMA and the refresh are ordered after the work already queued
+ * on `stream` and run on the library's internal streams, driven by a host
+ * thread of the library; the call returns at once (`stream` only waits for a
+ * device copy of the operands the steps use).  Until the refresh is completed
+ * by sc_refresh_wait, every sc_step uses the factors, filter and projectors of
+ * the previous refresh (tau as set at this call), however far the refresh has
+ * got: which factors a step uses never depends on timing.  sc_refresh_wait
+ * orders its stream after the refresh and switches the following steps to the
+ * new factors; every other entry point except sc_step, sc_set_lr,
+ * sc_set_step, sc_get_step and sc_refresh_pending completes a pending refresh
+ * the same way first (with a host wait where it takes no stream).
+ * G_anc: as for sc_anchor_update; the matrices must stay valid and unchanged
+ * until the refresh has been completed.  A second call while one is pending
+ * completes the pending one first.  SC_ERR_INVALID_ARG while kernel timing is on
+ * (sc_profile).  The copy of the step operands takes about as much device
+ * memory as the weights (allocated at the first call, kept by the handle). */
+int sc_anchor_update_async(sc_handle h, const void* const* G_anc, void* stream);
+
+/* Complete a pending asynchronous refresh: join the library's host thread (it
+ * returns once the refresh is fully queued), make `stream` wait for the
+ * refresh's device work, and switch later steps to its factors; reports the
+ * refresh's error, if any.  SC_OK when none is pending. */
+int sc_refresh_wait(sc_handle h, void* stream);
+
+/* *pending = 1 while the host thread of a pending asynchronous refresh is still
+ * queueing it, else 0 (then sc_refresh_wait returns without blocking the host;
+ * the device work may still be running). */
+int sc_refresh_pending(sc_handle h, int* pending);
+
 /* One optimizer step ("Key design 3" and AdamW): for every matrix i
  *   G_filt = U diag(d) (U^T G V) diag(d) V^T,  G_proj = alpha G + (1-alpha) G_filt,
  *   t <- t + 1; AdamW(W_i, G_proj) in place.

@@ -28,7 +28,7 @@ _lib = None
 
 EXPORTED_SYMBOLS = (
     "sc_default_hparams", "sc_opt_create", "sc_opt_destroy", "sc_anchor_update", "sc_refresh",
-    "sc_step", "sc_set_lr", "sc_set_tau", "sc_set_state", "sc_get_state", "sc_set_step",
+    "sc_anchor_update_async", "sc_refresh_wait", "sc_refresh_pending", "sc_step", "sc_set_lr", "sc_set_tau", "sc_set_state", "sc_get_state", "sc_set_step",
     "sc_get_step", "sc_set_factors", "sc_get_factors", "sc_keep_proj", "sc_get_filtered",
     "sc_get_stats", "sc_get_sweep_counts", "sc_profile", "sc_get_kernel_times", "sc_last_error",
 )
@@ -85,6 +85,9 @@ def load_library():
         "sc_opt_destroy": (ctypes.c_int, [vp]),
         "sc_anchor_update": (ctypes.c_int, [vp, ctypes.POINTER(vp), vp]),
         "sc_refresh": (ctypes.c_int, [vp, vp]),
+        "sc_anchor_update_async": (ctypes.c_int, [vp, ctypes.POINTER(vp), vp]),
+        "sc_refresh_wait": (ctypes.c_int, [vp, vp]),
+        "sc_refresh_pending": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_int)]),
         "sc_step": (ctypes.c_int, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp]),
         "sc_set_lr": (ctypes.c_int, [vp, ctypes.c_float]),
         "sc_set_tau": (ctypes.c_int, [vp, ctypes.c_float]),
@@ -191,6 +194,23 @@ class SpectralAdamW:
 
     def refresh(self):
         _check(self._lib.sc_refresh(self._h, self._stream()))
+
+    def anchor_update_async(self, G_anc):
+        """EMA with G_anc and SVD refresh beside the following steps, which use the
+        previous factors until refresh_wait().  G_anc must stay valid and
+        unchanged until then."""
+        _check(self._lib.sc_anchor_update_async(self._h, self._ptrs(G_anc, self.g_dtype, "G_anc"),
+                                                self._stream()))
+
+    def refresh_wait(self):
+        """Complete a pending asynchronous refresh: the current stream waits for it
+        and later steps use its factors."""
+        _check(self._lib.sc_refresh_wait(self._h, self._stream()))
+
+    def refresh_pending(self) -> bool:
+        p = ctypes.c_int()
+        _check(self._lib.sc_refresh_pending(self._h, ctypes.byref(p)))
+        return bool(p.value)
 
     def step(self, W, G_mask):
         """One spectral-corrected AdamW step; W is updated in place."""

@@ -10,12 +10,14 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <new>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "internal.hpp"
@@ -175,8 +177,26 @@ struct sc_opt {
     int npipes = 0;
     hipEvent_t fork = nullptr;
     bool have_factors = false;   // W holds orthonormal rows from a refresh / sc_set_factors
-    // step GEMMs
-    GemmGroup s1_nn_a, s1_nn_b, s1_nt, s2_nn, s3_tn, s3_nn;
+    // step GEMMs: [0] read the refresh's step operands (F, P_L, P_R, d); [1] read
+    // the copy published when an asynchronous refresh starts
+    GemmGroup step[2][6];
+    // asynchronous refresh (sc_anchor_update_async): a host worker thread drives
+    // the refresh on the internal streams behind `astream`; steps issued until
+    // sc_refresh_wait (or another entry point) completes it use step[1] on the
+    // published operands; completion joins the worker and makes the caller's
+    // stream wait for a_done
+    struct PubBuf {
+        float *F, *PL, *PR, *d;
+    };
+    std::vector<PubBuf> pub;
+    char* pub_arena = nullptr;
+    hipStream_t astream = nullptr;
+    hipEvent_t a_ready = nullptr, a_pub = nullptr, a_done = nullptr;
+    std::thread worker;
+    std::atomic<bool> a_finished{false};
+    bool a_pending = false;
+    int a_rc = 0;
+    std::string a_err;
     int64_t t = 0;
     int refreshes = 0;
     std::vector<char> stale;
@@ -665,7 +685,139 @@ int do_refresh(sc_opt* h, hipStream_t st) {
     return SC_OK;
 }
 
+// ---- asynchronous refresh ---------------------------------------------------------------
+
+int build_step_groups(sc_opt* h, int set);
+
+// Published copy of the step operands (F, P_L, P_R, d), the step tables that
+// read it, and the stream and events of the asynchronous refresh; allocated at
+// the first sc_anchor_update_async.
+int ensure_async(sc_opt* h) {
+    if (h->pub_arena) return SC_OK;
+    const size_t f = sizeof(float);
+    std::vector<size_t> off(4 * (size_t)h->n);
+    size_t total = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = total;
+        total += align_up(bytes, 256);
+        return o;
+    };
+    for (int i = 0; i < h->n; ++i) {
+        const MatDev& m = h->mh[i];
+        off[4 * i + 0] = take((size_t)m.k * m.K_ld * f);
+        off[4 * i + 1] = take(m.PL ? (size_t)m.m * m.m * f : 0);
+        off[4 * i + 2] = take(m.PR ? (size_t)m.n * m.n * f : 0);
+        off[4 * i + 3] = take((size_t)m.kpad * f);
+    }
+    void* a = nullptr;
+    if (hipMalloc(&a, total) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(SC_ERR_OOM, "device allocation of %zu bytes (published step operands) failed", total);
+    }
+    h->pub_arena = (char*)a;
+    HIP_TRY(hipMemset(h->pub_arena, 0, total));
+    h->pub.resize(h->n);
+    for (int i = 0; i < h->n; ++i) {
+        const MatDev& m = h->mh[i];
+        h->pub[i].F = (float*)(h->pub_arena + off[4 * i + 0]);
+        h->pub[i].PL = m.PL ? (float*)(h->pub_arena + off[4 * i + 1]) : nullptr;
+        h->pub[i].PR = m.PR ? (float*)(h->pub_arena + off[4 * i + 2]) : nullptr;
+        h->pub[i].d = (float*)(h->pub_arena + off[4 * i + 3]);
+    }
+    HIP_TRY(hipStreamCreateWithFlags(&h->astream, hipStreamNonBlocking));
+    HIP_TRY(hipEventCreateWithFlags(&h->a_ready, hipEventDisableTiming));
+    HIP_TRY(hipEventCreateWithFlags(&h->a_pub, hipEventDisableTiming));
+    HIP_TRY(hipEventCreateWithFlags(&h->a_done, hipEventDisableTiming));
+    return build_step_groups(h, 1);
+}
+
+// Copy the step operands in use into the published set (stream st).
+int publish_step_operands(sc_opt* h, hipStream_t st) {
+    const size_t f = sizeof(float);
+    for (int i = 0; i < h->n; ++i) {
+        const MatDev& m = h->mh[i];
+        HIP_TRY(hipMemcpyAsync(h->pub[i].F, m.F, (size_t)m.k * m.K_ld * f, hipMemcpyDeviceToDevice, st));
+        if (m.PL)
+            HIP_TRY(hipMemcpyAsync(h->pub[i].PL, m.PL, (size_t)m.m * m.m * f, hipMemcpyDeviceToDevice, st));
+        if (m.PR)
+            HIP_TRY(hipMemcpyAsync(h->pub[i].PR, m.PR, (size_t)m.n * m.n * f, hipMemcpyDeviceToDevice, st));
+        HIP_TRY(hipMemcpyAsync(h->pub[i].d, m.d, (size_t)m.kpad * f, hipMemcpyDeviceToDevice, st));
+    }
+    return SC_OK;
+}
+
+// End an asynchronous refresh: join its host thread (which returns once the
+// whole refresh is queued), then order stream st after it (host_wait: block the
+// host until it has run) and report its result.  No-op when none is pending.
+int finish_async(sc_opt* h, hipStream_t st, bool host_wait) {
+    if (!h->a_pending) return SC_OK;
+    h->worker.join();
+    h->a_pending = false;
+    if (h->a_rc != SC_OK) {
+        g_err = h->a_err;
+        return h->a_rc;
+    }
+    if (host_wait)
+        HIP_TRY(hipEventSynchronize(h->a_done));
+    else
+        HIP_TRY(hipStreamWaitEvent(st, h->a_done, 0));
+    return SC_OK;
+}
+
 // ---- construction -------------------------------------------------------------------------
+
+// Step GEMM tables of one operand set: set 0 reads the refresh's F, P_L, P_R
+// and d, set 1 the copy published for an asynchronous refresh.  Executed chain
+// (fewer flops than U D U^T G V D V^T left to right): square G_filt = P_L (G P_R);
+// tall G_filt = F^T ((D F G) P_R); wide G_filt = (P_L (G F^T D)) F.
+int build_step_groups(sc_opt* h, int set) {
+    GemmGroup* g = h->step[set];
+    for (int q = 0; q < 6; ++q) g[q] = GemmGroup{};
+    const bool gbf = h->gdt == SC_BF16;
+    g[0].abf = gbf;  // square: A = G
+    g[1].bbf = gbf;  // tall: B = G
+    g[2].tb = true;  // wide: A = G, B = F^T
+    g[2].abf = gbf;
+    g[4].ta = true;
+    for (int i = 0; i < h->n; ++i) {
+        const MatDev& m = h->mh[i];
+        const float* F = set ? h->pub[i].F : m.F;
+        const float* PL = set ? h->pub[i].PL : m.PL;
+        const float* PR = set ? h->pub[i].PR : m.PR;
+        const float* d = set ? h->pub[i].d : m.d;
+        GemmProb p;
+        if (m.m == m.n) {
+            p = make_prob(nullptr, m.n, PR, m.n, m.T, m.n, m.m, m.n, m.n);  // T = G P_R
+            p.a_ptr = i;
+            g[0].h.push_back(p);
+            p = make_prob(PL, m.m, m.T, m.n, m.Gfilt, m.n, m.m, m.n, m.m);  // G_filt = P_L T
+            g[3].h.push_back(p);
+        } else if (m.tall) {
+            p = make_prob(F, m.K_ld, nullptr, m.n, m.Y, m.k, m.k, m.n, m.m);  // Y = D F G
+            p.b_ptr = i;
+            p.row_scale = d;
+            g[1].h.push_back(p);
+            p = make_prob(m.Y, m.k, PR, m.n, m.T, m.k, m.k, m.n, m.n);  // T = Y P_R
+            g[3].h.push_back(p);
+            p = make_prob(F, m.K_ld, m.T, m.k, m.Gfilt, m.n, m.m, m.n, m.k);  // G_filt = F^T T
+            g[4].h.push_back(p);
+        } else {
+            p = make_prob(nullptr, m.n, F, m.K_ld, m.Y, m.k, m.m, m.k, m.n);  // Y = G F^T D
+            p.a_ptr = i;
+            p.col_scale = d;
+            g[2].h.push_back(p);
+            p = make_prob(PL, m.m, m.Y, m.k, m.T, m.k, m.m, m.k, m.m);  // T = P_L Y
+            g[3].h.push_back(p);
+            p = make_prob(m.T, m.k, F, m.K_ld, m.Gfilt, m.n, m.m, m.n, m.k);  // G_filt = T F
+            g[5].h.push_back(p);
+        }
+    }
+    int rc;
+    for (int q = 0; q < 6; ++q)
+        if ((rc = upload_group(h, g[q]))) return rc;
+    return SC_OK;
+}
+
 
 int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
     const int n = h->n;
@@ -679,8 +831,8 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         return o;
     };
     struct Offs {
-        size_t Manc, madam, vadam, A, V, F, W, PL, PR, s, d, norm2, Gfilt, Y, T, E, gram, rot, rflag,
-            perm, cnorm, chol;
+        size_t Manc, madam, vadam, A, V, F, W, PL, PR, s, d, norm2, Gfilt, Y, T, E, invn, gram, rot,
+            rflag, perm, cnorm, chol;
     };
     std::vector<Offs> o(n);
     for (int i = 0; i < n; ++i) {
@@ -733,6 +885,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         o[i].Y = take(kk);
         o[i].T = take(kk);
         o[i].E = take(kk);
+        o[i].invn = take((size_t)m.kpad * f);
         o[i].gram = take((size_t)(m.nb / 2) * m.nsplit * kPw * kPw * sizeof(double));
         o[i].rot = take((size_t)(m.nb / 2) * kPw * kPw * f);
         o[i].rflag = take((size_t)(m.nb / 2) * sizeof(int));
@@ -769,6 +922,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         m.Y = (float*)(b + o[i].Y);
         m.T = (float*)(b + o[i].T);
         m.E = (float*)(b + o[i].E);
+        m.invn = (float*)(b + o[i].invn);
         m.gram = (double*)(b + o[i].gram);
         m.rot = (float*)(b + o[i].rot);
         m.rot_flag = (int*)(b + o[i].rflag);
@@ -925,18 +1079,12 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         for (int i : gm[g]) pipe_of[i] = g;
 
     // GEMM problem tables
-    const bool gbf = h->gdt == SC_BF16;
     for (int g = 0; g < h->npipes; ++g) {
         h->pipes[g].lowdin_eW.tb = true;
         h->pipes[g].proj.ta = true;
         h->pipes[g].warm_nt.tb = true;
         h->pipes[g].polish_nt.tb = true;
     }
-    h->s1_nn_a.abf = gbf;  // square: A = G
-    h->s1_nn_b.bbf = gbf;  // tall: B = G
-    h->s1_nt.tb = true;    // wide: A = G, B = F^T
-    h->s1_nt.abf = gbf;
-    h->s3_tn.ta = true;
     for (int i = 0; i < n; ++i) {
         MatDev& m = h->mh[i];
         Pipe& P = h->pipes[pipe_of[i]];
@@ -970,7 +1118,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             // after the factor phase: V rows = scaled rows of X^T times W (= V_prev),
             // only where the factorization was accepted; then A_rows = V op(M)
             p = make_prob(m.A, m.K_ld, m.W, m.k, m.V, m.kpad, m.k, m.k, m.k);
-            p.row_scale = m.Y;
+            p.row_scale = m.invn;
             p.gate = &h->flags_d[i].precond;
             P.factor_v.h.push_back(p);
             if (m.tall) {
@@ -991,32 +1139,6 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         p = make_prob(m.W, m.k, m.W, m.k, m.tall ? m.PR : m.PL, m.k, m.k, m.k, m.k);
         p.k_scale = m.d;
         P.proj.h.push_back(p);
-        // step chain
-        if (square) {
-            p = make_prob(nullptr, m.n, m.PR, m.n, m.T, m.n, m.m, m.n, m.n);  // T = G P_R
-            p.a_ptr = i;
-            h->s1_nn_a.h.push_back(p);
-            p = make_prob(m.PL, m.m, m.T, m.n, m.Gfilt, m.n, m.m, m.n, m.m);  // G_filt = P_L T
-            h->s2_nn.h.push_back(p);
-        } else if (m.tall) {
-            p = make_prob(m.F, m.K_ld, nullptr, m.n, m.Y, m.k, m.k, m.n, m.m);  // Y = D F G
-            p.b_ptr = i;
-            p.row_scale = m.d;
-            h->s1_nn_b.h.push_back(p);
-            p = make_prob(m.Y, m.k, m.PR, m.n, m.T, m.k, m.k, m.n, m.n);  // T = Y P_R
-            h->s2_nn.h.push_back(p);
-            p = make_prob(m.F, m.K_ld, m.T, m.k, m.Gfilt, m.n, m.m, m.n, m.k);  // G_filt = F^T T
-            h->s3_tn.h.push_back(p);
-        } else {
-            p = make_prob(nullptr, m.n, m.F, m.K_ld, m.Y, m.k, m.m, m.k, m.n);  // Y = G F^T D
-            p.a_ptr = i;
-            p.col_scale = m.d;
-            h->s1_nt.h.push_back(p);
-            p = make_prob(m.PL, m.m, m.Y, m.k, m.T, m.k, m.m, m.k, m.m);  // T = P_L Y
-            h->s2_nn.h.push_back(p);
-            p = make_prob(m.T, m.k, m.F, m.K_ld, m.Gfilt, m.n, m.m, m.n, m.k);  // G_filt = T F
-            h->s3_nn.h.push_back(p);
-        }
     }
     for (int g = 0; g < h->npipes; ++g) {
         Pipe& P = h->pipes[g];
@@ -1024,8 +1146,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
                               &P.lowdin_F, &P.lowdin_eW, &P.lowdin_W, &P.proj})
             if ((rc = upload_group(h, *gg))) return rc;
     }
-    for (GemmGroup* g : {&h->s1_nn_a, &h->s1_nn_b, &h->s1_nt, &h->s2_nn, &h->s3_tn, &h->s3_nn})
-        if ((rc = upload_group(h, *g))) return rc;
+    if ((rc = build_step_groups(h, 0))) return rc;
     h->stale.assign(n, 0);
     const double gsz = h->gdt == SC_BF16 ? 2.0 : 4.0, wsz = h->wdt == SC_BF16 ? 2.0 : 4.0;
     for (int i = 0; i < n; ++i) h->total_numel += (double)h->mh[i].numel;
@@ -1038,7 +1159,12 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
 void release(sc_opt* h) {
     if (!h) return;
     DeviceGuard g(h->device);
+    if (h->worker.joinable()) h->worker.join();
     (void)hipDeviceSynchronize();
+    if (h->astream) (void)hipStreamDestroy(h->astream);
+    for (hipEvent_t e : {h->a_ready, h->a_pub, h->a_done})
+        if (e) (void)hipEventDestroy(e);
+    if (h->pub_arena) (void)hipFree(h->pub_arena);
     for (auto& r : h->prof.recs) {
         (void)hipEventDestroy(r.a);
         (void)hipEventDestroy(r.b);
@@ -1151,6 +1277,7 @@ int sc_anchor_update(sc_handle h, const void* const* G_anc, void* stream) {
     if ((rc = check_ptrs(h, G_anc, h->gdt, "G_anc"))) return rc;
     DeviceGuard g(h->device);
     hipStream_t st = (hipStream_t)stream;
+    if ((rc = finish_async(h, st, false))) return rc;
     PtrTable pt = make_table(h, G_anc);
     HIP_TRY(timed(h, PK_EMA, st, [&] {
         return launch_ema(h->md, h->chunks_d, h->nchunks, pt, h->gdt == SC_BF16, h->hp.beta_anc,
@@ -1164,7 +1291,67 @@ int sc_refresh(sc_handle h, void* stream) {
     int rc;
     if ((rc = check_handle(h))) return rc;
     DeviceGuard g(h->device);
+    if ((rc = finish_async(h, (hipStream_t)stream, false))) return rc;
     return do_refresh(h, (hipStream_t)stream);
+}
+
+int sc_anchor_update_async(sc_handle h, const void* const* G_anc, void* stream) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    if ((rc = check_ptrs(h, G_anc, h->gdt, "G_anc"))) return rc;
+    if (h->prof.on)
+        return fail(SC_ERR_INVALID_ARG, "asynchronous refresh is not available while kernel timing is on");
+    DeviceGuard g(h->device);
+    hipStream_t st = (hipStream_t)stream;
+    if ((rc = finish_async(h, st, false))) return rc;
+    if ((rc = ensure_async(h))) return rc;
+    // the operands the steps use until the refresh ends: current tau, then copied
+    if (h->proj_stale && (rc = build_projectors(h, st))) return rc;
+    HIP_TRY(hipEventRecord(h->a_ready, st));
+    HIP_TRY(hipStreamWaitEvent(h->astream, h->a_ready, 0));
+    if ((rc = publish_step_operands(h, h->astream))) return rc;
+    HIP_TRY(hipEventRecord(h->a_pub, h->astream));
+    HIP_TRY(hipStreamWaitEvent(st, h->a_pub, 0));
+    PtrTable pt = make_table(h, G_anc);
+    HIP_TRY(launch_ema(h->md, h->chunks_d, h->nchunks, pt, h->gdt == SC_BF16, h->hp.beta_anc,
+                       h->status_d + 1, h->astream));
+    h->any_stale = false;  // the refresh below covers every matrix
+    h->a_rc = SC_OK;
+    h->a_err.clear();
+    h->a_finished.store(false, std::memory_order_relaxed);
+    h->a_pending = true;
+    try {
+        h->worker = std::thread([h] {
+            DeviceGuard dg(h->device);
+            int r = do_refresh(h, h->astream);
+            if (r == SC_OK) {
+                const hipError_t e = hipEventRecord(h->a_done, h->astream);
+                if (e != hipSuccess) r = fail(SC_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+            }
+            h->a_rc = r;
+            if (r != SC_OK) h->a_err = g_err;
+            h->a_finished.store(true, std::memory_order_release);
+        });
+    } catch (...) {
+        h->a_pending = false;
+        return fail(SC_ERR_HIP, "could not start the refresh thread");
+    }
+    return SC_OK;
+}
+
+int sc_refresh_wait(sc_handle h, void* stream) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    DeviceGuard g(h->device);
+    return finish_async(h, (hipStream_t)stream, false);
+}
+
+int sc_refresh_pending(sc_handle h, int* pending) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    if (!pending) return fail(SC_ERR_INVALID_ARG, "pending is NULL");
+    *pending = h->a_pending && !h->a_finished.load(std::memory_order_acquire) ? 1 : 0;
+    return SC_OK;
 }
 
 int sc_step(sc_handle h, void* const* W, const void* const* G_mask, void* stream) {
@@ -1174,20 +1361,24 @@ int sc_step(sc_handle h, void* const* W, const void* const* G_mask, void* stream
     if ((rc = check_ptrs(h, G_mask, h->gdt, "G_mask"))) return rc;
     DeviceGuard g(h->device);
     hipStream_t st = (hipStream_t)stream;
-    if (h->any_stale) {
-        if ((rc = do_refresh(h, st))) return rc;
-    }
-    if (h->proj_stale) {
-        if ((rc = build_projectors(h, st))) return rc;
+    // until an asynchronous refresh is completed (sc_refresh_wait), steps read the
+    // operands published when it started, whether or not it has finished: the
+    // factors a step uses do not depend on timing
+    if (!h->a_pending) {
+        if (h->any_stale) {
+            if ((rc = do_refresh(h, st))) return rc;
+        }
+        if (h->proj_stale) {
+            if ((rc = build_projectors(h, st))) return rc;
+        }
     }
     PtrTable gt = make_table(h, G_mask);
     PtrTable wt = make_table(h, (const void* const*)W);
-    if ((rc = run_group(h, h->s1_nn_a, PK_STEP_GEMM1, gt, st))) return rc;
-    if ((rc = run_group(h, h->s1_nn_b, PK_STEP_GEMM1, gt, st))) return rc;
-    if ((rc = run_group(h, h->s1_nt, PK_STEP_GEMM1, gt, st))) return rc;
-    if ((rc = run_group(h, h->s2_nn, PK_STEP_GEMM2, gt, st))) return rc;
-    if ((rc = run_group(h, h->s3_tn, PK_STEP_GEMM3, gt, st))) return rc;
-    if ((rc = run_group(h, h->s3_nn, PK_STEP_GEMM3, gt, st))) return rc;
+    const GemmGroup* sg = h->step[h->a_pending ? 1 : 0];
+    static const int kinds[6] = {PK_STEP_GEMM1, PK_STEP_GEMM1, PK_STEP_GEMM1,
+                                 PK_STEP_GEMM2, PK_STEP_GEMM3, PK_STEP_GEMM3};
+    for (int q = 0; q < 6; ++q)
+        if ((rc = run_group(h, sg[q], kinds[q], gt, st))) return rc;
     const int64_t t = h->t + 1;
     const double lr = h->hp.lr, b1 = h->hp.beta1, b2 = h->hp.beta2;
     const double bc1 = 1.0 - std::pow(b1, (double)t);
@@ -1220,6 +1411,10 @@ int sc_set_tau(sc_handle h, float tau_p) {
     if ((rc = check_handle(h))) return rc;
     if (!(tau_p >= 0.0f) || !std::isfinite(tau_p))
         return fail(SC_ERR_INVALID_ARG, "tau_p must be finite and >= 0");
+    {
+        DeviceGuard g(h->device);
+        if ((rc = finish_async(h, nullptr, true))) return rc;
+    }
     h->hp.tau_p = tau_p;
     h->proj_stale = true;
     return SC_OK;
@@ -1236,6 +1431,7 @@ int sc_set_state(sc_handle h, int idx, int kind, const float* src, void* stream)
                                            : nullptr;
     if (!dst) return fail(SC_ERR_INVALID_ARG, "unknown state kind %d", kind);
     DeviceGuard g(h->device);
+    if ((rc = finish_async(h, (hipStream_t)stream, false))) return rc;
     HIP_TRY(hipMemcpyAsync(dst, src, sizeof(float) * m.numel, hipMemcpyDeviceToDevice,
                            (hipStream_t)stream));
     if (kind == SC_STATE_M_ANC) {
@@ -1256,6 +1452,7 @@ int sc_get_state(sc_handle h, int idx, int kind, float* dst, void* stream) {
                                                  : nullptr;
     if (!src) return fail(SC_ERR_INVALID_ARG, "unknown state kind %d", kind);
     DeviceGuard g(h->device);
+    if ((rc = finish_async(h, (hipStream_t)stream, false))) return rc;
     HIP_TRY(hipMemcpyAsync(dst, src, sizeof(float) * m.numel, hipMemcpyDeviceToDevice,
                            (hipStream_t)stream));
     return SC_OK;
@@ -1284,6 +1481,7 @@ int sc_set_factors(sc_handle h, int idx, const float* U, const float* s, const f
     if (!U || !s || !V) return fail(SC_ERR_INVALID_ARG, "U, s and V must be non-NULL");
     const MatDev& m = h->mh[idx];
     DeviceGuard g(h->device);
+    if ((rc = finish_async(h, (hipStream_t)stream, false))) return rc;
     hipStream_t st = (hipStream_t)stream;
     // A-side (rows of F, length K): U for m >= n, V for m < n; the other side -> W.
     const float* fa = m.tall ? U : V;
@@ -1309,6 +1507,7 @@ int sc_get_factors(sc_handle h, int idx, float* U, float* s, float* V, void* str
     if ((rc = check_handle(h)) || (rc = check_idx(h, idx))) return rc;
     const MatDev& m = h->mh[idx];
     DeviceGuard g(h->device);
+    if ((rc = finish_async(h, (hipStream_t)stream, false))) return rc;
     hipStream_t st = (hipStream_t)stream;
     float* fa = m.tall ? U : V;
     float* wa = m.tall ? V : U;
@@ -1322,6 +1521,7 @@ int sc_keep_proj(sc_handle h, int enable) {
     int rc;
     if ((rc = check_handle(h))) return rc;
     DeviceGuard g(h->device);
+    if ((rc = finish_async(h, nullptr, true))) return rc;
     if (enable && !h->proj_arena) {
         size_t total = 0;
         std::vector<size_t> offs(h->n);
@@ -1349,6 +1549,7 @@ int sc_get_filtered(sc_handle h, int idx, float* G_filt, float* G_proj, void* st
     const MatDev& m = h->mh[idx];
     if (G_proj && !m.Gproj) return fail(SC_ERR_INVALID_ARG, "G_proj is not kept (sc_keep_proj)");
     DeviceGuard g(h->device);
+    if ((rc = finish_async(h, (hipStream_t)stream, false))) return rc;
     hipStream_t st = (hipStream_t)stream;
     if (G_filt)
         HIP_TRY(hipMemcpyAsync(G_filt, m.Gfilt, sizeof(float) * m.numel, hipMemcpyDeviceToDevice,
@@ -1364,6 +1565,7 @@ int sc_get_stats(sc_handle h, sc_stats* out, int* per_mat_sweeps) {
     if ((rc = check_handle(h))) return rc;
     if (!out) return fail(SC_ERR_INVALID_ARG, "out is NULL");
     DeviceGuard g(h->device);
+    if ((rc = finish_async(h, nullptr, true))) return rc;
     HIP_TRY(hipDeviceSynchronize());
     HIP_TRY(hipMemcpy(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n, hipMemcpyDeviceToHost));
     int status[4];
@@ -1389,6 +1591,7 @@ int sc_get_sweep_counts(sc_handle h, int* total, int* factor) {
     int rc;
     if ((rc = check_handle(h))) return rc;
     DeviceGuard g(h->device);
+    if ((rc = finish_async(h, nullptr, true))) return rc;
     HIP_TRY(hipDeviceSynchronize());
     HIP_TRY(hipMemcpy(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n, hipMemcpyDeviceToHost));
     for (int i = 0; i < h->n; ++i) {
@@ -1402,6 +1605,7 @@ int sc_profile(sc_handle h, int enable) {
     int rc;
     if ((rc = check_handle(h))) return rc;
     DeviceGuard g(h->device);
+    if ((rc = finish_async(h, nullptr, true))) return rc;
     if (!h->prof.recs.empty()) {
         HIP_TRY(hipDeviceSynchronize());
         for (auto& r : h->prof.recs) {
@@ -1424,6 +1628,7 @@ int sc_get_kernel_times(sc_handle h, sc_kernel_time* out, int max_entries, int* 
     if (!count || (max_entries > 0 && !out))
         return fail(SC_ERR_INVALID_ARG, "out/count is NULL");
     DeviceGuard g(h->device);
+    if ((rc = finish_async(h, nullptr, true))) return rc;
     HIP_TRY(hipDeviceSynchronize());
     for (auto& r : h->prof.recs) {
         float ms = 0.0f;

@@ -355,7 +355,7 @@ __global__ __launch_bounds__(256) void chol_commit_kernel(const MatDev* __restri
 }
 
 // inv[j] = 1 / ||operand row j|| over its klen entries (float64 sum), j < k, into
-// md.Y, for the matrices whose factor phase ran: the row scales of V = U_x^T V_prev.
+// md.invn, for the matrices whose factor phase ran: the row scales of V = U_x^T V_prev.
 __global__ __launch_bounds__(256) void factor_invnorm_kernel(const MatDev* __restrict__ mats,
                                                              const MatFlags* __restrict__ flags,
                                                              const int* __restrict__ mat_idx) {
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(256) void factor_invnorm_kernel(const MatDev* __res
     double acc = 0.0;
     for (int c = threadIdx.x; c < md.klen; c += blockDim.x) acc += (double)x[c] * (double)x[c];
     acc = block_sum_f64(acc, red);
-    if (threadIdx.x == 0) md.Y[j] = acc > 0.0 ? (float)(1.0 / sqrt(acc)) : 0.0f;
+    if (threadIdx.x == 0) md.invn[j] = acc > 0.0 ? (float)(1.0 / sqrt(acc)) : 0.0f;
 }
 
 hipError_t launch_factor_invnorm(const MatDev* mats, const MatFlags* flags, const int* mat_idx,

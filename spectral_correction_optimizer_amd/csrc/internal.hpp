@@ -47,6 +47,7 @@ struct MatDev {
     float* Y;        // [k][k] step intermediate
     float* T;        // [k][k] step intermediate
     float* E;        // [k][k] refresh scratch (Gram of factors, scaled copies)
+    float* invn;     // [kpad] refresh scratch: inverse row norms of the factor-phase X
     double* gram;    // [nb/2][nsplit][2b][2b] split partial Gram blocks
     float* rot;      // [nb/2][2b][2b] R = Q - I of each pair
     int* rot_flag;   // [nb/2] 1 when the pair's rotation must be applied

@@ -74,6 +74,9 @@ def test_invalid_arguments(lib):
     assert lib.sc_anchor_update(None, None, None) == -1
     assert lib.sc_set_lr(None, 1.0) == -1
     assert lib.sc_get_stats(None, None, None) == -1
+    assert lib.sc_anchor_update_async(None, None, None) == -1
+    assert lib.sc_refresh_wait(None, None) == -1
+    assert lib.sc_refresh_pending(None, None) == -1
     assert lib.sc_opt_destroy(None) == 0
 
 

@@ -319,3 +319,64 @@ def test_certificate_failure_polishes_that_matrix_alone():
         say(f"  mat {i}: relF G_filt {err:.3e}")
         assert err <= 1e-4
     opt.close()
+
+def test_async_refresh_matches_synchronous_order():
+    """Asynchronous anchor updates (sc_anchor_update_async ... sc_refresh_wait)
+    give bitwise the weights of the synchronous call order in which the steps
+    issued while a refresh was pending come before it: those steps use the
+    previous factors, and the refresh itself computes the same factors.  A second
+    asynchronous update while one is pending completes the first one."""
+    import spectral_correction_optimizer_amd as sco
+    say("case: asynchronous refresh vs synchronous order, 192x256 + 512x128 + 128x128")
+    dev = torch.device("cuda")
+    shapes = [(192, 256), (512, 128), (128, 128)]
+    ins = [gen.MatrixInputs(97, 0, i, *sh) for i, sh in enumerate(shapes)]
+    GA = [[to_dev(gen.stored(mi.g_anc(k), "f32")[0], "f32", dev) for mi in ins] for k in range(4)]
+    G = [[to_dev(gen.stored(mi.g_mask(k), "f32")[0], "f32", dev) for mi in ins] for k in range(7)]
+
+    def run(asynchronous):
+        opt = sco.SpectralAdamW(shapes, device=dev)
+        for i, mi in enumerate(ins):
+            opt.set_state(i, "m_anc", to_dev(gen.stored(mi.m0(), "f32")[0], "f32", dev))
+        W = [to_dev(gen.stored(mi.w0(), "f32")[0], "f32", dev) for mi in ins]
+        opt.anchor_update(GA[0])
+        opt.step(W, G[0])
+        if asynchronous:
+            opt.anchor_update_async(GA[1])
+            opt.step(W, G[1])
+            opt.step(W, G[2])
+            opt.refresh_wait()
+            opt.step(W, G[3])
+            opt.anchor_update_async(GA[2])
+            opt.step(W, G[4])
+            opt.anchor_update_async(GA[3])  # completes the GA[2] refresh first
+            opt.step(W, G[5])
+            opt.refresh_wait()
+            assert not opt.refresh_pending()
+        else:
+            opt.step(W, G[1])
+            opt.step(W, G[2])
+            opt.anchor_update(GA[1])
+            opt.step(W, G[3])
+            opt.step(W, G[4])
+            opt.anchor_update(GA[2])
+            opt.step(W, G[5])
+            opt.anchor_update(GA[3])
+        opt.step(W, G[6])
+        torch.cuda.synchronize()
+        out = [w.cpu().numpy().copy() for w in W]
+        st = opt.stats()
+        opt.profile(True)
+        if asynchronous:
+            with pytest.raises(sco.ScoptError):
+                opt.anchor_update_async(GA[3])
+        opt.profile(False)
+        opt.close()
+        return out, st
+
+    wa, sa = run(True)
+    ws, ss = run(False)
+    say(f"  sweeps async {sa['sweeps']} sync {ss['sweeps']}")
+    assert sa["not_converged"] == 0 and ss["not_converged"] == 0
+    for a, b in zip(wa, ws):
+        assert np.array_equal(a, b)
