@@ -114,8 +114,9 @@ int sc_refresh(sc_handle h, void* stream);
 
 /* Asynchronous anchor arrival: the same EMA and refresh as sc_anchor_update,
  * run beside the steps that follow, so that the steps need not wait for it
- * ("Key design 2": the anchor circuit runs beside the fast replicas).  The EMA and the refresh are ordered after the work already queued
- * on `stream` and run on the library's internal streams, driven by a host
+ * ("Key design 2": the anchor circuit runs beside the fast replicas).  The
+ * EMA and the refresh are ordered after the work already queued on `stream`
+ * and run on the library's internal streams, driven by a host
  * thread of the library; the call returns at once (`stream` only waits for a
  * device copy of the operands the steps use).  Until the refresh is completed
  * by sc_refresh_wait, every sc_step uses the factors, filter and projectors of
