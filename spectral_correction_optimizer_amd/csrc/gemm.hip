@@ -44,7 +44,7 @@ struct TileLoader {
     float v[8], ks[KS ? 8 : 1];
     int row, half, rr, kk;
     __device__ void load(const T* __restrict__ p, int ld, int rows, int kdim, int r0, int k0,
-                         const float* kscale, const float* dummy, int roff = 0) {
+                         const float* kscale, int roff = 0) {
         row = roff + (KMAJOR ? (threadIdx.x & 127) : (threadIdx.x >> 1));
         half = KMAJOR ? (threadIdx.x >> 7) : (threadIdx.x & 1);
         rr = r0 + row;
@@ -67,7 +67,6 @@ struct TileLoader {
 #pragma unroll
             for (int j = 0; j < 8; ++j) ks[j] = gld(kscale + min(kk + j, kdim - 1));
         }
-        (void)dummy;
     }
     template <int NR>
     __device__ void store(__bf16 (*S)[NR * BK], int rows, int kdim, bool scaled) const {
@@ -126,9 +125,9 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
     TileLoader<TA, VEC, false, TEA> la0, la1;
     TileLoader<!TB, VEC, true, TEB> lb;
     auto load_tiles = [&](int k0) {
-        la0.load(Ap, P.lda, M, K, m0, k0, nullptr, nullptr, 0);
-        la1.load(Ap, P.lda, M, K, m0, k0, nullptr, nullptr, 128);
-        lb.load(Bp, P.ldb, N, K, n0, k0, kscale, P.C);
+        la0.load(Ap, P.lda, M, K, m0, k0, nullptr, 0);
+        la1.load(Ap, P.lda, M, K, m0, k0, nullptr, 128);
+        lb.load(Bp, P.ldb, N, K, n0, k0, kscale);
     };
     auto store_tiles = [&](int buf) {
         la0.template store<BM>(As[buf], M, K, false);
