@@ -80,9 +80,9 @@ def copy_calibration(nbytes):
 # were taken on (sha256 of the file); otherwise reported as null.
 TRAFFIC = {
     "jacobi_gram": {"source": "jacobi.hip", "sha256": "7be055545b6274f851e830ab96b6e9bdbf884bbd8cda3445af9ac92d288c8ca4",
-        "bytes_per_launch": 6.29215e+08},
+        "bytes_per_launch": 6.46594e+08},
     "jacobi_apply": {"source": "jacobi.hip", "sha256": "7be055545b6274f851e830ab96b6e9bdbf884bbd8cda3445af9ac92d288c8ca4",
-        "bytes_per_launch": 1.13307e+09},
+        "bytes_per_launch": 1.17104e+09},
     "combine_adamw": {"source": "elementwise.hip", "sha256": "0c09b9374f97495b495395fa41dedf152598946e324adfa6ca6fe895def28277",
         "bytes_per_launch": 3.1148e+10},
     "ema": {"source": "elementwise.hip", "sha256": "0c09b9374f97495b495395fa41dedf152598946e324adfa6ca6fe895def28277",
