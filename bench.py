@@ -41,7 +41,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="blocks16_1b",
-                    choices=["blocks16_1b", "blocks16_1b_bf16", "block_1b", "q_proj_2048"])
+                    choices=["blocks16_1b", "blocks16_1b_bf16", "block_1b", "q_proj_2048",
+                             "block_8b", "blocks4_8b"])
     ap.add_argument("--tau", type=float, default=None, help="override tau_p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true")

@@ -14,6 +14,7 @@ papernotes.org notes, sections "Key design 2/3" and "Training strategy"):
 * initial anchor momentum M0 = S + N(0, 1e-4)   (N(0, x): x is the std-dev);
 * each anchor gradient G_anc_k = S + fresh N(0, 1e-4);
 * each masked gradient G_mask_k = 0.5 * S + fresh N(0, 1e-3);
+* a second shape set, Llama-3-8B blocks, for the 8B-class workloads;
 * weights W0 ~ N(0, 0.02).
 
 Values are drawn in float64 and rounded once, round-to-nearest-even, to the
@@ -41,6 +42,19 @@ BLOCK_SHAPES = (
     ("down", 2048, 8192),
 )
 N_BLOCKS = 16
+
+# Llama-3-8B block shapes (public model configuration: hidden 4096, 32 query and
+# 8 key/value heads of 128, MLP 14336), row-major [out, in]; the 32 blocks'
+# fp32 states exceed one GPU, so workloads take a few blocks at a time
+BLOCK_SHAPES_8B = (
+    ("q", 4096, 4096),
+    ("k", 1024, 4096),
+    ("v", 1024, 4096),
+    ("o", 4096, 4096),
+    ("gate", 14336, 4096),
+    ("up", 14336, 4096),
+    ("down", 4096, 14336),
+)
 
 SIGNAL_SCALE = 1e-2
 SIGNAL_POWER = 1.5
@@ -178,4 +192,12 @@ def workload(name: str):
         return dict(shapes=shapes, ids=ids,
                     steps_per_anchor=25 if name == "blocks16_1b" else 1,
                     dtype="f32" if name == "blocks16_1b" else "bf16")
+    if name in ("block_8b", "blocks4_8b"):
+        nblk = 1 if name == "block_8b" else 4
+        shapes, ids = [], []
+        for b in range(nblk):
+            for i, (_, m, n) in enumerate(BLOCK_SHAPES_8B):
+                shapes.append((m, n))
+                ids.append((6, b, i))
+        return dict(shapes=shapes, ids=ids, steps_per_anchor=25, dtype="f32")
     raise KeyError(name)

@@ -573,18 +573,21 @@ __global__ __launch_bounds__(kApplyThreads) void jac_apply_kernel(const MatDev* 
 // sweeps, sort its physical rows by decreasing squared norm (ties by row
 // index) into perm, so that blocks hold columns of similar size; this cuts
 // the number of sweeps by about a quarter on the workloads' matrices.
-// Bitonic sort of up to 2048 (norm, row) keys in LDS, one workgroup per matrix.
+// Bitonic sort of up to kSortMax (norm, row) keys in LDS, one workgroup per matrix.
+namespace {
+constexpr int kSortMax = 4096;  // 32 KB of LDS
+}
 __global__ __launch_bounds__(256) void jac_sort_kernel(const MatDev* __restrict__ mats,
                                                        const MatFlags* __restrict__ flags,
                                                        const int* __restrict__ mat_idx,
                                                        int round) {
-    __shared__ float key[2048];
-    __shared__ int idx[2048];
+    __shared__ float key[kSortMax];
+    __shared__ int idx[kSortMax];
     const int i = mat_idx[blockIdx.x];
     if (flags[i].done) return;
     const MatDev& md = mats[i];
     if (round % (md.nb - 1) != 0) return;
-    if (md.kpad > 2048) return;  // beyond the LDS sort size the order stays as it is
+    if (md.kpad > kSortMax) return;  // beyond the LDS sort size the order stays as it is
     int n2 = 1;
     while (n2 < md.kpad) n2 <<= 1;
     for (int j = threadIdx.x; j < n2; j += blockDim.x) {

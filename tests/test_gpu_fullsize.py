@@ -202,3 +202,40 @@ def test_sampled_noisy_parity_16_blocks(dtype, tau, sample):
                  f"{int(bad.sum())} above 1 ulp, their |G_proj| <= {float(np.abs(ora.last_proj[0])[bad].max()) if bad.any() else 0.0:.2e})")
     say(f"  mat {idx} {m}x{n}: relF G_filt {ef:.3e} G_proj {ep:.3e} {wnote} oracle sweeps {ora.sweeps[0]}")
     assert ef <= REL_TOL and ep <= REL_TOL and ok_w
+
+
+def test_known_factors_8b_block_shapes():
+    """One Llama-3-8B block (q/o 4096x4096, k/v 1024x4096, gate/up 14336x4096,
+    down 4096x14336) in one handle, anchor momenta with known SVD: a noiseless
+    power-law signal of rank 512 (its Haar factors are quick to draw at these
+    sizes; the other singular values are zero up to the float32 rounding of M).
+    G_filt and G_proj against the oracle's projection from the known factors."""
+    import spectral_correction_optimizer_amd as sco
+    dev = torch.device("cuda")
+    shapes = [(m, n) for _, m, n in gen.BLOCK_SHAPES_8B]
+    say(f"case: 8B block known-factor shapes {shapes}")
+    ins = [gen.MatrixInputs(71, 0, i, m, n, r0=512, noise=False) for i, (m, n) in enumerate(shapes)]
+    hp = dict(gen.DEFAULT_HP)
+    opt = sco.SpectralAdamW(shapes, device=dev, **hp)
+    opt.keep_proj(True)
+    Gs, Ws = [], []
+    for i, mi in enumerate(ins):
+        opt.set_state(i, "m_anc", to_dev(gen.stored(mi.signal(), "f32")[0], "f32", dev))
+        Gs.append(gen.stored(mi.g_mask(0) + 1e-3 * np.random.default_rng(i).standard_normal(
+            (mi.m, mi.n)), "f32"))
+        Ws.append(to_dev(gen.stored(mi.w0(), "f32")[0], "f32", dev))
+    say("  inputs ready")
+    opt.refresh()
+    opt.step(Ws, [to_dev(p, "f32", dev) for p, _ in Gs])
+    st = opt.stats()
+    say(f"  sweeps {st['sweeps']} not_converged {st['not_converged']}")
+    assert st["not_converged"] == 0
+    for i, mi in enumerate(ins):
+        U0, s0, V0 = mi.factors()
+        ref = oracle.project(U0, oracle.tikhonov(s0, hp["tau_p"]), V0, Gs[i][1])
+        gf, gp = opt.get_filtered(i, proj=True)
+        ef = relf(from_dev(gf), ref)
+        ep = relf(from_dev(gp), oracle.combine(Gs[i][1], ref, hp["alpha"]))
+        say(f"  {shapes[i]}: relF G_filt {ef:.3e} G_proj {ep:.3e}")
+        assert ef < 1e-4 and ep < 1e-4
+    opt.close()
