@@ -269,3 +269,6 @@ class Optimizer:
             self.last_proj[i] = G_proj
             out.append(W_new)
         return out
+
+
+from . import masking  # noqa: E402  (O7: the in-graph activation mask, oracle/masking.py)

@@ -306,4 +306,137 @@ def pin_storage_rounding(o):
     assert o.round_storage(np.array([0.1]), "f32")[0] == float(np.float32(0.1))
 
 
+# ---- the in-graph activation mask ("Key design 1") -------------------------------
+
+def pin_mask_keep_count(o):
+    """K = round((1 - p) H) kept dimensions per token, ties rounded up (reading)."""
+    mk = o.masking
+    assert mk.keep_count(2048, 0.95) == 102  # 102.4
+    assert mk.keep_count(2048, 0.90) == 205  # 204.8
+    assert mk.keep_count(4096, 0.95) == 205  # 204.8
+    assert mk.keep_count(10, 0.25) == 8      # 7.5
+    assert mk.keep_count(8, 0.0) == 8 and mk.keep_count(8, 1.0) == 0
+
+
+def _unshift(y, s):
+    """Inverse of x -> x ^ (x >> s) on uint64 words."""
+    x = y.copy()
+    for _ in range(64 // s + 1):
+        x = y ^ (x >> np.uint64(s))
+    return x
+
+
+def pin_mask_mixer_inverts(o):
+    """The SplitMix64 output function (Steele, Lea and Flood 2014: xor-shifts by 30, 27,
+    31 and the odd multipliers 0xBF58476D1CE4E5B9, 0x94D049BB133111EB) is a bijection of
+    64-bit words: undoing its steps with the modular inverses of the multipliers
+    recovers the input, which fails for a dropped or altered step or constant."""
+    mk = o.masking
+    z = np.random.default_rng(5).integers(0, 2 ** 63, 2000, dtype=np.uint64) * np.uint64(2) + \
+        np.random.default_rng(6).integers(0, 2, 2000, dtype=np.uint64)
+    y = mk.mix64(z)
+    i1 = np.uint64(pow(0xBF58476D1CE4E5B9, -1, 2 ** 64))
+    i2 = np.uint64(pow(0x94D049BB133111EB, -1, 2 ** 64))
+    with np.errstate(over="ignore"):
+        x = _unshift(y, 31) * i2
+        x = _unshift(x, 27) * i1
+    x = _unshift(x, 30)
+    assert np.array_equal(x, z)
+    assert all(mk.mix64_int(int(a)) == int(b) for a, b in zip(z[:64], y[:64]))
+
+
+def pin_mask_avalanche(o):
+    """Flipping any one input bit flips about half of the 64 output bits: the hash
+    behaves like a random function, which the uniform-subset reading relies on."""
+    mk = o.masking
+    z = np.random.default_rng(7).integers(0, 2 ** 63, 4000, dtype=np.uint64)
+    y = mk.mix64(z)
+    for b in range(64):
+        d = y ^ mk.mix64(z ^ np.uint64(1 << b))
+        flips = np.unpackbits(d.view(np.uint8)).reshape(-1, 64).sum(axis=1)
+        assert 31.0 < flips.mean() < 33.0, (b, flips.mean())
+
+
+def pin_mask_exact_k(o):
+    """Every token keeps exactly K distinct dimensions in [0, H), listed in ascending
+    order; K = 0 keeps none and K = H keeps all."""
+    mk = o.masking
+    for T, H, K in [(5, 64, 16), (3, 100, 0), (3, 100, 100), (2, 2048, 102), (4, 7, 3)]:
+        idx = mk.indices(2, 9, 1, T, H, K)
+        assert idx.shape == (T, K) and idx.dtype == np.int32
+        if K:
+            assert (np.diff(idx, axis=1) > 0).all() and idx.min() >= 0 and idx.max() < H
+        if K == H:
+            assert (idx == np.arange(H)).all()
+
+
+def pin_mask_nested(o):
+    """Smallest-hash selection: the kept set for K1 < K2 lies inside the one for K2."""
+    mk = o.masking
+    a = mk.indices(4, 1, 0, 8, 256, 12)
+    b = mk.indices(4, 1, 0, 8, 256, 40)
+    for r in range(8):
+        assert set(a[r]).issubset(set(b[r]))
+
+
+def pin_mask_uniform(o):
+    """Over many tokens each dimension is kept with frequency K/H and each pair of
+    dimensions with K(K-1)/(H(H-1)) (uniform random K-subsets)."""
+    mk = o.masking
+    T, H, K = 20000, 32, 8
+    m = mk.mask(mk.indices(1, 2, 3, T, H, K), H).astype(np.float64)
+    e = T * K / H
+    chi2 = (((m.sum(axis=0) - e) ** 2) / e).sum()
+    assert chi2 < 75.0, chi2  # 31 degrees of freedom: far beyond the 99.99% point
+    co = (m.T @ m) / T
+    off = co[~np.eye(H, dtype=bool)]
+    assert abs(off.mean() - K * (K - 1) / (H * (H - 1))) < 2e-3
+
+
+def pin_mask_keys(o):
+    """The mask depends on the layer, the step, the batch and the token, and on nothing
+    else: equal keys give equal masks, any changed key a different one."""
+    mk = o.masking
+    base = mk.indices(3, 5, 7, 4, 128, 20)
+    assert np.array_equal(base, mk.indices(3, 5, 7, 4, 128, 20))
+    for other in [(4, 5, 7), (3, 6, 7), (3, 5, 8)]:
+        assert not np.array_equal(base, mk.indices(*other, 4, 128, 20))
+    assert not np.array_equal(base[0], base[1])
+    # the same token under a longer sequence keeps the same dimensions
+    assert np.array_equal(base, mk.indices(3, 5, 7, 9, 128, 20, rows=range(4)))
+
+
+def pin_mask_pack_unpack(o):
+    """pack keeps the K values of each token in ascending dimension order; unpack puts
+    them back with zeros elsewhere: unpack(pack(x)) = x * m and pack(unpack(v)) = v."""
+    mk = o.masking
+    x = _rand(11, 6, 50)
+    idx = mk.indices(0, 0, 0, 6, 50, 13)
+    m = mk.mask(idx, 50)
+    assert (m.sum(axis=1) == 13).all()
+    v = mk.pack(x, idx)
+    assert v.shape == (6, 13)
+    for r in range(6):
+        assert np.array_equal(v[r], x[r][np.flatnonzero(m[r])])
+    assert np.array_equal(mk.unpack(v, idx, 50), x * m)
+    assert np.array_equal(mk.pack(mk.unpack(v, idx, 50), idx), v)
+
+
+def pin_mask_gradient(o):
+    """The mask is an element-wise product in the graph ("Key design 1" gradient
+    equation): torch's gradient of h -> h * m, formed by gather and scatter, is the
+    upstream gradient times m, which is unpack(pack(upstream)) with the same indices."""
+    import torch
+    mk = o.masking
+    idx = mk.indices(6, 2, 1, 4, 12, 5)
+    x = torch.tensor(_rand(12, 4, 12), requires_grad=True)
+    ti = torch.tensor(idx, dtype=torch.int64)
+    y = torch.zeros_like(x).scatter(1, ti, x.gather(1, ti))
+    g = _rand(13, 4, 12)
+    y.backward(torch.tensor(g))
+    got = x.grad.numpy()
+    assert np.array_equal(got, g * mk.mask(idx, 12))
+    assert np.array_equal(got, mk.unpack(mk.pack(g, idx), idx, 12))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -145,3 +145,64 @@ def test_mutation_is_caught(name, oracle_mod, monkeypatch):
 def test_svd_mutation_is_caught(name, oracle_mod, monkeypatch):
     monkeypatch.setattr(oracle_mod, "svd", WRAPPERS[name](oracle_mod.svd))
     assert _pins_fail(oracle_mod), f"mutation {name} passed every pin"
+
+
+# ---- the in-graph activation mask ------------------------------------------------
+
+def _mask_mutations(mk):
+    """Plausible mistakes in oracle/masking.py, each as (attribute, replacement)."""
+    def keep_count_floor(H, p):
+        return int(np.floor((1.0 - p) * H))
+
+    def indices_coarse_hash(layer, step, batch, T, H, K, rows=None):
+        # ranks by the top 4 bits only: ties go to low dimensions, a biased subset
+        u = mk.hashes(mk.seed_of(layer, step, batch), T, H, rows) >> np.uint64(60)
+        out = np.empty((u.shape[0], K), dtype=np.int32)
+        j = np.arange(H)
+        for r in range(u.shape[0]):
+            out[r] = np.sort(np.lexsort((j, u[r]))[:K])
+        return out
+
+    def indices_unsorted(layer, step, batch, T, H, K, rows=None):
+        u = mk.hashes(mk.seed_of(layer, step, batch), T, H, rows)
+        out = np.empty((u.shape[0], K), dtype=np.int32)
+        j = np.arange(H)
+        for r in range(u.shape[0]):
+            out[r] = np.lexsort((j, u[r]))[:K]  # kept in hash order, not dimension order
+        return out
+
+    seed_of = mk.seed_of if mk is not None else None
+
+    def seed_without_layer(layer, step, batch):
+        return seed_of(0, step, batch)
+
+    def mix64_no_second_shift(z):
+        z = np.asarray(z, dtype=np.uint64)
+        with np.errstate(over="ignore"):
+            z = (z ^ (z >> np.uint64(30))) * np.uint64(mk.M1)
+            z = z * np.uint64(mk.M2)
+        return z ^ (z >> np.uint64(31))
+
+    def unpack_shifted(v, idx, H):
+        out = np.zeros((v.shape[0], H), dtype=np.asarray(v).dtype)
+        np.put_along_axis(out, np.minimum(idx.astype(np.int64) + 1, H - 1), v, axis=1)
+        return out
+
+    return {
+        "mask_keep_count_floor": ("keep_count", keep_count_floor),
+        "mask_coarse_hash": ("indices", indices_coarse_hash),
+        "mask_unsorted_pack_order": ("indices", indices_unsorted),
+        "mask_seed_without_layer": ("seed_of", seed_without_layer),
+        "mask_mixer_step_dropped": ("mix64", mix64_no_second_shift),
+        "mask_unpack_off_by_one": ("unpack", unpack_shifted),
+    }
+
+
+MASK_MUTATIONS = sorted(_mask_mutations(None).keys())
+
+
+@pytest.mark.parametrize("name", MASK_MUTATIONS)
+def test_mask_mutation_is_caught(name, oracle_mod, monkeypatch):
+    attr, fn = _mask_mutations(oracle_mod.masking)[name]
+    monkeypatch.setattr(oracle_mod.masking, attr, fn)
+    assert _pins_fail(oracle_mod), f"mutation {name} passed every pin"
