@@ -55,6 +55,9 @@ def parse():
                          "refresh (sc_anchor_update_async ... sc_refresh_wait)")
     ap.add_argument("--no-precondition", action="store_true",
                     help="plain Jacobi sweeps for every matrix (no Cholesky factor phase)")
+    ap.add_argument("--mask", action="store_true",
+                    help="only time the in-graph activation mask (indices, pack, unpack) at the "
+                         "Llama-3.2-1B pipeline boundary (65536 tokens x 2048, rate 0.95) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 3 times (to scale HBM "
                          "byte counters) and exit")
@@ -185,8 +188,55 @@ def async_measure(opt, W, g_anc, G_mask, n):
             "wall_ms": round(start.elapsed_time(end), 2)}
 
 
+def mask_bench(reps):
+    """The in-graph activation mask at one pipeline boundary of the Llama-3.2-1B
+    setting (batch 32 x context 2048 tokens, hidden 2048, mask rate 0.95):
+    HIP-event times of sc_mask_indices, sc_mask_pack and sc_mask_unpack on the
+    caller's stream (bf16 and fp32 payloads), algorithmic bytes of pack/unpack."""
+    import torch
+
+    import spectral_correction_optimizer_amd as sco
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    T, H = 65536, 2048
+    K = sco.mask_keep_count(H, 0.95)
+    seed = sco.mask_seed(3, 100, 7)
+    idx = sco.mask_indices(seed, T, H, K, device=dev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize(dev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize(dev)
+        return a.elapsed_time(b) / reps
+
+    t_idx = timed(lambda: sco.mask_indices(seed, T, H, K, device=dev))
+    res = {"metric": "in-graph activation mask at the Llama-3.2-1B pipeline boundary",
+           "config": {"workload": "mask_1b_boundary", "tokens": T, "hidden": H, "rate": 0.95, "kept": K},
+           "indices_ms": round(t_idx, 4), "indices_tokens_per_s": round(T / (t_idx * 1e-3), 0)}
+    for name, dt, es in (("bf16", torch.bfloat16, 2), ("f32", torch.float32, 4)):
+        x = torch.randn(T, H, device=dev).to(dt)
+        v = sco.mask_pack(x, idx)
+        t_pack = timed(lambda: sco.mask_pack(x, idx))
+        t_unp = timed(lambda: sco.mask_unpack(v, idx, H))
+        b_pack = T * K * (2 * es + 4)           # read kept values and indices, write packed
+        b_unp = T * K * (es + 4) + T * H * es   # read packed values and indices, write dense rows
+        res[name] = {"pack_ms": round(t_pack, 4), "pack_gbps": round(b_pack / (t_pack * 1e6), 1),
+                     "unpack_ms": round(t_unp, 4), "unpack_gbps": round(b_unp / (t_unp * 1e6), 1),
+                     "unpack_frac_hbm": round(b_unp / (t_unp * 1e6) / PEAK_HBM_GBPS, 4),
+                     "bytes_pack": b_pack, "bytes_unpack": b_unp}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
+    if args.mask:
+        mask_bench(max(args.steps, 1) * 10)
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return

@@ -243,6 +243,40 @@ int sc_get_kernel_times(sc_handle h, sc_kernel_time* out, int max_entries, int* 
 /* Message of the last error on the calling thread ("" if none). */
 const char* sc_last_error(void);
 
+/* ---- In-graph activation mask ("Key design 1") ----------------------------------
+ * At a pipeline boundary each of T tokens keeps K of its H hidden dimensions;
+ * the kept set is a deterministic function of (layer, step, batch), so sender
+ * and receiver rebuild it locally and only the K kept values per token travel;
+ * the gradient of the masked states travels back through the same set.  Token
+ * i keeps the K dimensions j with the smallest u = mix64(seed + (i*H + j + 1) *
+ * 0x9E3779B97F4A7C15) (ties to the smaller j), in ascending order; mix64 is the
+ * SplitMix64 output function.  These calls need no handle.  Limits: 1 <= H <=
+ * 4096, 0 <= K <= H, T >= 0; T = 0 or K = 0 queues nothing (unpack with K = 0
+ * writes zeros); pack and unpack clamp index entries outside [0, H) into it
+ * (valid index sets come from sc_mask_indices).  Errors: SC_ERR_INVALID_ARG for bad sizes, a NULL pointer or an
+ * unknown dtype, before any GPU work. */
+
+/* K = floor((1 - p) * H + 1/2) kept dimensions per token at mask rate p in [0, 1]. */
+int sc_mask_keep_count(int H, float p, int* K);
+
+/* The mask seed of (layer, step, batch):
+ * mix64(mix64(mix64((layer+1)*G) ^ (step+1)*G) ^ (batch+1)*G), G = 0x9E3779B97F4A7C15,
+ * 64-bit wrapping arithmetic. */
+int sc_mask_seed(uint64_t layer, uint64_t step, uint64_t batch, uint64_t* seed);
+
+/* idx: device int32 [T][K], written with the kept dimensions of each token. */
+int sc_mask_indices(uint64_t seed, int64_t T, int H, int K, int32_t* idx, void* stream);
+
+/* packed[i][k] = x[i][idx[i][k]]: x device [T][H] of dtype, packed device [T][K]. */
+int sc_mask_pack(sc_dtype dtype, const void* x, const int32_t* idx, int64_t T, int H, int K,
+                 void* packed, void* stream);
+
+/* x[i][j] = packed[i][k] where idx[i][k] = j, else 0: the masked states (forward,
+ * receiver) or the masked gradient (backward, sender; packed = the packed
+ * gradient).  x device [T][H] of dtype, overwritten. */
+int sc_mask_unpack(sc_dtype dtype, const void* packed, const int32_t* idx, int64_t T, int H, int K,
+                   void* x, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

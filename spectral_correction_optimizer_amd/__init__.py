@@ -20,7 +20,8 @@ import os
 
 import torch  # loaded first: libscopt then binds to torch's HIP runtime
 
-__all__ = ["SpectralAdamW", "ScoptError", "library_path", "load_library", "EXPORTED_SYMBOLS"]
+__all__ = ["SpectralAdamW", "ScoptError", "library_path", "load_library", "EXPORTED_SYMBOLS",
+           "mask_keep_count", "mask_seed", "mask_indices", "mask_pack", "mask_unpack"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libscopt.so")
@@ -31,6 +32,7 @@ EXPORTED_SYMBOLS = (
     "sc_anchor_update_async", "sc_refresh_wait", "sc_refresh_pending", "sc_step", "sc_set_lr", "sc_set_tau", "sc_set_state", "sc_get_state", "sc_set_step",
     "sc_get_step", "sc_set_factors", "sc_get_factors", "sc_keep_proj", "sc_get_filtered",
     "sc_get_stats", "sc_get_sweep_counts", "sc_profile", "sc_get_kernel_times", "sc_last_error",
+    "sc_mask_keep_count", "sc_mask_seed", "sc_mask_indices", "sc_mask_pack", "sc_mask_unpack",
 )
 
 SC_F32, SC_BF16 = 0, 1
@@ -106,6 +108,15 @@ def load_library():
         "sc_get_kernel_times": (ctypes.c_int, [vp, ctypes.POINTER(KernelTime), ctypes.c_int,
                                                ctypes.POINTER(ctypes.c_int)]),
         "sc_last_error": (ctypes.c_char_p, []),
+        "sc_mask_keep_count": (ctypes.c_int, [ctypes.c_int, ctypes.c_float, ctypes.POINTER(ctypes.c_int)]),
+        "sc_mask_seed": (ctypes.c_int, [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                        ctypes.POINTER(ctypes.c_uint64)]),
+        "sc_mask_indices": (ctypes.c_int, [ctypes.c_uint64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                           vp, vp]),
+        "sc_mask_pack": (ctypes.c_int, [ctypes.c_int, vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                        vp, vp]),
+        "sc_mask_unpack": (ctypes.c_int, [ctypes.c_int, vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                          vp, vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -310,3 +321,67 @@ class SpectralAdamW:
             self.close()
         except Exception:
             pass
+
+
+# ---- in-graph activation mask ("Key design 1"): stateless calls --------------------
+
+def mask_keep_count(H: int, p: float) -> int:
+    """Kept dimensions per token at mask rate p: floor((1 - p) H + 1/2)."""
+    k = ctypes.c_int()
+    _check(load_library().sc_mask_keep_count(int(H), float(p), ctypes.byref(k)))
+    return k.value
+
+
+def mask_seed(layer: int, step: int, batch: int) -> int:
+    """The mask seed of (layer, step, batch)."""
+    s = ctypes.c_uint64()
+    _check(load_library().sc_mask_seed(int(layer), int(step), int(batch), ctypes.byref(s)))
+    return s.value
+
+
+def _cur_stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def mask_indices(seed: int, T: int, H: int, K: int, device=None) -> "torch.Tensor":
+    """Kept dimensions of each of T tokens: int32 [T, K] on the device, ascending."""
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    _check(load_library().sc_mask_indices(int(seed), int(T), int(H), int(K),
+                                          ctypes.c_void_p(idx.data_ptr()), _cur_stream(dev)))
+    return idx
+
+
+def _mask_dt(t):
+    if t.dtype == torch.float32:
+        return SC_F32
+    if t.dtype == torch.bfloat16:
+        return SC_BF16
+    raise ValueError(f"mask tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def mask_pack(x: "torch.Tensor", idx: "torch.Tensor") -> "torch.Tensor":
+    """Kept values of each token (x: [T, H] contiguous; idx: int32 [T, K])."""
+    T, H = x.shape
+    K = idx.shape[1]
+    if not (x.is_contiguous() and idx.is_contiguous() and idx.dtype == torch.int32 and idx.shape[0] == T
+            and idx.device == x.device):
+        raise ValueError("mask_pack: contiguous x [T, H] and int32 idx [T, K] on one device")
+    out = torch.empty((T, K), dtype=x.dtype, device=x.device)
+    _check(load_library().sc_mask_pack(_mask_dt(x), ctypes.c_void_p(x.data_ptr()),
+                                       ctypes.c_void_p(idx.data_ptr()), T, H, K,
+                                       ctypes.c_void_p(out.data_ptr()), _cur_stream(x.device)))
+    return out
+
+
+def mask_unpack(packed: "torch.Tensor", idx: "torch.Tensor", H: int) -> "torch.Tensor":
+    """Dense [T, H] rows with the packed values at idx and zeros elsewhere."""
+    T, K = packed.shape
+    if not (packed.is_contiguous() and idx.is_contiguous() and idx.dtype == torch.int32
+            and tuple(idx.shape) == (T, K) and idx.device == packed.device):
+        raise ValueError("mask_unpack: contiguous packed [T, K] and int32 idx [T, K] on one device")
+    out = torch.empty((T, H), dtype=packed.dtype, device=packed.device)
+    _check(load_library().sc_mask_unpack(_mask_dt(packed), ctypes.c_void_p(packed.data_ptr()),
+                                         ctypes.c_void_p(idx.data_ptr()), T, int(H), K,
+                                         ctypes.c_void_p(out.data_ptr()), _cur_stream(packed.device)))
+    return out

@@ -13,7 +13,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libscopt.so")
 
-SOURCES = ["api.cpp", "cholesky.hip", "elementwise.hip", "gemm.hip", "jacobi.hip"]
+SOURCES = ["api.cpp", "cholesky.hip", "elementwise.hip", "gemm.hip", "jacobi.hip", "mask.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

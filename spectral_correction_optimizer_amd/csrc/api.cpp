@@ -1657,3 +1657,69 @@ int sc_get_kernel_times(sc_handle h, sc_kernel_time* out, int max_entries, int* 
 }
 
 }  // extern "C"
+
+// ---- in-graph activation mask ----------------------------------------------------------
+
+namespace {
+uint64_t host_mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+int check_mask_sizes(int64_t T, int H, int K) {
+    if (T < 0 || H < 1 || H > kMaskMaxH || K < 0 || K > H)
+        return fail(SC_ERR_INVALID_ARG, "mask sizes out of range (T %lld, H %d, K %d; 1 <= H <= %d, 0 <= K <= H)",
+                    (long long)T, H, K, kMaskMaxH);
+    if (T > (int64_t)1 << 40) return fail(SC_ERR_INVALID_ARG, "T too large");
+    return SC_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int sc_mask_keep_count(int H, float p, int* K) {
+    if (!K) return fail(SC_ERR_INVALID_ARG, "K is NULL");
+    if (H < 1 || !(p >= 0.0f && p <= 1.0f)) return fail(SC_ERR_INVALID_ARG, "need H >= 1 and p in [0, 1]");
+    *K = (int)std::floor((1.0 - (double)p) * H + 0.5);
+    return SC_OK;
+}
+
+int sc_mask_seed(uint64_t layer, uint64_t step, uint64_t batch, uint64_t* seed) {
+    if (!seed) return fail(SC_ERR_INVALID_ARG, "seed is NULL");
+    const uint64_t g = 0x9E3779B97F4A7C15ull;
+    uint64_t s = host_mix64((layer + 1) * g);
+    s = host_mix64(s ^ ((step + 1) * g));
+    *seed = host_mix64(s ^ ((batch + 1) * g));
+    return SC_OK;
+}
+
+int sc_mask_indices(uint64_t seed, int64_t T, int H, int K, int32_t* idx, void* stream) {
+    int rc;
+    if ((rc = check_mask_sizes(T, H, K))) return rc;
+    if (T > 0 && K > 0 && !idx) return fail(SC_ERR_INVALID_ARG, "idx is NULL");
+    HIP_TRY(launch_mask_indices(seed, T, H, K, idx, (hipStream_t)stream));
+    return SC_OK;
+}
+
+int sc_mask_pack(sc_dtype dtype, const void* x, const int32_t* idx, int64_t T, int H, int K, void* packed,
+                 void* stream) {
+    int rc;
+    if ((rc = check_mask_sizes(T, H, K))) return rc;
+    if (dtype != SC_F32 && dtype != SC_BF16) return fail(SC_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (T > 0 && K > 0 && (!x || !idx || !packed)) return fail(SC_ERR_INVALID_ARG, "NULL pointer");
+    HIP_TRY(launch_mask_pack(dtype == SC_BF16, x, idx, T, H, K, packed, (hipStream_t)stream));
+    return SC_OK;
+}
+
+int sc_mask_unpack(sc_dtype dtype, const void* packed, const int32_t* idx, int64_t T, int H, int K, void* x,
+                   void* stream) {
+    int rc;
+    if ((rc = check_mask_sizes(T, H, K))) return rc;
+    if (dtype != SC_F32 && dtype != SC_BF16) return fail(SC_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+    if (T > 0 && (!x || (K > 0 && (!idx || !packed)))) return fail(SC_ERR_INVALID_ARG, "NULL pointer");
+    HIP_TRY(launch_mask_unpack(dtype == SC_BF16, packed, idx, T, H, K, x, (hipStream_t)stream));
+    return SC_OK;
+}
+
+}  // extern "C"

@@ -191,4 +191,13 @@ hipError_t launch_phase2_reset(const MatDev* mats, MatFlags* flags, const int* m
 hipError_t launch_transpose(const float* src, int rows, int cols, int ld_src, float* dst,
                             int ld_dst, hipStream_t st);
 
+
+// ---- in-graph activation mask (mask.hip) ------------------------------------------
+constexpr int kMaskMaxH = 4096;  // hidden sizes up to 4096 (LDS: 48 KB per token sort)
+hipError_t launch_mask_indices(uint64_t seed, int64_t T, int H, int K, int32_t* idx, hipStream_t st);
+hipError_t launch_mask_pack(bool bf16, const void* x, const int32_t* idx, int64_t T, int H, int K,
+                            void* packed, hipStream_t st);
+hipError_t launch_mask_unpack(bool bf16, const void* packed, const int32_t* idx, int64_t T, int H, int K,
+                              void* x, hipStream_t st);
+
 }  // namespace scopt

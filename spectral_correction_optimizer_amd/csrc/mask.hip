@@ -1,0 +1,202 @@
+// In-graph activation mask on gfx950 ("Key design 1" of the papernotes.org
+// notes on "Communication-Efficient LLM Adaptation over Decentralized GPU
+// Meshes"): at a pipeline boundary every token keeps K of its H hidden
+// dimensions, chosen by a pseudo-random function of (layer, step, batch) that
+// sender and receiver evaluate locally, so only the K kept values travel; the
+// gradient goes back through the same index set.
+//
+// The kept set of token i is the K dimensions j with the smallest 64-bit hash
+// u = mix64(seed + (i H + j + 1) gamma) (ties to the smaller j), listed in
+// ascending order; mix64 is the SplitMix64 output function (Steele, Lea and
+// Flood, OOPSLA 2014), gamma its golden-ratio increment.
+//
+//   mask_indices  one workgroup per token: the hashes below a threshold that
+//                 almost surely admits the K smallest (all H when it does not),
+//                 a bitonic sort of them by (hash, dimension), then the first K
+//                 dimensions sorted ascending (integer work, ALU bound)
+//   mask_pack     kept values of each token, in index order (a gather; bound by
+//                 HBM sectors touched)
+//   mask_unpack   dense rows with zeros elsewhere (an LDS row per token, then
+//                 coalesced row writes; HBM bound)
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace scopt {
+
+namespace {
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+// ascending bitonic sort of n (a power of two, <= 2 * blockDim.x * iterations)
+// entries of (key, val) in LDS, by key then val
+template <typename K, typename V>
+__device__ void bitonic_sort(K* key, V* val, int n) {
+    for (int size = 2; size <= n; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t = threadIdx.x; t < n / 2; t += blockDim.x) {
+                const int lo = 2 * t - (t & (stride - 1));
+                const int hi = lo + stride;
+                const bool up = (lo & size) == 0;  // this run ascends
+                const K ka = key[lo], kb = key[hi];
+                const V va = val[lo], vb = val[hi];
+                const bool a_first = ka < kb || (ka == kb && va < vb);
+                if (a_first != up) {
+                    key[lo] = kb;
+                    key[hi] = ka;
+                    val[lo] = vb;
+                    val[hi] = va;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+}  // namespace
+
+// The K smallest of H uniform 64-bit hashes lie, almost surely, below a
+// threshold t0 at which w = K + 5 sqrt(K) + 16 of the H values are expected
+// (the count below t0 is binomial, standard deviation under sqrt(w)): the
+// workgroup collects the hashes below t0 (order of collection immaterial),
+// sorts those candidates instead of all H, and keeps the first K.  Exact
+// whenever at least K and at most `cap` values fall below t0 (every value left
+// out is then larger than every kept one), cap the power of two at or above
+// w + 6 sqrt(w); otherwise (about once in 10^7 tokens), or when cap would
+// exceed kCand or w is not well below H, all H are sorted.
+namespace {
+constexpr int kCand = 512;
+}
+
+__global__ __launch_bounds__(256) void mask_indices_kernel(uint64_t seed, int64_t T, int H, int K,
+                                                           int32_t* __restrict__ idx) {
+    __shared__ uint64_t key[kMaskMaxH];
+    __shared__ int32_t dim[kMaskMaxH];
+    __shared__ int ncand;
+    int hp = 1;
+    while (hp < H) hp <<= 1;
+    const double want = K + 5.0 * sqrt((double)K) + 16.0;  // expected candidates below t0
+    int cap = 1;
+    while (cap < want + 6.0 * sqrt(want)) cap <<= 1;
+    const bool fast = cap <= kCand && want < 0.5 * H;
+    const uint64_t t0 = fast ? (uint64_t)(want / H * 18446744073709551616.0) : ~0ull;
+    for (int64_t row = blockIdx.x; row < T; row += gridDim.x) {
+        const uint64_t base = (uint64_t)row * (uint64_t)H + 1ull;
+        int n = hp;
+        bool done = false;
+        if (fast) {
+            if (threadIdx.x == 0) ncand = 0;
+            __syncthreads();
+            for (int j = threadIdx.x; j < H; j += blockDim.x) {
+                const uint64_t u = mix64(seed + (base + (uint64_t)j) * kGamma);
+                if (u < t0) {
+                    const int slot = atomicAdd(&ncand, 1);
+                    if (slot < cap) {
+                        key[slot] = u;
+                        dim[slot] = j;
+                    }
+                }
+            }
+            __syncthreads();
+            const int c = ncand;
+            if (c >= K && c <= cap) {
+                for (int j = c + threadIdx.x; j < cap; j += blockDim.x) {
+                    key[j] = ~0ull;
+                    dim[j] = 0x7fffffff;
+                }
+                __syncthreads();
+                n = cap;
+                done = true;
+            }
+            __syncthreads();  // every thread has read ncand before it is reset
+        }
+        if (!done) {
+            for (int j = threadIdx.x; j < hp; j += blockDim.x) {
+                key[j] = j < H ? mix64(seed + (base + (uint64_t)j) * kGamma) : ~0ull;
+                dim[j] = j < H ? j : 0x7fffffff;
+            }
+            __syncthreads();
+            n = hp;
+        }
+        bitonic_sort(key, dim, n);
+        // the first K dimensions, sorted ascending (keys reused as 64-bit values)
+        int kp = 1;
+        while (kp < K) kp <<= 1;
+        for (int j = threadIdx.x; j < kp; j += blockDim.x) key[j] = j < K ? (uint64_t)dim[j] : ~0ull;
+        __syncthreads();
+        if (K > 1) bitonic_sort(key, dim, kp);
+        int32_t* out = idx + row * K;
+        for (int j = threadIdx.x; j < K; j += blockDim.x) gst(out + j, (int32_t)key[j]);
+        __syncthreads();
+    }
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void mask_pack_kernel(const E* __restrict__ x, const int32_t* __restrict__ idx,
+                                                        int64_t T, int H, int K, E* __restrict__ packed) {
+    const int64_t n = T * (int64_t)K;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t row = e / K;
+        const int j = min(max(gld(idx + e), 0), H - 1);  // entries outside [0, H) are clamped
+        gst(packed + e, gld(x + row * H + j));
+    }
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void mask_unpack_kernel(const E* __restrict__ packed,
+                                                          const int32_t* __restrict__ idx, int64_t T, int H,
+                                                          int K, E* __restrict__ x) {
+    __shared__ E rowbuf[kMaskMaxH];
+    for (int64_t row = blockIdx.x; row < T; row += gridDim.x) {
+        for (int j = threadIdx.x; j < H; j += blockDim.x) rowbuf[j] = E(0);
+        __syncthreads();
+        for (int k = threadIdx.x; k < K; k += blockDim.x)
+            rowbuf[min(max(gld(idx + row * K + k), 0), H - 1)] = gld(packed + row * K + k);
+        __syncthreads();
+        for (int j = threadIdx.x; j < H; j += blockDim.x) gst(x + row * H + j, rowbuf[j]);
+        __syncthreads();
+    }
+}
+
+namespace {
+int grid_rows(int64_t T) { return (int)(T < 65536 ? T : 65536); }
+}  // namespace
+
+hipError_t launch_mask_indices(uint64_t seed, int64_t T, int H, int K, int32_t* idx, hipStream_t st) {
+    if (T <= 0 || K <= 0) return hipSuccess;
+    hipLaunchKernelGGL(mask_indices_kernel, dim3(grid_rows(T)), dim3(256), 0, st, seed, T, H, K, idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_mask_pack(bool bf16, const void* x, const int32_t* idx, int64_t T, int H, int K,
+                            void* packed, hipStream_t st) {
+    const int64_t n = T * (int64_t)K;
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256;
+    const dim3 grid((unsigned)(blocks < 65536 ? blocks : 65536));
+    if (bf16)
+        hipLaunchKernelGGL(mask_pack_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t*)x, idx, T, H,
+                           K, (uint16_t*)packed);
+    else
+        hipLaunchKernelGGL(mask_pack_kernel<float>, grid, dim3(256), 0, st, (const float*)x, idx, T, H, K,
+                           (float*)packed);
+    return hipGetLastError();
+}
+
+hipError_t launch_mask_unpack(bool bf16, const void* packed, const int32_t* idx, int64_t T, int H, int K,
+                              void* x, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (bf16)
+        hipLaunchKernelGGL(mask_unpack_kernel<uint16_t>, dim3(grid_rows(T)), dim3(256), 0, st,
+                           (const uint16_t*)packed, idx, T, H, K, (uint16_t*)x);
+    else
+        hipLaunchKernelGGL(mask_unpack_kernel<float>, dim3(grid_rows(T)), dim3(256), 0, st, (const float*)packed,
+                           idx, T, H, K, (float*)x);
+    return hipGetLastError();
+}
+
+}  // namespace scopt

@@ -78,6 +78,18 @@ def test_invalid_arguments(lib):
     assert lib.sc_refresh_wait(None, None) == -1
     assert lib.sc_refresh_pending(None, None) == -1
     assert lib.sc_opt_destroy(None) == 0
+    # the stateless mask calls validate before any GPU work
+    k = ctypes.c_int()
+    assert lib.sc_mask_keep_count(2048, 0.95, ctypes.byref(k)) == 0 and k.value == 102
+    assert lib.sc_mask_keep_count(0, 0.5, ctypes.byref(k)) == -1
+    assert lib.sc_mask_keep_count(8, 1.5, ctypes.byref(k)) == -1
+    assert lib.sc_mask_indices(0, 4, 4097, 1, None, None) == -1
+    assert lib.sc_mask_indices(0, 4, 64, 65, None, None) == -1
+    assert lib.sc_mask_indices(0, -1, 64, 8, None, None) == -1
+    assert lib.sc_mask_indices(0, 4, 64, 8, None, None) == -1      # NULL idx
+    assert lib.sc_mask_pack(7, None, None, 4, 64, 8, None, None) == -1
+    assert lib.sc_mask_unpack(0, None, None, 4, 64, 8, None, None) == -1
+    assert lib.sc_mask_indices(0, 0, 64, 8, None, None) == 0       # T = 0: nothing to do
 
 
 def test_no_device_is_reported(lib):
@@ -87,3 +99,12 @@ def test_no_device_is_reported(lib):
     rc, _ = _create(lib, 1, [8], [8])
     assert rc == -5
     assert "device" in lib.sc_last_error().decode()
+
+
+def test_mask_seed_and_count_match_oracle(lib):
+    """The library's host-side mask seed and keep count equal the oracle's."""
+    import oracle.masking as mk
+    for layer, step, batch in [(0, 0, 0), (3, 10, 7), (2 ** 40, 5, 2 ** 63), (2 ** 64 - 2, 1, 2)]:
+        assert sco.mask_seed(layer, step, batch) == mk.seed_of(layer, step, batch)
+    for H, p in [(2048, 0.95), (4096, 0.95), (10, 0.25), (8, 0.0), (8, 1.0), (1000, 0.9)]:
+        assert sco.mask_keep_count(H, p) == mk.keep_count(H, p)
