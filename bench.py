@@ -53,6 +53,10 @@ def parse():
     ap.add_argument("--async-refresh", type=int, default=0, metavar="N",
                     help="also time N steps alone and N steps issued beside an asynchronous "
                          "refresh (sc_anchor_update_async ... sc_refresh_wait)")
+    ap.add_argument("--solve-waves", type=int, default=0, choices=[0, 1, 2, 4, 8],
+                    help="wavefronts per Jacobi pair solve (0: by each launch's pair count)")
+    ap.add_argument("--solve-copies", type=int, default=0, choices=[0, 1, 2],
+                    help="LDS copies of the pair Gram in the multi-wave solve (0: by pair count)")
     ap.add_argument("--no-precondition", action="store_true",
                     help="plain Jacobi sweeps for every matrix (no Cholesky factor phase)")
     ap.add_argument("--mask", action="store_true",
@@ -83,9 +87,9 @@ def copy_calibration(nbytes):
 # on a plain device copy of known size), valid only for the kernel source they
 # were taken on (sha256 of the file); otherwise reported as null.
 TRAFFIC = {
-    "jacobi_gram": {"source": "jacobi.hip", "sha256": "7be055545b6274f851e830ab96b6e9bdbf884bbd8cda3445af9ac92d288c8ca4",
-        "bytes_per_launch": 6.46594e+08},
-    "jacobi_apply": {"source": "jacobi.hip", "sha256": "7be055545b6274f851e830ab96b6e9bdbf884bbd8cda3445af9ac92d288c8ca4",
+    "jacobi_gram": {"source": "jacobi.hip", "sha256": "3f5236f86d323d3513f1f96c0aa0cfb679a5c17533036f54adbfa5b1a3b95888",
+        "bytes_per_launch": 6.46609e+08},
+    "jacobi_apply": {"source": "jacobi.hip", "sha256": "3f5236f86d323d3513f1f96c0aa0cfb679a5c17533036f54adbfa5b1a3b95888",
         "bytes_per_launch": 1.17104e+09},
     "combine_adamw": {"source": "elementwise.hip", "sha256": "0c09b9374f97495b495395fa41dedf152598946e324adfa6ca6fe895def28277",
         "bytes_per_launch": 3.1148e+10},
@@ -282,6 +286,7 @@ def main():
     opt = sco.SpectralAdamW(shapes, w_dtype=tdt, g_dtype=tdt, device=dev,
                             max_sweeps=args.max_sweeps,
                             precondition=0 if args.no_precondition else 1, **hp)
+    opt.set_solve_waves(args.solve_waves, args.solve_copies)
     for i, x in enumerate(M0):
         opt.set_state(i, "m_anc", x)
     del M0
@@ -390,6 +395,7 @@ def main():
         "config": {"workload": args.workload, "matrices": nmat, "elements": elems,
                    "tau_p": hp["tau_p"], "alpha": hp["alpha"], "beta_anc": hp["beta_anc"],
                    "lr": hp["lr"]},
+        "solve_variant": {"waves": args.solve_waves or "auto", "copies": args.solve_copies or "auto"},
         "refresh_ms": round(r_med, 2),
         "step_ms": round(s_med, 3),
         "amortized_step_ms_anchor_every_25": round(s_med + r_med / 25.0, 3),

@@ -185,6 +185,16 @@ int sc_set_factors(sc_handle h, int idx, const float* U, const float* s, const f
  * The singular triplets are in no particular order. */
 int sc_get_factors(sc_handle h, int idx, float* U, float* s, float* V, void* stream);
 
+/* Variant of the 64-column pair solve of the Jacobi sweeps: `waves` = 1, 2, 4
+ * or 8 wavefronts per pair, `copies` = 1 or 2 copies of the pair's Gram and
+ * rotation in LDS (two copies: one barrier per step but half as many pairs
+ * per CU).  0 picks per launch by its number of pairs: up to 512 pairs 8
+ * waves and 2 copies, else 4 waves and 1 copy.  A tuning and test knob: every
+ * variant computes the same rotations in the same order and gives
+ * bit-identical results.  Other values, or copies 2 with one wave:
+ * SC_ERR_INVALID_ARG.  Waits for a pending asynchronous refresh. */
+int sc_set_solve_waves(sc_handle h, int waves, int copies);
+
 /* Keep G_proj of each step (costs one more store per element in the AdamW
  * pass and rows x cols floats per matrix). */
 int sc_keep_proj(sc_handle h, int enable);

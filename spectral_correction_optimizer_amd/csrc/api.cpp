@@ -203,6 +203,7 @@ struct sc_opt {
     bool any_stale = false;
     bool proj_stale = false;
     bool keep_proj = false;
+    int solve_waves = 0, solve_copies = 0;  // pair solve variant: 0 by the launch's pair count
     std::vector<void*> dev_allocs;
     Prof prof;
     double total_numel = 0.0;
@@ -517,7 +518,7 @@ int pipe_round(sc_opt* h, Pipe& p, hipStream_t st) {
     HIP_TRY(timed(h, PK_GRAM, st,
                   [&] { return launch_jacobi_gram(h->md, h->flags_d, L.gi, L.ngi, r, st); }));
     HIP_TRY(timed(h, PK_SOLVE, st,
-                  [&] { return launch_jacobi_solve(h->md, h->flags_d, L.si, L.nsi, r, st); }));
+                  [&] { return launch_jacobi_solve(h->md, h->flags_d, L.si, L.nsi, r, h->solve_waves, h->solve_copies, st); }));
     HIP_TRY(timed(h, PK_APPLY, st,
                   [&] { return launch_jacobi_apply(h->md, h->flags_d, L.ai, L.nai, r, st); }));
     if (last)
@@ -1514,6 +1515,21 @@ int sc_get_factors(sc_handle h, int idx, float* U, float* s, float* V, void* str
     if (fa) HIP_TRY(launch_transpose(m.F, m.k, m.tall ? m.m : m.n, m.K_ld, fa, m.k, st));
     if (wa) HIP_TRY(launch_transpose(m.W, m.k, m.k, m.k, wa, m.k, st));
     if (s) HIP_TRY(hipMemcpyAsync(s, m.s, sizeof(float) * m.k, hipMemcpyDeviceToDevice, st));
+    return SC_OK;
+}
+
+int sc_set_solve_waves(sc_handle h, int waves, int copies) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    if (waves != 0 && waves != 1 && waves != 2 && waves != 4 && waves != 8)
+        return fail(SC_ERR_INVALID_ARG, "waves must be 0, 1, 2, 4 or 8 (got %d)", waves);
+    if (copies < 0 || copies > 2 || (waves == 1 && copies == 2))
+        return fail(SC_ERR_INVALID_ARG, "copies must be 0, 1 or 2, and 0 or 1 for one wave (got %d)",
+                    copies);
+    DeviceGuard g(h->device);
+    if ((rc = finish_async(h, nullptr, true))) return rc;
+    h->solve_waves = waves;
+    h->solve_copies = copies;
     return SC_OK;
 }
 

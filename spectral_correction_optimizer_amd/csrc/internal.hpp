@@ -147,8 +147,15 @@ hipError_t launch_filter(const MatDev* mats, const int* mat_idx, int nmat, float
 
 hipError_t launch_jacobi_gram(const MatDev* mats, const MatFlags* flags, const GramItem* gi,
                               int ngi, int round, hipStream_t st);
+// Pair solve variants: waves = 1, 2, 4 or 8 wavefronts per pair; copies = 1 or
+// 2 copies of G and R^T in LDS (one wavefront: one copy).  0 picks by the
+// launch's pair count: up to kSolveSmallMax pairs eight waves and two copies
+// (two pairs per CU), else four waves and one copy (four pairs per CU).  All
+// variants give identical results.
+constexpr int kSolveSmallMax = 512;
+int solve_waves_for(int nsi);
 hipError_t launch_jacobi_solve(const MatDev* mats, MatFlags* flags, const SolveItem* si, int nsi,
-                               int round, hipStream_t st);
+                               int round, int waves, int copies, hipStream_t st);
 hipError_t launch_jacobi_apply(const MatDev* mats, const MatFlags* flags, const ApplyItem* ai,
                                int nai, int round, hipStream_t st);
 // At a matrix's sweep start: order its columns by decreasing norm (perm).

@@ -250,6 +250,27 @@ constexpr BlockTable make_block_table() {
     return t;
 }
 __constant__ BlockTable kBlocks = make_block_table();
+
+// Rotation of a pair with Gram entries g_pp, g_pq, g_qq: the angle that zeroes
+// g_pq, as c, s and c - 1; the identity when either column is at or below the
+// zero floor or the pair is orthogonal to the threshold tol.
+__device__ __forceinline__ void pair_rotation(float gpp, float gpq, float gqq, float floor2,
+                                              float tol, float& c, float& sn, float& cm1) {
+    c = 1.0f;
+    sn = 0.0f;
+    cm1 = 0.0f;
+    if (gpp > floor2 && gqq > floor2 && fabsf(gpq) > tol * __builtin_amdgcn_sqrtf(gpp * gqq)) {
+        const float zeta = (gqq - gpp) * 0.5f * __builtin_amdgcn_rcpf(gpq);
+        const float az = fabsf(zeta);
+        // t = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)), without overflow
+        const float den = az < 1e18f ? az + __builtin_amdgcn_sqrtf(fmaf(az, az, 1.0f)) : 2.0f * az;
+        const float t = copysignf(__builtin_amdgcn_rcpf(den), zeta);
+        const float hq = __builtin_amdgcn_sqrtf(fmaf(t, t, 1.0f));
+        c = __builtin_amdgcn_rcpf(hq);
+        sn = t * c;
+        cm1 = -t * sn * __builtin_amdgcn_rcpf(1.0f + hq);
+    }
+}
 }  // namespace
 
 __global__ __launch_bounds__(64) void jac_solve_kernel(const MatDev* __restrict__ mats,
@@ -393,18 +414,8 @@ __global__ __launch_bounds__(64) void jac_solve_kernel(const MatDev* __restrict_
         const float xoq = RT[2 * jr * SR + oq], yoq = RT[(2 * jr + 1) * SR + oq];
         // ---- rotation of pair jr (both lanes of the pair compute and publish it)
         const float gpp = dpq[0], gpq = dpq[1];
-        float c = 1.0f, sn = 0.0f, cm1 = 0.0f;
-        if (gpp > floor2 && gqq > floor2 && fabsf(gpq) > tol * __builtin_amdgcn_sqrtf(gpp * gqq)) {
-            const float zeta = (gqq - gpp) * 0.5f * __builtin_amdgcn_rcpf(gpq);
-            const float az = fabsf(zeta);
-            // t = sign(zeta) / (|zeta| + sqrt(1 + zeta^2)), without overflow
-            const float den = az < 1e18f ? az + __builtin_amdgcn_sqrtf(fmaf(az, az, 1.0f)) : 2.0f * az;
-            const float t = copysignf(__builtin_amdgcn_rcpf(den), zeta);
-            const float hq = __builtin_amdgcn_sqrtf(fmaf(t, t, 1.0f));
-            c = __builtin_amdgcn_rcpf(hq);
-            sn = t * c;
-            cm1 = -t * sn * __builtin_amdgcn_rcpf(1.0f + hq);
-        }
+        float c, sn, cm1;
+        pair_rotation(gpp, gpq, gqq, floor2, tol, c, sn, cm1);
         cc[jr] = c;
         ss[jr] = sn;
         __asm__ volatile("" ::: "memory");
@@ -474,6 +485,226 @@ __global__ __launch_bounds__(64) void jac_solve_kernel(const MatDev* __restrict_
     // rotated squared column norms (diagonal of Q^T G Q) for the next sweep's ordering
     gst(md.cnorm + pair_row(md, bI, bJ, l), (float)(G[l * SG + l] * dmax));
     if (l == 0) {
+        *rflag = 1;
+        atomicAdd(&fl.pairs_applied, 1);
+    }
+}
+
+// ---------------------------------------------------------------------------------
+// The same sweep on NW wavefronts per pair.  Wave w updates, within every bank
+// class, the pair-blocks of G numbered NU (4 w + l / 16) .. + NU - 1, and the
+// columns [64 w / NW, 64 (w + 1) / NW) of R^T; every wave computes all 32
+// rotations of a step (from the same entries of G, so identically).  Every entry
+// goes through the arithmetic of the one-wavefront kernel in the same order: the
+// results are identical.  The one-wavefront solve spends most of a step waiting
+// on LDS round trips (rotation parameters, then the next step's inputs) with
+// nothing else to issue on its SIMD; more waves per pair split the arithmetic
+// and give each SIMD other waves to run meanwhile.
+//  NB = 2: G and R^T are held twice; a step reads one copy and writes the other,
+//    so one barrier per step puts all writes of a step before the reads of the
+//    next and all reads of a step before the writes of the step after (69 KB of
+//    LDS, two pairs per CU: for launches of few pairs).
+//  NB = 1: one copy and two barriers per step, reads | writes (35 KB): four pairs
+//    per CU as with one wavefront (for launches that fill the chip).
+template <int NW, int NB>
+__global__ __launch_bounds__(64 * NW) void jac_solve_waves_kernel(const MatDev* __restrict__ mats,
+                                                                MatFlags* __restrict__ flags,
+                                                                const SolveItem* __restrict__ items,
+                                                                int round) {
+    static_assert(NW == 2 || NW == 4 || NW == 8, "two, four or eight wavefronts per pair");
+    static_assert(NB == 1 || NB == 2, "one or two copies of G and R^T");
+    constexpr int NU = 8 / NW;   // pair-blocks of G per lane
+    constexpr int NK = 8 / NW;   // 8-column groups of R^T per lane
+    constexpr int NE = 40 / NW;  // stored Gram entries per lane in the load
+    constexpr int CW = PW / NW;  // columns of R^T per wave
+    __shared__ __align__(16) float G[NB][PW * SG];
+    __shared__ __align__(16) float RT[NB][PW * SR];
+    __shared__ float cc[PW / 2], ss[PW / 2];
+    __shared__ double rs[PW];
+    __shared__ float mos[NW];
+
+    const SolveItem it = items[blockIdx.x];
+    MatFlags& fl = flags[it.mat];
+    if (fl.done) return;
+    const MatDev& md = mats[it.mat];
+    const float tol = md.tol;
+    const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int bI, bJ;
+    block_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
+
+    // 1. the pair Gram as in the one-wavefront kernel; every wave sums the
+    //    diagonal, the stored upper tiles are shared out (entries NE w .. + NE - 1)
+    const double* gp = md.gram + (int64_t)it.slot * md.nsplit * (PW * PW);
+    const int e0 = NE * w;
+    double dl = 0.0, acc[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = 0.0;
+    auto tile_row = [&](int e) {
+        const int t = e >> 2, ti = t < 4 ? 0 : t < 7 ? 1 : t < 9 ? 2 : 3;
+        return 16 * ti + (l >> 4) + 4 * (e & 3);
+    };
+    auto tile_col = [&](int e) {
+        const int t = e >> 2, ti = t < 4 ? 0 : t < 7 ? 1 : t < 9 ? 2 : 3;
+        const int tj = ti + t - (ti == 0 ? 0 : ti == 1 ? 4 : ti == 2 ? 7 : 9);
+        return 16 * tj + (l & 15);
+    };
+#pragma unroll 2
+    for (int sp = 0; sp < it.nsplit; ++sp) {
+        const double* g = gp + (int64_t)sp * PW * PW;
+        dl += gld(g + l * (PW + 1));
+#pragma unroll
+        for (int e = 0; e < NE; ++e) acc[e] += gld(g + tile_row(e0 + e) * PW + tile_col(e0 + e));
+    }
+    double dmax = dl;
+    for (int o = 32; o > 0; o >>= 1) dmax = fmax(dmax, __shfl_xor(dmax, o));
+    const double scale = dmax > 0.0 ? 1.0 / dmax : 1.0;
+    const double floor2d = (double)fl.floor2;
+    const float floor2 = (float)(floor2d * scale);
+    if (w == 0) rs[l] = dl > floor2d ? 1.0 / sqrt(dl) : 0.0;
+    __syncthreads();
+
+    // 2. the upper triangle into the first copy of G; the largest relative
+    //    off-diagonal over the waves
+    float mo = 0.0f;
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        const int a = tile_row(e0 + e), b = tile_col(e0 + e);
+        if (a <= b) G[0][a * SG + b] = (float)(acc[e] * scale);
+        if (a < b) mo = fmaxf(mo, (float)(fabs(acc[e]) * rs[a] * rs[b]));
+    }
+    for (int o = 32; o > 0; o >>= 1) mo = fmaxf(mo, __shfl_xor(mo, o));
+    if (l == 0) mos[w] = mo;
+    __syncthreads();
+    mo = mos[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) mo = fmaxf(mo, mos[i]);
+    if (threadIdx.x == 0) atomicMax(&fl.sweep_max, __float_as_uint(mo));
+    int* rflag = md.rot_flag + it.slot;
+    if (!(mo > tol)) {
+        if (w == 0) {
+            gst(md.cnorm + pair_row(md, bI, bJ, l), (float)dl);
+            if (l == 0) *rflag = 0;
+        }
+        return;
+    }
+    for (int e = threadIdx.x; e < PW * SR / 4; e += 64 * NW) *(v4f*)&RT[0][4 * e] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // 3. per-lane addresses (the one-wavefront kernel's, restricted to the wave's
+    //    share).  A correction of R's identity entries in a column of another
+    //    wave goes to the row's padding column PW, which is never read.
+    const int jr = l >> 1, hh = l & 1, cls = l & 15, odd = (l >> 4) & 1;
+    int blk_ij[NU], blk_rd[NU], blk_wr[NU][4];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int v = kBlocks.v[cls][NU * ((l >> 4) + 4 * w) + u];
+        const bool ok = v & 0x8000;
+        const int i = ok ? v & 255 : 0, j = ok ? (v >> 8) & 127 : 1;
+        blk_ij[u] = i | (j << 8);
+        blk_rd[u] = 2 * i * SG + 2 * j;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ee = odd ? (e ^ 1) : e;
+            const int r = slot_next(2 * i + (ee >> 1)), c = slot_next(2 * j + (ee & 1));
+            blk_wr[u][e] = ok ? min(r, c) * SG + max(r, c) : kSink;
+        }
+    }
+    const int sp_ = slot_next(2 * jr), sq_ = slot_next(2 * jr + 1);
+    const int dg_pp = sp_ * SG + sp_, dg_qq = sq_ * SG + sq_, dg_pq = min(sp_, sq_) * SG + max(sp_, sq_);
+    const int cb = CW * w;
+    const int rt_rd = 2 * jr * SR + cb + 4 * hh, rt_wp = sp_ * SR + cb + 4 * hh, rt_wq = sq_ * SR + cb + 4 * hh;
+    int kp = jr == 0 ? -1 : cycle_pos(2 * jr), kq = cycle_pos(2 * jr + 1);
+    __syncthreads();
+    v2f dpq = *(const v2f*)&G[0][2 * jr * SG + 2 * jr];
+    float gqq = G[0][(2 * jr + 1) * SG + 2 * jr + 1];
+    int cur = 0;
+#pragma unroll 1
+    for (int ir = 0; ir < PW - 1; ++ir) {
+        const float* Gr = G[cur];
+        float* Gw = G[NB == 2 ? cur ^ 1 : cur];
+        const float* Rr = RT[cur];
+        float* Rw = RT[NB == 2 ? cur ^ 1 : cur];
+        __asm__ volatile("" ::"v"(dpq), "v"(gqq));
+        v2f x0[NU], x1[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            x0[u] = *(const v2f*)&Gr[blk_rd[u]];
+            x1[u] = *(const v2f*)&Gr[blk_rd[u] + SG];
+        }
+        v4f xr[NK], yr[NK];
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+            xr[k] = *(const v4f*)&Rr[rt_rd + 8 * k];
+            yr[k] = *(const v4f*)&Rr[rt_rd + SR + 8 * k];
+        }
+        const int op = kp < 0 ? 0 : cycle_slot(kp), oq = cycle_slot(kq);
+        const float xop = Rr[2 * jr * SR + op], yop = Rr[(2 * jr + 1) * SR + op];
+        const float xoq = Rr[2 * jr * SR + oq], yoq = Rr[(2 * jr + 1) * SR + oq];
+        const float gpp = dpq[0], gpq = dpq[1];
+        float c, sn, cm1;
+        pair_rotation(gpp, gpq, gqq, floor2, tol, c, sn, cm1);
+        cc[jr] = c;
+        ss[jr] = sn;
+        __asm__ volatile("" ::: "memory");
+        float wv[NU][4];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int i = blk_ij[u] & 255, j = (blk_ij[u] >> 8) & 255;
+            const float ci = cc[i], si = ss[i], cj = cc[j], sj = ss[j];
+            const float y00 = cj * x0[u][0] - sj * x0[u][1], y01 = sj * x0[u][0] + cj * x0[u][1];
+            const float y10 = cj * x1[u][0] - sj * x1[u][1], y11 = sj * x1[u][0] + cj * x1[u][1];
+            const float z00 = ci * y00 - si * y10, z01 = ci * y01 - si * y11;
+            const float z10 = si * y00 + ci * y10, z11 = si * y01 + ci * y11;
+            wv[u][0] = odd ? z01 : z00;
+            wv[u][1] = odd ? z00 : z01;
+            wv[u][2] = odd ? z11 : z10;
+            wv[u][3] = odd ? z10 : z11;
+        }
+        if (NB == 1) __syncthreads();  // every wave has read this step's G and R^T
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Gw[blk_wr[u][e]] = wv[u][e];
+        if (w == 0) {
+            const float y00 = c * gpp - sn * gpq, y01 = sn * gpp + c * gpq;
+            const float y10 = c * gpq - sn * gqq, y11 = sn * gpq + c * gqq;
+            Gw[dg_pp] = c * y00 - sn * y10;
+            Gw[dg_pq] = c * y01 - sn * y11;
+            Gw[dg_qq] = sn * y01 + c * y11;
+        }
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+            v4f np, nq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                np[e] = fmaf(cm1, xr[k][e], xr[k][e]) - sn * yr[k][e];
+                nq[e] = fmaf(cm1, yr[k][e], yr[k][e]) + sn * xr[k][e];
+            }
+            *(v4f*)&Rw[rt_wp + 8 * k] = np;
+            *(v4f*)&Rw[rt_wq + 8 * k] = nq;
+        }
+        const int cop = op / CW == w ? op : PW, coq = oq / CW == w ? oq : PW;
+        Rw[sp_ * SR + cop] = fmaf(cm1, xop, xop) - sn * yop + cm1;
+        Rw[sq_ * SR + cop] = fmaf(cm1, yop, yop) + sn * xop + sn;
+        Rw[sp_ * SR + coq] = fmaf(cm1, xoq, xoq) - sn * yoq - sn;
+        Rw[sq_ * SR + coq] = fmaf(cm1, yoq, yoq) + sn * xoq + cm1;
+        kp = kp < 0 ? -1 : (kp == 0 ? 62 : kp - 1);
+        kq = kq == 0 ? 62 : kq - 1;
+        __syncthreads();
+        dpq = *(const v2f*)&Gw[2 * jr * SG + 2 * jr];
+        gqq = Gw[(2 * jr + 1) * SG + 2 * jr + 1];
+        if (NB == 2) cur ^= 1;
+    }
+    // 4. R and the rotated column norms from the copy the last step wrote
+    const float* Rf = RT[cur];
+    float* Rg = md.rot + (int64_t)it.slot * PW * PW;
+#pragma unroll 4
+    for (int b0 = cb; b0 < cb + CW; b0 += 4) {
+        const v4f v = *(const v4f*)&Rf[l * SR + b0];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gst(Rg + (b0 + e) * PW + l, v[e]);
+    }
+    if (w == 0) gst(md.cnorm + pair_row(md, bI, bJ, l), (float)(G[cur][l * SG + l] * dmax));
+    if (threadIdx.x == 0) {
         *rflag = 1;
         atomicAdd(&fl.pairs_applied, 1);
     }
@@ -654,9 +885,29 @@ hipError_t launch_jacobi_gram(const MatDev* mats, const MatFlags* flags, const G
     return hipGetLastError();
 }
 
+int solve_waves_for(int nsi) {
+    return nsi <= kSolveSmallMax ? 8 : 4;
+}
+
 hipError_t launch_jacobi_solve(const MatDev* mats, MatFlags* flags, const SolveItem* si, int nsi,
-                               int round, hipStream_t st) {
-    hipLaunchKernelGGL(jac_solve_kernel, dim3(nsi), dim3(64), 0, st, mats, flags, si, round);
+                               int round, int waves, int copies, hipStream_t st) {
+    if (waves == 0) waves = solve_waves_for(nsi);
+    if (copies == 0) copies = nsi <= kSolveSmallMax ? 2 : 1;
+    const bool two = copies == 2;
+    if (waves == 8 && two)
+        hipLaunchKernelGGL((jac_solve_waves_kernel<8, 2>), dim3(nsi), dim3(512), 0, st, mats, flags, si, round);
+    else if (waves == 8)
+        hipLaunchKernelGGL((jac_solve_waves_kernel<8, 1>), dim3(nsi), dim3(512), 0, st, mats, flags, si, round);
+    else if (waves == 4 && two)
+        hipLaunchKernelGGL((jac_solve_waves_kernel<4, 2>), dim3(nsi), dim3(256), 0, st, mats, flags, si, round);
+    else if (waves == 4)
+        hipLaunchKernelGGL((jac_solve_waves_kernel<4, 1>), dim3(nsi), dim3(256), 0, st, mats, flags, si, round);
+    else if (waves == 2 && two)
+        hipLaunchKernelGGL((jac_solve_waves_kernel<2, 2>), dim3(nsi), dim3(128), 0, st, mats, flags, si, round);
+    else if (waves == 2)
+        hipLaunchKernelGGL((jac_solve_waves_kernel<2, 1>), dim3(nsi), dim3(128), 0, st, mats, flags, si, round);
+    else
+        hipLaunchKernelGGL(jac_solve_kernel, dim3(nsi), dim3(64), 0, st, mats, flags, si, round);
     return hipGetLastError();
 }
 

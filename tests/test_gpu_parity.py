@@ -380,3 +380,49 @@ def test_async_refresh_matches_synchronous_order():
     assert sa["not_converged"] == 0 and ss["not_converged"] == 0
     for a, b in zip(wa, ws):
         assert np.array_equal(a, b)
+
+
+def test_solve_wave_variants_bitwise():
+    """The pair solve on one, two, four or eight wavefronts per pair, with one or two LDS
+    copies, computes the same rotations in the same order: factors, sweep counts
+    and weights agree bit for bit, on shapes with ragged pair blocks, a
+    Cholesky-preconditioned operand and both orientations.  Invalid variants are
+    rejected."""
+    import spectral_correction_optimizer_amd as sco
+    say("case: solve variants (waves x copies), 192x256 + 512x128 + 200x333 + 96x1000 + 700x64")
+    dev = torch.device("cuda")
+    shapes = [(192, 256), (512, 128), (200, 333), (96, 1000), (700, 64)]
+    ins = [gen.MatrixInputs(131, 0, i, *sh) for i, sh in enumerate(shapes)]
+    GA = [to_dev(gen.stored(mi.g_anc(0), "f32")[0], "f32", dev) for mi in ins]
+    G = [to_dev(gen.stored(mi.g_mask(0), "f32")[0], "f32", dev) for mi in ins]
+
+    def run(waves, copies):
+        opt = sco.SpectralAdamW(shapes, device=dev)
+        opt.set_solve_waves(waves, copies)
+        for i, mi in enumerate(ins):
+            opt.set_state(i, "m_anc", to_dev(gen.stored(mi.m0(), "f32")[0], "f32", dev))
+        W = [to_dev(gen.stored(mi.w0(), "f32")[0], "f32", dev) for mi in ins]
+        opt.anchor_update(GA)
+        opt.step(W, G)
+        torch.cuda.synchronize()
+        fac = [[t.cpu().numpy().copy() for t in opt.get_factors(i)] for i in range(len(shapes))]
+        out = [w.cpu().numpy().copy() for w in W]
+        st = opt.stats()
+        if waves == 0:
+            for bad in ((3, 0), (-1, 0), (16, 0), (2, 3), (1, 2), (4, -1)):
+                with pytest.raises(sco.ScoptError):
+                    opt.set_solve_waves(*bad)
+        opt.close()
+        return fac, out, st
+
+    ref_f, ref_w, ref_s = run(1, 0)
+    assert ref_s["not_converged"] == 0
+    for waves, copies in ((2, 2), (2, 1), (4, 2), (4, 1), (8, 2), (8, 1), (0, 0)):
+        f, w, st = run(waves, copies)
+        say(f"  waves {waves} copies {copies}: sweeps {st['sweeps']} (one wave: {ref_s['sweeps']})")
+        assert st["sweeps"] == ref_s["sweeps"] and st["factor_sweeps"] == ref_s["factor_sweeps"]
+        for a, b in zip(f, ref_f):
+            for x, y in zip(a, b):
+                assert np.array_equal(x, y)
+        for x, y in zip(w, ref_w):
+            assert np.array_equal(x, y)
