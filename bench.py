@@ -57,6 +57,8 @@ def parse():
                     help="wavefronts per Jacobi pair solve (0: by each launch's pair count)")
     ap.add_argument("--solve-copies", type=int, default=0, choices=[0, 1, 2],
                     help="LDS copies of the pair Gram in the multi-wave solve (0: by pair count)")
+    ap.add_argument("--fused-gram", action="store_true",
+                    help="fused rotation apply + next-round pair Gram (sc_set_fused_gram)")
     ap.add_argument("--no-precondition", action="store_true",
                     help="plain Jacobi sweeps for every matrix (no Cholesky factor phase)")
     ap.add_argument("--mask", action="store_true",
@@ -287,6 +289,7 @@ def main():
                             max_sweeps=args.max_sweeps,
                             precondition=0 if args.no_precondition else 1, **hp)
     opt.set_solve_waves(args.solve_waves, args.solve_copies)
+    opt.set_fused_gram(args.fused_gram)
     for i, x in enumerate(M0):
         opt.set_state(i, "m_anc", x)
     del M0
@@ -358,7 +361,8 @@ def main():
                              "gbps": round(d["bytes"] / (d["total_ms"] * 1e6), 1) if d["bytes"] else None}
         name, d = dom
         per_launch_s = d["total_ms"] / d["launches"] / 1e3
-        if name in ("jacobi_apply", "ema", "combine_adamw", "jacobi_load", "rownorm", "normalize"):
+        if name in ("jacobi_apply", "jacobi_apply_gram", "ema", "combine_adamw", "jacobi_load",
+                    "rownorm", "normalize"):
             ach = d["bytes"] / d["launches"] / per_launch_s / 1e9
             roofline = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1),
                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -396,6 +400,7 @@ def main():
                    "tau_p": hp["tau_p"], "alpha": hp["alpha"], "beta_anc": hp["beta_anc"],
                    "lr": hp["lr"]},
         "solve_variant": {"waves": args.solve_waves or "auto", "copies": args.solve_copies or "auto"},
+        "fused_gram": args.fused_gram,
         "refresh_ms": round(r_med, 2),
         "step_ms": round(s_med, 3),
         "amortized_step_ms_anchor_every_25": round(s_med + r_med / 25.0, 3),

@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -74,13 +75,13 @@ enum ProfKind {
     PK_EMA, PK_LOAD, PK_ROWNORM, PK_INIT_FLAGS, PK_GRAM, PK_SOLVE, PK_APPLY, PK_SWEEP_END,
     PK_NORMALIZE, PK_LOWDIN, PK_FILTER, PK_PROJECTORS, PK_STEP_GEMM1, PK_STEP_GEMM2,
     PK_STEP_GEMM3, PK_ADAMW, PK_WARM, PK_SORT, PK_CHOL_GEMM, PK_CHOL, PK_POLISH_GEMM,
-    PK_GRAM_E, PK_COUNT
+    PK_GRAM_E, PK_APPLY_GRAM, PK_COUNT
 };
 const char* const kProfNames[PK_COUNT] = {
     "ema", "jacobi_load", "rownorm", "jacobi_init", "jacobi_gram", "jacobi_solve",
     "jacobi_apply", "jacobi_sweep_end", "normalize", "lowdin_gemm", "filter", "projector_gemm",
     "step_gemm1", "step_gemm2", "step_gemm3", "combine_adamw", "warm_start", "jacobi_sort",
-    "chol_syrk", "cholesky", "polish_gemm", "final_gram"};
+    "chol_syrk", "cholesky", "polish_gemm", "final_gram", "jacobi_apply_gram"};
 
 // Optional kernel timing: HIP events recorded around every launch on the
 // caller's stream; totals are folded in by sc_get_kernel_times.
@@ -105,6 +106,9 @@ int round_up(int x, int a) { return (x + a - 1) / a * a; }
 // Pipelines of the refresh (one internal stream each).
 constexpr int kPipes = 2;
 constexpr int kMaxSplits = 8;
+// Longest split of the fused apply + next Gram: each of its four waves sums its
+// Gram tiles over 32 columns per 128-column chunk in float32, at most 256.
+constexpr int kFusedMaxCols = 8 * kApplyCols;
 int split_len(int len, int nt) { return std::max(256, round_up((len + nt - 1) / nt, 256)); }
 int split_count(int len, int nt) { return (len + split_len(len, nt) - 1) / split_len(len, nt); }
 // Splits per pair for a launch over `pairs` pairs: enough workgroups to fill the
@@ -146,6 +150,12 @@ struct sc_opt {
         int nsi = 0;
         ApplyItem* ai = nullptr;
         int nai = 0;
+        // with the fused apply: every item of ai except the A rows of the matrices
+        // in fi, whose apply comes with the next round's Gram
+        ApplyItem* ai_f = nullptr;
+        int nai_f = 0;
+        FusedItem* fi = nullptr;
+        int nfi = 0;
         int* mats = nullptr;
         int nmat = 0;
         int max_nb = 2;
@@ -203,6 +213,8 @@ struct sc_opt {
     bool any_stale = false;
     bool proj_stale = false;
     bool keep_proj = false;
+    bool fuse = false;                        // fused apply + next Gram where a matrix allows it
+    std::vector<std::array<char, 2>> fused;   // per matrix: fused over the factor / full rows
     int solve_waves = 0, solve_copies = 0;  // pair solve variant: 0 by the launch's pair count
     std::vector<void*> dev_allocs;
     Prof prof;
@@ -436,13 +448,31 @@ void account_sweeps(sc_opt* h) {
         const double pairs[2] = {(double)f.pairs_pre, (double)(f.pairs_applied - f.pairs_pre)};
         const double len[2] = {(double)m.klen, (double)m.K};
         const double vlen[2] = {0.0, (double)m.k};
+        const double sweeps[2] = {(double)f.sweep_base, (double)(f.sweeps - f.sweep_base)};
         for (int ph = 0; ph < 2; ++ph) {
-            h->prof.flops[PK_GRAM] += rounds[ph] * (m.nb / 2) * 2.0 * pw * pw * len[ph];
-            h->prof.bytes[PK_GRAM] += rounds[ph] * (m.nb / 2) * 4.0 * pw * len[ph];
-            h->prof.flops[PK_APPLY] += pairs[ph] * 2.0 * pw * pw * (len[ph] + vlen[ph]);
             h->prof.flops[PK_SOLVE] += pairs[ph] * (pw * (pw - 1) / 2) * 18.0 * pw;
-            h->prof.bytes[PK_APPLY] +=
-                pairs[ph] * (8.0 * pw * (len[ph] + vlen[ph]) + 4.0 * pw * pw);
+            if (h->fuse && h->fused[i][ph]) {
+                // Gram read standalone in a sweep's first round only; the fused
+                // kernel reads every pair's rows every round, writes the rotated
+                // ones, and forms three 32 x 32 tiles per pair of the next round
+                h->prof.flops[PK_GRAM] += sweeps[ph] * (m.nb / 2) * 2.0 * pw * pw * len[ph];
+                h->prof.bytes[PK_GRAM] += sweeps[ph] * (m.nb / 2) * 4.0 * pw * len[ph];
+                h->prof.flops[PK_APPLY_GRAM] +=
+                    pairs[ph] * 2.0 * pw * pw * len[ph] +
+                    (rounds[ph] - sweeps[ph]) * (m.nb / 2) * 3.0 * 2.0 * 32 * 32 * len[ph];
+                h->prof.bytes[PK_APPLY_GRAM] += rounds[ph] * (m.nb / 2) * 4.0 * pw * len[ph] +
+                                                pairs[ph] * (4.0 * pw * len[ph] + 4.0 * pw * pw);
+                if (vlen[ph] > 0.0) {
+                    h->prof.flops[PK_APPLY] += pairs[ph] * 2.0 * pw * pw * vlen[ph];
+                    h->prof.bytes[PK_APPLY] += pairs[ph] * (8.0 * pw * vlen[ph] + 4.0 * pw * pw);
+                }
+            } else {
+                h->prof.flops[PK_GRAM] += rounds[ph] * (m.nb / 2) * 2.0 * pw * pw * len[ph];
+                h->prof.bytes[PK_GRAM] += rounds[ph] * (m.nb / 2) * 4.0 * pw * len[ph];
+                h->prof.flops[PK_APPLY] += pairs[ph] * 2.0 * pw * pw * (len[ph] + vlen[ph]);
+                h->prof.bytes[PK_APPLY] +=
+                    pairs[ph] * (8.0 * pw * (len[ph] + vlen[ph]) + 4.0 * pw * pw);
+            }
         }
     }
 }
@@ -516,11 +546,21 @@ int pipe_round(sc_opt* h, Pipe& p, hipStream_t st) {
             return launch_jacobi_sort(h->md, h->flags_d, L.mats, L.nmat, r, st);
         }));
     HIP_TRY(timed(h, PK_GRAM, st,
-                  [&] { return launch_jacobi_gram(h->md, h->flags_d, L.gi, L.ngi, r, st); }));
+                  [&] { return launch_jacobi_gram(h->md, h->flags_d, L.gi, L.ngi, r, h->fuse ? 1 : 0, st); }));
     HIP_TRY(timed(h, PK_SOLVE, st,
                   [&] { return launch_jacobi_solve(h->md, h->flags_d, L.si, L.nsi, r, h->solve_waves, h->solve_copies, st); }));
-    HIP_TRY(timed(h, PK_APPLY, st,
-                  [&] { return launch_jacobi_apply(h->md, h->flags_d, L.ai, L.nai, r, st); }));
+    if (h->fuse && L.nfi) {
+        if (L.nai_f)
+            HIP_TRY(timed(h, PK_APPLY, st, [&] {
+                return launch_jacobi_apply(h->md, h->flags_d, L.ai_f, L.nai_f, r, st);
+            }));
+        HIP_TRY(timed(h, PK_APPLY_GRAM, st, [&] {
+            return launch_jacobi_apply_gram(h->md, h->flags_d, L.fi, L.nfi, r, st);
+        }));
+    } else {
+        HIP_TRY(timed(h, PK_APPLY, st,
+                      [&] { return launch_jacobi_apply(h->md, h->flags_d, L.ai, L.nai, r, st); }));
+    }
     if (last)
         HIP_TRY(timed(h, PK_SWEEP_END, st, [&] {
             return launch_jacobi_sweep_end(h->md, h->flags_d, L.mats, L.nmat, r, h->hp.max_sweeps,
@@ -823,6 +863,7 @@ int build_step_groups(sc_opt* h, int set) {
 int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
     const int n = h->n;
     h->mh.resize(n);
+    h->fused.assign(n, std::array<char, 2>{0, 0});
     // layout pass: sizes of every buffer, carved from one arena
     std::vector<size_t> off;
     size_t total = 0;
@@ -1010,7 +1051,8 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         for (int which = 0; which < 3; ++which) {
             std::vector<GramItem> gi;
             std::vector<SolveItem> si;
-            std::vector<ApplyItem> ai;
+            std::vector<ApplyItem> ai, ai_f;
+            std::vector<FusedItem> fi;
             std::vector<int> mats;
             auto& L = P.L[which];
             int pairs = 0;
@@ -1021,26 +1063,51 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
                 const MatDev& m = h->mh[i];
                 if (which == LIST_POLISH && !m.klen) continue;  // preconditioned matrices only
                 const int len = (which == LIST_FACTOR && m.klen) ? m.klen : m.K_ld;
-                const int sl = split_len(len, nt), ns = split_count(len, nt);
+                int sl = split_len(len, nt), ns = split_count(len, nt);
+                // the fused apply + next Gram: power-of-two block counts of four or
+                // more (two XOR rounds close groups of four blocks) whose splits
+                // fit kFusedMaxCols (more, shorter splits when needed)
+                bool fuse = false;
+                if (m.nb >= 4 && (m.nb & (m.nb - 1)) == 0) {
+                    const int ntf = std::min(kMaxSplits,
+                                             std::max(nt, (len + kFusedMaxCols - 1) / kFusedMaxCols));
+                    if (split_len(len, ntf) <= kFusedMaxCols) {
+                        sl = split_len(len, ntf);
+                        ns = split_count(len, ntf);
+                        fuse = true;
+                    }
+                }
+                h->fused[i][which == LIST_FACTOR && m.klen ? 0 : 1] = fuse;
+                if (fuse)
+                    for (int grp = 0; grp < m.nb / 4; ++grp)
+                        for (int sp = 0; sp < ns; ++sp)
+                            fi.push_back(FusedItem{i, grp, sp, sp * sl, std::min(len, (sp + 1) * sl)});
                 mats.push_back(i);
                 L.max_nb = std::max(L.max_nb, m.nb);
                 if (std::find(L.nbs.begin(), L.nbs.end(), m.nb) == L.nbs.end()) L.nbs.push_back(m.nb);
                 for (int s = 0; s < m.nb / 2; ++s) {
                     for (int sp = 0; sp < ns; ++sp)
-                        gi.push_back(GramItem{i, s, sp, sp * sl, std::min(len, (sp + 1) * sl)});
+                        gi.push_back(GramItem{i, s, sp, sp * sl, std::min(len, (sp + 1) * sl),
+                                              fuse ? 1 : 0});
                     si.push_back(SolveItem{i, s, ns});
                     const int nca = (len + kApplyCols - 1) / kApplyCols;
-                    for (int c = 0; c < nca; c += kApplyRun)
+                    for (int c = 0; c < nca; c += kApplyRun) {
                         ai.push_back(ApplyItem{i, s, 0, c, std::min(kApplyRun, nca - c)});
+                        if (!fuse) ai_f.push_back(ai.back());
+                    }
                     if (which == LIST_FACTOR && m.klen) continue;  // no V in the factor phase
                     const int ncv = (m.kpad + kApplyCols - 1) / kApplyCols;
-                    for (int c = 0; c < ncv; c += kApplyRun)
+                    for (int c = 0; c < ncv; c += kApplyRun) {
                         ai.push_back(ApplyItem{i, s, 1, c, std::min(kApplyRun, ncv - c)});
+                        ai_f.push_back(ai.back());
+                    }
                 }
             }
             if ((rc = upload(gi, &L.gi, &L.ngi))) return rc;
             if ((rc = upload(si, &L.si, &L.nsi))) return rc;
             if ((rc = upload(ai, &L.ai, &L.nai))) return rc;
+            if ((rc = upload(ai_f, &L.ai_f, &L.nai_f))) return rc;
+            if ((rc = upload(fi, &L.fi, &L.nfi))) return rc;
             if ((rc = upload(mats, &L.mats, &L.nmat))) return rc;
         }
         std::vector<int> cap;
@@ -1530,6 +1597,15 @@ int sc_set_solve_waves(sc_handle h, int waves, int copies) {
     if ((rc = finish_async(h, nullptr, true))) return rc;
     h->solve_waves = waves;
     h->solve_copies = copies;
+    return SC_OK;
+}
+
+int sc_set_fused_gram(sc_handle h, int enable) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    DeviceGuard g(h->device);
+    if ((rc = finish_async(h, nullptr, true))) return rc;
+    h->fuse = enable != 0;
     return SC_OK;
 }
 

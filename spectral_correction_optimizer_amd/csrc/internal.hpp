@@ -78,10 +78,15 @@ struct MatFlags {
 
 // ---- work items ------------------------------------------------------------------
 
-struct GramItem { int mat, slot, split, x0, x1; };  // operand columns [x0, x1) of one split
+// operand columns [x0, x1) of one split; fused: the matrix's Grams after the first
+// round of a sweep come from jac_apply_gram_kernel
+struct GramItem { int mat, slot, split, x0, x1, fused; };
 struct SolveItem { int mat, slot, nsplit; };
 // which: 0 = A rows, 1 = V rows; chunks [chunk, chunk + nchunk) of kApplyCols columns
 struct ApplyItem { int mat, slot, which, chunk, nchunk; };
+// fused apply + next Gram: four-block group of a power-of-two block count over
+// operand columns [x0, x1) of split `split` (at most 8 chunks of kApplyCols)
+struct FusedItem { int mat, group, split, x0, x1; };
 struct Chunk { int mat; int64_t off; int len; };    // elementwise chunk of one matrix
 struct SyrkItem { int mat, ti, tj; };               // lower 128 x 128 tile (ti >= tj) of A^T A
 
@@ -146,7 +151,7 @@ hipError_t launch_filter(const MatDev* mats, const int* mat_idx, int nmat, float
 // ---- Jacobi sweeps -------------------------------------------------------------------
 
 hipError_t launch_jacobi_gram(const MatDev* mats, const MatFlags* flags, const GramItem* gi,
-                              int ngi, int round, hipStream_t st);
+                              int ngi, int round, int skip_fused, hipStream_t st);
 // Pair solve variants: waves = 1, 2, 4 or 8 wavefronts per pair; copies = 1 or
 // 2 copies of G and R^T in LDS (one wavefront: one copy).  0 picks by the
 // launch's pair count: up to kSolveSmallMax pairs eight waves and two copies
@@ -156,6 +161,8 @@ constexpr int kSolveSmallMax = 512;
 int solve_waves_for(int nsi);
 hipError_t launch_jacobi_solve(const MatDev* mats, MatFlags* flags, const SolveItem* si, int nsi,
                                int round, int waves, int copies, hipStream_t st);
+hipError_t launch_jacobi_apply_gram(const MatDev* mats, const MatFlags* flags, const FusedItem* fi,
+                                   int nfi, int round, hipStream_t st);
 hipError_t launch_jacobi_apply(const MatDev* mats, const MatFlags* flags, const ApplyItem* ai,
                                int nai, int round, hipStream_t st);
 // At a matrix's sweep start: order its columns by decreasing norm (perm).

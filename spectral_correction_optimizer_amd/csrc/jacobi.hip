@@ -67,12 +67,14 @@ __device__ __forceinline__ float gram_frag(const float (*Xs)[GXS], int k, int t,
 __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict__ mats,
                                                        const MatFlags* __restrict__ flags,
                                                        const GramItem* __restrict__ items,
-                                                       int round) {
+                                                       int round, int skip_fused) {
     __shared__ float Xs[2][KC][GXS];
     const GramItem it = items[blockIdx.x];
     if (flags[it.mat].done) return;
     const MatDev& md = mats[it.mat];
     const int nb = md.nb;
+    // after a sweep's first round the fused apply of the previous round wrote it
+    if (skip_fused && it.fused && round % (nb - 1) != 0) return;
     int bI, bJ;
     block_pair(nb, round % (nb - 1), it.slot, &bI, &bJ);
     const int x_begin = it.x0, x_end = it.x1;
@@ -800,6 +802,235 @@ __global__ __launch_bounds__(kApplyThreads) void jac_apply_kernel(const MatDev* 
 }
 
 // ---------------------------------------------------------------------------------
+// Rotation apply of a round fused with the next round's pair Grams.  For a
+// power-of-two block count, round r pairs block p with p ^ m (m = nb - 1 - r) and
+// round r + 1 with p ^ m', m' = m - 1: the four blocks {p, p^m, p^m', p^m^m'} form
+// two pairs in each round.  A workgroup takes such a group over one column split,
+// in 128-column chunks: waves 0-3 apply pair A's rotation and waves 4-7 pair B's,
+// 32 columns each (as jac_apply_kernel, the next chunk's loads in flight), and
+// store the rotated rows; the chunk's 128 new rows then go through LDS into the
+// next round's six 32 x 32 Gram tiles (two pairs: lower-lower, lower-upper,
+// upper-upper), dealt as 24 (tile, 32-column quarter) units, three per wave, on
+// the bfloat16 matrix cores with each float split exactly into three bfloat16
+// parts and the six largest part products (v_mfma_f32_32x32x16_bf16, float32
+// accumulation over a unit's <= 256 columns of the split).  At the end of the
+// split the four quarters of each tile are summed in float64 in a fixed order
+// into the split partial the solve of round r + 1 reads, so the operand is not
+// read again for that round's Gram.  In the last round of a sweep (the next one
+// starts with the sort) only the rotations are applied.
+namespace {
+constexpr int TLD = 2 * PW + 4;  // LDS row stride of a chunk's 128 new rows (128 columns)
+
+__device__ __forceinline__ int insert_zero_bit(int v, int b) {
+    return ((v >> b) << (b + 1)) | (v & ((1 << b) - 1));
+}
+__device__ __forceinline__ int remove_bit(int v, int b) {
+    return ((v >> (b + 1)) << b) | (v & ((1 << b) - 1));
+}
+__device__ __forceinline__ v16f mfma_split6(const Split8& a, const Split8& b, v16f acc) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.l, b.h, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.m, b.m, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.h, b.l, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.m, b.h, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.h, b.m, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.h, b.h, acc, 0, 0, 0);
+    return acc;
+}
+}  // namespace
+
+__global__ __launch_bounds__(512) void jac_apply_gram_kernel(const MatDev* __restrict__ mats,
+                                                          const MatFlags* __restrict__ flags,
+                                                          const FusedItem* __restrict__ items,
+                                                          int round) {
+    // the two rotations as bfloat16 planes (hi, mid, lo) in MFMA operand order:
+    // [pair][plane][32-row output tile][16-row k-step][lane]
+    __shared__ v8bf Rp[2][3][2][4][64];
+    __shared__ __align__(16) float Ts[2 * PW][TLD];
+    const FusedItem it = items[blockIdx.x];
+    if (flags[it.mat].done) return;
+    const MatDev& md = mats[it.mat];
+    const int nb = md.nb, rr = round % (nb - 1);
+    const bool gram = rr < nb - 2;  // the next round belongs to this sweep
+    // the group's pairs: A = (a0, a1), B = (b0, b1) (lower block first) in this
+    // round, A' = (n0, n1), B' = (n2, n3) in the next
+    int a0, a1, b0, b1, slotA, slotB, n0 = 0, n1 = 0, n2 = 0, n3 = 0, slotA2 = 0, slotB2 = 0;
+    if (gram) {
+        const int m = nb - 1 - rr, h = 31 - __builtin_clz(m), m2 = m - 1;
+        const int h2 = 31 - __builtin_clz(m2);
+        // two pivot bits on which m and m2 are independent: p has zeros there
+        const int lo = (m & (m - 1)) == 0 ? h - 1 : __builtin_ctz(m);
+        const int p = insert_zero_bit(insert_zero_bit(it.group, lo), h);
+        a0 = p;
+        a1 = p ^ m;
+        b0 = ((p ^ m2) >> h) & 1 ? p ^ m2 ^ m : p ^ m2;
+        b1 = b0 ^ m;
+        slotA = remove_bit(a0, h);
+        slotB = remove_bit(b0, h);
+        n0 = p;
+        n1 = p ^ m2;
+        n2 = ((p ^ m) >> h2) & 1 ? p ^ m ^ m2 : p ^ m;
+        n3 = n2 ^ m2;
+        slotA2 = remove_bit(n0, h2);
+        slotB2 = remove_bit(n2, h2);
+    } else {
+        slotA = 2 * it.group;
+        slotB = slotA + 1;
+        block_pair(nb, rr, slotA, &a0, &a1);
+        block_pair(nb, rr, slotB, &b0, &b1);
+    }
+    const bool rotA = md.rot_flag[slotA] != 0, rotB = md.rot_flag[slotB] != 0;
+    if (!gram && !rotA && !rotB) return;
+    const int ld = md.K_ld;
+    const __amdgpu_buffer_rsrc_t buf = buf_rsrc(md.A, (uint32_t)md.kpad * ld * 4u);
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int q = wave >> 2, wq = wave & 3;  // the wave's pair and column quarter
+    const bool rot = q == 0 ? rotA : rotB;
+    const int hl = lane >> 5, ll = lane & 31;
+    int voff[PW / 2];
+#pragma unroll
+    for (int s = 0; s < PW / 2; ++s)
+        voff[s] = (pair_row(md, q == 0 ? a0 : b0, q == 0 ? a1 : b1, apply_row(s, hl)) * ld + ll) * 4;
+    auto col0 = [&](int c) { return it.x0 + c * kApplyCols + wq * 32; };
+    auto load = [&](float (&x)[PW / 2], int c) {
+        const int so = col0(c) * 4;
+#pragma unroll
+        for (int s = 0; s < PW / 2; ++s) x[s] = buf_load_f32<kBufNT>(buf, voff[s], so);
+    };
+    // Gram units of the wave: u = 3 wave + j -> tile u / 4 (0-2 of A', 3-5 of B':
+    // lower-lower, lower-upper, upper-upper), columns 32 (u % 4) .. + 31 of a chunk
+    auto tblk = [&](int blk) { return blk == a0 ? 0 : blk == a1 ? 1 : blk == b0 ? 2 : 3; };
+    const int bu0 = 32 * tblk(n0), bv0 = 32 * tblk(n1), bu1 = 32 * tblk(n2), bv1 = 32 * tblk(n3);
+    int urow[3], vrow[3], ucol[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int u = 3 * wave + j, t = u >> 2;
+        const int bu = t < 3 ? bu0 : bu1, bv = t < 3 ? bv0 : bv1, tt = t % 3;
+        urow[j] = (tt == 2 ? bv : bu) + ll;
+        vrow[j] = (tt == 0 ? bu : bv) + ll;
+        ucol[j] = 32 * (u & 3) + 8 * hl;
+    }
+    v16f gacc[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) gacc[j][r] = 0.0f;
+    auto frag = [&](int row, int col) {
+        float f[8];
+        const v4f lo4 = *(const v4f*)&Ts[row][col], hi4 = *(const v4f*)&Ts[row][col + 4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[e] = lo4[e];
+            f[4 + e] = hi4[e];
+        }
+        return split8(f);
+    };
+    auto update = [&](float (&x)[PW / 2], int c) {
+        if (rot) {
+            // R^T X on the bfloat16 matrix cores: k-step t covers rows 16 t .. + 15,
+            // of which the lane's x[8 t .. 8 t + 7] are the half hl (apply_row), so
+            // its B operand is its own registers
+            Split8 xs[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                float f[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] = x[8 * t + e];
+                xs[t] = split8(f);
+            }
+            v16f acc0, acc1;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                acc0[r] = 0.0f;
+                acc1[r] = 0.0f;
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const Split8 r0{Rp[q][0][0][t][lane], Rp[q][1][0][t][lane], Rp[q][2][0][t][lane]};
+                const Split8 r1{Rp[q][0][1][t][lane], Rp[q][1][1][t][lane], Rp[q][2][1][t][lane]};
+                acc0 = mfma_split6(r0, xs[t], acc0);
+                acc1 = mfma_split6(r1, xs[t], acc1);
+            }
+            const int so = col0(c) * 4;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                x[r] += acc0[r];
+                x[16 + r] += acc1[r];
+                buf_store_f32<kBufNT>(x[r], buf, voff[r], so);
+                buf_store_f32<kBufNT>(x[16 + r], buf, voff[16 + r], so);
+            }
+        }
+        if (!gram) return;
+        // the chunk's new rows (row = 64 pair + pair row, column = chunk column)
+#pragma unroll
+        for (int s = 0; s < PW / 2; ++s) Ts[PW * q + apply_row(s, hl)][32 * wq + ll] = x[s];
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const Split8 fu = frag(urow[j], ucol[j] + 16 * ks);
+                const Split8 fv = frag(vrow[j], ucol[j] + 16 * ks);
+                gacc[j] = mfma_split6(fu, fv, gacc[j]);
+            }
+        __syncthreads();  // before the next chunk's rows
+    };
+    float xa[PW / 2], xb[PW / 2];
+    load(xa, 0);
+    // operand A of tile tl, k-step t for lane l: R^T[32 tl + l % 32][b] = R[b][32 tl + l % 32]
+    // at the 8 rows b = apply_row(8 t + e, l / 32) of the lane's half of the k-step
+    for (int idx = threadIdx.x; idx < 2 * 2 * 4 * 64; idx += 512) {
+        const int pq = idx >> 9, tl = (idx >> 8) & 1, t = (idx >> 6) & 3, l = idx & 63;
+        const float* R = md.rot + (int64_t)(pq == 0 ? slotA : slotB) * PW * PW;
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = gld(R + apply_row(8 * t + e, l >> 5) * PW + 32 * tl + (l & 31));
+        const Split8 sp = split8(f);
+        Rp[pq][0][tl][t][l] = sp.h;
+        Rp[pq][1][tl][t][l] = sp.m;
+        Rp[pq][2][tl][t][l] = sp.l;
+    }
+    __syncthreads();
+    if (!gram && !rot) return;  // no barrier follows without the Gram
+    const int n = (it.x1 - it.x0) / kApplyCols;
+    for (int c = 0; c < n; c += 2) {
+        if (c + 1 < n) load(xb, c + 1);
+        update(xa, c);
+        if (c + 1 >= n) break;
+        if (c + 2 < n) load(xa, c + 2);
+        update(xb, c + 1);
+    }
+    if (!gram) return;
+    // 4. per tile the four column quarters summed in float64 (quarter order) into
+    //    the split partials of the next round's pairs: tiles 0-2 of A' (units
+    //    0-11, waves 0-3), 3-5 of B' (units 12-23, waves 4-7); the upper tiles of
+    //    the 64 x 64 Gram (its lower triangle is not read)
+    float* red = &Ts[0][0];
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+        if ((wave >> 2) == ps)
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4)
+                    *(v4f*)&red[((3 * wave + j - 12 * ps) * 64 + lane) * 16 + 4 * r4] =
+                        v4f{gacc[j][4 * r4], gacc[j][4 * r4 + 1], gacc[j][4 * r4 + 2], gacc[j][4 * r4 + 3]};
+        __syncthreads();
+        double* out = md.gram + ((int64_t)(ps == 0 ? slotA2 : slotB2) * md.nsplit + it.split) * (PW * PW);
+        for (int e = threadIdx.x; e < 3 * 1024; e += 512) {
+            const int t = e >> 10, l = (e >> 4) & 63, r = e & 15;
+            double sum = 0.0;
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4) sum += (double)red[(4 * t + k4) * 1024 + (e & 1023)];
+            const int i = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3), jj = l & 31;
+            const int row = (t == 2 ? 32 : 0) + i, col = (t == 0 ? 0 : 32) + jj;
+            gst(out + row * PW + col, sum);
+        }
+        __syncthreads();
+    }
+}
+
+
+// ---------------------------------------------------------------------------------
 // Sweep-start ordering (de Rijk): at the first round of each of a matrix's
 // sweeps, sort its physical rows by decreasing squared norm (ties by row
 // index) into perm, so that blocks hold columns of similar size; this cuts
@@ -880,8 +1111,8 @@ __global__ void jac_sweep_end_kernel(const MatDev* __restrict__ mats, MatFlags* 
 }
 
 hipError_t launch_jacobi_gram(const MatDev* mats, const MatFlags* flags, const GramItem* gi,
-                              int ngi, int round, hipStream_t st) {
-    hipLaunchKernelGGL(jac_gram_kernel, dim3(ngi), dim3(256), 0, st, mats, flags, gi, round);
+                              int ngi, int round, int skip_fused, hipStream_t st) {
+    hipLaunchKernelGGL(jac_gram_kernel, dim3(ngi), dim3(256), 0, st, mats, flags, gi, round, skip_fused);
     return hipGetLastError();
 }
 
@@ -913,7 +1144,15 @@ hipError_t launch_jacobi_solve(const MatDev* mats, MatFlags* flags, const SolveI
 
 hipError_t launch_jacobi_apply(const MatDev* mats, const MatFlags* flags, const ApplyItem* ai,
                                int nai, int round, hipStream_t st) {
+    if (nai == 0) return hipSuccess;
     hipLaunchKernelGGL(jac_apply_kernel, dim3(nai), dim3(kApplyThreads), 0, st, mats, flags, ai, round);
+    return hipGetLastError();
+}
+
+hipError_t launch_jacobi_apply_gram(const MatDev* mats, const MatFlags* flags, const FusedItem* fi,
+                                   int nfi, int round, hipStream_t st) {
+    if (nfi == 0) return hipSuccess;
+    hipLaunchKernelGGL(jac_apply_gram_kernel, dim3(nfi), dim3(512), 0, st, mats, flags, fi, round);
     return hipGetLastError();
 }
 

@@ -426,3 +426,53 @@ def test_solve_wave_variants_bitwise():
                 assert np.array_equal(x, y)
         for x, y in zip(w, ref_w):
             assert np.array_equal(x, y)
+
+
+def test_fused_gram_matches_unfused():
+    """The fused rotation apply + next-round Gram (bfloat16 three-way split) and
+    the standalone float32 Gram give the same SVD to float32 accuracy: singular
+    values, reconstruction, G_filt within the parity gate and W after a step (on
+    the elements the W gate covers, |G_proj| >= 1e-6), on
+    power-of-two block counts (fused), others (not fused) and Cholesky-
+    preconditioned operands (fused over the factor rows)."""
+    import spectral_correction_optimizer_amd as sco
+    say("case: fused vs unfused Gram, 256x256 + 512x128 + 320x1024 + 1024x256 + 2048x512 + 96x1000")
+    dev = torch.device("cuda")
+    shapes = [(256, 256), (512, 128), (320, 1024), (1024, 256), (2048, 512), (96, 1000)]
+    ins = [gen.MatrixInputs(151, 0, i, *sh) for i, sh in enumerate(shapes)]
+    GA = [to_dev(gen.stored(mi.g_anc(0), "f32")[0], "f32", dev) for mi in ins]
+    G = [to_dev(gen.stored(mi.g_mask(0), "f32")[0], "f32", dev) for mi in ins]
+
+    def run(fuse):
+        opt = sco.SpectralAdamW(shapes, device=dev)
+        opt.set_fused_gram(fuse)
+        opt.keep_proj(True)
+        for i, mi in enumerate(ins):
+            opt.set_state(i, "m_anc", to_dev(gen.stored(mi.m0(), "f32")[0], "f32", dev))
+        W = [to_dev(gen.stored(mi.w0(), "f32")[0], "f32", dev) for mi in ins]
+        opt.anchor_update(GA)
+        opt.step(W, G)
+        torch.cuda.synchronize()
+        fac = [[t.double().cpu().numpy() for t in opt.get_factors(i)] for i in range(len(shapes))]
+        gf = [[t.double().cpu().numpy() for t in opt.get_filtered(i, proj=True)]
+              for i in range(len(shapes))]
+        out = [w.double().cpu().numpy() for w in W]
+        st = opt.stats()
+        opt.close()
+        return fac, gf, out, st
+
+    fa, gfa, wa, sa = run(True)
+    fb, gfb, wb, sb = run(False)
+    say(f"  sweeps fused {sa['sweeps']} unfused {sb['sweeps']}")
+    assert sa["not_converged"] == 0 and sb["not_converged"] == 0
+    for i, (m, n) in enumerate(shapes):
+        (Ua, sva, Va), (Ub, svb, Vb) = fa[i], fb[i]
+        s_err = np.abs(np.sort(sva)[::-1] - np.sort(svb)[::-1]).max() / svb.max()
+        rec = np.linalg.norm((Ua * sva) @ Va.T - (Ub * svb) @ Vb.T) / np.linalg.norm((Ub * svb) @ Vb.T)
+        g_rel = np.linalg.norm(gfa[i][0] - gfb[i][0]) / np.linalg.norm(gfb[i][0])
+        # W on the elements the parity gate covers: |G_proj| >= 1e-6 (near g = 0
+        # the first AdamW update amplifies any G_proj difference by lr / eps)
+        keep = np.abs(gfb[i][1]) >= 1e-6
+        w_err = np.abs(wa[i] - wb[i])[keep].max()
+        say(f"  {m}x{n}: s {s_err:.2e} recon {rec:.2e} G_filt {g_rel:.2e} W {w_err:.2e}")
+        assert s_err < 1e-5 and rec < 1e-5 and g_rel < 1e-4 and w_err < 1e-7
