@@ -59,6 +59,10 @@ def parse():
                     help="LDS copies of the pair Gram in the multi-wave solve (0: by pair count)")
     ap.add_argument("--fused-gram", action="store_true",
                     help="fused rotation apply + next-round pair Gram (sc_set_fused_gram)")
+    ap.add_argument("--cold-start", action="store_true",
+                    help="every refresh starts its sweeps from A = M (no warm start)")
+    ap.add_argument("--drift", type=float, default=0.0, metavar="THETA",
+                    help="drifting anchor signal: cos(k theta) S + sin(k theta) S' at anchor k")
     ap.add_argument("--no-precondition", action="store_true",
                     help="plain Jacobi sweeps for every matrix (no Cholesky factor phase)")
     ap.add_argument("--mask", action="store_true",
@@ -274,7 +278,7 @@ def main():
     t_gen = time.perf_counter()
     M0, W, G_anc, G_mask = [], [], [[] for _ in range(total_iters)], [[] for _ in range(total_iters)]
     for (cfg, blk, mat), (m, n) in zip(ids, shapes):
-        mi = DeviceMatrixInputs(cfg, blk, mat, m, n, dev, dtype=tdt)
+        mi = DeviceMatrixInputs(cfg, blk, mat, m, n, dev, dtype=tdt, drift=args.drift)
         M0.append(mi.m0())
         W.append(mi.w0())
         for k in range(total_iters):
@@ -287,7 +291,8 @@ def main():
 
     opt = sco.SpectralAdamW(shapes, w_dtype=tdt, g_dtype=tdt, device=dev,
                             max_sweeps=args.max_sweeps,
-                            precondition=0 if args.no_precondition else 1, **hp)
+                            precondition=0 if args.no_precondition else 1,
+                            warm_start=0 if args.cold_start else 1, **hp)
     opt.set_solve_waves(args.solve_waves, args.solve_copies)
     opt.set_fused_gram(args.fused_gram)
     for i, x in enumerate(M0):
@@ -401,6 +406,8 @@ def main():
                    "lr": hp["lr"]},
         "solve_variant": {"waves": args.solve_waves or "auto", "copies": args.solve_copies or "auto"},
         "fused_gram": args.fused_gram,
+        "warm_start": not args.cold_start,
+        "drift": args.drift,
         "refresh_ms": round(r_med, 2),
         "step_ms": round(s_med, 3),
         "amortized_step_ms_anchor_every_25": round(s_med + r_med / 25.0, 3),

@@ -30,6 +30,7 @@ ENTROPY = 260914339
 
 # stream ids inside a spawn key
 S_U0, S_V0, S_M0, S_GANC, S_GMASK, S_W = 0, 1, 2, 3, 4, 5
+S_U1, S_V1 = 6, 7  # second signal of the drifting variant (timing workloads only)
 
 # Llama-3.2-1B block shapes, row-major [out, in]
 BLOCK_SHAPES = (

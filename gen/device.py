@@ -10,7 +10,8 @@ from __future__ import annotations
 import torch
 
 from . import (ENTROPY, GANC_NOISE, GMASK_NOISE, GMASK_SIGNAL, M0_NOISE, S_GANC, S_GMASK, S_M0,
-               S_U0, S_V0, S_W, SIGNAL_POWER, SIGNAL_SCALE, W_STD)
+               S_U0, S_U1, S_V0, S_V1, S_W, SIGNAL_POWER, SIGNAL_SCALE, W_STD)
+import math
 
 
 def _seed(cfg, block, mat, stream, k=0) -> int:
@@ -44,18 +45,36 @@ def _haar(device, key, n, r, max_iter=60):
 
 
 class DeviceMatrixInputs:
-    def __init__(self, cfg, block, mat, m, n, device, dtype=torch.float32):
+    """drift = theta > 0: the drifting variant, whose anchor gradient k carries the
+    signal cos(k theta) S + sin(k theta) S' (S' an independent signal of the same
+    spectrum), so the dominant subspaces turn between anchor updates; theta = 0
+    is the fixed-subspace recipe."""
+
+    def __init__(self, cfg, block, mat, m, n, device, dtype=torch.float32, drift=0.0):
         self.key = (cfg, block, mat)
         self.m, self.n = m, n
         self.device = device
         self.dtype = dtype
+        self.drift = float(drift)
         r = min(m, n)
-        u0 = _haar(device, self.key + (S_U0,), m, r)
-        v0 = _haar(device, self.key + (S_V0,), n, r)
         i = torch.arange(1, r + 1, device=device, dtype=torch.float32)
         s0 = SIGNAL_SCALE * i.pow(-SIGNAL_POWER)
+        u0 = _haar(device, self.key + (S_U0,), m, r)
+        v0 = _haar(device, self.key + (S_V0,), n, r)
         self.signal = ((u0 * s0) @ v0.t().contiguous()).contiguous()
         del u0, v0
+        self.signal2 = None
+        if self.drift > 0.0:
+            u1 = _haar(device, self.key + (S_U1,), m, r)
+            v1 = _haar(device, self.key + (S_V1,), n, r)
+            self.signal2 = ((u1 * s0) @ v1.t().contiguous()).contiguous()
+            del u1, v1
+
+    def _anchor_signal(self, k):
+        if self.signal2 is None:
+            return self.signal
+        a = k * self.drift
+        return math.cos(a) * self.signal + math.sin(a) * self.signal2
 
     def _noise(self, stream, k, std):
         return std * torch.randn((self.m, self.n), generator=_gen(self.device, *self.key, stream, k),
@@ -65,7 +84,8 @@ class DeviceMatrixInputs:
         return (self.signal + self._noise(S_M0, 0, M0_NOISE)).contiguous()
 
     def g_anc(self, k):
-        return (self.signal + self._noise(S_GANC, k, GANC_NOISE)).to(self.dtype).contiguous()
+        return (self._anchor_signal(k) + self._noise(S_GANC, k, GANC_NOISE)).to(
+            self.dtype).contiguous()
 
     def g_mask(self, k):
         return (GMASK_SIGNAL * self.signal + self._noise(S_GMASK, k, GMASK_NOISE)).to(
