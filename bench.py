@@ -93,10 +93,10 @@ def copy_calibration(nbytes):
 # on a plain device copy of known size), valid only for the kernel source they
 # were taken on (sha256 of the file); otherwise reported as null.
 TRAFFIC = {
-    "jacobi_gram": {"source": "jacobi.hip", "sha256": "99d38fc177b694896f35ead0bb436af3390682f9e4ac65214741dc0c2c7f7f1e",
-        "bytes_per_launch": 6.46635e+08},
-    "jacobi_apply": {"source": "jacobi.hip", "sha256": "99d38fc177b694896f35ead0bb436af3390682f9e4ac65214741dc0c2c7f7f1e",
-        "bytes_per_launch": 1.17104e+09},
+    "jacobi_gram": {"source": "jacobi.hip", "sha256": "bbfe8b9be07ef3b7219d28ca23219085025352e43a750bfc95e40f228f52b20c",
+        "bytes_per_launch": 6.3279e+08},
+    "jacobi_apply": {"source": "jacobi.hip", "sha256": "bbfe8b9be07ef3b7219d28ca23219085025352e43a750bfc95e40f228f52b20c",
+        "bytes_per_launch": 1.13225e+09},
     "combine_adamw": {"source": "elementwise.hip", "sha256": "0c09b9374f97495b495395fa41dedf152598946e324adfa6ca6fe895def28277",
         "bytes_per_launch": 3.1148e+10},
     "ema": {"source": "elementwise.hip", "sha256": "0c09b9374f97495b495395fa41dedf152598946e324adfa6ca6fe895def28277",
