@@ -57,8 +57,8 @@ def parse():
                     help="wavefronts per Jacobi pair solve (0: by each launch's pair count)")
     ap.add_argument("--solve-copies", type=int, default=0, choices=[0, 1, 2],
                     help="LDS copies of the pair Gram in the multi-wave solve (0: by pair count)")
-    ap.add_argument("--fused-gram", action="store_true",
-                    help="fused rotation apply + next-round pair Gram (sc_set_fused_gram)")
+    ap.add_argument("--no-fused-gram", action="store_true",
+                    help="every Jacobi round's pair Gram from the operand (no fused apply + Gram)")
     ap.add_argument("--cold-start", action="store_true",
                     help="every refresh starts its sweeps from A = M (no warm start)")
     ap.add_argument("--drift", type=float, default=0.0, metavar="THETA",
@@ -93,14 +93,16 @@ def copy_calibration(nbytes):
 # on a plain device copy of known size), valid only for the kernel source they
 # were taken on (sha256 of the file); otherwise reported as null.
 TRAFFIC = {
-    "jacobi_gram": {"source": "jacobi.hip", "sha256": "bbfe8b9be07ef3b7219d28ca23219085025352e43a750bfc95e40f228f52b20c",
-        "bytes_per_launch": 6.3279e+08},
-    "jacobi_apply": {"source": "jacobi.hip", "sha256": "bbfe8b9be07ef3b7219d28ca23219085025352e43a750bfc95e40f228f52b20c",
-        "bytes_per_launch": 1.13225e+09},
+    "jacobi_gram": {"source": "jacobi.hip", "sha256": "46943ceb447454ad8fe327e2f553772c9dc6ac96b54db8cc8306ee3f41f1d3e2",
+        "bytes_per_launch": 1.12481e+07},
+    "jacobi_apply": {"source": "jacobi.hip", "sha256": "46943ceb447454ad8fe327e2f553772c9dc6ac96b54db8cc8306ee3f41f1d3e2",
+        "bytes_per_launch": 6.30421e+08},
     "combine_adamw": {"source": "elementwise.hip", "sha256": "0c09b9374f97495b495395fa41dedf152598946e324adfa6ca6fe895def28277",
         "bytes_per_launch": 3.1148e+10},
     "ema": {"source": "elementwise.hip", "sha256": "0c09b9374f97495b495395fa41dedf152598946e324adfa6ca6fe895def28277",
         "bytes_per_launch": 1.16866e+10},
+    "jacobi_apply_gram": {"source": "jacobi.hip", "sha256": "46943ceb447454ad8fe327e2f553772c9dc6ac96b54db8cc8306ee3f41f1d3e2",
+        "bytes_per_launch": 1.07244e+09},
 }
 
 
@@ -294,7 +296,7 @@ def main():
                             precondition=0 if args.no_precondition else 1,
                             warm_start=0 if args.cold_start else 1, **hp)
     opt.set_solve_waves(args.solve_waves, args.solve_copies)
-    opt.set_fused_gram(args.fused_gram)
+    opt.set_fused_gram(not args.no_fused_gram)
     for i, x in enumerate(M0):
         opt.set_state(i, "m_anc", x)
     del M0
@@ -405,7 +407,7 @@ def main():
                    "tau_p": hp["tau_p"], "alpha": hp["alpha"], "beta_anc": hp["beta_anc"],
                    "lr": hp["lr"]},
         "solve_variant": {"waves": args.solve_waves or "auto", "copies": args.solve_copies or "auto"},
-        "fused_gram": args.fused_gram,
+        "fused_gram": not args.no_fused_gram,
         "warm_start": not args.cold_start,
         "drift": args.drift,
         "refresh_ms": round(r_med, 2),

@@ -195,14 +195,14 @@ int sc_get_factors(sc_handle h, int idx, float* U, float* s, float* V, void* str
  * SC_ERR_INVALID_ARG.  Waits for a pending asynchronous refresh. */
 int sc_set_solve_waves(sc_handle h, int waves, int copies);
 
-/* Fused rotation apply + next-round pair Gram in the Jacobi sweeps (disabled by
+/* Fused rotation apply + next-round pair Gram in the Jacobi sweeps (enabled by
  * default): for matrices with a power-of-two number of 32-column blocks (four
  * or more) the apply of each round also forms the next round's pair Grams from
  * the rotated rows (bfloat16 matrix cores, each float split exactly into three
- * parts, six part products), saving one read of the operand per round.  The
- * default computes every round's Gram from the operand with float32 products;
- * the two agree to float32 rounding, not bit for bit.  Waits for a pending
- * asynchronous refresh. */
+ * parts, six part products), saving one read of the operand per round.
+ * enable = 0 computes every round's Gram from the operand with float32
+ * products; the two agree to float32 rounding, not bit for bit.  Waits for a
+ * pending asynchronous refresh. */
 int sc_set_fused_gram(sc_handle h, int enable);
 
 /* Keep G_proj of each step (costs one more store per element in the AdamW

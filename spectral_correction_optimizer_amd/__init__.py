@@ -282,7 +282,7 @@ class SpectralAdamW:
         _check(self._lib.sc_set_solve_waves(self._h, int(waves), int(copies)))
 
     def set_fused_gram(self, enable: bool = True):
-        """Fused rotation apply + next-round pair Gram (default off)."""
+        """Fused rotation apply + next-round pair Gram (default on)."""
         _check(self._lib.sc_set_fused_gram(self._h, 1 if enable else 0))
 
     def keep_proj(self, enable: bool = True):

@@ -213,7 +213,7 @@ struct sc_opt {
     bool any_stale = false;
     bool proj_stale = false;
     bool keep_proj = false;
-    bool fuse = false;                        // fused apply + next Gram where a matrix allows it
+    bool fuse = true;                         // fused apply + next Gram where a matrix allows it
     std::vector<std::array<char, 2>> fused;   // per matrix: fused over the factor / full rows
     int solve_waves = 0, solve_copies = 0;  // pair solve variant: 0 by the launch's pair count
     std::vector<void*> dev_allocs;

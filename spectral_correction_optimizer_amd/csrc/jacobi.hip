@@ -838,11 +838,12 @@ __global__ __launch_bounds__(kApplyThreads) void jac_apply_kernel(const MatDev* 
 // 32 columns each (as jac_apply_kernel, the next chunk's loads in flight), and
 // store the rotated rows; the chunk's 128 new rows then go through LDS into the
 // next round's six 32 x 32 Gram tiles (two pairs: lower-lower, lower-upper,
-// upper-upper), dealt as 24 (tile, 32-column quarter) units, three per wave, on
-// the bfloat16 matrix cores with each float split exactly into three bfloat16
-// parts and the six largest part products (v_mfma_f32_32x32x16_bf16, float32
-// accumulation over a unit's <= 256 columns of the split).  At the end of the
-// split the four quarters of each tile are summed in float64 in a fixed order
+// upper-upper): wave w forms the three tiles of pair w / 4 over columns
+// 32 (w % 4) .. + 31 of each chunk, splitting its two row fragments once per
+// k-step, on the bfloat16 matrix cores with each float split exactly into three
+// bfloat16 parts and the six largest part products (v_mfma_f32_32x32x16_bf16,
+// float32 accumulation over the wave's <= 256 columns of the split).  At the end
+// of the split the four quarters of each tile are summed in float64 in a fixed order
 // into the split partial the solve of round r + 1 reads, so the operand is not
 // read again for that round's Gram.  In the last round of a sweep (the next one
 // starts with the sort) only the rotations are applied.
@@ -915,19 +916,12 @@ __global__ __launch_bounds__(512) void jac_apply_gram_kernel(const MatDev* __res
 #pragma unroll
         for (int s = 0; s < PW / 2; ++s) x[s] = buf_load_f32<kBufNT>(buf, voff[s], so);
     };
-    // Gram units of the wave: u = 3 wave + j -> tile u / 4 (0-2 of A', 3-5 of B':
-    // lower-lower, lower-upper, upper-upper), columns 32 (u % 4) .. + 31 of a chunk
+    // the wave's Gram work: the next round's pair wave / 4 (A' or B'; its lower
+    // block U and upper block V as rows of the chunk block), tiles U U^T, U V^T,
+    // V V^T over the chunk's columns 32 (wave % 4) .. + 31
     auto tblk = [&](int blk) { return blk == a0 ? 0 : blk == a1 ? 1 : blk == b0 ? 2 : 3; };
-    const int bu0 = 32 * tblk(n0), bv0 = 32 * tblk(n1), bu1 = 32 * tblk(n2), bv1 = 32 * tblk(n3);
-    int urow[3], vrow[3], ucol[3];
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-        const int u = 3 * wave + j, t = u >> 2;
-        const int bu = t < 3 ? bu0 : bu1, bv = t < 3 ? bv0 : bv1, tt = t % 3;
-        urow[j] = (tt == 2 ? bv : bu) + ll;
-        vrow[j] = (tt == 0 ? bu : bv) + ll;
-        ucol[j] = 32 * (u & 3) + 8 * hl;
-    }
+    const int urow = 32 * tblk(wave < 4 ? n0 : n2) + ll, vrow = 32 * tblk(wave < 4 ? n1 : n3) + ll;
+    const int ucol = 32 * (wave & 3) + 8 * hl;
     v16f gacc[3];
 #pragma unroll
     for (int j = 0; j < 3; ++j)
@@ -984,13 +978,13 @@ __global__ __launch_bounds__(512) void jac_apply_gram_kernel(const MatDev* __res
         for (int s = 0; s < PW / 2; ++s) Ts[PW * q + apply_row(s, hl)][32 * wq + ll] = x[s];
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const Split8 fu = frag(urow[j], ucol[j] + 16 * ks);
-                const Split8 fv = frag(vrow[j], ucol[j] + 16 * ks);
-                gacc[j] = mfma_split6(fu, fv, gacc[j]);
-            }
+        for (int ks = 0; ks < 2; ++ks) {
+            const Split8 fu = frag(urow, ucol + 16 * ks);
+            const Split8 fv = frag(vrow, ucol + 16 * ks);
+            gacc[0] = mfma_split6(fu, fu, gacc[0]);
+            gacc[1] = mfma_split6(fu, fv, gacc[1]);
+            gacc[2] = mfma_split6(fv, fv, gacc[2]);
+        }
         __syncthreads();  // before the next chunk's rows
     };
     float xa[PW / 2], xb[PW / 2];
@@ -1020,9 +1014,9 @@ __global__ __launch_bounds__(512) void jac_apply_gram_kernel(const MatDev* __res
     }
     if (!gram) return;
     // 4. per tile the four column quarters summed in float64 (quarter order) into
-    //    the split partials of the next round's pairs: tiles 0-2 of A' (units
-    //    0-11, waves 0-3), 3-5 of B' (units 12-23, waves 4-7); the upper tiles of
-    //    the 64 x 64 Gram (its lower triangle is not read)
+    //    the split partials of the next round's pairs: A' from waves 0-3, B' from
+    //    waves 4-7; the upper tiles of the 64 x 64 Gram (its lower triangle is not
+    //    read)
     float* red = &Ts[0][0];
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps) {
@@ -1031,7 +1025,7 @@ __global__ __launch_bounds__(512) void jac_apply_gram_kernel(const MatDev* __res
             for (int j = 0; j < 3; ++j)
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4)
-                    *(v4f*)&red[((3 * wave + j - 12 * ps) * 64 + lane) * 16 + 4 * r4] =
+                    *(v4f*)&red[((3 * (wave - 4 * ps) + j) * 64 + lane) * 16 + 4 * r4] =
                         v4f{gacc[j][4 * r4], gacc[j][4 * r4 + 1], gacc[j][4 * r4 + 2], gacc[j][4 * r4 + 3]};
         __syncthreads();
         double* out = md.gram + ((int64_t)(ps == 0 ? slotA2 : slotB2) * md.nsplit + it.split) * (PW * PW);
@@ -1039,7 +1033,7 @@ __global__ __launch_bounds__(512) void jac_apply_gram_kernel(const MatDev* __res
             const int t = e >> 10, l = (e >> 4) & 63, r = e & 15;
             double sum = 0.0;
 #pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4) sum += (double)red[(4 * t + k4) * 1024 + (e & 1023)];
+            for (int k4 = 0; k4 < 4; ++k4) sum += (double)red[(3 * k4 + t) * 1024 + (e & 1023)];
             const int i = 8 * (r >> 2) + 4 * (l >> 5) + (r & 3), jj = l & 31;
             const int row = (t == 2 ? 32 : 0) + i, col = (t == 0 ? 0 : 32) + jj;
             gst(out + row * PW + col, sum);
