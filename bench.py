@@ -94,7 +94,7 @@ def copy_calibration(nbytes):
 # were taken on (sha256 of the file); otherwise reported as null.
 TRAFFIC = {
     "jacobi_gram": {"source": "jacobi.hip", "sha256": "46943ceb447454ad8fe327e2f553772c9dc6ac96b54db8cc8306ee3f41f1d3e2",
-        "bytes_per_launch": 1.12481e+07},
+        "bytes_per_launch": 2.26492e+08},
     "jacobi_apply": {"source": "jacobi.hip", "sha256": "46943ceb447454ad8fe327e2f553772c9dc6ac96b54db8cc8306ee3f41f1d3e2",
         "bytes_per_launch": 6.30421e+08},
     "combine_adamw": {"source": "elementwise.hip", "sha256": "0c09b9374f97495b495395fa41dedf152598946e324adfa6ca6fe895def28277",
@@ -102,7 +102,7 @@ TRAFFIC = {
     "ema": {"source": "elementwise.hip", "sha256": "0c09b9374f97495b495395fa41dedf152598946e324adfa6ca6fe895def28277",
         "bytes_per_launch": 1.16866e+10},
     "jacobi_apply_gram": {"source": "jacobi.hip", "sha256": "46943ceb447454ad8fe327e2f553772c9dc6ac96b54db8cc8306ee3f41f1d3e2",
-        "bytes_per_launch": 1.07244e+09},
+        "bytes_per_launch": 1.07243e+09},
 }
 
 

@@ -156,6 +156,7 @@ struct sc_opt {
         int nai_f = 0;
         FusedItem* fi = nullptr;
         int nfi = 0;
+        bool all_fused = false;  // every matrix of the list has the fused apply + Gram
         int* mats = nullptr;
         int nmat = 0;
         int max_nb = 2;
@@ -545,8 +546,11 @@ int pipe_round(sc_opt* h, Pipe& p, hipStream_t st) {
         HIP_TRY(timed(h, PK_SORT, st, [&] {
             return launch_jacobi_sort(h->md, h->flags_d, L.mats, L.nmat, r, st);
         }));
-    HIP_TRY(timed(h, PK_GRAM, st,
-                  [&] { return launch_jacobi_gram(h->md, h->flags_d, L.gi, L.ngi, r, h->fuse ? 1 : 0, st); }));
+    // with every matrix fused the standalone Gram only serves sweeps' first rounds
+    if (!(h->fuse && L.all_fused) || first)
+        HIP_TRY(timed(h, PK_GRAM, st, [&] {
+            return launch_jacobi_gram(h->md, h->flags_d, L.gi, L.ngi, r, h->fuse ? 1 : 0, st);
+        }));
     HIP_TRY(timed(h, PK_SOLVE, st,
                   [&] { return launch_jacobi_solve(h->md, h->flags_d, L.si, L.nsi, r, h->solve_waves, h->solve_copies, st); }));
     if (h->fuse && L.nfi) {
@@ -1052,6 +1056,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             std::vector<GramItem> gi;
             std::vector<SolveItem> si;
             std::vector<ApplyItem> ai, ai_f;
+            bool any_unfused = false;
             std::vector<FusedItem> fi;
             std::vector<int> mats;
             auto& L = P.L[which];
@@ -1078,6 +1083,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
                     }
                 }
                 h->fused[i][which == LIST_FACTOR && m.klen ? 0 : 1] = fuse;
+                any_unfused = any_unfused || !fuse;
                 if (fuse)
                     for (int grp = 0; grp < m.nb / 4; ++grp)
                         for (int sp = 0; sp < ns; ++sp)
@@ -1108,6 +1114,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             if ((rc = upload(ai, &L.ai, &L.nai))) return rc;
             if ((rc = upload(ai_f, &L.ai_f, &L.nai_f))) return rc;
             if ((rc = upload(fi, &L.fi, &L.nfi))) return rc;
+            L.all_fused = !mats.empty() && !any_unfused;
             if ((rc = upload(mats, &L.mats, &L.nmat))) return rc;
         }
         std::vector<int> cap;
