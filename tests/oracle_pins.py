@@ -306,6 +306,112 @@ def pin_storage_rounding(o):
     assert o.round_storage(np.array([0.1]), "f32")[0] == float(np.float32(0.1))
 
 
+# ---- the stateful driver: anchor EMA -> refresh -> steps, with storage rounding ------
+
+_WORKED_HP = dict(tau_p=1.0, alpha=0.3, beta_anc=0.75, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                  weight_decay=1e-2)
+# an anchor gradient with every row non-zero (the worked M has a zero fourth row)
+_WORKED_GANC = [[1.0, 2.0, 0.0], [0.0, -1.0, 1.0], [0.5, 0.0, -2.0], [1.0, 1.0, 1.0]]
+
+
+def pin_optimizer_driver_worked_4x3(o):
+    """``Optimizer`` chains the EMA of "Key design 2", the refresh, the filter and
+    projection of "Key design 3" and AdamW in the right order and with the right
+    arguments: two anchor arrivals with the same gradient G from M0 give
+    M = b^2 M0 + (1 - b^2) G, and M0 is chosen so that this is the hand-worked M;
+    the steps then reproduce the hand-worked G_filt, G_proj and the AdamW closed
+    form.  An anchor arrival between steps (here one that leaves M in place) does
+    not advance the step count."""
+    g = json.load(open(os.path.join(GOLDEN, "worked_4x3.json")))
+    a = g["adamw"]
+    hp = dict(_WORKED_HP)
+    assert hp["tau_p"] == g["tau_p"] and hp["alpha"] == g["alpha"] and hp["lr"] == a["lr"]
+    b = hp["beta_anc"]
+    M = np.array(g["M"])
+    Ga = np.array(_WORKED_GANC)
+    M0 = (M - (1.0 - b * b) * Ga) / (b * b)
+    opt = o.Optimizer([(4, 3)], hp, w_dtype="f64", state_dtype="f64", threads=1)
+    opt.set_anchor_momentum(0, M0)
+    opt.anchor_update([Ga])
+    assert not np.allclose(opt.M[0], M, atol=1e-3)  # one arrival is not there yet
+    opt.anchor_update([Ga])
+    assert np.allclose(opt.M[0], M, rtol=0, atol=1e-14), opt.M[0]
+    U, s, V = opt.factors[0]
+    assert np.allclose(s, g["singular_values"], rtol=0, atol=1e-14), s
+    assert np.allclose(opt.d[0], [float(Fraction(x)) for x in g["d"]], rtol=0, atol=1e-14)
+    assert opt.t == 0
+    G = np.array(g["G_mask"])
+    gp = _frac(g["G_proj"])
+    W = np.full((4, 3), a["W0"])
+    c = 1.0 - a["lr"] * a["weight_decay"]
+    r = gp / (np.abs(gp) + a["eps"])
+    for t in range(1, a["T"] + 1):
+        W = opt.step([W], [G])[0]
+        assert opt.t == t
+        assert np.allclose(opt.last_filt[0], _frac(g["G_filt"]), rtol=0, atol=1e-14)
+        assert np.allclose(opt.last_proj[0], gp, rtol=0, atol=1e-14)
+        WT = c ** t * a["W0"] - a["lr"] * r * (1.0 - c ** t) / (1.0 - c)
+        assert np.allclose(W, WT, rtol=0, atol=1e-14), (t, np.abs(W - WT).max())
+        if t == 2:
+            opt.anchor_update([M])  # b M + (1 - b) M = M: same factors, t unchanged
+            assert opt.t == 2 and np.allclose(opt.M[0], M, rtol=0, atol=1e-14)
+
+
+def _rne_f32(x):
+    return np.asarray(x, np.float64).astype(np.float32).astype(np.float64)
+
+
+def _rne_bf16(x):
+    """Round float64 to bfloat16 (8 significant bits), nearest-even, on the bit
+    pattern: add half of the dropped 45-bit field (minus one unless the kept
+    last bit is odd) and clear the field.  Normal numbers only."""
+    x = np.asarray(x, np.float64)
+    u = x.view(np.uint64)
+    keep = (u >> np.uint64(45)) & np.uint64(1)
+    u = (u + np.uint64((1 << 44) - 1) + keep) & ~np.uint64((1 << 45) - 1)
+    return u.view(np.float64)
+
+
+def pin_optimizer_storage_rounding(o):
+    """After every call, the state the driver stores in a narrower type (M_anc
+    after an anchor arrival; m, v and W after a step) is the round-to-nearest-even
+    of what the same call computes in float64 from the same stored inputs.  The
+    float64 driver is re-seeded with the narrow driver's state before each call."""
+    rng_ = np.random.default_rng(123)
+    shape = (7, 5)
+    hp = dict(tau_p=1e-3, alpha=0.3, beta_anc=0.9, lr=2e-5, beta1=0.9, beta2=0.999, eps=1e-8,
+              weight_decay=0.01)
+    w_round = {"f32": _rne_f32, "bf16": _rne_bf16}
+    assert _rne_bf16(np.array([1.0 + 2.0 ** -8]))[0] == 1.0
+    assert _rne_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
+    for wdt in ("f32", "bf16"):
+        nar = o.Optimizer([shape], hp, w_dtype=wdt, state_dtype="f32", threads=1)
+        wide = o.Optimizer([shape], hp, w_dtype="f64", state_dtype="f64", threads=1)
+        M0 = _rne_f32(1e-2 * rng_.standard_normal(shape))
+        nar.set_anchor_momentum(0, M0)
+        W = w_round[wdt](0.02 * rng_.standard_normal(shape))
+        for call in range(6):
+            if call in (0, 3):
+                Ga = _rne_f32(1e-2 * rng_.standard_normal(shape))
+                wide.M[0] = nar.M[0].copy()
+                nar.anchor_update([Ga])
+                wide.anchor_update([Ga])
+                assert np.array_equal(nar.M[0], _rne_f32(wide.M[0])), (wdt, call)
+                assert not np.array_equal(nar.M[0], wide.M[0])
+                continue
+            wide.M[0], wide.m[0], wide.v[0], wide.t = nar.M[0].copy(), nar.m[0].copy(), \
+                nar.v[0].copy(), nar.t
+            wide.factors[0], wide.d[0] = nar.factors[0], nar.d[0]
+            G = _rne_f32(1e-3 * rng_.standard_normal(shape))
+            Wn = nar.step([W], [G])[0]
+            Ww = wide.step([W], [G])[0]
+            assert np.array_equal(nar.m[0], _rne_f32(wide.m[0])), (wdt, call, "m")
+            assert np.array_equal(nar.v[0], _rne_f32(wide.v[0])), (wdt, call, "v")
+            assert np.array_equal(Wn, w_round[wdt](Ww)), (wdt, call, "W")
+            assert not (np.array_equal(nar.v[0], wide.v[0]) and np.array_equal(nar.m[0], wide.m[0]))
+            W = Wn
+
+
 # ---- the in-graph activation mask ("Key design 1") -------------------------------
 
 def pin_mask_keep_count(o):

@@ -147,6 +147,89 @@ def test_svd_mutation_is_caught(name, oracle_mod, monkeypatch):
     assert _pins_fail(oracle_mod), f"mutation {name} passed every pin"
 
 
+# ---- the stateful driver (oracle.Optimizer): call sites and storage rounding -------
+
+def _driver_mutations(o):
+    """Plausible mistakes in how ``Optimizer`` chains the steps, each as
+    (method name, replacement)."""
+    Opt = o.Optimizer
+    step_orig = Opt.step
+
+    def anchor_swapped(self, G_anc_list):
+        for i, G in enumerate(G_anc_list):
+            self.M[i] = o.round_storage(o.ema(G, self.M[i], self.hp["beta_anc"]), self.state_dtype)
+            self._refresh(i)
+
+    def anchor_no_refresh(self, G_anc_list):
+        for i, G in enumerate(G_anc_list):
+            self.M[i] = o.round_storage(o.ema(self.M[i], G, self.hp["beta_anc"]), self.state_dtype)
+            if self.factors[i] is None:
+                self._refresh(i)
+
+    def anchor_not_rounded(self, G_anc_list):
+        for i, G in enumerate(G_anc_list):
+            self.M[i] = o.ema(self.M[i], G, self.hp["beta_anc"])
+            self._refresh(i)
+
+    def anchor_advances_t(self, G_anc_list):
+        self.t += 1
+        for i, G in enumerate(G_anc_list):
+            self.M[i] = o.round_storage(o.ema(self.M[i], G, self.hp["beta_anc"]), self.state_dtype)
+            self._refresh(i)
+
+    def _step_variant(skip):
+        def step(self, W_list, G_mask_list):
+            hp = self.hp
+            self.t += 1
+            out = []
+            for i, (W, G) in enumerate(zip(W_list, G_mask_list)):
+                if self.factors[i] is None:
+                    self._refresh(i)
+                U, s, V = self.factors[i]
+                G = np.asarray(G, np.float64)
+                G_filt = o.project(U, self.d[i], V, G)
+                G_proj = o.combine(G, G_filt, hp["alpha"])
+                W_new, m_new, v_new = o.adamw(W, self.m[i], self.v[i], G_proj, self.t, hp["lr"],
+                                              hp["beta1"], hp["beta2"], hp["eps"],
+                                              hp["weight_decay"])
+                self.m[i] = m_new if skip == "m" else o.round_storage(m_new, self.state_dtype)
+                self.v[i] = v_new if skip == "v" else o.round_storage(v_new, self.state_dtype)
+                if skip != "W":
+                    W_new = o.round_storage(W_new, self.w_dtype)
+                self.last_filt[i] = G_filt
+                self.last_proj[i] = G_proj
+                out.append(W_new)
+            return out
+        return step
+
+    assert step_orig is not None
+    return {
+        "driver_ema_args_swapped": ("anchor_update", anchor_swapped),
+        "driver_anchor_keeps_old_factors": ("anchor_update", anchor_no_refresh),
+        "driver_anchor_momentum_not_rounded": ("anchor_update", anchor_not_rounded),
+        "driver_anchor_advances_step_count": ("anchor_update", anchor_advances_t),
+        "driver_m_not_rounded": ("step", _step_variant("m")),
+        "driver_v_not_rounded": ("step", _step_variant("v")),
+        "driver_w_not_rounded": ("step", _step_variant("W")),
+    }
+
+
+DRIVER_MUTATIONS = ["driver_anchor_advances_step_count", "driver_anchor_keeps_old_factors",
+                    "driver_anchor_momentum_not_rounded", "driver_ema_args_swapped",
+                    "driver_m_not_rounded", "driver_v_not_rounded", "driver_w_not_rounded"]
+
+
+@pytest.mark.parametrize("name", DRIVER_MUTATIONS)
+def test_driver_mutation_is_caught(name, oracle_mod, monkeypatch):
+    attr, fn = _driver_mutations(oracle_mod)[name]
+    monkeypatch.setattr(oracle_mod.Optimizer, attr, fn)
+    assert _pins_fail(oracle_mod), f"mutation {name} passed every pin"
+
+
+def test_driver_mutation_list_is_complete(oracle_mod):
+    assert sorted(_driver_mutations(oracle_mod)) == DRIVER_MUTATIONS
+
+
 # ---- the in-graph activation mask ------------------------------------------------
 
 def _mask_mutations(mk):
