@@ -12,9 +12,12 @@ Gaussian noise).
 
 Prints one JSON line: value = ms per pass (refresh + step); the refresh and
 step parts, the amortized per-step time when the anchor arrives every 25
-steps, a roofline figure for the dominant kernel (HIP events around its
-launches, algorithmic work from the library's counters) and the fp64 CPU
-oracle timed on a bounded sample of the same workload.
+steps, a roofline figure for the dominant kernel (HIP events around each of
+its launches in the timed region, on the stream it runs on, algorithmic work
+from the library's counters) and the fp64 CPU oracle timed on a bounded
+sample of the same workload.  Every pass draws fresh anchor and masked
+gradients, so the anchor EMA moves towards its steady state over the passes
+(the default 5 warm-up + 20 timed passes reach it).
 """
 from __future__ import annotations
 
@@ -30,7 +33,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_FP32_MFMA_TFLOPS = 157.3
-PEAK_FP32_VALU_TFLOPS = 157.3  # fp32 vector peak (256 CUs x 2.4 GHz x 256 flop/clk, packed FMA)
+# fp32 vector peak without packed FP32 (the library is built without it): 256 CUs x
+# 4 SIMDs x 16 lanes x 2 flop (FMA) x 2.4 GHz
+PEAK_FP32_VALU_TFLOPS = 78.6
 PEAK_HBM_GBPS = 8000.0
 METRIC = "spectral-AdamW step ms + SVD refresh ms, 1B-shape params; %MFMA/%HBM peak"
 
@@ -38,17 +43,24 @@ METRIC = "spectral-AdamW step ms + SVD refresh ms, 1B-shape params; %MFMA/%HBM p
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="blocks16_1b",
                     choices=["blocks16_1b", "blocks16_1b_bf16", "block_1b", "q_proj_2048",
                              "block_8b", "blocks4_8b"])
     ap.add_argument("--tau", type=float, default=None, help="override tau_p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-kernel-times", action="store_true")
-    ap.add_argument("--profile-timed", action="store_true",
-                    help="time kernels inside the timed region itself (serializes the two "
-                         "Jacobi streams) instead of in one extra pass after it")
+    ap.add_argument("--no-kernel-times", action="store_true",
+                    help="no per-kernel event timing in the timed region")
+    ap.add_argument("--serial-kernel-times", action="store_true",
+                    help="per-kernel times from one extra pass after the timed region with every "
+                         "kernel alone on one stream (no overlap), instead of the timed region")
+    ap.add_argument("--trace-sweeps", action="store_true",
+                    help="diagnostic: synchronize after every pass and print its sweep counts "
+                         "by shape (stderr)")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="only time the oracle in full on one matrix of each shape class (one "
+                         "anchor update, one step) plus a single-thread run, and exit")
     ap.add_argument("--max-sweeps", type=int, default=30)
     ap.add_argument("--async-refresh", type=int, default=0, metavar="N",
                     help="also time N steps alone and N steps issued beside an asynchronous "
@@ -88,32 +100,24 @@ def copy_calibration(nbytes):
                       "read_bytes": n * 4, "write_bytes": n * 4}), flush=True)
 
 
-# HBM bytes per launch of a kernel family from rocprofv3 counter passes
-# (FETCH_SIZE x read calibration + WRITE_SIZE x write calibration, calibrated
-# on a plain device copy of known size), valid only for the kernel source they
-# were taken on (sha256 of the file); otherwise reported as null.
-TRAFFIC = {
-    "jacobi_gram": {"source": "jacobi.hip", "sha256": "46943ceb447454ad8fe327e2f553772c9dc6ac96b54db8cc8306ee3f41f1d3e2",
-        "bytes_per_launch": 2.26492e+08},
-    "jacobi_apply": {"source": "jacobi.hip", "sha256": "46943ceb447454ad8fe327e2f553772c9dc6ac96b54db8cc8306ee3f41f1d3e2",
-        "bytes_per_launch": 6.30421e+08},
-    "combine_adamw": {"source": "elementwise.hip", "sha256": "0c09b9374f97495b495395fa41dedf152598946e324adfa6ca6fe895def28277",
-        "bytes_per_launch": 3.1148e+10},
-    "ema": {"source": "elementwise.hip", "sha256": "0c09b9374f97495b495395fa41dedf152598946e324adfa6ca6fe895def28277",
-        "bytes_per_launch": 1.16866e+10},
-    "jacobi_apply_gram": {"source": "jacobi.hip", "sha256": "46943ceb447454ad8fe327e2f553772c9dc6ac96b54db8cc8306ee3f41f1d3e2",
-        "bytes_per_launch": 1.07243e+09},
-}
+# HBM bytes per launch of a kernel family from two rocprofv3 counter passes
+# (FETCH_SIZE, then WRITE_SIZE, each scaled by the reading of a plain device
+# copy of known size) over the same command's dispatches: keyed by the kernel
+# source (sha256 of the file), the workload and the pass schedule (warm-up and
+# timed passes), since the bytes per launch depend on the launch mix (sweeps,
+# rotated pairs); anything else is reported as null.
+TRAFFIC = {}
 
 
-def traffic_for(name):
+def traffic_for(name, workload, warmup, steps):
     import hashlib
-    t = TRAFFIC.get(name)
-    if not t:
-        return None
-    src = os.path.join(ROOT, "spectral_correction_optimizer_amd", "csrc", t["source"])
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    return t["bytes_per_launch"] if h == t["sha256"] else None
+    for t in TRAFFIC.get(name, []):
+        if (t["workload"], t["warmup"], t["steps"]) != (workload, warmup, steps):
+            continue
+        src = os.path.join(ROOT, "spectral_correction_optimizer_amd", "csrc", t["source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() == t["sha256"]:
+            return t["bytes_per_launch"]
+    return None
 
 
 def flops_step_chain(m, n):
@@ -126,43 +130,113 @@ def flops_step_chain(m, n):
     return 4.0 * K * k * k + 2.0 * k ** 3
 
 
-def cpu_baseline(hp):
-    """Time the fp64 oracle on one 512x2048 (k_proj-shaped) matrix of the
-    workload: one anchor update (EMA + Jacobi SVD) and one step; scale to the
-    112-matrix pass by the ratio of Jacobi per-sweep flops (8 K k^2 + 4 k^3,
-    equal sweep counts assumed) and of step-chain flops."""
-    import numpy as np
+def _sweep_flops(m, n):
+    K, k = max(m, n), min(m, n)
+    return 8.0 * K * k * k + 4.0 * k ** 3
 
+
+# Oracle sweeps per refresh for each shape class of the 16-block workload, from
+# `bench.py --cpu-full` (one matrix of each class, anchor momentum of block 0
+# after one anchor arrival): the bounded baseline below times one sweep and one
+# step per class and scales the sweep by these counts.
+ORACLE_SWEEPS = {}
+
+
+def _shape_classes():
+    import gen
+    classes = {}
+    for _, m, n in gen.BLOCK_SHAPES:
+        classes[(m, n)] = classes.get((m, n), 0) + gen.N_BLOCKS
+    return classes
+
+
+def cpu_baseline(hp):
+    """The fp64 oracle on the machine's host cores, on a bounded sample of the
+    16-block pass: for each of the four shape classes one matrix of block 0, one
+    Jacobi sweep of its anchor momentum (oracle.svd with a one-sweep cap) and one
+    step (projection + combination + AdamW); each class's refresh is the sweep
+    time times the oracle's sweep count for that class (ORACLE_SWEEPS, measured
+    in full by --cpu-full), and the pass is the sum over classes times the
+    number of matrices of each class.  Plus one sweep of the k_proj shape on a
+    single thread for the scaling."""
     import gen
     import oracle
 
     threads = oracle.default_threads()
-    m, n = 512, 2048
-    mi = gen.MatrixInputs(4, 0, 1, m, n)
-    ora = oracle.Optimizer([(m, n)], hp, threads=threads)
-    ora.set_anchor_momentum(0, gen.stored(mi.m0(), "f32")[1])
-    W = [gen.stored(mi.w0(), "f32")[1]]
-    G_anc = gen.stored(mi.g_anc(0), "f32")[1]
-    G = gen.stored(mi.g_mask(0), "f32")[1]
+    per_class, total_ms, t_all = {}, 0.0, time.perf_counter()
+    mats = {(m, n): i for i, (_, m, n) in enumerate(gen.BLOCK_SHAPES)}
+    for (m, n), count in _shape_classes().items():
+        mi = gen.MatrixInputs(4, 0, mats[(m, n)], m, n)
+        M = gen.stored(mi.m0(), "f32")[1]
+        t0 = time.perf_counter()
+        U, sv, V, _ = oracle.svd(M, max_sweeps=1, threads=threads)
+        t_sweep = time.perf_counter() - t0
+        # the step on the one-sweep factors costs what it costs on converged ones
+        ora = oracle.Optimizer([(m, n)], hp, threads=threads)
+        ora.set_anchor_momentum(0, M)
+        ora.factors[0] = (U, sv, V)
+        ora.d[0] = oracle.tikhonov(sv, hp["tau_p"])
+        W = [gen.stored(mi.w0(), "f32")[1]]
+        G = [gen.stored(mi.g_mask(0), "f32")[1]]
+        t0 = time.perf_counter()
+        ora.step(W, G)
+        t_step = time.perf_counter() - t0
+        sw = ORACLE_SWEEPS.get(f"{m}x{n}")
+        refresh_ms = t_sweep * 1e3 * sw if sw else None
+        per_class[f"{m}x{n}"] = {"count": count, "sweep_s": round(t_sweep, 3), "oracle_sweeps": sw,
+                                 "step_s": round(t_step, 3)}
+        if refresh_ms is not None:
+            total_ms += count * (refresh_ms + t_step * 1e3)
+    mi = gen.MatrixInputs(4, 0, 1, 512, 2048)
     t0 = time.perf_counter()
-    ora.anchor_update([G_anc])
-    t1 = time.perf_counter()
-    ora.step(W, [G])
-    t2 = time.perf_counter()
+    oracle.svd(gen.stored(mi.m0(), "f32")[1], max_sweeps=1, threads=1)
+    t_single = time.perf_counter() - t0
+    complete = all(v["oracle_sweeps"] for v in per_class.values())
+    return {"value": round(total_ms, 1) if complete else None, "unit": "ms", "cores": threads,
+            "kind": "oracle",
+            "sample": ("one matrix per shape class (block 0): one Jacobi sweep + one step each, "
+                       "sweeps scaled by the oracle's full sweep count per class, times the class "
+                       f"counts of the 112-matrix pass; {time.perf_counter() - t_all:.1f} s of CPU "
+                       f"time on {threads} threads"),
+            "per_class": per_class,
+            "single_thread_sweep_s_512x2048": round(t_single, 3)}
 
-    def sweep_flops(a, b):
-        K, k = max(a, b), min(a, b)
-        return 8.0 * K * k * k + 4.0 * k ** 3
 
-    shapes = [(mm, nn) for _ in range(gen.N_BLOCKS) for _, mm, nn in gen.BLOCK_SHAPES]
-    svd_scale = sum(sweep_flops(*s) for s in shapes) / sweep_flops(m, n)
-    step_scale = sum(flops_step_chain(*s) for s in shapes) / flops_step_chain(m, n)
-    ms = ((t1 - t0) * svd_scale + (t2 - t1) * step_scale) * 1e3
-    return {"value": round(ms, 1), "unit": "ms", "cores": threads, "kind": "oracle",
-            "sample": (f"one 512x2048 matrix (k_proj shape, block 0): anchor update "
-                       f"{(t1 - t0):.2f} s (Jacobi sweeps {ora.sweeps[0]}) + step {(t2 - t1):.3f} s, "
-                       f"scaled x{svd_scale:.0f} (Jacobi sweep flops) and x{step_scale:.0f} "
-                       f"(chain flops) to the 112-matrix pass; extrapolated")}
+def cpu_full(hp):
+    """The oracle in full on one matrix of each shape class: one anchor update
+    (EMA + Jacobi SVD to convergence) and one step, with its thread count, plus
+    the 512x2048 anchor update on one thread; prints one JSON line."""
+    import gen
+    import oracle
+
+    threads = oracle.default_threads()
+    mats = {(m, n): i for i, (_, m, n) in enumerate(gen.BLOCK_SHAPES)}
+    res = {"threads": threads, "classes": {}}
+    for (m, n), count in _shape_classes().items():
+        mi = gen.MatrixInputs(4, 0, mats[(m, n)], m, n)
+        ora = oracle.Optimizer([(m, n)], hp, threads=threads)
+        ora.set_anchor_momentum(0, gen.stored(mi.m0(), "f32")[1])
+        ga = gen.stored(mi.g_anc(0), "f32")[1]
+        W = [gen.stored(mi.w0(), "f32")[1]]
+        G = [gen.stored(mi.g_mask(0), "f32")[1]]
+        t0 = time.perf_counter()
+        ora.anchor_update([ga])
+        t1 = time.perf_counter()
+        ora.step(W, G)
+        t2 = time.perf_counter()
+        res["classes"][f"{m}x{n}"] = {"count": count, "anchor_update_s": round(t1 - t0, 2),
+                                     "sweeps": ora.sweeps[0], "step_s": round(t2 - t1, 3)}
+        print(f"# {m}x{n}: anchor update {t1 - t0:.1f} s ({ora.sweeps[0]} sweeps), "
+              f"step {t2 - t1:.2f} s", file=sys.stderr, flush=True)
+    res["pass_s"] = round(sum(c["count"] * (c["anchor_update_s"] + c["step_s"])
+                              for c in res["classes"].values()), 1)
+    mi = gen.MatrixInputs(4, 0, 1, 512, 2048)
+    ora = oracle.Optimizer([(512, 2048)], hp, threads=1)
+    ora.set_anchor_momentum(0, gen.stored(mi.m0(), "f32")[1])
+    t0 = time.perf_counter()
+    ora.anchor_update([gen.stored(mi.g_anc(0), "f32")[1]])
+    res["single_thread_512x2048_anchor_update_s"] = round(time.perf_counter() - t0, 2)
+    print(json.dumps(res), flush=True)
 
 
 def async_measure(opt, W, g_anc, G_mask, n):
@@ -259,9 +333,16 @@ def main():
                           "built", "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
+    import gen
+    hp = dict(gen.DEFAULT_HP)
+    if args.tau is not None:
+        hp["tau_p"] = args.tau
+    if args.cpu_full:
+        cpu_full(hp)
+        return
+
     import torch
 
-    import gen
     from gen.device import DeviceMatrixInputs
     import spectral_correction_optimizer_amd as sco
 
@@ -270,26 +351,27 @@ def main():
     wl = gen.workload(args.workload)
     bf16 = wl["dtype"] == "bf16"
     tdt = torch.bfloat16 if bf16 else torch.float32
-    hp = dict(gen.DEFAULT_HP)
-    if args.tau is not None:
-        hp["tau_p"] = args.tau
     shapes, ids = wl["shapes"], wl["ids"]
-    extra_pass = not args.no_kernel_times and not args.profile_timed
-    total_iters = args.warmup + args.steps + (1 if extra_pass else 0)
+    live_kt = not args.no_kernel_times and not args.serial_kernel_times
+    extra_pass = args.serial_kernel_times
 
+    # Inputs: each pass k reads fresh anchor and masked gradients drawn by the
+    # seeded device generator.  Those of the timed passes are drawn before the
+    # timed region and stay resident in HBM; warm-up passes draw theirs as they go.
     t_gen = time.perf_counter()
-    M0, W, G_anc, G_mask = [], [], [[] for _ in range(total_iters)], [[] for _ in range(total_iters)]
-    for (cfg, blk, mat), (m, n) in zip(ids, shapes):
-        mi = DeviceMatrixInputs(cfg, blk, mat, m, n, dev, dtype=tdt, drift=args.drift)
-        M0.append(mi.m0())
-        W.append(mi.w0())
-        for k in range(total_iters):
-            G_anc[k].append(mi.g_anc(k))
-            G_mask[k].append(mi.g_mask(k))
-        del mi
+    src = [DeviceMatrixInputs(cfg, blk, mat, m, n, dev, dtype=tdt, drift=args.drift)
+           for (cfg, blk, mat), (m, n) in zip(ids, shapes)]
+    W = [mi.w0() for mi in src]
+
+    def inputs(k):
+        return [mi.g_anc(k) for mi in src], [mi.g_mask(k) for mi in src]
+
+    first_timed = args.warmup
+    timed_in = [inputs(first_timed + j) for j in range(args.steps)]
     torch.cuda.synchronize(dev)
     t_gen = time.perf_counter() - t_gen
-    print(f"# inputs generated in {t_gen:.1f} s", file=sys.stderr, flush=True)
+    print(f"# inputs of the {args.steps} timed passes generated in {t_gen:.1f} s", file=sys.stderr,
+          flush=True)
 
     opt = sco.SpectralAdamW(shapes, w_dtype=tdt, g_dtype=tdt, device=dev,
                             max_sweeps=args.max_sweeps,
@@ -297,30 +379,42 @@ def main():
                             warm_start=0 if args.cold_start else 1, **hp)
     opt.set_solve_waves(args.solve_waves, args.solve_copies)
     opt.set_fused_gram(not args.no_fused_gram)
-    for i, x in enumerate(M0):
-        opt.set_state(i, "m_anc", x)
-    del M0
+    for i, mi in enumerate(src):
+        opt.set_state(i, "m_anc", mi.m0())
+
+    def trace(tag):
+        if args.trace_sweeps:
+            st = opt.stats()
+            by = {}
+            for (m, n), sw, fs in zip(shapes, st["sweeps"], st["factor_sweeps"]):
+                by.setdefault(f"{m}x{n}", set()).add((sw, fs))
+            print(f"# {tag}: sweeps (total, factor phase) by shape "
+                  f"{ {k: sorted(v) for k, v in by.items()} }", file=sys.stderr, flush=True)
 
     for k in range(args.warmup):
-        opt.anchor_update(G_anc[k])
-        opt.step(W, G_mask[k])
+        ga, gm = inputs(k)
+        opt.anchor_update(ga)
+        opt.step(W, gm)
+        del ga, gm
+        trace(f"warmup pass {k}")
         print(f"# warmup {k} done", file=sys.stderr, flush=True)
     torch.cuda.synchronize(dev)
 
-    if args.profile_timed:
+    if live_kt:
         opt.profile(True)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    sweeps = []
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for j in range(args.steps):
-        k = args.warmup + j
+        ga, gm = timed_in[j]
         ev[j][0].record()
-        opt.anchor_update(G_anc[k])
+        opt.anchor_update(ga)
         ev[j][1].record()
-        opt.step(W, G_mask[k])
+        opt.step(W, gm)
         ev[j][2].record()
+        if args.trace_sweeps:
+            trace(f"timed pass {j}")
         print(f"# timed step {j} enqueued", file=sys.stderr, flush=True)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
@@ -328,21 +422,24 @@ def main():
     step_ms = [b.elapsed_time(c) for _, b, c in ev]
     st = opt.stats()
     kt = {}
-    if args.profile_timed:
+    if live_kt:
         kt = opt.kernel_times()
         opt.profile(False)
-    elif extra_pass:
-        # one more pass with per-kernel event timing (Jacobi rounds serialized
-        # on the caller's stream), outside the timed region
-        k = args.warmup + args.steps
-        opt.profile(True)
-        opt.anchor_update(G_anc[k])
-        opt.step(W, G_mask[k])
+    del timed_in
+    if extra_pass:
+        # one more pass with every kernel alone on the caller's stream
+        ga, gm = inputs(args.warmup + args.steps)
+        opt.profile(True, serial=True)
+        opt.anchor_update(ga)
+        opt.step(W, gm)
         kt = opt.kernel_times()
         opt.profile(False)
+        del ga, gm
     async_info = None
     if args.async_refresh > 0:
-        async_info = async_measure(opt, W, G_anc[-1], G_mask, args.async_refresh)
+        ga, _ = inputs(args.warmup + args.steps + 1)
+        gms = [inputs(args.warmup + args.steps + 2 + j)[1] for j in range(2)]
+        async_info = async_measure(opt, W, ga, gms, args.async_refresh)
     sweeps_by_shape, factor_by_shape = {}, {}
     for (m, n), sw, fs in zip(shapes, st["sweeps"], st["factor_sweeps"]):
         key = f"{m}x{n}"
@@ -368,12 +465,17 @@ def main():
                              "gbps": round(d["bytes"] / (d["total_ms"] * 1e6), 1) if d["bytes"] else None}
         name, d = dom
         per_launch_s = d["total_ms"] / d["launches"] / 1e3
+        traffic = None
+        if live_kt:
+            traffic = traffic_for(name, args.workload, args.warmup, args.steps)
         if name in ("jacobi_apply", "jacobi_apply_gram", "ema", "combine_adamw", "jacobi_load",
                     "rownorm", "normalize"):
             ach = d["bytes"] / d["launches"] / per_launch_s / 1e9
             roofline = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1),
                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                        "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic_for(name)}
+                        "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                        "bytes_per_launch": round(d["bytes"] / d["launches"]),
+                        "avg_launch_ms": round(per_launch_s * 1e3, 4)}
         else:
             # the pair solve is vector-ALU work (rotations in LDS); the rest are MFMA
             alu = name == "jacobi_solve"
@@ -381,7 +483,8 @@ def main():
             ach = d["flops"] / d["launches"] / per_launch_s / 1e12
             roofline = {"kernel": name, "bound": "alu" if alu else "mfma", "achieved": round(ach, 2),
                         "peak": peak, "unit": "TFLOP/s",
-                        "frac": round(ach / peak, 4), "traffic": traffic_for(name)}
+                        "frac": round(ach / peak, 4), "traffic": traffic,
+                        "avg_launch_ms": round(per_launch_s * 1e3, 4)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -411,6 +514,9 @@ def main():
         "warm_start": not args.cold_start,
         "drift": args.drift,
         "refresh_ms": round(r_med, 2),
+        "refresh_ms_p10_p90": [round(statistics.quantiles(refresh_ms, n=10)[0], 2),
+                               round(statistics.quantiles(refresh_ms, n=10)[-1], 2)]
+        if len(refresh_ms) >= 2 else None,
         "step_ms": round(s_med, 3),
         "amortized_step_ms_anchor_every_25": round(s_med + r_med / 25.0, 3),
         "step_chain_tflops": round(chain_flops / (s_med * 1e9), 2),
@@ -418,8 +524,10 @@ def main():
         "jacobi_sweeps_by_shape": sweeps_by_shape,
         "jacobi_factor_sweeps_by_shape": factor_by_shape,
         "cholesky_rejected": st["factor_rejected"],
-        "kernel_times_source": ("timed region" if args.profile_timed else
-                                "one extra pass after the timed region, Jacobi rounds serialized"),
+        "kernel_times_source": ("timed region, production schedule (each launch timed on its own "
+                                "stream)" if live_kt else
+                                "one extra pass after the timed region, every kernel alone"
+                                if extra_pass else None),
         "jacobi_not_converged": st["not_converged"],
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -20,11 +20,17 @@
  *   - "device pointer": memory on the handle's device (hipMalloc'ed by the
  *     caller, e.g. a torch tensor's data_ptr()); "host pointer": CPU memory.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls
- *     that take a stream only enqueue work on it; the caller keeps inputs
- *     alive and unmodified until that work is done (usual stream ordering).
- *     sc_anchor_update / sc_refresh additionally synchronize the stream a few
- *     times to stop the Jacobi sweeps once every matrix has converged (see
- *     sc_hparams.sync_check).
+ *     that take a stream enqueue work on it; the caller keeps inputs alive and
+ *     unmodified until that work is done (usual stream ordering).  One
+ *     exception, on by default: with sc_hparams.sync_check = 1,
+ *     sc_anchor_update and sc_refresh (and sc_step when it has to refresh stale
+ *     factors) poll the Jacobi convergence flags from the host so that no
+ *     sweep beyond convergence is queued, and so block the calling thread
+ *     until the refresh is within about one sweep of its end on the device
+ *     (the 112-matrix 1B-shape workload: most of the refresh's device time).
+ *     With sync_check = 0 they only enqueue (a fixed sweep budget whose
+ *     rounds exit at once on converged matrices); sc_anchor_update_async moves
+ *     the polling to a library thread.
  *   - Return value: SC_OK (0) or a negative SC_ERR_* code; sc_last_error()
  *     gives a message for the calling thread.  Arguments are validated before
  *     any GPU work is enqueued; an invalid call changes nothing.
@@ -64,8 +70,13 @@ typedef struct {
     float jacobi_tol;   /* rotation and convergence threshold on |a_p.a_q| / (|a_p||a_q|);
                            0 = default: rotate above 16 * 2^-24, stop after a sweep whose
                            largest ratio is <= 2^-24 * max(16, sqrt(max(rows, cols))) */
-    int sync_check;     /* 1: poll convergence flags on the host (stops early);
-                           0: fully asynchronous, always max_sweeps sweeps */
+    int sync_check;     /* 1: poll convergence flags on the host, queue no sweep past
+                           convergence (blocks the caller, see above);
+                           0: enqueue only: every phase of the refresh queues
+                           max_sweeps sweeps (plain or factor phase, then the
+                           polishing of factor-phase matrices that fail the Gram
+                           certificate); a matrix's rounds exit at once after its
+                           convergence, so choose max_sweeps near the sweeps needed */
     int warm_start;     /* 1: a refresh starts its sweeps from the previous factors
                            (A = M V_prev); 0: always from A = M, V = I */
     int precondition;   /* 1: for matrices with max(rows, cols) >= 2 min(rows, cols) the
@@ -75,7 +86,7 @@ typedef struct {
                            rotations), then polish on A = M V until converged; a
                            matrix whose factorization is rejected runs the plain
                            sweeps.  Used by refreshes that start from previous
-                           factors (warm_start = 1) and with sync_check = 1. */
+                           factors (warm_start = 1). */
 } sc_hparams;
 
 /* Fill `hp` with the defaults of the pages' training strategy:
@@ -95,8 +106,8 @@ void sc_default_hparams(sc_hparams* hp);
 int sc_opt_create(sc_handle* out, int n_mats, const int64_t* rows, const int64_t* cols,
                   sc_dtype w_dtype, sc_dtype g_dtype, const sc_hparams* hp, int device);
 
-/* Free every device allocation of the handle (after synchronizing its device).
- * NULL is accepted. */
+/* Free every device allocation of the handle, after waiting for the handle's
+ * queued work as sc_get_stats does.  NULL is accepted. */
 int sc_opt_destroy(sc_handle h);
 
 /* Anchor arrival ("Key design 2"): for every matrix i,
@@ -219,32 +230,40 @@ typedef struct {
     int64_t step;          /* AdamW step count t */
     int refreshes;         /* SVD refreshes done */
     int sweeps_max;        /* most Jacobi sweeps any matrix needed in the last refresh */
-    int not_converged;     /* matrices that hit max_sweeps in the last refresh */
+    int not_converged;     /* matrices whose last refresh hit max_sweeps or met a
+                              non-finite operand */
     int nonfinite_grad;    /* 1 if a non-finite G_mask value was seen by a step */
     int nonfinite_anchor;  /* 1 if a non-finite G_anc value was seen by an EMA */
     int factor_sweeps_max; /* most sweeps any matrix ran on its Cholesky factor (last refresh) */
     int factor_rejected;   /* matrices whose Cholesky factorization was rejected (last refresh) */
 } sc_stats;
 
-/* Synchronize the handle's work (device-wide) and report counters.
+/* Wait (host) for the handle's own queued work -- its last refresh and last
+ * step, on the streams they were queued on, and its internal streams; not
+ * device-wide -- and report counters.  not_converged counts matrices whose
+ * last refresh hit max_sweeps or met a non-finite operand (NaN or infinity in
+ * the anchor momentum: their factors are not finite).
  * per_mat_sweeps: optional host array of n_mats ints receiving the sweeps of
  * each matrix in the last refresh (factor and polishing sweeps together). */
 int sc_get_stats(sc_handle h, sc_stats* out, int* per_mat_sweeps);
 
-/* Synchronize the handle's work (device-wide) and copy per-matrix sweep counts
+/* Wait for the handle's work as sc_get_stats does and copy per-matrix sweep counts
  * of the last refresh into host arrays of n_mats ints (either may be NULL):
  * total[i] all sweeps, factor[i] the sweeps run on the Cholesky factor (0 when
  * the matrix was not preconditioned or its factorization was rejected). */
 int sc_get_sweep_counts(sc_handle h, int* total, int* factor);
 
 /* Kernel timing for measurement: when enabled, every kernel launch of the
- * handle is bracketed by a pair of HIP events on the launch stream (small
- * host overhead per launch; device timing is unaffected).  Enabling or
- * disabling resets the accumulated totals.  A refresh run with timing on also
- * synchronizes the stream once after its sweeps to read the work counters,
- * waits for each convergence poll before queueing more rounds, and runs all
- * kernels on the caller's stream (without timing the refresh is split over two
- * internal streams so that independent matrices overlap). */
+ * handle is bracketed by a pair of HIP events on the stream it runs on (small
+ * host overhead per launch).  enable = 1: the launches keep their production
+ * schedule (the refresh split over two internal streams whose kernels overlap,
+ * convergence polls that do not block), so a timed run is the production run
+ * and each launch's time includes sharing the GPU with the other stream's
+ * kernels; the work counters of each refresh are copied behind it and folded
+ * in by sc_get_kernel_times.  enable = 2: serialized, every kernel alone on the
+ * caller's stream and each convergence poll waited for (slower pass; kernel
+ * times without overlap).  enable = 0: off.  Any change resets the totals.
+ * SC_ERR_INVALID_ARG for other values. */
 int sc_profile(sc_handle h, int enable);
 
 typedef struct {
@@ -255,7 +274,7 @@ typedef struct {
     double bytes;      /* algorithmic HBM bytes of those launches (streaming kernels) */
 } sc_kernel_time;
 
-/* Synchronize the device, fold finished timings in, and copy up to
+/* Wait for the timed launches' events, fold finished timings in, and copy up to
  * max_entries per-family records to `out` (host array); *count receives the
  * number of families with at least one launch. */
 int sc_get_kernel_times(sc_handle h, sc_kernel_time* out, int max_entries, int* count);

@@ -234,11 +234,17 @@ class Optimizer:
         self.d[i] = tikhonov(s, self.hp["tau_p"])
         self.sweeps[i] = sweeps
 
-    def anchor_update(self, G_anc_list):
-        """O1 then O2/O3 for every matrix."""
+    def anchor_update(self, G_anc_list, defer_refresh: bool = False):
+        """O1 then O2/O3 for every matrix.  defer_refresh: mark the factors stale
+        instead; the next step (or anchor update) recomputes them from the same
+        M, so results are identical and an EMA-only chain of anchor arrivals
+        costs no SVD."""
         for i, G in enumerate(G_anc_list):
             self.M[i] = round_storage(ema(self.M[i], G, self.hp["beta_anc"]), self.state_dtype)
-            self._refresh(i)
+            if defer_refresh:
+                self.factors[i] = None
+            else:
+                self._refresh(i)
 
     def set_tau(self, tau_p: float):
         self.hp["tau_p"] = float(tau_p)

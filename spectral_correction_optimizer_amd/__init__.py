@@ -308,9 +308,11 @@ class SpectralAdamW:
         d["factor_sweeps"] = list(fac)
         return d
 
-    def profile(self, enable: bool = True):
-        """Enable / disable per-kernel event timing (resets the totals)."""
-        _check(self._lib.sc_profile(self._h, 1 if enable else 0))
+    def profile(self, enable: bool = True, serial: bool = False):
+        """Enable / disable per-kernel event timing (resets the totals).  serial:
+        every kernel alone on the current stream (slower pass); otherwise the
+        production schedule, each launch timed on its own stream."""
+        _check(self._lib.sc_profile(self._h, (2 if serial else 1) if enable else 0))
 
     def kernel_times(self):
         """{family: dict(launches, total_ms, flops, bytes)} accumulated since profile(True)."""

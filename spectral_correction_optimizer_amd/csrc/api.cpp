@@ -87,6 +87,14 @@ const char* const kProfNames[PK_COUNT] = {
 // caller's stream; totals are folded in by sc_get_kernel_times.
 struct Prof {
     bool on = false;
+    // serialized: every pipe on the caller's stream and each convergence poll
+    // waited for (kernels timed alone); otherwise the launches keep the
+    // production schedule (two pipes on their streams, non-blocking polls) and
+    // each is timed on the stream it runs on
+    bool serial = false;
+    // per refresh, a pinned copy of the flags taken behind its last kernel; the
+    // work counters of those refreshes are folded in by sc_get_kernel_times
+    std::vector<MatFlags*> snaps, snap_pool;
     struct Rec {
         int kind;
         hipEvent_t a, b;
@@ -130,6 +138,11 @@ struct sc_opt {
     MatFlags* flags_d = nullptr;
     MatFlags* flags_h = nullptr;  // pinned
     int* status_d = nullptr;      // [0] non-finite G_mask, [1] non-finite G_anc
+    int* status_h = nullptr;      // pinned copy of status_d (sc_get_stats)
+    // Recorded on the caller's stream at the end of the last refresh / step, so
+    // that the query calls wait for this handle's work only (not device-wide).
+    hipEvent_t ev_refresh = nullptr, ev_step = nullptr;
+    bool ev_refresh_rec = false, ev_step_rec = false;
     char* arena = nullptr;
     char* proj_arena = nullptr;
     Chunk* chunks_d = nullptr;
@@ -438,10 +451,10 @@ int pipe_finalize(sc_opt* h, Pipe& p, hipStream_t st) {
 // applies one cyclic sweep of 64 * 63 / 2 rotations, each to two rows and two
 // columns of the 64 x 64 Gram and to two rows of R: 18 * 64 flops per rotation
 // (vector ALU work, no HBM traffic).
-void account_sweeps(sc_opt* h) {
+void account_sweeps(sc_opt* h, const MatFlags* flags) {
     for (int i = 0; i < h->n; ++i) {
         const MatDev& m = h->mh[i];
-        const MatFlags& f = h->flags_h[i];
+        const MatFlags& f = flags[i];
         const double pw = kPw;
         // a matrix stops only at the end of one of its sweeps (nb - 1 rounds each)
         const double rounds[2] = {(double)f.sweep_base * (m.nb - 1),
@@ -581,7 +594,7 @@ int pipe_poll(sc_opt* h, Pipe& p, hipStream_t st) {
     HIP_TRY(hipMemcpyAsync(p.flags_h, h->flags_d, sizeof(MatFlags) * h->n, hipMemcpyDeviceToHost,
                            st));
     HIP_TRY(hipEventRecord(p.poll, st));
-    if (h->prof.on) HIP_TRY(hipEventSynchronize(p.poll));
+    if (h->prof.on && h->prof.serial) HIP_TRY(hipEventSynchronize(p.poll));
     p.poll_pending = true;
     return SC_OK;
 }
@@ -615,6 +628,12 @@ int pipe_after_rounds(sc_opt* h, Pipe& p, hipStream_t st) {
         if ((rc = pipe_final_gram(h, p, st))) return rc;
         HIP_TRY(timed(h, PK_INIT_FLAGS, st,
                       [&] { return launch_certify(h->md, h->flags_d, p.cap, p.ncap, st); }));
+        if (!h->hp.sync_check) {
+            // enqueue only: polishing rounds for every factor-phase matrix; the
+            // certified ones are done and their launches exit at once
+            pipe_start_rounds(h, p, LIST_POLISH, 1);
+            return SC_OK;
+        }
         p.stage = STAGE_CERT;
         return pipe_poll(h, p, st);
     }
@@ -629,7 +648,7 @@ int do_refresh(sc_opt* h, hipStream_t st) {
     const bool warm = h->hp.warm_start && h->have_factors;
     // With kernel timing on, every pipe runs on the caller's stream so that each
     // kernel's events bracket it alone (no overlap between pipes).
-    const bool split = !h->prof.on;
+    const bool split = !(h->prof.on && h->prof.serial);
     auto pst = [&](Pipe& p) { return split ? p.st : st; };
     if (split) {
         HIP_TRY(hipEventRecord(h->fork, st));
@@ -640,7 +659,7 @@ int do_refresh(sc_opt* h, hipStream_t st) {
         // The factor phase needs a well-conditioned Gram: from the previous factors the
         // columns of A = M V_prev are close to orthogonal.  From a cold start (A = M) a
         // graded spectrum would make most factorizations fail, so it is skipped.
-        p.pre = p.ncap > 0 && h->hp.sync_check && warm;
+        p.pre = p.ncap > 0 && warm;
         if ((rc = pipe_pre(h, p, pst(p), warm))) return rc;
         pipe_start_rounds(h, p, p.pre ? LIST_FACTOR : LIST_PLAIN, 4);
     }
@@ -717,11 +736,21 @@ int do_refresh(sc_opt* h, hipStream_t st) {
             HIP_TRY(hipStreamWaitEvent(st, h->pipes[q].join, 0));
         }
     if (h->prof.on) {
-        HIP_TRY(hipMemcpyAsync(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n,
-                               hipMemcpyDeviceToHost, st));
-        HIP_TRY(hipStreamSynchronize(st));
-        account_sweeps(h);
+        // the work counters of this refresh, copied behind it without a host wait
+        MatFlags* snap = nullptr;
+        if (!h->prof.snap_pool.empty()) {
+            snap = h->prof.snap_pool.back();
+            h->prof.snap_pool.pop_back();
+        } else {
+            void* q = nullptr;
+            HIP_TRY(hipHostMalloc(&q, sizeof(MatFlags) * h->n, hipHostMallocDefault));
+            snap = (MatFlags*)q;
+        }
+        h->prof.snaps.push_back(snap);
+        HIP_TRY(hipMemcpyAsync(snap, h->flags_d, sizeof(MatFlags) * h->n, hipMemcpyDeviceToHost, st));
     }
+    HIP_TRY(hipEventRecord(h->ev_refresh, st));
+    h->ev_refresh_rec = true;
     h->proj_stale = false;
     h->have_factors = true;
     h->refreshes += 1;
@@ -992,6 +1021,10 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
     h->dev_allocs.push_back(p);
     h->status_d = (int*)p;
     HIP_TRY(hipMemset(h->status_d, 0, 4 * sizeof(int)));
+    HIP_TRY(hipHostMalloc(&p, 4 * sizeof(int), hipHostMallocDefault));
+    h->status_h = (int*)p;
+    HIP_TRY(hipEventCreateWithFlags(&h->ev_refresh, hipEventDisableTiming));
+    HIP_TRY(hipEventCreateWithFlags(&h->ev_step, hipEventDisableTiming));
 
     // work lists
     std::vector<Chunk> ch;
@@ -1231,11 +1264,37 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
     return SC_OK;
 }
 
+// Block the host until the handle's last refresh and last step (and, through
+// its internal streams, any refresh work still in flight) have run.
+int wait_handle(sc_opt* h) {
+    if (h->ev_refresh_rec) HIP_TRY(hipEventSynchronize(h->ev_refresh));
+    if (h->ev_step_rec) HIP_TRY(hipEventSynchronize(h->ev_step));
+    for (int q = 0; q < h->npipes; ++q)
+        if (h->pipes[q].st) HIP_TRY(hipStreamSynchronize(h->pipes[q].st));
+    if (h->astream) HIP_TRY(hipStreamSynchronize(h->astream));
+    return SC_OK;
+}
+
+// Copy the device flags and status words to their pinned host copies (after
+// wait_handle) on an internal stream.
+int read_flags(sc_opt* h) {
+    hipStream_t q = h->pipes[0].st;
+    HIP_TRY(hipMemcpyAsync(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n, hipMemcpyDeviceToHost, q));
+    HIP_TRY(hipMemcpyAsync(h->status_h, h->status_d, 4 * sizeof(int), hipMemcpyDeviceToHost, q));
+    HIP_TRY(hipStreamSynchronize(q));
+    return SC_OK;
+}
+
 void release(sc_opt* h) {
     if (!h) return;
     DeviceGuard g(h->device);
     if (h->worker.joinable()) h->worker.join();
-    (void)hipDeviceSynchronize();
+    // the handle's own work only: its last refresh and step, its internal streams
+    (void)wait_handle(h);
+    (void)hipGetLastError();
+    for (hipEvent_t e : {h->ev_refresh, h->ev_step})
+        if (e) (void)hipEventDestroy(e);
+    if (h->status_h) (void)hipHostFree(h->status_h);
     if (h->astream) (void)hipStreamDestroy(h->astream);
     for (hipEvent_t e : {h->a_ready, h->a_pub, h->a_done})
         if (e) (void)hipEventDestroy(e);
@@ -1245,6 +1304,8 @@ void release(sc_opt* h) {
         (void)hipEventDestroy(r.b);
     }
     for (hipEvent_t e : h->prof.pool) (void)hipEventDestroy(e);
+    for (MatFlags* f : h->prof.snaps) (void)hipHostFree(f);
+    for (MatFlags* f : h->prof.snap_pool) (void)hipHostFree(f);
     for (auto& P : h->pipes) {
         if (P.st) (void)hipStreamDestroy(P.st);
         if (P.join) (void)hipEventDestroy(P.join);
@@ -1469,6 +1530,8 @@ int sc_step(sc_handle h, void* const* W, const void* const* G_mask, void* stream
     }));
     if (h->prof.on)
         h->prof.bytes[PK_ADAMW] += h->adamw_bytes + (h->keep_proj ? 4.0 * h->total_numel : 0.0);
+    HIP_TRY(hipEventRecord(h->ev_step, st));
+    h->ev_step_rec = true;
     h->t = t;
     return SC_OK;
 }
@@ -1634,6 +1697,7 @@ int sc_keep_proj(sc_handle h, int enable) {
             return fail(SC_ERR_OOM, "device allocation of %zu bytes failed", total);
         }
         h->proj_arena = (char*)p;
+        if ((rc = wait_handle(h))) return rc;
         HIP_TRY(hipMemset(p, 0, total));
         for (int i = 0; i < h->n; ++i) h->mh[i].Gproj = (float*)(h->proj_arena + offs[i]);
         HIP_TRY(hipMemcpy(h->md, h->mh.data(), sizeof(MatDev) * h->n, hipMemcpyHostToDevice));
@@ -1665,10 +1729,8 @@ int sc_get_stats(sc_handle h, sc_stats* out, int* per_mat_sweeps) {
     if (!out) return fail(SC_ERR_INVALID_ARG, "out is NULL");
     DeviceGuard g(h->device);
     if ((rc = finish_async(h, nullptr, true))) return rc;
-    HIP_TRY(hipDeviceSynchronize());
-    HIP_TRY(hipMemcpy(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n, hipMemcpyDeviceToHost));
-    int status[4];
-    HIP_TRY(hipMemcpy(status, h->status_d, sizeof(status), hipMemcpyDeviceToHost));
+    if ((rc = wait_handle(h)) || (rc = read_flags(h))) return rc;
+    const int* status = h->status_h;
     memset(out, 0, sizeof(*out));
     out->n_mats = h->n;
     out->step = h->t;
@@ -1691,8 +1753,7 @@ int sc_get_sweep_counts(sc_handle h, int* total, int* factor) {
     if ((rc = check_handle(h))) return rc;
     DeviceGuard g(h->device);
     if ((rc = finish_async(h, nullptr, true))) return rc;
-    HIP_TRY(hipDeviceSynchronize());
-    HIP_TRY(hipMemcpy(h->flags_h, h->flags_d, sizeof(MatFlags) * h->n, hipMemcpyDeviceToHost));
+    if ((rc = wait_handle(h)) || (rc = read_flags(h))) return rc;
     for (int i = 0; i < h->n; ++i) {
         if (total) total[i] = h->flags_h[i].sweeps;
         if (factor) factor[i] = h->flags_h[i].sweep_base;
@@ -1704,20 +1765,25 @@ int sc_profile(sc_handle h, int enable) {
     int rc;
     if ((rc = check_handle(h))) return rc;
     DeviceGuard g(h->device);
+    if (enable < 0 || enable > 2) return fail(SC_ERR_INVALID_ARG, "enable must be 0, 1 or 2");
     if ((rc = finish_async(h, nullptr, true))) return rc;
-    if (!h->prof.recs.empty()) {
-        HIP_TRY(hipDeviceSynchronize());
+    if (!h->prof.recs.empty() || !h->prof.snaps.empty()) {
+        if ((rc = wait_handle(h))) return rc;
+        for (auto& r : h->prof.recs) HIP_TRY(hipEventSynchronize(r.b));
         for (auto& r : h->prof.recs) {
             h->prof.pool.push_back(r.a);
             h->prof.pool.push_back(r.b);
         }
         h->prof.recs.clear();
+        for (MatFlags* f : h->prof.snaps) h->prof.snap_pool.push_back(f);
+        h->prof.snaps.clear();
     }
     for (int k = 0; k < PK_COUNT; ++k) {
         h->prof.launches[k] = 0;
         h->prof.ms[k] = h->prof.flops[k] = h->prof.bytes[k] = 0.0;
     }
     h->prof.on = enable != 0;
+    h->prof.serial = enable == 2;
     return SC_OK;
 }
 
@@ -1728,7 +1794,13 @@ int sc_get_kernel_times(sc_handle h, sc_kernel_time* out, int max_entries, int* 
         return fail(SC_ERR_INVALID_ARG, "out/count is NULL");
     DeviceGuard g(h->device);
     if ((rc = finish_async(h, nullptr, true))) return rc;
-    HIP_TRY(hipDeviceSynchronize());
+    if ((rc = wait_handle(h))) return rc;
+    for (MatFlags* f : h->prof.snaps) {
+        account_sweeps(h, f);
+        h->prof.snap_pool.push_back(f);
+    }
+    h->prof.snaps.clear();
+    for (auto& r : h->prof.recs) HIP_TRY(hipEventSynchronize(r.b));
     for (auto& r : h->prof.recs) {
         float ms = 0.0f;
         if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) h->prof.ms[r.kind] += ms;

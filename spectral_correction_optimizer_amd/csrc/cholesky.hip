@@ -441,7 +441,7 @@ __global__ __launch_bounds__(256) void gram_to_e_kernel(const MatDev* __restrict
         float e = 0.0f;
         if (gr < k && gc < k && gc < gr) {
             e = (float)(gld(C + (int64_t)gr * k + gc) * rdi[r] * cdi[c]);
-            mo = fmaxf(mo, fabsf(e));
+            mo = max_nan_inf(mo, fabsf(e));
         }
         T[r][c] = e;
         if (gr < k && gc < k && (a != b || gc <= gr)) gst(md.E + (int64_t)gr * k + gc, e);

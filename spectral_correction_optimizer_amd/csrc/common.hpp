@@ -40,6 +40,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Running maximum of non-negative convergence measures in which a NaN counts as
+// +infinity (fmaxf would drop it): a non-finite operand then reads as far from
+// converged instead of as converged.
+__device__ __forceinline__ float max_nan_inf(float m, float x) {
+    return x <= m ? m : (x == x ? x : __builtin_huge_valf());
+}
+
 // Device-memory accessors that compile to global_load / global_store.  A
 // pointer read from a struct in memory is generic, and generic (flat) accesses
 // are counted by the LDS wait counter as well: an s_waitcnt for an LDS read

@@ -343,7 +343,7 @@ __global__ __launch_bounds__(64) void jac_solve_kernel(const MatDev* __restrict_
     for (int e = 0; e < 40; ++e) {
         const int a = tile_row(e), b = tile_col(e);
         if (a <= b) G[a * SG + b] = (float)(acc[e] * scale);
-        if (a < b) mo = fmaxf(mo, (float)(fabs(acc[e]) * rs[a] * rs[b]));
+        if (a < b) mo = max_nan_inf(mo, (float)(fabs(acc[e]) * rs[a] * rs[b]));
     }
     for (int o = 32; o > 0; o >>= 1) mo = fmaxf(mo, __shfl_xor(mo, o));
     if (l == 0) atomicMax(&fl.sweep_max, __float_as_uint(mo));
@@ -572,7 +572,7 @@ __global__ __launch_bounds__(64 * NW) void jac_solve_waves_kernel(const MatDev* 
     for (int e = 0; e < NE; ++e) {
         const int a = tile_row(e0 + e), b = tile_col(e0 + e);
         if (a <= b) G[0][a * SG + b] = (float)(acc[e] * scale);
-        if (a < b) mo = fmaxf(mo, (float)(fabs(acc[e]) * rs[a] * rs[b]));
+        if (a < b) mo = max_nan_inf(mo, (float)(fabs(acc[e]) * rs[a] * rs[b]));
     }
     for (int o = 32; o > 0; o >>= 1) mo = fmaxf(mo, __shfl_xor(mo, o));
     if (l == 0) mos[w] = mo;
@@ -1115,7 +1115,9 @@ __global__ void jac_sweep_end_kernel(const MatDev* __restrict__ mats, MatFlags* 
     f.sweeps += 1;
     const float mo = __uint_as_float(f.sweep_max);
     f.sweep_max = 0u;
-    if (!(mo > mats[i].tol_conv)) {
+    if (!(mo <= 3.402823466e38f)) {
+        f.done = 1;  // a non-finite operand: stop, reported as not converged
+    } else if (!(mo > mats[i].tol_conv)) {
         f.converged = 1;
         f.done = 1;
     } else if (f.sweeps - f.sweep_base >= max_sweeps) {

@@ -332,7 +332,7 @@ def pin_optimizer_driver_worked_4x3(o):
     M0 = (M - (1.0 - b * b) * Ga) / (b * b)
     opt = o.Optimizer([(4, 3)], hp, w_dtype="f64", state_dtype="f64", threads=1)
     opt.set_anchor_momentum(0, M0)
-    opt.anchor_update([Ga])
+    opt.anchor_update([Ga], defer_refresh=True)
     assert not np.allclose(opt.M[0], M, atol=1e-3)  # one arrival is not there yet
     opt.anchor_update([Ga])
     assert np.allclose(opt.M[0], M, rtol=0, atol=1e-14), opt.M[0]
@@ -355,6 +355,31 @@ def pin_optimizer_driver_worked_4x3(o):
         if t == 2:
             opt.anchor_update([M])  # b M + (1 - b) M = M: same factors, t unchanged
             assert opt.t == 2 and np.allclose(opt.M[0], M, rtol=0, atol=1e-14)
+
+
+def pin_optimizer_deferred_refresh(o):
+    """An anchor arrival whose SVD refresh is deferred to the next step gives the
+    same weights, bit for bit, as one refreshed at once (the factors are a
+    function of M alone), and the deferred chain really uses the new M."""
+    rng_ = np.random.default_rng(77)
+    shape = (6, 4)
+    hp = dict(tau_p=1e-3, alpha=0.3, beta_anc=0.9, lr=2e-5, beta1=0.9, beta2=0.999, eps=1e-8,
+              weight_decay=0.01)
+    ga = [1e-2 * rng_.standard_normal(shape) for _ in range(3)]
+    gm = [1e-3 * rng_.standard_normal(shape) for _ in range(3)]
+    W0 = 0.02 * rng_.standard_normal(shape)
+    outs = []
+    for defer in (False, True, None):
+        opt = o.Optimizer([shape], hp, threads=1)
+        opt.set_anchor_momentum(0, 1e-2 * np.ones(shape))
+        W = W0.copy()
+        for k in range(3):
+            if defer is not None or k == 0:
+                opt.anchor_update([ga[k]], defer_refresh=bool(defer))
+            W = opt.step([W], [gm[k]])[0]
+        outs.append(W)
+    assert np.array_equal(outs[0], outs[1])
+    assert not np.array_equal(outs[0], outs[2])  # later anchors do change the result
 
 
 def _rne_f32(x):

@@ -110,98 +110,188 @@ def test_full_workload_handle_runs_and_is_consistent():
 # Sampled parity at full size on noisy inputs, in the benchmark's launch
 # configuration: all 112 matrices of the 16-block workload in one handle, the
 # sampled ones drawn by the host generator (the oracle gets the identical
-# stored values), the others generated on the device.  One refresh and one
-# step; the oracle runs each sampled matrix on its own.  The float32 samples
-# cover the code paths: square operands (plain sweeps), m < n and m > n
-# (Cholesky factor phase, certificate, polishing for the 512x2048 ones).  The
-# bfloat16 configuration (W, G_mask and G_anc in bfloat16, float32 states) is
-# sampled at the two outer filter strengths.
+# stored values), the others generated on the device.  The schedules are the
+# ones the benchmark times: anchor arrivals back to back, so that every refresh
+# after the first starts from the previous factors (warm start, the Cholesky
+# factor phase of the k = 2048 and k = 512 operands, the Gram certificate and,
+# where it fails, polishing sweeps on the 8192-long rows), then several steps.
+#   f32_warm:    2 arrivals, 5 steps; q, k, gate, down (the three shape classes)
+#   bf16_warm:   bfloat16 W / G_mask / G_anc, 2 arrivals, 3 steps at tau 1e-3,
+#                1e-4, 1e-2 (sc_set_tau: same factors, new filter); o and gate
+#   f32_steady:  20 arrivals (the anchor EMA near its steady state), 2 steps;
+#                q and down
+# The oracle follows the same arrivals with its EMA only (the refresh deferred
+# to the next step, which gives identical factors) and then runs the steps.
 NB = len(gen.BLOCK_SHAPES)
-CASES = [("f32", 1e-3, (3, 0)), ("f32", 1e-3, (7, 1)), ("f32", 1e-3, (11, 4)), ("f32", 1e-3, (15, 6)),
-         ("bf16", 1e-4, (5, 3)), ("bf16", 1e-4, (9, 2)), ("bf16", 1e-2, (5, 3)), ("bf16", 1e-2, (9, 2))]
-CASE_IDS = ["f32_q_blk3", "f32_k_blk7", "f32_gate_blk11", "f32_down_blk15",
-            "bf16_tau1e-4_o_blk5", "bf16_tau1e-4_v_blk9", "bf16_tau1e-2_o_blk5", "bf16_tau1e-2_v_blk9"]
+RUNS = {
+    "f32_warm": dict(dtype="f32", anchors=2, taus=[1e-3] * 5, samples=[(3, 0), (7, 1), (11, 4), (15, 6)]),
+    "bf16_warm": dict(dtype="bf16", anchors=2, taus=[1e-3, 1e-4, 1e-2], samples=[(5, 3), (9, 4)]),
+    "f32_steady": dict(dtype="f32", anchors=20, taus=[1e-3] * 2, samples=[(2, 0), (13, 6)]),
+}
+CASES = [(run, smp) for run, cfg in RUNS.items() for smp in cfg["samples"]]
+CASE_IDS = [f"{run}_{gen.BLOCK_SHAPES[m][0]}_blk{b}" for run, (b, m) in CASES]
 _runs = {}
 
 
-def _sampled_run(dtype, tau):
-    """GPU outputs of the sampled matrices for one (dtype, tau) configuration."""
-    key = (dtype, tau)
-    if key in _runs:
-        return _runs[key]
+def _sampled_run(name):
+    """GPU run of one schedule; returns, per sampled matrix, its GPU outputs of
+    every step and an oracle driver that has seen the same arrivals."""
+    if name in _runs:
+        return _runs[name]
     _runs.clear()
     import spectral_correction_optimizer_amd as sco
     from gen.device import DeviceMatrixInputs
+    cfg = RUNS[name]
+    dtype = cfg["dtype"]
     dev = torch.device("cuda")
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
     wl = gen.workload("blocks16_1b")
-    hp = dict(gen.DEFAULT_HP, tau_p=tau)
-    picked = sorted({b * NB + m for d, t, (b, m) in CASES if (d, t) == key})
-    say(f"case: 112-matrix workload, {dtype}, tau {tau}, host-generated samples {picked}")
+    hp = dict(gen.DEFAULT_HP, tau_p=cfg["taus"][0])
+    picked = sorted({b * NB + m for b, m in cfg["samples"]})
+    say(f"case: 112-matrix workload, {name}: {cfg['anchors']} arrivals then {len(cfg['taus'])} steps, "
+        f"host-generated samples {picked}")
     opt = sco.SpectralAdamW(wl["shapes"], w_dtype=tdt, g_dtype=tdt, device=dev, **hp)
     opt.keep_proj(True)
-    W, G, GA, host = [], [], [], {}
+    src, W, ora = {}, [], {}
     for idx, ((c, b, m_), (m, n)) in enumerate(zip(wl["ids"], wl["shapes"])):
         if idx in picked:
             mi = gen.MatrixInputs(c, b, m_, m, n)
             m0 = gen.stored(mi.m0(), "f32")
-            ga, gm, w0 = (gen.stored(x, dtype) for x in (mi.g_anc(0), mi.g_mask(0), mi.w0()))
-            host[idx] = (m0[1], ga[1], gm[1], w0[1])
+            w0 = gen.stored(mi.w0(), dtype)
             opt.set_state(idx, "m_anc", to_dev(m0[0], "f32", dev))
-            GA.append(to_dev(ga[0], dtype, dev))
-            G.append(to_dev(gm[0], dtype, dev))
             W.append(to_dev(w0[0], dtype, dev))
+            o = oracle.Optimizer([(m, n)], hp, w_dtype=dtype, state_dtype="f32")
+            o.set_anchor_momentum(0, m0[1])
+            ora[idx] = dict(opt=o, W=[w0[1]], G=[])
         else:
             mi = DeviceMatrixInputs(c, b, m_, m, n, dev, dtype=tdt)
             opt.set_state(idx, "m_anc", mi.m0())
-            GA.append(mi.g_anc(0))
-            G.append(mi.g_mask(0))
             W.append(mi.w0())
-        del mi
-    opt.anchor_update(GA)
-    opt.step(W, G)
+        src[idx] = mi
+    for k in range(cfg["anchors"]):
+        GA = []
+        for idx, mi in src.items():
+            if idx in ora:
+                pay, val = gen.stored(mi.g_anc(k), dtype)
+                GA.append(to_dev(pay, dtype, dev))
+                ora[idx]["opt"].anchor_update([val], defer_refresh=True)
+            else:
+                GA.append(mi.g_anc(k))
+        opt.anchor_update(GA)
+        del GA
+        if k % 5 == 4 or k == cfg["anchors"] - 1:
+            say(f"  arrival {k + 1} queued")
+    st_refresh = opt.stats()
+    say(f"  last refresh: sweeps by matrix {sorted(set(st_refresh['sweeps']))}, factor-phase sweeps "
+        f"{sorted(set(st_refresh['factor_sweeps']))}, not converged {st_refresh['not_converged']}")
+    out = {idx: [] for idx in ora}
+    for j, tau in enumerate(cfg["taus"]):
+        if tau != opt.hp["tau_p"]:
+            opt.set_tau(tau)
+            opt.hp["tau_p"] = tau
+        G = []
+        for idx, mi in src.items():
+            if idx in ora:
+                pay, val = gen.stored(mi.g_mask(j), dtype)
+                G.append(to_dev(pay, dtype, dev))
+                ora[idx]["G"].append((tau, val))
+            else:
+                G.append(mi.g_mask(j))
+        opt.step(W, G)
+        del G
+        for idx in ora:
+            gf, gp = opt.get_filtered(idx, proj=True)
+            out[idx].append((from_dev(gf), from_dev(gp), from_dev(W[idx])))
     st = opt.stats()
-    say(f"  GPU pass done: sweeps max {st['sweeps_max']} not_converged {st['not_converged']}")
-    out = {}
-    for idx in picked:
-        gf, gp = opt.get_filtered(idx, proj=True)
-        out[idx] = (from_dev(gf), from_dev(gp), from_dev(W[idx]))
+    say(f"  GPU steps done: not_converged {st['not_converged']}")
     opt.close()
-    del W, G, GA
+    del W, src
     torch.cuda.empty_cache()
-    _runs[key] = (wl, hp, host, out, st)
-    return _runs[key]
+    _runs[name] = (wl, hp, ora, out, st_refresh)
+    return _runs[name]
 
 
-@pytest.mark.parametrize("dtype,tau,sample", CASES, ids=CASE_IDS)
-def test_sampled_noisy_parity_16_blocks(dtype, tau, sample):
+@pytest.mark.parametrize("run,sample", CASES, ids=CASE_IDS)
+def test_sampled_noisy_parity_16_blocks(run, sample):
     from tests.gpu_harness import REL_TOL, SMALL_G, W_TOL, bf16_ulp
-    wl, hp, host, out, st = _sampled_run(dtype, tau)
+    wl, hp, ora, out, st = _sampled_run(run)
+    dtype = RUNS[run]["dtype"]
     idx = sample[0] * NB + sample[1]
     m, n = wl["shapes"][idx]
     assert st["not_converged"] == 0
-    M0, GA, GM, W0 = host[idx]
-    ora = oracle.Optimizer([(m, n)], hp, w_dtype=dtype, state_dtype="f32")
-    ora.set_anchor_momentum(0, M0)
-    ora.anchor_update([GA])
-    W1 = ora.step([W0], [GM])[0]
-    gf, gp, w = out[idx]
-    ef, ep = relf(gf, ora.last_filt[0]), relf(gp, ora.last_proj[0])
-    err = np.abs(w - W1)
-    if dtype == "f32":
-        keep = np.abs(ora.last_proj[0]) >= SMALL_G
-        ew, ok_w = float(err[keep].max()), float(err[keep].max()) <= W_TOL
-        wnote = f"W {ew:.3e} (excluded {int((~keep).sum())}, max {float(err[~keep].max()) if (~keep).any() else 0.0:.3e})"
-    else:
-        keep = np.abs(ora.last_proj[0]) >= SMALL_G
-        ulps = err / bf16_ulp(W1)
-        ok_w = float(ulps[keep].max()) <= 1.0
-        bad = ulps > 1.0
-        wnote = (f"W max {float(ulps[keep].max()):.2f} bf16 ulp ({int((ulps > 0).sum())} elements "
-                 f"differ; excluded {int((~keep).sum())}, max {float(ulps[~keep].max()) if (~keep).any() else 0.0:.1f} ulp; "
-                 f"{int(bad.sum())} above 1 ulp, their |G_proj| <= {float(np.abs(ora.last_proj[0])[bad].max()) if bad.any() else 0.0:.2e})")
-    say(f"  mat {idx} {m}x{n}: relF G_filt {ef:.3e} G_proj {ep:.3e} {wnote} oracle sweeps {ora.sweeps[0]}")
-    assert ef <= REL_TOL and ep <= REL_TOL and ok_w
+    if RUNS[run]["anchors"] > 1 and max(m, n) >= 2 * min(m, n):
+        assert st["factor_sweeps"][idx] > 0, "the warm refresh ran no factor phase"
+    o, W, keep = ora[idx]["opt"], ora[idx]["W"][0], None
+    for j, (tau, G) in enumerate(ora[idx]["G"]):
+        if tau != o.hp["tau_p"]:
+            o.set_tau(tau)
+        W = o.step([W], [G])[0]
+        if keep is None:
+            keep = np.abs(o.last_proj[0]) >= SMALL_G
+        gf, gp, w = out[idx][j]
+        ef, ep = relf(gf, o.last_filt[0]), relf(gp, o.last_proj[0])
+        err = np.abs(w - W)
+        if dtype == "f32":
+            ew = float(err[keep].max())
+            ok_w = ew <= W_TOL
+            wnote = f"W {ew:.3e} (excluded {int((~keep).sum())}, max {float(err[~keep].max()) if (~keep).any() else 0.0:.3e})"
+        else:
+            ulps = err / bf16_ulp(W)
+            ok_w = float(ulps[keep].max()) <= 1.0
+            wnote = (f"W max {float(ulps[keep].max()):.2f} bf16 ulp ({int((ulps > 0).sum())} differ, "
+                     f"excluded {int((~keep).sum())})")
+        say(f"  mat {idx} {m}x{n} step {j + 1} tau {tau:g}: relF G_filt {ef:.3e} G_proj {ep:.3e} {wnote}"
+            + (f" oracle sweeps {o.sweeps[0]} GPU sweeps {st['sweeps'][idx]} (factor {st['factor_sweeps'][idx]})"
+               if j == 0 else ""))
+        assert ef <= REL_TOL and ep <= REL_TOL and ok_w
+
+
+def test_one_block_refresh_and_20_steps():
+    """One Llama-3.2-1B block (7 matrices, its own handle): one cold refresh and
+    20 steps with fresh masked-gradient noise, as the one-block workload is
+    timed; q, k and down (the square, wide-short and wide-long operands) against
+    the oracle at steps 1, 10 and 20."""
+    from tests.gpu_harness import REL_TOL, SMALL_G, W_TOL
+    import spectral_correction_optimizer_amd as sco
+    dev = torch.device("cuda")
+    wl = gen.workload("block_1b")
+    hp = dict(gen.DEFAULT_HP)
+    picked = [0, 1, 6]
+    say(f"case: one block {wl['shapes']}, 1 refresh + 20 steps, samples {picked}")
+    ins = [gen.MatrixInputs(c, b, m_, m, n) for (c, b, m_), (m, n) in zip(wl["ids"], wl["shapes"])]
+    opt = sco.SpectralAdamW(wl["shapes"], device=dev, **hp)
+    opt.keep_proj(True)
+    ora = oracle.Optimizer([wl["shapes"][i] for i in picked], hp)
+    W, Wo = [], []
+    for i, mi in enumerate(ins):
+        pay, val = gen.stored(mi.m0(), "f32")
+        opt.set_state(i, "m_anc", to_dev(pay, "f32", dev))
+        pw, vw = gen.stored(mi.w0(), "f32")
+        W.append(to_dev(pw, "f32", dev))
+        if i in picked:
+            ora.set_anchor_momentum(picked.index(i), val)
+            Wo.append(vw)
+    ga = [gen.stored(mi.g_anc(0), "f32") for mi in ins]
+    opt.anchor_update([to_dev(p, "f32", dev) for p, _ in ga])
+    ora.anchor_update([ga[i][1] for i in picked])
+    say(f"  refresh done (oracle sweeps {ora.sweeps}, GPU {opt.stats()['sweeps']})")
+    keep = None
+    for step in range(20):
+        gm = [gen.stored(mi.g_mask(step), "f32") for mi in ins]
+        opt.step(W, [to_dev(p, "f32", dev) for p, _ in gm])
+        Wo = ora.step(Wo, [gm[i][1] for i in picked])
+        if keep is None:
+            keep = [np.abs(p) >= SMALL_G for p in ora.last_proj]
+        if step + 1 not in (1, 10, 20):
+            continue
+        for j, i in enumerate(picked):
+            gf, gp = opt.get_filtered(i, proj=True)
+            ef, ep = relf(from_dev(gf), ora.last_filt[j]), relf(from_dev(gp), ora.last_proj[j])
+            ew = float(np.abs(from_dev(W[i]) - Wo[j])[keep[j]].max())
+            say(f"  step {step + 1} mat {i} {wl['shapes'][i]}: relF G_filt {ef:.3e} G_proj {ep:.3e} W {ew:.3e}")
+            assert ef <= REL_TOL and ep <= REL_TOL and ew <= W_TOL
+    assert opt.stats()["not_converged"] == 0
+    opt.close()
 
 
 def test_known_factors_8b_block_shapes():

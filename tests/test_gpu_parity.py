@@ -476,3 +476,149 @@ def test_fused_gram_matches_unfused():
         w_err = np.abs(wa[i] - wb[i])[keep].max()
         say(f"  {m}x{n}: s {s_err:.2e} recon {rec:.2e} G_filt {g_rel:.2e} W {w_err:.2e}")
         assert s_err < 1e-5 and rec < 1e-5 and g_rel < 1e-4 and w_err < 1e-7
+
+
+def test_sync_check_0_enqueue_only_matches_oracle():
+    """The enqueue-only refresh (sync_check = 0: no host polls, a fixed sweep
+    budget whose rounds exit at once on converged matrices, the factor phase and
+    the polishing of matrices failing the Gram certificate decided on the device)
+    against the oracle over two warm refreshes of the three shape classes."""
+    shapes = [(520, 96), (96, 520), (1024, 256), (256, 256), (200, 136)]
+    say(f"case: sync_check=0 {shapes}, refresh every 2 steps, 4 steps")
+    sc = Scenario(shapes, [(132, 0, i) for i in range(len(shapes))], steps=4, anchor_every=2,
+                  max_sweeps=16)
+    rep = sc.run(gpu_hp=dict(sync_check=0))
+    Scenario.check(rep)
+    st = rep["stats"]
+    say(f"  stats {st}")
+    assert st["not_converged"] == 0 and st["factor_rejected"] == 0
+    assert st["factor_sweeps_max"] > 0  # the factor phase ran without host decisions
+
+
+def test_sweep_cap_reports_not_converged():
+    """max_sweeps = 1 stops every matrix after one sweep of a cold refresh: the
+    stats report each matrix as not converged with one sweep, and a step still
+    runs on the partial factors."""
+    import spectral_correction_optimizer_amd as sco
+    dev = torch.device("cuda")
+    shapes = [(256, 192), (128, 320)]
+    say(f"case: max_sweeps=1 on {shapes}")
+    ins = [gen.MatrixInputs(133, 0, i, *sh) for i, sh in enumerate(shapes)]
+    opt = sco.SpectralAdamW(shapes, device=dev, max_sweeps=1)
+    for i, mi in enumerate(ins):
+        opt.set_state(i, "m_anc", to_dev(gen.stored(mi.m0(), "f32")[0], "f32", dev))
+    opt.refresh()
+    st = opt.stats()
+    say(f"  stats {st}")
+    assert st["not_converged"] == len(shapes) and st["sweeps"] == [1] * len(shapes)
+    W = [torch.zeros(*sh, device=dev) for sh in shapes]
+    opt.step(W, [to_dev(gen.stored(mi.g_mask(0), "f32")[0], "f32", dev) for mi in ins])
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(w).all().item() for w in W)
+    opt.close()
+
+
+def test_nonfinite_anchor_flag_and_other_matrices_unaffected():
+    """A NaN in one matrix's anchor gradient: the anchor flag is raised, that
+    matrix stops after its first sweep and is reported as not converged (a NaN
+    no longer reads as a converged sweep), and the other matrix of the handle
+    still matches the oracle."""
+    import spectral_correction_optimizer_amd as sco
+    dev = torch.device("cuda")
+    shapes = [(192, 128), (160, 96)]
+    say(f"case: NaN in the anchor gradient of matrix 1 of {shapes}")
+    ins = [gen.MatrixInputs(134, 0, i, *sh) for i, sh in enumerate(shapes)]
+    opt = sco.SpectralAdamW(shapes, device=dev)
+    ora = oracle.Optimizer(shapes[:1], opt_hp(opt))
+    for i, mi in enumerate(ins):
+        pay, val = gen.stored(mi.m0(), "f32")
+        opt.set_state(i, "m_anc", to_dev(pay, "f32", dev))
+        if i == 0:
+            ora.set_anchor_momentum(0, val)
+    ga = [gen.stored(mi.g_anc(0), "f32") for mi in ins]
+    bad = ga[1][0].copy()
+    bad[7, 3] = np.nan
+    assert opt.stats()["nonfinite_anchor"] == 0
+    opt.anchor_update([to_dev(ga[0][0], "f32", dev), to_dev(bad, "f32", dev)])
+    ora.anchor_update([ga[0][1]])
+    st = opt.stats()
+    say(f"  stats {st}")
+    assert st["nonfinite_anchor"] == 1 and st["not_converged"] == 1
+    assert st["sweeps"][1] == 1
+    gm = [gen.stored(mi.g_mask(0), "f32") for mi in ins]
+    W = [to_dev(gen.stored(mi.w0(), "f32")[0], "f32", dev) for mi in ins]
+    Wo = ora.step([gen.stored(ins[0].w0(), "f32")[1]], [gm[0][1]])
+    opt.step(W, [to_dev(p, "f32", dev) for p, _ in gm])
+    ef = relf(from_dev(opt.get_filtered(0)), ora.last_filt[0])
+    keep = np.abs(ora.last_proj[0]) >= 1e-6
+    ew = float(np.abs(from_dev(W[0]) - Wo[0])[keep].max())
+    say(f"  matrix 0: relF G_filt {ef:.3e} W {ew:.3e}")
+    assert ef <= 1e-4 and ew <= 1e-7
+    opt.close()
+
+
+def opt_hp(opt):
+    return {k: opt.hp[k] for k in ("tau_p", "alpha", "beta_anc", "lr", "beta1", "beta2", "eps",
+                                   "weight_decay")}
+
+
+def test_async_refresh_matches_oracle():
+    """The asynchronous anchor updates against the oracle run in the synchronous
+    order they stand for: steps issued while a refresh is pending use the
+    previous factors, so the oracle takes those steps before the anchor update.
+    G_filt and G_proj of every step and the weights at the end are compared."""
+    import spectral_correction_optimizer_amd as sco
+    from tests.gpu_harness import REL_TOL, SMALL_G, W_TOL
+    dev = torch.device("cuda")
+    shapes = [(192, 256), (512, 128), (128, 128)]
+    say(f"case: asynchronous refresh vs the oracle in synchronous order, {shapes}")
+    ins = [gen.MatrixInputs(135, 0, i, *sh) for i, sh in enumerate(shapes)]
+    GA = [[gen.stored(mi.g_anc(k), "f32") for mi in ins] for k in range(3)]
+    G = [[gen.stored(mi.g_mask(k), "f32") for mi in ins] for k in range(6)]
+    opt = sco.SpectralAdamW(shapes, device=dev)
+    opt.keep_proj(True)
+    ora = oracle.Optimizer(shapes, opt_hp(opt))
+    W, Wo = [], []
+    for i, mi in enumerate(ins):
+        pay, val = gen.stored(mi.m0(), "f32")
+        opt.set_state(i, "m_anc", to_dev(pay, "f32", dev))
+        ora.set_anchor_momentum(i, val)
+        pay, val = gen.stored(mi.w0(), "f32")
+        W.append(to_dev(pay, "f32", dev))
+        Wo.append(val)
+    dv = lambda xs: [to_dev(p, "f32", dev) for p, _ in xs]
+    hv = lambda xs: [v for _, v in xs]
+    worst = [0.0, 0.0]
+    small = None
+
+    def step(k):
+        nonlocal Wo, small
+        opt.step(W, dv(G[k]))
+        Wo = ora.step(Wo, hv(G[k]))
+        if small is None:
+            small = [np.abs(p) < SMALL_G for p in ora.last_proj]
+        for i in range(len(shapes)):
+            gf, gp = opt.get_filtered(i, proj=True)
+            worst[0] = max(worst[0], relf(from_dev(gf), ora.last_filt[i]))
+            worst[1] = max(worst[1], relf(from_dev(gp), ora.last_proj[i]))
+
+    opt.anchor_update(dv(GA[0]))
+    ora.anchor_update(hv(GA[0]))
+    step(0)
+    opt.anchor_update_async(dv(GA[1]))   # pending while steps 1 and 2 run
+    step(1)
+    step(2)
+    opt.refresh_wait()
+    ora.anchor_update(hv(GA[1]))
+    step(3)
+    opt.anchor_update_async(dv(GA[2]))
+    step(4)
+    opt.refresh_wait()
+    ora.anchor_update(hv(GA[2]))
+    step(5)
+    torch.cuda.synchronize()
+    werr = max(float(np.abs(from_dev(W[i]) - Wo[i])[~small[i]].max()) for i in range(len(shapes)))
+    say(f"  worst relF G_filt {worst[0]:.3e} G_proj {worst[1]:.3e} W {werr:.3e}")
+    assert worst[0] <= REL_TOL and worst[1] <= REL_TOL and werr <= W_TOL
+    assert opt.stats()["not_converged"] == 0
+    opt.close()
