@@ -566,7 +566,9 @@ def test_async_refresh_matches_oracle():
     """The asynchronous anchor updates against the oracle run in the synchronous
     order they stand for: steps issued while a refresh is pending use the
     previous factors, so the oracle takes those steps before the anchor update.
-    G_filt and G_proj of every step and the weights at the end are compared."""
+    G_filt and G_proj of the steps outside a pending window (reading them back
+    completes the refresh) and the weights at the end, which carry every step,
+    are compared."""
     import spectral_correction_optimizer_amd as sco
     from tests.gpu_harness import REL_TOL, SMALL_G, W_TOL
     dev = torch.device("cuda")
@@ -591,28 +593,35 @@ def test_async_refresh_matches_oracle():
     worst = [0.0, 0.0]
     small = None
 
-    def step(k):
+    def step(k, inspect=True):
+        # inspect=False while a refresh is pending: reading G_filt back would
+        # complete the refresh and switch the next steps to the new factors
         nonlocal Wo, small
         opt.step(W, dv(G[k]))
         Wo = ora.step(Wo, hv(G[k]))
         if small is None:
             small = [np.abs(p) < SMALL_G for p in ora.last_proj]
+        if not inspect:
+            return
         for i in range(len(shapes)):
             gf, gp = opt.get_filtered(i, proj=True)
             worst[0] = max(worst[0], relf(from_dev(gf), ora.last_filt[i]))
             worst[1] = max(worst[1], relf(from_dev(gp), ora.last_proj[i]))
 
-    opt.anchor_update(dv(GA[0]))
+    # the anchor gradients of an asynchronous update must stay allocated until its
+    # refresh is completed (the EMA reads them on the library's own stream)
+    ga_dev = [dv(GA[k]) for k in range(3)]
+    opt.anchor_update(ga_dev[0])
     ora.anchor_update(hv(GA[0]))
     step(0)
-    opt.anchor_update_async(dv(GA[1]))   # pending while steps 1 and 2 run
-    step(1)
-    step(2)
+    opt.anchor_update_async(ga_dev[1])   # pending while steps 1 and 2 run
+    step(1, inspect=False)
+    step(2, inspect=False)
     opt.refresh_wait()
     ora.anchor_update(hv(GA[1]))
     step(3)
-    opt.anchor_update_async(dv(GA[2]))
-    step(4)
+    opt.anchor_update_async(ga_dev[2])
+    step(4, inspect=False)
     opt.refresh_wait()
     ora.anchor_update(hv(GA[2]))
     step(5)
