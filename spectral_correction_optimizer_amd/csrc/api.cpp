@@ -197,6 +197,7 @@ struct sc_opt {
         // progress of the refresh in flight
         int stage = 0, which = 0, r = 0, rps = 1, max_rounds = 0, first_check = 0, poll_round = 0;
         bool pre = false, poll_pending = false;
+        bool targeted = false;  // polishing sweeps restricted to the pairs the certificate marks
     } pipes[kPipes];
     int npipes = 0;
     hipEvent_t fork = nullptr;
@@ -386,7 +387,9 @@ PtrTable make_table(const sc_opt* h, const void* const* p) {
 // ---- refresh ------------------------------------------------------------------------
 
 enum { LIST_PLAIN = 0, LIST_FACTOR = 1, LIST_POLISH = 2 };
-enum { STAGE_ROUNDS = 0, STAGE_CERT = 1, STAGE_DONE = 2 };
+// STAGE_CERT: waiting for the certificate of the factor phase's A = M V;
+// STAGE_CERT2: for the re-certification after selective polishing
+enum { STAGE_ROUNDS = 0, STAGE_CERT = 1, STAGE_CERT2 = 2, STAGE_DONE = 3 };
 typedef sc_opt::Pipe Pipe;
 
 // d = s / (s + tau) and the projectors X^T diag(d) X of the pipe's matrices.
@@ -462,9 +465,23 @@ void account_sweeps(sc_opt* h, const MatFlags* flags) {
         const double pairs[2] = {(double)f.pairs_pre, (double)(f.pairs_applied - f.pairs_pre)};
         const double len[2] = {(double)m.klen, (double)m.K};
         const double vlen[2] = {0.0, (double)m.k};
-        const double sweeps[2] = {(double)f.sweep_base, (double)(f.sweeps - f.sweep_base)};
+        // selective polishing sweeps (few pairs, unfused: each Gram from the operand,
+        // rotated pairs' A and V rows) apart from the full sweeps
+        const double sel_sw = f.sel_sweeps;
+        const double rounds_sel = sel_sw * (m.nb - 1);
+        const double sweeps[2] = {(double)f.sweep_base, (double)(f.sweeps - f.sweep_base) - sel_sw};
+        const double rounds_full[2] = {rounds[0], rounds[1] - rounds_sel};
+        const double pairs_full[2] = {pairs[0], pairs[1] - f.sel_rot};
+        if (f.sel_sweeps > 0) {
+            const double L = m.K;
+            h->prof.flops[PK_SOLVE] += f.sel_rot * (pw * (pw - 1) / 2) * 18.0 * pw;
+            h->prof.flops[PK_GRAM] += f.sel_pairs * 2.0 * pw * pw * L;
+            h->prof.bytes[PK_GRAM] += f.sel_pairs * 4.0 * pw * L;
+            h->prof.flops[PK_APPLY] += f.sel_rot * 2.0 * pw * pw * (L + m.k);
+            h->prof.bytes[PK_APPLY] += f.sel_rot * (8.0 * pw * (L + m.k) + 4.0 * pw * pw);
+        }
         for (int ph = 0; ph < 2; ++ph) {
-            h->prof.flops[PK_SOLVE] += pairs[ph] * (pw * (pw - 1) / 2) * 18.0 * pw;
+            h->prof.flops[PK_SOLVE] += pairs_full[ph] * (pw * (pw - 1) / 2) * 18.0 * pw;
             if (h->fuse && h->fused[i][ph]) {
                 // Gram read standalone in a sweep's first round only; the fused
                 // kernel reads every pair's rows every round, writes the rotated
@@ -472,20 +489,20 @@ void account_sweeps(sc_opt* h, const MatFlags* flags) {
                 h->prof.flops[PK_GRAM] += sweeps[ph] * (m.nb / 2) * 2.0 * pw * pw * len[ph];
                 h->prof.bytes[PK_GRAM] += sweeps[ph] * (m.nb / 2) * 4.0 * pw * len[ph];
                 h->prof.flops[PK_APPLY_GRAM] +=
-                    pairs[ph] * 2.0 * pw * pw * len[ph] +
-                    (rounds[ph] - sweeps[ph]) * (m.nb / 2) * 3.0 * 2.0 * 32 * 32 * len[ph];
-                h->prof.bytes[PK_APPLY_GRAM] += rounds[ph] * (m.nb / 2) * 4.0 * pw * len[ph] +
-                                                pairs[ph] * (4.0 * pw * len[ph] + 4.0 * pw * pw);
+                    pairs_full[ph] * 2.0 * pw * pw * len[ph] +
+                    (rounds_full[ph] - sweeps[ph]) * (m.nb / 2) * 3.0 * 2.0 * 32 * 32 * len[ph];
+                h->prof.bytes[PK_APPLY_GRAM] += rounds_full[ph] * (m.nb / 2) * 4.0 * pw * len[ph] +
+                                                pairs_full[ph] * (4.0 * pw * len[ph] + 4.0 * pw * pw);
                 if (vlen[ph] > 0.0) {
-                    h->prof.flops[PK_APPLY] += pairs[ph] * 2.0 * pw * pw * vlen[ph];
-                    h->prof.bytes[PK_APPLY] += pairs[ph] * (8.0 * pw * vlen[ph] + 4.0 * pw * pw);
+                    h->prof.flops[PK_APPLY] += pairs_full[ph] * 2.0 * pw * pw * vlen[ph];
+                    h->prof.bytes[PK_APPLY] += pairs_full[ph] * (8.0 * pw * vlen[ph] + 4.0 * pw * pw);
                 }
             } else {
-                h->prof.flops[PK_GRAM] += rounds[ph] * (m.nb / 2) * 2.0 * pw * pw * len[ph];
-                h->prof.bytes[PK_GRAM] += rounds[ph] * (m.nb / 2) * 4.0 * pw * len[ph];
-                h->prof.flops[PK_APPLY] += pairs[ph] * 2.0 * pw * pw * (len[ph] + vlen[ph]);
+                h->prof.flops[PK_GRAM] += rounds_full[ph] * (m.nb / 2) * 2.0 * pw * pw * len[ph];
+                h->prof.bytes[PK_GRAM] += rounds_full[ph] * (m.nb / 2) * 4.0 * pw * len[ph];
+                h->prof.flops[PK_APPLY] += pairs_full[ph] * 2.0 * pw * pw * (len[ph] + vlen[ph]);
                 h->prof.bytes[PK_APPLY] +=
-                    pairs[ph] * (8.0 * pw * (len[ph] + vlen[ph]) + 4.0 * pw * pw);
+                    pairs_full[ph] * (8.0 * pw * (len[ph] + vlen[ph]) + 4.0 * pw * pw);
             }
         }
     }
@@ -539,7 +556,8 @@ void pipe_start_rounds(sc_opt* h, Pipe& p, int which, int first_check_sweeps, in
     p.which = which;
     p.r = 0;
     p.rps = std::max(1, (max_nb ? max_nb : p.L[which].max_nb) - 1);
-    p.max_rounds = p.L[which].nmat ? h->hp.max_sweeps * p.rps : 0;
+    const int cap = p.targeted ? std::min(kSelSweeps, h->hp.max_sweeps) : h->hp.max_sweeps;
+    p.max_rounds = p.L[which].nmat ? cap * p.rps : 0;
     p.first_check = std::min(p.max_rounds, first_check_sweeps * p.rps);
     p.poll_pending = false;
 }
@@ -559,14 +577,16 @@ int pipe_round(sc_opt* h, Pipe& p, hipStream_t st) {
         HIP_TRY(timed(h, PK_SORT, st, [&] {
             return launch_jacobi_sort(h->md, h->flags_d, L.mats, L.nmat, r, st);
         }));
-    // with every matrix fused the standalone Gram only serves sweeps' first rounds
-    if (!(h->fuse && L.all_fused) || first)
+    // with every matrix fused the standalone Gram only serves sweeps' first rounds;
+    // selective polishing works on few pairs per round, each Gram from the operand
+    const bool fuse = h->fuse && !p.targeted;
+    if (!(fuse && L.all_fused) || first)
         HIP_TRY(timed(h, PK_GRAM, st, [&] {
-            return launch_jacobi_gram(h->md, h->flags_d, L.gi, L.ngi, r, h->fuse ? 1 : 0, st);
+            return launch_jacobi_gram(h->md, h->flags_d, L.gi, L.ngi, r, fuse ? 1 : 0, st);
         }));
     HIP_TRY(timed(h, PK_SOLVE, st,
                   [&] { return launch_jacobi_solve(h->md, h->flags_d, L.si, L.nsi, r, h->solve_waves, h->solve_copies, st); }));
-    if (h->fuse && L.nfi) {
+    if (fuse && L.nfi) {
         if (L.nai_f)
             HIP_TRY(timed(h, PK_APPLY, st, [&] {
                 return launch_jacobi_apply(h->md, h->flags_d, L.ai_f, L.nai_f, r, st);
@@ -608,8 +628,40 @@ bool pipe_all_done(const sc_opt* h, const Pipe& p) {
 // End of a pipe's sweeps.  After the factor phase: V from the factor, A = M V,
 // the final Gram and its certificate (polled); otherwise the final Gram and the
 // finalization.
+// Selective polishing of the matrices that failed the certificate: mark their
+// pairs with a block above the threshold, then at most kSelSweeps sweeps that
+// work only on those pairs (max_nb: rounds per sweep; 0 = the list's largest).
+int pipe_start_selective(sc_opt* h, Pipe& p, hipStream_t st, int max_nb) {
+    HIP_TRY(timed(h, PK_INIT_FLAGS, st, [&] {
+        return launch_polish_mark(h->md, h->flags_d, p.cap, p.ncap, p.L[LIST_POLISH].max_nb, st);
+    }));
+    p.targeted = true;
+    pipe_start_rounds(h, p, LIST_POLISH, 1, max_nb);
+    return SC_OK;
+}
+
+// Full polishing sweeps for the matrices the re-certification still rejects.
+int pipe_start_full_polish(sc_opt* h, Pipe& p, hipStream_t st, int max_nb) {
+    HIP_TRY(timed(h, PK_INIT_FLAGS, st,
+                  [&] { return launch_polish_full(h->flags_d, p.cap, p.ncap, st); }));
+    p.targeted = false;
+    pipe_start_rounds(h, p, LIST_POLISH, 1, max_nb);
+    return SC_OK;
+}
+
 int pipe_after_rounds(sc_opt* h, Pipe& p, hipStream_t st) {
     int rc;
+    if (p.which == LIST_POLISH && p.targeted) {
+        // re-certify: the Gram of the selectively polished matrices again, then the
+        // certificate over every factor-phase matrix (the others keep theirs)
+        if ((rc = pipe_final_gram(h, p, st, true))) return rc;
+        HIP_TRY(timed(h, PK_INIT_FLAGS, st,
+                      [&] { return launch_certify(h->md, h->flags_d, p.cap, p.ncap, st); }));
+        p.targeted = false;
+        if (!h->hp.sync_check) return pipe_start_full_polish(h, p, st, 0);
+        p.stage = STAGE_CERT2;
+        return pipe_poll(h, p, st);
+    }
     if (p.which == LIST_FACTOR) {
         // Right singular vectors of A from the factor phase: V <- diag(1/|x_j|) X^T V_prev
         // (rows), then the true operand A = M V.  A rejected matrix keeps V = V_prev and
@@ -629,10 +681,9 @@ int pipe_after_rounds(sc_opt* h, Pipe& p, hipStream_t st) {
         HIP_TRY(timed(h, PK_INIT_FLAGS, st,
                       [&] { return launch_certify(h->md, h->flags_d, p.cap, p.ncap, st); }));
         if (!h->hp.sync_check) {
-            // enqueue only: polishing rounds for every factor-phase matrix; the
-            // certified ones are done and their launches exit at once
-            pipe_start_rounds(h, p, LIST_POLISH, 1);
-            return SC_OK;
+            // enqueue only: selective, then full polishing rounds for every
+            // factor-phase matrix; certified ones are done, their launches exit at once
+            return pipe_start_selective(h, p, st, 0);
         }
         p.stage = STAGE_CERT;
         return pipe_poll(h, p, st);
@@ -683,17 +734,20 @@ int do_refresh(sc_opt* h, hipStream_t st) {
                 } else {
                     p.poll_pending = false;
                     const bool all = pipe_all_done(h, p);
-                    if (p.stage == STAGE_CERT) {
+                    if (p.stage == STAGE_CERT || p.stage == STAGE_CERT2) {
                         if (all) {
                             if ((rc = pipe_finalize(h, p, ps))) return rc;
                             p.stage = STAGE_DONE;
                         } else {
-                            // polish the matrices that failed the certificate
+                            // polish the matrices that failed the certificate: first
+                            // selectively, then (re-certification failed) in full
                             int nb = 2;
                             for (int i : p.host_mats)
                                 if (h->mh[i].klen && !p.flags_h[i].done)
                                     nb = std::max(nb, h->mh[i].nb);
-                            pipe_start_rounds(h, p, LIST_POLISH, 1, nb);
+                            rc = p.stage == STAGE_CERT ? pipe_start_selective(h, p, ps, nb)
+                                                       : pipe_start_full_polish(h, p, ps, nb);
+                            if (rc) return rc;
                         }
                         queued = true;
                         continue;
@@ -907,7 +961,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
     };
     struct Offs {
         size_t Manc, madam, vadam, A, V, F, W, PL, PR, s, d, norm2, Gfilt, Y, T, E, invn, gram, rot,
-            rflag, perm, cnorm, chol;
+            rflag, perm, cnorm, chol, bmax;
     };
     std::vector<Offs> o(n);
     for (int i = 0; i < n; ++i) {
@@ -967,6 +1021,8 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         o[i].perm = take((size_t)m.kpad * sizeof(int));
         o[i].cnorm = take((size_t)m.kpad * sizeof(float));
         o[i].chol = take((size_t)m.k * m.k * sizeof(double));
+        const bool sel = m.klen && m.kpad <= kSelMaxK;
+        o[i].bmax = take(sel ? (size_t)m.nb * m.nb * sizeof(float) : 0);
     }
     void* arena = nullptr;
     if (hipMalloc(&arena, total) != hipSuccess) {
@@ -1004,6 +1060,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         m.perm = (int*)(b + o[i].perm);
         m.cnorm = (float*)(b + o[i].cnorm);
         m.chol = (double*)(b + o[i].chol);
+        m.bmax = (m.klen && m.kpad <= kSelMaxK) ? (float*)(b + o[i].bmax) : nullptr;
     }
     void* p = nullptr;
     HIP_TRY(hipMalloc(&p, sizeof(MatDev) * n));

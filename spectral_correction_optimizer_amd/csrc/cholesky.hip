@@ -507,12 +507,74 @@ __global__ void phase2_reset_kernel(MatFlags* __restrict__ flags, const int* __r
     f.sweep_base = f.sweeps;
     f.pairs_pre = f.pairs_applied;
     f.check_off = 0u;
+    f.sel = 0;
 }
 
 hipError_t launch_phase2_reset(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
                                hipStream_t st) {
     (void)mats;
     hipLaunchKernelGGL(phase2_reset_kernel, dim3((nmat + 63) / 64), dim3(64), 0, st, flags, mat_idx,
+                       nmat);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
+// Selective polishing.  A matrix fails the certificate when a few of its column
+// pairs are not orthogonal enough; at the workload's spectra these are the
+// pairs of a large and a small singular value (an error of the factor phase's
+// right vectors is amplified by their ratio in A = M V), all in the blocks of
+// the largest columns.  One workgroup per (block I of the column order,
+// matrix) reduces the certificate's E over the columns of block I against
+// every block J: bmax[I][J] = max |E_ij| (NaN counted as infinity).  The first
+// workgroup of a matrix then sets sel, which limits the polishing sweeps to
+// the pairs marked above the convergence threshold (pair_selected).
+__global__ __launch_bounds__(256) void polish_mark_kernel(const MatDev* __restrict__ mats,
+                                                          MatFlags* __restrict__ flags,
+                                                          const int* __restrict__ mat_idx) {
+    __shared__ int inv[kSelMaxK];
+    __shared__ unsigned int bm[kSelMaxK / kJb];
+    const int i = mat_idx[blockIdx.y];
+    const MatDev& md = mats[i];
+    MatFlags& f = flags[i];
+    if (f.done || !md.bmax) return;
+    const int bI = blockIdx.x, nb = md.nb, k = md.k;
+    if (bI >= nb) return;
+    for (int j = threadIdx.x; j < md.kpad; j += blockDim.x) inv[gld(md.perm + j)] = j;
+    for (int j = threadIdx.x; j < nb; j += blockDim.x) bm[j] = 0u;
+    __syncthreads();
+    for (int a = 0; a < kJb; ++a) {
+        const int pa = gld(md.perm + bI * kJb + a);  // physical row; padding rows are zero
+        if (pa >= k) continue;
+        const float* e = md.E + (int64_t)pa * k;
+        for (int c = threadIdx.x; c < k; c += blockDim.x) {
+            const float v = fabsf(gld(e + c));
+            const unsigned int u = v == v ? __float_as_uint(v) : 0x7f800000u;
+            if (u) atomicMax(&bm[inv[c] / kJb], u);
+        }
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < nb; j += blockDim.x)
+        gst(md.bmax + (int64_t)bI * nb + j, __uint_as_float(bm[j]));
+    if (bI == 0 && threadIdx.x == 0) f.sel = 1;
+}
+
+hipError_t launch_polish_mark(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
+                              int max_nb, hipStream_t st) {
+    hipLaunchKernelGGL(polish_mark_kernel, dim3(max_nb, nmat), dim3(256), 0, st, mats, flags, mat_idx);
+    return hipGetLastError();
+}
+
+__global__ void polish_full_kernel(MatFlags* __restrict__ flags, const int* __restrict__ mat_idx,
+                                   int nmat) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= nmat) return;
+    MatFlags& f = flags[mat_idx[t]];
+    f.sel = 0;
+    f.sweep_max = 0u;
+}
+
+hipError_t launch_polish_full(MatFlags* flags, const int* mat_idx, int nmat, hipStream_t st) {
+    hipLaunchKernelGGL(polish_full_kernel, dim3((nmat + 63) / 64), dim3(64), 0, st, flags, mat_idx,
                        nmat);
     return hipGetLastError();
 }

@@ -57,6 +57,8 @@ struct MatDev {
     float tol_conv;  // a sweep whose largest such ratio is <= tol_conv ends the sweeps
     int pad1;
     double* chol;    // [k][k] Gram of A, then its Cholesky factor (lower triangle); klen > 0 only
+    float* bmax;     // [nb][nb] selective polishing: largest |E_ij| per block pair (klen > 0
+                     // and kpad <= kSelMaxK only, else null)
 };
 
 // Per-matrix device flags / counters.
@@ -73,8 +75,16 @@ struct MatFlags {
     int pairs_pre;           // pairs_applied at the end of the factor phase
     unsigned int check_off;  // largest |a_p.a_q| / (|a_p| |a_q|) of the final operand (float bits)
     int regram;              // 1 when the certificate failed: polished, its final Gram is redone
-    int pad[1];
+    int sel;                 // 1 while polishing sweeps work only on the pairs bmax marks
+    int sel_pairs;           // pair Grams solved in selective sweeps (work accounting)
+    int sel_rot;             // pairs rotated in selective sweeps (work accounting)
+    int sel_sweeps;          // selective sweeps run
 };
+
+// Selective polishing: largest k (and kpad) whose inverse column order fits the
+// marking kernel's LDS, and the sweep cap of the selective phase.
+constexpr int kSelMaxK = 4096;
+constexpr int kSelSweeps = 3;
 
 // ---- work items ------------------------------------------------------------------
 
@@ -200,6 +210,14 @@ hipError_t launch_factor_invnorm(const MatDev* mats, const MatFlags* flags, cons
 // Start of the polishing phase for the matrices in mat_idx (A already recomputed).
 hipError_t launch_phase2_reset(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
                                hipStream_t st);
+// Selective polishing of the matrices in mat_idx that failed the certificate
+// (not done): bmax from the certificate's E in the current column order, then
+// sel = 1.  max_nb: largest block count.
+hipError_t launch_polish_mark(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
+                              int max_nb, hipStream_t st);
+// After selective polishing failed its re-certification: sel = 0, so that full
+// polishing sweeps follow for the matrices that are not done.
+hipError_t launch_polish_full(MatFlags* flags, const int* mat_idx, int nmat, hipStream_t st);
 
 // dst[c * ld_dst + r] = src[r * ld_src + c] for r < rows, c < cols
 hipError_t launch_transpose(const float* src, int rows, int cols, int ld_src, float* dst,

@@ -40,6 +40,19 @@ __device__ __forceinline__ int pair_row(const MatDev& md, int blkI, int blkJ, in
     return gld(md.perm + (rho < kJb ? blkI * kJb + rho : blkJ * kJb + (rho - kJb)));
 }
 
+// Selective polishing (sel set after a failed certificate): only pairs with a
+// block above the convergence threshold in the certificate's normalized Gram
+// (the cross block or either diagonal block, from bmax) are worked on; the
+// others were certified and keep their orthogonality up to second-order terms
+// of the rotations elsewhere (the re-certification checks it).
+__device__ __forceinline__ bool pair_selected(const MatDev& md, const MatFlags& fl, int bI, int bJ) {
+    if (!fl.sel) return true;
+    const float t = md.tol_conv;
+    const float* b = md.bmax;
+    const int nb = md.nb;
+    return gld(b + bI * nb + bJ) > t || gld(b + bI * nb + bI) > t || gld(b + bJ * nb + bJ) > t;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------------
@@ -77,6 +90,7 @@ __global__ __launch_bounds__(256) void jac_gram_kernel(const MatDev* __restrict_
     if (skip_fused && it.fused && round % (nb - 1) != 0) return;
     int bI, bJ;
     block_pair(nb, round % (nb - 1), it.slot, &bI, &bJ);
+    if (!pair_selected(md, flags[it.mat], bI, bJ)) return;
     const int x_begin = it.x0, x_end = it.x1;
 
     // loader: 64 rows x 32 columns = 512 float4 slots, 2 per thread
@@ -304,6 +318,11 @@ __global__ __launch_bounds__(64) void jac_solve_kernel(const MatDev* __restrict_
     const int l = threadIdx.x;
     int bI, bJ;
     block_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
+    if (!pair_selected(md, fl, bI, bJ)) {
+        if (l == 0) md.rot_flag[it.slot] = 0;
+        return;
+    }
+    if (fl.sel && l == 0) atomicAdd(&fl.sel_pairs, 1);
 
     // 1. the pair Gram: split partials summed in fixed order (fp64).  Lane l
     //    takes the diagonal entry of column l and 4 entries of each stored upper
@@ -489,6 +508,7 @@ __global__ __launch_bounds__(64) void jac_solve_kernel(const MatDev* __restrict_
     if (l == 0) {
         *rflag = 1;
         atomicAdd(&fl.pairs_applied, 1);
+        if (fl.sel) atomicAdd(&fl.sel_rot, 1);
     }
 }
 
@@ -533,6 +553,11 @@ __global__ __launch_bounds__(64 * NW) void jac_solve_waves_kernel(const MatDev* 
     const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int bI, bJ;
     block_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
+    if (!pair_selected(md, fl, bI, bJ)) {
+        if (threadIdx.x == 0) md.rot_flag[it.slot] = 0;
+        return;
+    }
+    if (fl.sel && threadIdx.x == 0) atomicAdd(&fl.sel_pairs, 1);
 
     // 1. the pair Gram as in the one-wavefront kernel; every wave sums the
     //    diagonal, the stored upper tiles are shared out (entries NE w .. + NE - 1)
@@ -709,6 +734,7 @@ __global__ __launch_bounds__(64 * NW) void jac_solve_waves_kernel(const MatDev* 
     if (threadIdx.x == 0) {
         *rflag = 1;
         atomicAdd(&fl.pairs_applied, 1);
+        if (fl.sel) atomicAdd(&fl.sel_rot, 1);
     }
 }
 
@@ -1059,7 +1085,7 @@ __global__ __launch_bounds__(256) void jac_sort_kernel(const MatDev* __restrict_
     __shared__ float key[kSortMax];
     __shared__ int idx[kSortMax];
     const int i = mat_idx[blockIdx.x];
-    if (flags[i].done) return;
+    if (flags[i].done || flags[i].sel) return;  // selective sweeps keep bmax's column order
     const MatDev& md = mats[i];
     if (round % (md.nb - 1) != 0) return;
     if (md.kpad > kSortMax) return;  // beyond the LDS sort size the order stays as it is
@@ -1113,6 +1139,7 @@ __global__ void jac_sweep_end_kernel(const MatDev* __restrict__ mats, MatFlags* 
     const int nbm1 = mats[i].nb - 1;
     if (round % nbm1 != nbm1 - 1) return;
     f.sweeps += 1;
+    if (f.sel) f.sel_sweeps += 1;
     const float mo = __uint_as_float(f.sweep_max);
     f.sweep_max = 0u;
     if (!(mo <= 3.402823466e38f)) {
@@ -1120,7 +1147,8 @@ __global__ void jac_sweep_end_kernel(const MatDev* __restrict__ mats, MatFlags* 
     } else if (!(mo > mats[i].tol_conv)) {
         f.converged = 1;
         f.done = 1;
-    } else if (f.sweeps - f.sweep_base >= max_sweeps) {
+    } else if (f.sel ? f.sel_sweeps >= kSelSweeps
+                     : f.sweeps - f.sweep_base - f.sel_sweeps >= max_sweeps) {
         f.done = 1;
     }
 }

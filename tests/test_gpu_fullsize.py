@@ -236,10 +236,13 @@ def test_sampled_noisy_parity_16_blocks(run, sample):
             ok_w = ew <= W_TOL
             wnote = f"W {ew:.3e} (excluded {int((~keep).sum())}, max {float(err[~keep].max()) if (~keep).any() else 0.0:.3e})"
         else:
+            # bfloat16 W is state on both sides, rounded at every step: a rounding
+            # that falls the other way at one step persists, so after j steps the
+            # gate is j ulps (one per step; a single step is held to one ulp)
             ulps = err / bf16_ulp(W)
-            ok_w = float(ulps[keep].max()) <= 1.0
+            ok_w = float(ulps[keep].max()) <= j + 1
             wnote = (f"W max {float(ulps[keep].max()):.2f} bf16 ulp ({int((ulps > 0).sum())} differ, "
-                     f"excluded {int((~keep).sum())})")
+                     f"{int((ulps > 1).sum())} by more than one; excluded {int((~keep).sum())})")
         say(f"  mat {idx} {m}x{n} step {j + 1} tau {tau:g}: relF G_filt {ef:.3e} G_proj {ep:.3e} {wnote}"
             + (f" oracle sweeps {o.sweeps[0]} GPU sweeps {st['sweeps'][idx]} (factor {st['factor_sweeps'][idx]})"
                if j == 0 else ""))
