@@ -71,8 +71,6 @@ def parse():
                     help="LDS copies of the pair Gram in the multi-wave solve (0: by pair count)")
     ap.add_argument("--no-fused-gram", action="store_true",
                     help="every Jacobi round's pair Gram from the operand (no fused apply + Gram)")
-    ap.add_argument("--no-interleave", action="store_true",
-                    help="let the two refresh pipelines' rotation applies overlap freely")
     ap.add_argument("--cold-start", action="store_true",
                     help="every refresh starts its sweeps from A = M (no warm start)")
     ap.add_argument("--drift", type=float, default=0.0, metavar="THETA",
@@ -381,7 +379,6 @@ def main():
                             warm_start=0 if args.cold_start else 1, **hp)
     opt.set_solve_waves(args.solve_waves, args.solve_copies)
     opt.set_fused_gram(not args.no_fused_gram)
-    opt.set_pipe_interleave(not args.no_interleave)
     for i, mi in enumerate(src):
         opt.set_state(i, "m_anc", mi.m0())
 
@@ -514,7 +511,6 @@ def main():
                    "lr": hp["lr"]},
         "solve_variant": {"waves": args.solve_waves or "auto", "copies": args.solve_copies or "auto"},
         "fused_gram": not args.no_fused_gram,
-        "pipe_interleave": not args.no_interleave,
         "warm_start": not args.cold_start,
         "drift": args.drift,
         "refresh_ms": round(r_med, 2),

@@ -216,15 +216,6 @@ int sc_set_solve_waves(sc_handle h, int waves, int copies);
  * pending asynchronous refresh. */
 int sc_set_fused_gram(sc_handle h, int enable);
 
-/* Alternation of the refresh's two pipelines (enabled by default): the refresh
- * splits the matrices over two internal streams; with this on, the rotation
- * applies of one stream's Jacobi rounds (which stream the operands through HBM)
- * wait for the other stream's previous applies, so that one stream applies
- * while the other runs its pair solves (LDS and vector-ALU bound) instead of
- * two applies sharing HBM.  Results do not depend on it.  Waits for a pending
- * asynchronous refresh. */
-int sc_set_pipe_interleave(sc_handle h, int enable);
-
 /* Keep G_proj of each step (costs one more store per element in the AdamW
  * pass and rows x cols floats per matrix). */
 int sc_keep_proj(sc_handle h, int enable);

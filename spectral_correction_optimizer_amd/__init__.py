@@ -31,7 +31,7 @@ EXPORTED_SYMBOLS = (
     "sc_default_hparams", "sc_opt_create", "sc_opt_destroy", "sc_anchor_update", "sc_refresh",
     "sc_anchor_update_async", "sc_refresh_wait", "sc_refresh_pending", "sc_step", "sc_set_lr", "sc_set_tau", "sc_set_state", "sc_get_state", "sc_set_step",
     "sc_get_step", "sc_set_factors", "sc_get_factors", "sc_keep_proj", "sc_get_filtered",
-    "sc_set_solve_waves", "sc_set_fused_gram", "sc_set_pipe_interleave",
+    "sc_set_solve_waves", "sc_set_fused_gram",
     "sc_get_stats", "sc_get_sweep_counts", "sc_profile", "sc_get_kernel_times", "sc_last_error",
     "sc_mask_keep_count", "sc_mask_seed", "sc_mask_indices", "sc_mask_pack", "sc_mask_unpack",
 )
@@ -103,7 +103,6 @@ def load_library():
         "sc_keep_proj": (ctypes.c_int, [vp, ctypes.c_int]),
         "sc_set_solve_waves": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int]),
         "sc_set_fused_gram": (ctypes.c_int, [vp, ctypes.c_int]),
-        "sc_set_pipe_interleave": (ctypes.c_int, [vp, ctypes.c_int]),
         "sc_get_filtered": (ctypes.c_int, [vp, ctypes.c_int, vp, vp, vp]),
         "sc_get_stats": (ctypes.c_int, [vp, ctypes.POINTER(Stats), ctypes.POINTER(ctypes.c_int)]),
         "sc_get_sweep_counts": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_int),
@@ -285,10 +284,6 @@ class SpectralAdamW:
     def set_fused_gram(self, enable: bool = True):
         """Fused rotation apply + next-round pair Gram (default on)."""
         _check(self._lib.sc_set_fused_gram(self._h, 1 if enable else 0))
-
-    def set_pipe_interleave(self, enable: bool = True):
-        """Alternate the two refresh pipelines' rotation applies (default on)."""
-        _check(self._lib.sc_set_pipe_interleave(self._h, 1 if enable else 0))
 
     def keep_proj(self, enable: bool = True):
         _check(self._lib.sc_keep_proj(self._h, 1 if enable else 0))

@@ -193,9 +193,6 @@ struct sc_opt {
         GemmGroup lowdin_F, lowdin_eW, lowdin_W, proj;
         hipStream_t st = nullptr;
         hipEvent_t join = nullptr, poll = nullptr;
-        // end of this pipe's last rotation apply (the other pipe's next apply waits on it)
-        hipEvent_t apply_ev = nullptr;
-        bool apply_rec = false;
         MatFlags* flags_h = nullptr;  // pinned target of this pipe's flag polls
         // progress of the refresh in flight
         int stage = 0, which = 0, r = 0, rps = 1, max_rounds = 0, first_check = 0, poll_round = 0;
@@ -232,12 +229,6 @@ struct sc_opt {
     bool proj_stale = false;
     bool keep_proj = false;
     bool fuse = true;                         // fused apply + next Gram where a matrix allows it
-    // The rotation applies of a round stream the operand through HBM; the pair
-    // solves wait on LDS and the vector ALUs.  With interleave each pipe's applies
-    // wait for the other pipe's previous applies, so the two pipes alternate: one
-    // applies while the other solves, instead of two applies sharing HBM.
-    bool interleave = true;
-    bool split_now = false;  // the refresh in flight runs its pipes on their own streams
     std::vector<std::array<char, 2>> fused;   // per matrix: fused over the factor / full rows
     int solve_waves = 0, solve_copies = 0;  // pair solve variant: 0 by the launch's pair count
     std::vector<void*> dev_allocs;
@@ -595,13 +586,6 @@ int pipe_round(sc_opt* h, Pipe& p, hipStream_t st) {
         }));
     HIP_TRY(timed(h, PK_SOLVE, st,
                   [&] { return launch_jacobi_solve(h->md, h->flags_d, L.si, L.nsi, r, h->solve_waves, h->solve_copies, st); }));
-    // the applies of the two pipes alternate (see sc_opt::interleave)
-    const bool alt = h->interleave && h->split_now;
-    if (alt)
-        for (int q = 0; q < h->npipes; ++q) {
-            const Pipe& o = h->pipes[q];
-            if (&o != &p && o.apply_rec) HIP_TRY(hipStreamWaitEvent(st, o.apply_ev, 0));
-        }
     if (fuse && L.nfi) {
         if (L.nai_f)
             HIP_TRY(timed(h, PK_APPLY, st, [&] {
@@ -613,10 +597,6 @@ int pipe_round(sc_opt* h, Pipe& p, hipStream_t st) {
     } else {
         HIP_TRY(timed(h, PK_APPLY, st,
                       [&] { return launch_jacobi_apply(h->md, h->flags_d, L.ai, L.nai, r, st); }));
-    }
-    if (alt) {
-        HIP_TRY(hipEventRecord(p.apply_ev, st));
-        p.apply_rec = true;
     }
     if (last)
         HIP_TRY(timed(h, PK_SWEEP_END, st, [&] {
@@ -721,8 +701,6 @@ int do_refresh(sc_opt* h, hipStream_t st) {
     // kernel's events bracket it alone (no overlap between pipes).
     const bool split = !(h->prof.on && h->prof.serial);
     auto pst = [&](Pipe& p) { return split ? p.st : st; };
-    h->split_now = split;
-    for (int q = 0; q < h->npipes; ++q) h->pipes[q].apply_rec = false;
     if (split) {
         HIP_TRY(hipEventRecord(h->fork, st));
         for (int q = 0; q < h->npipes; ++q) HIP_TRY(hipStreamWaitEvent(h->pipes[q].st, h->fork, 0));
@@ -1255,7 +1233,6 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         HIP_TRY(hipStreamCreateWithFlags(&P.st, hipStreamNonBlocking));
         HIP_TRY(hipEventCreateWithFlags(&P.join, hipEventDisableTiming));
         HIP_TRY(hipEventCreateWithFlags(&P.poll, hipEventDisableTiming));
-        HIP_TRY(hipEventCreateWithFlags(&P.apply_ev, hipEventDisableTiming));
         void* q = nullptr;
         HIP_TRY(hipHostMalloc(&q, sizeof(MatFlags) * n, hipHostMallocDefault));
         P.flags_h = (MatFlags*)q;
@@ -1390,7 +1367,6 @@ void release(sc_opt* h) {
         if (P.st) (void)hipStreamDestroy(P.st);
         if (P.join) (void)hipEventDestroy(P.join);
         if (P.poll) (void)hipEventDestroy(P.poll);
-        if (P.apply_ev) (void)hipEventDestroy(P.apply_ev);
         if (P.flags_h) (void)hipHostFree(P.flags_h);
     }
     if (h->fork) (void)hipEventDestroy(h->fork);
@@ -1757,15 +1733,6 @@ int sc_set_fused_gram(sc_handle h, int enable) {
     DeviceGuard g(h->device);
     if ((rc = finish_async(h, nullptr, true))) return rc;
     h->fuse = enable != 0;
-    return SC_OK;
-}
-
-int sc_set_pipe_interleave(sc_handle h, int enable) {
-    int rc;
-    if ((rc = check_handle(h))) return rc;
-    DeviceGuard g(h->device);
-    if ((rc = finish_async(h, nullptr, true))) return rc;
-    h->interleave = enable != 0;
     return SC_OK;
 }
 

@@ -631,44 +631,3 @@ def test_async_refresh_matches_oracle():
     assert worst[0] <= REL_TOL and worst[1] <= REL_TOL and werr <= W_TOL
     assert opt.stats()["not_converged"] == 0
     opt.close()
-
-
-def test_pipe_interleave_bitwise():
-    """The two refresh pipelines (factor-phase matrices against plain ones here)
-    with and without the alternation of their rotation applies: the same
-    kernels run on disjoint matrices in the same order within each pipe, so
-    factors and weights agree bit for bit over two warm refreshes."""
-    import spectral_correction_optimizer_amd as sco
-    say("case: pipe interleave on/off, 256x256 x2 + 1024x256 + 256x768")
-    dev = torch.device("cuda")
-    shapes = [(256, 256), (256, 256), (1024, 256), (256, 768)]
-    ins = [gen.MatrixInputs(136, 0, i, *sh) for i, sh in enumerate(shapes)]
-    GA = [[to_dev(gen.stored(mi.g_anc(k), "f32")[0], "f32", dev) for mi in ins] for k in range(2)]
-    G = [to_dev(gen.stored(mi.g_mask(0), "f32")[0], "f32", dev) for mi in ins]
-
-    def run(inter):
-        opt = sco.SpectralAdamW(shapes, device=dev)
-        opt.set_pipe_interleave(inter)
-        for i, mi in enumerate(ins):
-            opt.set_state(i, "m_anc", to_dev(gen.stored(mi.m0(), "f32")[0], "f32", dev))
-        W = [to_dev(gen.stored(mi.w0(), "f32")[0], "f32", dev) for mi in ins]
-        opt.anchor_update(GA[0])
-        opt.anchor_update(GA[1])
-        opt.step(W, G)
-        torch.cuda.synchronize()
-        fac = [[t.cpu().numpy().copy() for t in opt.get_factors(i)] for i in range(len(shapes))]
-        out = [w.cpu().numpy().copy() for w in W]
-        st = opt.stats()
-        opt.close()
-        return fac, out, st
-
-    fa, wa, sa = run(True)
-    fb, wb, sb = run(False)
-    say(f"  sweeps {sa['sweeps']} factor {sa['factor_sweeps']}")
-    assert sa["sweeps"] == sb["sweeps"] and sa["not_converged"] == 0
-    assert max(sa["factor_sweeps"]) > 0
-    for a, b in zip(fa, fb):
-        for x, y in zip(a, b):
-            assert np.array_equal(x, y)
-    for x, y in zip(wa, wb):
-        assert np.array_equal(x, y)
