@@ -163,6 +163,24 @@ int sc_refresh_pending(sc_handle h, int* pending);
  * read only. */
 int sc_step(sc_handle h, void* const* W, const void* const* G_mask, void* stream);
 
+/* sc_step without allocations, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step and the same results, but the GEMM chain's
+ * intermediates live in a file-scope device array of the library, 128 MiB per
+ * GPU, held from the library's first use of that GPU until the process ends,
+ * instead of the handle's memory; the matrices run in batches whose
+ * intermediates fit it.  The call allocates nothing (no hipMalloc, no events,
+ * no library routine that allocates).  Every handle on a GPU shares that
+ * GPU's array: calls on one GPU whose work overlaps (other streams, other
+ * threads) race on it and must be ordered by the caller; the array keeps the
+ * last call's contents.  Arguments as sc_step.  Errors: SC_ERR_SHAPE when one
+ * matrix's intermediates exceed the array (4 min(rows, cols)^2 bytes for a
+ * square matrix, twice that otherwise: min(rows, cols) above 5792 or 4096),
+ * before any GPU work; SC_ERR_INVALID_ARG while an asynchronous refresh is
+ * pending or kernel timing is on.  Stale factors are refreshed first, as by
+ * sc_step. */
+int sc_step_noalloc(sc_handle h, void* const* W, const void* const* G_mask, void* stream);
+
 /* Change the learning rate used by later steps (e.g. a cosine schedule). */
 int sc_set_lr(sc_handle h, float lr);
 

@@ -29,7 +29,7 @@ _lib = None
 
 EXPORTED_SYMBOLS = (
     "sc_default_hparams", "sc_opt_create", "sc_opt_destroy", "sc_anchor_update", "sc_refresh",
-    "sc_anchor_update_async", "sc_refresh_wait", "sc_refresh_pending", "sc_step", "sc_set_lr", "sc_set_tau", "sc_set_state", "sc_get_state", "sc_set_step",
+    "sc_anchor_update_async", "sc_refresh_wait", "sc_refresh_pending", "sc_step", "sc_step_noalloc", "sc_set_lr", "sc_set_tau", "sc_set_state", "sc_get_state", "sc_set_step",
     "sc_get_step", "sc_set_factors", "sc_get_factors", "sc_keep_proj", "sc_get_filtered",
     "sc_set_solve_waves", "sc_set_fused_gram",
     "sc_get_stats", "sc_get_sweep_counts", "sc_profile", "sc_get_kernel_times", "sc_last_error",
@@ -92,6 +92,7 @@ def load_library():
         "sc_refresh_wait": (ctypes.c_int, [vp, vp]),
         "sc_refresh_pending": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_int)]),
         "sc_step": (ctypes.c_int, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp]),
+        "sc_step_noalloc": (ctypes.c_int, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp]),
         "sc_set_lr": (ctypes.c_int, [vp, ctypes.c_float]),
         "sc_set_tau": (ctypes.c_int, [vp, ctypes.c_float]),
         "sc_set_state": (ctypes.c_int, [vp, ctypes.c_int, ctypes.c_int, vp, vp]),
@@ -230,6 +231,12 @@ class SpectralAdamW:
         """One spectral-corrected AdamW step; W is updated in place."""
         _check(self._lib.sc_step(self._h, self._ptrs(W, self.w_dtype, "W"),
                                  self._ptrs(G_mask, self.g_dtype, "G_mask"), self._stream()))
+
+    def step_noalloc(self, W, G_mask):
+        """The same step through the allocation-free entry point (intermediates in
+        the library's per-GPU scratch array)."""
+        _check(self._lib.sc_step_noalloc(self._h, self._ptrs(W, self.w_dtype, "W"),
+                                         self._ptrs(G_mask, self.g_dtype, "G_mask"), self._stream()))
 
     def set_lr(self, lr: float):
         _check(self._lib.sc_set_lr(self._h, float(lr)))

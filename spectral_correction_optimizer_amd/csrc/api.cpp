@@ -16,6 +16,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <thread>
@@ -205,6 +206,12 @@ struct sc_opt {
     // step GEMMs: [0] read the refresh's step operands (F, P_L, P_R, d); [1] read
     // the copy published when an asynchronous refresh starts
     GemmGroup step[2][6];
+    // sc_step_noalloc: the same chain in batches over the file-scope scratch array
+    struct NoAllocBatch {
+        GemmGroup g[6];
+    };
+    std::vector<NoAllocBatch> na;
+    std::string na_err;  // why the handle cannot use it ("" when it can)
     // asynchronous refresh (sc_anchor_update_async): a host worker thread drives
     // the refresh on the internal streams behind `astream`; steps issued until
     // sc_refresh_wait (or another entry point) completes it use step[1] on the
@@ -898,51 +905,138 @@ int finish_async(sc_opt* h, hipStream_t st, bool host_wait) {
 // and d, set 1 the copy published for an asynchronous refresh.  Executed chain
 // (fewer flops than U D U^T G V D V^T left to right): square G_filt = P_L (G P_R);
 // tall G_filt = F^T ((D F G) P_R); wide G_filt = (P_L (G F^T D)) F.
-int build_step_groups(sc_opt* h, int set) {
-    GemmGroup* g = h->step[set];
+// Step GEMM problems of matrix i (see build_step_groups) into the six groups g,
+// with the intermediates Y and T at the given addresses.
+void add_step_probs(GemmGroup* g, int i, const MatDev& m, const float* F, const float* PL,
+                    const float* PR, const float* d, float* Y, float* T) {
+    GemmProb p;
+    if (m.m == m.n) {
+        p = make_prob(nullptr, m.n, PR, m.n, T, m.n, m.m, m.n, m.n);  // T = G P_R
+        p.a_ptr = i;
+        g[0].h.push_back(p);
+        p = make_prob(PL, m.m, T, m.n, m.Gfilt, m.n, m.m, m.n, m.m);  // G_filt = P_L T
+        g[3].h.push_back(p);
+    } else if (m.tall) {
+        p = make_prob(F, m.K_ld, nullptr, m.n, Y, m.k, m.k, m.n, m.m);  // Y = D F G
+        p.b_ptr = i;
+        p.row_scale = d;
+        g[1].h.push_back(p);
+        p = make_prob(Y, m.k, PR, m.n, T, m.k, m.k, m.n, m.n);  // T = Y P_R
+        g[3].h.push_back(p);
+        p = make_prob(F, m.K_ld, T, m.k, m.Gfilt, m.n, m.m, m.n, m.k);  // G_filt = F^T T
+        g[4].h.push_back(p);
+    } else {
+        p = make_prob(nullptr, m.n, F, m.K_ld, Y, m.k, m.m, m.k, m.n);  // Y = G F^T D
+        p.a_ptr = i;
+        p.col_scale = d;
+        g[2].h.push_back(p);
+        p = make_prob(PL, m.m, Y, m.k, T, m.k, m.m, m.k, m.m);  // T = P_L Y
+        g[3].h.push_back(p);
+        p = make_prob(T, m.k, F, m.K_ld, m.Gfilt, m.n, m.m, m.n, m.k);  // G_filt = T F
+        g[5].h.push_back(p);
+    }
+}
+
+void init_step_groups(GemmGroup* g, bool gbf) {
     for (int q = 0; q < 6; ++q) g[q] = GemmGroup{};
-    const bool gbf = h->gdt == SC_BF16;
     g[0].abf = gbf;  // square: A = G
     g[1].bbf = gbf;  // tall: B = G
     g[2].tb = true;  // wide: A = G, B = F^T
     g[2].abf = gbf;
     g[4].ta = true;
+}
+
+// Step GEMM tables of one operand set: set 0 reads the refresh's F, P_L, P_R
+// and d, set 1 the copy published for an asynchronous refresh.  Executed chain
+// (fewer flops than U D U^T G V D V^T left to right): square G_filt = P_L (G P_R);
+// tall G_filt = F^T ((D F G) P_R); wide G_filt = (P_L (G F^T D)) F.
+int build_step_groups(sc_opt* h, int set) {
+    GemmGroup* g = h->step[set];
+    init_step_groups(g, h->gdt == SC_BF16);
     for (int i = 0; i < h->n; ++i) {
         const MatDev& m = h->mh[i];
         const float* F = set ? h->pub[i].F : m.F;
         const float* PL = set ? h->pub[i].PL : m.PL;
         const float* PR = set ? h->pub[i].PR : m.PR;
         const float* d = set ? h->pub[i].d : m.d;
-        GemmProb p;
-        if (m.m == m.n) {
-            p = make_prob(nullptr, m.n, PR, m.n, m.T, m.n, m.m, m.n, m.n);  // T = G P_R
-            p.a_ptr = i;
-            g[0].h.push_back(p);
-            p = make_prob(PL, m.m, m.T, m.n, m.Gfilt, m.n, m.m, m.n, m.m);  // G_filt = P_L T
-            g[3].h.push_back(p);
-        } else if (m.tall) {
-            p = make_prob(F, m.K_ld, nullptr, m.n, m.Y, m.k, m.k, m.n, m.m);  // Y = D F G
-            p.b_ptr = i;
-            p.row_scale = d;
-            g[1].h.push_back(p);
-            p = make_prob(m.Y, m.k, PR, m.n, m.T, m.k, m.k, m.n, m.n);  // T = Y P_R
-            g[3].h.push_back(p);
-            p = make_prob(F, m.K_ld, m.T, m.k, m.Gfilt, m.n, m.m, m.n, m.k);  // G_filt = F^T T
-            g[4].h.push_back(p);
-        } else {
-            p = make_prob(nullptr, m.n, F, m.K_ld, m.Y, m.k, m.m, m.k, m.n);  // Y = G F^T D
-            p.a_ptr = i;
-            p.col_scale = d;
-            g[2].h.push_back(p);
-            p = make_prob(PL, m.m, m.Y, m.k, m.T, m.k, m.m, m.k, m.m);  // T = P_L Y
-            g[3].h.push_back(p);
-            p = make_prob(m.T, m.k, F, m.K_ld, m.Gfilt, m.n, m.m, m.n, m.k);  // G_filt = T F
-            g[5].h.push_back(p);
-        }
+        add_step_probs(g, i, m, F, PL, PR, d, m.Y, m.T);
     }
     int rc;
     for (int q = 0; q < 6; ++q)
         if ((rc = upload_group(h, g[q]))) return rc;
+    return SC_OK;
+}
+
+// ---- the allocation-free step (sc_step_noalloc) ------------------------------------
+
+// The step intermediates Y and T of sc_step_noalloc live in this file-scope
+// device array instead of the handle's memory.  Every GPU holds its own copy.
+// In host code the name only stands in for the symbol: the device address comes
+// from hipGetSymbolAddress, once per device (scratch_address), and only that
+// address is passed to kernels.
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on device dev (which must be current).
+int scratch_address(int dev, char** out) {
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(SC_ERR_NO_DEVICE, "device %d beyond the %d the library tracks", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return fail(SC_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = (char*)g_scratch_ptr[dev];
+    return SC_OK;
+}
+
+// Step tables of sc_step_noalloc: matrices in handle order, cut into batches
+// whose Y and T fit the scratch array together; each batch runs the chain's
+// stages before the next reuses the array.  A matrix whose intermediates alone
+// exceed it leaves the entry point unusable for the handle (na_err says why).
+int build_noalloc_groups(sc_opt* h) {
+    char* base = nullptr;
+    int rc;
+    if ((rc = scratch_address(h->device, &base))) return rc;
+    h->na.clear();
+    h->na_err.clear();
+    size_t used = kNoAllocScratchBytes;  // forces a first batch
+    for (int i = 0; i < h->n; ++i) {
+        const MatDev& m = h->mh[i];
+        const size_t kk = align_up((size_t)m.k * m.k * sizeof(float), 256);
+        const size_t need = (m.m == m.n ? 1 : 2) * kk;
+        if (need > kNoAllocScratchBytes) {
+            char buf[256];
+            snprintf(buf, sizeof(buf),
+                     "matrix %d (%d x %d) needs %zu bytes of step intermediates, more than the %zu "
+                     "bytes of the allocation-free step's scratch (4 min(rows, cols)^2 bytes for a square matrix, twice that otherwise)",
+                     i, m.m, m.n, need, kNoAllocScratchBytes);
+            h->na_err = buf;
+            h->na.clear();
+            return SC_OK;
+        }
+        if (used + need > kNoAllocScratchBytes) {
+            h->na.emplace_back();
+            init_step_groups(h->na.back().g, h->gdt == SC_BF16);
+            used = 0;
+        }
+        float* T = (float*)(base + used);
+        float* Y = m.m == m.n ? nullptr : (float*)(base + used + kk);
+        add_step_probs(h->na.back().g, i, m, m.F, m.PL, m.PR, m.d, Y, T);
+        used += need;
+    }
+    for (auto& b : h->na)
+        for (int q = 0; q < 6; ++q)
+            if ((rc = upload_group(h, b.g[q]))) return rc;
     return SC_OK;
 }
 
@@ -1312,6 +1406,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             if ((rc = upload_group(h, *gg))) return rc;
     }
     if ((rc = build_step_groups(h, 0))) return rc;
+    if ((rc = build_noalloc_groups(h))) return rc;
     h->stale.assign(n, 0);
     const double gsz = h->gdt == SC_BF16 ? 2.0 : 4.0, wsz = h->wdt == SC_BF16 ? 2.0 : 4.0;
     for (int i = 0; i < n; ++i) h->total_numel += (double)h->mh[i].numel;
@@ -1386,6 +1481,11 @@ int check_idx(sc_opt* h, int idx) {
     if (idx < 0 || idx >= h->n) return fail(SC_ERR_INVALID_ARG, "matrix index %d out of range", idx);
     return SC_OK;
 }
+
+// Timing families of the six step GEMM groups.
+const int kStepKinds[6] = {PK_STEP_GEMM1, PK_STEP_GEMM1, PK_STEP_GEMM1,
+                           PK_STEP_GEMM2, PK_STEP_GEMM3, PK_STEP_GEMM3};
+int step_adamw(sc_opt* h, void* const* W, const void* const* G_mask, hipStream_t st);
 
 }  // namespace
 
@@ -1566,12 +1666,42 @@ int sc_step(sc_handle h, void* const* W, const void* const* G_mask, void* stream
         }
     }
     PtrTable gt = make_table(h, G_mask);
-    PtrTable wt = make_table(h, (const void* const*)W);
     const GemmGroup* sg = h->step[h->a_pending ? 1 : 0];
-    static const int kinds[6] = {PK_STEP_GEMM1, PK_STEP_GEMM1, PK_STEP_GEMM1,
-                                 PK_STEP_GEMM2, PK_STEP_GEMM3, PK_STEP_GEMM3};
     for (int q = 0; q < 6; ++q)
-        if ((rc = run_group(h, sg[q], kinds[q], gt, st))) return rc;
+        if ((rc = run_group(h, sg[q], kStepKinds[q], gt, st))) return rc;
+    return step_adamw(h, W, G_mask, st);
+}
+
+int sc_step_noalloc(sc_handle h, void* const* W, const void* const* G_mask, void* stream) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    if ((rc = check_ptrs(h, (const void* const*)W, h->wdt, "W"))) return rc;
+    if ((rc = check_ptrs(h, G_mask, h->gdt, "G_mask"))) return rc;
+    if (!h->na_err.empty()) return fail(SC_ERR_SHAPE, "%s", h->na_err.c_str());
+    if (h->a_pending)
+        return fail(SC_ERR_INVALID_ARG,
+                    "an asynchronous refresh is pending: complete it with sc_refresh_wait first");
+    if (h->prof.on)
+        return fail(SC_ERR_INVALID_ARG, "kernel timing is on: it creates events (sc_profile(h, 0))");
+    DeviceGuard g(h->device);
+    hipStream_t st = (hipStream_t)stream;
+    // a refresh or projector rebuild allocates nothing
+    if (h->any_stale && (rc = do_refresh(h, st))) return rc;
+    if (h->proj_stale && (rc = build_projectors(h, st))) return rc;
+    PtrTable gt = make_table(h, G_mask);
+    for (const auto& b : h->na)
+        for (int q = 0; q < 6; ++q)
+            if ((rc = run_group(h, b.g[q], kStepKinds[q], gt, st))) return rc;
+    return step_adamw(h, W, G_mask, st);
+}
+
+}  // extern "C"
+
+namespace {
+// The combination and AdamW of a step, after its GEMM chain has written G_filt.
+int step_adamw(sc_opt* h, void* const* W, const void* const* G_mask, hipStream_t st) {
+    PtrTable gt = make_table(h, G_mask);
+    PtrTable wt = make_table(h, (const void* const*)W);
     const int64_t t = h->t + 1;
     const double lr = h->hp.lr, b1 = h->hp.beta1, b2 = h->hp.beta2;
     const double bc1 = 1.0 - std::pow(b1, (double)t);
@@ -1592,6 +1722,9 @@ int sc_step(sc_handle h, void* const* W, const void* const* G_mask, void* stream
     h->t = t;
     return SC_OK;
 }
+}  // namespace
+
+extern "C" {
 
 int sc_set_lr(sc_handle h, float lr) {
     int rc;
