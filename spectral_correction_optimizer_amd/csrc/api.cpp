@@ -50,7 +50,7 @@ int fail(int code, const char* fmt, ...) {
     } while (0)
 
 constexpr int64_t kMaxDim = 65536;
-constexpr int kChunk = 16384;  // elements per elementwise workgroup
+constexpr int kChunk = 1024;  // elements per elementwise (EMA, AdamW) workgroup
 
 struct DeviceGuard {
     int prev = -1;
@@ -68,6 +68,7 @@ struct GemmGroup {
     GemmProb* d = nullptr;
     int total = 0;
     bool ta = false, tb = false, abf = false, bbf = false;
+    int parts = 3;  // 2: correction products (see launch_gemm)
 };
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -339,7 +340,8 @@ int run_group(sc_opt* h, const GemmGroup& g, int kind, const PtrTable& pt, hipSt
     if (g.h.empty()) return SC_OK;
     const bool vec = group_vec(g, pt);
     HIP_TRY(timed(h, kind, st, [&] {
-        return launch_gemm(g.d, (int)g.h.size(), g.total, g.ta, g.tb, g.abf, g.bbf, vec, pt, st);
+        return launch_gemm(g.d, (int)g.h.size(), g.total, g.ta, g.tb, g.abf, g.bbf, vec, g.parts,
+                           pt, st);
     }));
     if (h->prof.on) h->prof.flops[kind] += group_flops(g);
     return SC_OK;
@@ -1339,6 +1341,10 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
 
     // GEMM problem tables
     for (int g = 0; g < h->npipes; ++g) {
+        // E X of the Loewdin step: a correction of size |E| (<= the convergence
+        // threshold per entry) added to X, formed from two bfloat16 parts per operand
+        h->pipes[g].lowdin_F.parts = 2;
+        h->pipes[g].lowdin_W.parts = 2;
         h->pipes[g].lowdin_eW.tb = true;
         h->pipes[g].proj.ta = true;
         h->pipes[g].warm_nt.tb = true;

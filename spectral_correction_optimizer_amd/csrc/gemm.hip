@@ -68,7 +68,9 @@ struct TileLoader {
             for (int j = 0; j < 8; ++j) ks[j] = gld(kscale + min(kk + j, kdim - 1));
         }
     }
-    template <int NR>
+    // NP = 3: the exact three-way split; NP = 2: hi and mid parts only
+    // (|x - hi - mid| <= 2^-16 |x|), for products that are small corrections.
+    template <int NR, int NP>
     __device__ void store(__bf16 (*S)[NR * BK], int rows, int kdim, bool scaled) const {
         float f[8];
 #pragma unroll
@@ -77,11 +79,22 @@ struct TileLoader {
             if (KS && scaled) x *= ks[KS ? j : 0];
             f[j] = x;
         }
-        const Split8 s = split8(f);
         const int o = split_chunk16(row, half);
-        *(v8bf*)&S[0][o] = s.h;
-        *(v8bf*)&S[1][o] = s.m;
-        *(v8bf*)&S[2][o] = s.l;
+        if constexpr (NP == 3) {
+            const Split8 s = split8(f);
+            *(v8bf*)&S[0][o] = s.h;
+            *(v8bf*)&S[1][o] = s.m;
+            *(v8bf*)&S[2][o] = s.l;
+        } else {
+            v8bf h, m;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                h[j] = (__bf16)f[j];
+                m[j] = (__bf16)(f[j] - (float)h[j]);
+            }
+            *(v8bf*)&S[0][o] = h;
+            *(v8bf*)&S[1][o] = m;
+        }
     }
 };
 
@@ -97,11 +110,17 @@ struct TileLoader {
 // Heinecke ("Leveraging the bfloat16 artificial intelligence datatype for
 // higher-precision computations", 2019); the bfloat16 cores run it 2.7x faster
 // than float32 MFMA for the same float32-level result.
-template <bool TA, bool TB, bool VEC, typename TEA, typename TEB>
+// NP = 2 (two parts per operand, the products hi*hi, hi*mid, mid*hi) leaves out
+// at most about 3 * 2^-16 |a b| per term: used only for the Loewdin step's E X,
+// a correction added to X whose entries |E_ij| are at or below the convergence
+// threshold (~1e-6), so the error relative to X stays at or below float32
+// rounding.
+template <int NP, bool TA, bool TB, bool VEC, typename TEA, typename TEB>
 __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __restrict__ probs,
                                                               int nprob, PtrTable ptrs) {
-    __shared__ __align__(16) __bf16 As[2][3][BM * BK];
-    __shared__ __align__(16) __bf16 Bs[2][3][BN * BK];
+    static_assert(NP == 2 || NP == 3, "two or three bfloat16 parts per operand");
+    __shared__ __align__(16) __bf16 As[2][NP][BM * BK];
+    __shared__ __align__(16) __bf16 Bs[2][NP][BN * BK];
     static_assert(BM == 256 && BN == 128, "tile shape of the wave layout below");
 
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -130,9 +149,9 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
         lb.load(Bp, P.ldb, N, K, n0, k0, kscale);
     };
     auto store_tiles = [&](int buf) {
-        la0.template store<BM>(As[buf], M, K, false);
-        la1.template store<BM>(As[buf], M, K, false);
-        lb.template store<BN>(Bs[buf], N, K, kscale != nullptr);
+        la0.template store<BM, NP>(As[buf], M, K, false);
+        la1.template store<BM, NP>(As[buf], M, K, false);
+        lb.template store<BN, NP>(Bs[buf], N, K, kscale != nullptr);
     };
 
     // waves 2 x 2, each 128 (m) x 64 (n): 4 x 2 MFMA blocks of 32 x 32
@@ -162,9 +181,9 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
         if (kt + 1 < nk) load_tiles((kt + 1) * BK);
-        v8bf a[4][3], b[2][3];
+        v8bf a[4][NP], b[2][NP];
 #pragma unroll
-        for (int p = 0; p < 3; ++p) {
+        for (int p = 0; p < NP; ++p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) a[i][p] = *(const v8bf*)&As[buf][p][fa[i]];
 #pragma unroll
@@ -175,7 +194,11 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
     _Pragma("unroll") for (int i = 0; i < 4; ++i)                                               \
         _Pragma("unroll") for (int j = 0; j < 2; ++j)                                           \
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][PA], b[j][PB], acc[i][j], 0, 0, 0);
-        SC_TERM(2, 0) SC_TERM(1, 1) SC_TERM(0, 2) SC_TERM(1, 0) SC_TERM(0, 1) SC_TERM(0, 0)
+        if constexpr (NP == 3) {
+            SC_TERM(2, 0) SC_TERM(1, 1) SC_TERM(0, 2) SC_TERM(1, 0) SC_TERM(0, 1) SC_TERM(0, 0)
+        } else {
+            SC_TERM(1, 0) SC_TERM(0, 1) SC_TERM(0, 0)
+        }
 #undef SC_TERM
         if (kt + 1 < nk) store_tiles(buf ^ 1);
         __syncthreads();
@@ -207,17 +230,21 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
 }
 
 hipError_t launch_gemm(const GemmProb* probs_dev, int nprob, int total_tiles, bool ta, bool tb,
-                       bool a_bf16, bool b_bf16, bool vec, const PtrTable& ptrs, hipStream_t st) {
+                       bool a_bf16, bool b_bf16, bool vec, int parts, const PtrTable& ptrs,
+                       hipStream_t st) {
     if (nprob <= 0 || total_tiles <= 0) return hipSuccess;
     dim3 grid(total_tiles), blk(256);
     if (ta) vec = false;  // a k-major A has no row loads to vectorize
-#define SC_GEMM_CASE(TA_, TB_, V_, EA, EB)                                                      \
-    if (ta == TA_ && tb == TB_ && vec == V_ && a_bf16 == (sizeof(EA) == 2) &&                  \
+#define SC_GEMM_CASE_NP(NP_, TA_, TB_, V_, EA, EB)                                              \
+    if (parts == NP_ && ta == TA_ && tb == TB_ && vec == V_ && a_bf16 == (sizeof(EA) == 2) &&  \
         b_bf16 == (sizeof(EB) == 2)) {                                                          \
-        hipLaunchKernelGGL((gemm_grouped_kernel<TA_, TB_, V_, EA, EB>), grid, blk, 0, st,       \
+        hipLaunchKernelGGL((gemm_grouped_kernel<NP_, TA_, TB_, V_, EA, EB>), grid, blk, 0, st,  \
                            probs_dev, nprob, ptrs);                                             \
         return hipGetLastError();                                                               \
     }
+#define SC_GEMM_CASE(TA_, TB_, V_, EA, EB) SC_GEMM_CASE_NP(3, TA_, TB_, V_, EA, EB)
+    SC_GEMM_CASE_NP(2, false, false, true, float, float)
+    SC_GEMM_CASE_NP(2, false, false, false, float, float)
     SC_GEMM_CASE(false, false, true, float, float)
     SC_GEMM_CASE(false, false, false, float, float)
     SC_GEMM_CASE(false, false, true, uint16_t, float)
@@ -230,6 +257,7 @@ hipError_t launch_gemm(const GemmProb* probs_dev, int nprob, int total_tiles, bo
     SC_GEMM_CASE(false, true, false, uint16_t, float)
     SC_GEMM_CASE(true, false, false, float, float)
 #undef SC_GEMM_CASE
+#undef SC_GEMM_CASE_NP
     return hipErrorInvalidValue;
 }
 
