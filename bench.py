@@ -69,6 +69,8 @@ def parse():
                     help="wavefronts per Jacobi pair solve (0: by each launch's pair count)")
     ap.add_argument("--solve-copies", type=int, default=0, choices=[0, 1, 2],
                     help="LDS copies of the pair Gram in the multi-wave solve (0: by pair count)")
+    ap.add_argument("--v-rounds", type=int, default=2, choices=[1, 2],
+                    help="rounds of V-row rotations per pass over V in the fused sweeps")
     ap.add_argument("--no-fused-gram", action="store_true",
                     help="every Jacobi round's pair Gram from the operand (no fused apply + Gram)")
     ap.add_argument("--cold-start", action="store_true",
@@ -416,6 +418,7 @@ def main():
                             warm_start=0 if args.cold_start else 1, **hp)
     opt.set_solve_waves(args.solve_waves, args.solve_copies)
     opt.set_fused_gram(not args.no_fused_gram)
+    opt.set_v_rounds(args.v_rounds)
     for i, mi in enumerate(src):
         opt.set_state(i, "m_anc", mi.m0())
 
@@ -565,6 +568,7 @@ def main():
                    "lr": hp["lr"]},
         "solve_variant": {"waves": args.solve_waves or "auto", "copies": args.solve_copies or "auto"},
         "fused_gram": not args.no_fused_gram,
+        "v_rounds": args.v_rounds,
         "warm_start": not args.cold_start,
         "drift": args.drift,
         "refresh_ms": round(r_med, 2),

@@ -234,6 +234,16 @@ int sc_set_solve_waves(sc_handle h, int waves, int copies);
  * pending asynchronous refresh. */
 int sc_set_fused_gram(sc_handle h, int enable);
 
+/* Rotations of the V rows (the right factor accumulated in the Jacobi sweeps)
+ * in the fused sweeps: rounds = 2 (default) applies each pair of consecutive
+ * rounds of a sweep in one pass over V (V does not feed the sweeps, so a
+ * round's V update can wait for the next round's), rounds = 1 one pass per
+ * round.  Same products in the same order: V is bit-identical either way.
+ * Other values: SC_ERR_INVALID_ARG.  Waits for a pending asynchronous refresh.
+ * A schedule of the thin SVD of the anchor momentum ("Key design 3" of the
+ * papernotes.org notes); it changes no result. */
+int sc_set_v_rounds(sc_handle h, int rounds);
+
 /* Keep G_proj of each step (costs one more store per element in the AdamW
  * pass and rows x cols floats per matrix). */
 int sc_keep_proj(sc_handle h, int enable);

@@ -171,6 +171,13 @@ struct sc_opt {
         int nai_f = 0;
         FusedItem* fi = nullptr;
         int nfi = 0;
+        // with the fused apply: the V rows of the matrices in fi, two rounds per pass
+        // (jac_apply_v2_kernel; columns of V in x0 / x1), and their block counts
+        FusedItem* vi = nullptr;
+        int nvi = 0;
+        std::vector<int> vnbs;
+        ApplyItem* av = nullptr;  // the same V rows one round per pass (sc_set_v_rounds 1)
+        int nav = 0;
         bool all_fused = false;  // every matrix of the list has the fused apply + Gram
         int* mats = nullptr;
         int nmat = 0;
@@ -237,6 +244,7 @@ struct sc_opt {
     bool proj_stale = false;
     bool keep_proj = false;
     bool fuse = true;                         // fused apply + next Gram where a matrix allows it
+    int v_rounds = 2;                         // fused matrices' V rows: rounds per pass (1 or 2)
     std::vector<std::array<char, 2>> fused;   // per matrix: fused over the factor / full rows
     int solve_waves = 0, solve_copies = 0;  // pair solve variant: 0 by the launch's pair count
     std::vector<void*> dev_allocs;
@@ -503,8 +511,11 @@ void account_sweeps(sc_opt* h, const MatFlags* flags) {
                 h->prof.bytes[PK_APPLY_GRAM] += rounds_full[ph] * (m.nb / 2) * 4.0 * pw * len[ph] +
                                                 pairs_full[ph] * (4.0 * pw * len[ph] + 4.0 * pw * pw);
                 if (vlen[ph] > 0.0) {
+                    // V rows of a rotated pair read and written once per round, or
+                    // once per two rounds (jac_apply_v2_kernel), plus R
+                    const double vpass = h->v_rounds == 2 ? 4.0 : 8.0;
                     h->prof.flops[PK_APPLY] += pairs_full[ph] * 2.0 * pw * pw * vlen[ph];
-                    h->prof.bytes[PK_APPLY] += pairs_full[ph] * (8.0 * pw * vlen[ph] + 4.0 * pw * pw);
+                    h->prof.bytes[PK_APPLY] += pairs_full[ph] * (vpass * pw * vlen[ph] + 4.0 * pw * pw);
                 }
             } else {
                 h->prof.flops[PK_GRAM] += rounds_full[ph] * (m.nb / 2) * 2.0 * pw * pw * len[ph];
@@ -599,6 +610,17 @@ int pipe_round(sc_opt* h, Pipe& p, hipStream_t st) {
         if (L.nai_f)
             HIP_TRY(timed(h, PK_APPLY, st, [&] {
                 return launch_jacobi_apply(h->md, h->flags_d, L.ai_f, L.nai_f, r, st);
+            }));
+        // V rows two rounds at a time: a sweep's odd rounds and its last round
+        bool vround = false;
+        for (int nb : L.vnbs) vround = vround || (r % (nb - 1)) % 2 == 1 || r % (nb - 1) == nb - 2;
+        if (h->v_rounds == 2 && L.nvi && vround)
+            HIP_TRY(timed(h, PK_APPLY, st, [&] {
+                return launch_jacobi_apply_v2(h->md, h->flags_d, L.vi, L.nvi, r, st);
+            }));
+        if (h->v_rounds == 1 && L.nav)
+            HIP_TRY(timed(h, PK_APPLY, st, [&] {
+                return launch_jacobi_apply(h->md, h->flags_d, L.av, L.nav, r, st);
             }));
         HIP_TRY(timed(h, PK_APPLY_GRAM, st, [&] {
             return launch_jacobi_apply_gram(h->md, h->flags_d, L.fi, L.nfi, r, st);
@@ -1112,8 +1134,9 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         o[i].E = take(kk);
         o[i].invn = take((size_t)m.kpad * f);
         o[i].gram = take((size_t)(m.nb / 2) * m.nsplit * kPw * kPw * sizeof(double));
-        o[i].rot = take((size_t)(m.nb / 2) * kPw * kPw * f);
-        o[i].rflag = take((size_t)(m.nb / 2) * sizeof(int));
+        // two buffers (round parity): V rows take two rounds' rotations per pass
+        o[i].rot = take((size_t)2 * (m.nb / 2) * kPw * kPw * f);
+        o[i].rflag = take((size_t)2 * (m.nb / 2) * sizeof(int));
         o[i].perm = take((size_t)m.kpad * sizeof(int));
         o[i].cnorm = take((size_t)m.kpad * sizeof(float));
         o[i].chol = take((size_t)m.k * m.k * sizeof(double));
@@ -1241,9 +1264,9 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         for (int which = 0; which < 3; ++which) {
             std::vector<GramItem> gi;
             std::vector<SolveItem> si;
-            std::vector<ApplyItem> ai, ai_f;
+            std::vector<ApplyItem> ai, ai_f, av;
             bool any_unfused = false;
-            std::vector<FusedItem> fi;
+            std::vector<FusedItem> fi, vi;
             std::vector<int> mats;
             auto& L = P.L[which];
             int pairs = 0;
@@ -1270,10 +1293,18 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
                 }
                 h->fused[i][which == LIST_FACTOR && m.klen ? 0 : 1] = fuse;
                 any_unfused = any_unfused || !fuse;
+                const bool vrows = !(which == LIST_FACTOR && m.klen);  // V moves outside the factor phase
                 if (fuse)
-                    for (int grp = 0; grp < m.nb / 4; ++grp)
+                    for (int grp = 0; grp < m.nb / 4; ++grp) {
                         for (int sp = 0; sp < ns; ++sp)
                             fi.push_back(FusedItem{i, grp, sp, sp * sl, std::min(len, (sp + 1) * sl)});
+                        if (vrows)
+                            for (int x0 = 0; x0 < m.kpad; x0 += kV2Run * kV2Cols)
+                                vi.push_back(FusedItem{i, grp, 0, x0, std::min(m.kpad, x0 + kV2Run * kV2Cols)});
+                    }
+                if (fuse && vrows &&
+                    std::find(L.vnbs.begin(), L.vnbs.end(), m.nb) == L.vnbs.end())
+                    L.vnbs.push_back(m.nb);
                 mats.push_back(i);
                 L.max_nb = std::max(L.max_nb, m.nb);
                 if (std::find(L.nbs.begin(), L.nbs.end(), m.nb) == L.nbs.end()) L.nbs.push_back(m.nb);
@@ -1287,11 +1318,11 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
                         ai.push_back(ApplyItem{i, s, 0, c, std::min(kApplyRun, nca - c)});
                         if (!fuse) ai_f.push_back(ai.back());
                     }
-                    if (which == LIST_FACTOR && m.klen) continue;  // no V in the factor phase
+                    if (!vrows) continue;  // no V in the factor phase
                     const int ncv = (m.kpad + kApplyCols - 1) / kApplyCols;
                     for (int c = 0; c < ncv; c += kApplyRun) {
                         ai.push_back(ApplyItem{i, s, 1, c, std::min(kApplyRun, ncv - c)});
-                        ai_f.push_back(ai.back());
+                        (fuse ? av : ai_f).push_back(ai.back());
                     }
                 }
             }
@@ -1300,6 +1331,8 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             if ((rc = upload(ai, &L.ai, &L.nai))) return rc;
             if ((rc = upload(ai_f, &L.ai_f, &L.nai_f))) return rc;
             if ((rc = upload(fi, &L.fi, &L.nfi))) return rc;
+            if ((rc = upload(vi, &L.vi, &L.nvi))) return rc;
+            if ((rc = upload(av, &L.av, &L.nav))) return rc;
             L.all_fused = !mats.empty() && !any_unfused;
             if ((rc = upload(mats, &L.mats, &L.nmat))) return rc;
         }
@@ -1872,6 +1905,16 @@ int sc_set_fused_gram(sc_handle h, int enable) {
     DeviceGuard g(h->device);
     if ((rc = finish_async(h, nullptr, true))) return rc;
     h->fuse = enable != 0;
+    return SC_OK;
+}
+
+int sc_set_v_rounds(sc_handle h, int rounds) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    if (rounds != 1 && rounds != 2) return fail(SC_ERR_INVALID_ARG, "rounds must be 1 or 2");
+    DeviceGuard g(h->device);
+    if ((rc = finish_async(h, nullptr, true))) return rc;
+    h->v_rounds = rounds;
     return SC_OK;
 }
 

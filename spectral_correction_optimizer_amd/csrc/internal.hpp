@@ -13,6 +13,9 @@ constexpr int kPw = 2 * kJb;   // pair width
 constexpr int kApplyCols = 128;            // columns per rotation-apply workgroup
 constexpr int kApplyThreads = 2 * kApplyCols;  // a 64-lane wave updates 32 columns
 constexpr int kApplyRun = 4;  // column chunks per rotation-apply workgroup (pipelined)
+constexpr int kV2Cols = 256;  // V columns per chunk of the two-round V apply (8 waves x 32)
+constexpr int kV2Threads = 8 * 64;
+constexpr int kV2Run = 4;     // chunks per two-round V apply workgroup
 
 // Caller pointers of one call (weights / gradients), passed by value.
 struct PtrTable {
@@ -49,8 +52,8 @@ struct MatDev {
     float* E;        // [k][k] refresh scratch (Gram of factors, scaled copies)
     float* invn;     // [kpad] refresh scratch: inverse row norms of the factor-phase X
     double* gram;    // [nb/2][nsplit][2b][2b] split partial Gram blocks
-    float* rot;      // [nb/2][2b][2b] R = Q - I of each pair
-    int* rot_flag;   // [nb/2] 1 when the pair's rotation must be applied
+    float* rot;      // [2][nb/2][2b][2b] R = Q - I of each pair, by round parity
+    int* rot_flag;   // [2][nb/2] 1 when the pair's rotation must be applied
     int nsplit;      // K-splits of a pair Gram (room in `gram`; a phase may use fewer)
     int klen;        // row length of the Cholesky-factor operand: k rounded up to 128 (0: none)
     float tol;       // a pair is rotated when |a_p.a_q| / (|a_p| |a_q|) > tol
@@ -178,6 +181,12 @@ hipError_t launch_jacobi_apply_gram(const MatDev* mats, const MatFlags* flags, c
                                    int nfi, int round, hipStream_t st);
 hipError_t launch_jacobi_apply(const MatDev* mats, const MatFlags* flags, const ApplyItem* ai,
                                int nai, int round, hipStream_t st);
+// V rows of power-of-two block counts: in a sweep's odd rounds the rotations of
+// that round and the one before in one pass, in its last round that round's;
+// other rounds return at once.  Items: FusedItem with x0 / x1 columns of V (runs
+// of kV2Run chunks of kV2Cols), group < nb / 4.
+hipError_t launch_jacobi_apply_v2(const MatDev* mats, const MatFlags* flags, const FusedItem* vi,
+                                  int nvi, int round, hipStream_t st);
 // At a matrix's sweep start: order its columns by decreasing norm (perm).
 hipError_t launch_jacobi_sort(const MatDev* mats, const MatFlags* flags, const int* mat_idx,
                               int nmat, int round, hipStream_t st);

@@ -40,6 +40,16 @@ __device__ __forceinline__ int pair_row(const MatDev& md, int blkI, int blkJ, in
     return gld(md.perm + (rho < kJb ? blkI * kJb + rho : blkJ * kJb + (rho - kJb)));
 }
 
+// R = Q - I and the rotate flag of each pair slot, in two buffers by the parity
+// of the round, so that a round's rotations stay readable through the next round
+// (the V rows take two rounds' rotations in one pass: jac_apply_v2_kernel).
+__device__ __forceinline__ float* rot_of(const MatDev& md, int round, int slot) {
+    return md.rot + ((int64_t)(round & 1) * (md.nb / 2) + slot) * (PW * PW);
+}
+__device__ __forceinline__ int* rflag_of(const MatDev& md, int round, int slot) {
+    return md.rot_flag + (round & 1) * (md.nb / 2) + slot;
+}
+
 // Selective polishing (sel set after a failed certificate): only pairs with a
 // block above the convergence threshold in the certificate's normalized Gram
 // (the cross block or either diagonal block, from bmax) are worked on; the
@@ -319,7 +329,7 @@ __global__ __launch_bounds__(64) void jac_solve_kernel(const MatDev* __restrict_
     int bI, bJ;
     block_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
     if (!pair_selected(md, fl, bI, bJ)) {
-        if (l == 0) md.rot_flag[it.slot] = 0;
+        if (l == 0) *rflag_of(md, round, it.slot) = 0;
         return;
     }
     if (fl.sel && l == 0) atomicAdd(&fl.sel_pairs, 1);
@@ -366,7 +376,7 @@ __global__ __launch_bounds__(64) void jac_solve_kernel(const MatDev* __restrict_
     }
     for (int o = 32; o > 0; o >>= 1) mo = fmaxf(mo, __shfl_xor(mo, o));
     if (l == 0) atomicMax(&fl.sweep_max, __float_as_uint(mo));
-    int* rflag = md.rot_flag + it.slot;
+    int* rflag = rflag_of(md, round, it.slot);
     if (!(mo > tol)) {
         // columns unchanged: their norms for the next sweep's ordering
         gst(md.cnorm + pair_row(md, bI, bJ, l), (float)dl);
@@ -496,7 +506,7 @@ __global__ __launch_bounds__(64) void jac_solve_kernel(const MatDev* __restrict_
     __syncthreads();
     // 4. R row-major [b][a] (X_new[a] = X[a] + sum_b R[b][a] X[b]); the frame is the
     //    original one again, so R[b][a] = R^T[a][b]
-    float* Rg = md.rot + (int64_t)it.slot * PW * PW;
+    float* Rg = rot_of(md, round, it.slot);
 #pragma unroll 4
     for (int b0 = 0; b0 < PW; b0 += 4) {
         const v4f v = *(const v4f*)&RT[l * SR + b0];
@@ -554,7 +564,7 @@ __global__ __launch_bounds__(64 * NW) void jac_solve_waves_kernel(const MatDev* 
     int bI, bJ;
     block_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
     if (!pair_selected(md, fl, bI, bJ)) {
-        if (threadIdx.x == 0) md.rot_flag[it.slot] = 0;
+        if (threadIdx.x == 0) *rflag_of(md, round, it.slot) = 0;
         return;
     }
     if (fl.sel && threadIdx.x == 0) atomicAdd(&fl.sel_pairs, 1);
@@ -606,7 +616,7 @@ __global__ __launch_bounds__(64 * NW) void jac_solve_waves_kernel(const MatDev* 
 #pragma unroll
     for (int i = 1; i < NW; ++i) mo = fmaxf(mo, mos[i]);
     if (threadIdx.x == 0) atomicMax(&fl.sweep_max, __float_as_uint(mo));
-    int* rflag = md.rot_flag + it.slot;
+    int* rflag = rflag_of(md, round, it.slot);
     if (!(mo > tol)) {
         if (w == 0) {
             gst(md.cnorm + pair_row(md, bI, bJ, l), (float)dl);
@@ -723,7 +733,7 @@ __global__ __launch_bounds__(64 * NW) void jac_solve_waves_kernel(const MatDev* 
     }
     // 4. R and the rotated column norms from the copy the last step wrote
     const float* Rf = RT[cur];
-    float* Rg = md.rot + (int64_t)it.slot * PW * PW;
+    float* Rg = rot_of(md, round, it.slot);
 #pragma unroll 4
     for (int b0 = cb; b0 < cb + CW; b0 += 4) {
         const v4f v = *(const v4f*)&Rf[l * SR + b0];
@@ -779,7 +789,7 @@ __global__ __launch_bounds__(kApplyThreads) void jac_apply_kernel(const MatDev* 
     const ApplyItem it = items[blockIdx.x];
     if (flags[it.mat].done) return;
     const MatDev& md = mats[it.mat];
-    if (md.rot_flag[it.slot] == 0) return;
+    if (*rflag_of(md, round, it.slot) == 0) return;
     int bI, bJ;
     block_pair(md.nb, round % (md.nb - 1), it.slot, &bI, &bJ);
     float* base = it.which == 0 ? md.A : md.V;
@@ -831,7 +841,7 @@ __global__ __launch_bounds__(kApplyThreads) void jac_apply_kernel(const MatDev* 
     };
     float xa[PW / 2], xb[PW / 2];
     load(xa, 0);
-    const float* R = md.rot + (int64_t)it.slot * PW * PW;
+    const float* R = rot_of(md, round, it.slot);
     // operand A of tile tl, k-step t for lane l: R^T[32 tl + l % 32][b] = R[b][32 tl + l % 32]
     // at the 8 rows b = apply_row(8 t + e, l / 32)
     for (int idx = threadIdx.x; idx < 2 * 4 * 64; idx += kApplyThreads) {
@@ -924,7 +934,7 @@ __global__ __launch_bounds__(512) void jac_apply_gram_kernel(const MatDev* __res
         block_pair(nb, rr, slotA, &a0, &a1);
         block_pair(nb, rr, slotB, &b0, &b1);
     }
-    const bool rotA = md.rot_flag[slotA] != 0, rotB = md.rot_flag[slotB] != 0;
+    const bool rotA = *rflag_of(md, round, slotA) != 0, rotB = *rflag_of(md, round, slotB) != 0;
     if (!gram && !rotA && !rotB) return;
     const int ld = md.K_ld;
     const __amdgpu_buffer_rsrc_t buf = buf_rsrc(md.A, (uint32_t)md.kpad * ld * 4u);
@@ -1019,7 +1029,7 @@ __global__ __launch_bounds__(512) void jac_apply_gram_kernel(const MatDev* __res
     // at the 8 rows b = apply_row(8 t + e, l / 32) of the lane's half of the k-step
     for (int idx = threadIdx.x; idx < 2 * 2 * 4 * 64; idx += 512) {
         const int pq = idx >> 9, tl = (idx >> 8) & 1, t = (idx >> 6) & 3, l = idx & 63;
-        const float* R = md.rot + (int64_t)(pq == 0 ? slotA : slotB) * PW * PW;
+        const float* R = rot_of(md, round, pq == 0 ? slotA : slotB);
         float f[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) f[e] = gld(R + apply_row(8 * t + e, l >> 5) * PW + 32 * tl + (l & 31));
@@ -1068,6 +1078,157 @@ __global__ __launch_bounds__(512) void jac_apply_gram_kernel(const MatDev* __res
     }
 }
 
+
+// ---------------------------------------------------------------------------------
+// V rows: the rotations of two consecutive rounds in one pass.  V does not feed the
+// sweeps (every round's rotations come from A's Gram), so the update of V for round
+// r (even within the sweep) waits and is applied together with round r + 1's.  For
+// r even, m = nb - 1 - r is odd, and the group {p, p^m, p^1, p^m^1} (p with zeros
+// at bit 0 and at the top bit h of m) holds two pairs of each round:
+//   round r:      (p, p^m), (p^1, p^m^1)
+//   round r + 1:  (p, p^m^1), (p^1, p^m)          (m' = m - 1 = m ^ 1)
+// With the blocks in register slots 0 = p, 1 = p^m, 2 = p^1, 3 = p^m^1 the pairs are
+// (0, 1), (2, 3) and then (0, 3), (2, 1) for every group and round.  A wave keeps 32
+// columns of the group's 128 rows in registers (16 rows of each block per lane, in
+// the row order of jac_apply_kernel) through both rounds' products and moves them
+// once; the next chunk's loads are in flight meanwhile.  In the last round of a
+// sweep (r = nb - 2) it applies that round's two pairs of group g, slots 2g, 2g + 1.
+// Each product is formed exactly as in jac_apply_kernel (same split, same part
+// products in the same order, float32 sums) and the rows between the two rounds
+// are the same float32 values: V is bitwise the same as with one pass per round.
+__global__ __launch_bounds__(kV2Threads) void jac_apply_v2_kernel(const MatDev* __restrict__ mats,
+                                                                const MatFlags* __restrict__ flags,
+                                                                const FusedItem* __restrict__ items,
+                                                                int round) {
+    // the four rotations as bfloat16 planes in MFMA operand order:
+    // [pair][plane][32-row output tile][16-row k-step][lane]
+    __shared__ v8bf Rp[4][3][2][4][64];
+    const FusedItem it = items[blockIdx.x];
+    if (flags[it.mat].done) return;
+    const MatDev& md = mats[it.mat];
+    const int nb = md.nb, rr = round % (nb - 1);
+    const bool two = (rr & 1) != 0;  // rounds r = rr - 1 and rr
+    if (!two && rr < nb - 2) return;  // this round's V update waits for the next round
+    int blk[4], slot[4], rnd[4];      // pairs 0, 1: first round; 2, 3: second round
+    if (two) {
+        const int m = nb - rr, h = 31 - __builtin_clz(m);
+        const int p = insert_zero_bit(insert_zero_bit(it.group, 0), h);
+        blk[0] = p;
+        blk[1] = p ^ m;
+        blk[2] = p ^ 1;
+        blk[3] = p ^ m ^ 1;
+        slot[0] = remove_bit(blk[0], h);
+        slot[1] = remove_bit(blk[2], h);
+        slot[2] = remove_bit(blk[0], h);  // (p, p^m^1): the top bit of m - 1 is h
+        slot[3] = remove_bit(blk[2], h);  // (p^1, p^m)
+        rnd[0] = rnd[1] = round - 1;
+        rnd[2] = rnd[3] = round;
+    } else {
+        slot[0] = 2 * it.group;
+        slot[1] = slot[0] + 1;
+        block_pair(nb, rr, slot[0], &blk[0], &blk[1]);
+        block_pair(nb, rr, slot[1], &blk[2], &blk[3]);
+        slot[2] = slot[3] = 0;
+        rnd[0] = rnd[1] = rnd[2] = rnd[3] = round;
+    }
+    bool rot[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) rot[q] = (q < 2 || two) && *rflag_of(md, rnd[q], slot[q]) != 0;
+    // a block is moved when a rotated pair holds it
+    const bool need[4] = {rot[0] || rot[2], rot[0] || rot[3], rot[1] || rot[3], rot[1] || rot[2]};
+    if (!(need[0] || need[1] || need[2] || need[3])) return;
+    const int ld = md.kpad;  // multiple of 64
+    const __amdgpu_buffer_rsrc_t buf = buf_rsrc(md.V, (uint32_t)md.kpad * ld * 4u);
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hl = lane >> 5, ll = lane & 31;
+    // lane's rows: 16 of each block (apply_row(e, hl), e < 16, of the block's 32),
+    // two physical row numbers (< 2^16) per register; byte offset row * 4 ld + 4 ll
+    unsigned int rows2[4][8];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            rows2[b][e] = (unsigned int)gld(md.perm + blk[b] * kJb + apply_row(2 * e, hl)) |
+                          ((unsigned int)gld(md.perm + blk[b] * kJb + apply_row(2 * e + 1, hl)) << 16);
+    const unsigned int ld4 = 4u * ld, ll4 = 4u * ll;
+    auto voff = [&](int b, int e) {
+        const unsigned int r = (e & 1) ? rows2[b][e >> 1] >> 16 : rows2[b][e >> 1] & 0xffffu;
+        return (int)(__umul24(r, ld4) + ll4);
+    };
+    auto col0 = [&](int c) { return it.x0 + c * kV2Cols + wave * 32; };
+    auto load = [&](float (&x)[4][16], int c) {
+        if (col0(c) >= ld) return;
+        const int so = col0(c) * 4;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            if (need[b])
+#pragma unroll
+                for (int e = 0; e < 16; ++e) x[b][e] = buf_load_f32<kBufNT>(buf, voff(b, e), so);
+    };
+    // X <- X + R^T X for the pair (U, W) of register slots, rotation q
+    auto apply = [&](float (&x)[4][16], int q, int U, int W) {
+        v16f acc0, acc1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            acc0[r] = 0.0f;
+            acc1[r] = 0.0f;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = t < 2 ? x[U][8 * t + e] : x[W][8 * (t - 2) + e];
+            const Split8 xs = split8(f);
+            const Split8 r0{Rp[q][0][0][t][lane], Rp[q][1][0][t][lane], Rp[q][2][0][t][lane]};
+            const Split8 r1{Rp[q][0][1][t][lane], Rp[q][1][1][t][lane], Rp[q][2][1][t][lane]};
+            acc0 = mfma_split6(r0, xs, acc0);
+            acc1 = mfma_split6(r1, xs, acc1);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            x[U][r] += acc0[r];
+            x[W][r] += acc1[r];
+        }
+    };
+    auto update = [&](float (&x)[4][16], int c) {
+        if (col0(c) >= ld) return;
+        if (rot[0]) apply(x, 0, 0, 1);
+        if (rot[1]) apply(x, 1, 2, 3);
+        if (rot[2]) apply(x, 2, 0, 3);
+        if (rot[3]) apply(x, 3, 2, 1);
+        const int so = col0(c) * 4;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+            if (need[b])
+#pragma unroll
+                for (int e = 0; e < 16; ++e) buf_store_f32<kBufNT>(x[b][e], buf, voff(b, e), so);
+    };
+    float xa[4][16], xb[4][16];
+    load(xa, 0);
+    // operand A of tile tl, k-step t for lane l: R^T[32 tl + l % 32][b] = R[b][32 tl + l % 32]
+    // at the 8 rows b = apply_row(8 t + e, l / 32) (as jac_apply_kernel)
+    for (int idx = threadIdx.x; idx < 4 * 2 * 4 * 64; idx += kV2Threads) {
+        const int q = idx >> 9, tl = (idx >> 8) & 1, t = (idx >> 6) & 3, l = idx & 63;
+        if (!rot[q]) continue;
+        const float* R = rot_of(md, rnd[q], slot[q]);
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = gld(R + apply_row(8 * t + e, l >> 5) * PW + 32 * tl + (l & 31));
+        const Split8 sp = split8(f);
+        Rp[q][0][tl][t][l] = sp.h;
+        Rp[q][1][tl][t][l] = sp.m;
+        Rp[q][2][tl][t][l] = sp.l;
+    }
+    __syncthreads();
+    const int n = (it.x1 - it.x0 + kV2Cols - 1) / kV2Cols;
+    for (int c = 0; c < n; c += 2) {
+        if (c + 1 < n) load(xb, c + 1);
+        update(xa, c);
+        if (c + 1 >= n) break;
+        if (c + 2 < n) load(xa, c + 2);
+        update(xb, c + 1);
+    }
+}
 
 // ---------------------------------------------------------------------------------
 // Sweep-start ordering (de Rijk): at the first round of each of a matrix's
@@ -1196,6 +1357,14 @@ hipError_t launch_jacobi_apply_gram(const MatDev* mats, const MatFlags* flags, c
                                    int nfi, int round, hipStream_t st) {
     if (nfi == 0) return hipSuccess;
     hipLaunchKernelGGL(jac_apply_gram_kernel, dim3(nfi), dim3(512), 0, st, mats, flags, fi, round);
+    return hipGetLastError();
+}
+
+hipError_t launch_jacobi_apply_v2(const MatDev* mats, const MatFlags* flags, const FusedItem* vi,
+                                  int nvi, int round, hipStream_t st) {
+    if (nvi <= 0) return hipSuccess;
+    hipLaunchKernelGGL(jac_apply_v2_kernel, dim3(nvi), dim3(kV2Threads), 0, st, mats, flags, vi,
+                       round);
     return hipGetLastError();
 }
 

@@ -428,6 +428,56 @@ def test_solve_wave_variants_bitwise():
             assert np.array_equal(x, y)
 
 
+def test_v_rounds_bitwise():
+    """The V rows of the fused sweeps updated two rounds per pass (default) and one
+    round per pass give bit-identical factors, sweep counts and weights: a cold
+    and a warm refresh (Cholesky factor phase and polishing on the tall operands),
+    power-of-two block counts from 4 to 16 in one list, a 128-column V (a partial
+    256-column chunk), and a block count that is not a power of two (per-round
+    path beside the fused ones).  Invalid values are rejected."""
+    import spectral_correction_optimizer_amd as sco
+    say("case: V rows 1 vs 2 rounds per pass, 256x256 + 512x128 + 128x1024 + 1024x512 + 512x512 + 320x640")
+    dev = torch.device("cuda")
+    shapes = [(256, 256), (512, 128), (128, 1024), (1024, 512), (512, 512), (320, 640)]
+    ins = [gen.MatrixInputs(171, 0, i, *sh) for i, sh in enumerate(shapes)]
+    GA = [[to_dev(gen.stored(mi.g_anc(k), "f32")[0], "f32", dev) for mi in ins] for k in range(2)]
+    G = [to_dev(gen.stored(mi.g_mask(0), "f32")[0], "f32", dev) for mi in ins]
+
+    def run(rounds):
+        opt = sco.SpectralAdamW(shapes, device=dev)
+        opt.set_v_rounds(rounds)
+        for i, mi in enumerate(ins):
+            opt.set_state(i, "m_anc", to_dev(gen.stored(mi.m0(), "f32")[0], "f32", dev))
+        W = [to_dev(gen.stored(mi.w0(), "f32")[0], "f32", dev) for mi in ins]
+        sweeps = []
+        for k in range(2):
+            opt.anchor_update(GA[k])
+            st = opt.stats()
+            sweeps.append((st["sweeps"], st["factor_sweeps"]))
+        opt.step(W, G)
+        torch.cuda.synchronize()
+        fac = [[t.cpu().numpy().copy() for t in opt.get_factors(i)] for i in range(len(shapes))]
+        out = [w.cpu().numpy().copy() for w in W]
+        st = opt.stats()
+        if rounds == 2:
+            for bad in (0, 3, -1):
+                with pytest.raises(sco.ScoptError):
+                    opt.set_v_rounds(bad)
+        opt.close()
+        return fac, out, sweeps, st
+
+    ref_f, ref_w, ref_sw, ref_s = run(1)
+    f, w, sw, st = run(2)
+    say(f"  sweeps (total, factor) per refresh: {sw} (one round per pass: {ref_sw})")
+    assert ref_s["not_converged"] == 0 and st["not_converged"] == 0
+    assert sw == ref_sw
+    for a, b in zip(f, ref_f):
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+    for x, y in zip(w, ref_w):
+        assert np.array_equal(x, y)
+
+
 def test_fused_gram_matches_unfused():
     """The fused rotation apply + next-round Gram (bfloat16 three-way split) and
     the standalone float32 Gram give the same SVD to float32 accuracy: singular
