@@ -244,6 +244,22 @@ int sc_set_fused_gram(sc_handle h, int enable);
  * papernotes.org notes); it changes no result. */
 int sc_set_v_rounds(sc_handle h, int rounds);
 
+/* Sweep-stop rule of the Jacobi sweeps (default 1e-4): a matrix's sweeps also
+ * end after a sweep whose largest relative off-diagonal |a_p.a_q| / (|a_p||a_q|)
+ * was at most `stop` (convergence is quadratic by then, so the next sweep would
+ * rotate almost nothing), and a certificate over the final operand's Gram checks
+ * the result: after the Cholesky factor phase the one of A = M V (pairs above
+ * the convergence threshold are polished), after plain sweeps the final Gram's
+ * (a matrix above the threshold sweeps on; applied only with sync_check, whose
+ * polls read the outcome).  In the factor phase the value is capped at 1e-4:
+ * that certificate does not cover V, which is as orthogonal as the factor's
+ * rows are converged.  stop = 0 turns the rule off (sweeps end only on a
+ * sweep that saw nothing above the threshold).  SC_ERR_INVALID_ARG unless
+ * 0 <= stop < 1.  Waits for a pending asynchronous refresh.  A schedule of the
+ * thin SVD of the anchor momentum ("Key design 3" of the papernotes.org notes);
+ * the results meet the same convergence threshold either way. */
+int sc_set_sweep_stop(sc_handle h, float stop);
+
 /* Keep G_proj of each step (costs one more store per element in the AdamW
  * pass and rows x cols floats per matrix). */
 int sc_keep_proj(sc_handle h, int enable);

@@ -207,6 +207,7 @@ struct sc_opt {
         int stage = 0, which = 0, r = 0, rps = 1, max_rounds = 0, first_check = 0, poll_round = 0;
         bool pre = false, poll_pending = false;
         bool targeted = false;  // polishing sweeps restricted to the pairs the certificate marks
+        bool resumed = false;   // plain sweeps resumed after the sweep-stop rule's certificate
     } pipes[kPipes];
     int npipes = 0;
     hipEvent_t fork = nullptr;
@@ -245,6 +246,7 @@ struct sc_opt {
     bool keep_proj = false;
     bool fuse = true;                         // fused apply + next Gram where a matrix allows it
     int v_rounds = 2;                         // fused matrices' V rows: rounds per pass (1 or 2)
+    float sweep_stop = 1e-4f;                 // sweep-stop rule (0 = off), see jac_sweep_end_kernel
     std::vector<std::array<char, 2>> fused;   // per matrix: fused over the factor / full rows
     int solve_waves = 0, solve_copies = 0;  // pair solve variant: 0 by the launch's pair count
     std::vector<void*> dev_allocs;
@@ -406,7 +408,8 @@ PtrTable make_table(const sc_opt* h, const void* const* p) {
 enum { LIST_PLAIN = 0, LIST_FACTOR = 1, LIST_POLISH = 2 };
 // STAGE_CERT: waiting for the certificate of the factor phase's A = M V;
 // STAGE_CERT2: for the re-certification after selective polishing
-enum { STAGE_ROUNDS = 0, STAGE_CERT = 1, STAGE_CERT2 = 2, STAGE_DONE = 3 };
+// STAGE_CERTP: for the certificate of plain sweeps that ended on the sweep-stop rule
+enum { STAGE_ROUNDS = 0, STAGE_CERT = 1, STAGE_CERT2 = 2, STAGE_DONE = 3, STAGE_CERTP = 4 };
 typedef sc_opt::Pipe Pipe;
 
 // d = s / (s + tau) and the projectors X^T diag(d) X of the pipe's matrices.
@@ -583,6 +586,19 @@ void pipe_start_rounds(sc_opt* h, Pipe& p, int which, int first_check_sweeps, in
 }
 
 // One Jacobi round of the pipe's current list set.
+// The sweep-stop rule in the Cholesky factor phase is capped: the certificate
+// that follows checks A = M V but not V, whose orthogonality comes from the
+// factor's convergence (V <- normalized X^T V_prev); on the 16-block workload a
+// factor sweep that saw at most 1e-4 was followed by one that saw only the
+// rotation threshold, so V is as orthogonal as after a sweep that sees nothing.
+constexpr float kFactorStopMax = 1e-4f;
+// The sweep-stop rule for plain sweeps: only where the host polls (the
+// certificate's outcome decides whether sweeps resume) and not after a resume.
+// A and V are rotated together there, so the final Gram's certificate covers it.
+float plain_stop(const sc_opt* h, const Pipe& p) {
+    return p.which == LIST_PLAIN && h->hp.sync_check && !p.resumed ? h->sweep_stop : 0.0f;
+}
+
 int pipe_round(sc_opt* h, Pipe& p, hipStream_t st) {
     const sc_opt::Lists& L = p.L[p.which];
     const int r = p.r;
@@ -632,7 +648,10 @@ int pipe_round(sc_opt* h, Pipe& p, hipStream_t st) {
     if (last)
         HIP_TRY(timed(h, PK_SWEEP_END, st, [&] {
             return launch_jacobi_sweep_end(h->md, h->flags_d, L.mats, L.nmat, r, h->hp.max_sweeps,
-                                           st);
+                                           p.which == LIST_FACTOR
+                                               ? std::min(h->sweep_stop, kFactorStopMax)
+                                               : 0.0f,
+                                           plain_stop(h, p), st);
         }));
     return SC_OK;
 }
@@ -680,7 +699,9 @@ int pipe_start_full_polish(sc_opt* h, Pipe& p, hipStream_t st, int max_nb) {
     return SC_OK;
 }
 
-int pipe_after_rounds(sc_opt* h, Pipe& p, hipStream_t st) {
+// polled: the pipe's host flags show the state after its last round (a poll saw
+// every matrix done), so they tell whether any plain sweeps ended on the sweep-stop rule.
+int pipe_after_rounds(sc_opt* h, Pipe& p, hipStream_t st, bool polled) {
     int rc;
     if (p.which == LIST_POLISH && p.targeted) {
         // re-certify: the Gram of the selectively polished matrices again, then the
@@ -719,7 +740,23 @@ int pipe_after_rounds(sc_opt* h, Pipe& p, hipStream_t st) {
         p.stage = STAGE_CERT;
         return pipe_poll(h, p, st);
     }
-    if ((rc = pipe_final_gram(h, p, st, p.which == LIST_POLISH))) return rc;
+    bool early = plain_stop(h, p) > 0.0f;
+    if (early && polled) {
+        early = false;
+        for (int i : p.host_mats) early = early || p.flags_h[i].early;
+    }
+    if (early) {
+        // plain sweeps that ended on the sweep-stop rule: the final Gram's certificate;
+        // failing matrices sweep on (polled)
+        if ((rc = pipe_final_gram(h, p, st))) return rc;
+        HIP_TRY(timed(h, PK_INIT_FLAGS, st, [&] {
+            return launch_certify_early(h->md, h->flags_d, p.L[LIST_PLAIN].mats,
+                                        p.L[LIST_PLAIN].nmat, st);
+        }));
+        p.stage = STAGE_CERTP;
+        return pipe_poll(h, p, st);
+    }
+    if ((rc = pipe_final_gram(h, p, st, p.which == LIST_POLISH || p.resumed))) return rc;
     if ((rc = pipe_finalize(h, p, st))) return rc;
     p.stage = STAGE_DONE;
     return SC_OK;
@@ -742,6 +779,7 @@ int do_refresh(sc_opt* h, hipStream_t st) {
         // columns of A = M V_prev are close to orthogonal.  From a cold start (A = M) a
         // graded spectrum would make most factorizations fail, so it is skipped.
         p.pre = p.ncap > 0 && warm;
+        p.resumed = false;
         if ((rc = pipe_pre(h, p, pst(p), warm))) return rc;
         pipe_start_rounds(h, p, p.pre ? LIST_FACTOR : LIST_PLAIN, 4);
     }
@@ -765,6 +803,18 @@ int do_refresh(sc_opt* h, hipStream_t st) {
                 } else {
                     p.poll_pending = false;
                     const bool all = pipe_all_done(h, p);
+                    if (p.stage == STAGE_CERTP) {
+                        if (all) {
+                            if ((rc = pipe_finalize(h, p, ps))) return rc;
+                            p.stage = STAGE_DONE;
+                        } else {
+                            // sweeps on for the matrices the certificate rejected
+                            p.resumed = true;
+                            pipe_start_rounds(h, p, LIST_PLAIN, 1);
+                        }
+                        queued = true;
+                        continue;
+                    }
                     if (p.stage == STAGE_CERT || p.stage == STAGE_CERT2) {
                         if (all) {
                             if ((rc = pipe_finalize(h, p, ps))) return rc;
@@ -784,7 +834,7 @@ int do_refresh(sc_opt* h, hipStream_t st) {
                         continue;
                     }
                     if (all || p.r >= p.max_rounds) {
-                        if ((rc = pipe_after_rounds(h, p, ps))) return rc;
+                        if ((rc = pipe_after_rounds(h, p, ps, all))) return rc;
                         queued = true;
                         continue;
                     }
@@ -801,7 +851,7 @@ int do_refresh(sc_opt* h, hipStream_t st) {
                     p.poll_round = p.r;
                 }
             } else if (p.r >= p.max_rounds && !p.poll_pending) {
-                if ((rc = pipe_after_rounds(h, p, ps))) return rc;
+                if ((rc = pipe_after_rounds(h, p, ps, false))) return rc;
                 queued = true;
             }
         }
@@ -1915,6 +1965,16 @@ int sc_set_v_rounds(sc_handle h, int rounds) {
     DeviceGuard g(h->device);
     if ((rc = finish_async(h, nullptr, true))) return rc;
     h->v_rounds = rounds;
+    return SC_OK;
+}
+
+int sc_set_sweep_stop(sc_handle h, float stop) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    if (!(stop >= 0.0f && stop < 1.0f)) return fail(SC_ERR_INVALID_ARG, "stop must be in [0, 1)");
+    DeviceGuard g(h->device);
+    if ((rc = finish_async(h, nullptr, true))) return rc;
+    h->sweep_stop = stop;
     return SC_OK;
 }
 

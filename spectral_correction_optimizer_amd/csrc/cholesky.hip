@@ -484,6 +484,28 @@ __global__ void certify_kernel(const MatDev* __restrict__ mats, MatFlags* __rest
     }
 }
 
+__global__ void certify_early_kernel(const MatDev* __restrict__ mats, MatFlags* __restrict__ flags,
+                                     const int* __restrict__ mat_idx, int nmat) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= nmat) return;
+    const int i = mat_idx[t];
+    MatFlags& f = flags[i];
+    if (!f.early) return;
+    f.early = 0;
+    if (!(__uint_as_float(f.check_off) > mats[i].tol_conv)) return;
+    f.converged = 0;
+    f.done = 0;
+    f.check_off = 0u;
+    f.regram = 1;
+}
+
+hipError_t launch_certify_early(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
+                                hipStream_t st) {
+    hipLaunchKernelGGL(certify_early_kernel, dim3((nmat + 63) / 64), dim3(64), 0, st, mats, flags,
+                       mat_idx, nmat);
+    return hipGetLastError();
+}
+
 hipError_t launch_certify(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
                           hipStream_t st) {
     hipLaunchKernelGGL(certify_kernel, dim3((nmat + 63) / 64), dim3(64), 0, st, mats, flags, mat_idx,

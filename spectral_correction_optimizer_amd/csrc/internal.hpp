@@ -82,6 +82,7 @@ struct MatFlags {
     int sel_pairs;           // pair Grams solved in selective sweeps (work accounting)
     int sel_rot;             // pairs rotated in selective sweeps (work accounting)
     int sel_sweeps;          // selective sweeps run
+    int early;               // 1 when plain sweeps ended on the sweep-stop rule (certificate pending)
 };
 
 // Selective polishing: largest k (and kpad) whose inverse column order fits the
@@ -190,9 +191,12 @@ hipError_t launch_jacobi_apply_v2(const MatDev* mats, const MatFlags* flags, con
 // At a matrix's sweep start: order its columns by decreasing norm (perm).
 hipError_t launch_jacobi_sort(const MatDev* mats, const MatFlags* flags, const int* mat_idx,
                               int nmat, int round, hipStream_t st);
+// A sweep that saw nothing above tol_conv ends a matrix's sweeps; so does one that
+// saw at most stop_factor (factor phase) or stop_plain (plain sweeps; early = 1,
+// the final Gram's certificate decides): 0 turns the rule off.
 hipError_t launch_jacobi_sweep_end(const MatDev* mats, MatFlags* flags, const int* mat_idx,
-                                   int nmat, int round, int max_sweeps,
-                                   hipStream_t st);
+                                   int nmat, int round, int max_sweeps, float stop_factor,
+                                   float stop_plain, hipStream_t st);
 
 // ---- Cholesky preconditioning of tall operands ------------------------------------------
 
@@ -215,6 +219,11 @@ hipError_t launch_gram_to_e(const MatDev* mats, MatFlags* flags, const int* mat_
 // otherwise not done (polishing sweeps follow) and check_off cleared.
 hipError_t launch_certify(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
                           hipStream_t st);
+// For the matrices in mat_idx whose plain sweeps ended on the sweep-stop rule
+// (early): kept when check_off <= tol_conv, else not done, regram = 1 (more
+// sweeps follow, then their final Gram again); early cleared.
+hipError_t launch_certify_early(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
+                                hipStream_t st);
 // inv[j] = 1 / sqrt(cnorm[j]) for j < k of the accepted matrices (into md.Y):
 // row scales that make V = L^T-phase vectors x W_prev orthonormal.
 hipError_t launch_factor_invnorm(const MatDev* mats, const MatFlags* flags, const int* mat_idx,

@@ -1288,17 +1288,18 @@ hipError_t launch_jacobi_sort(const MatDev* mats, const MatFlags* flags, const i
 
 // ---------------------------------------------------------------------------------
 // End-of-round bookkeeping: a matrix whose sweep ended this round is
-// converged when nothing above tolerance was seen during the sweep.  The factor
-// phase also ends after a sweep whose largest measure is at most kFactorStop: its
-// convergence is quadratic by then (measured on the 16-block workload: sweeps
-// that saw at most 1e-4 were followed by ones that saw about 1e-6, the rotation
-// threshold), and the certificate of A = M V that follows the factor phase checks
-// the result (pairs that fail it are polished), so that last sweep, which rotates
-// almost nothing, is not run.
-constexpr float kFactorStop = 1e-4f;
+// converged when nothing above tolerance was seen during the sweep, or when the
+// sweep saw at most the sweep-stop value (stop_factor in the Cholesky factor
+// phase, stop_plain in plain sweeps; 0 = off).  By then the convergence is
+// quadratic (on the 16-block workload, sweeps that saw at most 1e-4 were
+// followed by ones that saw about 1e-6, the rotation threshold), so the sweep
+// that would only confirm it rotates almost nothing; a certificate checks the
+// result instead: after the factor phase the one of A = M V (failing pairs are
+// polished), after plain sweeps the final Gram's (early = 1; a failing matrix
+// sweeps on).
 __global__ void jac_sweep_end_kernel(const MatDev* __restrict__ mats, MatFlags* __restrict__ flags,
                                      const int* __restrict__ mat_idx, int nmat, int round,
-                                     int max_sweeps) {
+                                     int max_sweeps, float stop_factor, float stop_plain) {
     const int t = blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= nmat) return;
     const int i = mat_idx[t];
@@ -1310,11 +1311,16 @@ __global__ void jac_sweep_end_kernel(const MatDev* __restrict__ mats, MatFlags* 
     if (f.sel) f.sel_sweeps += 1;
     const float mo = __uint_as_float(f.sweep_max);
     f.sweep_max = 0u;
+    const float stop = f.precond ? stop_factor : stop_plain;
     if (!(mo <= 3.402823466e38f)) {
         f.done = 1;  // a non-finite operand: stop, reported as not converged
-    } else if (!(mo > mats[i].tol_conv) || (f.precond && !(mo > kFactorStop))) {
+    } else if (!(mo > mats[i].tol_conv)) {
         f.converged = 1;
         f.done = 1;
+    } else if (!(mo > stop)) {
+        f.converged = 1;
+        f.done = 1;
+        if (!f.precond) f.early = 1;
     } else if (f.sel ? f.sel_sweeps >= kSelSweeps
                      : f.sweeps - f.sweep_base - f.sel_sweeps >= max_sweeps) {
         f.done = 1;
@@ -1376,10 +1382,10 @@ hipError_t launch_jacobi_apply_v2(const MatDev* mats, const MatFlags* flags, con
 }
 
 hipError_t launch_jacobi_sweep_end(const MatDev* mats, MatFlags* flags, const int* mat_idx,
-                                   int nmat, int round, int max_sweeps,
-                                   hipStream_t st) {
+                                   int nmat, int round, int max_sweeps, float stop_factor,
+                                   float stop_plain, hipStream_t st) {
     hipLaunchKernelGGL(jac_sweep_end_kernel, dim3((nmat + 63) / 64), dim3(64), 0, st, mats, flags,
-                       mat_idx, nmat, round, max_sweeps);
+                       mat_idx, nmat, round, max_sweeps, stop_factor, stop_plain);
     return hipGetLastError();
 }
 

@@ -77,13 +77,15 @@ class Scenario:
         self.threads = threads
         self.max_sweeps = max_sweeps
 
-    def run(self, device="cuda", check_every_step=True, gpu_hp=None):
+    def run(self, device="cuda", check_every_step=True, gpu_hp=None, setup=None):
         dev = torch.device(device)
         tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
         import spectral_correction_optimizer_amd as sco
         opt = sco.SpectralAdamW(self.shapes, w_dtype=tdt[self.w_dtype], g_dtype=tdt[self.g_dtype],
                                 device=dev, max_sweeps=self.max_sweeps, **self.hp, **(gpu_hp or {}))
         opt.keep_proj(True)
+        if setup is not None:
+            setup(opt)
         ora = oracle.Optimizer(self.shapes, self.hp, w_dtype=self.w_dtype, state_dtype="f32",
                                threads=self.threads)
         W_dev, W_ora = [], []

@@ -545,6 +545,34 @@ def test_sync_check_0_enqueue_only_matches_oracle():
     assert st["factor_sweeps_max"] > 0  # the factor phase ran without host decisions
 
 
+@pytest.mark.parametrize("stop", [0.9, 0.0])
+def test_sweep_stop_rule_against_oracle(stop):
+    """The sweep-stop rule at 0.9 ends the plain sweeps after a matrix's first
+    sweep: the final Gram's certificate rejects them, their sweeps resume and
+    their final Gram is redone, and the result still matches the oracle (in the
+    factor phase the rule stays capped at 1e-4); with the rule off (0) sweeps end
+    only on the convergence threshold.  Cold and warm refreshes of the three
+    shape classes."""
+    import spectral_correction_optimizer_amd as sco
+    shapes = [(256, 256), (128, 512), (512, 128), (1024, 256), (200, 136)]
+    say(f"case: sweep stop {stop}, {shapes}, refresh every 2 steps, 4 steps")
+    sc = Scenario(shapes, [(181, 0, i) for i in range(len(shapes))], steps=4, anchor_every=2)
+
+    def setup(opt):
+        for bad in (-0.1, 1.0, float("nan")):
+            with pytest.raises(sco.ScoptError):
+                opt.set_sweep_stop(bad)
+        opt.set_sweep_stop(stop)
+
+    rep = sc.run(setup=setup)
+    Scenario.check(rep)
+    st = rep["stats"]
+    say(f"  stats {st}")
+    assert st["not_converged"] == 0
+    # every refresh still ran more than one sweep per matrix
+    assert all(min(g) >= 2 for g, _ in rep["sweeps"])
+
+
 def test_sweep_cap_reports_not_converged():
     """max_sweeps = 1 stops every matrix after one sweep of a cold refresh: the
     stats report each matrix as not converged with one sweep, and a step still
