@@ -109,27 +109,27 @@ def copy_calibration(nbytes):
 
 
 # Measured HBM traffic of a kernel family relative to its algorithmic bytes: two
-# rocprofv3 counter runs of the same command (FETCH_SIZE, then WRITE_SIZE, each
-# scaled by its reading for a plain 1 GiB device copy: 2.0 and 1.0 bytes per
-# reported byte), summed over the timed passes' dispatches, divided by the
-# algorithmic bytes the same runs' live kernel accounting gives for those
-# dispatches.  The line's traffic per launch is this ratio times its own
+# rocprofv3 counter runs of the same command with kernel timing in every timed
+# pass (--live-passes 20; FETCH_SIZE, then WRITE_SIZE, each scaled by its reading
+# for a plain 1 GiB device copy: 2.0 and 1.0 bytes per reported byte), summed over
+# the timed passes' dispatches, divided by the algorithmic bytes the same runs'
+# live kernel accounting gives for those dispatches.  The line's traffic per launch is this ratio times its own
 # algorithmic bytes per launch (the number of empty launches queued past a
 # converged sweep depends on host timing, so per-dispatch averages of two runs
 # differ while the ratio does not).  Keyed by the kernel source (sha256), the
 # workload and the pass schedule; anything else is reported as null.
 TRAFFIC = {
     "jacobi_apply_gram": [{"source": "jacobi.hip", "workload": "blocks16_1b", "warmup": 5, "steps": 20,
-                           "sha256": "9c261e7038970eb911d868d849adda35896d84b3124512ba49ee129f267ff075",
-                           "ratio": 1.078,  # 24.69 TB counted / 22.91 TB algorithmic, 26451 dispatches
+                           "sha256": "3f360f51648a4d159ed3f3ea1f6258de9dbadf5f4bb9ef00db0fcb9b35a4974c",
+                           "ratio": 1.075,  # 935.1 MB counted / 869.6 MB algorithmic per launch, 25434 dispatches
                            }],
     "combine_adamw": [{"source": "elementwise.hip", "workload": "blocks16_1b", "warmup": 5, "steps": 20,
-                       "sha256": "9c46f10aa921b5400611de920e56dc857c7fc19d823786fab27c5d7484af934c",
-                       "ratio": 1.0003,  # 31.148 GB counted / 31.138 GB algorithmic per launch
+                       "sha256": "8323014c23791afa0e6cdf2b0d6afafb08af0cf832ff6b2a0513e605c6b3e64b",
+                       "ratio": 1.0049,  # 31.291 GB counted / 31.139 GB algorithmic per launch
                        }],
     "ema": [{"source": "elementwise.hip", "workload": "blocks16_1b", "warmup": 5, "steps": 20,
-             "sha256": "9c46f10aa921b5400611de920e56dc857c7fc19d823786fab27c5d7484af934c",
-             "ratio": 1.0008,  # 11.687 GB counted / 11.677 GB algorithmic per launch
+             "sha256": "8323014c23791afa0e6cdf2b0d6afafb08af0cf832ff6b2a0513e605c6b3e64b",
+             "ratio": 1.0130,  # 11.829 GB counted / 11.677 GB algorithmic per launch
              }],
 }
 
