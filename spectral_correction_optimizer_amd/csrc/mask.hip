@@ -10,14 +10,20 @@
 // ascending order; mix64 is the SplitMix64 output function (Steele, Lea and
 // Flood, OOPSLA 2014), gamma its golden-ratio increment.
 //
-//   mask_indices  one workgroup per token: the hashes below a threshold that
-//                 almost surely admits the K smallest (all H when it does not),
-//                 a bitonic sort of them by (hash, dimension), then the first K
-//                 dimensions sorted ascending (integer work, ALU bound)
+//   mask_indices  one wavefront per token (mask_indices_wave_kernel): the
+//                 hashes below a threshold that admits between K and `cap` of
+//                 them, collected in dimension order; a register bitonic sort
+//                 of their hashes gives the K-th smallest, and the candidates up
+//                 to it are the kept set, already in ascending order.  For
+//                 parameters where `cap` would be large or K not well below H,
+//                 one workgroup per token sorts all H (mask_indices_kernel).
+//                 Integer work, ALU bound.
 //   mask_pack     kept values of each token, in index order (a gather; bound by
 //                 HBM sectors touched)
 //   mask_unpack   dense rows with zeros elsewhere (an LDS row per token, then
 //                 coalesced row writes; HBM bound)
+#include <cmath>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -134,6 +140,107 @@ __global__ __launch_bounds__(256) void mask_indices_kernel(uint64_t seed, int64_
     }
 }
 
+// One wavefront per token (64-thread workgroups, so __syncthreads orders the
+// wave's LDS accesses).  The hashes of a token are distinct (mix64 is a
+// bijection and the inputs seed + (i H + j + 1) gamma differ for distinct j,
+// gamma odd), so the number of them below t grows by one at each hash: starting
+// from t0, bisection on t finds a threshold with K <= count <= CAP (almost
+// always t0 itself).  Those candidates are collected in dimension order (ballot
+// compaction), their hashes sorted in registers (R = CAP / 64 per lane, bitonic;
+// lanes exchange through shuffles), and every candidate whose hash is at most
+// the K-th smallest is kept: exactly K, in ascending dimension order.
+template <int R>
+__global__ __launch_bounds__(64) void mask_indices_wave_kernel(uint64_t seed, int64_t T, int H, int K,
+                                                              uint64_t t0, int32_t* __restrict__ idx) {
+    constexpr int CAP = 64 * R;
+    __shared__ uint64_t ck[CAP];
+    __shared__ int32_t cj[CAP];
+    const int lane = threadIdx.x;
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int64_t row = blockIdx.x; row < T; row += gridDim.x) {
+        const uint64_t base = (uint64_t)row * (uint64_t)H + 1ull;
+        uint64_t t = t0, lo = 0, hi = 0;
+        bool have_hi = false;
+        int n;
+        for (;;) {
+            n = 0;
+            for (int j0 = 0; j0 < H; j0 += 64) {
+                const int j = j0 + lane;
+                const uint64_t u = j < H ? mix64(seed + (base + (uint64_t)j) * kGamma) : ~0ull;
+                const bool c = j < H && u < t;
+                const uint64_t m = __ballot(c);
+                const int pos = n + __popcll(m & below);
+                if (c && pos < CAP) {
+                    ck[pos] = u;
+                    cj[pos] = j;
+                }
+                n += __popcll(m);
+            }
+            if (n >= K && n <= CAP) break;
+            if (n < K) {
+                lo = t;
+                t = have_hi ? lo + (hi - lo) / 2 : (t > (~0ull >> 1) ? ~0ull : 2 * t + 1);
+            } else {
+                hi = t;
+                have_hi = true;
+                t = lo + (hi - lo) / 2;
+            }
+        }
+        __syncthreads();
+        // the K-th smallest candidate hash: ascending bitonic sort of CAP entries,
+        // entry e = R lane + r (padding ~0 is above every candidate, all < t)
+        uint64_t v[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int e = R * lane + r;
+            v[r] = e < n ? ck[e] : ~0ull;
+        }
+        for (int size = 2; size <= CAP; size <<= 1) {
+            for (int stride = size >> 1; stride >= R; stride >>= 1) {
+                const int d = stride / R;  // partner lane distance
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const int e = R * lane + r;
+                    const uint64_t y = __shfl_xor(v[r], d);
+                    const bool keep_min = ((e & stride) == 0) == ((e & size) == 0);
+                    v[r] = keep_min ? (v[r] < y ? v[r] : y) : (v[r] < y ? y : v[r]);
+                }
+            }
+#pragma unroll
+            for (int stride = R / 2; stride > 0; stride >>= 1) {
+                if (stride >= size) continue;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if (r & stride) continue;
+                    const int e = R * lane + r;
+                    const bool up = (e & size) == 0;
+                    const uint64_t a = v[r], b = v[r + stride];
+                    if ((a > b) == up) {
+                        v[r] = b;
+                        v[r + stride] = a;
+                    }
+                }
+            }
+        }
+        uint64_t mine = v[0];
+#pragma unroll
+        for (int r = 1; r < R; ++r)
+            if ((K - 1) % R == r) mine = v[r];
+        const uint64_t uk = __shfl(mine, (K - 1) / R);
+        // the kept dimensions, in candidate (ascending dimension) order
+        int32_t* out = idx + row * K;
+        int cnt = 0;
+        for (int i0 = 0; i0 < n; i0 += 64) {
+            const int i = i0 + lane;
+            const bool sel = i < n && ck[i] <= uk;
+            const uint64_t m = __ballot(sel);
+            if (sel) gst(out + cnt + __popcll(m & below), cj[i]);
+            cnt += __popcll(m);
+        }
+        __syncthreads();  // the candidate lists are rewritten for the next token
+    }
+}
+
 template <typename E>
 __global__ __launch_bounds__(256) void mask_pack_kernel(const E* __restrict__ x, const int32_t* __restrict__ idx,
                                                         int64_t T, int H, int K, E* __restrict__ packed) {
@@ -168,6 +275,23 @@ int grid_rows(int64_t T) { return (int)(T < 65536 ? T : 65536); }
 
 hipError_t launch_mask_indices(uint64_t seed, int64_t T, int H, int K, int32_t* idx, hipStream_t st) {
     if (T <= 0 || K <= 0) return hipSuccess;
+    // the candidate threshold of the one-wavefront kernel: w = K + 5 sqrt(K) + 16 hashes
+    // expected below t0, room for w + 6 sqrt(w) candidates
+    const double want = K + 5.0 * std::sqrt((double)K) + 16.0;
+    int cap = 64;
+    while (cap < want + 6.0 * std::sqrt(want)) cap <<= 1;
+    if (cap <= 512 && want < 0.5 * H) {
+        const uint64_t t0 = (uint64_t)(want / H * 18446744073709551616.0);
+        const dim3 grid(grid_rows(T) * 4 < T ? grid_rows(T) * 4 : (unsigned)T);
+#define SC_MASK_WAVE(R_)                                                                        \
+    if (cap == 64 * R_) {                                                                     \
+        hipLaunchKernelGGL(mask_indices_wave_kernel<R_>, grid, dim3(64), 0, st, seed, T, H, K, \
+                           t0, idx);                                                          \
+        return hipGetLastError();                                                             \
+    }
+        SC_MASK_WAVE(1) SC_MASK_WAVE(2) SC_MASK_WAVE(4) SC_MASK_WAVE(8)
+#undef SC_MASK_WAVE
+    }
     hipLaunchKernelGGL(mask_indices_kernel, dim3(grid_rows(T)), dim3(256), 0, st, seed, T, H, K, idx);
     return hipGetLastError();
 }
