@@ -68,8 +68,10 @@ typedef struct {
     float weight_decay; /* decoupled weight decay, scaled by lr, >= 0 */
     int max_sweeps;     /* Jacobi sweep cap per refresh, >= 1 (e.g. 30) */
     float jacobi_tol;   /* rotation and convergence threshold on |a_p.a_q| / (|a_p||a_q|);
-                           0 = default: rotate above 16 * 2^-24, stop after a sweep whose
-                           largest ratio is <= 2^-24 * max(16, sqrt(max(rows, cols))) */
+                           0 = default: rotate above 16 * 2^-24 (8 * 2^-24 for operands
+                           with a Cholesky factor phase, max >= 2 min of rows, cols), stop
+                           after a sweep whose largest ratio is
+                           <= 2^-24 * max(16, sqrt(max(rows, cols))) */
     int sync_check;     /* 1: poll convergence flags on the host, queue no sweep past
                            convergence (blocks the caller, see above);
                            0: enqueue only: every phase of the refresh queues

@@ -1161,6 +1161,13 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         // (square operands keep the plain sweeps: A^T A squares their condition
         // number and the factor phase then needs more sweeps, not fewer)
         m.klen = (h->hp.precondition && m.K >= 2 * m.k) ? round_up(m.k, 128) : 0;
+        // Operands with a factor phase rotate pairs above 8 * 2^-24: the certificate of
+        // A = M V sees the factor's residual off-diagonals amplified by the condition
+        // number (E(A) ~ kappa E(X)); rotating down to half the plain threshold leaves
+        // room for kappa up to ~10 at the steady state of the 16-block workload, whose
+        // long matrices then pass the certificate without polishing (pass 639-645 ->
+        // 616-623 ms; 4 or 6 * 2^-24 rotate more noise for no gain, 10-12 let some fail).
+        if (m.klen && !(h->hp.jacobi_tol > 0.0f)) m.tol = (float)(8.0 * eps);
         m.nsplit = split_count(m.K_ld, kMaxSplits);  // capacity of the partial buffer
         if (m.klen) m.nsplit = std::max(m.nsplit, split_count(m.klen, kMaxSplits));
         const size_t f = sizeof(float);
