@@ -262,6 +262,23 @@ int sc_set_v_rounds(sc_handle h, int rounds);
  * the results meet the same convergence threshold either way. */
 int sc_set_sweep_stop(sc_handle h, float stop);
 
+/* Quad passes of the Jacobi sweeps (default on): for matrices whose column-block
+ * count nb (k rounded up to 64, over 32) is 4, 16, 64 or 256, the nb - 1 pair
+ * rounds of a sweep are taken three at a time: the masks of the XOR rounds
+ * split into lines {m0, m1, m0 ^ m1}, whose three rounds pair blocks inside
+ * groups of four, so one pass per line forms each group's 128 x 128 Gram,
+ * solves the three rounds' block pairs in LDS (the next round's Gram from the
+ * rotated one) and applies their product to the group's rows: one read of the
+ * operand for the Gram and one read and write for the rotation per three
+ * rounds.  Every block pair is still solved once per sweep, in another order;
+ * the results meet the same convergence threshold.  enable = 0 keeps the pair
+ * rounds.  A list of matrices (a refresh pipeline's plain or factor-phase set)
+ * runs quad passes only when all its block counts allow it; polishing sweeps
+ * keep the pair rounds.  Waits for a pending asynchronous refresh.  A schedule
+ * of the thin SVD of the anchor momentum ("Key design 3" of the papernotes.org
+ * notes). */
+int sc_set_quad(sc_handle h, int enable);
+
 /* Keep G_proj of each step (costs one more store per element in the AdamW
  * pass and rows x cols floats per matrix). */
 int sc_keep_proj(sc_handle h, int enable);

@@ -31,7 +31,7 @@ EXPORTED_SYMBOLS = (
     "sc_default_hparams", "sc_opt_create", "sc_opt_destroy", "sc_anchor_update", "sc_refresh",
     "sc_anchor_update_async", "sc_refresh_wait", "sc_refresh_pending", "sc_step", "sc_step_noalloc", "sc_set_lr", "sc_set_tau", "sc_set_state", "sc_get_state", "sc_set_step",
     "sc_get_step", "sc_set_factors", "sc_get_factors", "sc_keep_proj", "sc_get_filtered",
-    "sc_set_solve_waves", "sc_set_fused_gram", "sc_set_v_rounds", "sc_set_sweep_stop",
+    "sc_set_solve_waves", "sc_set_fused_gram", "sc_set_v_rounds", "sc_set_sweep_stop", "sc_set_quad",
     "sc_get_stats", "sc_get_sweep_counts", "sc_profile", "sc_get_kernel_times", "sc_last_error",
     "sc_mask_keep_count", "sc_mask_seed", "sc_mask_indices", "sc_mask_pack", "sc_mask_unpack",
 )
@@ -106,6 +106,7 @@ def load_library():
         "sc_set_fused_gram": (ctypes.c_int, [vp, ctypes.c_int]),
         "sc_set_v_rounds": (ctypes.c_int, [vp, ctypes.c_int]),
         "sc_set_sweep_stop": (ctypes.c_int, [vp, ctypes.c_float]),
+        "sc_set_quad": (ctypes.c_int, [vp, ctypes.c_int]),
         "sc_get_filtered": (ctypes.c_int, [vp, ctypes.c_int, vp, vp, vp]),
         "sc_get_stats": (ctypes.c_int, [vp, ctypes.POINTER(Stats), ctypes.POINTER(ctypes.c_int)]),
         "sc_get_sweep_counts": (ctypes.c_int, [vp, ctypes.POINTER(ctypes.c_int),
@@ -303,6 +304,11 @@ class SpectralAdamW:
         """Sweep-stop rule of the Jacobi sweeps (0 = off); a certificate checks
         the result."""
         _check(self._lib.sc_set_sweep_stop(self._h, float(stop)))
+
+    def set_quad(self, enable: bool = True):
+        """Quad passes of the Jacobi sweeps (default on): three pair rounds per
+        pass over groups of four column blocks, where the block counts allow."""
+        _check(self._lib.sc_set_quad(self._h, 1 if enable else 0))
 
     def keep_proj(self, enable: bool = True):
         _check(self._lib.sc_keep_proj(self._h, 1 if enable else 0))

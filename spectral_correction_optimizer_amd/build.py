@@ -13,7 +13,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libscopt.so")
 
-SOURCES = ["api.cpp", "cholesky.hip", "elementwise.hip", "gemm.hip", "jacobi.hip", "mask.hip"]
+SOURCES = ["api.cpp", "cholesky.hip", "elementwise.hip", "gemm.hip", "jacobi.hip", "mask.hip",
+           "quad.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -40,7 +41,7 @@ def _compile(src: str) -> str:
 
 def build_library(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(7, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs

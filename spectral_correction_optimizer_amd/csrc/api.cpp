@@ -77,13 +77,14 @@ enum ProfKind {
     PK_EMA, PK_LOAD, PK_ROWNORM, PK_INIT_FLAGS, PK_GRAM, PK_SOLVE, PK_APPLY, PK_SWEEP_END,
     PK_NORMALIZE, PK_LOWDIN, PK_FILTER, PK_PROJECTORS, PK_STEP_GEMM1, PK_STEP_GEMM2,
     PK_STEP_GEMM3, PK_ADAMW, PK_WARM, PK_SORT, PK_CHOL_GEMM, PK_CHOL, PK_POLISH_GEMM,
-    PK_GRAM_E, PK_APPLY_GRAM, PK_COUNT
+    PK_GRAM_E, PK_APPLY_GRAM, PK_QUAD_GRAM, PK_QUAD_SOLVE, PK_QUAD_APPLY, PK_COUNT
 };
 const char* const kProfNames[PK_COUNT] = {
     "ema", "jacobi_load", "rownorm", "jacobi_init", "jacobi_gram", "jacobi_solve",
     "jacobi_apply", "jacobi_sweep_end", "normalize", "lowdin_gemm", "filter", "projector_gemm",
     "step_gemm1", "step_gemm2", "step_gemm3", "combine_adamw", "warm_start", "jacobi_sort",
-    "chol_syrk", "cholesky", "polish_gemm", "final_gram", "jacobi_apply_gram"};
+    "chol_syrk", "cholesky", "polish_gemm", "final_gram", "jacobi_apply_gram", "quad_gram",
+    "quad_solve", "quad_apply"};
 
 // Optional kernel timing: HIP events recorded around every launch on the
 // caller's stream; totals are folded in by sc_get_kernel_times.
@@ -179,6 +180,15 @@ struct sc_opt {
         ApplyItem* av = nullptr;  // the same V rows one round per pass (sc_set_v_rounds 1)
         int nav = 0;
         bool all_fused = false;  // every matrix of the list has the fused apply + Gram
+        // quad passes (every matrix's block count quad_capable, not polishing): group
+        // Grams, group solves, group applies (A and V rows)
+        bool quad = false;
+        FusedItem* qg = nullptr;
+        int nqg = 0;
+        SolveItem* qs = nullptr;
+        int nqs = 0;
+        QuadItem* qa = nullptr;
+        int nqa = 0;
         int* mats = nullptr;
         int nmat = 0;
         int max_nb = 2;
@@ -248,6 +258,8 @@ struct sc_opt {
     int v_rounds = 2;                         // fused matrices' V rows: rounds per pass (1 or 2)
     float sweep_stop = 1e-4f;                 // sweep-stop rule (0 = off), see jac_sweep_end_kernel
     std::vector<std::array<char, 2>> fused;   // per matrix: fused over the factor / full rows
+    bool quad = true;                         // quad passes where a list allows them
+    std::vector<std::array<char, 2>> quadm;   // per matrix: quad passes over the factor / full rows
     int solve_waves = 0, solve_copies = 0;  // pair solve variant: 0 by the launch's pair count
     std::vector<void*> dev_allocs;
     Prof prof;
@@ -500,7 +512,23 @@ void account_sweeps(sc_opt* h, const MatFlags* flags) {
             h->prof.flops[PK_APPLY] += f.sel_rot * 2.0 * pw * pw * (L + m.k);
             h->prof.bytes[PK_APPLY] += f.sel_rot * (8.0 * pw * (L + m.k) + 4.0 * pw * pw);
         }
+        const double quads[2] = {(double)f.quads_pre, (double)(f.quads_applied - f.quads_pre)};
         for (int ph = 0; ph < 2; ++ph) {
+            if (h->quad && h->quadm[i][ph]) {
+                // quad passes: every group's 128 rows read by the group Gram every pass
+                // (ten 32 x 32 tiles); the solve's pair sweeps as in the pair rounds; a
+                // group with a rotation has its 128 rows of the operand and of V read and
+                // written once, plus R (128 x 128)
+                const double qn = 4.0 * kJb;
+                const double gpass = sweeps[ph] * quad_passes(m.nb) * (m.nb / 4);
+                h->prof.flops[PK_QUAD_GRAM] += gpass * 10.0 * 2.0 * kJb * kJb * len[ph];
+                h->prof.bytes[PK_QUAD_GRAM] += gpass * 4.0 * qn * len[ph];
+                h->prof.flops[PK_QUAD_SOLVE] += pairs_full[ph] * (pw * (pw - 1) / 2) * 18.0 * pw;
+                h->prof.flops[PK_QUAD_APPLY] += quads[ph] * 2.0 * qn * qn * (len[ph] + vlen[ph]);
+                h->prof.bytes[PK_QUAD_APPLY] +=
+                    quads[ph] * (8.0 * qn * (len[ph] + vlen[ph]) + 4.0 * qn * qn);
+                continue;
+            }
             h->prof.flops[PK_SOLVE] += pairs_full[ph] * (pw * (pw - 1) / 2) * 18.0 * pw;
             if (h->fuse && h->fused[i][ph]) {
                 // Gram read standalone in a sweep's first round only; the fused
@@ -578,7 +606,8 @@ void pipe_start_rounds(sc_opt* h, Pipe& p, int which, int first_check_sweeps, in
     p.stage = STAGE_ROUNDS;
     p.which = which;
     p.r = 0;
-    p.rps = std::max(1, (max_nb ? max_nb : p.L[which].max_nb) - 1);
+    const int nbl = max_nb ? max_nb : p.L[which].max_nb;
+    p.rps = (h->quad && p.L[which].quad) ? quad_passes(nbl) : std::max(1, nbl - 1);
     const int cap = p.targeted ? std::min(kSelSweeps, h->hp.max_sweeps) : h->hp.max_sweeps;
     p.max_rounds = p.L[which].nmat ? cap * p.rps : 0;
     p.first_check = std::min(p.max_rounds, first_check_sweeps * p.rps);
@@ -599,8 +628,40 @@ float plain_stop(const sc_opt* h, const Pipe& p) {
     return p.which == LIST_PLAIN && h->hp.sync_check && !p.resumed ? h->sweep_stop : 0.0f;
 }
 
+float factor_stop(const sc_opt* h, const Pipe& p) {
+    return p.which == LIST_FACTOR ? std::min(h->sweep_stop, kFactorStopMax) : 0.0f;
+}
+
+// One quad pass (three pair rounds over groups of four blocks) of the pipe's list.
+int pipe_quad_pass(sc_opt* h, Pipe& p, hipStream_t st) {
+    const sc_opt::Lists& L = p.L[p.which];
+    const int r = p.r;
+    bool first = false, last = false;
+    for (int nb : L.nbs) {
+        first = first || r % quad_passes(nb) == 0;
+        last = last || r % quad_passes(nb) == quad_passes(nb) - 1;
+    }
+    if (first)
+        HIP_TRY(timed(h, PK_SORT, st, [&] {
+            return launch_jacobi_sort(h->md, h->flags_d, L.mats, L.nmat, r, 1, st);
+        }));
+    HIP_TRY(timed(h, PK_QUAD_GRAM, st,
+                  [&] { return launch_quad_gram(h->md, h->flags_d, L.qg, L.nqg, r, st); }));
+    HIP_TRY(timed(h, PK_QUAD_SOLVE, st,
+                  [&] { return launch_quad_solve(h->md, h->flags_d, L.qs, L.nqs, r, st); }));
+    HIP_TRY(timed(h, PK_QUAD_APPLY, st,
+                  [&] { return launch_quad_apply(h->md, h->flags_d, L.qa, L.nqa, r, st); }));
+    if (last)
+        HIP_TRY(timed(h, PK_SWEEP_END, st, [&] {
+            return launch_jacobi_sweep_end(h->md, h->flags_d, L.mats, L.nmat, r, 1, h->hp.max_sweeps,
+                                           factor_stop(h, p), plain_stop(h, p), st);
+        }));
+    return SC_OK;
+}
+
 int pipe_round(sc_opt* h, Pipe& p, hipStream_t st) {
     const sc_opt::Lists& L = p.L[p.which];
+    if (h->quad && L.quad) return pipe_quad_pass(h, p, st);
     const int r = p.r;
     // the sort acts on the first round of a matrix's sweep, the sweep end on its
     // last: launched only in rounds where some matrix of the list has one
@@ -611,7 +672,7 @@ int pipe_round(sc_opt* h, Pipe& p, hipStream_t st) {
     }
     if (first)
         HIP_TRY(timed(h, PK_SORT, st, [&] {
-            return launch_jacobi_sort(h->md, h->flags_d, L.mats, L.nmat, r, st);
+            return launch_jacobi_sort(h->md, h->flags_d, L.mats, L.nmat, r, 0, st);
         }));
     // with every matrix fused the standalone Gram only serves sweeps' first rounds;
     // selective polishing works on few pairs per round, each Gram from the operand
@@ -647,11 +708,8 @@ int pipe_round(sc_opt* h, Pipe& p, hipStream_t st) {
     }
     if (last)
         HIP_TRY(timed(h, PK_SWEEP_END, st, [&] {
-            return launch_jacobi_sweep_end(h->md, h->flags_d, L.mats, L.nmat, r, h->hp.max_sweeps,
-                                           p.which == LIST_FACTOR
-                                               ? std::min(h->sweep_stop, kFactorStopMax)
-                                               : 0.0f,
-                                           plain_stop(h, p), st);
+            return launch_jacobi_sweep_end(h->md, h->flags_d, L.mats, L.nmat, r, 0, h->hp.max_sweeps,
+                                           factor_stop(h, p), plain_stop(h, p), st);
         }));
     return SC_OK;
 }
@@ -1119,6 +1177,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
     const int n = h->n;
     h->mh.resize(n);
     h->fused.assign(n, std::array<char, 2>{0, 0});
+    h->quadm.assign(n, std::array<char, 2>{0, 0});
     // layout pass: sizes of every buffer, carved from one arena
     std::vector<size_t> off;
     size_t total = 0;
@@ -1170,6 +1229,8 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         if (m.klen && !(h->hp.jacobi_tol > 0.0f)) m.tol = (float)(8.0 * eps);
         m.nsplit = split_count(m.K_ld, kMaxSplits);  // capacity of the partial buffer
         if (m.klen) m.nsplit = std::max(m.nsplit, split_count(m.klen, kMaxSplits));
+        // quad passes: group Gram splits of at most kQuadGramCols columns
+        if (quad_capable(m.nb)) m.nsplit = std::max(m.nsplit, (m.K_ld + kQuadGramCols - 1) / kQuadGramCols);
         const size_t f = sizeof(float);
         const size_t mn = (size_t)m.numel * f;
         const size_t kk = (size_t)m.k * m.k * f;
@@ -1190,7 +1251,11 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
         o[i].T = take(kk);
         o[i].E = take(kk);
         o[i].invn = take((size_t)m.kpad * f);
-        o[i].gram = take((size_t)(m.nb / 2) * m.nsplit * kPw * kPw * sizeof(double));
+        // pair partials [nb/2][nsplit][64][64]; quad passes per group [nsplit][10][32][32]
+        // and the group's 128 x 128 float32 Gram
+        o[i].gram = take(std::max((size_t)(m.nb / 2) * m.nsplit * kPw * kPw,
+                                  quad_capable(m.nb) ? (size_t)(m.nb / 4) * (m.nsplit * 10 * 1024 + 8192) : 0) *
+                         sizeof(double));
         // two buffers (round parity): V rows take two rounds' rotations per pass
         o[i].rot = take((size_t)2 * (m.nb / 2) * kPw * kPw * f);
         o[i].rflag = take((size_t)2 * (m.nb / 2) * sizeof(int));
@@ -1323,9 +1388,16 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             std::vector<SolveItem> si;
             std::vector<ApplyItem> ai, ai_f, av;
             bool any_unfused = false;
-            std::vector<FusedItem> fi, vi;
+            std::vector<FusedItem> fi, vi, qg;
+            std::vector<SolveItem> qs;
+            std::vector<QuadItem> qa;
             std::vector<int> mats;
             auto& L = P.L[which];
+            // quad passes: every matrix of the list quad-capable (polishing keeps the
+            // pair rounds: its selective sweeps work on marked block pairs)
+            bool quad = which != LIST_POLISH;
+            for (int i : gm[g])
+                if (which != LIST_POLISH || h->mh[i].klen) quad = quad && quad_capable(h->mh[i].nb);
             int pairs = 0;
             for (int i : gm[g])
                 if (which != LIST_POLISH || h->mh[i].klen) pairs += h->mh[i].nb / 2;
@@ -1351,6 +1423,22 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
                 h->fused[i][which == LIST_FACTOR && m.klen ? 0 : 1] = fuse;
                 any_unfused = any_unfused || !fuse;
                 const bool vrows = !(which == LIST_FACTOR && m.klen);  // V moves outside the factor phase
+                h->quadm[i][which == LIST_FACTOR && m.klen ? 0 : 1] = quad;
+                if (quad) {
+                    const int qns = (len + kQuadGramCols - 1) / kQuadGramCols;
+                    const int qsl = round_up((len + qns - 1) / qns, 128);
+                    const int span = kQuadRun * kQuadCols;
+                    for (int grp = 0; grp < m.nb / 4; ++grp) {
+                        for (int sp = 0; sp < qns; ++sp)
+                            qg.push_back(FusedItem{i, grp, sp, sp * qsl, std::min(len, (sp + 1) * qsl)});
+                        qs.push_back(SolveItem{i, grp, qns});
+                        for (int x0 = 0; x0 < len; x0 += span)
+                            qa.push_back(QuadItem{i, grp, 0, x0, std::min(len, x0 + span)});
+                        if (vrows)
+                            for (int x0 = 0; x0 < m.kpad; x0 += span)
+                                qa.push_back(QuadItem{i, grp, 1, x0, std::min(m.kpad, x0 + span)});
+                    }
+                }
                 if (fuse)
                     for (int grp = 0; grp < m.nb / 4; ++grp) {
                         for (int sp = 0; sp < ns; ++sp)
@@ -1390,6 +1478,10 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             if ((rc = upload(fi, &L.fi, &L.nfi))) return rc;
             if ((rc = upload(vi, &L.vi, &L.nvi))) return rc;
             if ((rc = upload(av, &L.av, &L.nav))) return rc;
+            if ((rc = upload(qg, &L.qg, &L.nqg))) return rc;
+            if ((rc = upload(qs, &L.qs, &L.nqs))) return rc;
+            if ((rc = upload(qa, &L.qa, &L.nqa))) return rc;
+            L.quad = quad && !mats.empty();
             L.all_fused = !mats.empty() && !any_unfused;
             if ((rc = upload(mats, &L.mats, &L.nmat))) return rc;
         }
@@ -1982,6 +2074,15 @@ int sc_set_sweep_stop(sc_handle h, float stop) {
     DeviceGuard g(h->device);
     if ((rc = finish_async(h, nullptr, true))) return rc;
     h->sweep_stop = stop;
+    return SC_OK;
+}
+
+int sc_set_quad(sc_handle h, int enable) {
+    int rc;
+    if ((rc = check_handle(h))) return rc;
+    DeviceGuard g(h->device);
+    if ((rc = finish_async(h, nullptr, true))) return rc;
+    h->quad = enable != 0;
     return SC_OK;
 }
 

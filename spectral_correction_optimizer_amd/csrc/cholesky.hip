@@ -528,6 +528,7 @@ __global__ void phase2_reset_kernel(MatFlags* __restrict__ flags, const int* __r
     f.sweep_max = 0u;
     f.sweep_base = f.sweeps;
     f.pairs_pre = f.pairs_applied;
+    f.quads_pre = f.quads_applied;
     f.check_off = 0u;
     f.sel = 0;
 }

@@ -341,6 +341,8 @@ __global__ __launch_bounds__(256) void init_flags_kernel(const MatDev* __restric
         f.sel_rot = 0;
         f.sel_sweeps = 0;
         f.early = 0;
+        f.quads_applied = 0;
+        f.quads_pre = 0;
     }
     // identity column order; column norms for the first sweep's ordering
     for (int j = threadIdx.x; j < md.kpad; j += blockDim.x) {

@@ -16,6 +16,16 @@ constexpr int kApplyRun = 4;  // column chunks per rotation-apply workgroup (pip
 constexpr int kV2Cols = 256;  // V columns per chunk of the two-round V apply (8 waves x 32)
 constexpr int kV2Threads = 8 * 64;
 constexpr int kV2Run = 4;     // chunks per two-round V apply workgroup
+// Quad passes (quad.hip): three pair rounds of one pass over groups of four blocks
+constexpr int kQuadCols = 256;  // columns per chunk of the group apply (8 waves x 32)
+constexpr int kQuadThreads = 8 * 64;
+constexpr int kQuadRun = 4;     // chunks per group-apply workgroup
+constexpr int kQuadGramCols = 1024;  // largest column split of the group Gram
+// Block counts whose pair rounds split into quad passes: powers of four from 4 to 256.
+__host__ __device__ inline bool quad_capable(int nb) {
+    return nb == 4 || nb == 16 || nb == 64 || nb == 256;
+}
+__host__ __device__ inline int quad_passes(int nb) { return (nb - 1) / 3; }
 
 // Caller pointers of one call (weights / gradients), passed by value.
 struct PtrTable {
@@ -83,6 +93,8 @@ struct MatFlags {
     int sel_rot;             // pairs rotated in selective sweeps (work accounting)
     int sel_sweeps;          // selective sweeps run
     int early;               // 1 when plain sweeps ended on the sweep-stop rule (certificate pending)
+    int quads_applied;       // quad passes: groups whose composed rotation was applied
+    int quads_pre;           // quads_applied at the end of the factor phase
 };
 
 // Selective polishing: largest k (and kpad) whose inverse column order fits the
@@ -98,6 +110,8 @@ struct GramItem { int mat, slot, split, x0, x1, fused; };
 struct SolveItem { int mat, slot, nsplit; };
 // which: 0 = A rows, 1 = V rows; chunks [chunk, chunk + nchunk) of kApplyCols columns
 struct ApplyItem { int mat, slot, which, chunk, nchunk; };
+// quad passes: group apply of group `group`, A rows (which = 0) or V rows (1), columns [x0, x1)
+struct QuadItem { int mat, group, which, x0, x1; };
 // fused apply + next Gram: four-block group of a power-of-two block count over
 // operand columns [x0, x1) of split `split` (at most 8 chunks of kApplyCols)
 struct FusedItem { int mat, group, split, x0, x1; };
@@ -188,14 +202,26 @@ hipError_t launch_jacobi_apply(const MatDev* mats, const MatFlags* flags, const 
 // of kV2Run chunks of kV2Cols), group < nb / 4.
 hipError_t launch_jacobi_apply_v2(const MatDev* mats, const MatFlags* flags, const FusedItem* vi,
                                   int nvi, int round, hipStream_t st);
-// At a matrix's sweep start: order its columns by decreasing norm (perm).
+// Quad passes (quad.hip) of the matrices whose block count is quad_capable: pass
+// `pass` of the list, each matrix at pass % quad_passes(nb) of its sweep.
+// gram: the group Grams (items: group, split, operand columns x0 .. x1, at most
+// kQuadGramCols, multiples of 128); solve: the three rounds of each group (items:
+// slot = group, nsplit = the matrix's splits); apply: the composed rotations.
+hipError_t launch_quad_gram(const MatDev* mats, const MatFlags* flags, const FusedItem* items, int n,
+                            int pass, hipStream_t st);
+hipError_t launch_quad_solve(const MatDev* mats, MatFlags* flags, const SolveItem* items, int n,
+                             int pass, hipStream_t st);
+hipError_t launch_quad_apply(const MatDev* mats, const MatFlags* flags, const QuadItem* items, int n,
+                             int pass, hipStream_t st);
+// At a matrix's sweep start: order its columns by decreasing norm (perm).  quad:
+// the list runs quad passes (quad_passes(nb) per sweep instead of nb - 1 rounds).
 hipError_t launch_jacobi_sort(const MatDev* mats, const MatFlags* flags, const int* mat_idx,
-                              int nmat, int round, hipStream_t st);
+                              int nmat, int round, int quad, hipStream_t st);
 // A sweep that saw nothing above tol_conv ends a matrix's sweeps; so does one that
 // saw at most stop_factor (factor phase) or stop_plain (plain sweeps; early = 1,
 // the final Gram's certificate decides): 0 turns the rule off.
 hipError_t launch_jacobi_sweep_end(const MatDev* mats, MatFlags* flags, const int* mat_idx,
-                                   int nmat, int round, int max_sweeps, float stop_factor,
+                                   int nmat, int round, int quad, int max_sweeps, float stop_factor,
                                    float stop_plain, hipStream_t st);
 
 // ---- Cholesky preconditioning of tall operands ------------------------------------------

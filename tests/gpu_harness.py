@@ -141,6 +141,7 @@ class Scenario:
                     report["w"].append((step, i, float(ulps.max())))
                     report["excluded"].append((step, i, int((ulps > 0).sum()), 0.0))
         report["stats"] = opt.stats()
+        report["kernel_times"] = opt.kernel_times()
         opt.close()
         return report
 

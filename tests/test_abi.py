@@ -81,6 +81,7 @@ def test_invalid_arguments(lib):
     assert lib.sc_set_fused_gram(None, 1) == -1
     assert lib.sc_set_v_rounds(None, 2) == -1
     assert lib.sc_set_sweep_stop(None, ctypes.c_float(1e-4)) == -1
+    assert lib.sc_set_quad(None, 1) == -1
     assert lib.sc_opt_destroy(None) == 0
     # the stateless mask calls validate before any GPU work
     k = ctypes.c_int()
