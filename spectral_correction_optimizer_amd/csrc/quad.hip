@@ -119,23 +119,25 @@ __device__ __forceinline__ double* quad_part(const MatDev& md, int g) {
 
 // ---------------------------------------------------------------------------------
 // Group Gram over operand columns [x0, x1) (at most 1024, a multiple of 128):
-// chunks of QGW = 256 columns pass through LDS (row = group row; a wave loads
-// one row's 1 KB per instruction); the next chunk's loads are issued as soon as
-// the current one is in LDS, so they are in flight during its products.  Wave w
-// forms the five tiles of its set (w / 4) over the chunk's columns 64 (w % 4) ..
-// + 63, so each wave sums at most 256 columns in float32; the four column
-// quarters of each tile are then summed in float64 in a fixed order into the
-// split's partial (tile-major, row-major).
+// chunks of 128 columns; each thread loads 8 consecutive columns of a row (16
+// threads per row: 512 contiguous bytes), splits them once into bfloat16 hi / mid
+// / lo and stores the three planes in LDS (row-major, MFMA fragment order), so the
+// product phase only reads fragments.  The next chunk's loads are issued as soon
+// as the current one is in LDS.  Wave w forms the five tiles of its set (w / 4)
+// over the chunk's columns 32 (w % 4) .. + 31 (two 16-column k-steps), so each
+// wave sums at most 256 columns in float32; the four column quarters of each tile
+// are then summed in float64 in a fixed order into the split's partial
+// (tile-major, row-major).
 namespace {
-constexpr int QGW = 256;        // columns per chunk of the group Gram
-constexpr int QGLD = QGW + 4;   // LDS row stride of a chunk
+constexpr int QGW = 128;        // columns per chunk of the group Gram
+constexpr int QGRS = QGW + 8;   // bfloat16 row stride of a plane (16-byte aligned rows)
 }  // namespace
 
 __global__ __launch_bounds__(512) void jac_quad_gram_kernel(const MatDev* __restrict__ mats,
                                                         const MatFlags* __restrict__ flags,
                                                         const FusedItem* __restrict__ items,
                                                         int pass) {
-    __shared__ __align__(16) float Ts[QN][QGLD];
+    __shared__ __align__(16) __bf16 Ps[3][QN * QGRS];
     const FusedItem it = items[blockIdx.x];
     if (flags[it.mat].done) return;
     const MatDev& md = mats[it.mat];
@@ -145,24 +147,21 @@ __global__ __launch_bounds__(512) void jac_quad_gram_kernel(const MatDev* __rest
     const __amdgpu_buffer_rsrc_t buf = buf_rsrc(md.A, (uint32_t)md.kpad * ld * 4u);
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hl = lane >> 5, ll = lane & 31;
-    // loader: wave w takes rows 16 w .. + 15, one row per instruction (16 bytes per lane)
-    int roff[16];
+    // loader: rows 32 u + tid / 16 (u < 4), columns 8 (tid % 16) .. + 7
+    const int lrow = threadIdx.x >> 4, lcol = 8 * (threadIdx.x & 15);
+    int roff[4];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int r = 16 * wave + j;
-        roff[j] = (gld(md.perm + blk[r >> 5] * kJb + (r & 31)) * ld + 4 * lane) * 4;
-    }
+    for (int u = 0; u < 4; ++u) roff[u] = (gld(md.perm + blk[u] * kJb + lrow) * ld + lcol) * 4;
     typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-    v4u x[16];
+    v4u x[8];
     auto load = [&](int c) {
         // wave-uniform: the buffer offset must be a scalar (else every load loops)
         const int c0 = it.x0 + c * QGW;
         const int so = __builtin_amdgcn_readfirstlane(c0 * 4);
-        const bool in = c0 + 4 * lane < it.x1;  // a ragged last chunk reads zeros past x1
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            x[j] = __builtin_amdgcn_raw_buffer_load_b128(buf, roff[j], so, kBufNT);
-            if (!in) x[j] = v4u{0u, 0u, 0u, 0u};
+        for (int u = 0; u < 4; ++u) {
+            x[2 * u] = __builtin_amdgcn_raw_buffer_load_b128(buf, roff[u], so, kBufNT);
+            x[2 * u + 1] = __builtin_amdgcn_raw_buffer_load_b128(buf, roff[u] + 16, so, kBufNT);
         }
     };
     const int set = wave >> 2, cq = wave & 3;
@@ -172,47 +171,68 @@ __global__ __launch_bounds__(512) void jac_quad_gram_kernel(const MatDev* __rest
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
     auto frag = [&](int b, int col) {
-        float f[8];
-        const v4f lo4 = *(const v4f*)&Ts[32 * b + ll][col], hi4 = *(const v4f*)&Ts[32 * b + ll][col + 4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            f[e] = lo4[e];
-            f[4 + e] = hi4[e];
-        }
-        return split8(f);
+        const int o = (32 * b + ll) * QGRS + col;
+        return Split8{*(const v8bf*)&Ps[0][o], *(const v8bf*)&Ps[1][o], *(const v8bf*)&Ps[2][o]};
     };
-    const int n = (it.x1 - it.x0 + QGW - 1) / QGW;
+    const int n = (it.x1 - it.x0) / QGW;
     load(0);
 #pragma unroll 1
     for (int c = 0; c < n; ++c) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) *(v4u*)&Ts[16 * wave + j][4 * lane] = x[j];
+        for (int u = 0; u < 4; ++u) {
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                f[e] = __uint_as_float(x[2 * u][e]);
+                f[4 + e] = __uint_as_float(x[2 * u + 1][e]);
+            }
+            const Split8 sp = split8(f);
+            const int o = (32 * u + lrow) * QGRS + lcol;
+            *(v8bf*)&Ps[0][o] = sp.h;
+            *(v8bf*)&Ps[1][o] = sp.m;
+            *(v8bf*)&Ps[2][o] = sp.l;
+        }
         __syncthreads();
         if (c + 1 < n) load(c + 1);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int col = 64 * cq + 16 * ks + 8 * hl;
+        for (int ks = 0; ks < 2; ++ks) {
+            const int col = 32 * cq + 16 * ks + 8 * hl;
+            // the five tiles' part products interleaved (independent accumulators
+            // back to back); each tile's six products in mfma_split6's order
+            Split8 fa[5], fb[5];
             if (set == 0) {
                 const Split8 f0 = frag(0, col), f1 = frag(1, col), f2 = frag(2, col), f3 = frag(3, col);
-                acc[0] = mfma_split6(f0, f0, acc[0]);
-                acc[1] = mfma_split6(f0, f1, acc[1]);
-                acc[2] = mfma_split6(f0, f2, acc[2]);
-                acc[3] = mfma_split6(f0, f3, acc[3]);
-                acc[4] = mfma_split6(f1, f1, acc[4]);
+                fa[0] = f0; fb[0] = f0;
+                fa[1] = f0; fb[1] = f1;
+                fa[2] = f0; fb[2] = f2;
+                fa[3] = f0; fb[3] = f3;
+                fa[4] = f1; fb[4] = f1;
             } else {
                 const Split8 f1 = frag(1, col), f2 = frag(2, col), f3 = frag(3, col);
-                acc[0] = mfma_split6(f1, f2, acc[0]);
-                acc[1] = mfma_split6(f1, f3, acc[1]);
-                acc[2] = mfma_split6(f2, f2, acc[2]);
-                acc[3] = mfma_split6(f2, f3, acc[3]);
-                acc[4] = mfma_split6(f3, f3, acc[4]);
+                fa[0] = f1; fb[0] = f2;
+                fa[1] = f1; fb[1] = f3;
+                fa[2] = f2; fb[2] = f2;
+                fa[3] = f2; fb[3] = f3;
+                fa[4] = f3; fb[4] = f3;
             }
+#pragma unroll
+            for (int t = 0; t < 5; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[t].l, fb[t].h, acc[t], 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < 5; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[t].m, fb[t].m, acc[t], 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < 5; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[t].h, fb[t].l, acc[t], 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < 5; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[t].m, fb[t].h, acc[t], 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < 5; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[t].h, fb[t].m, acc[t], 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < 5; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[t].h, fb[t].h, acc[t], 0, 0, 0);
         }
         __syncthreads();  // before the next chunk's rows
     }
     // column quarters in float64, quarter order; thread owns entries e = tid + 512 k
     // of the partial (tile e / 1024, MFMA output order within it)
-    float* red = &Ts[0][0];
+    float* red = (float*)&Ps[0][0];
     double sum[QPART / 512];
 #pragma unroll
     for (int k = 0; k < QPART / 512; ++k) sum[k] = 0.0;
