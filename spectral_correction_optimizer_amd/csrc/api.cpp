@@ -1396,8 +1396,12 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             // quad passes: every matrix of the list quad-capable (polishing keeps the
             // pair rounds: its selective sweeps work on marked block pairs)
             bool quad = which != LIST_POLISH;
+            int qgroups = 0;  // groups of a quad pass over the list
             for (int i : gm[g])
-                if (which != LIST_POLISH || h->mh[i].klen) quad = quad && quad_capable(h->mh[i].nb);
+                if (which != LIST_POLISH || h->mh[i].klen) {
+                    quad = quad && quad_capable(h->mh[i].nb);
+                    qgroups += h->mh[i].nb / 4;
+                }
             int pairs = 0;
             for (int i : gm[g])
                 if (which != LIST_POLISH || h->mh[i].klen) pairs += h->mh[i].nb / 2;
@@ -1425,7 +1429,10 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
                 const bool vrows = !(which == LIST_FACTOR && m.klen);  // V moves outside the factor phase
                 h->quadm[i][which == LIST_FACTOR && m.klen ? 0 : 1] = quad;
                 if (quad) {
-                    const int qns = (len + kQuadGramCols - 1) / kQuadGramCols;
+                    // group Gram splits: whole rows when the list's groups fill the chip,
+                    // else up to one per kQuadGramCols columns
+                    const int qns = std::min((len + kQuadGramCols - 1) / kQuadGramCols,
+                                             std::max(1, (kQuadGramFill + qgroups - 1) / std::max(qgroups, 1)));
                     const int qsl = round_up((len + qns - 1) / qns, 128);
                     const int span = kQuadRun * kQuadCols;
                     for (int grp = 0; grp < m.nb / 4; ++grp) {

@@ -20,7 +20,8 @@ constexpr int kV2Run = 4;     // chunks per two-round V apply workgroup
 constexpr int kQuadCols = 256;  // columns per chunk of the group apply (8 waves x 32)
 constexpr int kQuadThreads = 8 * 64;
 constexpr int kQuadRun = 4;     // chunks per group-apply workgroup
-constexpr int kQuadGramCols = 1024;  // largest column split of the group Gram
+constexpr int kQuadGramCols = 1024;  // column split of the group Gram when the groups are few
+constexpr int kQuadGramFill = 512;   // group Gram workgroups per pass that fill the chip
 // Block counts whose pair rounds split into quad passes: powers of four from 4 to 256.
 __host__ __device__ inline bool quad_capable(int nb) {
     return nb == 4 || nb == 16 || nb == 64 || nb == 256;

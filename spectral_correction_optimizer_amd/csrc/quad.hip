@@ -118,16 +118,16 @@ __device__ __forceinline__ double* quad_part(const MatDev& md, int g) {
 }  // namespace
 
 // ---------------------------------------------------------------------------------
-// Group Gram over operand columns [x0, x1) (at most 1024, a multiple of 128):
+// Group Gram over operand columns [x0, x1) (a multiple of 128):
 // chunks of 128 columns; each thread loads 8 consecutive columns of a row (16
 // threads per row: 512 contiguous bytes), splits them once into bfloat16 hi / mid
 // / lo and stores the three planes in LDS (row-major, MFMA fragment order), so the
 // product phase only reads fragments.  The next chunk's loads are issued as soon
 // as the current one is in LDS.  Wave w forms the five tiles of its set (w / 4)
-// over the chunk's columns 32 (w % 4) .. + 31 (two 16-column k-steps), so each
-// wave sums at most 256 columns in float32; the four column quarters of each tile
-// are then summed in float64 in a fixed order into the split's partial
-// (tile-major, row-major).
+// over the chunk's columns 32 (w % 4) .. + 31 (two 16-column k-steps); after every
+// 8 chunks (so each wave sums at most 256 columns in float32) the four column
+// quarters of each tile are added in float64 in a fixed order to the split's
+// sums, written at the end as its partial (tile-major, row-major).
 namespace {
 constexpr int QGW = 128;        // columns per chunk of the group Gram
 constexpr int QGRS = QGW + 8;   // bfloat16 row stride of a plane (16-byte aligned rows)
@@ -175,6 +175,33 @@ __global__ __launch_bounds__(512) void jac_quad_gram_kernel(const MatDev* __rest
         return Split8{*(const v8bf*)&Ps[0][o], *(const v8bf*)&Ps[1][o], *(const v8bf*)&Ps[2][o]};
     };
     const int n = (it.x1 - it.x0) / QGW;
+    // float64 sums of the four column quarters, folded in after every 8 chunks (each
+    // wave then has summed at most 256 columns in float32); thread owns entries
+    // e = tid + 512 k of the partial (tile e / 1024, MFMA output order within it)
+    float* red = (float*)&Ps[0][0];
+    double sum[QPART / 512];
+#pragma unroll
+    for (int k = 0; k < QPART / 512; ++k) sum[k] = 0.0;
+    auto fold = [&]() {
+#pragma unroll 1
+        for (int qq = 0; qq < 4; ++qq) {
+            if (cq == qq)
+#pragma unroll
+                for (int t = 0; t < 5; ++t)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4)
+                        *(v4f*)&red[((5 * set + t) * 64 + lane) * 16 + 4 * r4] =
+                            v4f{acc[t][4 * r4], acc[t][4 * r4 + 1], acc[t][4 * r4 + 2], acc[t][4 * r4 + 3]};
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < QPART / 512; ++k) sum[k] += (double)red[threadIdx.x + 512 * k];
+            __syncthreads();
+        }
+#pragma unroll
+        for (int t = 0; t < 5; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+    };
     load(0);
 #pragma unroll 1
     for (int c = 0; c < n; ++c) {
@@ -229,26 +256,7 @@ __global__ __launch_bounds__(512) void jac_quad_gram_kernel(const MatDev* __rest
             for (int t = 0; t < 5; ++t) acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[t].h, fb[t].h, acc[t], 0, 0, 0);
         }
         __syncthreads();  // before the next chunk's rows
-    }
-    // column quarters in float64, quarter order; thread owns entries e = tid + 512 k
-    // of the partial (tile e / 1024, MFMA output order within it)
-    float* red = (float*)&Ps[0][0];
-    double sum[QPART / 512];
-#pragma unroll
-    for (int k = 0; k < QPART / 512; ++k) sum[k] = 0.0;
-#pragma unroll 1
-    for (int qq = 0; qq < 4; ++qq) {
-        if (cq == qq)
-#pragma unroll
-            for (int t = 0; t < 5; ++t)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4)
-                    *(v4f*)&red[((5 * set + t) * 64 + lane) * 16 + 4 * r4] =
-                        v4f{acc[t][4 * r4], acc[t][4 * r4 + 1], acc[t][4 * r4 + 2], acc[t][4 * r4 + 3]};
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < QPART / 512; ++k) sum[k] += (double)red[threadIdx.x + 512 * k];
-        __syncthreads();
+        if ((c & 7) == 7 || c + 1 == n) fold();
     }
     double* out = quad_part(md, it.group) + (int64_t)it.split * QPART;
 #pragma unroll
