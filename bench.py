@@ -122,16 +122,20 @@ def copy_calibration(nbytes):
 # differ while the ratio does not).  Keyed by the kernel source (sha256), the
 # workload and the pass schedule; anything else is reported as null.
 TRAFFIC = {
-    "jacobi_apply_gram": [{"source": "jacobi.hip", "workload": "blocks16_1b", "warmup": 5, "steps": 20,
-                           "sha256": "3f360f51648a4d159ed3f3ea1f6258de9dbadf5f4bb9ef00db0fcb9b35a4974c",
-                           "ratio": 1.075,  # 935.1 MB counted / 869.6 MB algorithmic per launch, 25434 dispatches
-                           }],
+    "quad_apply": [{"source": "quad.hip", "workload": "blocks16_1b", "warmup": 5, "steps": 20,
+                    "sha256": "87ba78a92d435b454b626695c4977576949426a864dffaa05d2fa0a15a507087",
+                    "ratio": 1.0405,  # 1427.4 MB counted / 1371.8 MB algorithmic per launch, 8190 dispatches
+                    }],
+    "quad_gram": [{"source": "quad.hip", "workload": "blocks16_1b", "warmup": 5, "steps": 20,
+                   "sha256": "87ba78a92d435b454b626695c4977576949426a864dffaa05d2fa0a15a507087",
+                   "ratio": 1.0834,  # 556.2 MB counted (float64 partials included) / 513.4 MB algorithmic
+                   }],
     "combine_adamw": [{"source": "elementwise.hip", "workload": "blocks16_1b", "warmup": 5, "steps": 20,
-                       "sha256": "8323014c23791afa0e6cdf2b0d6afafb08af0cf832ff6b2a0513e605c6b3e64b",
+                       "sha256": "9cc82042d998df956f80bc6a1b0f3e910778b84d9cd6a62faa1e280899c2c30e",
                        "ratio": 1.0049,  # 31.291 GB counted / 31.139 GB algorithmic per launch
                        }],
     "ema": [{"source": "elementwise.hip", "workload": "blocks16_1b", "warmup": 5, "steps": 20,
-             "sha256": "8323014c23791afa0e6cdf2b0d6afafb08af0cf832ff6b2a0513e605c6b3e64b",
+             "sha256": "9cc82042d998df956f80bc6a1b0f3e910778b84d9cd6a62faa1e280899c2c30e",
              "ratio": 1.0130,  # 11.829 GB counted / 11.677 GB algorithmic per launch
              }],
 }
@@ -521,8 +525,8 @@ def main():
         name, d = dom
         per_launch_s = d["total_ms"] / d["launches"] / 1e3
         ratio = traffic_ratio(name, args.workload, args.warmup, args.steps) if live_kt else None
-        if name in ("jacobi_apply", "jacobi_apply_gram", "ema", "combine_adamw", "jacobi_load",
-                    "rownorm", "normalize"):
+        if name in ("jacobi_apply", "jacobi_apply_gram", "quad_apply", "quad_gram", "ema",
+                    "combine_adamw", "jacobi_load", "rownorm", "normalize"):
             ach = d["bytes"] / d["launches"] / per_launch_s / 1e9
             bpl = d["bytes"] / d["launches"]
             roofline = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1),
