@@ -77,9 +77,10 @@ def parse():
                     help="rounds of V-row rotations per pass over V in the fused sweeps")
     ap.add_argument("--sweep-stop", type=float, default=1e-4,
                     help="sweep-stop rule of the Jacobi sweeps (0 = off), certificate-checked")
-    ap.add_argument("--quad", type=int, default=1, choices=[0, 1],
+    ap.add_argument("--quad", type=int, default=1, choices=[0, 1, 2],
                     help="quad passes of the Jacobi sweeps (three pair rounds per pass over "
-                         "groups of four column blocks) where the block counts allow")
+                         "groups of four column blocks): 0 off, 1 where the block counts allow "
+                         "and the groups fill the GPU, 2 wherever the block counts allow")
     ap.add_argument("--no-fused-gram", action="store_true",
                     help="every Jacobi round's pair Gram from the operand (no fused apply + Gram)")
     ap.add_argument("--cold-start", action="store_true",
@@ -433,7 +434,7 @@ def main():
     opt.set_fused_gram(not args.no_fused_gram)
     opt.set_v_rounds(args.v_rounds)
     opt.set_sweep_stop(args.sweep_stop)
-    opt.set_quad(bool(args.quad))
+    opt.set_quad(args.quad)
     for i, mi in enumerate(src):
         opt.set_state(i, "m_anc", mi.m0())
 

@@ -262,7 +262,7 @@ int sc_set_v_rounds(sc_handle h, int rounds);
  * the results meet the same convergence threshold either way. */
 int sc_set_sweep_stop(sc_handle h, float stop);
 
-/* Quad passes of the Jacobi sweeps (default on): for matrices whose column-block
+/* Quad passes of the Jacobi sweeps (mode 1, the default): for matrices whose column-block
  * count nb (k rounded up to 64, over 32) is 4, 16, 64 or 256, the nb - 1 pair
  * rounds of a sweep are taken three at a time: the masks of the XOR rounds
  * split into lines {m0, m1, m0 ^ m1}, whose three rounds pair blocks inside
@@ -271,13 +271,16 @@ int sc_set_sweep_stop(sc_handle h, float stop);
  * rotated one) and applies their product to the group's rows: one read of the
  * operand for the Gram and one read and write for the rotation per three
  * rounds.  Every block pair is still solved once per sweep, in another order;
- * the results meet the same convergence threshold.  enable = 0 keeps the pair
- * rounds.  A list of matrices (a refresh pipeline's plain or factor-phase set)
- * runs quad passes only when all its block counts allow it; polishing sweeps
- * keep the pair rounds.  Waits for a pending asynchronous refresh.  A schedule
+ * the results meet the same convergence threshold.  A list of matrices (a
+ * refresh pipeline's plain or factor-phase set) runs quad passes only when all
+ * its block counts allow it; mode 1 also requires at least 256 groups of four
+ * blocks per pass (a group's three rounds run in sequence, so fewer groups leave
+ * the GPU idle), mode 2 takes them wherever the block counts allow, mode 0
+ * keeps the pair rounds.  Polishing sweeps keep the pair rounds.  Other modes:
+ * SC_ERR_INVALID_ARG.  Waits for a pending asynchronous refresh.  A schedule
  * of the thin SVD of the anchor momentum ("Key design 3" of the papernotes.org
  * notes). */
-int sc_set_quad(sc_handle h, int enable);
+int sc_set_quad(sc_handle h, int mode);
 
 /* Keep G_proj of each step (costs one more store per element in the AdamW
  * pass and rows x cols floats per matrix). */

@@ -305,10 +305,11 @@ class SpectralAdamW:
         the result."""
         _check(self._lib.sc_set_sweep_stop(self._h, float(stop)))
 
-    def set_quad(self, enable: bool = True):
-        """Quad passes of the Jacobi sweeps (default on): three pair rounds per
-        pass over groups of four column blocks, where the block counts allow."""
-        _check(self._lib.sc_set_quad(self._h, 1 if enable else 0))
+    def set_quad(self, mode: int = 1):
+        """Quad passes of the Jacobi sweeps (three pair rounds per pass over groups
+        of four column blocks): 0 off, 1 (default) where a list's block counts
+        allow and its groups fill the GPU, 2 wherever the block counts allow."""
+        _check(self._lib.sc_set_quad(self._h, int(mode)))
 
     def keep_proj(self, enable: bool = True):
         _check(self._lib.sc_keep_proj(self._h, 1 if enable else 0))

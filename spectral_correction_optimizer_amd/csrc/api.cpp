@@ -181,8 +181,9 @@ struct sc_opt {
         int nav = 0;
         bool all_fused = false;  // every matrix of the list has the fused apply + Gram
         // quad passes (every matrix's block count quad_capable, not polishing): group
-        // Grams, group solves, group applies (A and V rows)
-        bool quad = false;
+        // Grams, group solves, group applies (A and V rows); quad_auto: also enough
+        // groups per pass to fill the GPU (kQuadMinGroups)
+        bool quad = false, quad_auto = false;
         FusedItem* qg = nullptr;
         int nqg = 0;
         SolveItem* qs = nullptr;
@@ -258,8 +259,8 @@ struct sc_opt {
     int v_rounds = 2;                         // fused matrices' V rows: rounds per pass (1 or 2)
     float sweep_stop = 1e-4f;                 // sweep-stop rule (0 = off), see jac_sweep_end_kernel
     std::vector<std::array<char, 2>> fused;   // per matrix: fused over the factor / full rows
-    bool quad = true;                         // quad passes where a list allows them
-    std::vector<std::array<char, 2>> quadm;   // per matrix: quad passes over the factor / full rows
+    int quad_mode = 1;                        // quad passes: 0 off, 1 where a list fills the GPU, 2 where allowed
+    std::vector<std::array<char, 2>> quadm;   // per matrix, factor / full rows: 1 quad-capable list, 2 also filling
     int solve_waves = 0, solve_copies = 0;  // pair solve variant: 0 by the launch's pair count
     std::vector<void*> dev_allocs;
     Prof prof;
@@ -514,7 +515,8 @@ void account_sweeps(sc_opt* h, const MatFlags* flags) {
         }
         const double quads[2] = {(double)f.quads_pre, (double)(f.quads_applied - f.quads_pre)};
         for (int ph = 0; ph < 2; ++ph) {
-            if (h->quad && h->quadm[i][ph]) {
+            const int qm = h->quadm[i][ph];
+            if (h->quad_mode == 2 ? qm >= 1 : h->quad_mode == 1 ? qm == 2 : false) {
                 // quad passes: every group's 128 rows read by the group Gram every pass
                 // (ten 32 x 32 tiles); the solve's pair sweeps as in the pair rounds; a
                 // group with a rotation has its 128 rows of the operand and of V read and
@@ -602,12 +604,17 @@ int pipe_pre(sc_opt* h, Pipe& p, hipStream_t st, bool warm) {
 // Rounds of list set `which` until every matrix of the pipe is done.  The host
 // polls once per `rps` rounds: a sweep of the largest matrix still in work
 // (max_nb; 0 = the largest of the list).  Each matrix counts its own sweeps.
+// Quad passes for this list under the handle's mode.
+bool use_quad(const sc_opt* h, const sc_opt::Lists& L) {
+    return h->quad_mode == 2 ? L.quad : h->quad_mode == 1 ? L.quad_auto : false;
+}
+
 void pipe_start_rounds(sc_opt* h, Pipe& p, int which, int first_check_sweeps, int max_nb = 0) {
     p.stage = STAGE_ROUNDS;
     p.which = which;
     p.r = 0;
     const int nbl = max_nb ? max_nb : p.L[which].max_nb;
-    p.rps = (h->quad && p.L[which].quad) ? quad_passes(nbl) : std::max(1, nbl - 1);
+    p.rps = use_quad(h, p.L[which]) ? quad_passes(nbl) : std::max(1, nbl - 1);
     const int cap = p.targeted ? std::min(kSelSweeps, h->hp.max_sweeps) : h->hp.max_sweeps;
     p.max_rounds = p.L[which].nmat ? cap * p.rps : 0;
     p.first_check = std::min(p.max_rounds, first_check_sweeps * p.rps);
@@ -661,7 +668,7 @@ int pipe_quad_pass(sc_opt* h, Pipe& p, hipStream_t st) {
 
 int pipe_round(sc_opt* h, Pipe& p, hipStream_t st) {
     const sc_opt::Lists& L = p.L[p.which];
-    if (h->quad && L.quad) return pipe_quad_pass(h, p, st);
+    if (use_quad(h, L)) return pipe_quad_pass(h, p, st);
     const int r = p.r;
     // the sort acts on the first round of a matrix's sweep, the sweep end on its
     // last: launched only in rounds where some matrix of the list has one
@@ -1402,6 +1409,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
                     quad = quad && quad_capable(h->mh[i].nb);
                     qgroups += h->mh[i].nb / 4;
                 }
+            const bool qfill = qgroups >= kQuadMinGroups;
             int pairs = 0;
             for (int i : gm[g])
                 if (which != LIST_POLISH || h->mh[i].klen) pairs += h->mh[i].nb / 2;
@@ -1427,7 +1435,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
                 h->fused[i][which == LIST_FACTOR && m.klen ? 0 : 1] = fuse;
                 any_unfused = any_unfused || !fuse;
                 const bool vrows = !(which == LIST_FACTOR && m.klen);  // V moves outside the factor phase
-                h->quadm[i][which == LIST_FACTOR && m.klen ? 0 : 1] = quad;
+                h->quadm[i][which == LIST_FACTOR && m.klen ? 0 : 1] = quad ? (qfill ? 2 : 1) : 0;
                 if (quad) {
                     // group Gram splits: whole rows when the list's groups fill the chip,
                     // else up to one per kQuadGramCols columns
@@ -1489,6 +1497,7 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             if ((rc = upload(qs, &L.qs, &L.nqs))) return rc;
             if ((rc = upload(qa, &L.qa, &L.nqa))) return rc;
             L.quad = quad && !mats.empty();
+            L.quad_auto = L.quad && qfill;
             L.all_fused = !mats.empty() && !any_unfused;
             if ((rc = upload(mats, &L.mats, &L.nmat))) return rc;
         }
@@ -2084,12 +2093,13 @@ int sc_set_sweep_stop(sc_handle h, float stop) {
     return SC_OK;
 }
 
-int sc_set_quad(sc_handle h, int enable) {
+int sc_set_quad(sc_handle h, int mode) {
     int rc;
     if ((rc = check_handle(h))) return rc;
+    if (mode < 0 || mode > 2) return fail(SC_ERR_INVALID_ARG, "quad mode must be 0, 1 or 2");
     DeviceGuard g(h->device);
     if ((rc = finish_async(h, nullptr, true))) return rc;
-    h->quad = enable != 0;
+    h->quad_mode = mode;
     return SC_OK;
 }
 

@@ -22,6 +22,12 @@ constexpr int kQuadThreads = 8 * 64;
 constexpr int kQuadRun = 4;     // chunks per group-apply workgroup
 constexpr int kQuadGramCols = 1024;  // column split of the group Gram when the groups are few
 constexpr int kQuadGramFill = 512;   // group Gram workgroups per pass that fill the chip
+// A list runs quad passes only with at least this many groups per pass: a group's
+// three rounds run in sequence on one CU, so fewer groups leave the chip idle (one
+// 2048 x 2048 matrix, 16 groups: 63.6 ms per pass against 46.6 in pair rounds; one
+// Llama-3.2-1B block, 56 groups: 87.9 against 79.7; 16 blocks, 512 + 896: 590
+// against 625).
+constexpr int kQuadMinGroups = 256;
 // Block counts whose pair rounds split into quad passes: powers of four from 4 to 256.
 __host__ __device__ inline bool quad_capable(int nb) {
     return nb == 4 || nb == 16 || nb == 64 || nb == 256;

@@ -42,7 +42,9 @@ def test_quad_passes_against_oracle(quad):
                   anchor_every=2)
 
     def setup(opt):
-        opt.set_quad(bool(quad))
+        # mode 2: quad passes wherever the block counts allow (these lists are
+        # below the group count of the default mode)
+        opt.set_quad(2 if quad else 0)
         opt.profile(True)
 
     rep = sc.run(setup=setup)
@@ -67,6 +69,28 @@ def test_quad_passes_need_every_block_count():
     shapes = [(512, 512), (512, 512), (256, 256), (256, 256)]
     say(f"case: {shapes} (nb 16 and 8), one refresh, 2 steps")
     sc = Scenario(shapes, [(212, 0, i) for i in range(len(shapes))], steps=2)
-    rep = sc.run(setup=lambda opt: opt.profile(True))
+    def setup(opt):
+        opt.set_quad(2)
+        opt.profile(True)
+
+    rep = sc.run(setup=setup)
+    Scenario.check(rep)
+    assert _launches(rep, "quad_gram") == 0 and _launches(rep, "jacobi_solve") > 0
+
+
+def test_default_mode_needs_enough_groups():
+    """The default mode (1) keeps the pair rounds for lists with fewer than 256
+    groups per pass (these shapes: 13); modes outside 0-2 are rejected."""
+    import spectral_correction_optimizer_amd as sco
+    say(f"case: default quad mode on {QUAD_SHAPES}, one refresh, 2 steps")
+    sc = Scenario(QUAD_SHAPES, [(213, 0, i) for i in range(len(QUAD_SHAPES))], steps=2)
+
+    def setup(opt):
+        for bad in (-1, 3):
+            with pytest.raises(sco.ScoptError):
+                opt.set_quad(bad)
+        opt.profile(True)
+
+    rep = sc.run(setup=setup)
     Scenario.check(rep)
     assert _launches(rep, "quad_gram") == 0 and _launches(rep, "jacobi_solve") > 0
