@@ -329,7 +329,8 @@ def mask_bench(reps):
     """The in-graph activation mask at one pipeline boundary of the Llama-3.2-1B
     setting (batch 32 x context 2048 tokens, hidden 2048, mask rate 0.95):
     HIP-event times of sc_mask_indices, sc_mask_pack and sc_mask_unpack on the
-    caller's stream (bf16 and fp32 payloads), algorithmic bytes of pack/unpack."""
+    caller's stream (bf16 and fp32 payloads), algorithmic bytes of pack/unpack,
+    and the 128-byte lines the pack's gather reads."""
     import torch
 
     import spectral_correction_optimizer_amd as sco
@@ -362,7 +363,16 @@ def mask_bench(reps):
         t_unp = timed(lambda: sco.mask_unpack(v, idx, H))
         b_pack = T * K * (2 * es + 4)           # read kept values and indices, write packed
         b_unp = T * K * (es + 4) + T * H * es   # read packed values and indices, write dense rows
+        # pack gathers: HBM serves whole 128-byte lines, and a line of a row is read when
+        # any of the K kept dimensions (K distinct of H) falls in it
+        per_line = 128 // es
+        p_none = 1.0
+        for i in range(K):
+            p_none *= max(H - per_line - i, 0) / (H - i)
+        b_lines = int(T * (H / per_line) * (1.0 - p_none) * 128) + T * K * (es + 4)
         res[name] = {"pack_ms": round(t_pack, 4), "pack_gbps": round(b_pack / (t_pack * 1e6), 1),
+                     "pack_line_bytes": b_lines, "pack_line_gbps": round(b_lines / (t_pack * 1e6), 1),
+                     "pack_line_frac_hbm": round(b_lines / (t_pack * 1e6) / PEAK_HBM_GBPS, 4),
                      "unpack_ms": round(t_unp, 4), "unpack_gbps": round(b_unp / (t_unp * 1e6), 1),
                      "unpack_frac_hbm": round(b_unp / (t_unp * 1e6) / PEAK_HBM_GBPS, 4),
                      "bytes_pack": b_pack, "bytes_unpack": b_unp}

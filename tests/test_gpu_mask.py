@@ -20,10 +20,11 @@ def _gpu():
 
 # one-wavefront kernel with 64 / 128 / 256 / 512 candidates per token: (50, 1000, 1),
 # (37, 100, 13), (64, 2048, 102), (16, 4096, 205); one workgroup sorting all H:
-# (1, 1, 1), (37, 100, 100), (5, 3000, 1500), (8, 2048, 300), (3, 2, 1)
+# (1, 1, 1), (37, 100, 100), (5, 3000, 1500), (8, 2048, 300), (3, 2, 1); more tokens
+# than unpack workgroups (9000), so LDS rows are reused, with 16-byte and element stores
 @pytest.mark.parametrize("T,H,K", [(1, 1, 1), (37, 100, 0), (37, 100, 100), (37, 100, 13), (64, 2048, 102),
                                    (16, 4096, 205), (5, 3000, 1500), (300, 257, 31), (3, 2, 1),
-                                   (50, 1000, 1), (40, 512, 5), (8, 2048, 300)])
+                                   (50, 1000, 1), (40, 512, 5), (8, 2048, 300), (9000, 64, 3), (9000, 97, 9)])
 def test_indices_pack_unpack_exact(T, H, K):
     import spectral_correction_optimizer_amd as sco
     say(f"case: mask T {T} H {H} K {K}")
