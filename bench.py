@@ -622,6 +622,11 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
     }
+    if live_kt and kt_alone:
+        # the extra pass: each kernel's total with every kernel alone on one stream
+        out["kernels_alone_ms"] = {n: round(d["total_ms"], 3) for n, d in
+                                   sorted(kt_alone.items(), key=lambda kv: -kv[1]["total_ms"])}
+        out["kernels_alone_sum_ms"] = round(sum(d["total_ms"] for d in kt_alone.values()), 2)
     if async_info is not None:
         async_info["sequential_ms"] = round(r_med + args.async_refresh * async_info["step_ms_alone"], 2)
         out["async_refresh"] = async_info

@@ -186,18 +186,42 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 struct Split8 {
     v8bf h, m, l;
 };
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+// Two floats rounded to bfloat16 (nearest even) in one instruction
+// (v_cvt_pk_bf16_f32), packed low / high; the parts read back as floats by a
+// shift and a mask.
+__device__ __forceinline__ unsigned int pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(unsigned int, __builtin_convertvector((v2f){a, b}, v2bf));
+}
+__device__ __forceinline__ float bf16_lo(unsigned int p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned int p) { return __uint_as_float(p & 0xffff0000u); }
+// f = h + m + l exactly: h = bf16(f), m = bf16(f - h), l = bf16(f - h - m), each
+// rounded to nearest even, two elements per conversion
 __device__ __forceinline__ Split8 split8(const float (&f)[8]) {
-    Split8 s;
+    v4u h, m, l;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const __bf16 h = (__bf16)f[i];
-        const float r1 = f[i] - (float)h;
-        const __bf16 m = (__bf16)r1;
-        s.h[i] = h;
-        s.m[i] = m;
-        s.l[i] = (__bf16)(r1 - (float)m);
+    for (int i = 0; i < 4; ++i) {
+        const unsigned int hp = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+        const float r0 = f[2 * i] - bf16_lo(hp), r1 = f[2 * i + 1] - bf16_hi(hp);
+        const unsigned int mp = pack_bf16x2(r0, r1);
+        h[i] = hp;
+        m[i] = mp;
+        l[i] = pack_bf16x2(r0 - bf16_lo(mp), r1 - bf16_hi(mp));
     }
-    return s;
+    return Split8{__builtin_bit_cast(v8bf, h), __builtin_bit_cast(v8bf, m), __builtin_bit_cast(v8bf, l)};
+}
+// the first two parts only (|f - h - m| <= 2^-16 |f|)
+__device__ __forceinline__ void split8_hm(const float (&f)[8], v8bf& hv, v8bf& mv) {
+    v4u h, m;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const unsigned int hp = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+        h[i] = hp;
+        m[i] = pack_bf16x2(f[2 * i] - bf16_lo(hp), f[2 * i + 1] - bf16_hi(hp));
+    }
+    hv = __builtin_bit_cast(v8bf, h);
+    mv = __builtin_bit_cast(v8bf, m);
 }
 
 // LDS layout of a split operand tile: per plane, rows of 16 k (k contiguous) as

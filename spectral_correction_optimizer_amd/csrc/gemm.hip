@@ -87,11 +87,7 @@ struct TileLoader {
             *(v8bf*)&S[2][o] = s.l;
         } else {
             v8bf h, m;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                h[j] = (__bf16)f[j];
-                m[j] = (__bf16)(f[j] - (float)h[j]);
-            }
+            split8_hm(f, h, m);
             *(v8bf*)&S[0][o] = h;
             *(v8bf*)&S[1][o] = m;
         }

@@ -152,7 +152,6 @@ __global__ __launch_bounds__(512) void jac_quad_gram_kernel(const MatDev* __rest
     int roff[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) roff[u] = (gld(md.perm + blk[u] * kJb + lrow) * ld + lcol) * 4;
-    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
     v4u x[8];
     auto load = [&](int c) {
         // wave-uniform: the buffer offset must be a scalar (else every load loops)
