@@ -603,20 +603,16 @@ __global__ __launch_bounds__(kQuadThreads) void jac_quad_apply_kernel(const MatD
     const __amdgpu_buffer_rsrc_t buf = buf_rsrc(it.which ? md.V : md.A, (uint32_t)md.kpad * ld * 4u);
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hl = lane >> 5, ll = lane & 31;
-    // lane's rows: 16 of each block (apply_row(e, hl), e < 16), two physical row
-    // numbers (< 2^16) per register; byte offset row * 4 ld + 4 ll
-    unsigned int rows2[4][8];
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            rows2[b][e] = (unsigned int)gld(md.perm + blk[b] * kJb + apply_row(2 * e, hl)) |
-                          ((unsigned int)gld(md.perm + blk[b] * kJb + apply_row(2 * e + 1, hl)) << 16);
-    const unsigned int ld4 = 4u * ld, ll4 = 4u * ll;
-    auto voff = [&](int b, int e) {
-        const unsigned int r = (e & 1) ? rows2[b][e >> 1] >> 16 : rows2[b][e >> 1] & 0xffffu;
-        return (int)(__umul24(r, ld4) + ll4);
-    };
+    // byte offsets row * 4 ld of the group's rows in the lanes' order: [block][lane
+    // half][e] holds row apply_row(e, hl) of the block (16 per half)
+    __shared__ __align__(16) unsigned int roff[4][2][16];
+    if (threadIdx.x < 128) {
+        const int b = threadIdx.x >> 5, h = (threadIdx.x >> 4) & 1, e = threadIdx.x & 15;
+        roff[b][h][e] = (unsigned int)gld(md.perm + blk[b] * kJb + apply_row(e, h)) * (4u * ld);
+    }
+    __syncthreads();
+    const unsigned int ll4 = 4u * ll;
+    auto rows4 = [&](int b, int q) { return *(const v4u*)&roff[b][hl][4 * q]; };
     auto col0 = [&](int c) { return it.x0 + c * kQuadCols + wave * 32; };
     auto load = [&](float (&x)[4][16], int c) {
         if (col0(c) >= it.x1) return;
@@ -624,33 +620,41 @@ __global__ __launch_bounds__(kQuadThreads) void jac_quad_apply_kernel(const MatD
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) x[b][e] = buf_load_f32<kBufNT>(buf, voff(b, e), so);
+            for (int q = 0; q < 4; ++q) {
+                const v4u ro = rows4(b, q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[b][4 * q + e] = buf_load_f32<kBufNT>(buf, (int)(ro[e] + ll4), so);
+            }
     };
     auto update = [&](const float (&x)[4][16], int c) {
         if (col0(c) >= it.x1) return;
         const int so = __builtin_amdgcn_readfirstlane(col0(c) * 4);
+        v16f acc[4];
 #pragma unroll
-        for (int U = 0; U < 4; ++U) {
-            v16f acc;
+        for (int U = 0; U < 4; ++U)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+            for (int r = 0; r < 16; ++r) acc[U][r] = 0.0f;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                float f[8];
+        for (int t = 0; t < 8; ++t) {
+            float f[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    f[e] = x[t >> 1][8 * (t & 1) + e];
-                    // the split is formed again for each tile instead of being
-                    // kept for all four (96 registers)
-                    __asm__ volatile("" : "+v"(f[e]));
-                }
-                const Split8 xs = split8(f);
+            for (int e = 0; e < 8; ++e) f[e] = x[t >> 1][8 * (t & 1) + e];
+            const Split8 xs = split8(f);
+#pragma unroll
+            for (int U = 0; U < 4; ++U) {
                 const Split8 r0{Rp[U][0][t][lane], Rp[U][1][t][lane], Rp[U][2][t][lane]};
-                acc = mfma_split6(r0, xs, acc);
+                acc[U] = mfma_split6(r0, xs, acc[U]);
             }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) buf_store_f32<kBufNT>(x[U][r] + acc[r], buf, voff(U, r), so);
         }
+#pragma unroll
+        for (int U = 0; U < 4; ++U)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const v4u ro = rows4(U, q);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    buf_store_f32<kBufNT>(x[U][4 * q + e] + acc[U][4 * q + e], buf, (int)(ro[e] + ll4), so);
+            }
     };
     float xa[4][16], xb[4][16];
     load(xa, 0);
