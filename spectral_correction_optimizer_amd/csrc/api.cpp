@@ -359,11 +359,18 @@ bool group_vec(const GemmGroup& g, const PtrTable& pt) {
     return true;
 }
 
+// Whether every problem of a group tiles exactly (M, N, K multiples of the tile).
+bool group_full(const GemmGroup& g) {
+    for (const GemmProb& p : g.h)
+        if (p.M % kGemmBM || p.N % kGemmBN || p.K % 16) return false;
+    return true;
+}
+
 int run_group(sc_opt* h, const GemmGroup& g, int kind, const PtrTable& pt, hipStream_t st) {
     if (g.h.empty()) return SC_OK;
-    const bool vec = group_vec(g, pt);
+    const bool vec = group_vec(g, pt), full = group_full(g);
     HIP_TRY(timed(h, kind, st, [&] {
-        return launch_gemm(g.d, (int)g.h.size(), g.total, g.ta, g.tb, g.abf, g.bbf, vec, g.parts,
+        return launch_gemm(g.d, (int)g.h.size(), g.total, g.ta, g.tb, g.abf, g.bbf, vec, full, g.parts,
                            pt, st);
     }));
     if (h->prof.on) h->prof.flops[kind] += group_flops(g);

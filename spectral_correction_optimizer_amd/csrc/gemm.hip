@@ -37,9 +37,10 @@ static_assert(BK == 16, "split_chunk16 lays out 16 k per row");
 //     consecutive rows.
 // Every load is issued (addresses clamped into the operand; rows, kdim >= 1)
 // and elements outside it are zeroed when the tile is stored, so loading is
-// free of per-lane branches.  KS: the loader also fetches the k scales of its
-// 8 values when the problem has them.
-template <bool KMAJOR, bool VEC, bool KS, typename T>
+// free of per-lane branches.  FULL: every tile lies inside its operand (rows
+// and K multiples of the tile), so nothing is clamped or zeroed.  KS: the
+// loader also fetches the k scales of its 8 values when the problem has them.
+template <bool KMAJOR, bool VEC, bool KS, bool FULL, typename T>
 struct TileLoader {
     float v[8], ks[KS ? 8 : 1];
     int row, half, rr, kk;
@@ -49,23 +50,24 @@ struct TileLoader {
         half = KMAJOR ? (threadIdx.x >> 7) : (threadIdx.x & 1);
         rr = r0 + row;
         kk = k0 + 8 * half;
-        const int rc = min(rr, rows - 1);
+        const int rc = FULL ? rr : min(rr, rows - 1);
+        auto kc = [&](int k) { return FULL ? k : min(k, kdim - 1); };
         if (!KMAJOR && VEC) {
-            const T* q = p + (int64_t)rc * ld + min(kk, kdim - 8);
+            const T* q = p + (int64_t)rc * ld + (FULL ? kk : min(kk, kdim - 8));
             const float4 a = load4(q), b = load4(q + 4);
             v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
             v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
         } else if (!KMAJOR) {
             const T* q = p + (int64_t)rc * ld;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = Elem<T>::load(q, min(kk + j, kdim - 1));
+            for (int j = 0; j < 8; ++j) v[j] = Elem<T>::load(q, kc(kk + j));
         } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = Elem<T>::load(p, (int64_t)min(kk + j, kdim - 1) * ld + rc);
+            for (int j = 0; j < 8; ++j) v[j] = Elem<T>::load(p, (int64_t)kc(kk + j) * ld + rc);
         }
         if (KS && kscale) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) ks[j] = gld(kscale + min(kk + j, kdim - 1));
+            for (int j = 0; j < 8; ++j) ks[j] = gld(kscale + kc(kk + j));
         }
     }
     // NP = 3: the exact three-way split; NP = 2: hi and mid parts only
@@ -75,7 +77,7 @@ struct TileLoader {
         float f[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            float x = (rr < rows && kk + j < kdim) ? v[j] : 0.0f;
+            float x = (FULL || (rr < rows && kk + j < kdim)) ? v[j] : 0.0f;
             if (KS && scaled) x *= ks[KS ? j : 0];
             f[j] = x;
         }
@@ -111,7 +113,7 @@ struct TileLoader {
 // a correction added to X whose entries |E_ij| are at or below the convergence
 // threshold (~1e-6), so the error relative to X stays at or below float32
 // rounding.
-template <int NP, bool TA, bool TB, bool VEC, typename TEA, typename TEB>
+template <int NP, bool TA, bool TB, bool VEC, bool FULL, typename TEA, typename TEB>
 __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __restrict__ probs,
                                                               int nprob, PtrTable ptrs) {
     static_assert(NP == 2 || NP == 3, "two or three bfloat16 parts per operand");
@@ -137,8 +139,8 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
 
     // A: [M][K] unless transposed; B: [K][N] unless transposed ([N][K]).
     // A's 256 tile rows take two loaders (rows 0-127 and 128-255).
-    TileLoader<TA, VEC, false, TEA> la0, la1;
-    TileLoader<!TB, VEC, true, TEB> lb;
+    TileLoader<TA, VEC, false, FULL, TEA> la0, la1;
+    TileLoader<!TB, VEC, true, FULL, TEB> lb;
     auto load_tiles = [&](int k0) {
         la0.load(Ap, P.lda, M, K, m0, k0, nullptr, 0);
         la1.load(Ap, P.lda, M, K, m0, k0, nullptr, 128);
@@ -226,18 +228,20 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
 }
 
 hipError_t launch_gemm(const GemmProb* probs_dev, int nprob, int total_tiles, bool ta, bool tb,
-                       bool a_bf16, bool b_bf16, bool vec, int parts, const PtrTable& ptrs,
+                       bool a_bf16, bool b_bf16, bool vec, bool full, int parts, const PtrTable& ptrs,
                        hipStream_t st) {
     if (nprob <= 0 || total_tiles <= 0) return hipSuccess;
     dim3 grid(total_tiles), blk(256);
     if (ta) vec = false;  // a k-major A has no row loads to vectorize
-#define SC_GEMM_CASE_NP(NP_, TA_, TB_, V_, EA, EB)                                              \
-    if (parts == NP_ && ta == TA_ && tb == TB_ && vec == V_ && a_bf16 == (sizeof(EA) == 2) &&  \
-        b_bf16 == (sizeof(EB) == 2)) {                                                          \
-        hipLaunchKernelGGL((gemm_grouped_kernel<NP_, TA_, TB_, V_, EA, EB>), grid, blk, 0, st,  \
+#define SC_GEMM_CASE_F(NP_, TA_, TB_, V_, F_, EA, EB)                                           \
+    if (parts == NP_ && ta == TA_ && tb == TB_ && vec == V_ && full == F_ &&                   \
+        a_bf16 == (sizeof(EA) == 2) && b_bf16 == (sizeof(EB) == 2)) {                           \
+        hipLaunchKernelGGL((gemm_grouped_kernel<NP_, TA_, TB_, V_, F_, EA, EB>), grid, blk, 0, st, \
                            probs_dev, nprob, ptrs);                                             \
         return hipGetLastError();                                                               \
     }
+#define SC_GEMM_CASE_NP(NP_, TA_, TB_, V_, EA, EB) \
+    SC_GEMM_CASE_F(NP_, TA_, TB_, V_, false, EA, EB) SC_GEMM_CASE_F(NP_, TA_, TB_, V_, true, EA, EB)
 #define SC_GEMM_CASE(TA_, TB_, V_, EA, EB) SC_GEMM_CASE_NP(3, TA_, TB_, V_, EA, EB)
     SC_GEMM_CASE_NP(2, false, false, true, float, float)
     SC_GEMM_CASE_NP(2, false, false, false, float, float)
@@ -254,6 +258,7 @@ hipError_t launch_gemm(const GemmProb* probs_dev, int nprob, int total_tiles, bo
     SC_GEMM_CASE(true, false, false, float, float)
 #undef SC_GEMM_CASE
 #undef SC_GEMM_CASE_NP
+#undef SC_GEMM_CASE_F
     return hipErrorInvalidValue;
 }
 

@@ -150,11 +150,13 @@ struct GemmProb {
 // prefix filled); ta/tb: operand stored transposed; a_bf16/b_bf16: operand
 // element type; vec: every problem's row-major operands (A unless ta, B if
 // tb) have 16-byte aligned rows (8 for bfloat16) and K a multiple of 8.
+// full: every problem's M, N and K are multiples of the 256 x 128 x 16 tile (no
+// clamped addresses or zeroed elements).
 // parts: 3 = float32-level products (six bfloat16 part products); 2 = three part
 // products, for correction terms only (float32 operands, neither transposed).
 // ptrs: caller pointers referenced by a_ptr/b_ptr.
 hipError_t launch_gemm(const GemmProb* probs_dev, int nprob, int total_tiles, bool ta, bool tb,
-                       bool a_bf16, bool b_bf16, bool vec, int parts, const PtrTable& ptrs,
+                       bool a_bf16, bool b_bf16, bool vec, bool full, int parts, const PtrTable& ptrs,
                        hipStream_t st);
 constexpr int kGemmBM = 256, kGemmBN = 128;
 
