@@ -107,7 +107,11 @@ __device__ __forceinline__ int remove_bit(int v, int b) {
 // step); NB = 1: one copy, two barriers per step.  The barriers are workgroup
 // barriers: every wave of the workgroup runs the 63 steps.  Returns the copy that
 // holds the result (G rotated, R^T = (Q - I)^T).
-template <int NW, int NB>
+// QF: R^T holds Q^T itself (I on entry, Q^T on exit): the rows of a rotated pair
+// need no correction of the identity's entries, whose columns move with the frame
+// (their bookkeeping is a fifth of a step's arithmetic).  The caller takes Q - I
+// from it with diag_to_delta.
+template <int NW, int NB, bool QF = false>
 __device__ __forceinline__ int pair_sweep(float (*G)[PW * SG], float (*RT)[PW * SR], float* cc,
                                           float* ss, int l, int w, float floor2, float tol) {
     constexpr int NU = 8 / NW;   // pair-blocks of G per lane
@@ -136,7 +140,7 @@ __device__ __forceinline__ int pair_sweep(float (*G)[PW * SG], float (*RT)[PW * 
     const int dg_pp = sp_ * SG + sp_, dg_qq = sq_ * SG + sq_, dg_pq = min(sp_, sq_) * SG + max(sp_, sq_);
     const int cb = CW * w;
     const int rt_rd = 2 * jr * SR + cb + 4 * hh, rt_wp = sp_ * SR + cb + 4 * hh, rt_wq = sq_ * SR + cb + 4 * hh;
-    int kp = jr == 0 ? -1 : cycle_pos(2 * jr), kq = cycle_pos(2 * jr + 1);
+    int kp = QF ? 0 : (jr == 0 ? -1 : cycle_pos(2 * jr)), kq = QF ? 0 : cycle_pos(2 * jr + 1);
     __syncthreads();
     v2f dpq = *(const v2f*)&G[0][2 * jr * SG + 2 * jr];
     float gqq = G[0][(2 * jr + 1) * SG + 2 * jr + 1];
@@ -160,9 +164,14 @@ __device__ __forceinline__ int pair_sweep(float (*G)[PW * SG], float (*RT)[PW * 
             xr[k] = *(const v4f*)&Rr[rt_rd + 8 * k];
             yr[k] = *(const v4f*)&Rr[rt_rd + SR + 8 * k];
         }
-        const int op = kp < 0 ? 0 : cycle_slot(kp), oq = cycle_slot(kq);
-        const float xop = Rr[2 * jr * SR + op], yop = Rr[(2 * jr + 1) * SR + op];
-        const float xoq = Rr[2 * jr * SR + oq], yoq = Rr[(2 * jr + 1) * SR + oq];
+        const int op = QF ? 0 : (kp < 0 ? 0 : cycle_slot(kp)), oq = QF ? 0 : cycle_slot(kq);
+        float xop = 0.0f, yop = 0.0f, xoq = 0.0f, yoq = 0.0f;
+        if constexpr (!QF) {
+            xop = Rr[2 * jr * SR + op];
+            yop = Rr[(2 * jr + 1) * SR + op];
+            xoq = Rr[2 * jr * SR + oq];
+            yoq = Rr[(2 * jr + 1) * SR + oq];
+        }
         const float gpp = dpq[0], gpq = dpq[1];
         float c, sn, cm1;
         pair_rotation(gpp, gpq, gqq, floor2, tol, c, sn, cm1);
@@ -206,19 +215,47 @@ __device__ __forceinline__ int pair_sweep(float (*G)[PW * SG], float (*RT)[PW * 
             *(v4f*)&Rw[rt_wp + 8 * k] = np;
             *(v4f*)&Rw[rt_wq + 8 * k] = nq;
         }
-        const int cop = op / CW == w ? op : PW, coq = oq / CW == w ? oq : PW;
-        Rw[sp_ * SR + cop] = fmaf(cm1, xop, xop) - sn * yop + cm1;
-        Rw[sq_ * SR + cop] = fmaf(cm1, yop, yop) + sn * xop + sn;
-        Rw[sp_ * SR + coq] = fmaf(cm1, xoq, xoq) - sn * yoq - sn;
-        Rw[sq_ * SR + coq] = fmaf(cm1, yoq, yoq) + sn * xoq + cm1;
-        kp = kp < 0 ? -1 : (kp == 0 ? 62 : kp - 1);
-        kq = kq == 0 ? 62 : kq - 1;
+        if constexpr (!QF) {
+            const int cop = op / CW == w ? op : PW, coq = oq / CW == w ? oq : PW;
+            Rw[sp_ * SR + cop] = fmaf(cm1, xop, xop) - sn * yop + cm1;
+            Rw[sq_ * SR + cop] = fmaf(cm1, yop, yop) + sn * xop + sn;
+            Rw[sp_ * SR + coq] = fmaf(cm1, xoq, xoq) - sn * yoq - sn;
+            Rw[sq_ * SR + coq] = fmaf(cm1, yoq, yoq) + sn * xoq + cm1;
+            kp = kp < 0 ? -1 : (kp == 0 ? 62 : kp - 1);
+            kq = kq == 0 ? 62 : kq - 1;
+        }
         __syncthreads();
         dpq = *(const v2f*)&Gw[2 * jr * SG + 2 * jr];
         gqq = Gw[(2 * jr + 1) * SG + 2 * jr + 1];
         if (NB == 2) cur ^= 1;
     }
     return cur;
+}
+
+// Q^T (stride SR, 64 x 64, as a QF sweep leaves it) to (Q - I)^T, by NT threads
+// (t < NT, four per row).  The off-diagonal entries are those of Q - I already.
+// A diagonal entry near 1 has lost its small distance to 1 in float32, so that
+// distance is taken from the column's other entries (Q orthogonal): with S the
+// sum of their squares, q_cc - 1 = -S / (1 + sqrt(1 - S)), exact to float32
+// rounding relative to S; when q_cc is not near 1 (at or below 1/2) q_cc - 1
+// itself is that accurate.  Row c of Q^T is column c of Q.
+template <int NT>
+__device__ __forceinline__ void diag_to_delta(float* RT, int t) {
+    static_assert(NT == 4 * PW, "four threads per row");
+    const int c = t >> 2, qq = t & 3;
+    float sq = 0.0f;
+#pragma unroll
+    for (int e = 0; e < PW / 4; ++e) {
+        const int r = 16 * qq + e;
+        const float v = RT[c * SR + r];
+        sq = r == c ? sq : fmaf(v, v, sq);
+    }
+    sq += __shfl_xor(sq, 1);
+    sq += __shfl_xor(sq, 2);
+    if ((c >> 4) == qq) {
+        const float d = RT[c * SR + c];
+        RT[c * SR + c] = d > 0.5f ? -sq / (1.0f + __builtin_amdgcn_sqrtf(fmaxf(1.0f - sq, 0.0f))) : d - 1.0f;
+    }
 }
 
 }  // namespace

@@ -398,14 +398,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void j
         if (tid == 0) *rflag = 0;
         return;
     }
+    // both pairs' Q^T = I before a round's sweeps (a row of stride SR is 17 vectors)
+    auto rt_identity = [&]() {
+        for (int e = tid; e < 2 * PW * SR / 4; e += 512) {
+            const int rem = (4 * e) % (PW * SR), d = rem / SR - rem % SR;
+            *(v4f*)&LS[QLR0 + 4 * e] = v4f{d == 0 ? 1.0f : 0.0f, d == 1 ? 1.0f : 0.0f,
+                                           d == 2 ? 1.0f : 0.0f, d == 3 ? 1.0f : 0.0f};
+        }
+    };
     // the cross block into registers (thread t: row t / 8, columns 8 (t % 8) .. + 7),
-    // R^T = 0 for the first sweeps
+    // Q^T = I for the first round
     const int ct = tid >> 3, cc0 = 8 * (tid & 7);
     float cr[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) cr[e] = X[ct * PW + cc0 + e];
     __syncthreads();
-    for (int e = tid; e < 2 * PW * SR / 4; e += 512) *(v4f*)&LS[QLR0 + 4 * e] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    rt_identity();
     __syncthreads();
 
     bool have_r = false;  // R holds the rounds so far
@@ -440,9 +448,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void j
             //    addresses are formed here rather than kept across the other phases
             int lr_ = l, wr_ = w;
             __asm__ volatile("" : "+v"(lr_), "+s"(wr_));
-            pair_sweep<4, 1>((float(*)[PW * SG])Gq, (float(*)[PW * SR])RTq, cc[q], ss[q], lr_, wr_,
-                             floor2, tol);
+            pair_sweep<4, 1, true>((float(*)[PW * SG])Gq, (float(*)[PW * SR])RTq, cc[q], ss[q], lr_, wr_,
+                                   floor2, tol);
             __syncthreads();
+            diag_to_delta<256>(RTq, pt);  // ordered before its readers by the barrier below
         }
         if (k == 2) {
             // column norms after the last round, from the pair Grams
@@ -567,7 +576,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void j
 #pragma unroll
         for (int e = 0; e < 8; ++e) cr[e] = X[ct * PW + cc0 + e];
         __syncthreads();
-        for (int e = tid; e < 2 * PW * SR / 4; e += 512) *(v4f*)&LS[QLR0 + 4 * e] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        rt_identity();
         __syncthreads();
     }
     if (tid == 0) {
