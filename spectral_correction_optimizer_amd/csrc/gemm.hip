@@ -178,7 +178,10 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
     }
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1;
-        if (kt + 1 < nk) load_tiles((kt + 1) * BK);
+        // the next tile (the last one again in the last step: the loop body stays one
+        // block, so the next tile's split can be scheduled between the products)
+        const int kn = (kt + 1 < nk ? kt + 1 : kt) * BK;
+        load_tiles(kn);
         v8bf a[4][NP], b[2][NP];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -198,7 +201,17 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
             SC_TERM(1, 0) SC_TERM(0, 1) SC_TERM(0, 0)
         }
 #undef SC_TERM
-        if (kt + 1 < nk) store_tiles(buf ^ 1);
+        // written to the other buffer, which no wave reads before the barrier
+        store_tiles(buf ^ 1);
+        // the fragment reads first, then the products interleaved with the next
+        // tile's split and stores
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * NP + 2 * NP, 0);
+#pragma unroll
+        for (int i = 0; i < 8 * NP; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x200, 16, 0);
         __syncthreads();
     }
 
