@@ -120,35 +120,40 @@ def copy_calibration(nbytes):
 # live kernel accounting gives for those dispatches.  The line's traffic per launch is this ratio times its own
 # algorithmic bytes per launch (the number of empty launches queued past a
 # converged sweep depends on host timing, so per-dispatch averages of two runs
-# differ while the ratio does not).  Keyed by the kernel source (sha256), the
-# workload and the pass schedule; anything else is reported as null.
+# differ while the ratio does not).  Keyed by the sources the kernel is compiled
+# from (sha256 of their concatenation), the workload and the pass schedule;
+# anything else is reported as null.
+QUAD_SOURCES = ["quad.hip", "jacobi_dev.hpp", "common.hpp", "internal.hpp"]
+ELEMENTWISE_SOURCES = ["elementwise.hip", "common.hpp", "internal.hpp"]
 TRAFFIC = {
-    "quad_apply": [{"source": "quad.hip", "workload": "blocks16_1b", "warmup": 5, "steps": 20,
-                    "sha256": "87ba78a92d435b454b626695c4977576949426a864dffaa05d2fa0a15a507087",
-                    "ratio": 1.0405,  # 1427.4 MB counted / 1371.8 MB algorithmic per launch, 8190 dispatches
-                    }],
-    "quad_gram": [{"source": "quad.hip", "workload": "blocks16_1b", "warmup": 5, "steps": 20,
-                   "sha256": "87ba78a92d435b454b626695c4977576949426a864dffaa05d2fa0a15a507087",
-                   "ratio": 1.0834,  # 556.2 MB counted (float64 partials included) / 513.4 MB algorithmic
-                   }],
-    "combine_adamw": [{"source": "elementwise.hip", "workload": "blocks16_1b", "warmup": 5, "steps": 20,
-                       "sha256": "9cc82042d998df956f80bc6a1b0f3e910778b84d9cd6a62faa1e280899c2c30e",
-                       "ratio": 1.0049,  # 31.291 GB counted / 31.139 GB algorithmic per launch
-                       }],
-    "ema": [{"source": "elementwise.hip", "workload": "blocks16_1b", "warmup": 5, "steps": 20,
-             "sha256": "9cc82042d998df956f80bc6a1b0f3e910778b84d9cd6a62faa1e280899c2c30e",
-             "ratio": 1.0130,  # 11.829 GB counted / 11.677 GB algorithmic per launch
-             }],
+    "quad_apply": [{"sources": QUAD_SOURCES, "workload": "blocks16_1b", "warmup": 5, "steps": 20,
+                    "sha256": "cf70548d251b797ff4d78a2c1b6cec1ad14ace6cd4f1e07a8cc508cd4dc3f4ea",
+                    "ratio": 1.0404}],  # 1434.3 MB counted / 1378.5 MB algorithmic per launch, 8147 dispatches
+    "quad_gram": [{"sources": QUAD_SOURCES, "workload": "blocks16_1b", "warmup": 5, "steps": 20,
+                   "sha256": "cf70548d251b797ff4d78a2c1b6cec1ad14ace6cd4f1e07a8cc508cd4dc3f4ea",
+                   "ratio": 1.0833}],  # 559.2 MB counted (float64 partials included) / 516.1 MB algorithmic
+    "combine_adamw": [{"sources": ELEMENTWISE_SOURCES, "workload": "blocks16_1b", "warmup": 5, "steps": 20,
+                       "sha256": "6427ee178a3f72913ecc6804c3b19ecaa4d4a85040c8b419e634d2903da6133b",
+                       "ratio": 1.0049}],  # 31.290 GB counted / 31.138 GB algorithmic per launch
+    "ema": [{"sources": ELEMENTWISE_SOURCES, "workload": "blocks16_1b", "warmup": 5, "steps": 20,
+             "sha256": "6427ee178a3f72913ecc6804c3b19ecaa4d4a85040c8b419e634d2903da6133b",
+             "ratio": 1.0130}],  # 11.829 GB counted / 11.677 GB algorithmic per launch
 }
 
 
-def traffic_ratio(name, workload, warmup, steps):
+def sources_sha(files):
     import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "spectral_correction_optimizer_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def traffic_ratio(name, workload, warmup, steps):
     for t in TRAFFIC.get(name, []):
-        if (t["workload"], t["warmup"], t["steps"]) != (workload, warmup, steps):
+        if (t["workload"], t["warmup"], t["steps"]) != (workload, warmup, steps) or t["ratio"] is None:
             continue
-        src = os.path.join(ROOT, "spectral_correction_optimizer_amd", "csrc", t["source"])
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() == t["sha256"]:
+        if sources_sha(t["sources"]) == t["sha256"]:
             return t["ratio"]
     return None
 

@@ -206,6 +206,7 @@ struct sc_opt {
         int nsyrk_cap = 0;
         SyrkItem* syrk_all = nullptr;  // the same for every matrix (final Gram)
         int nsyrk_all = 0;
+        bool syrk_cap_full = true, syrk_all_full = true;  // every k a multiple of 128
         int max_kpad = 64, max_K = 128, max_k = 1, max_nbk = 0, max_klen = 0, max_t64 = 1;
         GemmGroup warm_nt, warm_nn;      // warm start: A_rows = W M^T (m >= n) or W M (m < n)
         GemmGroup factor_v;              // V rows <- diag(1/|x_j|) X^T V_prev (gated per matrix)
@@ -452,7 +453,7 @@ int build_projectors(sc_opt* h, hipStream_t st) {
 // only_regram, for the matrices polished after failing the certificate alone.
 int pipe_final_gram(sc_opt* h, Pipe& p, hipStream_t st, bool only_regram = false) {
     HIP_TRY(timed(h, PK_GRAM_E, st, [&] {
-        return launch_chol_syrk(h->md, h->flags_d, p.syrk_all, p.nsyrk_all, only_regram, st);
+        return launch_chol_syrk(h->md, h->flags_d, p.syrk_all, p.nsyrk_all, only_regram, p.syrk_all_full, st);
     }));
     HIP_TRY(timed(h, PK_GRAM_E, st, [&] {
         return launch_gram_to_e(h->md, h->flags_d, p.mats, p.nmat, p.max_t64, only_regram, st);
@@ -591,7 +592,7 @@ int pipe_pre(sc_opt* h, Pipe& p, hipStream_t st, bool warm) {
     if (p.pre) {
         // Factor phase: Jacobi on X = L, A^T A = L L^T (k-long rows, no V).
         HIP_TRY(timed(h, PK_CHOL_GEMM, st, [&] {
-            return launch_chol_syrk(h->md, h->flags_d, p.syrk_cap, p.nsyrk_cap, 0, st);
+            return launch_chol_syrk(h->md, h->flags_d, p.syrk_cap, p.nsyrk_cap, 0, p.syrk_cap_full, st);
         }));
         HIP_TRY(timed(h, PK_CHOL, st, [&] {
             return launch_cholesky(h->md, h->flags_d, p.cap, p.ncap, p.max_nbk, p.max_klen, st);
@@ -1519,7 +1520,9 @@ int build(sc_opt* h, const int64_t* rows, const int64_t* cols) {
             const int kt = (m.k + 127) / 128;
             for (int ti = 0; ti < kt; ++ti)
                 for (int tj = 0; tj <= ti; ++tj) sa.push_back(SyrkItem{i, ti, tj});
+            P.syrk_all_full = P.syrk_all_full && m.k % 128 == 0;
             if (m.klen) {
+                P.syrk_cap_full = P.syrk_cap_full && m.k % 128 == 0;
                 cap.push_back(i);
                 P.max_nbk = std::max(P.max_nbk, (m.k + 63) / 64);
                 P.max_klen = std::max(P.max_klen, m.klen);

@@ -51,11 +51,15 @@ __device__ __forceinline__ bool chol_active(const MatDev& md, const MatFlags& f,
 // accumulation, the dropped ones below 2^-23 of each product).  K advances by 16
 // columns through double-buffered LDS holding the split rows of both strips
 // (the diagonal tiles read one strip); the float32 accumulators are folded into
-// float64 every 256 columns.
+// float64 every 256 columns.  Within a fold span the loop body is one block (the
+// next step's loads and split are issued unconditionally, the last step's into
+// the idle buffer) so the next step's split is scheduled between the products.
+// FULL: k is a multiple of the tile, every strip row exists (no masking).
 namespace {
 constexpr int SB = 128, SKB = 16, SFOLD = 256;
 }
 
+template <bool FULL>
 __global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict__ mats,
                                                         const MatFlags* __restrict__ flags,
                                                         const SyrkItem* __restrict__ items,
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict
         for (int t = 0; t < 2; ++t) {
             if (t >= nstrip) break;
             const int row = r0[t] + lrow;
-            const float* q = md.A + (int64_t)min(row, k - 1) * ld + x0 + 8 * lhalf;
+            const float* q = md.A + (int64_t)(FULL ? row : min(row, k - 1)) * ld + x0 + 8 * lhalf;
             reg[t][0] = load4(q);
             reg[t][1] = load4(q + 4);
         }
@@ -87,7 +91,7 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             if (t >= nstrip) break;
-            const bool in = r0[t] + lrow < k;
+            const bool in = FULL || r0[t] + lrow < k;
             const float f[8] = {in ? reg[t][0].x : 0.f, in ? reg[t][0].y : 0.f, in ? reg[t][0].z : 0.f,
                                 in ? reg[t][0].w : 0.f, in ? reg[t][1].x : 0.f, in ? reg[t][1].y : 0.f,
                                 in ? reg[t][1].z : 0.f, in ? reg[t][1].w : 0.f};
@@ -120,36 +124,45 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict
     gload(0);
     lstore(0);
     __syncthreads();
-    for (int st = 0; st < nst; ++st) {
-        const int buf = st & 1;
-        if (st + 1 < nst) gload((st + 1) * SKB);
-        v8bf a[2][3], b[2][3];
+    for (int st0 = 0; st0 < nst; st0 += SFOLD / SKB) {
+        const int st1 = min(st0 + SFOLD / SKB, nst);
+        for (int st = st0; st < st1; ++st) {
+            const int buf = st & 1;
+            const int sn = st + 1 < nst ? st + 1 : st;
+            gload(sn * SKB);
+            v8bf a[2][3], b[2][3];
 #pragma unroll
-        for (int p = 0; p < 3; ++p) {
-            a[0][p] = *(const v8bf*)&Xs[buf][0][p][fa0];
-            a[1][p] = *(const v8bf*)&Xs[buf][0][p][fa1];
-            b[0][p] = *(const v8bf*)&Xs[buf][sj][p][fb0];
-            b[1][p] = *(const v8bf*)&Xs[buf][sj][p][fb1];
-        }
+            for (int p = 0; p < 3; ++p) {
+                a[0][p] = *(const v8bf*)&Xs[buf][0][p][fa0];
+                a[1][p] = *(const v8bf*)&Xs[buf][0][p][fa1];
+                b[0][p] = *(const v8bf*)&Xs[buf][sj][p][fb0];
+                b[1][p] = *(const v8bf*)&Xs[buf][sj][p][fb1];
+            }
 #define SC_TERM(PA, PB)                                                                        \
     _Pragma("unroll") for (int i = 0; i < 2; ++i)                                               \
         _Pragma("unroll") for (int j = 0; j < 2; ++j)                                           \
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][PA], b[j][PB], acc[i][j], 0, 0, 0);
-        SC_TERM(2, 0) SC_TERM(1, 1) SC_TERM(0, 2) SC_TERM(1, 0) SC_TERM(0, 1) SC_TERM(0, 0)
+            SC_TERM(2, 0) SC_TERM(1, 1) SC_TERM(0, 2) SC_TERM(1, 0) SC_TERM(0, 1) SC_TERM(0, 0)
 #undef SC_TERM
-        if (((st + 1) * SKB) % SFOLD == 0 || st + 1 == nst) {
+            lstore(buf ^ 1);  // the idle buffer: no wave reads it before the barrier
+            __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
 #pragma unroll
-            for (int a2 = 0; a2 < 2; ++a2)
-#pragma unroll
-                for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        acc64[a2][b2][r] += (double)acc[a2][b2][r];
-                        acc[a2][b2][r] = 0.0f;
-                    }
+            for (int i = 0; i < 24; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x200, 6, 0);
+            __syncthreads();
         }
-        if (st + 1 < nst) lstore(buf ^ 1);
-        __syncthreads();
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+            for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    acc64[a2][b2][r] += (double)acc[a2][b2][r];
+                    acc[a2][b2][r] = 0.0f;
+                }
     }
     // 32x32 output layout: lane l, register r -> row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
 #pragma unroll
@@ -379,9 +392,13 @@ hipError_t launch_factor_invnorm(const MatDev* mats, const MatFlags* flags, cons
 }
 
 hipError_t launch_chol_syrk(const MatDev* mats, const MatFlags* flags, const SyrkItem* items,
-                            int nitems, int only_regram, hipStream_t st) {
-    hipLaunchKernelGGL(chol_syrk_kernel, dim3(nitems), dim3(256), 0, st, mats, flags, items,
-                       only_regram);
+                            int nitems, int only_regram, bool full, hipStream_t st) {
+    if (full)
+        hipLaunchKernelGGL(chol_syrk_kernel<true>, dim3(nitems), dim3(256), 0, st, mats, flags, items,
+                           only_regram);
+    else
+        hipLaunchKernelGGL(chol_syrk_kernel<false>, dim3(nitems), dim3(256), 0, st, mats, flags, items,
+                           only_regram);
     return hipGetLastError();
 }
 

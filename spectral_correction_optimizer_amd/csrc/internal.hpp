@@ -235,9 +235,10 @@ hipError_t launch_jacobi_sweep_end(const MatDev* mats, MatFlags* flags, const in
 
 // ---- Cholesky preconditioning of tall operands ------------------------------------------
 
-// chol = A^T A (lower 128 x 128 tiles listed in items), float64 sums.
+// chol = A^T A (lower 128 x 128 tiles listed in items), float64 sums; full: every
+// listed matrix's k is a multiple of 128.
 hipError_t launch_chol_syrk(const MatDev* mats, const MatFlags* flags, const SyrkItem* items,
-                            int nitems, int only_regram, hipStream_t st);
+                            int nitems, int only_regram, bool full, hipStream_t st);
 // chol = L L^T (in place, lower triangle) for the matrices in mat_idx; on success the
 // rows of A become the columns of L (length klen) and precond = 1, else chol_fail = 1
 // and done = 1 (the matrix sits the factor phase out).  max_nbk: largest ceil(k / 64),
