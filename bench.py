@@ -127,16 +127,16 @@ QUAD_SOURCES = ["quad.hip", "jacobi_dev.hpp", "common.hpp", "internal.hpp"]
 ELEMENTWISE_SOURCES = ["elementwise.hip", "common.hpp", "internal.hpp"]
 TRAFFIC = {
     "quad_apply": [{"sources": QUAD_SOURCES, "workload": "blocks16_1b", "warmup": 5, "steps": 20,
-                    "sha256": "cf70548d251b797ff4d78a2c1b6cec1ad14ace6cd4f1e07a8cc508cd4dc3f4ea",
+                    "sha256": "54ab20e788c4eadbbc0746b36372d7897eb839ac9928476d96040a069f88014a",
                     "ratio": 1.0404}],  # 1434.3 MB counted / 1378.5 MB algorithmic per launch, 8147 dispatches
     "quad_gram": [{"sources": QUAD_SOURCES, "workload": "blocks16_1b", "warmup": 5, "steps": 20,
-                   "sha256": "cf70548d251b797ff4d78a2c1b6cec1ad14ace6cd4f1e07a8cc508cd4dc3f4ea",
+                   "sha256": "54ab20e788c4eadbbc0746b36372d7897eb839ac9928476d96040a069f88014a",
                    "ratio": 1.0833}],  # 559.2 MB counted (float64 partials included) / 516.1 MB algorithmic
     "combine_adamw": [{"sources": ELEMENTWISE_SOURCES, "workload": "blocks16_1b", "warmup": 5, "steps": 20,
-                       "sha256": "6427ee178a3f72913ecc6804c3b19ecaa4d4a85040c8b419e634d2903da6133b",
+                       "sha256": "7a2acbba2b3c4fdf68f0a7790ea97659638a9ea6f9e49cf2ac23f4cbce7141ba",
                        "ratio": 1.0049}],  # 31.290 GB counted / 31.138 GB algorithmic per launch
     "ema": [{"sources": ELEMENTWISE_SOURCES, "workload": "blocks16_1b", "warmup": 5, "steps": 20,
-             "sha256": "6427ee178a3f72913ecc6804c3b19ecaa4d4a85040c8b419e634d2903da6133b",
+             "sha256": "7a2acbba2b3c4fdf68f0a7790ea97659638a9ea6f9e49cf2ac23f4cbce7141ba",
              "ratio": 1.0130}],  # 11.829 GB counted / 11.677 GB algorithmic per launch
 }
 
