@@ -45,26 +45,28 @@ __device__ __forceinline__ bool chol_active(const MatDev& md, const MatFlags& f,
 
 // ---------------------------------------------------------------------------------
 // C = A^T A over the rows of the Jacobi operand (row j = column j of A, length
-// K_ld, zero padded).  One workgroup per lower 128 x 128 tile (ti >= tj); four
-// waves of 64 x 64, each 2 x 2 blocks of v_mfma_f32_32x32x16_bf16 over the
-// exact three-way bfloat16 split of the operand (six part products, float32
-// accumulation, the dropped ones below 2^-23 of each product).  K advances by 16
-// columns through double-buffered LDS holding the split rows of both strips
-// (the diagonal tiles read one strip); the float32 accumulators are folded into
-// float64 every 256 columns.  Within a fold span the loop body is one block (the
-// next step's loads and split are issued unconditionally, the last step's into
-// the idle buffer) so the next step's split is scheduled between the products.
-// FULL: k is a multiple of the tile, every strip row exists (no masking).
+// K_ld, zero padded).  One workgroup per lower 128 x 128 tile (ti >= tj); eight
+// waves of 64 x 32 (2 x 1 blocks of v_mfma_f32_32x32x16_bf16) over the exact
+// three-way bfloat16 split of the operand (six part products, float32
+// accumulation, the dropped ones below 2^-23 of each product).  K advances by 32
+// columns (two 16-column halves) through double-buffered LDS holding the split
+// rows of both strips (the diagonal tiles read one strip); the float32
+// accumulators are folded into float64 every 256 columns.  Eight waves of 64 x 32
+// keep the float64 sums at 64 registers a lane, so two waves share each SIMD.
+// Within a fold span the loop body is one block (the next step's loads and split
+// are issued unconditionally, the last step's into the idle buffer) so the next
+// step's split is scheduled between the products.  FULL: k is a multiple of the
+// tile, every strip row exists (no masking).
 namespace {
-constexpr int SB = 128, SKB = 16, SFOLD = 256;
+constexpr int SB = 128, SKB = 32, SFOLD = 256;
 }
 
 template <bool FULL>
-__global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict__ mats,
+__global__ __launch_bounds__(512) void chol_syrk_kernel(const MatDev* __restrict__ mats,
                                                         const MatFlags* __restrict__ flags,
                                                         const SyrkItem* __restrict__ items,
                                                         int only_regram) {
-    __shared__ __align__(16) __bf16 Xs[2][2][3][SB * SKB];  // [buffer][strip][plane]
+    __shared__ __align__(16) __bf16 Xs[2][2][3][2][SB * 16];  // [buffer][strip][plane][half of the step]
     const SyrkItem it = items[blockIdx.x];
     if (only_regram && !flags[it.mat].regram) return;
     const MatDev& md = mats[it.mat];
@@ -72,17 +74,17 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict
     const int k = md.k, ld = md.K_ld;
     const int r0[2] = {it.ti * SB, it.tj * SB};
 
-    // loader: thread t holds 8 consecutive columns (half t & 1 of the step's 16)
-    // of strip row t >> 1; rows at or beyond k read as zero
+    // loader: thread t holds 8 consecutive columns 16 s + 8 h (s = (t >> 1) & 1,
+    // h = t & 1) of the step's 32, of strip row t >> 2; rows at or beyond k read as zero
     const int nstrip = diag ? 1 : 2;
-    const int lrow = threadIdx.x >> 1, lhalf = threadIdx.x & 1;
+    const int lrow = threadIdx.x >> 2, lsub = (threadIdx.x >> 1) & 1, lhalf = threadIdx.x & 1;
     float4 reg[2][2];
     auto gload = [&](int x0) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             if (t >= nstrip) break;
             const int row = r0[t] + lrow;
-            const float* q = md.A + (int64_t)(FULL ? row : min(row, k - 1)) * ld + x0 + 8 * lhalf;
+            const float* q = md.A + (int64_t)(FULL ? row : min(row, k - 1)) * ld + x0 + 16 * lsub + 8 * lhalf;
             reg[t][0] = load4(q);
             reg[t][1] = load4(q + 4);
         }
@@ -97,29 +99,27 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict
                                 in ? reg[t][1].z : 0.f, in ? reg[t][1].w : 0.f};
             const Split8 sp = split8(f);
             const int o = split_chunk16(lrow, lhalf);
-            *(v8bf*)&Xs[buf][t][0][o] = sp.h;
-            *(v8bf*)&Xs[buf][t][1][o] = sp.m;
-            *(v8bf*)&Xs[buf][t][2][o] = sp.l;
+            *(v8bf*)&Xs[buf][t][0][lsub][o] = sp.h;
+            *(v8bf*)&Xs[buf][t][1][lsub][o] = sp.m;
+            *(v8bf*)&Xs[buf][t][2][lsub][o] = sp.l;
         }
     };
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int hl = lane >> 5, ll = lane & 31;
-    const int wr = (wave >> 1) * 64, wc = (wave & 1) * 64;
+    const int wr = (wave >> 2) * 64, wc = (wave & 3) * 32;
     const int sj = diag ? 0 : 1;
     const int fa0 = split_chunk16(wr + ll, hl), fa1 = split_chunk16(wr + 32 + ll, hl);
-    const int fb0 = split_chunk16(wc + ll, hl), fb1 = split_chunk16(wc + 32 + ll, hl);
-    v16f acc[2][2];
-    double acc64[2][2][16];
+    const int fb = split_chunk16(wc + ll, hl);
+    v16f acc[2];
+    double acc64[2][16];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                acc[a][b][r] = 0.0f;
-                acc64[a][b][r] = 0.0;
-            }
+        for (int r = 0; r < 16; ++r) {
+            acc[a][r] = 0.0f;
+            acc64[a][r] = 0.0;
+        }
     const int nst = ld / SKB;  // K_ld is a multiple of 128
     gload(0);
     lstore(0);
@@ -130,22 +130,23 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict
             const int buf = st & 1;
             const int sn = st + 1 < nst ? st + 1 : st;
             gload(sn * SKB);
-            v8bf a[2][3], b[2][3];
 #pragma unroll
-            for (int p = 0; p < 3; ++p) {
-                a[0][p] = *(const v8bf*)&Xs[buf][0][p][fa0];
-                a[1][p] = *(const v8bf*)&Xs[buf][0][p][fa1];
-                b[0][p] = *(const v8bf*)&Xs[buf][sj][p][fb0];
-                b[1][p] = *(const v8bf*)&Xs[buf][sj][p][fb1];
-            }
-#define SC_TERM(PA, PB)                                                                        \
-    _Pragma("unroll") for (int i = 0; i < 2; ++i)                                               \
-        _Pragma("unroll") for (int j = 0; j < 2; ++j)                                           \
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][PA], b[j][PB], acc[i][j], 0, 0, 0);
-            SC_TERM(2, 0) SC_TERM(1, 1) SC_TERM(0, 2) SC_TERM(1, 0) SC_TERM(0, 1) SC_TERM(0, 0)
+            for (int h = 0; h < 2; ++h) {
+                v8bf a[2][3], b[3];
+#pragma unroll
+                for (int p = 0; p < 3; ++p) {
+                    a[0][p] = *(const v8bf*)&Xs[buf][0][p][h][fa0];
+                    a[1][p] = *(const v8bf*)&Xs[buf][0][p][h][fa1];
+                    b[p] = *(const v8bf*)&Xs[buf][sj][p][h][fb];
+                }
+#define SC_TERM(PA, PB)                                         \
+    _Pragma("unroll") for (int i = 0; i < 2; ++i)                \
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i][PA], b[PB], acc[i], 0, 0, 0);
+                SC_TERM(2, 0) SC_TERM(1, 1) SC_TERM(0, 2) SC_TERM(1, 0) SC_TERM(0, 1) SC_TERM(0, 0)
 #undef SC_TERM
+            }
             lstore(buf ^ 1);  // the idle buffer: no wave reads it before the barrier
-            __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
 #pragma unroll
             for (int i = 0; i < 24; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -157,24 +158,20 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(const MatDev* __restrict
 #pragma unroll
         for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-            for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    acc64[a2][b2][r] += (double)acc[a2][b2][r];
-                    acc[a2][b2][r] = 0.0f;
-                }
+            for (int r = 0; r < 16; ++r) {
+                acc64[a2][r] += (double)acc[a2][r];
+                acc[a2][r] = 0.0f;
+            }
     }
     // 32x32 output layout: lane l, register r -> row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
 #pragma unroll
     for (int a2 = 0; a2 < 2; ++a2)
 #pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = r0[0] + wr + 32 * a2 + 8 * (r >> 2) + 4 * hl + (r & 3);
-                const int col = r0[1] + wc + 32 * b2 + ll;
-                if (row < k && col < k) gst(md.chol + (int64_t)row * k + col, acc64[a2][b2][r]);
-            }
+        for (int r = 0; r < 16; ++r) {
+            const int row = r0[0] + wr + 32 * a2 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            const int col = r0[1] + wc + ll;
+            if (row < k && col < k) gst(md.chol + (int64_t)row * k + col, acc64[a2][r]);
+        }
 }
 
 // ---------------------------------------------------------------------------------
@@ -394,10 +391,10 @@ hipError_t launch_factor_invnorm(const MatDev* mats, const MatFlags* flags, cons
 hipError_t launch_chol_syrk(const MatDev* mats, const MatFlags* flags, const SyrkItem* items,
                             int nitems, int only_regram, bool full, hipStream_t st) {
     if (full)
-        hipLaunchKernelGGL(chol_syrk_kernel<true>, dim3(nitems), dim3(256), 0, st, mats, flags, items,
+        hipLaunchKernelGGL(chol_syrk_kernel<true>, dim3(nitems), dim3(512), 0, st, mats, flags, items,
                            only_regram);
     else
-        hipLaunchKernelGGL(chol_syrk_kernel<false>, dim3(nitems), dim3(256), 0, st, mats, flags, items,
+        hipLaunchKernelGGL(chol_syrk_kernel<false>, dim3(nitems), dim3(512), 0, st, mats, flags, items,
                            only_regram);
     return hipGetLastError();
 }
