@@ -212,11 +212,9 @@ __global__ __launch_bounds__(256) void chol_diag_kernel(const MatDev* __restrict
         for (int r = c + 1 + threadIdx.x; r < CT; r += blockDim.x)
             T[r][c] = l > 0.0 ? T[r][c] / l : 0.0;
         __syncthreads();
-        const int rem = CT - c - 1;
-        for (int idx = threadIdx.x; idx < rem * rem; idx += blockDim.x) {
-            const int r = c + 1 + idx / rem, s = c + 1 + idx % rem;
-            if (s <= r) T[r][s] -= T[r][c] * T[s][c];
-        }
+        // trailing lower triangle: thread (tid / 16, tid % 16) strides rows and columns by 16
+        for (int r = c + 1 + (threadIdx.x >> 4); r < CT; r += 16)
+            for (int s = c + 1 + (threadIdx.x & 15); s <= r; s += 16) T[r][s] -= T[r][c] * T[s][c];
         __syncthreads();
     }
     if (fail) {
@@ -254,17 +252,22 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(const MatDev* __restric
         B[r][c] = (r0 + r < k && c0 + c < k) ? C[(int64_t)(r0 + r) * k + c0 + c] : 0.0;
     }
     __syncthreads();
-    if (threadIdx.x < CT) {
-        const int r = threadIdx.x;
-        for (int c = 0; c < CT; ++c) {
-            const double* Lc = Lp + c * (c + 1) / 2;
-            double acc = B[r][c];
-            for (int s = 0; s < c; ++s) acc -= B[r][s] * Lc[s];
-            const double d = Lc[c];
-            B[r][c] = d > 0.0 ? acc / d : 0.0;
+    // X L^T = B column by column (right-looking): column c is final once the
+    // terms of columns s < c are subtracted (in that order) and it is divided by
+    // L_cc; then every thread subtracts its share of column c's terms from the
+    // columns after it
+    for (int c = 0; c < CT; ++c) {
+        if (threadIdx.x < CT) {
+            const double d = Lp[c * (c + 1) / 2 + c];
+            B[threadIdx.x][c] = d > 0.0 ? B[threadIdx.x][c] / d : 0.0;
         }
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < CT * (CT - 1 - c); idx += blockDim.x) {
+            const int r = idx & (CT - 1), sc = c + 1 + (idx >> 6);
+            B[r][sc] -= B[r][c] * Lp[sc * (sc + 1) / 2 + c];
+        }
+        __syncthreads();
     }
-    __syncthreads();
     for (int idx = threadIdx.x; idx < CT * CT; idx += blockDim.x) {
         const int r = idx >> 6, c = idx & 63;
         if (r0 + r < k && c0 + c < k) C[(int64_t)(r0 + r) * k + c0 + c] = B[r][c];
@@ -273,12 +276,14 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(const MatDev* __restric
 
 // C_ib,kb -= L_ib,jb L_kb,jb^T for jb < kb <= ib (the lower trailing tiles).
 // 16 x 16 threads, each a 4 x 4 block of outputs (rows ty + 16 a, columns
-// tx + 16 b); the two panels pass through LDS 32 columns at a time.
+// tx + 16 b); the two panels pass through LDS 32 columns at a time, transposed
+// (rows padded by one element: the transposing stores of 32 consecutive k then
+// fall in distinct banks).
 __global__ __launch_bounds__(256) void chol_update_kernel(const MatDev* __restrict__ mats,
                                                           const MatFlags* __restrict__ flags,
                                                           const int* __restrict__ mat_idx, int jb) {
-    __shared__ double P[32][CT];  // L_ib,jb, k-major: P[s][r]
-    __shared__ double Q[32][CT];  // L_kb,jb, k-major: Q[s][c]
+    __shared__ double P[32][CT + 1];  // L_ib,jb, k-major: P[s][r]
+    __shared__ double Q[32][CT + 1];  // L_kb,jb, k-major: Q[s][c]
     const int i = mat_idx[blockIdx.y];
     const MatFlags& f = flags[i];
     const MatDev& md = mats[i];
