@@ -274,64 +274,83 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(const MatDev* __restric
     }
 }
 
-// C_ib,kb -= L_ib,jb L_kb,jb^T for jb < kb <= ib (the lower trailing tiles).
-// 16 x 16 threads, each a 4 x 4 block of outputs (rows ty + 16 a, columns
-// tx + 16 b); the two panels pass through LDS 32 columns at a time, transposed
-// (rows padded by one element: the transposing stores of 32 consecutive k then
-// fall in distinct banks).
+// C_ib,kb -= L_ib,jb L_kb,jb^T for jb < kb <= ib (the lower trailing tiles), over
+// 128 x 128 blocks of the trailing lower triangle (four 64 x 64 tiles: each panel
+// block is read once for four tiles).  16 x 16 threads, each an 8 x 8 block of
+// outputs (rows ty + 16 a, columns tx + 16 b), every sum over the panel's 64
+// columns in order; the two panels pass through LDS 16 columns at a time,
+// transposed (rows padded by one element).  Entries above the diagonal or beyond
+// k are not written.
 __global__ __launch_bounds__(256) void chol_update_kernel(const MatDev* __restrict__ mats,
                                                           const MatFlags* __restrict__ flags,
                                                           const int* __restrict__ mat_idx, int jb) {
-    __shared__ double P[32][CT + 1];  // L_ib,jb, k-major: P[s][r]
-    __shared__ double Q[32][CT + 1];  // L_kb,jb, k-major: Q[s][c]
+    constexpr int UB = 2 * CT, US = 16;
+    __shared__ double P[US][UB + 1];  // L_ib,jb rows, k-major: P[s][r]
+    __shared__ double Q[US][UB + 1];  // L_kb,jb rows, k-major: Q[s][c]
     const int i = mat_idx[blockIdx.y];
     const MatFlags& f = flags[i];
     const MatDev& md = mats[i];
     if (!chol_active(md, f, jb)) return;
     const int k = md.k, nbk = (k + CT - 1) / CT;
-    const int nt = nbk - jb - 1;  // trailing tile rows of this matrix
+    const int nt = nbk - jb - 1;      // trailing tile rows of this matrix
+    const int nu = (nt + 1) / 2;      // in 128-row blocks
     const int t = blockIdx.x;
-    if (t >= nt * (nt + 1) / 2) return;
-    // t -> (a, b), 0 <= b <= a < nt, row by row over the lower triangle
+    if (t >= nu * (nu + 1) / 2) return;
+    // t -> (a, b), 0 <= b <= a < nu, row by row over the lower triangle
     int a = (int)((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
     while ((a + 1) * (a + 2) / 2 <= t) ++a;
     while (a * (a + 1) / 2 > t) --a;
     const int b = t - a * (a + 1) / 2;
-    const int ri = (jb + 1 + a) * CT, rk = (jb + 1 + b) * CT, c0 = jb * CT;
+    const int ri = (jb + 1) * CT + a * UB, rk = (jb + 1) * CT + b * UB, c0 = jb * CT;
     double* C = md.chol;
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-    double acc[4][4];
+    double acc[8][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
-    for (int s0 = 0; s0 < CT; s0 += 32) {
-        for (int idx = threadIdx.x; idx < 32 * CT; idx += blockDim.x) {
-            const int r = idx >> 5, s = idx & 31;
-            const int gs = c0 + s0 + s;
-            P[s][r] = (ri + r < k && gs < k) ? C[(int64_t)(ri + r) * k + gs] : 0.0;
-            Q[s][r] = (rk + r < k && gs < k) ? C[(int64_t)(rk + r) * k + gs] : 0.0;
+        for (int v = 0; v < 8; ++v) acc[u][v] = 0.0;
+    // the next chunk's panel entries are loaded into registers while the current
+    // chunk is multiplied (element j of a thread: idx = tid + 256 j, row idx / 16,
+    // column idx % 16 of the chunk)
+    constexpr int NE = US * UB / 256;
+    double pr[NE], qr[NE];
+    auto gl = [&](int s0) {
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
+            const int idx = threadIdx.x + 256 * j, r = idx >> 4, gs = c0 + s0 + (idx & (US - 1));
+            pr[j] = (ri + r < k && gs < k) ? C[(int64_t)(ri + r) * k + gs] : 0.0;
+            qr[j] = (rk + r < k && gs < k) ? C[(int64_t)(rk + r) * k + gs] : 0.0;
+        }
+    };
+    gl(0);
+    for (int s0 = 0; s0 < CT; s0 += US) {
+#pragma unroll
+        for (int j = 0; j < NE; ++j) {
+            const int idx = threadIdx.x + 256 * j, r = idx >> 4, s = idx & (US - 1);
+            P[s][r] = pr[j];
+            Q[s][r] = qr[j];
         }
         __syncthreads();
-#pragma unroll 8
-        for (int s = 0; s < 32; ++s) {
-            double pv[4], qv[4];
+        if (s0 + US < CT) gl(s0 + US);
+#pragma unroll 4
+        for (int s = 0; s < US; ++s) {
+            double pv[8], qv[8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < 8; ++u) {
                 pv[u] = P[s][ty + 16 * u];
                 qv[u] = Q[s][tx + 16 * u];
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < 8; ++u)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[u][v] = fma(pv[u], qv[v], acc[u][v]);
+                for (int v = 0; v < 8; ++v) acc[u][v] = fma(pv[u], qv[v], acc[u][v]);
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 8; ++u)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
+        for (int v = 0; v < 8; ++v) {
             const int row = ri + ty + 16 * u, col = rk + tx + 16 * v;
             if (row < k && col < k && col <= row) C[(int64_t)row * k + col] -= acc[u][v];
         }
@@ -412,7 +431,8 @@ hipError_t launch_cholesky(const MatDev* mats, MatFlags* flags, const int* mat_i
         if (nt > 0) {
             hipLaunchKernelGGL(chol_panel_kernel, dim3(nt, nmat), dim3(256), 0, st, mats, flags,
                                mat_idx, jb);
-            hipLaunchKernelGGL(chol_update_kernel, dim3(nt * (nt + 1) / 2, nmat), dim3(256), 0, st,
+            const int nu = (nt + 1) / 2;  // 128-row blocks of the trailing triangle
+            hipLaunchKernelGGL(chol_update_kernel, dim3(nu * (nu + 1) / 2, nmat), dim3(256), 0, st,
                                mats, flags, mat_idx, jb);
         }
     }
