@@ -232,6 +232,119 @@ __device__ __forceinline__ int pair_sweep(float (*G)[PW * SG], float (*RT)[PW * 
     return cur;
 }
 
+// The QF sweep of the group solve with the 32 rotations of a step computed once,
+// by wave 0 of the pair, and published as (c, s, c - 1) in rot[] before the step's
+// first barrier; the other waves read them after it (the step already has two
+// barriers: reads | writes).  The same rotations and arithmetic as pair_sweep<NW, 1,
+// true>, so the same results, with the rotation's vector work (about a quarter of a
+// step, square roots and reciprocals included) done by one wave instead of four.
+// On entry G holds the pair Gram and R^T = I (copy 0, as pair_sweep).
+template <int NW>
+__device__ __forceinline__ void pair_sweep_q(float* G, float* RT, v4f* rot, int l, int w, float floor2,
+                                             float tol) {
+    constexpr int NU = 8 / NW;   // pair-blocks of G per lane
+    constexpr int NK = 8 / NW;   // 8-column groups of R^T per lane
+    constexpr int CW = PW / NW;  // columns of R^T per wave
+    const int jr = l >> 1, hh = l & 1, cls = l & 15, odd = (l >> 4) & 1;
+    int blk_ij[NU], blk_rd[NU], blk_wr[NU][4];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        const int v = kBlocks.v[cls][NU * ((l >> 4) + 4 * w) + u];
+        const bool ok = v & 0x8000;
+        const int i = ok ? v & 255 : 0, j = ok ? (v >> 8) & 127 : 1;
+        blk_ij[u] = i | (j << 8);
+        blk_rd[u] = 2 * i * SG + 2 * j;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ee = odd ? (e ^ 1) : e;
+            const int r = slot_next(2 * i + (ee >> 1)), c = slot_next(2 * j + (ee & 1));
+            blk_wr[u][e] = ok ? min(r, c) * SG + max(r, c) : kSink;
+        }
+    }
+    const int sp_ = slot_next(2 * jr), sq_ = slot_next(2 * jr + 1);
+    const int dg_pp = sp_ * SG + sp_, dg_qq = sq_ * SG + sq_, dg_pq = min(sp_, sq_) * SG + max(sp_, sq_);
+    const int cb = CW * w;
+    const int rt_rd = 2 * jr * SR + cb + 4 * hh, rt_wp = sp_ * SR + cb + 4 * hh, rt_wq = sq_ * SR + cb + 4 * hh;
+    __syncthreads();
+    v2f dpq = {0.0f, 0.0f};
+    float gqq = 0.0f;
+    if (w == 0) {
+        dpq = *(const v2f*)&G[2 * jr * SG + 2 * jr];
+        gqq = G[(2 * jr + 1) * SG + 2 * jr + 1];
+    }
+#pragma unroll 1
+    for (int ir = 0; ir < PW - 1; ++ir) {
+        __asm__ volatile("" ::"v"(dpq), "v"(gqq));
+        v2f x0[NU], x1[NU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            x0[u] = *(const v2f*)&G[blk_rd[u]];
+            x1[u] = *(const v2f*)&G[blk_rd[u] + SG];
+        }
+        v4f xr[NK], yr[NK];
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+            xr[k] = *(const v4f*)&RT[rt_rd + 8 * k];
+            yr[k] = *(const v4f*)&RT[rt_rd + SR + 8 * k];
+        }
+        const float gpp = dpq[0], gpq = dpq[1];
+        float c = 1.0f, sn = 0.0f, cm1 = 0.0f;
+        if (w == 0) {
+            pair_rotation(gpp, gpq, gqq, floor2, tol, c, sn, cm1);
+            if (hh == 0) rot[jr] = v4f{c, sn, cm1, 0.0f};
+        }
+        __syncthreads();  // the rotations are published; every wave has read this step's G and R^T
+        if (w != 0) {
+            const v4f r = rot[jr];
+            c = r[0];
+            sn = r[1];
+            cm1 = r[2];
+        }
+        float wv[NU][4];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const int i = blk_ij[u] & 255, j = (blk_ij[u] >> 8) & 255;
+            const v2f csi = *(const v2f*)&rot[i], csj = *(const v2f*)&rot[j];
+            const float ci = csi[0], si = csi[1], cj = csj[0], sj = csj[1];
+            const float y00 = cj * x0[u][0] - sj * x0[u][1], y01 = sj * x0[u][0] + cj * x0[u][1];
+            const float y10 = cj * x1[u][0] - sj * x1[u][1], y11 = sj * x1[u][0] + cj * x1[u][1];
+            const float z00 = ci * y00 - si * y10, z01 = ci * y01 - si * y11;
+            const float z10 = si * y00 + ci * y10, z11 = si * y01 + ci * y11;
+            wv[u][0] = odd ? z01 : z00;
+            wv[u][1] = odd ? z00 : z01;
+            wv[u][2] = odd ? z11 : z10;
+            wv[u][3] = odd ? z10 : z11;
+        }
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) G[blk_wr[u][e]] = wv[u][e];
+        if (w == 0) {
+            const float y00 = c * gpp - sn * gpq, y01 = sn * gpp + c * gpq;
+            const float y10 = c * gpq - sn * gqq, y11 = sn * gpq + c * gqq;
+            G[dg_pp] = c * y00 - sn * y10;
+            G[dg_pq] = c * y01 - sn * y11;
+            G[dg_qq] = sn * y01 + c * y11;
+        }
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+            v4f np, nq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                np[e] = fmaf(cm1, xr[k][e], xr[k][e]) - sn * yr[k][e];
+                nq[e] = fmaf(cm1, yr[k][e], yr[k][e]) + sn * xr[k][e];
+            }
+            *(v4f*)&RT[rt_wp + 8 * k] = np;
+            *(v4f*)&RT[rt_wq + 8 * k] = nq;
+        }
+        __syncthreads();
+        if (w == 0) {
+            dpq = *(const v2f*)&G[2 * jr * SG + 2 * jr];
+            gqq = G[(2 * jr + 1) * SG + 2 * jr + 1];
+        }
+    }
+}
+
 // Q^T (stride SR, 64 x 64, as a QF sweep leaves it) to (Q - I)^T, by NT threads
 // (t < NT, four per row).  The off-diagonal entries are those of Q - I already.
 // A diagonal entry near 1 has lost its small distance to 1 in float32, so that

@@ -311,7 +311,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void j
                                                          const SolveItem* __restrict__ items,
                                                          int pass) {
     __shared__ __align__(16) float LS[QLEN];
-    __shared__ float cc[2][PW / 2], ss[2][PW / 2];
+    __shared__ v4f rot4[2][PW / 2];  // a step's rotations (c, s, c - 1) per pair
     __shared__ double dg[QN];
     __shared__ float mos[8];
     __shared__ double dmax_s;
@@ -448,8 +448,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void j
             //    addresses are formed here rather than kept across the other phases
             int lr_ = l, wr_ = w;
             __asm__ volatile("" : "+v"(lr_), "+s"(wr_));
-            pair_sweep<4, 1, true>((float(*)[PW * SG])Gq, (float(*)[PW * SR])RTq, cc[q], ss[q], lr_, wr_,
-                                   floor2, tol);
+            pair_sweep_q<4>(Gq, RTq, rot4[q], lr_, wr_, floor2, tol);
             __syncthreads();
             diag_to_delta<256>(RTq, pt);  // ordered before its readers by the barrier below
         }
