@@ -238,14 +238,18 @@ __device__ __forceinline__ int pair_sweep(float (*G)[PW * SG], float (*RT)[PW * 
 // barriers: reads | writes).  The same rotations and arithmetic as pair_sweep<NW, 1,
 // true>, so the same results, with the rotation's vector work (about a quarter of a
 // step, square roots and reciprocals included) done by one wave instead of four.
-// On entry G holds the pair Gram and R^T = I (copy 0, as pair_sweep).
+// On entry G holds the pair Gram and R^T = I (copy 0, as pair_sweep).  A lane
+// writes its blocks' four entries in the same order in every quarter-wave (the
+// pair rounds' sweep alternates it to spread the writes over the banks): the
+// swap's four selects a block cost more than the conflicts they avoid here
+// (group solve 0.65-0.68 -> 0.63-0.64 ms for 768 groups).
 template <int NW>
 __device__ __forceinline__ void pair_sweep_q(float* G, float* RT, v4f* rot, int l, int w, float floor2,
                                              float tol) {
     constexpr int NU = 8 / NW;   // pair-blocks of G per lane
     constexpr int NK = 8 / NW;   // 8-column groups of R^T per lane
     constexpr int CW = PW / NW;  // columns of R^T per wave
-    const int jr = l >> 1, hh = l & 1, cls = l & 15, odd = (l >> 4) & 1;
+    const int jr = l >> 1, hh = l & 1, cls = l & 15;
     int blk_ij[NU], blk_rd[NU], blk_wr[NU][4];
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -256,7 +260,7 @@ __device__ __forceinline__ void pair_sweep_q(float* G, float* RT, v4f* rot, int 
         blk_rd[u] = 2 * i * SG + 2 * j;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int ee = odd ? (e ^ 1) : e;
+            const int ee = e;
             const int r = slot_next(2 * i + (ee >> 1)), c = slot_next(2 * j + (ee & 1));
             blk_wr[u][e] = ok ? min(r, c) * SG + max(r, c) : kSink;
         }
@@ -310,10 +314,10 @@ __device__ __forceinline__ void pair_sweep_q(float* G, float* RT, v4f* rot, int 
             const float y10 = cj * x1[u][0] - sj * x1[u][1], y11 = sj * x1[u][0] + cj * x1[u][1];
             const float z00 = ci * y00 - si * y10, z01 = ci * y01 - si * y11;
             const float z10 = si * y00 + ci * y10, z11 = si * y01 + ci * y11;
-            wv[u][0] = odd ? z01 : z00;
-            wv[u][1] = odd ? z00 : z01;
-            wv[u][2] = odd ? z11 : z10;
-            wv[u][3] = odd ? z10 : z11;
+            wv[u][0] = z00;
+            wv[u][1] = z01;
+            wv[u][2] = z10;
+            wv[u][3] = z11;
         }
 #pragma unroll
         for (int u = 0; u < NU; ++u)
