@@ -274,34 +274,35 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(const MatDev* __restric
     }
 }
 
-// C_ib,kb -= L_ib,jb L_kb,jb^T for jb < kb <= ib (the lower trailing tiles), over
-// 128 x 128 blocks of the trailing lower triangle (four 64 x 64 tiles: each panel
-// block is read once for four tiles).  16 x 16 threads, each an 8 x 8 block of
-// outputs (rows ty + 16 a, columns tx + 16 b), every sum over the panel's 64
-// columns in order; the two panels pass through LDS 16 columns at a time,
-// transposed (rows padded by one element).  Entries above the diagonal or beyond
-// k are not written.
+// C -= sum over the npan panels jb .. jb + npan - 1 of L_:,p L_:,p^T, on the lower
+// part of the output columns [cfirst * 64, cend) (cend = (cfirst + cnt) * 64, or k
+// when cnt = 0) and the rows from cfirst * 64 on: one 64-wide column of tiles
+// (cnt = 1) or the whole trailing triangle.  128 x 128 blocks; 16 x 16 threads,
+// each an 8 x 8 block of outputs (rows ty + 16 a, columns tx + 16 b), each sum over
+// the panels' 64 npan columns in order; the panels pass through LDS 16 columns at
+// a time, transposed (rows padded by one element), the next chunk prefetched into
+// registers.  Entries above the diagonal or beyond k are not written.
 __global__ __launch_bounds__(256) void chol_update_kernel(const MatDev* __restrict__ mats,
                                                           const MatFlags* __restrict__ flags,
-                                                          const int* __restrict__ mat_idx, int jb) {
+                                                          const int* __restrict__ mat_idx, int jb, int npan,
+                                                          int cfirst, int cnt) {
     constexpr int UB = 2 * CT, US = 16;
-    __shared__ double P[US][UB + 1];  // L_ib,jb rows, k-major: P[s][r]
-    __shared__ double Q[US][UB + 1];  // L_kb,jb rows, k-major: Q[s][c]
+    __shared__ double P[US][UB + 1];  // the block's rows of the panels, k-major: P[s][r]
+    __shared__ double Q[US][UB + 1];  // the block's columns' rows of the panels: Q[s][c]
     const int i = mat_idx[blockIdx.y];
     const MatFlags& f = flags[i];
     const MatDev& md = mats[i];
     if (!chol_active(md, f, jb)) return;
     const int k = md.k, nbk = (k + CT - 1) / CT;
-    const int nt = nbk - jb - 1;      // trailing tile rows of this matrix
-    const int nu = (nt + 1) / 2;      // in 128-row blocks
+    if (cfirst >= nbk) return;
+    const int r0 = cfirst * CT;
+    const int cend = cnt ? min(nbk, cfirst + cnt) * CT : nbk * CT;
+    const int nrb = (k - r0 + UB - 1) / UB, ncb = (cend - r0 + UB - 1) / UB;
     const int t = blockIdx.x;
-    if (t >= nu * (nu + 1) / 2) return;
-    // t -> (a, b), 0 <= b <= a < nu, row by row over the lower triangle
-    int a = (int)((sqrtf(8.0f * t + 1.0f) - 1.0f) * 0.5f);
-    while ((a + 1) * (a + 2) / 2 <= t) ++a;
-    while (a * (a + 1) / 2 > t) --a;
-    const int b = t - a * (a + 1) / 2;
-    const int ri = (jb + 1) * CT + a * UB, rk = (jb + 1) * CT + b * UB, c0 = jb * CT;
+    if (t >= nrb * ncb) return;
+    const int a = t / ncb, b = t % ncb;
+    if (b > a) return;  // above the diagonal
+    const int ri = r0 + a * UB, rk = r0 + b * UB, c0 = jb * CT, ns = npan * CT;
     double* C = md.chol;
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
     double acc[8][8];
@@ -309,9 +310,7 @@ __global__ __launch_bounds__(256) void chol_update_kernel(const MatDev* __restri
     for (int u = 0; u < 8; ++u)
 #pragma unroll
         for (int v = 0; v < 8; ++v) acc[u][v] = 0.0;
-    // the next chunk's panel entries are loaded into registers while the current
-    // chunk is multiplied (element j of a thread: idx = tid + 256 j, row idx / 16,
-    // column idx % 16 of the chunk)
+    // element j of a thread in a chunk: idx = tid + 256 j, row idx / 16, column idx % 16
     constexpr int NE = US * UB / 256;
     double pr[NE], qr[NE];
     auto gl = [&](int s0) {
@@ -323,7 +322,7 @@ __global__ __launch_bounds__(256) void chol_update_kernel(const MatDev* __restri
         }
     };
     gl(0);
-    for (int s0 = 0; s0 < CT; s0 += US) {
+    for (int s0 = 0; s0 < ns; s0 += US) {
 #pragma unroll
         for (int j = 0; j < NE; ++j) {
             const int idx = threadIdx.x + 256 * j, r = idx >> 4, s = idx & (US - 1);
@@ -331,7 +330,7 @@ __global__ __launch_bounds__(256) void chol_update_kernel(const MatDev* __restri
             Q[s][r] = qr[j];
         }
         __syncthreads();
-        if (s0 + US < CT) gl(s0 + US);
+        if (s0 + US < ns) gl(s0 + US);
 #pragma unroll 4
         for (int s = 0; s < US; ++s) {
             double pv[8], qv[8];
@@ -352,7 +351,7 @@ __global__ __launch_bounds__(256) void chol_update_kernel(const MatDev* __restri
 #pragma unroll
         for (int v = 0; v < 8; ++v) {
             const int row = ri + ty + 16 * u, col = rk + tx + 16 * v;
-            if (row < k && col < k && col <= row) C[(int64_t)row * k + col] -= acc[u][v];
+            if (row < k && col < cend && col <= row) C[(int64_t)row * k + col] -= acc[u][v];
         }
 }
 
@@ -425,16 +424,33 @@ hipError_t launch_chol_syrk(const MatDev* mats, const MatFlags* flags, const Syr
 
 hipError_t launch_cholesky(const MatDev* mats, MatFlags* flags, const int* mat_idx, int nmat,
                            int max_nbk, int max_klen, hipStream_t st) {
-    for (int jb = 0; jb < max_nbk; ++jb) {
-        hipLaunchKernelGGL(chol_diag_kernel, dim3(nmat), dim3(256), 0, st, mats, flags, mat_idx, jb);
+    // Two panels per pass over the trailing triangle (look-ahead): factor panel jb,
+    // update only tile column jb + 1 with it, factor panel jb + 1, then update the rest
+    // of the trailing triangle with both.  Grids are sized for the largest matrix;
+    // the kernels skip what a smaller one does not have.
+    auto upd = [&](int jb, int npan, int cfirst, int cnt) {
+        const int rows = max_nbk * CT - cfirst * CT;
+        const int cols = cnt ? std::min(max_nbk - cfirst, cnt) * CT : rows;
+        const int nrb = (rows + 2 * CT - 1) / (2 * CT), ncb = (cols + 2 * CT - 1) / (2 * CT);
+        if (nrb > 0 && ncb > 0)
+            hipLaunchKernelGGL(chol_update_kernel, dim3(nrb * ncb, nmat), dim3(256), 0, st, mats, flags,
+                               mat_idx, jb, npan, cfirst, cnt);
+    };
+    auto panel = [&](int jb) {
         const int nt = max_nbk - jb - 1;
-        if (nt > 0) {
+        if (nt > 0)
             hipLaunchKernelGGL(chol_panel_kernel, dim3(nt, nmat), dim3(256), 0, st, mats, flags,
                                mat_idx, jb);
-            const int nu = (nt + 1) / 2;  // 128-row blocks of the trailing triangle
-            hipLaunchKernelGGL(chol_update_kernel, dim3(nu * (nu + 1) / 2, nmat), dim3(256), 0, st,
-                               mats, flags, mat_idx, jb);
-        }
+    };
+    for (int jb = 0; jb < max_nbk; jb += 2) {
+        hipLaunchKernelGGL(chol_diag_kernel, dim3(nmat), dim3(256), 0, st, mats, flags, mat_idx, jb);
+        if (jb + 1 >= max_nbk) break;
+        panel(jb);
+        upd(jb, 1, jb + 1, 1);
+        hipLaunchKernelGGL(chol_diag_kernel, dim3(nmat), dim3(256), 0, st, mats, flags, mat_idx, jb + 1);
+        if (jb + 2 >= max_nbk) break;
+        panel(jb + 1);
+        upd(jb, 2, jb + 2, 0);
     }
     hipLaunchKernelGGL(chol_commit_kernel, dim3((max_klen + CT - 1) / CT, max_nbk, nmat), dim3(256),
                        0, st, mats, flags, mat_idx);
