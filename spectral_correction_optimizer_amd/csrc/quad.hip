@@ -153,15 +153,12 @@ __global__ __launch_bounds__(512) void jac_quad_gram_kernel(const MatDev* __rest
 #pragma unroll
     for (int u = 0; u < 4; ++u) roff[u] = (gld(md.perm + blk[u] * kJb + lrow) * ld + lcol) * 4;
     v4u x[8];
-    auto load = [&](int c) {
+    // the loader's row of block u of chunk c
+    auto load_part = [&](int c, int u) {
         // wave-uniform: the buffer offset must be a scalar (else every load loops)
-        const int c0 = it.x0 + c * QGW;
-        const int so = __builtin_amdgcn_readfirstlane(c0 * 4);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            x[2 * u] = __builtin_amdgcn_raw_buffer_load_b128(buf, roff[u], so, kBufNT);
-            x[2 * u + 1] = __builtin_amdgcn_raw_buffer_load_b128(buf, roff[u] + 16, so, kBufNT);
-        }
+        const int so = __builtin_amdgcn_readfirstlane((it.x0 + c * QGW) * 4);
+        x[2 * u] = __builtin_amdgcn_raw_buffer_load_b128(buf, roff[u], so, kBufNT);
+        x[2 * u + 1] = __builtin_amdgcn_raw_buffer_load_b128(buf, roff[u] + 16, so, kBufNT);
     };
     const int set = wave >> 2, cq = wave & 3;
     v16f acc[5];
@@ -201,9 +198,13 @@ __global__ __launch_bounds__(512) void jac_quad_gram_kernel(const MatDev* __rest
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
     };
-    load(0);
-#pragma unroll 1
-    for (int c = 0; c < n; ++c) {
+    // Each block's row of the next chunk is requested as soon as this chunk's is
+    // split (its registers are then free), so the loads stay in flight through the
+    // split, both barriers and the products, not only through the products.  The
+    // last chunk is peeled: a branch around the loads would make the wait counts
+    // conservative (the last block's split would wait for the next chunk's loads).
+    auto chunk = [&](int c, auto more_t) {
+        constexpr bool more = decltype(more_t)::value;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             float f[8];
@@ -217,9 +218,9 @@ __global__ __launch_bounds__(512) void jac_quad_gram_kernel(const MatDev* __rest
             *(v8bf*)&Ps[0][o] = sp.h;
             *(v8bf*)&Ps[1][o] = sp.m;
             *(v8bf*)&Ps[2][o] = sp.l;
+            if constexpr (more) load_part(c + 1, u);
         }
         __syncthreads();
-        if (c + 1 < n) load(c + 1);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int col = 32 * cq + 16 * ks + 8 * hl;
@@ -256,7 +257,12 @@ __global__ __launch_bounds__(512) void jac_quad_gram_kernel(const MatDev* __rest
         }
         __syncthreads();  // before the next chunk's rows
         if ((c & 7) == 7 || c + 1 == n) fold();
-    }
+    };
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load_part(0, u);
+#pragma unroll 1
+    for (int c = 0; c + 1 < n; ++c) chunk(c, std::true_type{});
+    if (n > 0) chunk(n - 1, std::false_type{});
     double* out = quad_part(md, it.group) + (int64_t)it.split * QPART;
 #pragma unroll
     for (int k = 0; k < QPART / 512; ++k) {
