@@ -345,15 +345,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void j
     //    entry e = tid + 512 k (tile e / 1024, row (e / 32) % 32, column e % 32),
     //    scaled, into round 0's pair Grams and cross block; the largest relative
     //    off-diagonal of the group (every block pair of it)
-    auto psum = [&](int e) {
-        double a = 0.0;
-        for (int sp = 0; sp < it.nsplit; ++sp) a += gld(part + (int64_t)sp * QPART + e);
-        return a;
-    };
-    if (tid < QN) {
+    // Split 0 of the thread's 20 entries is requested together with the diagonal
+    // (one memory round trip instead of one per batch); later splits are added in
+    // batches below.  Each sum is formed in split order from 0.0, as before.
+    constexpr int NE = QPART / 512;
+    double v0[NE];
+    {
         const int b = tid >> 5, i = tid & 31;
         const int t = b == 0 ? 0 : b == 1 ? 4 : b == 2 ? 7 : 9;
-        dg[tid] = psum(t * 1024 + i * 33);
+        const int de = tid < QN ? t * 1024 + i * 33 : 0;
+        double a = 0.0;
+        a += gld(part + de);
+#pragma unroll
+        for (int k = 0; k < NE; ++k) v0[k] = 0.0 + gld(part + tid + 512 * k);
+        for (int sp = 1; sp < it.nsplit; ++sp) a += gld(part + (int64_t)sp * QPART + de);
+        if (tid < QN) dg[tid] = a;
     }
     __syncthreads();
     if (wave == 0) {
@@ -368,12 +374,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void j
     const float floor2 = (float)(floor2d * scale);
     float mo = 0.0f;
     constexpr int KB = 5;  // entries per batch of loads
-#pragma unroll 1
-    for (int k0 = 0; k0 < QPART / 512; k0 += KB) {
+    static_assert(NE % KB == 0, "whole batches");
+#pragma unroll
+    for (int k0 = 0; k0 < NE; k0 += KB) {
         double v[KB];
 #pragma unroll
-        for (int u = 0; u < KB; ++u) v[u] = 0.0;
-        for (int sp = 0; sp < it.nsplit; ++sp) {
+        for (int u = 0; u < KB; ++u) v[u] = v0[k0 + u];
+        for (int sp = 1; sp < it.nsplit; ++sp) {
             double t[KB];
 #pragma unroll
             for (int u = 0; u < KB; ++u) t[u] = gld(part + (int64_t)sp * QPART + tid + 512 * (k0 + u));
@@ -611,6 +618,24 @@ __global__ __launch_bounds__(kQuadThreads) void jac_quad_apply_kernel(const MatD
     if (flags[it.mat].done) return;
     const MatDev& md = mats[it.mat];
     if (gld(md.rot_flag + it.group) == 0) return;
+    // operand A of tile U, k-step t for lane l: R^T[32 U + l % 32][z] = R[z][32 U + l % 32]
+    // at the 8 group rows z = 32 (t / 2) + apply_row(8 (t % 2) + e, l / 32); thread
+    // idx handles (U, t, l) = (idx / 512, idx / 64 % 8, idx % 64) for idx = tid + 512 i.
+    // All 32 of a thread's loads are issued here, before the row offsets and the
+    // first chunk's loads, so that the three arrive in one memory round trip (the
+    // vector-memory counter completes in order: a wait for a later load also waits
+    // for every earlier one).
+    static_assert(4 * kQuadThreads == 4 * 8 * 64, "four (tile, k-step, lane) entries per thread");
+    const float* R = md.rot + (int64_t)it.group * (QN * QN);
+    float rf[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int idx = threadIdx.x + kQuadThreads * i;
+        const int U = idx >> 9, t = (idx >> 6) & 7, l = idx & 63;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            rf[i][e] = gld(R + (32 * (t >> 1) + apply_row(8 * (t & 1) + e, l >> 5)) * QN + 32 * U + (l & 31));
+    }
     int blk[4];
     quad_blocks(md.nb, pass, it.group, blk);
     const int ld = it.which ? md.kpad : md.K_ld;
@@ -672,16 +697,11 @@ __global__ __launch_bounds__(kQuadThreads) void jac_quad_apply_kernel(const MatD
     };
     float xa[4][16], xb[4][16];
     load(xa, 0);
-    // operand A of tile U, k-step t for lane l: R^T[32 U + l % 32][z] = R[z][32 U + l % 32]
-    // at the 8 group rows z = 32 (t / 2) + apply_row(8 (t % 2) + e, l / 32)
-    const float* R = md.rot + (int64_t)it.group * (QN * QN);
-    for (int idx = threadIdx.x; idx < 4 * 8 * 64; idx += kQuadThreads) {
-        const int U = idx >> 9, t = (idx >> 6) & 7, l = idx & 63;
-        float f[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            f[e] = gld(R + (32 * (t >> 1) + apply_row(8 * (t & 1) + e, l >> 5)) * QN + 32 * U + (l & 31));
-        const Split8 sp = split8(f);
+    for (int i = 0; i < 4; ++i) {
+        const int idx = threadIdx.x + kQuadThreads * i;
+        const int U = idx >> 9, t = (idx >> 6) & 7, l = idx & 63;
+        const Split8 sp = split8(rf[i]);
         Rp[U][0][t][l] = sp.h;
         Rp[U][1][t][l] = sp.m;
         Rp[U][2][t][l] = sp.l;
