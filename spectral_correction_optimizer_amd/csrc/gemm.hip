@@ -40,6 +40,9 @@ static_assert(BK == 16, "split_chunk16 lays out 16 k per row");
 // free of per-lane branches.  FULL: every tile lies inside its operand (rows
 // and K multiples of the tile), so nothing is clamped or zeroed.  KS: the
 // loader also fetches the k scales of its 8 values when the problem has them.
+// the stand-in source of an absent epilogue term (read, never applied)
+__device__ const float kEpiOne[1] = {1.0f};
+
 template <bool KMAJOR, bool VEC, bool KS, bool FULL, typename T>
 struct TileLoader {
     float v[8], ks[KS ? 8 : 1];
@@ -216,25 +219,47 @@ __global__ __launch_bounds__(256, 2) void gemm_grouped_kernel(const GemmProb* __
     }
 
     // Epilogue.  MFMA 32x32 output layout: lane l, register r ->
-    // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+    // row 8*(r/4) + 4*(l/32) + r%4, column l%32.  Per 32-row block, every load
+    // (row scales, column scales, Cin) is issued before any is used, at clamped
+    // (always valid) addresses and without branches: absent terms read one element
+    // of kEpiOne and are not applied.  (Per-element branches made each load a
+    // separate memory round trip.)
     const float alpha = P.alpha, beta = P.beta;
     const bool zdiag = (P.flags & GF_ZERO_DIAG) != 0;
+    const bool has_rs = P.row_scale != nullptr, has_cs = P.col_scale != nullptr, has_cin = P.Cin != nullptr;
+    const float* rsp = has_rs ? P.row_scale : kEpiOne;
+    const float* csp = has_cs ? P.col_scale : kEpiOne;
+    const float* cinp = has_cin ? P.Cin : kEpiOne;
+    const int rsm = has_rs ? 1 : 0, csm = has_cs ? 1 : 0, cinm = has_cin ? 1 : 0;
+    float cs[2];
+    int colc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int col = n0 + wn + 32 * j + ll;
+        colc[j] = min(col, N - 1);
+        cs[j] = gld(csp + csm * colc[j]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        float rs[16];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int col = n0 + wn + 32 * j + ll;
-            if (col >= N) continue;
-            const float cs = P.col_scale ? gld(P.col_scale + col) : 1.0f;
+            float cin[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rowc = min(m0 + wm + 32 * i + 8 * (r >> 2) + 4 * hl + (r & 3), M - 1);
+                if (j == 0) rs[r] = gld(rsp + rsm * rowc);
+                cin[r] = gld(cinp + cinm * ((int64_t)rowc * P.ldcin + colc[j]));
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * hl + (r & 3);
-                if (row >= M) continue;
-                float v = alpha * acc[i][j][r] * cs;
-                if (P.row_scale) v *= gld(P.row_scale + row);
+                float v = alpha * acc[i][j][r] * cs[j];
+                if (has_rs) v *= rs[r];
                 if (zdiag && row == col) v = 0.0f;
-                if (P.Cin) v += beta * gld(P.Cin + (int64_t)row * P.ldcin + col);
-                gst(P.C + (int64_t)row * P.ldc + col, v);
+                if (has_cin) v += beta * cin[r];
+                if (FULL || (row < M && col < N)) gst(P.C + (int64_t)row * P.ldc + col, v);
             }
         }
     }
