@@ -313,12 +313,16 @@ __global__ __launch_bounds__(256) void chol_update_kernel(const MatDev* __restri
     // element j of a thread in a chunk: idx = tid + 256 j, row idx / 16, column idx % 16
     constexpr int NE = US * UB / 256;
     double pr[NE], qr[NE];
+    // global-address-space loads at clamped addresses (generic loads would also
+    // count on the LDS wait counter, so every fragment read below would wait for
+    // this prefetch); out-of-range entries are zeroed when the values go to LDS,
+    // one chunk later, so that nothing waits for the loads before then
     auto gl = [&](int s0) {
 #pragma unroll
         for (int j = 0; j < NE; ++j) {
-            const int idx = threadIdx.x + 256 * j, r = idx >> 4, gs = c0 + s0 + (idx & (US - 1));
-            pr[j] = (ri + r < k && gs < k) ? C[(int64_t)(ri + r) * k + gs] : 0.0;
-            qr[j] = (rk + r < k && gs < k) ? C[(int64_t)(rk + r) * k + gs] : 0.0;
+            const int idx = threadIdx.x + 256 * j, r = idx >> 4, gsc = min(c0 + s0 + (idx & (US - 1)), k - 1);
+            pr[j] = gld(C + (int64_t)min(ri + r, k - 1) * k + gsc);
+            qr[j] = gld(C + (int64_t)min(rk + r, k - 1) * k + gsc);
         }
     };
     gl(0);
@@ -326,8 +330,9 @@ __global__ __launch_bounds__(256) void chol_update_kernel(const MatDev* __restri
 #pragma unroll
         for (int j = 0; j < NE; ++j) {
             const int idx = threadIdx.x + 256 * j, r = idx >> 4, s = idx & (US - 1);
-            P[s][r] = pr[j];
-            Q[s][r] = qr[j];
+            const bool sok = c0 + s0 + s < k;
+            P[s][r] = (ri + r < k && sok) ? pr[j] : 0.0;
+            Q[s][r] = (rk + r < k && sok) ? qr[j] : 0.0;
         }
         __syncthreads();
         if (s0 + US < ns) gl(s0 + US);
@@ -346,13 +351,33 @@ __global__ __launch_bounds__(256) void chol_update_kernel(const MatDev* __restri
         }
         __syncthreads();
     }
+    // C -= acc in batches of two rows: the batch's 16 old values are loaded
+    // together (global address space; clamped addresses inside the k x k matrix,
+    // values outside the block's lower triangle read but not written), all 16 new
+    // values formed, then the masked stores.  Per-element branches made each
+    // load, and with generic addresses each store, its own memory round trip.
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u0 = 0; u0 < 8; u0 += 2) {
+        double nv[2][8];
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            const int row = ri + ty + 16 * u, col = rk + tx + 16 * v;
-            if (row < k && col < cend && col <= row) C[(int64_t)row * k + col] -= acc[u][v];
-        }
+        for (int du = 0; du < 2; ++du)
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const int row = min(ri + ty + 16 * (u0 + du), k - 1), col = min(rk + tx + 16 * v, k - 1);
+                nv[du][v] = gld(C + (int64_t)row * k + col);
+            }
+#pragma unroll
+        for (int du = 0; du < 2; ++du)
+#pragma unroll
+            for (int v = 0; v < 8; ++v) nv[du][v] -= acc[u0 + du][v];
+#pragma unroll
+        for (int du = 0; du < 2; ++du)
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+                const int row = ri + ty + 16 * (u0 + du), col = rk + tx + 16 * v;
+                if (row < k && col < cend && col <= row) gst(C + (int64_t)row * k + col, nv[du][v]);
+            }
+    }
 }
 
 // Accepted factorizations: the rows of the Jacobi operand become the float32
