@@ -298,12 +298,22 @@ __device__ __forceinline__ int qloc(int u0, int u1, int x) {
 // SG), then the two R^T (stride SR); the cross block is staged (stride PW) in the
 // first R^T's space while no sweep runs.
 constexpr int QLG1 = PW * SG, QLR0 = 2 * PW * SG, QLR1 = QLR0 + PW * SR, QLEN = QLR1 + PW * SR;
-// Position (0 .. 3) of each slot in the pairing of round k: 0, 1 = pair P, 2, 3 = Q.
-__constant__ int kQuadPos[3][4] = {{0, 1, 2, 3}, {0, 2, 3, 1}, {0, 2, 1, 3}};
+// Position (0 .. 3) of each slot in the pairing of round k: 0, 1 = pair P, 2, 3 = Q,
+// packed two bits per slot (slot s at bits 2 s), so that a lookup by a lane's slot
+// is a shift, not a memory load (a table in memory indexed per lane took one load
+// per entry).
+constexpr int kQuadPosTab[3][4] = {{0, 1, 2, 3}, {0, 2, 3, 1}, {0, 2, 1, 3}};
+constexpr unsigned quad_pos_bits(int k) {
+    return (unsigned)kQuadPosTab[k][0] | (unsigned)kQuadPosTab[k][1] << 2 | (unsigned)kQuadPosTab[k][2] << 4 |
+           (unsigned)kQuadPosTab[k][3] << 6;
+}
+constexpr unsigned kQuadPosBits[3] = {quad_pos_bits(0), quad_pos_bits(1), quad_pos_bits(2)};
+static_assert(kQuadPosBits[0] == 0xE4u && kQuadPosBits[1] == 0x78u && kQuadPosBits[2] == 0xD8u, "slot positions");
 // LDS offset of the group Gram entry (x, y) in round k's pairing: the upper
 // triangle of pair P's or Q's Gram, or the cross block (P rows, Q columns).
 __device__ __forceinline__ int qslot_off(int k, int x, int y) {
-    const int ix = kQuadPos[k][x >> 5], iy = kQuadPos[k][y >> 5];
+    const unsigned pb = k == 0 ? kQuadPosBits[0] : k == 1 ? kQuadPosBits[1] : kQuadPosBits[2];
+    const int ix = (pb >> (2 * (x >> 5))) & 3, iy = (pb >> (2 * (y >> 5))) & 3;
     const int lx = 32 * (ix & 1) + (x & 31), ly = 32 * (iy & 1) + (y & 31);
     const int px = ix >> 1, py = iy >> 1;
     const int pair_off = (px ? QLG1 : 0) + min(lx, ly) * SG + max(lx, ly);
