@@ -127,11 +127,11 @@ QUAD_SOURCES = ["quad.hip", "jacobi_dev.hpp", "common.hpp", "internal.hpp"]
 ELEMENTWISE_SOURCES = ["elementwise.hip", "common.hpp", "internal.hpp"]
 TRAFFIC = {
     "quad_apply": [{"sources": QUAD_SOURCES, "workload": "blocks16_1b", "warmup": 5, "steps": 20,
-                    "sha256": "3718cc7d71168ae95f75e4240acbdbe00e103e6c71b852da9cbd673bb61a8929",
+                    "sha256": "cd9aa65adc943dd4049dea487535fddb9efa23f3375c43c87bc57f8a209250d9",
                     "ratio": 1.0404}],  # 1424.9 MB counted / 1369.6 MB algorithmic per launch, 8190 dispatches
     "quad_gram": [{"sources": QUAD_SOURCES, "workload": "blocks16_1b", "warmup": 5, "steps": 20,
-                   "sha256": "3718cc7d71168ae95f75e4240acbdbe00e103e6c71b852da9cbd673bb61a8929",
-                   "ratio": 1.1154}],  # 571.2 MB counted (float64 partials included) / 512.2 MB algorithmic
+                   "sha256": "cd9aa65adc943dd4049dea487535fddb9efa23f3375c43c87bc57f8a209250d9",
+                   "ratio": 1.1129}],  # 569.9 MB counted (float64 partials included) / 512.1 MB algorithmic
     "combine_adamw": [{"sources": ELEMENTWISE_SOURCES, "workload": "blocks16_1b", "warmup": 5, "steps": 20,
                        "sha256": "7a2acbba2b3c4fdf68f0a7790ea97659638a9ea6f9e49cf2ac23f4cbce7141ba",
                        "ratio": 1.0049}],  # 31.290 GB counted / 31.138 GB algorithmic per launch
